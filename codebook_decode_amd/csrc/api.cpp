@@ -1,0 +1,418 @@
+// libhr C ABI: host-side validation and the launch sequence of the prefill
+// chain and the delayed-codebook step.  Every check runs before the first
+// launch, so a failing call enqueues nothing.  No device memory is allocated,
+// freed or read here; all work goes to the caller's stream.
+//
+// Launch order of one layer (flashrt-structures prefill_tower/fp8_chain.py,
+// `run`, with the residual kept in fp32 and added inside the O / down GEMM
+// epilogues):
+//   rmsnorm(in) -> QKV GEMM -> q/k norm + RoPE + KV write -> attention ->
+//   O GEMM (h +=) -> rmsnorm(post) -> gate/up GEMM + SwiGLU -> down GEMM (h +=)
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "hr.h"
+#include "hr_ops.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+hr_status fail(hr_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HR_TRY(expr)                  \
+  do {                                \
+    hr_status _s = (expr);            \
+    if (_s != HR_OK) return _s;       \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hr_status need(const void* p, const char* name) {
+  if (p == nullptr) return fail(HR_EINVAL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(HR_EALIGN, "%s is not 16-byte aligned", name);
+  return HR_OK;
+}
+
+hr_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(HR_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return HR_OK;
+}
+
+size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+hr_status check_dims(const hr_dims* d) {
+  if (!d) return fail(HR_EINVAL, "dims is NULL");
+  if (d->hidden <= 0 || d->n_q_heads <= 0 || d->n_kv_heads <= 0 || d->head_dim <= 0 || d->ffn <= 0)
+    return fail(HR_EINVAL, "non-positive dimension");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(HR_EUNSUPPORTED, "head_dim %d not in {64, 128}", d->head_dim);
+  if (d->n_q_heads % d->n_kv_heads != 0) return fail(HR_EUNSUPPORTED, "n_q_heads %% n_kv_heads != 0");
+  const int group = d->n_q_heads / d->n_kv_heads;
+  if (group != 1 && group != 2 && group != 4)
+    return fail(HR_EUNSUPPORTED, "query heads per kv head %d not in {1, 2, 4}", group);
+  if (d->hidden % 64 || d->ffn % 64) return fail(HR_EUNSUPPORTED, "hidden and ffn must be multiples of 64");
+  if (d->hidden > 8192) return fail(HR_EUNSUPPORTED, "hidden %d > 8192", d->hidden);
+  if (!(d->rope_theta > 0.f) || !(d->rms_eps >= 0.f) || !std::isfinite(d->rope_theta))
+    return fail(HR_EINVAL, "rope_theta must be > 0 and rms_eps >= 0");
+  return HR_OK;
+}
+
+hr_status check_kv(const hr_dims* d, const hr_kv* kv, const char* name) {
+  if (!kv) return fail(HR_EINVAL, "%s is NULL", name);
+  HR_TRY(need(kv->k, "kv.k"));
+  HR_TRY(need(kv->v, "kv.v"));
+  if (kv->capacity <= 0 || kv->n_slots <= 0) return fail(HR_EINVAL, "%s: capacity and n_slots must be > 0", name);
+  (void)d;
+  return HR_OK;
+}
+
+hr_status check_batch(const hr_dims* d, const hr_batch* b, const hr_kv* kv) {
+  if (!b) return fail(HR_EINVAL, "batch is NULL");
+  if (b->n_seq <= 0) return fail(HR_EINVAL, "n_seq must be > 0");
+  if (!b->h_cu_seqlens || !b->h_start_pos || !b->h_cache_slot)
+    return fail(HR_EINVAL, "host mirrors of cu_seqlens / start_pos / cache_slot are required");
+  if (!b->cu_seqlens || !b->start_pos || !b->cache_slot)
+    return fail(HR_EINVAL, "device cu_seqlens / start_pos / cache_slot are required");
+  if (!d->causal && (!b->used_keys || !b->h_used_keys))
+    return fail(HR_EINVAL, "non-causal batches need used_keys (device and host)");
+  const int32_t* cu = b->h_cu_seqlens;
+  if (cu[0] != 0) return fail(HR_EINVAL, "cu_seqlens[0] = %d, expected 0", cu[0]);
+  for (int s = 0; s < b->n_seq; ++s) {
+    const int len = cu[s + 1] - cu[s];
+    if (len < 0) return fail(HR_EINVAL, "cu_seqlens not monotone at %d", s);
+    if (len > b->max_seqlen)
+      return fail(HR_EBOUND, "sequence %d has %d rows > max_seqlen %d", s, len, b->max_seqlen);
+    const int sp = b->h_start_pos[s], slot = b->h_cache_slot[s];
+    if (sp < 0) return fail(HR_EINVAL, "start_pos[%d] = %d < 0", s, sp);
+    if (slot < 0 || slot >= kv->n_slots)
+      return fail(HR_ECAPACITY, "cache_slot[%d] = %d outside [0, %d)", s, slot, kv->n_slots);
+    if (int64_t(sp) + len > kv->capacity)
+      return fail(HR_ECAPACITY, "sequence %d: start_pos %d + %d rows > capacity %d", s, sp, len, kv->capacity);
+    if (!d->causal) {
+      const int u = b->h_used_keys[s];
+      if (sp != 0) return fail(HR_EUNSUPPORTED, "non-causal sequences must start at position 0");
+      if (len > 0 && u < 1) return fail(HR_EINVAL, "used_keys[%d] = %d < 1", s, u);
+      if (u > len) return fail(HR_EBOUND, "used_keys[%d] = %d > %d rows", s, u, len);
+    }
+  }
+  if (cu[b->n_seq] != b->total_tokens)
+    return fail(HR_EINVAL, "cu_seqlens[n_seq] = %d != total_tokens %d", cu[b->n_seq], b->total_tokens);
+  return HR_OK;
+}
+
+hr_status check_layer(const hr_dims* d, const hr_layer* L, int idx) {
+  if (!L) return fail(HR_EINVAL, "layer %d is NULL", idx);
+  if (L->wtype != HR_BF16 && L->wtype != HR_FP8_E4M3) return fail(HR_EINVAL, "layer %d: bad wtype", idx);
+  const void* ptrs[] = {L->in_norm_w, L->post_norm_w, L->q_norm_w, L->k_norm_w,
+                        L->w_qkv,     L->w_o,         L->w_gu,     L->w_down};
+  const char* names[] = {"in_norm_w", "post_norm_w", "q_norm_w", "k_norm_w", "w_qkv", "w_o", "w_gu", "w_down"};
+  for (int i = 0; i < 8; ++i) {
+    if (!ptrs[i]) return fail(HR_EINVAL, "layer %d: %s is NULL", idx, names[i]);
+    if (!aligned16(ptrs[i])) return fail(HR_EALIGN, "layer %d: %s is not 16-byte aligned", idx, names[i]);
+  }
+  if (L->wtype == HR_FP8_E4M3) {
+    if (!L->ws_qkv || !L->ws_o || !L->ws_gu || !L->ws_down)
+      return fail(HR_EINVAL, "layer %d: FP8 weight scales missing", idx);
+    const float a[] = {L->as_qkv, L->as_o, L->as_gu, L->as_down};
+    for (float v : a)
+      if (!(v > 0.f) || !std::isfinite(v))
+        return fail(HR_EINVAL, "layer %d: FP8 activation scales must be finite and > 0", idx);
+  }
+  (void)d;
+  return HR_OK;
+}
+
+struct Ws {
+  uint8_t *x, *qkv, *q, *attn, *act, *head;
+};
+
+size_t ws_layout(const hr_dims* d, int32_t T, Ws* w, uint8_t* base) {
+  const size_t D = d->hidden, F = d->ffn, A = size_t(d->n_q_heads) * d->head_dim;
+  const size_t NQKV = size_t(d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
+  const size_t t = size_t(T > 0 ? T : 0);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    uint8_t* p = base ? base + off : nullptr;
+    off += up256(bytes);
+    return p;
+  };
+  Ws tmp;
+  tmp.x = take(t * (D > A ? D : A) * 2);
+  tmp.qkv = take(t * NQKV * 2);
+  tmp.q = take(t * A * 2);
+  tmp.attn = take(t * A * 2);
+  tmp.act = take(t * F * 2);
+  tmp.head = take(size_t(64) * D * 2);
+  if (w) *w = tmp;
+  return off;
+}
+
+// one layer's kernels over buffers already validated
+hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_batch* b, float* h, const hr_kv* kv,
+                    const Ws& w, bool first_norm_done, hipStream_t st) {
+  const int T = b->total_tokens, D = d->hidden, F = d->ffn, Hq = d->n_q_heads, Hkv = d->n_kv_heads;
+  const int dh = d->head_dim, A = Hq * dh, NQKV = (Hq + 2 * Hkv) * dh;
+  const bool fp8 = L->wtype == HR_FP8_E4M3;
+  if (!first_norm_done)
+    hr::launch_rmsnorm(h, T, D, L->in_norm_w, d->rms_eps, w.x, fp8, fp8 ? 1.0f / L->as_qkv : 1.f, st);
+  hr::launch_linear(w.x, L->w_qkv, L->ws_qkv, L->as_qkv, fp8, T, NQKV, D, HR_EPI_BF16, w.qkv, 0.f, st);
+  hr::launch_qknorm_rope_kv(w.qkv, T, Hq, Hkv, dh, d->rope_theta, d->rms_eps, b->cu_seqlens, b->start_pos,
+                            b->cache_slot, b->used_keys, b->n_seq, d->causal != 0, L->q_norm_w, L->k_norm_w,
+                            w.q, kv->k, kv->v, kv->capacity, st);
+  hr::launch_attention(w.q, kv->k, kv->v, b->cu_seqlens, b->start_pos, b->cache_slot, b->used_keys, b->n_seq,
+                       b->max_seqlen, Hq, Hkv, dh, kv->capacity, d->causal != 0, w.attn, fp8,
+                       fp8 ? 1.0f / L->as_o : 1.f, st);
+  hr::launch_linear(w.attn, L->w_o, L->ws_o, L->as_o, fp8, T, D, A, HR_EPI_RESIDUAL, h, 0.f, st);
+  hr::launch_rmsnorm(h, T, D, L->post_norm_w, d->rms_eps, w.x, fp8, fp8 ? 1.0f / L->as_gu : 1.f, st);
+  hr::launch_linear(w.x, L->w_gu, L->ws_gu, L->as_gu, fp8, T, 2 * F, D, HR_EPI_SWIGLU, w.act,
+                    fp8 ? L->as_down : 0.f, st);
+  hr::launch_linear(w.act, L->w_down, L->ws_down, L->as_down, fp8, T, D, F, HR_EPI_RESIDUAL, h, 0.f, st);
+  return check_launch("prefill layer");
+}
+
+hr_status run_head(const float* h, const hr_batch* b, int D, const void* final_w, float eps,
+                   const void* head_w, int K, int V, float* logits, void* zbuf, hipStream_t st) {
+  const int N = K * V;
+  for (int s0 = 0; s0 < b->n_seq; s0 += 32) {
+    const int n = (b->n_seq - s0) < 32 ? (b->n_seq - s0) : 32;
+    hr::launch_final_split(h, b->cu_seqlens, s0, n, D, final_w, eps, n, zbuf, st);
+    hr::launch_head_gemm(zbuf, n, head_w, N, D, logits + size_t(s0) * N, st);
+  }
+  return check_launch("head");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hr_last_error(void) { return g_err.c_str(); }
+
+size_t hr_workspace_bytes(const hr_dims* dims, hr_wtype wtype, int32_t total_tokens) {
+  (void)wtype;
+  if (!dims || total_tokens < 0) return 0;
+  return ws_layout(dims, total_tokens, nullptr, nullptr);
+}
+
+hr_status hr_prefill_layer(const hr_dims* dims, const hr_layer* layer, const hr_batch* batch, float* h,
+                           const hr_kv* kv, void* ws, size_t ws_bytes, hipStream_t stream) {
+  HR_TRY(check_dims(dims));
+  HR_TRY(check_layer(dims, layer, 0));
+  HR_TRY(check_kv(dims, kv, "kv"));
+  HR_TRY(check_batch(dims, batch, kv));
+  if (batch->total_tokens == 0) return HR_OK;
+  HR_TRY(need(h, "h"));
+  HR_TRY(need(ws, "ws"));
+  const size_t need_ws = ws_layout(dims, batch->total_tokens, nullptr, nullptr);
+  if (ws_bytes < need_ws) return fail(HR_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need_ws);
+  Ws w;
+  ws_layout(dims, batch->total_tokens, &w, static_cast<uint8_t*>(ws));
+  return run_layer(dims, layer, batch, h, kv, w, false, stream);
+}
+
+hr_status hr_prefill_stack(const hr_dims* dims, const hr_layer* layers, const hr_batch* batch,
+                           const int32_t* ids, const void* embed, int32_t vocab, const void* x_embeds,
+                           const hr_kv* kv, const void* final_norm_w, const void* head_w,
+                           int32_t n_codebooks, int32_t cb_vocab, float* h_out, float* logits_out,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  HR_TRY(check_dims(dims));
+  if (dims->n_layers <= 0) return fail(HR_EINVAL, "n_layers must be > 0");
+  if (!layers || !kv) return fail(HR_EINVAL, "layers and kv arrays are required");
+  for (int l = 0; l < dims->n_layers; ++l) {
+    HR_TRY(check_layer(dims, &layers[l], l));
+    if (layers[l].wtype != layers[0].wtype) return fail(HR_EINVAL, "all layers must share one wtype");
+    HR_TRY(check_kv(dims, &kv[l], "kv[l]"));
+    HR_TRY(check_batch(dims, batch, &kv[l]));
+  }
+  if (ids) {
+    HR_TRY(need(embed, "embed"));
+    if (vocab <= 0) return fail(HR_EINVAL, "vocab must be > 0");
+  } else {
+    HR_TRY(need(x_embeds, "x_embeds (ids is NULL)"));
+  }
+  HR_TRY(need(final_norm_w, "final_norm_w"));
+  const bool want_head = head_w != nullptr && logits_out != nullptr;
+  if ((head_w != nullptr) != (logits_out != nullptr))
+    return fail(HR_EINVAL, "head_w and logits_out must both be given or both NULL");
+  if (want_head) {
+    HR_TRY(need(head_w, "head_w"));
+    HR_TRY(need(logits_out, "logits_out"));
+    if (n_codebooks <= 0 || cb_vocab <= 0) return fail(HR_EINVAL, "n_codebooks and cb_vocab must be > 0");
+    for (int s = 0; s < batch->n_seq; ++s)
+      if (batch->h_cu_seqlens[s + 1] <= batch->h_cu_seqlens[s])
+        return fail(HR_EINVAL, "sequence %d is empty: no last row for the head", s);
+  }
+  if (batch->total_tokens == 0) return HR_OK;
+  HR_TRY(need(h_out, "h_out"));
+  HR_TRY(need(ws, "ws"));
+  const size_t need_ws = ws_layout(dims, batch->total_tokens, nullptr, nullptr);
+  if (ws_bytes < need_ws) return fail(HR_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need_ws);
+  Ws w;
+  ws_layout(dims, batch->total_tokens, &w, static_cast<uint8_t*>(ws));
+  const int T = batch->total_tokens, D = dims->hidden;
+  const hr_layer& L0 = layers[0];
+  const bool fp8 = L0.wtype == HR_FP8_E4M3;
+  hr::launch_embed_rmsnorm(ids, embed, x_embeds, T, D, L0.in_norm_w, dims->rms_eps, h_out, w.x, fp8,
+                           fp8 ? 1.0f / L0.as_qkv : 1.f, stream);
+  for (int l = 0; l < dims->n_layers; ++l)
+    HR_TRY(run_layer(dims, &layers[l], batch, h_out, &kv[l], w, l == 0, stream));
+  if (want_head)
+    HR_TRY(run_head(h_out, batch, D, final_norm_w, dims->rms_eps, head_w, n_codebooks, cb_vocab, logits_out,
+                    w.head, stream));
+  return check_launch("prefill stack");
+}
+
+hr_status hr_codebook_step(int32_t B, int32_t K, int32_t V, int32_t bos_id, int32_t eoc_id,
+                           int32_t logits_is_fp32, const void* logits, int32_t* frame, uint8_t* eoc_seen,
+                           uint8_t* done, int32_t* codes, int32_t* aligned, int32_t max_frames,
+                           const void* cb_embed, int32_t D, void* emb_out, hipStream_t stream) {
+  if (B < 0 || K <= 0 || V < 2 || D <= 0) return fail(HR_EINVAL, "bad sizes B=%d K=%d V=%d D=%d", B, K, V, D);
+  if (K > 1024) return fail(HR_EUNSUPPORTED, "K = %d > 1024 codebooks", K);
+  if (D % 8) return fail(HR_EINVAL, "D = %d is not a multiple of 8", D);
+  if (bos_id < 0 || bos_id >= V || eoc_id < 0 || eoc_id >= V || bos_id == eoc_id)
+    return fail(HR_EINVAL, "bos_id %d / eoc_id %d must be distinct ids in [0, %d)", bos_id, eoc_id, V);
+  if (!logits || !frame || !eoc_seen || !done || !codes) return fail(HR_EINVAL, "NULL state pointer");
+  if (aligned && max_frames <= 0) return fail(HR_EINVAL, "max_frames must be > 0 when aligned is given");
+  HR_TRY(need(cb_embed, "cb_embed"));
+  HR_TRY(need(emb_out, "emb_out"));
+  if (B == 0) return HR_OK;
+  hr::launch_codebook_step(B, K, V, bos_id, eoc_id, logits_is_fp32 != 0, logits, frame, eoc_seen, done, codes,
+                           aligned, max_frames, cb_embed, D, emb_out, stream);
+  return check_launch("codebook step");
+}
+
+// ------------------------------------------------------------------ step-level entries (hr_ops.h)
+hr_status hr_embed_rmsnorm(const int32_t* ids, const void* embed, int32_t vocab, const void* x_embeds,
+                           int32_t T, int32_t D, const void* norm_w, float eps, float* h_out, void* x_out,
+                           hr_wtype x_type, float x_scale, hipStream_t stream) {
+  if (T < 0 || D <= 0 || D % 8 || D > 8192) return fail(HR_EINVAL, "bad T=%d / D=%d", T, D);
+  if (ids) {
+    HR_TRY(need(embed, "embed"));
+    if (vocab <= 0) return fail(HR_EINVAL, "vocab must be > 0");
+  } else {
+    HR_TRY(need(x_embeds, "x_embeds"));
+  }
+  HR_TRY(need(norm_w, "norm_w"));
+  HR_TRY(need(h_out, "h_out"));
+  HR_TRY(need(x_out, "x_out"));
+  if (x_type == HR_FP8_E4M3 && !(x_scale > 0.f)) return fail(HR_EINVAL, "x_scale must be > 0");
+  if (T == 0) return HR_OK;
+  hr::launch_embed_rmsnorm(ids, embed, x_embeds, T, D, norm_w, eps, h_out, x_out, x_type == HR_FP8_E4M3,
+                           x_type == HR_FP8_E4M3 ? 1.0f / x_scale : 1.f, stream);
+  return check_launch("embed_rmsnorm");
+}
+
+hr_status hr_rmsnorm(const float* h, int32_t T, int32_t D, const void* norm_w, float eps, void* x_out,
+                     hr_wtype x_type, float x_scale, hipStream_t stream) {
+  if (T < 0 || D <= 0 || D % 8 || D > 8192) return fail(HR_EINVAL, "bad T=%d / D=%d", T, D);
+  HR_TRY(need(h, "h"));
+  HR_TRY(need(norm_w, "norm_w"));
+  HR_TRY(need(x_out, "x_out"));
+  if (x_type == HR_FP8_E4M3 && !(x_scale > 0.f)) return fail(HR_EINVAL, "x_scale must be > 0");
+  if (T == 0) return HR_OK;
+  hr::launch_rmsnorm(h, T, D, norm_w, eps, x_out, x_type == HR_FP8_E4M3,
+                     x_type == HR_FP8_E4M3 ? 1.0f / x_scale : 1.f, stream);
+  return check_launch("rmsnorm");
+}
+
+hr_status hr_linear(const void* x, const void* w, const float* w_scale, float x_scale, hr_wtype wtype,
+                    int32_t M, int32_t N, int32_t K, hr_epilogue epi, void* out, float out_scale,
+                    hipStream_t stream) {
+  if (M < 0 || N <= 0 || K <= 0) return fail(HR_EINVAL, "bad M=%d N=%d K=%d", M, N, K);
+  if (epi != HR_EPI_BF16 && epi != HR_EPI_RESIDUAL && epi != HR_EPI_SWIGLU) return fail(HR_EINVAL, "bad epilogue");
+  if (wtype != HR_BF16 && wtype != HR_FP8_E4M3) return fail(HR_EINVAL, "bad wtype");
+  const bool fp8 = wtype == HR_FP8_E4M3;
+  if (K % (fp8 ? 128 : 64)) return fail(HR_EUNSUPPORTED, "K = %d must be a multiple of %d", K, fp8 ? 128 : 64);
+  if (N % 16 || (epi == HR_EPI_SWIGLU && N % 32))
+    return fail(HR_EUNSUPPORTED, "N = %d must be a multiple of 16 (32 for SwiGLU)", N);
+  HR_TRY(need(x, "x"));
+  HR_TRY(need(w, "w"));
+  HR_TRY(need(out, "out"));
+  if (fp8) {
+    if (!w_scale) return fail(HR_EINVAL, "FP8 needs w_scale");
+    if (!(x_scale > 0.f)) return fail(HR_EINVAL, "FP8 needs x_scale > 0");
+    if (epi == HR_EPI_SWIGLU && !(out_scale > 0.f)) return fail(HR_EINVAL, "FP8 SwiGLU needs out_scale > 0");
+  }
+  if (M == 0) return HR_OK;
+  hr::launch_linear(x, w, w_scale, x_scale, fp8, M, N, K, epi, out, out_scale, stream);
+  return check_launch("linear");
+}
+
+hr_status hr_qknorm_rope_kv(const hr_dims* dims, const hr_batch* batch, const void* qkv, const void* q_norm_w,
+                            const void* k_norm_w, void* q_out, const hr_kv* kv, hipStream_t stream) {
+  HR_TRY(check_dims(dims));
+  HR_TRY(check_kv(dims, kv, "kv"));
+  HR_TRY(check_batch(dims, batch, kv));
+  HR_TRY(need(qkv, "qkv"));
+  HR_TRY(need(q_norm_w, "q_norm_w"));
+  HR_TRY(need(k_norm_w, "k_norm_w"));
+  HR_TRY(need(q_out, "q_out"));
+  if (batch->total_tokens == 0) return HR_OK;
+  hr::launch_qknorm_rope_kv(qkv, batch->total_tokens, dims->n_q_heads, dims->n_kv_heads, dims->head_dim,
+                            dims->rope_theta, dims->rms_eps, batch->cu_seqlens, batch->start_pos,
+                            batch->cache_slot, batch->used_keys, batch->n_seq, dims->causal != 0, q_norm_w,
+                            k_norm_w, q_out, kv->k, kv->v, kv->capacity, stream);
+  return check_launch("qknorm_rope_kv");
+}
+
+hr_status hr_attention(const hr_dims* dims, const hr_batch* batch, const void* q, const hr_kv* kv, void* out,
+                       hr_wtype out_type, float out_scale, hipStream_t stream) {
+  HR_TRY(check_dims(dims));
+  HR_TRY(check_kv(dims, kv, "kv"));
+  HR_TRY(check_batch(dims, batch, kv));
+  HR_TRY(need(q, "q"));
+  HR_TRY(need(out, "out"));
+  if (out_type == HR_FP8_E4M3 && !(out_scale > 0.f)) return fail(HR_EINVAL, "out_scale must be > 0");
+  if (batch->total_tokens == 0) return HR_OK;
+  hr::launch_attention(q, kv->k, kv->v, batch->cu_seqlens, batch->start_pos, batch->cache_slot, batch->used_keys,
+                       batch->n_seq, batch->max_seqlen, dims->n_q_heads, dims->n_kv_heads, dims->head_dim,
+                       kv->capacity, dims->causal != 0, out, out_type == HR_FP8_E4M3,
+                       out_type == HR_FP8_E4M3 ? 1.0f / out_scale : 1.f, stream);
+  return check_launch("attention");
+}
+
+size_t hr_head_workspace_bytes(int32_t n_seq, int32_t D) {
+  (void)n_seq;
+  return D > 0 ? up256(size_t(64) * D * 2) : 0;
+}
+
+hr_status hr_head_logits(const float* h, const hr_batch* batch, int32_t D, const void* final_norm_w, float eps,
+                         const void* head_w, int32_t n_codebooks, int32_t cb_vocab, float* logits_out, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  if (!batch || batch->n_seq <= 0 || !batch->cu_seqlens || !batch->h_cu_seqlens)
+    return fail(HR_EINVAL, "batch with n_seq > 0 and cu_seqlens required");
+  if (D <= 0 || D % 64 || D > 8192) return fail(HR_EUNSUPPORTED, "D = %d must be a positive multiple of 64", D);
+  if (n_codebooks <= 0 || cb_vocab <= 0) return fail(HR_EINVAL, "n_codebooks and cb_vocab must be > 0");
+  for (int s = 0; s < batch->n_seq; ++s)
+    if (batch->h_cu_seqlens[s + 1] <= batch->h_cu_seqlens[s])
+      return fail(HR_EINVAL, "sequence %d is empty: no last row for the head", s);
+  HR_TRY(need(h, "h"));
+  HR_TRY(need(final_norm_w, "final_norm_w"));
+  HR_TRY(need(head_w, "head_w"));
+  HR_TRY(need(logits_out, "logits_out"));
+  HR_TRY(need(ws, "ws"));
+  if (ws_bytes < hr_head_workspace_bytes(batch->n_seq, D)) return fail(HR_EWORKSPACE, "head workspace too small");
+  return run_head(h, batch, D, final_norm_w, eps, head_w, n_codebooks, cb_vocab, logits_out, ws, stream);
+}
+
+hr_status hr_quantize_weight_e4m3(const void* w, int32_t N, int32_t K, uint8_t* w8, float* scale,
+                                  hipStream_t stream) {
+  if (N <= 0 || K <= 0) return fail(HR_EINVAL, "bad N=%d K=%d", N, K);
+  if (!w || !w8 || !scale) return fail(HR_EINVAL, "NULL pointer");
+  hr::launch_quant_weight(w, N, K, w8, scale, stream);
+  return check_launch("quantize_weight");
+}
+
+}  // extern "C"

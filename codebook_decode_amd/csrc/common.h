@@ -1,0 +1,90 @@
+// Device-side helpers shared by the gfx950 kernels: number formats, vector
+// types for the MFMA builtins, wavefront (64-lane) reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hr {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- bfloat16
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+
+// ---------------------------------------------------------------- OCP E4M3
+// fp32 -> e4m3fn code: nearest even, magnitudes beyond 448 saturate to 448.
+// Normal E4M3 values are (1 + m/8) 2^(e-7), e in 1..15; subnormals m 2^-9.
+__device__ __forceinline__ uint32_t f2e4m3(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0x7Fu;                    // NaN
+  float af = __uint_as_float(a);
+  uint32_t code;
+  if (af >= 448.0f) {
+    code = 0x7Eu;
+  } else if (af < 0.015625f) {                           // below 2^-6: step 2^-9
+    code = uint32_t(__builtin_rintf(af * 512.0f));       // 0..8; 8 is 2^-6 (code 8)
+  } else {
+    int e = int(a >> 23) - 127;                          // -6 .. 8
+    uint32_t mant = a & 0x7FFFFFu;
+    uint32_t keep = mant >> 20;
+    uint32_t rem = mant & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) keep++;
+    if (keep == 8u) { keep = 0; e++; }
+    code = (uint32_t(e + 7) << 3) | keep;
+    if (code > 0x7Eu) code = 0x7Eu;
+  }
+  return code == 0 ? 0u : (code | sign);
+}
+
+__device__ __forceinline__ float e4m3_to_f(uint32_t c) {
+  uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : float(m) * 0.001953125f;
+  return (c & 0x80u) ? -v : v;
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+// sum over groups of `width` consecutive lanes (width a power of two <= 64)
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int m = width >> 1; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int find_seq(const int32_t* cu, int n_seq, int t) {
+  int lo = 0, hi = n_seq - 1;                            // largest s with cu[s] <= t
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace hr

@@ -1,0 +1,43 @@
+// Internal launchers of libhr's kernels (host side).  Shapes are validated by
+// api.cpp before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hr_ops.h"
+
+namespace hr {
+
+constexpr int HR_EPI_HEAD = 3;  // internal: fp32 logits from hi/lo bf16 rows
+
+void launch_codebook_step(int B, int K, int V, int bos, int eoc, bool f32, const void* logits,
+                          int32_t* frame, uint8_t* eoc_seen, uint8_t* done, int32_t* codes,
+                          int32_t* aligned, int max_frames, const void* cb_embed, int D,
+                          void* emb_out, hipStream_t st);
+
+void launch_embed_rmsnorm(const int32_t* ids, const void* embed, const void* x_embeds, int T, int D,
+                          const void* w, float eps, float* h_out, void* x_out, bool fp8,
+                          float inv_scale, hipStream_t st);
+void launch_rmsnorm(const float* h, int T, int D, const void* w, float eps, void* x_out, bool fp8,
+                    float inv_scale, hipStream_t st);
+void launch_final_split(const float* h, const int32_t* cu, int seq0, int n, int D, const void* w,
+                        float eps, int n_rows, void* zsplit, hipStream_t st);
+void launch_quant_weight(const void* w, int N, int K, uint8_t* w8, float* scale, hipStream_t st);
+
+void launch_qknorm_rope_kv(const void* qkv, int T, int Hq, int Hkv, int d, float theta, float eps,
+                           const int32_t* cu, const int32_t* start_pos, const int32_t* cache_slot,
+                           const int32_t* used_keys, int n_seq, bool causal, const void* qw,
+                           const void* kw, void* q_out, void* kc, void* vc, int capacity,
+                           hipStream_t st);
+
+void launch_attention(const void* q, const void* kc, const void* vc, const int32_t* cu,
+                      const int32_t* sp, const int32_t* slot, const int32_t* used, int n_seq,
+                      int max_len, int Hq, int Hkv, int d, int cap, bool causal, void* out, bool fp8,
+                      float out_inv, hipStream_t st);
+
+void launch_linear(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8,
+                   int M, int N, int K, int epi, void* out, float out_scale, hipStream_t st);
+void launch_head_gemm(const void* zsplit, int n, const void* w, int N, int D, float* out,
+                      hipStream_t st);
+
+}  // namespace hr

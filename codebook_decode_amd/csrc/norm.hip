@@ -1,0 +1,199 @@
+// RMSNorm family (flashrt-structures prefill_tower/fp8_chain.py, `run`: norm
+// before the merged QKV and gate/up GEMMs, final fp32 RMSNorm times the final
+// weight; eps 1e-6):
+//   embed_rmsnorm : h = widen(embed[id]) (or given bf16 rows); x = RMS(h) * w
+//   rmsnorm       : x = RMS(h) * w from the fp32 residual
+//   final_split   : z = RMS(h[last row of s]) * w in fp32, stored as two bf16
+//                   terms hi = bf16(z), lo = bf16(z - hi) for the head GEMM
+//   quant_weight  : per-output-channel E4M3 packing of a bf16 weight
+// The fp32 residual h is read once into registers (one row per workgroup,
+// 8 elements per thread, 128-bit accesses); the row sum of squares is a
+// wavefront butterfly plus a cross-wave LDS step.
+#include "common.h"
+#include "launch.h"
+
+namespace hr {
+
+constexpr int kNormThreads = 256;
+constexpr int kNormMaxPerThread = 4;  // chunks of 8 -> D <= 256 * 32 = 8192
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+
+// Write 8 normalised values as bf16 (16 B) or e4m3 (8 B).
+__device__ __forceinline__ void store_x8(void* x_out, size_t idx8, const float* y, bool fp8,
+                                         float inv_scale) {
+  if (fp8) {
+    u32x2 o;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w |= f2e4m3(y[4 * j + i] * inv_scale) << (8 * i);
+      o[j] = w;
+    }
+    reinterpret_cast<u32x2*>(x_out)[idx8] = o;
+  } else {
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = pack_bf2(y[2 * j], y[2 * j + 1]);
+    reinterpret_cast<u32x4*>(x_out)[idx8] = o;
+  }
+}
+
+// mode 0: h given (fp32 rows); mode 1: rows from embed[ids]; mode 2: bf16 rows given
+template <int MODE>
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
+    const float* __restrict__ h_in, const int32_t* __restrict__ ids,
+    const uint16_t* __restrict__ rows_bf16, float* __restrict__ h_out, int D,
+    const uint16_t* __restrict__ w, float eps, void* __restrict__ x_out, int fp8, float inv_scale) {
+  __shared__ float red[kNormThreads / 64];
+  const int t = blockIdx.x;
+  const int n8 = D >> 3;
+  float v[kNormMaxPerThread][8];
+  float ss = 0.f;
+  const uint16_t* src16 = nullptr;
+  if (MODE == 1) src16 = rows_bf16 + size_t(ids[t]) * D;
+  if (MODE == 2) src16 = rows_bf16 + size_t(t) * D;
+#pragma unroll
+  for (int c = 0; c < kNormMaxPerThread; ++c) {
+    int i8 = threadIdx.x + c * kNormThreads;
+    if (i8 < n8) {
+      if (MODE == 0) {
+        const floatx4* p = reinterpret_cast<const floatx4*>(h_in + size_t(t) * D) + 2 * i8;
+        floatx4 a = p[0], b = p[1];
+        v[c][0] = a[0]; v[c][1] = a[1]; v[c][2] = a[2]; v[c][3] = a[3];
+        v[c][4] = b[0]; v[c][5] = b[1]; v[c][6] = b[2]; v[c][7] = b[3];
+      } else {
+        u32x4 q = reinterpret_cast<const u32x4*>(src16)[i8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { v[c][2 * j] = bf_lo(q[j]); v[c][2 * j + 1] = bf_hi(q[j]); }
+        floatx4* hp = reinterpret_cast<floatx4*>(h_out + size_t(t) * D) + 2 * i8;
+        hp[0] = floatx4{v[c][0], v[c][1], v[c][2], v[c][3]};
+        hp[1] = floatx4{v[c][4], v[c][5], v[c][6], v[c][7]};
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss += v[c][j] * v[c][j];
+    }
+  }
+  float tot = block_sum(ss, red);
+  float r = 1.0f / __builtin_sqrtf(tot / float(D) + eps);
+#pragma unroll
+  for (int c = 0; c < kNormMaxPerThread; ++c) {
+    int i8 = threadIdx.x + c * kNormThreads;
+    if (i8 < n8) {
+      u32x4 wq = reinterpret_cast<const u32x4*>(w)[i8];
+      float y[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y[2 * j] = v[c][2 * j] * r * bf_lo(wq[j]);
+        y[2 * j + 1] = v[c][2 * j + 1] * r * bf_hi(wq[j]);
+      }
+      store_x8(x_out, size_t(t) * n8 + i8, y, fp8 != 0, inv_scale);
+    }
+  }
+}
+
+// z = RMS(h[row]) * w (fp32); out rows s (hi) and n_rows + s (lo), bf16, stride D.
+__global__ __launch_bounds__(kNormThreads) void final_split_kernel(
+    const float* __restrict__ h, const int32_t* __restrict__ cu, int row0_seq, int D,
+    const uint16_t* __restrict__ w, float eps, int n_rows, uint16_t* __restrict__ zsplit) {
+  __shared__ float red[kNormThreads / 64];
+  const int s = blockIdx.x;
+  const int row = cu[row0_seq + s + 1] - 1;
+  const int n8 = D >> 3;
+  float v[kNormMaxPerThread][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < kNormMaxPerThread; ++c) {
+    int i8 = threadIdx.x + c * kNormThreads;
+    if (i8 < n8) {
+      const floatx4* p = reinterpret_cast<const floatx4*>(h + size_t(row) * D) + 2 * i8;
+      floatx4 a = p[0], b = p[1];
+      v[c][0] = a[0]; v[c][1] = a[1]; v[c][2] = a[2]; v[c][3] = a[3];
+      v[c][4] = b[0]; v[c][5] = b[1]; v[c][6] = b[2]; v[c][7] = b[3];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss += v[c][j] * v[c][j];
+    }
+  }
+  float tot = block_sum(ss, red);
+  float r = 1.0f / __builtin_sqrtf(tot / float(D) + eps);
+#pragma unroll
+  for (int c = 0; c < kNormMaxPerThread; ++c) {
+    int i8 = threadIdx.x + c * kNormThreads;
+    if (i8 < n8) {
+      u32x4 wq = reinterpret_cast<const u32x4*>(w)[i8];
+      u32x4 hi, lo;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float z0 = v[c][2 * j] * r * bf_lo(wq[j]);
+        float z1 = v[c][2 * j + 1] * r * bf_hi(wq[j]);
+        uint32_t h0 = f2bf(z0), h1 = f2bf(z1);
+        hi[j] = h0 | (h1 << 16);
+        lo[j] = pack_bf2(z0 - bf2f(uint16_t(h0)), z1 - bf2f(uint16_t(h1)));
+      }
+      reinterpret_cast<u32x4*>(zsplit + size_t(s) * D)[i8] = hi;
+      reinterpret_cast<u32x4*>(zsplit + size_t(n_rows + s) * D)[i8] = lo;
+    }
+  }
+}
+
+// One workgroup per weight row: scale = max|w| / 448, codes = e4m3(w / scale).
+__global__ __launch_bounds__(kNormThreads) void quant_weight_kernel(
+    const uint16_t* __restrict__ w, int K, uint8_t* __restrict__ w8, float* __restrict__ scale) {
+  __shared__ float red[kNormThreads / 64];
+  const int n = blockIdx.x;
+  const uint16_t* row = w + size_t(n) * K;
+  float m = 0.f;
+  for (int k = threadIdx.x; k < K; k += blockDim.x) m = fmaxf(m, fabsf(bf2f(row[k])));
+  m = wave_max(m);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  float amax = 0.f;
+  for (int i = 0; i < int(blockDim.x >> 6); ++i) amax = fmaxf(amax, red[i]);
+  float s = amax / 448.0f;
+  if (!(s > 0.f)) s = 1.0f;
+  if (threadIdx.x == 0) scale[n] = s;
+  for (int k = threadIdx.x; k < K; k += blockDim.x) w8[size_t(n) * K + k] = uint8_t(f2e4m3(bf2f(row[k]) / s));
+}
+
+void launch_embed_rmsnorm(const int32_t* ids, const void* embed, const void* x_embeds, int T, int D,
+                          const void* w, float eps, float* h_out, void* x_out, bool fp8,
+                          float inv_scale, hipStream_t st) {
+  const uint16_t* w16 = static_cast<const uint16_t*>(w);
+  if (ids)
+    rmsnorm_kernel<1><<<T, kNormThreads, 0, st>>>(nullptr, ids, static_cast<const uint16_t*>(embed),
+                                                  h_out, D, w16, eps, x_out, fp8, inv_scale);
+  else
+    rmsnorm_kernel<2><<<T, kNormThreads, 0, st>>>(nullptr, nullptr,
+                                                  static_cast<const uint16_t*>(x_embeds), h_out, D,
+                                                  w16, eps, x_out, fp8, inv_scale);
+}
+
+void launch_rmsnorm(const float* h, int T, int D, const void* w, float eps, void* x_out, bool fp8,
+                    float inv_scale, hipStream_t st) {
+  rmsnorm_kernel<0><<<T, kNormThreads, 0, st>>>(h, nullptr, nullptr, nullptr, D,
+                                                static_cast<const uint16_t*>(w), eps, x_out, fp8,
+                                                inv_scale);
+}
+
+void launch_final_split(const float* h, const int32_t* cu, int seq0, int n, int D, const void* w,
+                        float eps, int n_rows, void* zsplit, hipStream_t st) {
+  final_split_kernel<<<n, kNormThreads, 0, st>>>(h, cu, seq0, D, static_cast<const uint16_t*>(w),
+                                                 eps, n_rows, static_cast<uint16_t*>(zsplit));
+}
+
+void launch_quant_weight(const void* w, int N, int K, uint8_t* w8, float* scale, hipStream_t st) {
+  quant_weight_kernel<<<N, kNormThreads, 0, st>>>(static_cast<const uint16_t*>(w), K, w8, scale);
+}
+
+}  // namespace hr

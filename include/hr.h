@@ -1,0 +1,186 @@
+/*
+ * hr.h -- C ABI of libhr: batched prefill of a Qwen3-style decoder stack that
+ * feeds a multi-codebook audio head, and the head's delayed-codebook step, on
+ * one AMD Instinct MI355X (gfx950).
+ *
+ * What the calls compute (sources cited by page title and section):
+ *  - "Stabilize Higgs Audio termination and prefill" (FlashRT pull request 141),
+ *    Summary: the batched prefill is embedding lookup, projection GEMMs, q/k
+ *    norm + RoPE and KV writes; a delayed-codebook helper does per-frame
+ *    argmax, delay handling and codebook-embedding accumulation; the delayed
+ *    EOC check must cover every codebook (Root cause); FP8 activation scales
+ *    are static, taken once from a fixed calibration prompt.
+ *  - flashrt-structures 0.2.0, prefill_tower/fp8_chain.py, module docstring and
+ *    the per-call `run`: RMSNorm -> merged QKV GEMM -> split + RoPE + KV cache
+ *    -> attention over exactly the used keys -> output projection -> fused
+ *    residual + RMSNorm -> merged gate/up GEMM -> activation -> down GEMM;
+ *    static per-tensor activation scales `amax / FP8_MAX`, GEMM alpha =
+ *    activation scale x weight scale; a raw-pointer GEMM entry
+ *    `(x, w, out, M, N, K, alpha, beta, stream)` is the precedent for this ABI.
+ *  - "feat(higgs-audio): add checkpoint loading and validation foundation"
+ *    (pegainfer pull request 864), Summary: the backbone's final hidden feeds
+ *    the audio-head projection.
+ *  - vLLM-Omni pull request 8226 (Higgs Audio v3 on Model Runner V2), Purpose:
+ *    a launch bound smaller than the longest query silently breaks attention,
+ *    so bounds are checked, never assumed (HR_EBOUND).
+ *
+ * Conventions for every call:
+ *  - All tensors are row-major and live in device memory owned by the caller;
+ *    the library never allocates, frees or reads device memory on the host.
+ *  - bf16 tensors are passed as `const void*` (IEEE bfloat16 bit patterns);
+ *    e4m3 tensors as OCP FP8 E4M3 (e4m3fn) bytes.
+ *  - Every check runs on the host before the first launch; a call that
+ *    returns a non-OK status has enqueued nothing.  Work is enqueued on
+ *    `stream` in order; the call returns without synchronising.
+ *  - Device pointers must be 16-byte aligned (HR_EALIGN otherwise).
+ *  - hr_last_error() returns a thread-local message for the last failure.
+ */
+#ifndef HR_H
+#define HR_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HR_OK = 0,
+  HR_EINVAL = -1,        /* null pointer, bad size, cu_seqlens not monotone, ... */
+  HR_EUNSUPPORTED = -2,  /* shape outside what the kernels implement            */
+  HR_ECAPACITY = -3,     /* start_pos + len > capacity, cache_slot >= n_slots    */
+  HR_EBOUND = -4,        /* max_seqlen < a sequence length, used_keys > length   */
+  HR_EWORKSPACE = -5,    /* workspace smaller than hr_workspace_bytes()          */
+  HR_EALIGN = -6,        /* device pointer not 16-byte aligned                   */
+  HR_EHIP = -7           /* a HIP launch error                                   */
+} hr_status;
+
+typedef enum { HR_BF16 = 0, HR_FP8_E4M3 = 1 } hr_wtype;
+
+/* Shapes of the decoder.  Supported: head_dim in {64, 128};
+ * n_q_heads / n_kv_heads in {1, 2, 4}; hidden, ffn multiples of 64. */
+typedef struct {
+  int32_t hidden;      /* D */
+  int32_t n_q_heads;   /* Hq */
+  int32_t n_kv_heads;  /* Hkv */
+  int32_t head_dim;    /* d */
+  int32_t ffn;         /* F (SwiGLU width) */
+  int32_t n_layers;    /* L (hr_prefill_stack) */
+  float rope_theta;    /* RoPE base, e.g. 1e6 */
+  float rms_eps;       /* RMSNorm epsilon, e.g. 1e-6 */
+  int32_t causal;      /* 1: query i sees cache positions [0, start_pos+i];
+                          0: every query sees [0, used_keys[s]) and rows
+                             i >= used_keys[s] are trailing pads            */
+} hr_dims;
+
+/* One decoder layer: device pointers, weights row-major [out, in].
+ *  bf16:  w_* are bf16.
+ *  FP8:   w_* are e4m3 codes with per-output-channel fp32 scales ws_* so that
+ *         W[n, k] ~= ws[n] * e4m3(w[n, k]); as_* are the static per-tensor
+ *         activation scales (host floats): the GEMM input x is quantised as
+ *         e4m3(x / as) and the product is rescaled by as * ws[n].
+ * Row order of w_qkv: q heads, then k heads, then v heads ([(Hq+2Hkv)d, D]).
+ * Row order of w_gu: the gate projection, then the up projection ([2F, D]). */
+typedef struct {
+  hr_wtype wtype;
+  const void* in_norm_w;    /* bf16 [D] */
+  const void* post_norm_w;  /* bf16 [D] */
+  const void* q_norm_w;     /* bf16 [d] */
+  const void* k_norm_w;     /* bf16 [d] */
+  const void* w_qkv;        /* [(Hq+2Hkv)d, D] */
+  const void* w_o;          /* [D, Hq d] */
+  const void* w_gu;         /* [2F, D] */
+  const void* w_down;       /* [D, F] */
+  const float* ws_qkv;      /* FP8 only: [(Hq+2Hkv)d] */
+  const float* ws_o;        /* FP8 only: [D] */
+  const float* ws_gu;       /* FP8 only: [2F] */
+  const float* ws_down;     /* FP8 only: [D] */
+  float as_qkv, as_o, as_gu, as_down;  /* FP8 only, > 0 */
+} hr_layer;
+
+/* KV cache of one layer: bf16 [n_slots * capacity, Hkv, d]; position p of the
+ * sequence placed in slot s lives at row s * capacity + p.  Keys are stored
+ * after q/k RMSNorm and RoPE (rotate-half order), values as projected. */
+typedef struct {
+  void* k;
+  void* v;
+  int32_t capacity;
+  int32_t n_slots;
+} hr_kv;
+
+/* A packed varlen batch: the rows of sequence s are [cu_seqlens[s],
+ * cu_seqlens[s+1]).  A single prompt of length P is n_seq = 1, cu = {0, P}.
+ * Device arrays are read by the kernels; host mirrors (same contents) are
+ * read by the validation.  used_keys / h_used_keys may be NULL when causal. */
+typedef struct {
+  int32_t n_seq;
+  int32_t total_tokens;  /* T = cu_seqlens[n_seq] */
+  int32_t max_seqlen;    /* >= every sequence length (HR_EBOUND otherwise) */
+  const int32_t* cu_seqlens;   /* device [n_seq + 1] */
+  const int32_t* start_pos;    /* device [n_seq]: position of the first row */
+  const int32_t* cache_slot;   /* device [n_seq] */
+  const int32_t* used_keys;    /* device [n_seq] (non-causal) */
+  const int32_t* h_cu_seqlens; /* host mirrors */
+  const int32_t* h_start_pos;
+  const int32_t* h_cache_slot;
+  const int32_t* h_used_keys;
+} hr_batch;
+
+/* Bytes of scratch the prefill calls need for `total_tokens` rows. */
+size_t hr_workspace_bytes(const hr_dims* dims, hr_wtype wtype, int32_t total_tokens);
+
+/* One decoder layer over a packed batch.
+ *  h   fp32 [T, D], in/out: the residual stream (h <- layer(h)).
+ *  kv  this layer's cache; rows of this batch's positions are written.
+ *  ws  device scratch of at least hr_workspace_bytes(dims, layer->wtype, T). */
+hr_status hr_prefill_layer(const hr_dims* dims, const hr_layer* layer, const hr_batch* batch,
+                           float* h, const hr_kv* kv, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* The whole stack: h_0 = embed[ids] (or x_embeds when ids == NULL), layers
+ * 0..L-1, then z = RMSNorm(h_L; final_norm_w).
+ *  layers, kv   host arrays of L entries.
+ *  embed        bf16 [vocab, D]; ids int32 [T] in [0, vocab) (not range-checked
+ *               on the device: an out-of-range id is the caller's error).
+ *  x_embeds     bf16 [T, D] input rows, used iff ids == NULL.
+ *  h_out        fp32 [T, D]: receives h_L (the residual after the last layer).
+ *  head_w       bf16 [K*V, D] or NULL; logits_out fp32 [n_seq, K, V] receives
+ *               z(last row of each sequence) . head_w^T when both are given.
+ * All layers must share one wtype. */
+hr_status hr_prefill_stack(const hr_dims* dims, const hr_layer* layers, const hr_batch* batch,
+                           const int32_t* ids, const void* embed, int32_t vocab,
+                           const void* x_embeds, const hr_kv* kv, const void* final_norm_w,
+                           const void* head_w, int32_t n_codebooks, int32_t cb_vocab,
+                           float* h_out, float* logits_out, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* One delayed-codebook decode step for B streams (K codebooks of V ids).
+ *  logits     [B, K, V], bf16 (logits_is_fp32 = 0) or fp32 (1).
+ *  frame      int32 [B] in/out: decode step of each stream.
+ *  eoc_seen   uint8 [B, K] in/out: codebook k has emitted EOC (sticky).
+ *  done       uint8 [B] in/out: every codebook has emitted EOC.
+ *  codes      int32 [B, K] out: the ids emitted this step.
+ *  aligned    int32 [B, max_frames, K] or NULL: aligned frame f of codebook k
+ *             is written at the step it is emitted (t = f + k), if f < max_frames.
+ *  cb_embed   bf16 [K*V, D]; emb_out bf16 [B, D] = bf16(sum_k cb_embed[k*V+c_k])
+ *             summed in fp32 in codebook order, rounded once (nearest-even).
+ * Per stream: a done stream emits EOC everywhere and keeps its state.  Else with
+ * t = frame: codebook k emits BOS while t < k, EOC if it already emitted EOC,
+ * otherwise the lowest index of its row maximum; then frame = t+1 and
+ * done = all codebooks have emitted EOC.
+ * HR_EINVAL if bos_id or eoc_id is outside [0, V) or bos_id == eoc_id, or
+ * D is not a multiple of 8. */
+hr_status hr_codebook_step(int32_t B, int32_t K, int32_t V, int32_t bos_id, int32_t eoc_id,
+                           int32_t logits_is_fp32, const void* logits, int32_t* frame,
+                           uint8_t* eoc_seen, uint8_t* done, int32_t* codes, int32_t* aligned,
+                           int32_t max_frames, const void* cb_embed, int32_t D, void* emb_out,
+                           hipStream_t stream);
+
+const char* hr_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HR_H */

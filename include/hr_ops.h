@@ -1,0 +1,84 @@
+/*
+ * hr_ops.h -- the individual steps of the prefill chain declared in hr.h, each
+ * exposed on its own so that a caller (or a test) can run and check one step.
+ * hr_prefill_layer / hr_prefill_stack run exactly these kernels in this order.
+ * Conventions (ownership, alignment, errors, streams) are those of hr.h.
+ *
+ * Sources, by page title and section: flashrt-structures 0.2.0
+ * prefill_tower/fp8_chain.py (module docstring; `run`; `_build_rope`;
+ * `_prefill_mask_facts`; the quantiser table of `_quantize`), and
+ * "Stabilize Higgs Audio termination and prefill", Summary.
+ */
+#ifndef HR_OPS_H
+#define HR_OPS_H
+
+#include "hr.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Embedding lookup + input RMSNorm (steps A0, A1).
+ * h_out[t] = embed[ids[t]] widened to fp32 (x_embeds[t] when ids == NULL);
+ * x_out[t] = h[t] * (mean(h[t]^2) + eps)^-1/2 * norm_w, stored bf16, or as
+ * e4m3(x / x_scale) when x_type == HR_FP8_E4M3.  D a multiple of 8. */
+hr_status hr_embed_rmsnorm(const int32_t* ids, const void* embed, int32_t vocab,
+                           const void* x_embeds, int32_t T, int32_t D, const void* norm_w,
+                           float eps, float* h_out, void* x_out, hr_wtype x_type, float x_scale,
+                           hipStream_t stream);
+
+/* RMSNorm of the fp32 residual (steps A6, A9): x_out[t] = RMS(h[t]) * norm_w,
+ * bf16 or e4m3(x / x_scale).  (The residual add itself is fused into the
+ * epilogue of the O and down projections, HR_EPI_RESIDUAL.) */
+hr_status hr_rmsnorm(const float* h, int32_t T, int32_t D, const void* norm_w, float eps,
+                     void* x_out, hr_wtype x_type, float x_scale, hipStream_t stream);
+
+typedef enum {
+  HR_EPI_BF16 = 0,      /* out bf16 [M, N] = x W^T                               */
+  HR_EPI_RESIDUAL = 1,  /* out fp32 [M, N] += x W^T  (residual add)              */
+  HR_EPI_SWIGLU = 2     /* N = 2F (gate rows, then up rows); out [M, F] =
+                           silu(g) * u, bf16, or e4m3(./out_scale) in FP8 mode  */
+} hr_epilogue;
+
+/* Projection (steps A2, A5, A7, A8): x [M, K] times W [N, K]^T.
+ *  bf16:  x and w bf16; w_scale ignored.
+ *  FP8:   x and w e4m3; the product is scaled by x_scale * w_scale[n].
+ * K a multiple of 64, N a multiple of 16 (32 for SWIGLU). */
+hr_status hr_linear(const void* x, const void* w, const float* w_scale, float x_scale,
+                    hr_wtype wtype, int32_t M, int32_t N, int32_t K, hr_epilogue epi, void* out,
+                    float out_scale, hipStream_t stream);
+
+/* Per-head q/k RMSNorm + rotate-half RoPE + KV-cache write (step A3).
+ * qkv bf16 [T, (Hq+2Hkv)d] -> q_out bf16 [T, Hq, d] (normed, rotated);
+ * cache rows slot*capacity + start_pos + i receive k (normed, rotated) and v.
+ * RoPE angle of pair (m, m + d/2) at position p: p * theta^(-2m/d).
+ * Non-causal batches skip the cache write of pad rows i >= used_keys[s]. */
+hr_status hr_qknorm_rope_kv(const hr_dims* dims, const hr_batch* batch, const void* qkv,
+                            const void* q_norm_w, const void* k_norm_w, void* q_out,
+                            const hr_kv* kv, hipStream_t stream);
+
+/* GQA attention over the cache (step A4): out [T, Hq*d] with
+ * o_h = softmax(q_h K_g^T / sqrt(d)) V_g, g = h / (Hq/Hkv), over the causal
+ * window or the used keys (dims->causal).  bf16 out, or e4m3(o / out_scale). */
+hr_status hr_attention(const hr_dims* dims, const hr_batch* batch, const void* q, const hr_kv* kv,
+                       void* out, hr_wtype out_type, float out_scale, hipStream_t stream);
+
+/* Final RMSNorm + audio-head projection of each sequence's last row
+ * (steps A9 final, A10): z = RMS(h[last_s]; final_norm_w) in fp32, then
+ * logits[s, k, v] = z . head_w[k*V + v] in fp32 (z is split into two bf16
+ * terms so the product keeps fp32 accuracy).  ws >= hr_head_workspace_bytes. */
+size_t hr_head_workspace_bytes(int32_t n_seq, int32_t D);
+hr_status hr_head_logits(const float* h, const hr_batch* batch, int32_t D, const void* final_norm_w,
+                         float eps, const void* head_w, int32_t n_codebooks, int32_t cb_vocab,
+                         float* logits_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* FP8 weight packing: scale[n] = max_k |w[n, k]| / 448 (1 if the row is zero),
+ * w8[n, k] = e4m3(w[n, k] / scale[n]) with fp32 division, nearest-even,
+ * saturating at 448.  w bf16 [N, K]. */
+hr_status hr_quantize_weight_e4m3(const void* w, int32_t N, int32_t K, uint8_t* w8, float* scale,
+                                  hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HR_OPS_H */

@@ -1,0 +1,180 @@
+"""The C ABI on the CPU: libhr.so loads, exports every function include/*.h
+declares, and refuses bad calls on the host before any launch.
+
+Every call here carries exactly one planted error, so validation returns before
+a kernel could run; the device pointers are fake (aligned, never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import codebook_decode_amd.hr as H
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000           # 16-byte aligned, never dereferenced
+MISALIGNED = 0x100008
+
+
+def declared_functions():
+    names = set()
+    for hdr in ("hr.h", "hr_ops.h"):
+        text = open(os.path.join(ROOT, "include", hdr)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(hr_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_function():
+    lib = H.lib()
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+    assert {"hr_prefill_layer", "hr_prefill_stack", "hr_codebook_step"} <= set(names)
+
+
+def dims(causal=True, **kw):
+    d = dict(hidden=2560, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn=9728, n_layers=2,
+             rope_theta=1e6, rms_eps=1e-6, causal=causal)
+    d.update(kw)
+    return H.make_dims(**d)
+
+
+def layer(**kw):
+    L = H.HrLayer()
+    L.wtype = H.HR_BF16
+    for f in ("in_norm_w", "post_norm_w", "q_norm_w", "k_norm_w", "w_qkv", "w_o", "w_gu", "w_down"):
+        setattr(L, f, FAKE)
+    for k, v in kw.items():
+        setattr(L, k, v)
+    return L
+
+
+def batch(lens, starts=None, slots=None, used=None, max_seqlen=None):
+    n = len(lens)
+    return H.Batch(np.concatenate([[0], np.cumsum(lens)]), starts or [0] * n, slots or list(range(n)), used,
+                   max_seqlen, device="cpu")
+
+
+def kv(capacity=2048, n_slots=4, **kw):
+    k = H.HrKv(FAKE, FAKE, capacity, n_slots)
+    for a, v in kw.items():
+        setattr(k, a, v)
+    return k
+
+
+def call_layer(d, L, b, kvv, ws_bytes=1 << 40, h=FAKE, ws=FAKE):
+    lib = H.lib()
+    return lib.hr_prefill_layer(ctypes.byref(d), ctypes.byref(L), ctypes.byref(b.c), h, ctypes.byref(kvv), ws,
+                                ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    ("head_dim", H.HR_EUNSUPPORTED), ("group", H.HR_EUNSUPPORTED), ("hidden", H.HR_EUNSUPPORTED),
+    ("null_weight", H.HR_EINVAL), ("misaligned_weight", H.HR_EALIGN), ("capacity", H.HR_ECAPACITY),
+    ("slot", H.HR_ECAPACITY), ("max_seqlen", H.HR_EBOUND), ("used_gt_len", H.HR_EBOUND),
+    ("used_missing", H.HR_EINVAL), ("cu_not_monotone", H.HR_EINVAL), ("workspace", H.HR_EWORKSPACE),
+    ("misaligned_h", H.HR_EALIGN), ("fp8_scale", H.HR_EINVAL), ("noncausal_start", H.HR_EUNSUPPORTED),
+])
+def test_prefill_layer_validation(case, status):
+    d, L, b, k = dims(), layer(), batch([13]), kv()
+    ws_bytes, h = 1 << 40, FAKE
+    if case == "head_dim":
+        d = dims(head_dim=96)
+    elif case == "group":
+        d = dims(n_kv_heads=4)                      # 8 query heads per kv head
+    elif case == "hidden":
+        d = dims(hidden=2500)
+    elif case == "null_weight":
+        L = layer(w_gu=None)
+    elif case == "misaligned_weight":
+        L = layer(w_o=MISALIGNED)
+    elif case == "capacity":
+        b = batch([13], starts=[2040])
+    elif case == "slot":
+        b = batch([13, 4], slots=[0, 4])
+    elif case == "max_seqlen":
+        b = batch([13, 20], max_seqlen=16)
+    elif case == "used_gt_len":
+        d, b = dims(causal=False), batch([13], used=[14])
+    elif case == "used_missing":
+        d = dims(causal=False)
+    elif case == "cu_not_monotone":
+        b = H.Batch(np.array([0, 5, 3]), [0, 0], [0, 1], device="cpu")
+    elif case == "workspace":
+        ws_bytes = H.hr_workspace_bytes(d, H.HR_BF16, 13) - 1
+    elif case == "misaligned_h":
+        h = MISALIGNED
+    elif case == "fp8_scale":
+        L = layer(wtype=H.HR_FP8_E4M3, ws_qkv=FAKE, ws_o=FAKE, ws_gu=FAKE, ws_down=FAKE,
+                  as_qkv=1.0, as_o=0.0, as_gu=1.0, as_down=1.0)
+    elif case == "noncausal_start":
+        d, b = dims(causal=False), batch([13], starts=[4], used=[13])
+    st = call_layer(d, L, b, k, ws_bytes, h)
+    assert st == status, (case, st, H.hr_last_error())
+    assert H.hr_last_error()
+
+
+def test_empty_batch_is_a_no_op():
+    assert call_layer(dims(), layer(), batch([0]), kv()) == H.HR_OK
+
+
+def test_workspace_bytes_grow_with_tokens():
+    d = dims()
+    a, b = H.hr_workspace_bytes(d, H.HR_BF16, 13), H.hr_workspace_bytes(d, H.HR_BF16, 512)
+    assert 0 < a < b
+    per_tok = (2560 * 2 + 6144 * 2 + 4096 * 2 * 2 + 9728 * 2)
+    assert b >= 512 * per_tok
+
+
+def test_stack_validation():
+    lib = H.lib()
+    d = dims()
+    Ls = (H.HrLayer * 2)(layer(), layer(wtype=H.HR_FP8_E4M3, ws_qkv=FAKE, ws_o=FAKE, ws_gu=FAKE, ws_down=FAKE,
+                                        as_qkv=1.0, as_o=1.0, as_gu=1.0, as_down=1.0))
+    Ks = (H.HrKv * 2)(kv(), kv())
+    b = batch([13])
+    st = lib.hr_prefill_stack(ctypes.byref(d), Ls, ctypes.byref(b.c), FAKE, FAKE, 151936, None, Ks, FAKE, None,
+                              8, 1026, FAKE, None, FAKE, 1 << 40, None)
+    assert st == H.HR_EINVAL and "wtype" in H.hr_last_error()
+    Ls2 = (H.HrLayer * 2)(layer(), layer())
+    st = lib.hr_prefill_stack(ctypes.byref(d), Ls2, ctypes.byref(b.c), FAKE, FAKE, 151936, None, Ks, FAKE, FAKE,
+                              8, 1026, FAKE, None, FAKE, 1 << 40, None)
+    assert st == H.HR_EINVAL and "head_w" in H.hr_last_error()
+    b0 = batch([3, 0, 2])
+    st = lib.hr_prefill_stack(ctypes.byref(d), Ls2, ctypes.byref(b0.c), FAKE, FAKE, 151936, None, Ks, FAKE, FAKE,
+                              8, 1026, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == H.HR_EINVAL and "empty" in H.hr_last_error()
+
+
+@pytest.mark.parametrize("B,K,V,bos,eoc,D,status", [
+    (4, 8, 1026, 1024, 1024, 2560, H.HR_EINVAL),     # bos == eoc
+    (4, 8, 1026, 1024, 1026, 2560, H.HR_EINVAL),     # eoc out of range
+    (4, 8, 1026, -1, 1025, 2560, H.HR_EINVAL),
+    (4, 8, 1026, 1024, 1025, 2561, H.HR_EINVAL),     # D not a multiple of 8
+    (4, 0, 1026, 1024, 1025, 2560, H.HR_EINVAL),
+    (4, 2000, 1026, 1024, 1025, 2560, H.HR_EUNSUPPORTED),
+])
+def test_codebook_validation(B, K, V, bos, eoc, D, status):
+    lib = H.lib()
+    st = lib.hr_codebook_step(B, K, V, bos, eoc, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, D, FAKE, None)
+    assert st == status, H.hr_last_error()
+
+
+def test_codebook_misaligned_embedding_refused():
+    lib = H.lib()
+    st = lib.hr_codebook_step(4, 8, 1026, 1024, 1025, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, MISALIGNED, 2560,
+                              FAKE, None)
+    assert st == H.HR_EALIGN
+
+
+def test_linear_validation():
+    lib = H.lib()
+    assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_BF16, 4, 16, 48, 0, FAKE, 0.0, None) == H.HR_EUNSUPPORTED
+    assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_BF16, 4, 24, 64, 0, FAKE, 0.0, None) == H.HR_EUNSUPPORTED
+    assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_FP8_E4M3, 4, 16, 128, 0, FAKE, 0.0, None) == H.HR_EINVAL
+    assert lib.hr_linear(FAKE, FAKE, FAKE, 1.0, H.HR_FP8_E4M3, 4, 32, 128, 2, FAKE, 0.0, None) == H.HR_EINVAL
+    assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_BF16, 4, 16, 64, 7, FAKE, 0.0, None) == H.HR_EINVAL

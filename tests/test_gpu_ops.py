@@ -1,0 +1,301 @@
+"""Each prefill step on the GPU against the float64 oracle, on seeded inputs,
+through the C ABI (include/hr_ops.h).  Sizes span several tiles with ragged
+tails; caches and outputs are NaN-poisoned to catch unwritten or stray writes."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import numerics as nx
+from oracle import prefill as op
+from oracle import fp8 as of
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def H():
+    import codebook_decode_amd.hr as H
+    H.lib()
+    return H
+
+
+def seeded_bf16(shape, key, std=1.0, mean=0.0):
+    return synth.normal_bf16(shape, (90,) + tuple(key), std, mean)
+
+
+# ----------------------------------------------------------------------------- A0 / A1 / A6 / A9
+@pytest.mark.parametrize("T,D", [(13, 2560), (300, 256), (1, 2560)])
+def test_embed_rmsnorm_and_rmsnorm(H, T, D):
+    import torch
+    from gpu_util import assert_bf16_close, dev, dev_bf16, f64_of_bf16, log
+    log(f"embed_rmsnorm T={T} D={D}")
+    vocab = 4096
+    E = seeded_bf16((vocab, D), (1, D), 0.02)
+    w = seeded_bf16((D,), (2, D), 0.1, 1.0)
+    ids = np.random.default_rng(T).integers(0, vocab, T).astype(np.int32)
+    h = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    x = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    H.hr_embed_rmsnorm(dev(ids), dev_bf16(E), vocab, None, T, D, dev_bf16(w), 1e-6, h, x)
+    torch.cuda.synchronize()
+    rows = nx.bf16_to_f64(E[ids])
+    np.testing.assert_array_equal(h.cpu().numpy().astype(np.float64), rows)     # exact widening
+    ref = op.rms_norm(rows, nx.bf16_to_f64(w), 1e-6)
+    assert_bf16_close(f64_of_bf16(x), ref, what="embed_rmsnorm x")
+    # plain RMSNorm of an fp32 residual with larger spread
+    hr = (np.random.default_rng(5).standard_normal((T, D)) * 7).astype(np.float32)
+    x2 = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    H.hr_rmsnorm(dev(hr), T, D, dev_bf16(w), 1e-6, x2)
+    torch.cuda.synchronize()
+    assert_bf16_close(f64_of_bf16(x2), op.rms_norm(hr.astype(np.float64), nx.bf16_to_f64(w), 1e-6),
+                      what="rmsnorm x")
+
+
+def test_rmsnorm_fp8_output(H):
+    import torch
+    from gpu_util import dev, dev_bf16
+    T, D, a = 40, 2560, 0.03
+    w = seeded_bf16((D,), (3,), 0.1, 1.0)
+    hr = (np.random.default_rng(6).standard_normal((T, D)) * 3).astype(np.float32)
+    x8 = torch.empty((T, D), dtype=torch.uint8, device="cuda")
+    H.hr_rmsnorm(dev(hr), T, D, dev_bf16(w), 1e-6, x8, H.HR_FP8_E4M3, a)
+    torch.cuda.synchronize()
+    got = nx.e4m3_decode(x8.cpu().numpy())
+    ref = op.rms_norm(hr.astype(np.float64), nx.bf16_to_f64(w), 1e-6) / a
+    want = nx.e4m3_round(ref)
+    # the fp32 and float64 quotients round to the same code except within
+    # rounding distance of a midpoint: allow one code step on a tiny fraction
+    diff = got != want
+    assert diff.mean() < 1e-3
+    step = np.abs(want) * 2.0 ** -3 + 2.0 ** -9
+    assert np.all(np.abs(got - want)[diff] <= step[diff])
+
+
+# ----------------------------------------------------------------------------- A2 / A5 / A7 / A8
+def _linear_case(H, M, N, K, epi, fp8=False, seed=0):
+    import torch
+    from gpu_util import dev, dev_bf16, dev_u8, f64_of_bf16, log
+    log(f"linear M={M} N={N} K={K} epi={epi} fp8={fp8}")
+    rng = np.random.default_rng(seed)
+    if fp8:
+        codes_x = rng.integers(0, 256, (M, K)).astype(np.uint8)
+        codes_w = rng.integers(0, 256, (N, K)).astype(np.uint8)
+        for c in (codes_x, codes_w):                        # no NaN codes
+            c[(c & 0x7F) == 0x7F] = 0x3C
+        xs, ws = 0.05, (rng.random(N) * 0.01 + 0.001).astype(np.float32)
+        xv = nx.e4m3_decode(codes_x) * xs
+        wv = nx.e4m3_decode(codes_w) * ws[:, None].astype(np.float64)
+        dx, dw, dws = dev_u8(codes_x), dev_u8(codes_w), dev(ws)
+        wtype = H.HR_FP8_E4M3
+    else:
+        xb = seeded_bf16((M, K), (10, M, K, seed), 1.0)
+        wb = seeded_bf16((N, K), (11, N, K, seed), 0.02)
+        xv, wv = nx.bf16_to_f64(xb), nx.bf16_to_f64(wb)
+        dx, dw, dws, xs = dev_bf16(xb), dev_bf16(wb), None, 1.0
+        wtype = H.HR_BF16
+    ref = xv @ wv.T
+    if epi == H.HR_EPI_BF16:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        H.hr_linear(dx, dw, dws, xs, wtype, M, N, K, epi, out)
+        torch.cuda.synchronize()
+        got = f64_of_bf16(out)
+        scale = np.sqrt(np.sum(np.abs(xv) ** 2, 1))[:, None] * np.sqrt(np.sum(wv ** 2, 1))[None, :]
+        err = np.abs(got - ref)
+        assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-5 * scale), float(err.max())
+    elif epi == H.HR_EPI_RESIDUAL:
+        h0 = np.random.default_rng(seed + 1).standard_normal((M, N)).astype(np.float32)
+        h = dev(h0)
+        H.hr_linear(dx, dw, dws, xs, wtype, M, N, K, epi, h)
+        torch.cuda.synchronize()
+        got = h.cpu().numpy().astype(np.float64)
+        want = h0 + ref
+        if fp8:
+            # the E4M3 MFMA sums its products with less than fp32 precision:
+            # bound the error by a fraction of sum_k |x_k w_k|
+            absdot = np.abs(xv) @ np.abs(wv).T
+            ratio = float(np.max(np.abs(got - want) / absdot))
+            log(f"fp8 residual max |err| / sum|x w| = {ratio:.3g}")
+            assert ratio <= 2.0 ** -11, ratio
+        else:
+            scale = np.sqrt(np.sum(xv ** 2, 1))[:, None] * np.sqrt(np.sum(wv ** 2, 1))[None, :]
+            assert np.all(np.abs(got - want) <= 1e-5 * scale + 2e-6 * np.abs(want)), float(np.abs(got - want).max())
+    else:
+        F = N // 2
+        out_scale = 0.02
+        if fp8:
+            out = torch.empty((M, F), dtype=torch.uint8, device="cuda")
+        else:
+            out = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+        H.hr_linear(dx, dw, dws, xs, wtype, M, N, K, epi, out, out_scale if fp8 else 0.0)
+        torch.cuda.synchronize()
+        act = op.silu(ref[:, :F]) * ref[:, F:]
+        if fp8:
+            got = nx.e4m3_decode(out.cpu().numpy()) * out_scale
+            want = nx.e4m3_round(act / out_scale) * out_scale
+            diff = got != want
+            assert diff.mean() < 2e-3
+            assert np.all(np.abs(got - want)[diff] <= (np.abs(want) * 2.0 ** -3 + 2.0 ** -9 * out_scale)[diff])
+        else:
+            got = f64_of_bf16(out)
+            gs = np.sqrt(np.sum(xv ** 2, 1))[:, None] * np.sqrt(np.sum(wv[:F] ** 2, 1) + np.sum(wv[F:] ** 2, 1))[None, :]
+            assert np.all(np.abs(got - act) <= 2.0 ** -8 * np.abs(act) + 1e-4 * gs), float(np.abs(got - act).max())
+
+
+@pytest.mark.parametrize("M", [1, 13, 40, 64])
+def test_linear_skinny_bf16(H, M):
+    _linear_case(H, M, 6144, 2560, H.HR_EPI_BF16, seed=M)
+    _linear_case(H, M, 2560, 4096, H.HR_EPI_RESIDUAL, seed=M)
+    _linear_case(H, M, 2 * 768, 256, H.HR_EPI_SWIGLU, seed=M)
+
+
+@pytest.mark.parametrize("M", [65, 200, 544])
+def test_linear_tiled_bf16(H, M):
+    _linear_case(H, M, 512, 2560, H.HR_EPI_BF16, seed=M)
+    _linear_case(H, M, 256, 768, H.HR_EPI_RESIDUAL, seed=M)
+    _linear_case(H, M, 2560, 1024, H.HR_EPI_RESIDUAL, seed=M + 1)
+    _linear_case(H, M, 2 * 768, 256, H.HR_EPI_SWIGLU, seed=M)
+
+
+@pytest.mark.parametrize("M", [13, 200])
+def test_linear_fp8(H, M):
+    _linear_case(H, M, 512, 1024, H.HR_EPI_BF16, fp8=True, seed=M)
+    _linear_case(H, M, 256, 512, H.HR_EPI_RESIDUAL, fp8=True, seed=M)
+    _linear_case(H, M, 2 * 256, 512, H.HR_EPI_SWIGLU, fp8=True, seed=M)
+
+
+def test_linear_rejects_bad_shapes(H):
+    import torch
+    x = torch.zeros(64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(H.HrError, match="HR_EUNSUPPORTED"):
+        H.hr_linear(x, x, None, 1.0, H.HR_BF16, 1, 16, 48, H.HR_EPI_BF16, x)
+
+
+# ----------------------------------------------------------------------------- A3
+def _dims(H, m, causal=True):
+    return H.make_dims(m.hidden, m.n_q_heads, m.n_kv_heads, m.head_dim, m.ffn, m.n_layers, m.rope_theta,
+                       m.rms_eps, causal)
+
+
+@pytest.mark.parametrize("model,lens,starts,slots,cap", [
+    (synth.QWEN3_4B, [13], [0], [0], 2048),
+    (synth.QWEN3_4B, [5, 1, 9], [0, 1500, 3], [2, 0, 1], 2048),
+    (synth.TINY, [6, 20], [0, 40], [1, 0], 64),
+])
+def test_qknorm_rope_kv(H, model, lens, starts, slots, cap):
+    import torch
+    from gpu_util import BF16_NAN, bits_of, dev_bf16, f64_of_bf16, log, poisoned_bf16
+    m = model
+    log(f"qknorm_rope_kv {m.name} lens={lens} starts={starts}")
+    T = sum(lens)
+    Hq, Hkv, d = m.n_q_heads, m.n_kv_heads, m.head_dim
+    qkv = seeded_bf16((T, m.qkv_rows), (20, T, d), 1.0)
+    qw = seeded_bf16((d,), (21, d), 0.1, 1.0)
+    kw = seeded_bf16((d,), (22, d), 0.1, 1.0)
+    n_slots = max(slots) + 1
+    kc, vc = poisoned_bf16((n_slots * cap, Hkv, d)), poisoned_bf16((n_slots * cap, Hkv, d))
+    q_out = poisoned_bf16((T, Hq, d))
+    b = H.Batch(np.concatenate([[0], np.cumsum(lens)]), starts, slots)
+    H.hr_qknorm_rope_kv(_dims(H, m), b, dev_bf16(qkv), dev_bf16(qw), dev_bf16(kw), q_out,
+                        H.make_kv(kc, vc, cap, n_slots))
+    torch.cuda.synchronize()
+    x = nx.bf16_to_f64(qkv)
+    cu = b.h_cu
+    kcb, vcb = bits_of(kc), bits_of(vc)
+    written = np.zeros(n_slots * cap, bool)
+    for s in range(len(lens)):
+        a, e = cu[s], cu[s + 1]
+        pos = starts[s] + np.arange(lens[s])
+        q = op.apply_rope(op.rms_norm(x[a:e, :Hq * d].reshape(-1, Hq, d), nx.bf16_to_f64(qw)), pos, m.rope_theta)
+        k = op.apply_rope(op.rms_norm(x[a:e, Hq * d:(Hq + Hkv) * d].reshape(-1, Hkv, d), nx.bf16_to_f64(kw)), pos,
+                          m.rope_theta)
+        rows = slots[s] * cap + pos
+        written[rows] = True
+        from gpu_util import assert_bf16_close
+        assert_bf16_close(f64_of_bf16(q_out[a:e]), q, abs_=1e-5, what="q")
+        assert_bf16_close(nx.bf16_to_f64(kcb[rows]), k, abs_=1e-5, what="k cache")
+        np.testing.assert_array_equal(vcb[rows], qkv[a:e, (Hq + Hkv) * d:].reshape(-1, Hkv, d))   # v copied
+    assert np.all(kcb[~written] == BF16_NAN) and np.all(vcb[~written] == BF16_NAN)
+
+
+# ----------------------------------------------------------------------------- A4
+@pytest.mark.parametrize("Hq,Hkv,d,lens,starts,causal,used", [
+    (32, 8, 128, [13], [0], True, None),
+    (32, 8, 128, [200, 7, 64], [0, 0, 30], True, None),
+    (4, 2, 64, [6, 70], [0, 10], True, None),
+    (8, 8, 64, [33], [0], True, None),
+    (32, 8, 128, [100], [0], False, [90]),
+])
+def test_attention(H, Hq, Hkv, d, lens, starts, causal, used):
+    import torch
+    from gpu_util import dev_bf16, f64_of_bf16, log
+    log(f"attention Hq={Hq} Hkv={Hkv} d={d} lens={lens} causal={causal}")
+    cap = max(s + l for s, l in zip(starts, lens)) + 3
+    n = len(lens)
+    T = sum(lens)
+    q = seeded_bf16((T, Hq, d), (30, T, Hq, d), 1.0)
+    kc = seeded_bf16((n * cap, Hkv, d), (31, cap, Hkv, d), 1.0)
+    vc = seeded_bf16((n * cap, Hkv, d), (32, cap, Hkv, d), 1.0)
+    b = H.Batch(np.concatenate([[0], np.cumsum(lens)]), starts, list(range(n)), used)
+    dims = H.make_dims(Hq * d, Hq, Hkv, d, 256, 1, 1e6, 1e-6, causal)
+    out = torch.full((T, Hq * d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    H.hr_attention(dims, b, dev_bf16(q), H.make_kv(dev_bf16(kc), dev_bf16(vc), cap, n), out)
+    torch.cuda.synchronize()
+    got = f64_of_bf16(out).reshape(T, Hq, d)
+    qv, kv_, vv = nx.bf16_to_f64(q), nx.bf16_to_f64(kc), nx.bf16_to_f64(vc)
+    cu = b.h_cu
+    grp = Hq // Hkv
+    for s in range(n):
+        a, e = cu[s], cu[s + 1]
+        pos = starts[s] + np.arange(lens[s])
+        if causal:
+            nk = starts[s] + lens[s]
+            vis = np.arange(nk)[None, :] <= pos[:, None]
+        else:
+            nk = used[s]
+            vis = np.ones((lens[s], nk), bool)
+        for hh in range(Hq):
+            g = hh // grp
+            ref = op.attention(qv[a:e, hh], kv_[s * cap:s * cap + nk, g], vv[s * cap:s * cap + nk, g], vis)
+            err = np.abs(got[a:e, hh] - ref)
+            assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 4e-3), (s, hh, float(err.max()))
+
+
+# ----------------------------------------------------------------------------- A9 final + A10
+@pytest.mark.parametrize("model,lens", [(synth.QWEN3_4B, [13]), (synth.QWEN3_4B, list(range(1, 34))),
+                                        (synth.TINY, [6, 3])])
+def test_head_logits(H, model, lens):
+    import torch
+    from gpu_util import dev, dev_bf16, log
+    m = model
+    log(f"head logits {m.name} n_seq={len(lens)}")
+    D, N = m.hidden, m.n_codebooks * m.cb_vocab
+    T = sum(lens)
+    h = (np.random.default_rng(len(lens)).standard_normal((T, D)) * 5).astype(np.float32)
+    wf = synth.final_norm(m)
+    wh = synth.head_weight(m)
+    b = H.Batch(np.concatenate([[0], np.cumsum(lens)]), [0] * len(lens), list(range(len(lens))))
+    out = torch.full((len(lens), N), float("nan"), device="cuda")
+    ws = torch.empty(H.hr_head_workspace_bytes(len(lens), D), dtype=torch.uint8, device="cuda")
+    H.hr_head_logits(dev(h), b, D, dev_bf16(wf), 1e-6, dev_bf16(wh), m.n_codebooks, m.cb_vocab, out, ws)
+    torch.cuda.synchronize()
+    z = op.rms_norm(h.astype(np.float64)[b.h_cu[1:] - 1], nx.bf16_to_f64(wf), 1e-6)
+    ref = op.head_logits(z, nx.bf16_to_f64(wh), m.n_codebooks, m.cb_vocab).reshape(len(lens), N)
+    got = out.cpu().numpy().astype(np.float64)
+    scale = np.sqrt(np.sum(z ** 2, 1))[:, None] * np.sqrt(np.sum(nx.bf16_to_f64(wh) ** 2, 1))[None, :]
+    assert np.all(np.abs(got - ref) <= 1e-5 * scale), float(np.abs(got - ref).max())
+
+
+# ----------------------------------------------------------------------------- FP8 weight packing
+def test_quantize_weight_bit_exact(H):
+    import torch
+    from gpu_util import dev_bf16
+    N, K = 300, 2560
+    wb = seeded_bf16((N, K), (40,), 0.02)
+    wb[7] = 0                                   # a zero row: scale 1, codes 0
+    w8 = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sc = torch.empty(N, dtype=torch.float32, device="cuda")
+    H.hr_quantize_weight_e4m3(dev_bf16(wb), N, K, w8, sc)
+    torch.cuda.synchronize()
+    s_ref, c_ref = of.weight_scales_e4m3(nx.bf16_to_f32(wb))
+    np.testing.assert_array_equal(sc.cpu().numpy(), s_ref)
+    got = w8.cpu().numpy()
+    np.testing.assert_array_equal(nx.e4m3_decode(got), nx.e4m3_decode(c_ref))
