@@ -131,9 +131,17 @@ def _linear_case(H, M, N, K, epi, fp8=False, seed=0):
         if fp8:
             got = nx.e4m3_decode(out.cpu().numpy()) * out_scale
             want = nx.e4m3_round(act / out_scale) * out_scale
-            diff = got != want
-            assert diff.mean() < 2e-3
-            assert np.all(np.abs(got - want)[diff] <= (np.abs(want) * 2.0 ** -3 + 2.0 ** -9 * out_scale)[diff])
+            # the pre-quantisation value carries the E4M3 MFMA's accumulation
+            # error (<= 2^-11 sum|x w| per product, measured on the residual
+            # case); propagate it through silu(g) u and add half an E4M3 step
+            absdot = np.abs(xv) @ np.abs(wv).T
+            g, u = ref[:, :F], ref[:, F:]
+            sig = 1 / (1 + np.exp(-g))
+            dsilu = sig * (1 + g * (1 - sig))
+            pre_err = 2.0 ** -11 * (np.abs(dsilu * u) * absdot[:, :F] + np.abs(op.silu(g)) * absdot[:, F:])
+            bound = pre_err + np.abs(act) * 2.0 ** -4 + 2.0 ** -10 * out_scale + 1e-12
+            assert np.all(np.abs(got - act) <= bound * 1.01), float(np.max(np.abs(got - act) / bound))
+            log(f"fp8 SwiGLU codes differing from the float64 quantisation: {float((got != want).mean()):.4f}")
         else:
             got = f64_of_bf16(out)
             gs = np.sqrt(np.sum(xv ** 2, 1))[:, None] * np.sqrt(np.sum(wv[:F] ** 2, 1) + np.sum(wv[F:] ** 2, 1))[None, :]
