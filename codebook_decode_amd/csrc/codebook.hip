@@ -6,9 +6,10 @@
 //
 // One workgroup per stream, 256 threads.  Each wavefront takes codebooks
 // w, w+4, ...: lanes scan strided ids and keep (max, lowest index), then a
-// butterfly reduction picks the row's first maximum.  One lane applies the
-// state update.  The workgroup then sums the K selected embedding rows with
-// 128-bit loads, in codebook order, in fp32, and rounds once to bf16.
+// butterfly reduction picks the row's first maximum.  Lane k applies codebook
+// k's delay / EOC update; one lane then updates the frame counter and done.
+// The workgroup then sums the K selected embedding rows with 128-bit loads,
+// in codebook order, in fp32, and rounds once to bf16.
 #include "common.h"
 #include "launch.h"
 
@@ -26,7 +27,7 @@ __global__ __launch_bounds__(256) void codebook_step_kernel(
     uint8_t* __restrict__ eoc_seen, uint8_t* __restrict__ done, int32_t* __restrict__ codes,
     int32_t* __restrict__ aligned, int max_frames, const uint16_t* __restrict__ cb_embed, int D,
     uint16_t* __restrict__ emb_out) {
-  extern __shared__ int32_t s_code[];  // [K] argmax ids, then chosen codes
+  extern __shared__ int32_t s_code[];  // [K] argmax ids, then chosen codes; [K, 2K) seen flags
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool is_done = done[b] != 0;
@@ -50,28 +51,29 @@ __global__ __launch_bounds__(256) void codebook_step_kernel(
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    if (is_done) {
-      for (int k = 0; k < K; ++k) s_code[k] = eoc;
-    } else {
-      const int t = frame[b];
-      bool all = true;
-      for (int k = 0; k < K; ++k) {
-        uint8_t seen = eoc_seen[size_t(b) * K + k];
-        int c = (t < k) ? bos : (seen ? eoc : s_code[k]);
-        if (c == eoc) seen = 1;
-        eoc_seen[size_t(b) * K + k] = seen;
-        all = all && seen;
-        s_code[k] = c;
-        if (aligned != nullptr && t >= k && t - k < max_frames)
-          aligned[(size_t(b) * max_frames + (t - k)) * K + k] = c;
-      }
-      frame[b] = t + 1;
-      done[b] = all ? 1 : 0;
+  // delay / EOC bookkeeping: one lane per codebook, then one lane for the stream
+  const int t = frame[b];
+  for (int k = threadIdx.x; k < K; k += blockDim.x) {
+    int c = eoc;
+    if (!is_done) {
+      const size_t ks = size_t(b) * K + k;
+      uint8_t seen = eoc_seen[ks];
+      c = (t < k) ? bos : (seen ? eoc : s_code[k]);
+      if (c == eoc && !seen) eoc_seen[ks] = 1;
+      if (aligned != nullptr && t >= k && t - k < max_frames)
+        aligned[(size_t(b) * max_frames + (t - k)) * K + k] = c;
+      s_code[K + k] = (seen || c == eoc) ? 1 : 0;
     }
-    for (int k = 0; k < K; ++k) codes[size_t(b) * K + k] = s_code[k];
+    s_code[k] = c;
+    codes[size_t(b) * K + k] = c;
   }
   __syncthreads();
+  if (threadIdx.x == 0 && !is_done) {
+    bool all = true;
+    for (int k = 0; k < K; ++k) all = all && s_code[K + k] != 0;
+    frame[b] = t + 1;
+    done[b] = all ? 1 : 0;
+  }
 
   // emb[b] = bf16( ((E[c0] + E[V+c1]) + ...) + E[(K-1)V + c_{K-1}] ), fp32 sum
   for (int d8 = threadIdx.x; d8 * 8 < D; d8 += blockDim.x) {
@@ -97,7 +99,7 @@ void launch_codebook_step(int B, int K, int V, int bos, int eoc, bool f32, const
                           int32_t* frame, uint8_t* eoc_seen, uint8_t* done, int32_t* codes,
                           int32_t* aligned, int max_frames, const void* cb_embed, int D,
                           void* emb_out, hipStream_t st) {
-  size_t shm = sizeof(int32_t) * size_t(K);
+  size_t shm = sizeof(int32_t) * size_t(2 * K);
   const uint16_t* E = static_cast<const uint16_t*>(cb_embed);
   uint16_t* out = static_cast<uint16_t*>(emb_out);
   if (f32)

@@ -27,6 +27,7 @@
 #include "common.h"
 #include "launch.h"
 
+
 namespace hr {
 
 __device__ __forceinline__ floatx4 mfma_bf16(u32x4 a, u32x4 b, floatx4 c) {
@@ -47,6 +48,31 @@ __device__ __forceinline__ floatx4 mma16(u32x4 a, u32x4 b, floatx4 c) {
     return mfma_fp8(a[2], a[3], b[2], b[3], c);
   } else {
     return mfma_bf16(a, b, c);
+  }
+}
+
+// 32 x 32 output block over one 64-byte K slab.  Each lane contributes two
+// 16-byte chunks of its row of A and of B.  bf16: two v_mfma_f32_32x32x16_bf16
+// (chunk 0 -> k-step 0, chunk 1 -> k-step 1); e4m3: one
+// v_mfma_scale_f32_32x32x64_f8f6f4 (format 0 = e4m3 on both sides, unit scale)
+// on the 32 contiguous bytes.  The 32x32 forms issue at twice the rate of the
+// 16x16 ones on gfx950 (measured 2.16 vs 1.24 PFLOP/s bf16).
+template <bool FP8>
+__device__ __forceinline__ floatx16 mma32(const u32x4 (&a)[2], const u32x4 (&b)[2], floatx16 c) {
+  if constexpr (FP8) {
+    typedef int intx8 __attribute__((ext_vector_type(8)));
+    intx8 av, bv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      av[i] = int(a[0][i]); av[4 + i] = int(a[1][i]);
+      bv[i] = int(b[0][i]); bv[4 + i] = int(b[1][i]);
+    }
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
+  } else {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]),
+                                                __builtin_bit_cast(bf16x8, b[0]), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[1]),
+                                                   __builtin_bit_cast(bf16x8, b[1]), c, 0, 0, 0);
   }
 }
 
@@ -214,116 +240,234 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
 }
 
 // ============================================================== tiled kernel
-constexpr int TBM = 128, TBN = 128, TBK = 128;   // TBK in bytes
-constexpr int TLD = TBK + 16;                    // padded LDS row (bytes)
+// BM x BN output tile per workgroup of WM x WN wavefronts; each wavefront owns a
+// (BM/WM) x (BN/WN) sub-tile of 16x16 MFMA blocks.  K advances in 64-byte slabs
+// (32 bf16 or 64 e4m3 values) copied global -> LDS directly
+// (global_load_lds_dwordx4: lane i of a wave writes 16 B at LDS base + 16 i)
+// through a ring of STAGES slabs.  A slab holds BM rows of A and BN rows of B,
+// 64 bytes each; 16-byte chunk c of row r sits at LDS chunk c ^ ((r >> 1) & 3),
+// so the 8 lanes of one ds_read_b128 phase (8 rows, one logical chunk) hit 8
+// distinct 16-byte bank groups (measured: zero bank conflicts).  The swizzle is
+// applied on the global side: each lane fetches the chunk its LDS slot must
+// hold.  One barrier per slab: after it every wave's copies of slab s have
+// landed and every wave is done with slab s-1, whose slot is refilled with slab
+// s+STAGES-1.
+constexpr int TBK = 64;   // slab depth in bytes
 
-template <int EPI, bool FP8>
-__global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint8_t* __restrict__ x,
-                                                         const uint8_t* __restrict__ w, int M, int N,
-                                                         int K_bytes, int tiles_m, EpiArgs e) {
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+
+__device__ __forceinline__ void lds_copy16(const uint8_t* g, uint8_t* lds_base) {
+  // generic -> local address-space cast (not an integer truncation)
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(g),
+                                   (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+}
+
+// wait until at most N of this thread's vector-memory loads are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// wait for every outstanding LDS access of this wave (lgkmcnt 0), nothing else
+__device__ __forceinline__ void wait_lds() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+}
+
+// Workgroup barrier without a memory fence: __syncthreads() would also wait for
+// every outstanding global load (vmcnt(0)) and drain the slab pipeline.  The
+// LDS-DMA copies this barrier publishes were already waited for by wait_vm;
+// the empty asm keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int LPS, int P>
+__device__ __forceinline__ void wait_pending(int pending) {
+  if constexpr (P == 0) {
+    wait_vm<0>();
+  } else {
+    if (pending >= P) wait_vm<P * LPS>();
+    else wait_pending<LPS, P - 1>(pending);
+  }
+}
+template <int LPS, int STAGES>
+__device__ __forceinline__ void wait_stages(int pending) {
+  // `pending` slabs issued after the one needed may stay in flight
+  static_assert(STAGES >= 3 && (STAGES - 2) * LPS < 64, "vmcnt range");
+  wait_pending<LPS, STAGES - 2>(pending);
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES>
+struct TileCfg {
+  static constexpr int kThreads = 64 * WM * WN;
+  static constexpr int kIM = BM / WM / 32;                  // 32-row blocks per wave
+  static constexpr int kJN = BN / WN / 32;                  // 32-col blocks per wave
+  static constexpr int kCopies = (BM + BN) / 16;            // 1 KB wave copies per slab
+  static constexpr int kLPS = kCopies / (WM * WN);          // copies per wave per slab
+  static constexpr int kSlabA = BM * TBK, kSlabB = BN * TBK;
+  static constexpr size_t kLds = size_t(STAGES) * (kSlabA + kSlabB);
+  static_assert(kCopies % (WM * WN) == 0, "copies must split evenly over the waves");
+  static_assert(BM % (32 * WM) == 0 && BN % (64 * WN) == 0, "tile shape");
+};
+
+template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
+    const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, int M, int N, int K_bytes,
+    int tiles_m, int n_tiles, EpiArgs e) {
+  using C = TileCfg<BM, BN, WM, WN, STAGES>;
+  constexpr int IM = C::kIM, JN = C::kJN, LPS = C::kLPS;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* sA = smem;                       // [2][TBM][TLD]
-  uint8_t* sB = smem + 2 * TBM * TLD;       // [2][TBN][TLD]
+  uint8_t* sA = smem;                                   // [STAGES][BM rows][64 B]
+  uint8_t* sB = smem + STAGES * C::kSlabA;              // [STAGES][BN rows][64 B]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
-  const int m0 = tm * TBM, n0 = tn * TBN;
-  const int g = lane >> 4, rc = lane & 15;
+  const int wm = wave / WN, wn = wave % WN;
+  // XCD-aware order: consecutive workgroup ids go round-robin over the 8 XCDs;
+  // give each XCD a contiguous run of tiles so the m-tiles that share a weight
+  // tile are served by one L2
+  int bid = blockIdx.x;
+  if (n_tiles % 8 == 0) bid = (bid % 8) * (n_tiles / 8) + bid / 8;
+  // grouped order: runs of GM m-tiles sweep n together, so the tiles running
+  // at once on one XCD share a few A and B panels in its L2
+  constexpr int GM = 4;
+  const int group = bid / (GM * (n_tiles / tiles_m));
+  const int first_m = group * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int in_group = bid - group * GM * (n_tiles / tiles_m);
+  const int tm = first_m + in_group % gm, tn = in_group / gm;
+  const int m0 = tm * BM, n0 = tn * BN;
 
-  // global rows this thread copies (4 x 16 B of A and of B per slab)
-  const uint8_t* ga[4];
-  const uint8_t* gb[4];
-  bool oka[4], okb[4];
-  int lrow[4], lcol[4];
+  // this wave's LPS 1-KB copies per slab: copy q covers 16 rows of A (q < BM/16)
+  // or of B; lane i fills LDS chunk 64 q' + i of that operand
+  const uint8_t* src[LPS];
+  int dst_off[LPS];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = tid + 256 * j;
-    lrow[j] = c >> 3;
-    lcol[j] = (c & 7) * 16;
-    const int ar = m0 + lrow[j];
-    oka[j] = ar < M;
-    ga[j] = x + size_t(oka[j] ? ar : 0) * K_bytes + lcol[j];
-    int br;
-    if constexpr (EPI == HR_EPI_SWIGLU) {
-      const int blk = lrow[j] >> 4, off = lrow[j] & 15;
-      const int a0 = (n0 >> 1) + (blk >> 1) * 16 + off;   // act column
-      br = (blk & 1) ? e.F + a0 : a0;
-      okb[j] = a0 < e.F;
+  for (int j = 0; j < LPS; ++j) {
+    const int q = wave + j * (WM * WN);
+    const bool is_a = q < BM / 16;
+    const int qq = is_a ? q : q - BM / 16;
+    const int chunk = qq * 64 + lane;
+    const int row = chunk >> 2, pc = chunk & 3;
+    const int lc = pc ^ swz(row);
+    dst_off[j] = is_a ? qq * 1024 : STAGES * C::kSlabA + qq * 1024;
+    if (is_a) {
+      src[j] = x + size_t(min(m0 + row, M - 1)) * K_bytes + lc * 16;
     } else {
-      br = n0 + lrow[j];
-      okb[j] = br < N;
+      int br;
+      if constexpr (EPI == HR_EPI_SWIGLU) {
+        // 32-row blocks of the B tile alternate gate / up rows of the same
+        // activation columns, so each wave holds a gate block and its up block
+        const int blk = row >> 5, off = row & 31;
+        const int a0 = min((n0 >> 1) + (blk >> 1) * 32 + off, e.F - 1);   // act column
+        br = (blk & 1) ? e.F + a0 : a0;
+      } else {
+        br = min(n0 + row, N - 1);
+      }
+      src[j] = w + size_t(br) * K_bytes + lc * 16;
     }
-    gb[j] = w + size_t(okb[j] ? br : 0) * K_bytes + lcol[j];
   }
   const int slabs_total = K_bytes / TBK;
   const int kz = blockIdx.z, ksplit = gridDim.z;
   const int sl0 = (slabs_total * kz) / ksplit, sl1 = (slabs_total * (kz + 1)) / ksplit;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int n_slabs = sl1 - sl0;
 
-  floatx4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int slab) {
+  auto issue = [&](int slab, int stage) {
     const size_t ko = size_t(slab) * TBK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ra[j] = oka[j] ? *reinterpret_cast<const u32x4*>(ga[j] + ko) : zero;
-      rb[j] = okb[j] ? *reinterpret_cast<const u32x4*>(gb[j] + ko) : zero;
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<u32x4*>(sA + (buf * TBM + lrow[j]) * TLD + lcol[j]) = ra[j];
-      *reinterpret_cast<u32x4*>(sB + (buf * TBN + lrow[j]) * TLD + lcol[j]) = rb[j];
+    for (int j = 0; j < LPS; ++j) {
+      const bool is_a = dst_off[j] < STAGES * C::kSlabA;
+      lds_copy16(src[j] + ko, smem + dst_off[j] + stage * (is_a ? C::kSlabA : C::kSlabB));
     }
   };
 
-  if (sl0 < sl1) {
-    gload(sl0);
-    sstore(0);
-  }
-  __syncthreads();
-  int buf = 0;
-  for (int sl = sl0; sl < sl1; ++sl) {
-    const bool more = sl + 1 < sl1;
-    if (more) gload(sl + 1);
-    const uint8_t* A = sA + (buf * TBM + wm * 64) * TLD;
-    const uint8_t* B = sB + (buf * TBN + wn * 64) * TLD;
+  floatx16 acc[IM][JN];
 #pragma unroll
-    for (int ks = 0; ks < TBK; ks += 64) {           // 64-byte halves of the slab
-      u32x4 fa[4], fb[4];
+  for (int i = 0; i < IM; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[i] = *reinterpret_cast<const u32x4*>(A + (i * 16 + rc) * TLD + ks + g * 16);
+    for (int j = 0; j < JN; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        fb[j] = *reinterpret_cast<const u32x4*>(B + (j * 16 + rc) * TLD + ks + g * 16);
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < n_slabs) issue(sl0 + s, s);
+
+  // a lane reads row (lane % 32) of each 32-row block, chunks c0 and c0 + step
+  // of the 64-byte slab: bf16 {h, 2 + h}, e4m3 {2h, 2h + 1}, h = lane / 32
+  const int h = lane >> 5, r32 = lane & 31;
+  const int c0 = FP8 ? 2 * h : h, cstep = FP8 ? 1 : 2;
+  const int a_row0 = wm * (BM / WM) + r32, b_row0 = wn * (BN / WN) + r32;
+  typedef u32x4 Frag[2];
+  auto read_frags = [&](int stage, Frag (&fa)[IM], Frag (&fb)[JN]) {
+    const uint8_t* A = sA + stage * C::kSlabA;
+    const uint8_t* B = sB + stage * C::kSlabB;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mma16<FP8>(fa[i], fb[j], acc[i][j]);
+    for (int j = 0; j < JN; ++j) {
+      const int r = b_row0 + j * 32;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        fb[j][c] = *reinterpret_cast<const u32x4*>(B + r * TBK + (((c0 + c * cstep) ^ swz(r)) << 4));
     }
-    if (more) sstore(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+#pragma unroll
+    for (int i = 0; i < IM; ++i) {
+      const int r = a_row0 + i * 32;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        fa[i][c] = *reinterpret_cast<const u32x4*>(A + r * TBK + (((c0 + c * cstep) ^ swz(r)) << 4));
+    }
+  };
+  auto mma_slab = [&](const Frag (&fa)[IM], const Frag (&fb)[JN]) {
+#pragma unroll
+    for (int i = 0; i < IM; ++i)
+#pragma unroll
+      for (int j = 0; j < JN; ++j) acc[i][j] = mma32<FP8>(fa[i], fb[j], acc[i][j]);
+  };
+  // Software pipeline: the fragments of slab it+1 are read from LDS while the
+  // MFMAs of slab it run, so LDS latency hides behind MFMA work.  Slab it+1
+  // must be resident one iteration early, hence STAGES-3 slabs stay in flight
+  // during the wait.  Slot (it-1) % STAGES is refilled after the barrier of
+  // iteration it: every wave's reads from it happened in iteration it-2.
+  Frag fa0[IM], fb0[JN], fa1[IM], fb1[JN];
+  if (n_slabs > 0) {
+    wait_stages<LPS, STAGES>(min(STAGES - 2, n_slabs - 1));
+    lds_barrier();
+    read_frags(0, fa0, fb0);
+  }
+  int it = 0;
+  auto step = [&](Frag (&fa)[IM], Frag (&fb)[JN], Frag (&fan)[IM], Frag (&fbn)[JN]) {
+    const bool more = it + 1 < n_slabs;
+    // this slab's fragments were read one MFMA burst ago: settle them here so
+    // no wait lands between the next slab's reads and these MFMAs
+    wait_lds();
+    if (more) {
+      wait_stages<LPS, STAGES>(min(STAGES - 3, n_slabs - 2 - it));
+      lds_barrier();
+      if (it + STAGES - 1 < n_slabs) issue(sl0 + it + STAGES - 1, (it + STAGES - 1) % STAGES);
+      read_frags((it + 1) % STAGES, fan, fbn);
+    }
+    mma_slab(fa, fb);
+    ++it;
+  };
+  // unrolled by two so the current / next fragment sets are fixed registers
+  while (it < n_slabs) {
+    step(fa0, fb0, fa1, fb1);
+    if (it < n_slabs) step(fa1, fb1, fa0, fb0);
   }
 
-  // epilogue: lane holds column rc of each block, rows 4g + r
+  // epilogue: 32x32 accumulator layout, lane holds column lane % 32 and rows
+  // 8 (r / 4) + 4 (lane / 32) + r % 4 of its block, r = 0..15
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < IM; ++i) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = m0 + wm * 64 + i * 16 + 4 * g + r;
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * (BM / WM) + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
       if (row >= M) continue;
       if constexpr (EPI == HR_EPI_SWIGLU) {
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int col = (n0 >> 1) + (wn * 2 + jj) * 16 + rc;
+        for (int jj = 0; jj < JN / 2; ++jj) {
+          const int col = (n0 >> 1) + (wn * (JN / 2) + jj) * 32 + r32;
           if (col < e.F) {
             const float gt = scaled<FP8>(e, acc[i][2 * jj][r], col);
             const float up = scaled<FP8>(e, acc[i][2 * jj + 1][r], e.F + col);
@@ -336,8 +480,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint8_t* __restri
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n0 + wn * 64 + j * 16 + rc;
+        for (int j = 0; j < JN; ++j) {
+          const int col = n0 + wn * (BN / WN) + j * 32 + r32;
           if (col >= N) continue;
           const float v = scaled<FP8>(e, acc[i][j][r], col);
           if constexpr (EPI == HR_EPI_BF16) {
@@ -369,21 +513,53 @@ static void skinny(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, con
   }
 }
 
-template <int EPI, bool FP8>
-static void tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
-                  int ksplit, hipStream_t st) {
-  const int tiles_m = (M + TBM - 1) / TBM;
+template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES>
+static void tiled_cfg(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
+                      int ksplit, hipStream_t st) {
+  using C = TileCfg<BM, BN, WM, WN, STAGES>;
+  const int tiles_m = (M + BM - 1) / BM;
   const int ncols = (EPI == HR_EPI_SWIGLU) ? 2 * e.F : N;
-  const int tiles_n = (ncols + TBN - 1) / TBN;
-  const size_t shm = size_t(2) * (TBM + TBN) * TLD;
-  dim3 grid(tiles_m * tiles_n, 1, ksplit);
-  static bool lds_raised = false;  // 72 KB of dynamic LDS: above the 64 KB default limit
-  if (!lds_raised) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled_kernel<EPI, FP8>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, int(shm));
+  const int tiles_n = (ncols + BN - 1) / BN;
+  const int n_tiles = tiles_m * tiles_n;
+  auto kern = gemm_tiled_kernel<EPI, FP8, BM, BN, WM, WN, STAGES>;
+  static bool lds_raised = false;  // above the 64 KB default dynamic-LDS limit
+  if (C::kLds > 65536 && !lds_raised) {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                        int(C::kLds));
     lds_raised = true;
   }
-  gemm_tiled_kernel<EPI, FP8><<<grid, 256, shm, st>>>(x, w, M, N, Kb, tiles_m, e);
+  dim3 grid(n_tiles, 1, ksplit);
+  kern<<<grid, C::kThreads, C::kLds, st>>>(x, w, M, N, Kb, tiles_m, n_tiles, e);
+}
+
+// Tile configuration of the large-M GEMM, chosen per projection from a sweep
+// on MI355X at M = 512 (tile / stages: QKV 256x128/4, O and down 128x128/4 with
+// split-K, gate/up 256x256/4); the split-K factor fills the grid for the
+// residual projections.
+template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES>
+static void tiled_fill(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
+                       hipStream_t st) {
+  const int ncols = (EPI == HR_EPI_SWIGLU) ? 2 * e.F : N;
+  const int tiles = ((M + BM - 1) / BM) * ((ncols + BN - 1) / BN);
+  int ks = 1;
+  if (EPI == HR_EPI_RESIDUAL && tiles < 256) ks = (256 + tiles - 1) / tiles;
+  const int max_ks = Kb / TBK / 4 > 0 ? Kb / TBK / 4 : 1;   // >= 4 slabs per split
+  if (ks > max_ks) ks = max_ks;
+  tiled_cfg<EPI, FP8, BM, BN, WM, WN, STAGES>(x, w, M, N, Kb, e, ks, st);
+}
+
+template <int EPI, bool FP8>
+static void tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
+                  hipStream_t st) {
+  if constexpr (EPI == HR_EPI_SWIGLU) {
+    if (M >= 384) return tiled_fill<EPI, FP8, 256, 256, 4, 2, 4>(x, w, M, N, Kb, e, st);
+    return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
+  } else if constexpr (EPI == HR_EPI_BF16) {
+    if (M >= 256) return tiled_fill<EPI, FP8, 256, 128, 4, 2, 4>(x, w, M, N, Kb, e, st);
+    return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
+  } else {
+    return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
+  }
 }
 
 void launch_linear(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8,
@@ -410,12 +586,8 @@ void launch_linear(const void* x, const void* w, const float* w_scale, float x_s
     if (fp8) skinny<EPI_, true>(xb, wb, M, N, Kb, e, blocks, ks, st);                         \
     else skinny<EPI_, false>(xb, wb, M, N, Kb, e, blocks, ks, st);                            \
   } else {                                                                                    \
-    const int tiles = ((M + TBM - 1) / TBM) * ((((EPI_ == HR_EPI_SWIGLU) ? N : N) + TBN - 1) / TBN); \
-    int ks = 1;                                                                               \
-    if (EPI_ == HR_EPI_RESIDUAL && tiles < 256) ks = (256 + tiles - 1) / tiles;               \
-    if (ks > Kb / TBK) ks = Kb / TBK;                                                         \
-    if (fp8) tiled<EPI_, true>(xb, wb, M, N, Kb, e, ks, st);                                  \
-    else tiled<EPI_, false>(xb, wb, M, N, Kb, e, ks, st);                                     \
+    if (fp8) tiled<EPI_, true>(xb, wb, M, N, Kb, e, st);                                      \
+    else tiled<EPI_, false>(xb, wb, M, N, Kb, e, st);                                         \
   }
   if (epi == HR_EPI_BF16) { HR_DISPATCH(HR_EPI_BF16) }
   else if (epi == HR_EPI_RESIDUAL) { HR_DISPATCH(HR_EPI_RESIDUAL) }

@@ -5,11 +5,13 @@
 // the same over both halves of head_dim, so pair (m, m + d/2) turns together)
 // and `run` (split the merged QKV rows, rotate, write the cache).
 //
-// One workgroup per token.  The d/2 angles p * theta^(-2m/d) are computed once
-// per token in float64 (sincos of the reduced double angle, rounded to fp32)
-// and kept in LDS.  A head row of d values is handled by d/2 lanes, lane m
-// owning the RoPE pair (m, m + d/2), so the rotation needs no lane exchange
-// and the head's sum of squares is a butterfly over d/2 lanes.
+// One workgroup per token.  The token's merged QKV row is staged in LDS with
+// 128-bit loads issued together (so the per-head loop makes no global round
+// trips); the d/2 angles p * theta^(-2m/d) are computed once per token in
+// float64 (sincos of the double angle, rounded to fp32) and kept in LDS.  A
+// head row of d values is handled by d/2 lanes, lane m owning the RoPE pair
+// (m, m + d/2), so the rotation needs no lane exchange and the head's sum of
+// squares is a butterfly over d/2 lanes.
 #include "common.h"
 #include "launch.h"
 
@@ -22,8 +24,15 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
     int causal, const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
     uint16_t* __restrict__ q_out, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
     int capacity) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t s_row[];   // the token's qkv row
   __shared__ float s_cos[64], s_sin[64];
   const int t = blockIdx.x;
+  const int n_rows = Hq + 2 * Hkv;
+  const int qkv_w = n_rows * d;
+  // stage the whole row with 128-bit loads (all issued before any use)
+  const u32x4* src = reinterpret_cast<const u32x4*>(qkv + size_t(t) * qkv_w);
+  for (int c = threadIdx.x; c < (qkv_w >> 3); c += blockDim.x)
+    reinterpret_cast<u32x4*>(s_row)[c] = src[c];
   const int s = find_seq(cu, n_seq, t);
   const int i = t - cu[s];
   const int p = start_pos[s] + i;
@@ -43,9 +52,6 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int per_wave = 64 / half;                 // head rows per wavefront pass
   const int sub = lane / half, m = lane % half;
-  const int n_rows = Hq + 2 * Hkv;
-  const int qkv_w = n_rows * d;
-  const uint16_t* src = qkv + size_t(t) * qkv_w;
   const float c = s_cos[m], sn = s_sin[m];
   const float wq0 = bf2f(qw[m]), wq1 = bf2f(qw[m + half]);
   const float wk0 = bf2f(kw[m]), wk1 = bf2f(kw[m + half]);
@@ -53,7 +59,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
     const int r = r0 + sub;
     const bool valid = r < n_rows;
     float x0 = 0.f, x1 = 0.f;
-    if (valid) { x0 = bf2f(src[r * d + m]); x1 = bf2f(src[r * d + m + half]); }
+    if (valid) { x0 = bf2f(s_row[r * d + m]); x1 = bf2f(s_row[r * d + m + half]); }
     float ss = group_sum(x0 * x0 + x1 * x1, half);
     if (!valid) continue;
     if (r < Hq + Hkv) {
@@ -68,8 +74,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
       if (is_q || write_kv) { dst[m] = uint16_t(f2bf(y0)); dst[m + half] = uint16_t(f2bf(y1)); }
     } else if (write_kv) {
       uint16_t* dst = vc + (row * Hkv + (r - Hq - Hkv)) * d;
-      dst[m] = src[r * d + m];
-      dst[m + half] = src[r * d + m + half];
+      dst[m] = s_row[r * d + m];
+      dst[m + half] = s_row[r * d + m + half];
     }
   }
 }
@@ -79,7 +85,8 @@ void launch_qknorm_rope_kv(const void* qkv, int T, int Hq, int Hkv, int d, float
                            const int32_t* used_keys, int n_seq, bool causal, const void* qw,
                            const void* kw, void* q_out, void* kc, void* vc, int capacity,
                            hipStream_t st) {
-  qknorm_rope_kv_kernel<<<T, 256, 0, st>>>(
+  const size_t shm = size_t(Hq + 2 * Hkv) * d * sizeof(uint16_t);
+  qknorm_rope_kv_kernel<<<T, 256, shm, st>>>(
       static_cast<const uint16_t*>(qkv), Hq, Hkv, d, theta, eps, cu, start_pos, cache_slot,
       used_keys, n_seq, causal ? 1 : 0, static_cast<const uint16_t*>(qw),
       static_cast<const uint16_t*>(kw), static_cast<uint16_t*>(q_out), static_cast<uint16_t*>(kc),
