@@ -8,25 +8,33 @@
 // o_h[i] = sum_j softmax_j(q_h[i] . K_g[j] / sqrt(d)) V_g[j], g = h / (Hq/Hkv),
 // j over [0, start_pos + i] (causal) or [0, used_keys) (non-causal).
 //
-// Workgroup = (query block, kv head g, sequence), 4 wavefronts.  The wavefronts
-// share every K/V tile: they are the GROUP query heads of g (times 4/GROUP
-// blocks of 16 positions).  Per 32-key tile:
-//   S^T = K . Q^T   (A = 16 keys x 32 d from LDS, B = the wave's 16 queries,
-//                    kept in registers) -> lane l holds query l%16 and keys
-//                    4(l/16)+r of each 16-key half;
-//   online softmax in base 2 per query (max over the 4 lanes of a column);
-//   O^T += V^T . P^T (A = V^T from an LDS copy stored transposed, B = the
-//                    lane's own 8 probabilities as bf16: the MFMA's k slots of
-//                    lane group q are keys {4q..4q+3, 16+4q..16+4q+3} for both
-//                    operands, so P needs no lane exchange).
-// Probabilities feed the MFMA in bf16; sums and rescaling stay fp32.
+// Workgroup = (query block, kv head g, sequence), 4 wavefronts sharing every
+// K/V tile: the GROUP query heads of g, times 4/GROUP blocks of 32 positions.
+// Per 64-key tile, with v_mfma_f32_32x32x16_bf16:
+//   S^T = K . Q^T  (A = 32 keys x 16 d from LDS, B = the wave's 32 queries,
+//                   kept in registers) -> lane l holds query l%32 and keys
+//                   8(r/4) + 4(l/32) + r%4, r = 0..15, of each 32-key block;
+//   online softmax in base 2 per query (the other half of a query's keys is in
+//                   lane l^32: one exchange);
+//   O^T += V^T . P^T: the MFMA's 8 k slots of lane half h are keys
+//                   {4h..4h+3, 8+4h..8+4h+3} of a 16-key step for BOTH operands,
+//                   which are exactly the lane's own probabilities r = 8kk..8kk+7,
+//                   so P goes from the score accumulator to the B operand with no
+//                   lane exchange; V is staged transposed in LDS.
+// The next tile's K and V are fetched into registers while the current tile is
+// computed.  Probabilities feed the MFMA in bf16; sums and rescaling stay fp32.
 #include "common.h"
 #include "launch.h"
 
 namespace hr {
 
-constexpr int KT = 32;        // keys per tile
-constexpr int VT_LD = 36;     // padded key stride of the transposed V tile (elements)
+constexpr int AKT = 64;        // keys per tile
+constexpr int VT_LD = 72;      // padded key stride of the transposed V tile (elements)
+
+__device__ __forceinline__ floatx16 mfma32_bf16(u32x4 a, u32x4 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
 
 template <int DH, int GROUP>
 __global__ __launch_bounds__(256) void attention_kernel(
@@ -34,12 +42,16 @@ __global__ __launch_bounds__(256) void attention_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ start_pos,
     const int32_t* __restrict__ cache_slot, const int32_t* __restrict__ used_keys, int Hq, int Hkv,
     int capacity, int causal, float scale_log2, void* __restrict__ out, int out_fp8, float out_inv) {
-  constexpr int QSUB = 4 / GROUP;             // 16-query sub-blocks per workgroup
-  constexpr int QPW = 16 * QSUB;
+  constexpr int QSUB = 4 / GROUP;             // 32-query sub-blocks per workgroup
+  constexpr int QPW = 32 * QSUB;
   constexpr int K_LD = DH + 8;                // padded row of the K tile (elements)
-  constexpr int NDS = DH / 32;                // 32-wide d steps of the score MFMA
-  constexpr int NDB = DH / 16;                // 16-wide d blocks of the output
-  __shared__ __attribute__((aligned(16))) uint16_t sK[KT * K_LD];
+  constexpr int NKS = DH / 16;                // 16-wide d steps of the score MFMA
+  constexpr int NDB = DH / 32;                // 32-wide d blocks of the output
+  constexpr int KCH = AKT * (DH / 8);         // 16-byte chunks of a K (or V) tile
+  constexpr int KPT = KCH / 256;              // K chunks per thread
+  constexpr int VPT = KCH / 2 / 256;          // V key-pair units per thread (2 loads each)
+  static_assert(KPT >= 1 && VPT >= 1, "tile / thread mapping");
+  __shared__ __attribute__((aligned(16))) uint16_t sK[AKT * K_LD];
   __shared__ __attribute__((aligned(16))) uint16_t sVt[DH * VT_LD];
 
   const int s = blockIdx.z, g = blockIdx.y;
@@ -52,139 +64,178 @@ __global__ __launch_bounds__(256) void attention_kernel(
   const size_t base = size_t(cache_slot[s]) * capacity;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hg = wave % GROUP, qsub = wave / GROUP;
-  const int h = g * GROUP + hg;
-  const int lg = lane >> 4, rc = lane & 15;
-  const int iq = i0 + qsub * 16 + rc;         // this lane's query (sequence-relative)
+  const int hh = g * GROUP + hg;
+  const int half = lane >> 5, r32 = lane & 31;
+  const int iq = i0 + qsub * 32 + r32;        // this lane's query (sequence-relative)
   const bool qok = iq < len;
   const int pos_q = start + iq;
   const int i_last = min(i0 + QPW, len) - 1;
   const int n_keys = causal ? start + i_last + 1 : used_keys[s];
 
-  // the wave's queries as the B operand: query rc, d = 32 ds + 8 lg + [0,8)
-  u32x4 qf[NDS];
+  // the wave's queries as the B operand: query r32, d = 16 ks + 8 half + [0,8)
+  u32x4 qf[NKS];
   {
-    const uint16_t* qrow = q + (size_t(tok0 + (qok ? iq : 0)) * Hq + h) * DH;
+    const uint16_t* qrow = q + (size_t(tok0 + (qok ? iq : 0)) * Hq + hh) * DH;
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qrow + ds * 32 + lg * 8);
-      qf[ds] = qok ? v : u32x4{0u, 0u, 0u, 0u};
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(qrow + ks * 16 + half * 8);
+      qf[ks] = qok ? v : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
-  floatx4 o[NDB];
+  // K/V tile fetch into registers: K chunk c -> (key c / (DH/8), d8 c % (DH/8));
+  // V unit u -> key pair (u % 32) of the tile, d8 = u / 32
+  u32x4 rk[KPT], rv[VPT][2];
+  auto fetch = [&](int k0) {
 #pragma unroll
-  for (int j = 0; j < NDB; ++j) o[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < KPT; ++j) {
+      const int c = tid + 256 * j;
+      const int key = c / (DH / 8), d8 = c % (DH / 8);
+      rk[j] = (k0 + key < n_keys)
+                  ? *reinterpret_cast<const u32x4*>(kc + ((base + k0 + key) * Hkv + g) * DH + d8 * 8)
+                  : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int u = tid + 256 * j;
+      const int key = 2 * (u % (AKT / 2)), d8 = u / (AKT / 2);
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        rv[j][e] = (k0 + key + e < n_keys)
+                       ? *reinterpret_cast<const u32x4*>(vc + ((base + k0 + key + e) * Hkv + g) * DH + d8 * 8)
+                       : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int c = tid + 256 * j;
+      const int key = c / (DH / 8), d8 = c % (DH / 8);
+      *reinterpret_cast<u32x4*>(sK + key * K_LD + d8 * 8) = rk[j];
+    }
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int u = tid + 256 * j;
+      const int key = 2 * (u % (AKT / 2)), d8 = u / (AKT / 2);
+      const u32x4 a = rv[j][0], b = rv[j][1];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        *reinterpret_cast<uint32_t*>(sVt + (d8 * 8 + 2 * w) * VT_LD + key) = (a[w] & 0xFFFFu) | (b[w] << 16);
+        *reinterpret_cast<uint32_t*>(sVt + (d8 * 8 + 2 * w + 1) * VT_LD + key) =
+            (a[w] >> 16) | (b[w] & 0xFFFF0000u);
+      }
+    }
+  };
+
+  floatx16 o[NDB];
+#pragma unroll
+  for (int j = 0; j < NDB; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[j][r] = 0.f;
   float m_run = -__builtin_inff();
   float l_part = 0.f;
 
-  const int n_tiles = (n_keys + KT - 1) / KT;
+  const int n_tiles = (n_keys + AKT - 1) / AKT;
+  if (n_tiles > 0) fetch(0);
   for (int kt = 0; kt < n_tiles; ++kt) {
-    const int k0 = kt * KT;
-    // K tile: 32 keys x DH -> sK[key][d]
-    for (int c = tid; c < KT * (DH / 8); c += 256) {
-      const int key = c / (DH / 8), d8 = c % (DH / 8);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (k0 + key < n_keys)
-        v = *reinterpret_cast<const u32x4*>(kc + ((base + k0 + key) * Hkv + g) * DH + d8 * 8);
-      *reinterpret_cast<u32x4*>(sK + key * K_LD + d8 * 8) = v;
-    }
-    // V tile, transposed: sVt[d][key] as bf16 pairs of adjacent keys
-    for (int c = tid; c < (KT / 2) * (DH / 8); c += 256) {
-      const int kp = c % (KT / 2), d8 = c / (KT / 2);
-      const int key = 2 * kp;
-      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-      if (k0 + key < n_keys)
-        a = *reinterpret_cast<const u32x4*>(vc + ((base + k0 + key) * Hkv + g) * DH + d8 * 8);
-      if (k0 + key + 1 < n_keys)
-        b = *reinterpret_cast<const u32x4*>(vc + ((base + k0 + key + 1) * Hkv + g) * DH + d8 * 8);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = (a[j] & 0xFFFFu) | (b[j] << 16);
-        const uint32_t hi = (a[j] >> 16) | (b[j] & 0xFFFF0000u);
-        *reinterpret_cast<uint32_t*>(sVt + (d8 * 8 + 2 * j) * VT_LD + key) = lo;
-        *reinterpret_cast<uint32_t*>(sVt + (d8 * 8 + 2 * j + 1) * VT_LD + key) = hi;
-      }
-    }
+    const int k0 = kt * AKT;
+    __syncthreads();                 // every wave is done with the previous tile
+    stage();
     __syncthreads();
+    if (kt + 1 < n_tiles) fetch(k0 + AKT);   // in flight during this tile's math
 
-    // scores for keys 16 hb + 4 lg + r, query rc
-    floatx4 sc[2];
+    // scores of 2 blocks of 32 keys
+    floatx16 sc[2];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      floatx4 a = {0.f, 0.f, 0.f, 0.f};
+    for (int blk = 0; blk < 2; ++blk) {
+      floatx16 a;
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        u32x4 kf = *reinterpret_cast<const u32x4*>(sK + (hb * 16 + rc) * K_LD + ds * 32 + lg * 8);
-        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf),
-                                                    __builtin_bit_cast(bf16x8, qf[ds]), a, 0, 0, 0);
+      for (int r = 0; r < 16; ++r) a[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(sK + (blk * 32 + r32) * K_LD + ks * 16 + half * 8);
+        a = mfma32_bf16(kf, qf[ks], a);
       }
-      sc[hb] = a;
+      sc[blk] = a;
+    }
+    // masks only where the tile crosses the causal diagonal of this wave's
+    // queries or the end of the keys (wave-uniform test)
+    const int wave_pos0 = start + i0 + qsub * 32;
+    const bool need_mask = (k0 + AKT > n_keys) || (causal && k0 + AKT - 1 > wave_pos0);
+    if (need_mask) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = k0 + blk * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool vis = j < n_keys && (!causal || j <= pos_q);
+          if (!vis) sc[blk][r] = -__builtin_inff();
+        }
     }
     float mt = -__builtin_inff();
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+    for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = k0 + hb * 16 + lg * 4 + r;
-        const bool vis = j < n_keys && (!causal || j <= pos_q);
-        const float v = vis ? sc[hb][r] * scale_log2 : -__builtin_inff();
-        sc[hb][r] = v;
-        mt = fmaxf(mt, v);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[blk][r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave)) * scale_log2;   // scale > 0: max commutes
     const float m_new = fmaxf(m_run, mt);
     const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    float p[2][4];
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     float psum = 0.f;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+    for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[hb][r] = exp2f(sc[hb][r] - m_use);
-        psum += p[hb][r];
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][r], scale_log2, -m_use));
+        sc[blk][r] = p;
+        psum += p;
       }
     l_part = l_part * alpha + psum;
     m_run = m_new;
 #pragma unroll
     for (int j = 0; j < NDB; ++j) o[j] *= alpha;
-    u32x4 pb;
-    pb[0] = pack_bf2(p[0][0], p[0][1]);
-    pb[1] = pack_bf2(p[0][2], p[0][3]);
-    pb[2] = pack_bf2(p[1][0], p[1][1]);
-    pb[3] = pack_bf2(p[1][2], p[1][3]);
+    // O^T += V^T P^T, 4 MFMAs (2 blocks x 2 k-steps of 16 keys) per d block
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const uint16_t* vrow = sVt + (db * 16 + rc) * VT_LD;
-      u32x2 x0 = *reinterpret_cast<const u32x2*>(vrow + 4 * lg);
-      u32x2 x1 = *reinterpret_cast<const u32x2*>(vrow + 16 + 4 * lg);
-      u32x4 va = {x0[0], x0[1], x1[0], x1[1]};
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va),
-                                                      __builtin_bit_cast(bf16x8, pb), o[db], 0, 0, 0);
-    }
-    __syncthreads();
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 pb;
+        pb[0] = pack_bf2_hw(sc[blk][8 * kk + 0], sc[blk][8 * kk + 1]);
+        pb[1] = pack_bf2_hw(sc[blk][8 * kk + 2], sc[blk][8 * kk + 3]);
+        pb[2] = pack_bf2_hw(sc[blk][8 * kk + 4], sc[blk][8 * kk + 5]);
+        pb[3] = pack_bf2_hw(sc[blk][8 * kk + 6], sc[blk][8 * kk + 7]);
+        const int kb = blk * 32 + kk * 16 + 4 * half;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const uint16_t* vrow = sVt + (db * 32 + r32) * VT_LD;
+          const u32x2 x0 = *reinterpret_cast<const u32x2*>(vrow + kb);
+          const u32x2 x1 = *reinterpret_cast<const u32x2*>(vrow + kb + 8);
+          const u32x4 va = {x0[0], x0[1], x1[0], x1[1]};
+          o[db] = mfma32_bf16(va, pb, o[db]);
+        }
+      }
   }
 
-  float l = l_part;
-  l += __shfl_xor(l, 16, kWave);
-  l += __shfl_xor(l, 32, kWave);
+  float l = l_part + __shfl_xor(l_part, 32, kWave);
   const float inv_l = l > 0.f ? 1.0f / l : 0.f;
   if (!qok) return;
-  const size_t orow = (size_t(tok0 + iq) * Hq + h) * DH;
+  const size_t orow = (size_t(tok0 + iq) * Hq + hh) * DH;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int d0 = db * 16 + 4 * lg;
-    float y0 = o[db][0] * inv_l, y1 = o[db][1] * inv_l, y2 = o[db][2] * inv_l, y3 = o[db][3] * inv_l;
-    if (out_fp8) {
-      uint32_t w = f2e4m3(y0 * out_inv) | (f2e4m3(y1 * out_inv) << 8) | (f2e4m3(y2 * out_inv) << 16) |
-                   (f2e4m3(y3 * out_inv) << 24);
-      *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(out) + orow + d0) = w;
-    } else {
-      u32x2 w = {pack_bf2(y0, y1), pack_bf2(y2, y3)};
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow + d0) = w;
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = db * 32 + 8 * rg + 4 * half;
+      const float y0 = o[db][4 * rg] * inv_l, y1 = o[db][4 * rg + 1] * inv_l;
+      const float y2 = o[db][4 * rg + 2] * inv_l, y3 = o[db][4 * rg + 3] * inv_l;
+      if (out_fp8) {
+        const uint32_t w = f2e4m3(y0 * out_inv) | (f2e4m3(y1 * out_inv) << 8) |
+                           (f2e4m3(y2 * out_inv) << 16) | (f2e4m3(y3 * out_inv) << 24);
+        *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(out) + orow + d0) = w;
+      } else {
+        const u32x2 w = {pack_bf2_hw(y0, y1), pack_bf2_hw(y2, y3)};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow + d0) = w;
+      }
     }
-  }
 }
 
 template <int DH, int GROUP>
@@ -192,7 +243,7 @@ static void launch_attn_t(const void* q, const void* kc, const void* vc, const i
                           const int32_t* sp, const int32_t* slot, const int32_t* used, int n_seq,
                           int max_len, int Hq, int Hkv, int cap, bool causal, void* out, bool fp8,
                           float out_inv, hipStream_t st) {
-  constexpr int QPW = 16 * (4 / GROUP);
+  constexpr int QPW = 32 * (4 / GROUP);
   dim3 grid((max_len + QPW - 1) / QPW, Hkv, n_seq);
   const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf(float(DH));
   attention_kernel<DH, GROUP><<<grid, 256, 0, st>>>(

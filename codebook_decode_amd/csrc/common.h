@@ -28,6 +28,15 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
 }
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
 
+// the same rounding (nearest even) with gfx950's packed convert, one
+// v_cvt_pk_bf16_f32 for two values; for hot loops on finite data
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf2_hw(float lo, float hi) {
+  float2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
 // ---------------------------------------------------------------- OCP E4M3
 // fp32 -> e4m3fn code: nearest even, magnitudes beyond 448 saturate to 448.
 // Normal E4M3 values are (1 + m/8) 2^(e-7), e in 1..15; subnormals m 2^-9.
