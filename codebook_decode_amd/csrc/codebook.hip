@@ -4,50 +4,91 @@
 // EOC, done once every codebook has emitted EOC) and the codebook-embedding sum
 // that feeds the next decode step.
 //
-// One workgroup per stream, 256 threads.  Each wavefront takes codebooks
-// w, w+4, ...: lanes scan strided ids and keep (max, lowest index), then a
-// butterfly reduction picks the row's first maximum.  Lane k applies codebook
-// k's delay / EOC update; one lane then updates the frame counter and done.
-// The workgroup then sums the K selected embedding rows with 128-bit loads,
-// in codebook order, in fp32, and rounds once to bf16.
+// One workgroup of 512 threads per stream.  The step is two dependent reads
+// (logits, then the chosen embedding rows), so the kernel is built to have
+// each read in flight at once rather than one load after another:
+//  * argmax: G lanes per codebook (G = 512 / K rounded down to a power of two,
+//    at most one wavefront); the row is read as aligned element pairs (one
+//    32-bit word of bf16, or 64 bits of fp32), up to kPairs pairs per lane
+//    issued before any compare; each lane keeps (max, lowest index) over its
+//    pairs in increasing index order and a butterfly over the G lanes picks
+//    the row's first maximum;
+//  * lane k applies codebook k's delay / EOC update; one lane updates the
+//    frame counter and done;
+//  * embedding sum: one 16-byte chunk of D per thread, the K rows loaded in
+//    batches of 8 before they are added, in codebook order, in fp32, rounded
+//    once to bf16.
 #include "common.h"
 #include "launch.h"
 
 namespace hr {
 
+constexpr int kCbThreads = 512;
+constexpr int kPairs = 12;      // pairs per lane per batch (V <= 1536 with 64 lanes in one batch)
+
+// value of pair unit u (elements 2u, 2u+1 of the logits tensor); the last
+// unit of an odd-sized tensor holds one element
 template <bool F32>
-__device__ __forceinline__ float logit_at(const void* p, size_t i) {
-  if (F32) return static_cast<const float*>(p)[i];
-  return bf2f(static_cast<const uint16_t*>(p)[i]);
+__device__ __forceinline__ void load_pair(const void* p, size_t u, size_t total, float& x0, float& x1) {
+  if (2 * u + 1 < total) {
+    if (F32) {
+      const float2_t v = reinterpret_cast<const float2_t*>(p)[u];
+      x0 = v[0];
+      x1 = v[1];
+    } else {
+      const uint32_t w = reinterpret_cast<const uint32_t*>(p)[u];
+      x0 = bf_lo(w);
+      x1 = bf_hi(w);
+    }
+  } else {
+    x0 = F32 ? static_cast<const float*>(p)[2 * u] : bf2f(static_cast<const uint16_t*>(p)[2 * u]);
+    x1 = -__builtin_inff();
+  }
 }
 
 template <bool F32>
-__global__ __launch_bounds__(256) void codebook_step_kernel(
-    int K, int V, int bos, int eoc, const void* __restrict__ logits, int32_t* __restrict__ frame,
-    uint8_t* __restrict__ eoc_seen, uint8_t* __restrict__ done, int32_t* __restrict__ codes,
-    int32_t* __restrict__ aligned, int max_frames, const uint16_t* __restrict__ cb_embed, int D,
-    uint16_t* __restrict__ emb_out) {
+__global__ __launch_bounds__(kCbThreads) void codebook_step_kernel(
+    int K, int V, int G, int bos, int eoc, const void* __restrict__ logits, size_t total,
+    int32_t* __restrict__ frame, uint8_t* __restrict__ eoc_seen, uint8_t* __restrict__ done,
+    int32_t* __restrict__ codes, int32_t* __restrict__ aligned, int max_frames,
+    const uint16_t* __restrict__ cb_embed, int D, uint16_t* __restrict__ emb_out) {
   extern __shared__ int32_t s_code[];  // [K] argmax ids, then chosen codes; [K, 2K) seen flags
   const int b = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool is_done = done[b] != 0;
 
   if (!is_done) {
-    for (int k = wave; k < K; k += 4) {
-      size_t row = (size_t(b) * K + k) * V;
+    const int groups = kCbThreads / G, grp = threadIdx.x / G, gl = threadIdx.x % G;
+    for (int k = grp; k < K; k += groups) {
+      const long long base = (static_cast<long long>(b) * K + k) * V;   // first element of the row
+      const size_t u0 = size_t(base) >> 1, u1 = (size_t(base) + V + 1) >> 1;
       float best = -__builtin_inff();
       int bi = 0x7FFFFFFF;
-      for (int v = lane; v < V; v += 64) {
-        float x = logit_at<F32>(logits, row + v);
-        if (x > best || bi == 0x7FFFFFFF) { best = x; bi = v; }
-      }
+      for (size_t u = u0 + gl; u < u1; u += size_t(G) * kPairs) {
+        float x[kPairs][2];
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        float ob = __shfl_xor(best, m, kWave);
-        int oi = __shfl_xor(bi, m, kWave);
+        for (int j = 0; j < kPairs; ++j) {
+          const size_t uu = u + size_t(j) * G;
+          if (uu < u1) load_pair<F32>(logits, uu, total, x[j][0], x[j][1]);
+        }
+#pragma unroll
+        for (int j = 0; j < kPairs; ++j) {
+          const size_t uu = u + size_t(j) * G;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const long long v = static_cast<long long>(2 * uu + h) - base;
+            if (uu < u1 && v >= 0 && v < V && (x[j][h] > best || bi == 0x7FFFFFFF)) {
+              best = x[j][h];
+              bi = int(v);
+            }
+          }
+        }
+      }
+      for (int m = G >> 1; m >= 1; m >>= 1) {
+        const float ob = __shfl_xor(best, m, kWave);
+        const int oi = __shfl_xor(bi, m, kWave);
         if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
       }
-      if (lane == 0) s_code[k] = bi;
+      if (gl == 0) s_code[k] = bi;
     }
   }
   __syncthreads();
@@ -78,15 +119,26 @@ __global__ __launch_bounds__(256) void codebook_step_kernel(
   // emb[b] = bf16( ((E[c0] + E[V+c1]) + ...) + E[(K-1)V + c_{K-1}] ), fp32 sum
   for (int d8 = threadIdx.x; d8 * 8 < D; d8 += blockDim.x) {
     float acc[8];
-    const u32x4* r0 = reinterpret_cast<const u32x4*>(cb_embed + size_t(s_code[0]) * D) + d8;
-    u32x4 w = *r0;
+    for (int k0 = 0; k0 < K; k0 += 8) {
+      u32x4 r[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) { acc[2 * j] = bf_lo(w[j]); acc[2 * j + 1] = bf_hi(w[j]); }
-    for (int k = 1; k < K; ++k) {
-      const u32x4* rk = reinterpret_cast<const u32x4*>(cb_embed + (size_t(k) * V + s_code[k]) * D) + d8;
-      u32x4 x = *rk;
+      for (int j = 0; j < 8; ++j)
+        if (k0 + j < K)
+          r[j] = reinterpret_cast<const u32x4*>(cb_embed + (size_t(k0 + j) * V + s_code[k0 + j]) * D)[d8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { acc[2 * j] += bf_lo(x[j]); acc[2 * j + 1] += bf_hi(x[j]); }
+      for (int j = 0; j < 8; ++j) {
+        if (k0 + j >= K) break;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (k0 + j == 0) {
+            acc[2 * q] = bf_lo(r[j][q]);
+            acc[2 * q + 1] = bf_hi(r[j][q]);
+          } else {
+            acc[2 * q] += bf_lo(r[j][q]);
+            acc[2 * q + 1] += bf_hi(r[j][q]);
+          }
+        }
+      }
     }
     u32x4 o;
 #pragma unroll
@@ -100,14 +152,17 @@ void launch_codebook_step(int B, int K, int V, int bos, int eoc, bool f32, const
                           int32_t* aligned, int max_frames, const void* cb_embed, int D,
                           void* emb_out, hipStream_t st) {
   size_t shm = sizeof(int32_t) * size_t(2 * K);
+  int G = 64;
+  while (G > 1 && G * K > kCbThreads) G >>= 1;
+  const size_t total = size_t(B) * K * V;
   const uint16_t* E = static_cast<const uint16_t*>(cb_embed);
   uint16_t* out = static_cast<uint16_t*>(emb_out);
   if (f32)
-    codebook_step_kernel<true><<<B, 256, shm, st>>>(K, V, bos, eoc, logits, frame, eoc_seen, done,
-                                                    codes, aligned, max_frames, E, D, out);
+    codebook_step_kernel<true><<<B, kCbThreads, shm, st>>>(K, V, G, bos, eoc, logits, total, frame, eoc_seen,
+                                                           done, codes, aligned, max_frames, E, D, out);
   else
-    codebook_step_kernel<false><<<B, 256, shm, st>>>(K, V, bos, eoc, logits, frame, eoc_seen, done,
-                                                     codes, aligned, max_frames, E, D, out);
+    codebook_step_kernel<false><<<B, kCbThreads, shm, st>>>(K, V, G, bos, eoc, logits, total, frame, eoc_seen,
+                                                            done, codes, aligned, max_frames, E, D, out);
 }
 
 }  // namespace hr

@@ -78,6 +78,20 @@ __device__ __forceinline__ floatx16 mma32(const u32x4 (&a)[2], const u32x4 (&b)[
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+// Small-M (<= 64 rows) fusion of QKV + q/k RMSNorm + RoPE + KV write: the
+// product is kept in fp32 and the last workgroup of each head applies the
+// per-head norm and rotation and writes q or the cache rows of that head (one
+// launch instead of two).
+struct RopeTail {
+  float* qkv32;       // [M, (Hq+2Hkv) d] fp32 product
+  const uint16_t* qw;
+  const uint16_t* kw;
+  float theta, eps;
+  const int32_t *cu, *start_pos, *cache_slot, *used_keys;
+  int n_seq, causal, Hq, Hkv, d, capacity;
+  uint16_t *q_out, *kc, *vc;
+};
+
 struct EpiArgs {
   int epi;            // hr_epilogue
   void* out;          // bf16 [M,N] | fp32 [M,N] (+=) | act [M,F] | fp32 logits
@@ -88,7 +102,103 @@ struct EpiArgs {
   int out_fp8;        // SwiGLU output in e4m3
   int F;              // SwiGLU width (gate rows [0,F), up rows [F,2F))
   int hilo_rows;      // head: rows [0,h) hold hi, [h,2h) lo terms; out = hi + lo
+  int* counter;       // QKV tail: arrival counters (zero on entry, reset on exit)
+  RopeTail rope;
 };
+
+// Cross-workgroup hand-off without cache-wide fences.  On gfx950 the L2 is
+// private to each XCD, so a device-scope fence costs a whole-L2 writeback
+// (release) and invalidate (acquire) -- per workgroup, tens of microseconds
+// for a grid, and the invalidate makes every other resident workgroup on the
+// XCD re-fetch its operands.  Instead every value handed to another
+// workgroup is written and read with device-scope atomic stores and loads
+// (write-through / coherent accesses), fp32 atomic adds are coherent by
+// construction, and ordering is the completion wait of each wavefront's
+// stores (vmcnt 0) before the workgroup barrier that precedes the counter
+// increment: the last arrival sees every other workgroup's values.
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// true in exactly one workgroup per `total` arrivals on *ctr (all threads)
+__device__ __forceinline__ bool last_arrival(int* ctr, int total) {
+  __shared__ int s_last;
+  // gfx9 s_waitcnt: vmcnt 0 (bits 3:0 and 15:14), expcnt 7, lgkmcnt 15
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = (__hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == total - 1) ? 1 : 0;
+  __syncthreads();
+  return s_last != 0;
+}
+
+// The tail below runs in one workgroup after every other one has finished, so
+// it is pure latency: every value it needs is requested before the first one
+// is used (no load waits on another load).
+
+// q/k RMSNorm + rotate-half RoPE + cache write of head row `r` for the M rows.
+// Work items (token, j) with j < d/2 own the RoPE pair (j, j + d/2); a token's
+// d/2 items are consecutive lanes, so the head norm is a d/2-lane butterfly.
+// Each thread takes up to kRopeItems items with all their loads in flight.
+constexpr int kRopeItems = 8;
+
+__device__ void rope_head_tail(int r, int M, const RopeTail& t, int nthreads) {
+  const int d = t.d, half = d >> 1;
+  const int j = threadIdx.x % half;                   // nthreads is a multiple of d/2
+  const int n_rows = t.Hq + 2 * t.Hkv;
+  const bool is_q = r < t.Hq, is_k = !is_q && r < t.Hq + t.Hkv;
+  const int n_items = M * half;
+  const double inv_freq = exp2(-double(2 * j) / double(d) * log2(double(t.theta)));
+  const float w0 = is_q ? bf2f(t.qw[j]) : (is_k ? bf2f(t.kw[j]) : 1.f);
+  const float w1 = is_q ? bf2f(t.qw[j + half]) : (is_k ? bf2f(t.kw[j + half]) : 1.f);
+  for (int base = 0; base < n_items; base += nthreads * kRopeItems) {
+    float x0[kRopeItems], x1[kRopeItems];
+    int pos[kRopeItems], wkv[kRopeItems];
+    size_t crow[kRopeItems];
+#pragma unroll
+    for (int it = 0; it < kRopeItems; ++it) {
+      const int item = base + it * nthreads + threadIdx.x;
+      const int m = item / half;
+      const bool ok = item < n_items;
+      const float* src = t.qkv32 + size_t(ok ? m : 0) * n_rows * d + size_t(r) * d;
+      x0[it] = ok ? coherent_load(src + j) : 0.f;
+      x1[it] = ok ? coherent_load(src + j + half) : 0.f;
+      const int s = ok ? find_seq(t.cu, t.n_seq, m) : 0;
+      const int i = m - t.cu[s];
+      pos[it] = t.start_pos[s] + i;
+      wkv[it] = ok && (t.causal || i < t.used_keys[s]);
+      crow[it] = size_t(t.cache_slot[s]) * t.capacity + pos[it];
+    }
+#pragma unroll
+    for (int it = 0; it < kRopeItems; ++it) {
+      const int item = base + it * nthreads + threadIdx.x;
+      const float ss = group_sum(x0[it] * x0[it] + x1[it] * x1[it], half);
+      if (item >= n_items) continue;
+      const int m = item / half;
+      if (is_q || is_k) {
+        const float inv = 1.0f / __builtin_sqrtf(ss / float(d) + t.eps);
+        const float a = x0[it] * inv * w0, b = x1[it] * inv * w1;
+        // angle p * theta^(-2j/d) in float64, reduced to [-pi, pi] before the
+        // fp32 sincos
+        const double phi = double(pos[it]) * inv_freq;
+        const double k2 = __builtin_rint(phi * 0.15915494309189535);
+        const float red = float(__builtin_fma(-k2, 6.283185307179586, phi));
+        float sn, cs;
+        sincosf(red, &sn, &cs);
+        const float y0 = a * cs - b * sn, y1 = b * cs + a * sn;
+        uint16_t* dst = is_q ? t.q_out + (size_t(m) * t.Hq + r) * d : t.kc + (crow[it] * t.Hkv + (r - t.Hq)) * d;
+        if (is_q || wkv[it]) { dst[j] = uint16_t(f2bf(y0)); dst[j + half] = uint16_t(f2bf(y1)); }
+      } else if (wkv[it]) {
+        uint16_t* dst = t.vc + (crow[it] * t.Hkv + (r - t.Hq - t.Hkv)) * d;
+        dst[j] = uint16_t(f2bf(x0[it]));
+        dst[j + half] = uint16_t(f2bf(x1[it]));
+      }
+    }
+  }
+}
 
 // value of one product element after the dtype scale
 template <bool FP8>
@@ -224,6 +334,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
           if (ksplit == 1) *o += scaled<FP8>(e, v[0], col);
           else unsafeAtomicAdd(o, scaled<FP8>(e, v[0], col));
         }
+      } else if constexpr (EPI == HR_EPI_QKV_ROPE) {
+        if (row < M) coherent_store(e.rope.qkv32 + size_t(row) * e.ldo + col, scaled<FP8>(e, v[0], col));
       } else {  // HR_EPI_HEAD: fp32 logits = hi-row product + lo-row product
         if (row < e.hilo_rows) {
           const int r2 = row + e.hilo_rows;   // the lo term of the same sequence
@@ -235,6 +347,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
           static_cast<float*>(e.out)[size_t(row) * e.ldo + col] = v[0] + lo;
         }
       }
+    }
+  }
+  if constexpr (EPI == HR_EPI_QKV_ROPE) {
+    const int blocks_per_head = e.rope.d / 16;
+    const int head = cb / blocks_per_head;
+    if (last_arrival(e.counter + head, blocks_per_head * gridDim.y)) {
+      rope_head_tail(head, M, e.rope, WAVES * 64);
+      if (threadIdx.x == 0) __hip_atomic_store(e.counter + head, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -310,7 +430,7 @@ struct TileCfg {
   static constexpr int kSlabA = BM * TBK, kSlabB = BN * TBK;
   static constexpr size_t kLds = size_t(STAGES) * (kSlabA + kSlabB);
   static_assert(kCopies % (WM * WN) == 0, "copies must split evenly over the waves");
-  static_assert(BM % (32 * WM) == 0 && BN % (64 * WN) == 0, "tile shape");
+  static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "tile shape");
 };
 
 template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES>
@@ -319,6 +439,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
     int tiles_m, int n_tiles, EpiArgs e) {
   using C = TileCfg<BM, BN, WM, WN, STAGES>;
   constexpr int IM = C::kIM, JN = C::kJN, LPS = C::kLPS;
+  static_assert(EPI != HR_EPI_SWIGLU || JN % 2 == 0, "SwiGLU waves hold gate/up block pairs");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* sA = smem;                                   // [STAGES][BM rows][64 B]
   uint8_t* sB = smem + STAGES * C::kSlabA;              // [STAGES][BN rows][64 B]
@@ -532,33 +653,42 @@ static void tiled_cfg(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, 
   kern<<<grid, C::kThreads, C::kLds, st>>>(x, w, M, N, Kb, tiles_m, n_tiles, e);
 }
 
-// Tile configuration of the large-M GEMM, chosen per projection from a sweep
-// on MI355X at M = 512 (tile / stages: QKV 256x128/4, O and down 128x128/4 with
-// split-K, gate/up 256x256/4); the split-K factor fills the grid for the
-// residual projections.
+// Launch with a split-K factor that fills the 256 CUs for the residual
+// projections (fp32 atomics into h), or the given one.
 template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES>
 static void tiled_fill(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
-                       hipStream_t st) {
+                       hipStream_t st, int ks_force = 0) {
   const int ncols = (EPI == HR_EPI_SWIGLU) ? 2 * e.F : N;
   const int tiles = ((M + BM - 1) / BM) * ((ncols + BN - 1) / BN);
   int ks = 1;
   if (EPI == HR_EPI_RESIDUAL && tiles < 256) ks = (256 + tiles - 1) / tiles;
+  if (EPI == HR_EPI_RESIDUAL && ks_force > 0) ks = ks_force;
   const int max_ks = Kb / TBK / 4 > 0 ? Kb / TBK / 4 : 1;   // >= 4 slabs per split
   if (ks > max_ks) ks = max_ks;
   tiled_cfg<EPI, FP8, BM, BN, WM, WN, STAGES>(x, w, M, N, Kb, e, ks, st);
 }
 
+// Tile configuration of the large-M GEMM, chosen per projection from a sweep
+// of 13 tile shapes and split-K factors on MI355X at M = 512 (bf16, the 4B
+// layer): QKV 64x128 (41.6 us against 48.3 for 256x128), O 128x64 split 3,
+// gate/up 256x256, down 256x128 split 6; the earlier shapes are kept above
+// M = 1024, where they were chosen.  Split-K fills the grid for the residual
+// projections.
 template <int EPI, bool FP8>
 static void tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
                   hipStream_t st) {
+  const int K_el = FP8 ? Kb : Kb / 2;
   if constexpr (EPI == HR_EPI_SWIGLU) {
     if (M >= 384) return tiled_fill<EPI, FP8, 256, 256, 4, 2, 4>(x, w, M, N, Kb, e, st);
     return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
   } else if constexpr (EPI == HR_EPI_BF16) {
-    if (M >= 256) return tiled_fill<EPI, FP8, 256, 128, 4, 2, 4>(x, w, M, N, Kb, e, st);
+    if (M > 1024) return tiled_fill<EPI, FP8, 256, 128, 4, 2, 4>(x, w, M, N, Kb, e, st);
+    if (M >= 256) return tiled_fill<EPI, FP8, 64, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
     return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
   } else {
-    return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
+    if (M > 1024 || M < 256) return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
+    if (K_el >= 8192) return tiled_fill<EPI, FP8, 256, 128, 4, 2, 4>(x, w, M, N, Kb, e, st, 6);
+    return tiled_fill<EPI, FP8, 128, 64, 2, 2, 4>(x, w, M, N, Kb, e, st, 3);
   }
 }
 
@@ -593,6 +723,28 @@ void launch_linear(const void* x, const void* w, const float* w_scale, float x_s
   else if (epi == HR_EPI_RESIDUAL) { HR_DISPATCH(HR_EPI_RESIDUAL) }
   else { HR_DISPATCH(HR_EPI_SWIGLU) }
 #undef HR_DISPATCH
+}
+
+// Small-M (<= 64) QKV + q/k norm + RoPE + KV write: x . W_qkv^T -> fp32
+// qkv32 -> per-head tails.
+void launch_qkv_rope(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8, int M,
+                     int N, int K, float* qkv32, int* counters, const QkvRopeParams& p, hipStream_t st) {
+  EpiArgs e{};
+  e.epi = HR_EPI_QKV_ROPE;
+  e.x_scale = x_scale;
+  e.w_scale = w_scale;
+  e.ldo = N;
+  e.counter = counters;
+  e.rope = RopeTail{qkv32, static_cast<const uint16_t*>(p.qw), static_cast<const uint16_t*>(p.kw), p.theta,
+                    p.eps, p.cu, p.start_pos, p.cache_slot, p.used_keys, p.n_seq, p.causal ? 1 : 0, p.Hq,
+                    p.Hkv, p.d, p.capacity, static_cast<uint16_t*>(p.q_out), static_cast<uint16_t*>(p.kc),
+                    static_cast<uint16_t*>(p.vc)};
+  const int Kb = fp8 ? K : 2 * K;
+  const int blocks = N / 16;
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  const uint8_t* wb = static_cast<const uint8_t*>(w);
+  if (fp8) skinny<HR_EPI_QKV_ROPE, true>(xb, wb, M, N, Kb, e, blocks, 1, st);
+  else skinny<HR_EPI_QKV_ROPE, false>(xb, wb, M, N, Kb, e, blocks, 1, st);
 }
 
 // Head: zsplit bf16 [2n, D] (hi rows then lo rows), W bf16 [N, D] -> fp32 [n, N]

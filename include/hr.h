@@ -171,7 +171,8 @@ hr_status hr_prefill_stack(const hr_dims* dims, const hr_layer* layers, const hr
  * otherwise the lowest index of its row maximum; then frame = t+1 and
  * done = all codebooks have emitted EOC.
  * HR_EINVAL if bos_id or eoc_id is outside [0, V) or bos_id == eoc_id, or
- * D is not a multiple of 8. */
+ * D is not a multiple of 8; HR_EALIGN if logits, cb_embed or emb_out is not
+ * 16-byte aligned. */
 hr_status hr_codebook_step(int32_t B, int32_t K, int32_t V, int32_t bos_id, int32_t eoc_id,
                            int32_t logits_is_fp32, const void* logits, int32_t* frame,
                            uint8_t* eoc_seen, uint8_t* done, int32_t* codes, int32_t* aligned,

@@ -178,3 +178,10 @@ def test_linear_validation():
     assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_FP8_E4M3, 4, 16, 128, 0, FAKE, 0.0, None) == H.HR_EINVAL
     assert lib.hr_linear(FAKE, FAKE, FAKE, 1.0, H.HR_FP8_E4M3, 4, 32, 128, 2, FAKE, 0.0, None) == H.HR_EINVAL
     assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_BF16, 4, 16, 64, 7, FAKE, 0.0, None) == H.HR_EINVAL
+
+
+def test_codebook_misaligned_logits_refused():
+    lib = H.lib()
+    st = lib.hr_codebook_step(4, 8, 1026, 1024, 1025, 0, MISALIGNED, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, 2560,
+                              FAKE, None)
+    assert st == H.HR_EALIGN

@@ -110,6 +110,53 @@ def test_workload_fp32_logits_bit_exact(H):
     _workload_vs_oracle(H, f32=True)
 
 
+ODD_CASES = [
+    # B, K, V, fp32 logits, tie-heavy: odd V puts rows at odd element offsets
+    # (pairs straddle rows); K = 33 gives 8 lanes per codebook, V = 2000 takes
+    # two load batches; integer-valued logits make most rows tie many times
+    (3, 5, 77, False, False),
+    (3, 5, 77, True, False),
+    (2, 33, 301, False, True),
+    (1, 8, 2000, True, False),
+    (4, 8, 1026, False, True),
+    (5, 3, 3, True, True),
+]
+
+
+@pytest.mark.parametrize("B,K,V,f32,ties", ODD_CASES, ids=[f"B{c[0]}_K{c[1]}_V{c[2]}_{'f32' if c[3] else 'bf16'}"
+                                                           f"{'_ties' if c[4] else ''}" for c in ODD_CASES])
+def test_odd_shapes_and_ties_bit_exact(H, B, K, V, f32, ties):
+    from gpu_util import log
+    rng = np.random.default_rng(1000 + B * 7 + K * 13 + V)
+    D, steps, maxf = 16, 4, 8
+    bos, eoc = V - 2, V - 1
+    E_bits = nx.f32_to_bf16((rng.standard_normal((K * V, D)) * 0.5).astype(np.float32))
+    E = nx.bf16_to_f32(E_bits)
+    if ties:
+        logits = [rng.integers(0, 4, (B, K, V)).astype(np.float32) for _ in range(steps)]
+    else:
+        logits = [(rng.standard_normal((B, K, V)) * 2).astype(np.float32) for _ in range(steps)]
+    if not f32:
+        logits = [nx.f32_to_bf16(lg) for lg in logits]
+    frame = rng.integers(0, K + 2, B).astype(np.int32)
+    seen = (rng.random((B, K)) < 0.2).astype(np.uint8)
+    done = np.zeros(B, np.uint8)
+    log(f"codebook odd case B={B} K={K} V={V} f32={f32} ties={ties}")
+    gpu, fr, gseen, gdone, aligned = run_gpu_steps(H, logits, frame, seen, done, E_bits, V, bos, eoc, maxf,
+                                                    f32=f32)
+    o_frame, o_seen, o_done = frame.copy(), seen.copy(), done.copy()
+    o_aligned = np.full((B, maxf, K), -1, np.int32)
+    for s in range(steps):
+        lg = logits[s] if f32 else nx.bf16_to_f32(logits[s])
+        codes, emb = oc.codebook_step(lg, o_frame, o_seen, o_done, bos, eoc, E, o_aligned, maxf)
+        np.testing.assert_array_equal(gpu[s][0], codes, err_msg=f"codes step {s}")
+        np.testing.assert_array_equal(gpu[s][1], emb, err_msg=f"emb step {s}")
+    np.testing.assert_array_equal(fr, o_frame)
+    np.testing.assert_array_equal(gseen, o_seen)
+    np.testing.assert_array_equal(gdone, o_done)
+    np.testing.assert_array_equal(aligned, o_aligned)
+
+
 def test_invalid_ids_refused(H):
     import torch
     d = torch.zeros(16, dtype=torch.bfloat16, device="cuda")

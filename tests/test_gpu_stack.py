@@ -5,7 +5,7 @@
   held to the per-layer bf16 checks; the free-running hr_prefill_stack (with
   the audio head) is compared on the final hidden state and the logits, and
   its argmax ids must equal the oracle's except where the oracle's top-2
-  margin is below 1e-3.
+  margin is below 3x the bf16-storage chain's largest logit error.
 * Free-running bar: rounding at the bf16 storage points compounds over 36
   layers (1 - cosine grows to ~1e-4 at P=13), so the GPU is held to the
   oracle run free with the same bf16 rounding points: its distance from the
@@ -56,6 +56,22 @@ def model_36(H):
 def check_free_running(c_gpu: float, c_chain: float) -> None:
     assert c_gpu >= 0.999, c_gpu
     assert 1.0 - c_gpu <= 1.5 * (1.0 - c_chain) + 1e-6, (c_gpu, c_chain)
+
+
+def check_ids(g_log, o_log, e_log):
+    """Argmax ids of the free-running stack: equal to the oracle's wherever
+    bf16 storage cannot flip the decision.  Swapping the top two ids takes an
+    error of at least the oracle's top-2 margin in their difference; the
+    bf16-storage chain's logits are off by up to e = max |chain - exact|, so a
+    difference may be off by 2e, and the GPU is held to 1.5x the chain (as for
+    the hidden state): ids may differ only where the margin is < 3e."""
+    from gpu_util import log, max_abs
+    e = max_abs(e_log, o_log)
+    g_ids, o_ids = g_log.argmax(-1), o_log.argmax(-1)
+    margin = oc.top2_margin(o_log)
+    log(f"ids gpu {g_ids.tolist()} oracle {o_ids.tolist()} margins {np.round(margin, 4).tolist()} "
+        f"(chain logit error {e:.3g})")
+    assert np.all((g_ids == o_ids) | (margin < 3.0 * e)), (g_ids, o_ids, margin, e)
 
 
 @pytest.mark.timeout(900)
@@ -121,10 +137,7 @@ def test_stack36_p13_per_layer_and_free_running(H, model_36):
         f"bf16-storage chain: h_L cos={ce_h:.7f} logits cos={ce_l:.7f}")
     check_free_running(c_h, ce_h)
     check_free_running(c_l, ce_l)
-    g_ids, o_ids = g_log.argmax(-1)[0], olog.argmax(-1)[0]
-    margin = oc.top2_margin(olog)[0]
-    log(f"ids gpu {g_ids.tolist()} oracle {o_ids.tolist()} margins {np.round(margin, 4).tolist()}")
-    assert np.all((g_ids == o_ids) | (margin < 1e-3))
+    check_ids(g_log[0], olog[0], e_log[0])
 
 
 @pytest.mark.timeout(900)
@@ -182,9 +195,7 @@ def test_varlen32_stack36_sampled_sequences(H, model_36):
             f"bf16-storage chain h_L cos={ce_h:.7f} logits cos={ce_l:.7f}")
         check_free_running(c_h, ce_h)
         check_free_running(c_l, ce_l)
-        g_ids, o_ids = g_log[s].argmax(-1), olog[0].argmax(-1)
-        margin = oc.top2_margin(olog[0])
-        assert np.all((g_ids == o_ids) | (margin < 1e-3)), (s, g_ids, o_ids, margin)
+        check_ids(g_log[s], olog[0], elog[0])
         # the cache rows of this sequence's slot: layer 0 and the last layer
         for l in (0, m.n_layers - 1):
             kb = kvs[l][0][s * cap: s * cap + L].float().cpu().numpy()
