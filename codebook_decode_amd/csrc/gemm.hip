@@ -51,28 +51,33 @@ __device__ __forceinline__ floatx4 mma16(u32x4 a, u32x4 b, floatx4 c) {
   }
 }
 
-// 32 x 32 output block over one 64-byte K slab.  Each lane contributes two
-// 16-byte chunks of its row of A and of B.  bf16: two v_mfma_f32_32x32x16_bf16
-// (chunk 0 -> k-step 0, chunk 1 -> k-step 1); e4m3: one
-// v_mfma_scale_f32_32x32x64_f8f6f4 (format 0 = e4m3 on both sides, unit scale)
-// on the 32 contiguous bytes.  The 32x32 forms issue at twice the rate of the
-// 16x16 ones on gfx950 (measured 2.16 vs 1.24 PFLOP/s bf16).
-template <bool FP8>
-__device__ __forceinline__ floatx16 mma32(const u32x4 (&a)[2], const u32x4 (&b)[2], floatx16 c) {
+// 32 x 32 output block over one K slab: NC 16-byte chunks of its row of A and
+// of B per lane.  bf16: chunk c feeds one v_mfma_f32_32x32x16_bf16; e4m3:
+// chunks (2m, 2m+1) feed one v_mfma_scale_f32_32x32x64_f8f6f4 (format 0 = e4m3
+// on both sides, unit scale) on those 32 contiguous bytes.  The 32x32 forms
+// issue at twice the rate of the 16x16 ones on gfx950 (measured 2.16 vs 1.24
+// PFLOP/s bf16).
+template <bool FP8, int NC>
+__device__ __forceinline__ floatx16 mma32(const u32x4 (&a)[NC], const u32x4 (&b)[NC], floatx16 c) {
   if constexpr (FP8) {
     typedef int intx8 __attribute__((ext_vector_type(8)));
-    intx8 av, bv;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      av[i] = int(a[0][i]); av[4 + i] = int(a[1][i]);
-      bv[i] = int(b[0][i]); bv[4 + i] = int(b[1][i]);
+    for (int m = 0; m < NC / 2; ++m) {
+      intx8 av, bv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        av[i] = int(a[2 * m][i]); av[4 + i] = int(a[2 * m + 1][i]);
+        bv[i] = int(b[2 * m][i]); bv[4 + i] = int(b[2 * m + 1][i]);
+      }
+      c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
     }
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
+    return c;
   } else {
-    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]),
-                                                __builtin_bit_cast(bf16x8, b[0]), c, 0, 0, 0);
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[1]),
-                                                   __builtin_bit_cast(bf16x8, b[1]), c, 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < NC; ++m)
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[m]), __builtin_bit_cast(bf16x8, b[m]),
+                                                  c, 0, 0, 0);
+    return c;
   }
 }
 
@@ -372,9 +377,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
 // hold.  One barrier per slab: after it every wave's copies of slab s have
 // landed and every wave is done with slab s-1, whose slot is refilled with slab
 // s+STAGES-1.
-constexpr int TBK = 64;   // slab depth in bytes
-
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+// LDS chunk swizzle for slabs of SB bytes per row: 64-byte rows pair up in a
+// 128-byte bank line, so chunk c of row r sits at c ^ ((r >> 1) & 3); 128-byte
+// rows fill the bank line alone: c ^ (r & 7).
+template <int SB>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (SB == 64) return (row >> 1) & 3;
+  else return row & 7;
+}
 
 __device__ __forceinline__ void lds_copy16(const uint8_t* g, uint8_t* lds_base) {
   // generic -> local address-space cast (not an integer truncation)
@@ -420,25 +430,28 @@ __device__ __forceinline__ void wait_stages(int pending) {
   wait_pending<LPS, STAGES - 2>(pending);
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+template <int BM, int BN, int WM, int WN, int STAGES, int SB = 64>
 struct TileCfg {
+  static_assert(SB == 64 || SB == 128, "slab depth");
   static constexpr int kThreads = 64 * WM * WN;
   static constexpr int kIM = BM / WM / 32;                  // 32-row blocks per wave
   static constexpr int kJN = BN / WN / 32;                  // 32-col blocks per wave
-  static constexpr int kCopies = (BM + BN) / 16;            // 1 KB wave copies per slab
+  static constexpr int kChunks = SB / 16;                   // 16-byte chunks per row
+  static constexpr int kRowsPerCopy = 1024 / SB;            // rows per 1 KB wave copy
+  static constexpr int kCopies = (BM + BN) / kRowsPerCopy;  // 1 KB wave copies per slab
   static constexpr int kLPS = kCopies / (WM * WN);          // copies per wave per slab
-  static constexpr int kSlabA = BM * TBK, kSlabB = BN * TBK;
+  static constexpr int kSlabA = BM * SB, kSlabB = BN * SB;
   static constexpr size_t kLds = size_t(STAGES) * (kSlabA + kSlabB);
   static_assert(kCopies % (WM * WN) == 0, "copies must split evenly over the waves");
   static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "tile shape");
 };
 
-template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES>
+template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int SB>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, int M, int N, int K_bytes,
     int tiles_m, int n_tiles, EpiArgs e) {
-  using C = TileCfg<BM, BN, WM, WN, STAGES>;
-  constexpr int IM = C::kIM, JN = C::kJN, LPS = C::kLPS;
+  using C = TileCfg<BM, BN, WM, WN, STAGES, SB>;
+  constexpr int IM = C::kIM, JN = C::kJN, LPS = C::kLPS, NC = C::kChunks / 2;
   static_assert(EPI != HR_EPI_SWIGLU || JN % 2 == 0, "SwiGLU waves hold gate/up block pairs");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* sA = smem;                                   // [STAGES][BM rows][64 B]
@@ -460,21 +473,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
   const int tm = first_m + in_group % gm, tn = in_group / gm;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // this wave's LPS 1-KB copies per slab: copy q covers 16 rows of A (q < BM/16)
-  // or of B; lane i fills LDS chunk 64 q' + i of that operand
-  const uint8_t* src[LPS];
+  // this wave's LPS 1-KB copies per slab: copy q covers 1024/SB rows of A or of
+  // B; lane i fills LDS chunk 64 q' + i of that operand.  Sources are 32-bit
+  // byte offsets from x or w (the host keeps both operands under 2 GB).
+  uint32_t src[LPS];
   int dst_off[LPS];
 #pragma unroll
   for (int j = 0; j < LPS; ++j) {
     const int q = wave + j * (WM * WN);
-    const bool is_a = q < BM / 16;
-    const int qq = is_a ? q : q - BM / 16;
+    const bool is_a = q < BM / C::kRowsPerCopy;
+    const int qq = is_a ? q : q - BM / C::kRowsPerCopy;
     const int chunk = qq * 64 + lane;
-    const int row = chunk >> 2, pc = chunk & 3;
-    const int lc = pc ^ swz(row);
+    const int row = chunk / C::kChunks, pc = chunk % C::kChunks;
+    const int lc = pc ^ swz<SB>(row);
     dst_off[j] = is_a ? qq * 1024 : STAGES * C::kSlabA + qq * 1024;
     if (is_a) {
-      src[j] = x + size_t(min(m0 + row, M - 1)) * K_bytes + lc * 16;
+      src[j] = uint32_t(min(m0 + row, M - 1)) * uint32_t(K_bytes) + lc * 16;
     } else {
       int br;
       if constexpr (EPI == HR_EPI_SWIGLU) {
@@ -486,20 +500,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
       } else {
         br = min(n0 + row, N - 1);
       }
-      src[j] = w + size_t(br) * K_bytes + lc * 16;
+      src[j] = uint32_t(br) * uint32_t(K_bytes) + lc * 16;
     }
   }
-  const int slabs_total = K_bytes / TBK;
+  const int slabs_total = K_bytes / SB;
   const int kz = blockIdx.z, ksplit = gridDim.z;
   const int sl0 = (slabs_total * kz) / ksplit, sl1 = (slabs_total * (kz + 1)) / ksplit;
   const int n_slabs = sl1 - sl0;
 
   auto issue = [&](int slab, int stage) {
-    const size_t ko = size_t(slab) * TBK;
+    const size_t ko = size_t(slab) * SB;
 #pragma unroll
     for (int j = 0; j < LPS; ++j) {
       const bool is_a = dst_off[j] < STAGES * C::kSlabA;
-      lds_copy16(src[j] + ko, smem + dst_off[j] + stage * (is_a ? C::kSlabA : C::kSlabB));
+      lds_copy16((is_a ? x : w) + src[j] + ko, smem + dst_off[j] + stage * (is_a ? C::kSlabA : C::kSlabB));
     }
   };
 
@@ -515,12 +529,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < n_slabs) issue(sl0 + s, s);
 
-  // a lane reads row (lane % 32) of each 32-row block, chunks c0 and c0 + step
-  // of the 64-byte slab: bf16 {h, 2 + h}, e4m3 {2h, 2h + 1}, h = lane / 32
+  // a lane reads row (lane % 32) of each 32-row block, NC chunks of the slab:
+  // bf16 chunk 2c + h feeds k-step c; e4m3 chunks 4m + 2h + {0, 1} feed MFMA m
+  // (h = lane / 32)
   const int h = lane >> 5, r32 = lane & 31;
-  const int c0 = FP8 ? 2 * h : h, cstep = FP8 ? 1 : 2;
   const int a_row0 = wm * (BM / WM) + r32, b_row0 = wn * (BN / WN) + r32;
-  typedef u32x4 Frag[2];
+  auto chunk_of = [&](int c) { return FP8 ? 4 * (c >> 1) + 2 * h + (c & 1) : 2 * c + h; };
+  typedef u32x4 Frag[NC];
   auto read_frags = [&](int stage, Frag (&fa)[IM], Frag (&fb)[JN]) {
     const uint8_t* A = sA + stage * C::kSlabA;
     const uint8_t* B = sB + stage * C::kSlabB;
@@ -528,22 +543,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
     for (int j = 0; j < JN; ++j) {
       const int r = b_row0 + j * 32;
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        fb[j][c] = *reinterpret_cast<const u32x4*>(B + r * TBK + (((c0 + c * cstep) ^ swz(r)) << 4));
+      for (int c = 0; c < NC; ++c)
+        fb[j][c] = *reinterpret_cast<const u32x4*>(B + r * SB + ((chunk_of(c) ^ swz<SB>(r)) << 4));
     }
 #pragma unroll
     for (int i = 0; i < IM; ++i) {
       const int r = a_row0 + i * 32;
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        fa[i][c] = *reinterpret_cast<const u32x4*>(A + r * TBK + (((c0 + c * cstep) ^ swz(r)) << 4));
+      for (int c = 0; c < NC; ++c)
+        fa[i][c] = *reinterpret_cast<const u32x4*>(A + r * SB + ((chunk_of(c) ^ swz<SB>(r)) << 4));
     }
   };
   auto mma_slab = [&](const Frag (&fa)[IM], const Frag (&fb)[JN]) {
 #pragma unroll
     for (int i = 0; i < IM; ++i)
 #pragma unroll
-      for (int j = 0; j < JN; ++j) acc[i][j] = mma32<FP8>(fa[i], fb[j], acc[i][j]);
+      for (int j = 0; j < JN; ++j) acc[i][j] = mma32<FP8, NC>(fa[i], fb[j], acc[i][j]);
   };
   // Software pipeline: the fragments of slab it+1 are read from LDS while the
   // MFMAs of slab it run, so LDS latency hides behind MFMA work.  Slab it+1
@@ -557,18 +572,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
     read_frags(0, fa0, fb0);
   }
   int it = 0;
+  constexpr int kReads = (IM + JN) * NC, kMfma = IM * JN * (FP8 ? NC / 2 : NC);
   auto step = [&](Frag (&fa)[IM], Frag (&fb)[JN], Frag (&fan)[IM], Frag (&fbn)[JN]) {
-    const bool more = it + 1 < n_slabs;
     // this slab's fragments were read one MFMA burst ago: settle them here so
     // no wait lands between the next slab's reads and these MFMAs
     wait_lds();
-    if (more) {
-      wait_stages<LPS, STAGES>(min(STAGES - 3, n_slabs - 2 - it));
-      lds_barrier();
-      if (it + STAGES - 1 < n_slabs) issue(sl0 + it + STAGES - 1, (it + STAGES - 1) % STAGES);
-      read_frags((it + 1) % STAGES, fan, fbn);
-    }
+    wait_stages<LPS, STAGES>(min(STAGES - 3, n_slabs - 2 - it));
+    lds_barrier();
+    if (it + STAGES - 1 < n_slabs) issue(sl0 + it + STAGES - 1, (it + STAGES - 1) % STAGES);
+    // the next slab's fragments (after the last slab: a stale slot, never
+    // used), issued one-for-one between this slab's MFMAs: issue is in order,
+    // so a burst of LDS reads stalled behind the copies into LDS would
+    // otherwise leave the matrix pipe idle (10% on the gate/up GEMM at M=512)
+    read_frags((it + 1) % STAGES, fan, fbn);
     mma_slab(fa, fb);
+#pragma unroll
+    for (int q = 0; q < (kReads < kMfma ? kReads : kMfma); ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    }
+    if constexpr (kMfma > kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
+    if constexpr (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kMfma, 0);
     ++it;
   };
   // unrolled by two so the current / next fragment sets are fixed registers
@@ -634,15 +658,15 @@ static void skinny(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, con
   }
 }
 
-template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES>
+template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int SB>
 static void tiled_cfg(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
                       int ksplit, hipStream_t st) {
-  using C = TileCfg<BM, BN, WM, WN, STAGES>;
+  using C = TileCfg<BM, BN, WM, WN, STAGES, SB>;
   const int tiles_m = (M + BM - 1) / BM;
   const int ncols = (EPI == HR_EPI_SWIGLU) ? 2 * e.F : N;
   const int tiles_n = (ncols + BN - 1) / BN;
   const int n_tiles = tiles_m * tiles_n;
-  auto kern = gemm_tiled_kernel<EPI, FP8, BM, BN, WM, WN, STAGES>;
+  auto kern = gemm_tiled_kernel<EPI, FP8, BM, BN, WM, WN, STAGES, SB>;
   static bool lds_raised = false;  // above the 64 KB default dynamic-LDS limit
   if (C::kLds > 65536 && !lds_raised) {
     hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -655,7 +679,7 @@ static void tiled_cfg(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, 
 
 // Launch with a split-K factor that fills the 256 CUs for the residual
 // projections (fp32 atomics into h), or the given one.
-template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES>
+template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int SB = 64>
 static void tiled_fill(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
                        hipStream_t st, int ks_force = 0) {
   const int ncols = (EPI == HR_EPI_SWIGLU) ? 2 * e.F : N;
@@ -663,9 +687,9 @@ static void tiled_fill(const uint8_t* x, const uint8_t* w, int M, int N, int Kb,
   int ks = 1;
   if (EPI == HR_EPI_RESIDUAL && tiles < 256) ks = (256 + tiles - 1) / tiles;
   if (EPI == HR_EPI_RESIDUAL && ks_force > 0) ks = ks_force;
-  const int max_ks = Kb / TBK / 4 > 0 ? Kb / TBK / 4 : 1;   // >= 4 slabs per split
+  const int max_ks = Kb / SB / 4 > 0 ? Kb / SB / 4 : 1;   // >= 4 slabs per split
   if (ks > max_ks) ks = max_ks;
-  tiled_cfg<EPI, FP8, BM, BN, WM, WN, STAGES>(x, w, M, N, Kb, e, ks, st);
+  tiled_cfg<EPI, FP8, BM, BN, WM, WN, STAGES, SB>(x, w, M, N, Kb, e, ks, st);
 }
 
 // Tile configuration of the large-M GEMM, chosen per projection from a sweep
