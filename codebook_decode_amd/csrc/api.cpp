@@ -65,6 +65,9 @@ hr_status check_dims(const hr_dims* d) {
     return fail(HR_EUNSUPPORTED, "query heads per kv head %d not in {1, 2, 4}", group);
   if (d->hidden % 64 || d->ffn % 64) return fail(HR_EUNSUPPORTED, "hidden and ffn must be multiples of 64");
   if (d->hidden > 8192) return fail(HR_EUNSUPPORTED, "hidden %d > 8192", d->hidden);
+  // the tiled GEMM addresses each operand with 32-bit byte offsets
+  if (uint64_t(2) * d->ffn * d->hidden * 2 >= (uint64_t(1) << 32))
+    return fail(HR_EUNSUPPORTED, "gate/up weight of %d x %d exceeds 4 GB", 2 * d->ffn, d->hidden);
   if (!(d->rope_theta > 0.f) || !(d->rms_eps >= 0.f) || !std::isfinite(d->rope_theta))
     return fail(HR_EINVAL, "rope_theta must be > 0 and rms_eps >= 0");
   return HR_OK;
@@ -110,6 +113,12 @@ hr_status check_batch(const hr_dims* d, const hr_batch* b, const hr_kv* kv) {
   }
   if (cu[b->n_seq] != b->total_tokens)
     return fail(HR_EINVAL, "cu_seqlens[n_seq] = %d != total_tokens %d", cu[b->n_seq], b->total_tokens);
+  {
+    const int64_t widest = d->ffn > d->hidden ? d->ffn : d->hidden;
+    const int64_t attn = int64_t(d->n_q_heads) * d->head_dim;
+    if (int64_t(b->total_tokens) * (widest > attn ? widest : attn) * 2 >= (int64_t(1) << 32))
+      return fail(HR_EUNSUPPORTED, "%d tokens: an activation matrix exceeds 4 GB", b->total_tokens);
+  }
   return HR_OK;
 }
 
@@ -355,6 +364,8 @@ hr_status hr_linear(const void* x, const void* w, const float* w_scale, float x_
   if (wtype != HR_BF16 && wtype != HR_FP8_E4M3) return fail(HR_EINVAL, "bad wtype");
   const bool fp8 = wtype == HR_FP8_E4M3;
   if (K % (fp8 ? 128 : 64)) return fail(HR_EUNSUPPORTED, "K = %d must be a multiple of %d", K, fp8 ? 128 : 64);
+  if (uint64_t(M > N ? M : N) * K * (fp8 ? 1 : 2) >= (uint64_t(1) << 32))
+    return fail(HR_EUNSUPPORTED, "an operand of %d x %d or %d x %d exceeds 4 GB", M, K, N, K);
   if (N % 16 || (epi == HR_EPI_SWIGLU && N % 32))
     return fail(HR_EUNSUPPORTED, "N = %d must be a multiple of 16 (32 for SwiGLU)", N);
   HR_TRY(need(x, "x"));

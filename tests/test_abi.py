@@ -78,6 +78,7 @@ def call_layer(d, L, b, kvv, ws_bytes=1 << 40, h=FAKE, ws=FAKE):
     ("slot", H.HR_ECAPACITY), ("max_seqlen", H.HR_EBOUND), ("used_gt_len", H.HR_EBOUND),
     ("used_missing", H.HR_EINVAL), ("cu_not_monotone", H.HR_EINVAL), ("workspace", H.HR_EWORKSPACE),
     ("misaligned_h", H.HR_EALIGN), ("fp8_scale", H.HR_EINVAL), ("noncausal_start", H.HR_EUNSUPPORTED),
+    ("weight_4gb", H.HR_EUNSUPPORTED), ("activation_4gb", H.HR_EUNSUPPORTED),
 ])
 def test_prefill_layer_validation(case, status):
     d, L, b, k = dims(), layer(), batch([13]), kv()
@@ -113,9 +114,15 @@ def test_prefill_layer_validation(case, status):
                   as_qkv=1.0, as_o=0.0, as_gu=1.0, as_down=1.0)
     elif case == "noncausal_start":
         d, b = dims(causal=False), batch([13], starts=[4], used=[13])
+    elif case == "weight_4gb":                       # 2F x D bf16 gate/up >= 4 GB
+        d = dims(hidden=8192, n_q_heads=64, n_kv_heads=16, ffn=131072)
+    elif case == "activation_4gb":                   # T x F bf16 >= 4 GB
+        b, k = batch([230000], max_seqlen=230000), kv(capacity=1 << 20)
     st = call_layer(d, L, b, k, ws_bytes, h)
     assert st == status, (case, st, H.hr_last_error())
     assert H.hr_last_error()
+    if case.endswith("4gb"):
+        assert "4 GB" in H.hr_last_error(), H.hr_last_error()
 
 
 def test_empty_batch_is_a_no_op():
@@ -173,6 +180,9 @@ def test_codebook_misaligned_embedding_refused():
 
 def test_linear_validation():
     lib = H.lib()
+    # an operand of 4 GB or more (32-bit byte offsets in the tiled GEMM)
+    assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_BF16, 65536, 64, 32768, 0, FAKE, 0.0, None) == \
+        H.HR_EUNSUPPORTED
     assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_BF16, 4, 16, 48, 0, FAKE, 0.0, None) == H.HR_EUNSUPPORTED
     assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_BF16, 4, 24, 64, 0, FAKE, 0.0, None) == H.HR_EUNSUPPORTED
     assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_FP8_E4M3, 4, 16, 128, 0, FAKE, 0.0, None) == H.HR_EINVAL
