@@ -29,6 +29,7 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 METRIC = "prefill ms/prompt at P=13, prompt tok/s at P=512; % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 
 
 def log(msg):
@@ -143,6 +144,186 @@ def gemm_gu_launches(H, m, P, dev_layers):
     return fns
 
 
+def gemm_traffic():
+    """Bytes per launch of the gate/up GEMM from the committed FETCH_SIZE /
+    WRITE_SIZE summary, if it was taken on the current GEMM source (else None)."""
+    import re
+    from codebook_decode_amd.profile_summary import source_digest
+    path = os.path.join(ROOT, "profiles", "gemm_gateup_m512_traffic.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_t = re.search(r"traffic_bytes_per_launch: (\d+)", txt)
+    m_h = re.search(r"gemm_source_sha256: ([0-9a-f]+)", txt)
+    if not m_t or not m_h or m_h.group(1) != source_digest():
+        return None
+    return int(m_t.group(1))
+
+
+def time_events(fn, reps, warm=2):
+    """Average wall time of fn() between HIP events on the current stream."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        fn()
+    end.record()
+    end.synchronize()
+    return start.elapsed_time(end) / 1e3 / reps
+
+
+def hbm(bytes_, sec):
+    gbs = bytes_ / sec / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def layer_rotated(H, m, dev_layers, lens=(6, 13), copies=4, reps=40):
+    """One bf16 layer at P tokens, rotating through `copies` layers' weights
+    (807 MB > the 256 MB MALL, so every call streams its weights from HBM)."""
+    import torch
+    import synth
+    from gpu_util import dev
+    from model_util import dims_of, kv_cache, workspace
+    dims = dims_of(H, m, True, 1)
+    cap = 2048
+    layers = [H.make_layer(dl) for dl in dev_layers[:copies]]
+    kvt = [kv_cache(m, 1, cap, poison=False) for _ in range(copies)]
+    kvs = [H.make_kv(k, v, cap, 1) for k, v in kvt]
+    weight_bytes = sum(t.numel() * t.element_size() for t in dev_layers[0].values())
+    out = {"weights_mb_per_layer": round(weight_bytes / 1e6, 2), "rotated_copies": copies}
+    for P in lens:
+        b = H.Batch([0, P], [0], [0])
+        h0 = dev(synth.bf16_bits_to_f32(synth.embed_rows(m, synth.prompt_ids(m, P))))
+        h = h0.clone()
+        ws = workspace(H, dims, H.HR_BF16, P)
+        i = [0]
+
+        def call():
+            k = i[0] % copies
+            H.hr_prefill_layer(dims, layers[k], b, h, kvs[k], ws)
+            i[0] += 1
+        sec = time_events(call, reps)
+        out[f"p{P}"] = {"us_per_layer": round(sec * 1e6, 2), "roofline": hbm(weight_bytes, sec)}
+    return out
+
+
+FP8_SCALES = {"qkv": 0.010010390956675132, "o": 0.0037856422949579236, "gu": 0.010591977409446089,
+              "dn": 0.021752634441032436}   # layer 0, static per-tensor: amax / 448 on the seeded 32-token prompt
+
+
+def fp8_layer(H, m, dev_layer, reps=20):
+    """FP8 layer of the 4B shape: 544 rows, the first 512 used, non-causal;
+    e4m3 weights with per-output-channel scales packed on the device."""
+    import torch
+    import synth
+    from gpu_util import dev
+    from model_util import dims_of, fp8_pack, kv_cache, workspace
+    P, rows, cap = 512, 544, 544
+    w8, ws8 = fp8_pack(H, dev_layer, m)
+    layer = H.make_layer(w8, H.HR_FP8_E4M3, FP8_SCALES, ws8)
+    dims = dims_of(H, m, False, 1)
+    kc, vc = kv_cache(m, 1, cap, poison=False)
+    kv = H.make_kv(kc, vc, cap, 1)
+    b = H.Batch([0, rows], [0], [0], [P])
+    h0 = np.zeros((rows, m.hidden), np.float32)
+    h0[:P] = synth.bf16_bits_to_f32(synth.embed_rows(m, synth.prompt_ids(m, P)))
+    h = dev(h0)
+    ws = workspace(H, dims, H.HR_FP8_E4M3, rows)
+    sec = time_events(lambda: H.hr_prefill_layer(dims, layer, b, h, kv, ws), reps)
+    e4m3_flops = 2.0 * P * m.hidden * (m.qkv_rows + 2 * m.ffn) + 2.0 * P * m.attn_width * m.hidden \
+        + 2.0 * P * m.ffn * m.hidden
+    attn_flops = 2.0 * 2 * m.n_q_heads * m.head_dim * P * P
+    t_floor = e4m3_flops / (FP8_PEAK_TFLOPS * 1e12) + attn_flops / (BF16_PEAK_TFLOPS * 1e12)
+    return {"workload": "fp8_layer_d2560_p512_pad544 (non-causal over 512 used keys)",
+            "us_per_layer_wall": round(sec * 1e6, 2), "e4m3_gflop": round(e4m3_flops / 1e9, 2),
+            "attention_gflop_bf16": round(attn_flops / 1e9, 2), "floor_us": round(t_floor * 1e6, 2),
+            "frac_of_floor": round(t_floor / sec, 4)}
+
+
+def varlen_batch(H, m, layers, shared, reps=3):
+    """32 prompts (lengths uniform on [6, 256], packed), 36 layers + head."""
+    import torch
+    import synth
+    from gpu_util import dev
+    from model_util import dims_of, kv_cache, workspace
+    w = synth.workloads()["varlen32_stack36_d2560"]
+    lens = np.array(w.prompt_lens)
+    n, cap = lens.size, w.capacity
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    ids = dev(np.concatenate([synth.prompt_ids(m, int(L), seq=s) for s, L in enumerate(lens)]))
+    dims = dims_of(H, m, True, len(layers))
+    b = H.Batch(cu, np.zeros(n), np.arange(n))
+    kvt = [kv_cache(m, n, cap, poison=False) for _ in layers]
+    kvs = [H.make_kv(k, v, cap, n) for k, v in kvt]
+    h = torch.empty((T, m.hidden), dtype=torch.float32, device="cuda")
+    logits = torch.empty((n, m.n_codebooks * m.cb_vocab), dtype=torch.float32, device="cuda")
+    ws = workspace(H, dims, H.HR_BF16, T)
+    sec = time_events(lambda: H.hr_prefill_stack(dims, layers, b, ids, shared["embed"], m.vocab, None, kvs,
+                                                 shared["final"], shared["head"], m.n_codebooks, m.cb_vocab, h,
+                                                 logits, ws), reps, warm=1)
+    del kvt
+    return {"workload": f"varlen32_stack36_d2560: {n} prompts, T={T}, lengths {lens.min()}..{lens.max()}",
+            "ms": round(sec * 1e3, 3), "tok_s": round(T / sec, 1)}
+
+
+def codebook_steps(H, m, shared, B=64, reps=100):
+    """The delayed-codebook step at B streams, 8 x 1026, bf16 logits."""
+    import torch
+    import synth
+    from gpu_util import dev, dev_bf16
+    K, V, D = m.n_codebooks, m.cb_vocab, m.hidden
+    logits = dev_bf16(synth.codebook_logits(B, K, V, 0, m.eoc_id))
+    st = synth.codebook_state(B, K)
+    frame, seen, done = dev(st["frame"]), dev(st["eoc_seen"]), dev(st["done"])
+    codes = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    emb = torch.empty((B, D), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        H.hr_codebook_step(B, K, V, m.bos_id, m.eoc_id, logits, frame, seen, done, codes, None, 0, shared["cb"], D,
+                           emb)
+    sec = time_events(call, reps)
+    bytes_ = B * (K * V * 2 + K * D * 2 + D * 2 + K * 4 + K + 8)
+    return {"B": B, "us_per_step": round(sec * 1e6, 2), "bytes": int(bytes_), "roofline": hbm(bytes_, sec)}
+
+
+def hbm_sweep(H, m, shared):
+    """The memory-bound kernels where their bytes outgrow launch latency:
+    RMSNorm (6 B per element), q/k norm + RoPE + KV write (24.6 KB per token),
+    codebook step (62.5 KB per stream)."""
+    import torch
+    from model_util import dims_of
+    out = {}
+    D = m.hidden
+    for T in (4096, 65536):
+        h = torch.randn((T, D), device="cuda")
+        x = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+        sec = time_events(lambda: H.hr_rmsnorm(h, T, D, shared["final"], m.rms_eps, x), 10)
+        out[f"rmsnorm_T{T}"] = {"us": round(sec * 1e6, 2), "roofline": hbm(6 * T * D, sec)}
+        del h, x
+    for T in (4096, 32768):
+        dims = dims_of(H, m, True, 1)
+        qkv = (torch.randn((T, m.qkv_rows), device="cuda") * 0.5).to(torch.bfloat16)
+        q = torch.empty((T, m.attn_width), dtype=torch.bfloat16, device="cuda")
+        kc = torch.empty((T, m.n_kv_heads, m.head_dim), dtype=torch.bfloat16, device="cuda")
+        vc = torch.empty_like(kc)
+        b = H.Batch([0, T], [0], [0])
+        kv = H.make_kv(kc, vc, T, 1)
+        qn = shared["final"][:m.head_dim]
+        sec = time_events(lambda: H.hr_qknorm_rope_kv(dims, b, qkv, qn, qn, q, kv), 10)
+        bytes_ = T * (m.qkv_rows * 2 + m.attn_width * 2 + 2 * m.n_kv_heads * m.head_dim * 2)
+        out[f"qknorm_rope_kv_T{T}"] = {"us": round(sec * 1e6, 2), "roofline": hbm(bytes_, sec)}
+        del qkv, q, kc, vc
+    for B in (4096, 16384):
+        r = codebook_steps(H, m, shared, B=B, reps=10)
+        out[f"codebook_B{B}"] = {"us": r["us_per_step"], "roofline": r["roofline"]}
+    return out
+
+
 def cpu_baseline(m, P, host_layers):
     """The float64 oracle on the P-token prefill of the whole stack (every layer
     given in ``host_layers``, scaled to m.n_layers if fewer), plus final norm
@@ -189,6 +370,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
     ap.add_argument("--layers", type=int, default=36)
+    ap.add_argument("--headline-only", action="store_true", help="skip the other measurement rows")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path is built and "
@@ -241,7 +423,7 @@ def main():
                    "prompt_len": P, "layers": m.n_layers, "graph": bool(args.graph)},
         "roofline": {"bound": "mfma", "kernel": "gemm_tiled SwiGLU (gate/up 512 x 19456 x 2560)",
                      "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": gemm_traffic(),
                      "avg_launch_us": round(t_gu * 1e6, 2)},
         "stack_p512": {"tflops_effective": round(stack_flops / sec / 1e12, 2),
                        "mfma_frac": round(stack_flops / sec / 1e12 / BF16_PEAK_TFLOPS, 4)},
@@ -252,6 +434,21 @@ def main():
                              "bytes_per_prompt": int(weight_bytes + head_bytes)},
                 "pages_context_ms": 6.82},
     }
+    # the other measurement rows: P=128, one layer at P=6/13 (weights streamed
+    # from HBM), FP8 layer, varlen batch, codebook step, memory-bound sweep
+    if m.n_layers == 36 and not args.headline_only:
+        log("timing P=128, the single layer, FP8, varlen, codebook and the HBM sweep")
+        st128 = Stack(H, m, 128, dev_layers, layers, shared)
+        sec128 = time_steps(st128.step, args.steps, args.warmup, args.graph)
+        del st128
+        out["p128"] = {"ms_per_prompt": round(sec128 * 1e3, 4),
+                       "roofline": hbm(weight_bytes + head_bytes, sec128)}
+        out["layer_d2560"] = layer_rotated(H, m, dev_layers)
+        out["fp8_layer"] = fp8_layer(H, m, dev_layers[0])
+        out["varlen32"] = varlen_batch(H, m, layers, shared)
+        out["codebook_b64"] = codebook_steps(H, m, shared)
+        out["hbm_sweep"] = hbm_sweep(H, m, shared)
+        torch.cuda.synchronize()
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(m, P, host_layers)
