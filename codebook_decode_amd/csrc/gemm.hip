@@ -14,16 +14,15 @@
 //    whole cache lines), the activation rows come from L2.  Cross-workgroup
 //    split-K (grid.y) is allowed for the residual epilogue, reduced with fp32
 //    atomics into h.  Wave partials are reduced in LDS in a fixed order.
-//  * tiled (M > 64): 128 x 128 output tile per 256-thread workgroup, 2 x 2
-//    wavefronts of 64 x 64 (4 x 4 MFMA 16x16 blocks), 128-byte K slabs double
-//    buffered global -> registers -> LDS (rows padded by 16 B), one barrier
-//    per slab.
-// MFMA: v_mfma_f32_16x16x32_bf16 (8 bf16 per lane) or v_mfma_f32_16x16x32_fp8_fp8
-// (8 e4m3 bytes per lane).  Lane l holds row/col l%16 and 8 consecutive k of
-// lane group l/16; since A and B use the same k placement, any consistent
-// assignment of memory k to (lane group, slot) is a valid contraction, which
-// lets each lane read 16 contiguous bytes.  Accumulator: lane l has column
-// l%16, rows 4*(l/16) + r.
+//    MFMA v_mfma_f32_16x16x32_bf16 / _fp8_fp8 with M padded to 16: lane l holds
+//    row/col l%16 and 8 consecutive k of lane group l/16; since A and B use the
+//    same k placement, any consistent assignment of memory k to (lane group,
+//    slot) is a valid contraction, which lets each lane read contiguous bytes.
+//  * tiled (M > 64): BM x BN output tile per workgroup of WM x WN wavefronts,
+//    32x32 MFMA blocks, K in slabs of 64 or 128 bytes per row copied HBM -> LDS
+//    by global_load_lds (no register round trip) through a multi-stage ring,
+//    XOR-swizzled so fragment reads are free of bank conflicts, one barrier per
+//    slab, fragment reads of the next slab interleaved with this slab's MFMAs.
 #include "common.h"
 #include "launch.h"
 
@@ -692,27 +691,38 @@ static void tiled_fill(const uint8_t* x, const uint8_t* w, int M, int N, int Kb,
   tiled_cfg<EPI, FP8, BM, BN, WM, WN, STAGES, SB>(x, w, M, N, Kb, e, ks, st);
 }
 
-// Tile configuration of the large-M GEMM, chosen per projection from a sweep
-// of 13 tile shapes and split-K factors on MI355X at M = 512 (bf16, the 4B
-// layer): QKV 64x128 (41.6 us against 48.3 for 256x128), O 128x64 split 3,
-// gate/up 256x256, down 256x128 split 6; the earlier shapes are kept above
-// M = 1024, where they were chosen.  Split-K fills the grid for the residual
-// projections.
+// Tile configuration of the large-M GEMM, per projection and M range, from
+// sweeps of 12-13 tile shapes, slab depths and split-K factors on MI355X with
+// the 4B layer's shapes (M = 128, 256, 512, 4192 bf16; M = 544 e4m3).  Small M
+// wants small tiles (more workgroups than CUs: QKV at M = 128 runs 39 -> 20 us
+// going from 128x128 to 64x64 tiles with 128-byte slabs); large M wants the
+// 256x256 tile (LDS traffic per MFMA).  Split-K fills the grid for the
+// residual projections.
 template <int EPI, bool FP8>
 static void tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
                   hipStream_t st) {
   const int K_el = FP8 ? Kb : Kb / 2;
   if constexpr (EPI == HR_EPI_SWIGLU) {
-    if (M >= 384) return tiled_fill<EPI, FP8, 256, 256, 4, 2, 4>(x, w, M, N, Kb, e, st);
-    return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
+    if (M > 384) return tiled_fill<EPI, FP8, 256, 256, 4, 2, 4>(x, w, M, N, Kb, e, st);
+    if (M > 128) return tiled_fill<EPI, FP8, 256, 128, 4, 2, 4>(x, w, M, N, Kb, e, st);
+    return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4, 128>(x, w, M, N, Kb, e, st);
   } else if constexpr (EPI == HR_EPI_BF16) {
-    if (M > 1024) return tiled_fill<EPI, FP8, 256, 128, 4, 2, 4>(x, w, M, N, Kb, e, st);
-    if (M >= 256) return tiled_fill<EPI, FP8, 64, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
-    return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
+    if (M > 1024) return tiled_fill<EPI, FP8, 256, 256, 4, 2, 4>(x, w, M, N, Kb, e, st);
+    if (M > 384) return tiled_fill<EPI, FP8, 64, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
+    if (M > 128) return tiled_fill<EPI, FP8, 128, 64, 2, 2, 6, 128>(x, w, M, N, Kb, e, st);
+    return tiled_fill<EPI, FP8, 64, 64, 2, 2, 8, 128>(x, w, M, N, Kb, e, st);
   } else {
-    if (M > 1024 || M < 256) return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
-    if (K_el >= 8192) return tiled_fill<EPI, FP8, 256, 128, 4, 2, 4>(x, w, M, N, Kb, e, st, 6);
-    return tiled_fill<EPI, FP8, 128, 64, 2, 2, 4>(x, w, M, N, Kb, e, st, 3);
+    if constexpr (FP8) {
+      if (M > 128) return tiled_fill<EPI, FP8, 128, 64, 4, 1, 4>(x, w, M, N, Kb, e, st);
+    }
+    if (M > 1024) return tiled_fill<EPI, FP8, 256, 256, 4, 2, 4>(x, w, M, N, Kb, e, st);
+    if (M > 384) {
+      if (K_el >= 8192) return tiled_fill<EPI, FP8, 256, 128, 4, 2, 4>(x, w, M, N, Kb, e, st, 6);
+      return tiled_fill<EPI, FP8, 128, 64, 2, 2, 4>(x, w, M, N, Kb, e, st, 3);
+    }
+    if (M > 128) return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
+    if (K_el >= 8192) return tiled_fill<EPI, FP8, 128, 64, 2, 2, 4>(x, w, M, N, Kb, e, st);
+    return tiled_fill<EPI, FP8, 64, 64, 2, 2, 4>(x, w, M, N, Kb, e, st);
   }
 }
 
