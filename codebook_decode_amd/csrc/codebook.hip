@@ -8,11 +8,12 @@
 // (logits, then the chosen embedding rows), so the kernel is built to have
 // each read in flight at once rather than one load after another:
 //  * argmax: G lanes per codebook (G = 512 / K rounded down to a power of two,
-//    at most one wavefront); the row is read as aligned element pairs (one
-//    32-bit word of bf16, or 64 bits of fp32), up to kPairs pairs per lane
-//    issued before any compare; each lane keeps (max, lowest index) over its
-//    pairs in increasing index order and a butterfly over the G lanes picks
-//    the row's first maximum;
+//    at most one wavefront); the row is read as aligned 16-byte units of the
+//    tensor (8 bf16 or 4 fp32; a unit may straddle two rows, the elements
+//    outside the row are skipped), up to kUnits units per lane issued before
+//    any compare; each lane keeps (max, lowest index) over its units in
+//    increasing index order and a butterfly over the G lanes picks the row's
+//    first maximum;
 //  * lane k applies codebook k's delay / EOC update; one lane updates the
 //    frame counter and done;
 //  * embedding sum: one 16-byte chunk of D per thread, the K rows loaded in
@@ -24,26 +25,37 @@
 namespace hr {
 
 constexpr int kCbThreads = 512;
-constexpr int kPairs = 12;      // pairs per lane per batch (V <= 1536 with 64 lanes in one batch)
+constexpr int kUnits = 5;       // 16-byte units per lane per batch (V <= 2560 bf16 / 1280 fp32 in one batch at 64 lanes)
 
 // value of pair unit u (elements 2u, 2u+1 of the logits tensor); the last
 // unit of an odd-sized tensor holds one element
+// 16-byte unit u of the logits tensor (elements [E u, E u + E), E = 8 bf16 or
+// 4 fp32; the tensor is 16-byte aligned); a unit that runs past the end of the
+// tensor is read element by element, the missing ones as -inf
 template <bool F32>
-__device__ __forceinline__ void load_pair(const void* p, size_t u, size_t total, float& x0, float& x1) {
-  if (2 * u + 1 < total) {
+__device__ __forceinline__ u32x4 load_unit(const void* p, size_t u, size_t total) {
+  constexpr int E = F32 ? 4 : 8;
+  if (size_t(E) * (u + 1) <= total) return reinterpret_cast<const u32x4*>(p)[u];
+  u32x4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
     if (F32) {
-      const float2_t v = reinterpret_cast<const float2_t*>(p)[u];
-      x0 = v[0];
-      x1 = v[1];
+      const size_t e = 4 * u + q;
+      v[q] = e < total ? __float_as_uint(static_cast<const float*>(p)[e]) : 0xFF800000u;
     } else {
-      const uint32_t w = reinterpret_cast<const uint32_t*>(p)[u];
-      x0 = bf_lo(w);
-      x1 = bf_hi(w);
+      const size_t e0 = 8 * u + 2 * q, e1 = e0 + 1;
+      const uint32_t lo = e0 < total ? static_cast<const uint16_t*>(p)[e0] : 0xFF80u;
+      const uint32_t hi = e1 < total ? static_cast<const uint16_t*>(p)[e1] : 0xFF80u;
+      v[q] = lo | (hi << 16);
     }
-  } else {
-    x0 = F32 ? static_cast<const float*>(p)[2 * u] : bf2f(static_cast<const uint16_t*>(p)[2 * u]);
-    x1 = -__builtin_inff();
   }
+  return v;
+}
+
+template <bool F32>
+__device__ __forceinline__ float unit_elem(const u32x4& v, int e) {   // e constant
+  if (F32) return __uint_as_float(v[e]);
+  return (e & 1) ? bf_hi(v[e >> 1]) : bf_lo(v[e >> 1]);
 }
 
 template <bool F32>
@@ -55,30 +67,38 @@ __global__ __launch_bounds__(kCbThreads) void codebook_step_kernel(
   extern __shared__ int32_t s_code[];  // [K] argmax ids, then chosen codes; [K, 2K) seen flags
   const int b = blockIdx.x;
   const bool is_done = done[b] != 0;
+  // the stream's state is read up front, with the logits, so the bookkeeping
+  // below waits on no memory
+  const int t = frame[b];
+  for (int k = threadIdx.x; k < K; k += blockDim.x) s_code[K + k] = eoc_seen[size_t(b) * K + k];
 
   if (!is_done) {
     const int groups = kCbThreads / G, grp = threadIdx.x / G, gl = threadIdx.x % G;
     for (int k = grp; k < K; k += groups) {
-      const long long base = (static_cast<long long>(b) * K + k) * V;   // first element of the row
-      const size_t u0 = size_t(base) >> 1, u1 = (size_t(base) + V + 1) >> 1;
+      constexpr int E = F32 ? 4 : 8;                         // elements per unit
+      const size_t base = (size_t(b) * K + k) * V;          // first element of the row
+      const size_t u0 = base / E;                           // its unit
+      const int off0 = int(base - u0 * E);                  // element offset within that unit
+      const int nu = int((base + V + E - 1) / E - u0);      // units touching the row
       float best = -__builtin_inff();
       int bi = 0x7FFFFFFF;
-      for (size_t u = u0 + gl; u < u1; u += size_t(G) * kPairs) {
-        float x[kPairs][2];
+      for (int ui = gl; ui < nu; ui += G * kUnits) {
+        u32x4 x[kUnits];
 #pragma unroll
-        for (int j = 0; j < kPairs; ++j) {
-          const size_t uu = u + size_t(j) * G;
-          if (uu < u1) load_pair<F32>(logits, uu, total, x[j][0], x[j][1]);
+        for (int j = 0; j < kUnits; ++j) {
+          const int idx = ui + j * G;
+          if (idx < nu) x[j] = load_unit<F32>(logits, u0 + idx, total);
         }
 #pragma unroll
-        for (int j = 0; j < kPairs; ++j) {
-          const size_t uu = u + size_t(j) * G;
+        for (int j = 0; j < kUnits; ++j) {
+          const int idx = ui + j * G;
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const long long v = static_cast<long long>(2 * uu + h) - base;
-            if (uu < u1 && v >= 0 && v < V && (x[j][h] > best || bi == 0x7FFFFFFF)) {
-              best = x[j][h];
-              bi = int(v);
+          for (int e = 0; e < E; ++e) {
+            const int v = E * idx + e - off0;
+            const float xv = unit_elem<F32>(x[j], e);
+            if (idx < nu && v >= 0 && v < V && (xv > best || bi == 0x7FFFFFFF)) {
+              best = xv;
+              bi = v;
             }
           }
         }
@@ -93,12 +113,11 @@ __global__ __launch_bounds__(kCbThreads) void codebook_step_kernel(
   }
   __syncthreads();
   // delay / EOC bookkeeping: one lane per codebook, then one lane for the stream
-  const int t = frame[b];
   for (int k = threadIdx.x; k < K; k += blockDim.x) {
     int c = eoc;
     if (!is_done) {
       const size_t ks = size_t(b) * K + k;
-      uint8_t seen = eoc_seen[ks];
+      const bool seen = s_code[K + k] != 0;
       c = (t < k) ? bos : (seen ? eoc : s_code[k]);
       if (c == eoc && !seen) eoc_seen[ks] = 1;
       if (aligned != nullptr && t >= k && t - k < max_frames)
