@@ -414,6 +414,42 @@ hr_status hr_attention(const hr_dims* dims, const hr_batch* batch, const void* q
   return check_launch("attention");
 }
 
+size_t hr_attention_chunked_workspace_bytes(const hr_dims* dims, int32_t total_tokens, int32_t n_slots) {
+  if (!dims || total_tokens < 0 || n_slots < 1) return 0;
+  const size_t t = size_t(total_tokens), S = size_t(n_slots), Hq = size_t(dims->n_q_heads);
+  return up256(S * t * Hq * size_t(dims->head_dim) * 4) + up256(S * t * Hq * 8);
+}
+
+hr_status hr_attention_chunked(const hr_dims* dims, const hr_batch* batch, const void* q, const hr_kv* kv,
+                               void* out, hr_wtype out_type, float out_scale, int32_t chunk_tiles,
+                               int32_t n_slots, void* ws, size_t ws_bytes, hipStream_t stream) {
+  HR_TRY(check_dims(dims));
+  HR_TRY(check_kv(dims, kv, "kv"));
+  HR_TRY(check_batch(dims, batch, kv));
+  HR_TRY(need(q, "q"));
+  HR_TRY(need(out, "out"));
+  if (out_type == HR_FP8_E4M3 && !(out_scale > 0.f)) return fail(HR_EINVAL, "out_scale must be > 0");
+  if (chunk_tiles < 1 || n_slots < 1 || n_slots > 64)
+    return fail(HR_EINVAL, "chunk_tiles must be >= 1 and n_slots in [1, 64] (got %d, %d)", chunk_tiles, n_slots);
+  if (batch->total_tokens == 0) return HR_OK;
+  const size_t need_ws = hr_attention_chunked_workspace_bytes(dims, batch->total_tokens, n_slots);
+  if (!ws || ws_bytes < need_ws)
+    return fail(HR_EWORKSPACE, "attention workspace needs %zu bytes, got %zu", need_ws, ws_bytes);
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(HR_EALIGN, "workspace must be 256-byte aligned");
+  const size_t t = size_t(batch->total_tokens), Hq = size_t(dims->n_q_heads);
+  hr::AttnSplit sp;
+  sp.chunk_tiles = chunk_tiles;
+  sp.n_slots = n_slots;
+  sp.part_o = static_cast<float*>(ws);
+  sp.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + up256(size_t(n_slots) * t * Hq * dims->head_dim * 4));
+  sp.T = batch->total_tokens;
+  hr::launch_attention(q, kv->k, kv->v, batch->cu_seqlens, batch->start_pos, batch->cache_slot, batch->used_keys,
+                       batch->n_seq, batch->max_seqlen, dims->n_q_heads, dims->n_kv_heads, dims->head_dim,
+                       kv->capacity, dims->causal != 0, out, out_type == HR_FP8_E4M3,
+                       out_type == HR_FP8_E4M3 ? 1.0f / out_scale : 1.f, stream, &sp);
+  return check_launch("attention (key chunks)");
+}
+
 size_t hr_head_workspace_bytes(int32_t n_seq, int32_t D) {
   (void)n_seq;
   return D > 0 ? up256(size_t(64) * D * 2) : 0;

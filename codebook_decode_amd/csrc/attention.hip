@@ -36,12 +36,26 @@ __device__ __forceinline__ floatx16 mfma32_bf16(u32x4 a, u32x4 b, floatx16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Key chunks of a query block with n_tiles 64-key tiles: at least chunk_tiles
+// tiles per chunk, and no more chunks than n_slots (longer rows take longer
+// chunks).  chunk_tiles == 0: one chunk.
+__device__ __forceinline__ void chunk_plan(int n_tiles, int chunk_tiles, int n_slots, int& ct, int& n_chunks) {
+  if (chunk_tiles <= 0 || n_tiles <= chunk_tiles) {
+    ct = n_tiles;
+    n_chunks = 1;
+    return;
+  }
+  ct = max(chunk_tiles, (n_tiles + n_slots - 1) / n_slots);
+  n_chunks = (n_tiles + ct - 1) / ct;
+}
+
 template <int DH, int GROUP>
-__global__ __launch_bounds__(256) void attention_kernel(
+__global__ __launch_bounds__(256, 2) void attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ start_pos,
     const int32_t* __restrict__ cache_slot, const int32_t* __restrict__ used_keys, int Hq, int Hkv,
-    int capacity, int causal, float scale_log2, void* __restrict__ out, int out_fp8, float out_inv) {
+    int capacity, int causal, float scale_log2, void* __restrict__ out, int out_fp8, float out_inv,
+    int chunk_tiles, int n_slots, float* __restrict__ part_o, float2_t* __restrict__ part_ml, int T) {
   constexpr int QSUB = 4 / GROUP;             // 32-query sub-blocks per workgroup
   constexpr int QPW = 32 * QSUB;
   constexpr int K_LD = DH + 8;                // padded row of the K tile (elements)
@@ -56,7 +70,9 @@ __global__ __launch_bounds__(256) void attention_kernel(
 
   const int s = blockIdx.z, g = blockIdx.y;
   const int len = cu[s + 1] - cu[s];
-  const int qb = gridDim.x - 1 - blockIdx.x;  // longest causal rows first
+  // blockIdx.x = (query block, key chunk slot); longest causal rows first
+  const int qb = gridDim.x / n_slots - 1 - int(blockIdx.x) / n_slots;
+  const int ck = int(blockIdx.x) % n_slots;
   const int i0 = qb * QPW;
   if (i0 >= len) return;
   const int tok0 = cu[s];
@@ -71,6 +87,14 @@ __global__ __launch_bounds__(256) void attention_kernel(
   const int pos_q = start + iq;
   const int i_last = min(i0 + QPW, len) - 1;
   const int n_keys = causal ? start + i_last + 1 : used_keys[s];
+  // key chunk: tiles [kt0, kt1) of this query block (all of them when not split)
+  const int n_tiles_all = (n_keys + AKT - 1) / AKT;
+  int ct, n_chunks;
+  chunk_plan(n_tiles_all, chunk_tiles, n_slots, ct, n_chunks);
+  if (ck >= n_chunks) return;
+  const bool split = n_chunks > 1;
+  const int kt0 = ck * ct;
+  const int kt1 = min(n_tiles_all, kt0 + ct);
 
   // the wave's queries as the B operand: query r32, d = 16 ks + 8 half + [0,8)
   u32x4 qf[NKS];
@@ -84,26 +108,31 @@ __global__ __launch_bounds__(256) void attention_kernel(
   }
 
   // K/V tile fetch into registers: K chunk c -> (key c / (DH/8), d8 c % (DH/8));
-  // V unit u -> key pair (u % 32) of the tile, d8 = u / 32
+  // V unit u -> key pair (u % 32) of the tile, d8 = u / 32.  Keys past the end
+  // read the last key's row instead (a written, finite row): their scores are
+  // masked to -inf, so they add 0 x finite.
   u32x4 rk[KPT], rv[VPT][2];
+  const uint16_t* kbase = kc + (base * Hkv + g) * DH;
+  const uint16_t* vbase = vc + (base * Hkv + g) * DH;
+  const size_t row_stride = size_t(Hkv) * DH;
+  const int last_key = n_keys - 1;
   auto fetch = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int c = tid + 256 * j;
       const int key = c / (DH / 8), d8 = c % (DH / 8);
-      rk[j] = (k0 + key < n_keys)
-                  ? *reinterpret_cast<const u32x4*>(kc + ((base + k0 + key) * Hkv + g) * DH + d8 * 8)
-                  : u32x4{0u, 0u, 0u, 0u};
+      const int row = min(k0 + key, last_key);
+      rk[j] = *reinterpret_cast<const u32x4*>(kbase + size_t(row) * row_stride + d8 * 8);
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int u = tid + 256 * j;
       const int key = 2 * (u % (AKT / 2)), d8 = u / (AKT / 2);
 #pragma unroll
-      for (int e = 0; e < 2; ++e)
-        rv[j][e] = (k0 + key + e < n_keys)
-                       ? *reinterpret_cast<const u32x4*>(vc + ((base + k0 + key + e) * Hkv + g) * DH + d8 * 8)
-                       : u32x4{0u, 0u, 0u, 0u};
+      for (int e = 0; e < 2; ++e) {
+        const int row = min(k0 + key + e, last_key);
+        rv[j][e] = *reinterpret_cast<const u32x4*>(vbase + size_t(row) * row_stride + d8 * 8);
+      }
     }
   };
   auto stage = [&]() {
@@ -135,14 +164,13 @@ __global__ __launch_bounds__(256) void attention_kernel(
   float m_run = -__builtin_inff();
   float l_part = 0.f;
 
-  const int n_tiles = (n_keys + AKT - 1) / AKT;
-  if (n_tiles > 0) fetch(0);
-  for (int kt = 0; kt < n_tiles; ++kt) {
+  if (kt0 < kt1) fetch(kt0 * AKT);
+  for (int kt = kt0; kt < kt1; ++kt) {
     const int k0 = kt * AKT;
     __syncthreads();                 // every wave is done with the previous tile
     stage();
     __syncthreads();
-    if (kt + 1 < n_tiles) fetch(k0 + AKT);   // in flight during this tile's math
+    if (kt + 1 < kt1) fetch(k0 + AKT);   // in flight during this tile's math
 
     // scores of 2 blocks of 32 keys
     floatx16 sc[2];
@@ -163,13 +191,14 @@ __global__ __launch_bounds__(256) void attention_kernel(
     const int wave_pos0 = start + i0 + qsub * 32;
     const bool need_mask = (k0 + AKT > n_keys) || (causal && k0 + AKT - 1 > wave_pos0);
     if (need_mask) {
+      // causal: key j visible to query pos_q iff j <= pos_q (which is < n_keys)
+      const int j_max = causal ? pos_q : last_key;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = k0 + blk * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = j < n_keys && (!causal || j <= pos_q);
-          if (!vis) sc[blk][r] = -__builtin_inff();
+          if (j > j_max) sc[blk][r] = -__builtin_inff();
         }
     }
     float mt = -__builtin_inff();
@@ -178,9 +207,19 @@ __global__ __launch_bounds__(256) void attention_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[blk][r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32, kWave)) * scale_log2;   // scale > 0: max commutes
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    // The reference max m_run moves only when a tile exceeds it by more than
+    // 8 (base 2): probabilities then stay <= 2^8, well inside bf16 and fp32
+    // range at unchanged relative precision, and most tiles skip rescaling
+    // the accumulators (the result o / l does not depend on the reference).
+    const bool grow = mt > m_run + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;   // 0 from -inf
+      if (grow) m_run = mt;
+      l_part *= alpha;
+#pragma unroll
+      for (int j = 0; j < NDB; ++j) o[j] *= alpha;
+    }
+    const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
     float psum = 0.f;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
@@ -190,10 +229,7 @@ __global__ __launch_bounds__(256) void attention_kernel(
         sc[blk][r] = p;
         psum += p;
       }
-    l_part = l_part * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int j = 0; j < NDB; ++j) o[j] *= alpha;
+    l_part += psum;
     // O^T += V^T P^T, 4 MFMAs (2 blocks x 2 k-steps of 16 keys) per d block
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
@@ -217,8 +253,23 @@ __global__ __launch_bounds__(256) void attention_kernel(
   }
 
   float l = l_part + __shfl_xor(l_part, 32, kWave);
-  const float inv_l = l > 0.f ? 1.0f / l : 0.f;
   if (!qok) return;
+  if (split) {
+    // partial of this key chunk: unnormalised o, running max (log2 units), sum
+    const size_t prow = (size_t(ck) * T + tok0 + iq) * Hq + hh;
+    float* po = part_o + prow * DH;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = db * 32 + 8 * rg + 4 * half;
+        *reinterpret_cast<floatx4*>(po + d0) =
+            floatx4{o[db][4 * rg], o[db][4 * rg + 1], o[db][4 * rg + 2], o[db][4 * rg + 3]};
+      }
+    if (half == 0) part_ml[prow] = float2_t{m_run, l};
+    return;
+  }
+  const float inv_l = l > 0.f ? 1.0f / l : 0.f;
   const size_t orow = (size_t(tok0 + iq) * Hq + hh) * DH;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -238,29 +289,83 @@ __global__ __launch_bounds__(256) void attention_kernel(
     }
 }
 
+// Combine the key-chunk partials of the split query blocks:
+// o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c, M = max_c m_c.
+// One workgroup per token; rows of unsplit query blocks were written final.
+template <int DH>
+__global__ __launch_bounds__(256) void attention_merge_kernel(
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ start_pos, const int32_t* __restrict__ used_keys,
+    int n_seq, int Hq, int causal, int qpw, int chunk_tiles, int n_slots, const float* __restrict__ part_o,
+    const float2_t* __restrict__ part_ml, int T, void* __restrict__ out, int out_fp8, float out_inv) {
+  const int t = blockIdx.x;
+  const int s = find_seq(cu, n_seq, t);
+  const int i = t - cu[s], len = cu[s + 1] - cu[s];
+  const int i_last = min((i / qpw) * qpw + qpw, len) - 1;
+  const int n_keys = causal ? start_pos[s] + i_last + 1 : used_keys[s];
+  int ct, nch;
+  chunk_plan((n_keys + AKT - 1) / AKT, chunk_tiles, n_slots, ct, nch);
+  if (nch <= 1) return;
+  for (int u = threadIdx.x; u < Hq * (DH / 4); u += 256) {
+    const int h = u / (DH / 4), d4 = u % (DH / 4);
+    float M = -__builtin_inff();
+    for (int c = 0; c < nch; ++c) M = fmaxf(M, part_ml[(size_t(c) * T + t) * Hq + h][0]);
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+    for (int c = 0; c < nch; ++c) {
+      const size_t prow = (size_t(c) * T + t) * Hq + h;
+      const float2_t ml = part_ml[prow];
+      const float wgt = (ml[0] == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(ml[0] - M);
+      L += wgt * ml[1];
+      acc += wgt * *reinterpret_cast<const floatx4*>(part_o + prow * DH + 4 * d4);
+    }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    const size_t orow = (size_t(t) * Hq + h) * DH + 4 * d4;
+    const float y0 = acc[0] * inv, y1 = acc[1] * inv, y2 = acc[2] * inv, y3 = acc[3] * inv;
+    if (out_fp8) {
+      *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(out) + orow) =
+          f2e4m3(y0 * out_inv) | (f2e4m3(y1 * out_inv) << 8) | (f2e4m3(y2 * out_inv) << 16) |
+          (f2e4m3(y3 * out_inv) << 24);
+    } else {
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow) = u32x2{pack_bf2(y0, y1), pack_bf2(y2, y3)};
+    }
+  }
+}
+
 template <int DH, int GROUP>
 static void launch_attn_t(const void* q, const void* kc, const void* vc, const int32_t* cu,
                           const int32_t* sp, const int32_t* slot, const int32_t* used, int n_seq,
                           int max_len, int Hq, int Hkv, int cap, bool causal, void* out, bool fp8,
-                          float out_inv, hipStream_t st) {
+                          float out_inv, const AttnSplit& sp_cfg, hipStream_t st) {
   constexpr int QPW = 32 * (4 / GROUP);
-  dim3 grid((max_len + QPW - 1) / QPW, Hkv, n_seq);
+  const int n_qb = (max_len + QPW - 1) / QPW;
+  const int slots = sp_cfg.chunk_tiles > 0 ? sp_cfg.n_slots : 1;
+  dim3 grid(n_qb * slots, Hkv, n_seq);
   const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf(float(DH));
   attention_kernel<DH, GROUP><<<grid, 256, 0, st>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
       static_cast<const uint16_t*>(vc), cu, sp, slot, used, Hq, Hkv, cap, causal ? 1 : 0,
-      scale_log2, out, fp8 ? 1 : 0, out_inv);
+      scale_log2, out, fp8 ? 1 : 0, out_inv, sp_cfg.chunk_tiles, slots, sp_cfg.part_o,
+      reinterpret_cast<float2_t*>(sp_cfg.part_ml), sp_cfg.T);
+  if (sp_cfg.chunk_tiles > 0)
+    attention_merge_kernel<DH><<<sp_cfg.T, 256, 0, st>>>(cu, sp, used, n_seq, Hq, causal ? 1 : 0, QPW,
+                                                         sp_cfg.chunk_tiles, slots, sp_cfg.part_o,
+                                                         reinterpret_cast<const float2_t*>(sp_cfg.part_ml),
+                                                         sp_cfg.T, out, fp8 ? 1 : 0, out_inv);
 }
+
+int attention_qpw(int Hq, int Hkv) { return 32 * (4 / (Hq / Hkv)); }
 
 void launch_attention(const void* q, const void* kc, const void* vc, const int32_t* cu,
                       const int32_t* sp, const int32_t* slot, const int32_t* used, int n_seq,
                       int max_len, int Hq, int Hkv, int d, int cap, bool causal, void* out, bool fp8,
-                      float out_inv, hipStream_t st) {
+                      float out_inv, hipStream_t st, const AttnSplit* split) {
   const int group = Hq / Hkv;
+  const AttnSplit none{};
+  const AttnSplit& cfg = split ? *split : none;
 #define HR_ATT(DH_, G_)                                                                         \
   if (d == DH_ && group == G_) {                                                                \
     launch_attn_t<DH_, G_>(q, kc, vc, cu, sp, slot, used, n_seq, max_len, Hq, Hkv, cap, causal, \
-                           out, fp8, out_inv, st);                                              \
+                           out, fp8, out_inv, cfg, st);                                         \
     return;                                                                                     \
   }
   HR_ATT(128, 4) HR_ATT(128, 2) HR_ATT(128, 1) HR_ATT(64, 4) HR_ATT(64, 2) HR_ATT(64, 1)

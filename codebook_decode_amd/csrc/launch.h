@@ -42,10 +42,21 @@ void launch_qknorm_rope_kv(const void* qkv, int T, int Hq, int Hkv, int d, float
                            const void* kw, void* q_out, void* kc, void* vc, int capacity,
                            hipStream_t st);
 
+// Key-chunk split of the attention (more workgroups for long rows): query
+// blocks with more than chunk_tiles 64-key tiles write fp32 partials per chunk
+// (n_slots chunk slots at most) and a merge kernel combines them.
+struct AttnSplit {
+  int chunk_tiles = 0;      // 0: no split
+  int n_slots = 1;
+  float* part_o = nullptr;  // [n_slots, T, Hq, d]
+  float* part_ml = nullptr; // [n_slots, T, Hq, 2]: running max (log2 units), sum
+  int T = 0;
+};
+int attention_qpw(int Hq, int Hkv);
 void launch_attention(const void* q, const void* kc, const void* vc, const int32_t* cu,
                       const int32_t* sp, const int32_t* slot, const int32_t* used, int n_seq,
                       int max_len, int Hq, int Hkv, int d, int cap, bool causal, void* out, bool fp8,
-                      float out_inv, hipStream_t st);
+                      float out_inv, hipStream_t st, const AttnSplit* split = nullptr);
 
 void launch_linear(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8,
                    int M, int N, int K, int epi, void* out, float out_scale, hipStream_t st);

@@ -86,6 +86,9 @@ def lib() -> ctypes.CDLL:
             "hr_linear": (c_i32, [c_vp, c_vp, c_vp, c_f32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_f32, c_vp]),
             "hr_qknorm_rope_kv": (c_i32, [P(HrDims), P(HrBatch), c_vp, c_vp, c_vp, c_vp, P(HrKv), c_vp]),
             "hr_attention": (c_i32, [P(HrDims), P(HrBatch), c_vp, P(HrKv), c_vp, c_i32, c_f32, c_vp]),
+            "hr_attention_chunked_workspace_bytes": (c_sz, [P(HrDims), c_i32, c_i32]),
+            "hr_attention_chunked": (c_i32, [P(HrDims), P(HrBatch), c_vp, P(HrKv), c_vp, c_i32, c_f32, c_i32,
+                                             c_i32, c_vp, c_sz, c_vp]),
             "hr_head_workspace_bytes": (c_sz, [c_i32, c_i32]),
             "hr_head_logits": (c_i32, [c_vp, P(HrBatch), c_i32, c_vp, c_f32, c_vp, c_i32, c_i32, c_vp, c_vp,
                                        c_sz, c_vp]),
@@ -164,7 +167,9 @@ class Batch:
 
 
 def make_kv(k, v, capacity: int, n_slots: int) -> HrKv:
-    return HrKv(ptr(k), ptr(v), capacity, n_slots)
+    kv = HrKv(ptr(k), ptr(v), capacity, n_slots)
+    kv._tensors = (k, v)          # the struct holds raw pointers: keep the caches alive with it
+    return kv
 
 
 def make_layer(t: dict, wtype: int = HR_BF16, scales: dict | None = None, wscales: dict | None = None) -> HrLayer:
@@ -178,6 +183,7 @@ def make_layer(t: dict, wtype: int = HR_BF16, scales: dict | None = None, wscale
         L.ws_qkv, L.ws_o = ptr(wscales["qkv"]), ptr(wscales["o"])
         L.ws_gu, L.ws_down = ptr(wscales["gu"]), ptr(wscales["dn"])
         L.as_qkv, L.as_o, L.as_gu, L.as_down = (scales["qkv"], scales["o"], scales["gu"], scales["dn"])
+    L._tensors = (t, wscales)     # raw pointers above: keep the weights alive with the struct
     return L
 
 
@@ -237,6 +243,18 @@ def hr_qknorm_rope_kv(dims, batch: Batch, qkv, q_norm_w, k_norm_w, q_out, kv: Hr
 def hr_attention(dims, batch: Batch, q, kv: HrKv, out, out_type=HR_BF16, out_scale=1.0, stream=None) -> None:
     _check(lib().hr_attention(ctypes.byref(dims), ctypes.byref(batch.c), ptr(q), ctypes.byref(kv), ptr(out),
                               out_type, out_scale, stream if stream is not None else current_stream()))
+
+
+def hr_attention_chunked_workspace_bytes(dims, total_tokens: int, n_slots: int) -> int:
+    return lib().hr_attention_chunked_workspace_bytes(ctypes.byref(dims), total_tokens, n_slots)
+
+
+def hr_attention_chunked(dims, batch: Batch, q, kv: HrKv, out, chunk_tiles: int, n_slots: int, ws,
+                         out_type=HR_BF16, out_scale=1.0, stream=None) -> None:
+    _check(lib().hr_attention_chunked(ctypes.byref(dims), ctypes.byref(batch.c), ptr(q), ctypes.byref(kv), ptr(out),
+                                      out_type, out_scale, chunk_tiles, n_slots, ptr(ws),
+                                      ws.numel() * ws.element_size(),
+                                      stream if stream is not None else current_stream()))
 
 
 def hr_head_workspace_bytes(n_seq: int, D: int) -> int:

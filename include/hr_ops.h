@@ -63,6 +63,23 @@ hr_status hr_qknorm_rope_kv(const hr_dims* dims, const hr_batch* batch, const vo
 hr_status hr_attention(const hr_dims* dims, const hr_batch* batch, const void* q, const hr_kv* kv,
                        void* out, hr_wtype out_type, float out_scale, hipStream_t stream);
 
+/* The same attention with each query block's keys split into chunks that run
+ * in separate workgroups (more parallel work for a few long rows), followed by
+ * a merge: chunk c keeps its running max m_c (base 2), sum l_c and unnormalised
+ * o_c in fp32, and o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c with
+ * M = max_c m_c, the standard combination of partial softmaxes.  A query block
+ * of n 64-key tiles takes max(chunk_tiles, ceil(n / n_slots)) tiles per chunk;
+ * blocks of at most chunk_tiles tiles are not split.  chunk_tiles >= 1,
+ * 1 <= n_slots <= 64.  ws: device scratch of at least
+ * hr_attention_chunked_workspace_bytes(dims, T, n_slots) bytes, 256-byte
+ * aligned (HR_EWORKSPACE / HR_EALIGN otherwise).  Worth it for rows much
+ * longer than the batch (a short continuation of a long cached prefix): a
+ * prefill from position 0 already has one query block per 32 rows. */
+size_t hr_attention_chunked_workspace_bytes(const hr_dims* dims, int32_t total_tokens, int32_t n_slots);
+hr_status hr_attention_chunked(const hr_dims* dims, const hr_batch* batch, const void* q, const hr_kv* kv,
+                               void* out, hr_wtype out_type, float out_scale, int32_t chunk_tiles,
+                               int32_t n_slots, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Final RMSNorm + audio-head projection of each sequence's last row
  * (steps A9 final, A10): z = RMS(h[last_s]; final_norm_w) in fp32, then
  * logits[s, k, v] = z . head_w[k*V + v] in fp32 (z is split into two bf16

@@ -195,3 +195,20 @@ def test_codebook_misaligned_logits_refused():
     st = lib.hr_codebook_step(4, 8, 1026, 1024, 1025, 0, MISALIGNED, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, 2560,
                               FAKE, None)
     assert st == H.HR_EALIGN
+
+
+@pytest.mark.parametrize("ct,slots,ws,ws_bytes,status", [
+    (0, 4, FAKE, 1 << 40, H.HR_EINVAL),           # chunk_tiles < 1
+    (2, 0, FAKE, 1 << 40, H.HR_EINVAL),           # no slot
+    (2, 65, FAKE, 1 << 40, H.HR_EINVAL),          # too many slots
+    (2, 4, FAKE, 1000, H.HR_EWORKSPACE),
+    (2, 4, None, 1 << 40, H.HR_EWORKSPACE),
+    (2, 4, FAKE + 16, 1 << 40, H.HR_EALIGN),
+])
+def test_attention_chunked_validation(ct, slots, ws, ws_bytes, status):
+    lib = H.lib()
+    d, b, k = dims(), batch([300]), kv()
+    st = lib.hr_attention_chunked(ctypes.byref(d), ctypes.byref(b.c), FAKE, ctypes.byref(k), FAKE, H.HR_BF16, 1.0,
+                                  ct, slots, ws, ws_bytes, None)
+    assert st == status, (st, H.hr_last_error())
+    assert H.hr_attention_chunked_workspace_bytes(d, 300, 4) >= 4 * 300 * 32 * (128 * 4 + 8)

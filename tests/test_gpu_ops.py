@@ -235,9 +235,29 @@ def test_qknorm_rope_kv(H, model, lens, starts, slots, cap):
     (32, 8, 128, [100], [0], False, [90]),
 ])
 def test_attention(H, Hq, Hkv, d, lens, starts, causal, used):
+    _attention_case(H, Hq, Hkv, d, lens, starts, causal, used)
+
+
+# key-chunked attention: (chunk_tiles, n_slots) forcing one-tile chunks, chunks
+# lengthened by the slot cap (a 9-tile row with 2 slots), rows continuing a
+# cached prefix, non-causal used keys with a short last chunk, fp8 output
+@pytest.mark.parametrize("Hq,Hkv,d,lens,starts,causal,used,ct,slots,fp8", [
+    (32, 8, 128, [512], [0], True, None, 2, 4, False),
+    (32, 8, 128, [300], [0], True, None, 1, 8, False),
+    (32, 8, 128, [544], [0], False, [512], 3, 3, False),
+    (32, 8, 128, [544], [0], False, [530], 2, 2, False),
+    (4, 2, 64, [200, 7, 90], [0, 0, 600], True, None, 2, 3, False),
+    (8, 8, 64, [130], [0], True, None, 1, 64, False),
+    (32, 8, 128, [256], [0], True, None, 1, 4, True),
+])
+def test_attention_chunked(H, Hq, Hkv, d, lens, starts, causal, used, ct, slots, fp8):
+    _attention_case(H, Hq, Hkv, d, lens, starts, causal, used, chunked=(ct, slots), fp8=fp8)
+
+
+def _attention_case(H, Hq, Hkv, d, lens, starts, causal, used, chunked=None, fp8=False):
     import torch
     from gpu_util import dev_bf16, f64_of_bf16, log
-    log(f"attention Hq={Hq} Hkv={Hkv} d={d} lens={lens} causal={causal}")
+    log(f"attention Hq={Hq} Hkv={Hkv} d={d} lens={lens} causal={causal} chunked={chunked} fp8={fp8}")
     cap = max(s + l for s, l in zip(starts, lens)) + 3
     n = len(lens)
     T = sum(lens)
@@ -246,10 +266,26 @@ def test_attention(H, Hq, Hkv, d, lens, starts, causal, used):
     vc = seeded_bf16((n * cap, Hkv, d), (32, cap, Hkv, d), 1.0)
     b = H.Batch(np.concatenate([[0], np.cumsum(lens)]), starts, list(range(n)), used)
     dims = H.make_dims(Hq * d, Hq, Hkv, d, 256, 1, 1e6, 1e-6, causal)
-    out = torch.full((T, Hq * d), float("nan"), dtype=torch.bfloat16, device="cuda")
-    H.hr_attention(dims, b, dev_bf16(q), H.make_kv(dev_bf16(kc), dev_bf16(vc), cap, n), out)
+    kc_d, vc_d = dev_bf16(kc), dev_bf16(vc)
+    kvd = H.make_kv(kc_d, vc_d, cap, n)
+    out_scale = 0.01
+    if fp8:
+        out = torch.full((T, Hq * d), 0x7F, dtype=torch.uint8, device="cuda")      # e4m3 NaN
+    else:
+        out = torch.full((T, Hq * d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    otype = H.HR_FP8_E4M3 if fp8 else H.HR_BF16
+    if chunked:
+        ct, slots = chunked
+        nb = H.hr_attention_chunked_workspace_bytes(dims, T, slots)
+        ws = torch.full((nb // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        H.hr_attention_chunked(dims, b, dev_bf16(q), kvd, out, ct, slots, ws, otype, out_scale)
+    else:
+        H.hr_attention(dims, b, dev_bf16(q), kvd, out, otype, out_scale)
     torch.cuda.synchronize()
-    got = f64_of_bf16(out).reshape(T, Hq, d)
+    if fp8:
+        got = nx.e4m3_decode(out.cpu().numpy()).reshape(T, Hq, d) * out_scale
+    else:
+        got = f64_of_bf16(out).reshape(T, Hq, d)
     qv, kv_, vv = nx.bf16_to_f64(q), nx.bf16_to_f64(kc), nx.bf16_to_f64(vc)
     cu = b.h_cu
     grp = Hq // Hkv
@@ -266,7 +302,10 @@ def test_attention(H, Hq, Hkv, d, lens, starts, causal, used):
             g = hh // grp
             ref = op.attention(qv[a:e, hh], kv_[s * cap:s * cap + nk, g], vv[s * cap:s * cap + nk, g], vis)
             err = np.abs(got[a:e, hh] - ref)
-            assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 4e-3), (s, hh, float(err.max()))
+            if fp8:     # e4m3 keeps 3 mantissa bits: half a step of 2^-3 relative, plus the bf16 path's error
+                assert np.all(err <= 2.0 ** -4 * np.abs(ref) + 2.0 ** -9 * out_scale + 4e-3), (s, hh, float(err.max()))
+            else:
+                assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 4e-3), (s, hh, float(err.max()))
 
 
 # ----------------------------------------------------------------------------- A9 final + A10
