@@ -146,12 +146,7 @@ hr_status check_layer(const hr_dims* d, const hr_layer* L, int idx) {
 
 struct Ws {
   uint8_t *x, *qkv, *q, *attn, *act, *head;
-  int* ctr;     // arrival counters of the fused small-batch projections
-  int n_ctr;
 };
-
-// batches up to this many tokens take the fused small-M projections
-constexpr int kSmallT = 64;
 
 size_t ws_layout(const hr_dims* d, int32_t T, Ws* w, uint8_t* base) {
   const size_t D = d->hidden, F = d->ffn, A = size_t(d->n_q_heads) * d->head_dim;
@@ -165,21 +160,17 @@ size_t ws_layout(const hr_dims* d, int32_t T, Ws* w, uint8_t* base) {
   };
   Ws tmp;
   tmp.x = take(t * (D > A ? D : A) * 2);
-  tmp.qkv = take(t * NQKV * (t <= size_t(kSmallT) ? 4 : 2));   // fp32 on the fused path
+  tmp.qkv = take(t * NQKV * 2);
   tmp.q = take(t * A * 2);
   tmp.attn = take(t * A * 2);
   tmp.act = take(t * F * 2);
   tmp.head = take(size_t(64) * D * 2);
-  tmp.n_ctr = d->n_q_heads + 2 * d->n_kv_heads;
-  tmp.ctr = reinterpret_cast<int*>(take(size_t(tmp.n_ctr) * sizeof(int)));
   if (w) *w = tmp;
   return off;
 }
 
 // one layer's kernels over buffers already validated.  `x_ready`: w.x already
-// holds RMSNorm_in(h) of this layer.  Batches of up to kSmallT tokens run the
-// QKV projection, the q/k norm, RoPE and the KV write as one launch (arrival
-// counters in w.ctr must be zero on entry; the kernel leaves them zero).
+// holds RMSNorm_in(h) of this layer.
 hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_batch* b, float* h, const hr_kv* kv,
                     const Ws& w, bool x_ready, hipStream_t st) {
   const int T = b->total_tokens, D = d->hidden, F = d->ffn, Hq = d->n_q_heads, Hkv = d->n_kv_heads;
@@ -187,18 +178,10 @@ hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_batch* b, floa
   const bool fp8 = L->wtype == HR_FP8_E4M3;
   if (!x_ready)
     hr::launch_rmsnorm(h, T, D, L->in_norm_w, d->rms_eps, w.x, fp8, fp8 ? 1.0f / L->as_qkv : 1.f, st);
-  if (T <= kSmallT) {
-    hr::QkvRopeParams p{L->q_norm_w, L->k_norm_w, d->rope_theta, d->rms_eps, b->cu_seqlens, b->start_pos,
-                        b->cache_slot, b->used_keys, b->n_seq, d->causal != 0, Hq, Hkv, dh, kv->capacity,
-                        w.q, kv->k, kv->v};
-    hr::launch_qkv_rope(w.x, L->w_qkv, L->ws_qkv, L->as_qkv, fp8, T, NQKV, D, reinterpret_cast<float*>(w.qkv),
-                        w.ctr, p, st);
-  } else {
-    hr::launch_linear(w.x, L->w_qkv, L->ws_qkv, L->as_qkv, fp8, T, NQKV, D, HR_EPI_BF16, w.qkv, 0.f, st);
-    hr::launch_qknorm_rope_kv(w.qkv, T, Hq, Hkv, dh, d->rope_theta, d->rms_eps, b->cu_seqlens, b->start_pos,
-                              b->cache_slot, b->used_keys, b->n_seq, d->causal != 0, L->q_norm_w, L->k_norm_w,
-                              w.q, kv->k, kv->v, kv->capacity, st);
-  }
+  hr::launch_linear(w.x, L->w_qkv, L->ws_qkv, L->as_qkv, fp8, T, NQKV, D, HR_EPI_BF16, w.qkv, 0.f, st);
+  hr::launch_qknorm_rope_kv(w.qkv, T, Hq, Hkv, dh, d->rope_theta, d->rms_eps, b->cu_seqlens, b->start_pos,
+                            b->cache_slot, b->used_keys, b->n_seq, d->causal != 0, L->q_norm_w, L->k_norm_w,
+                            w.q, kv->k, kv->v, kv->capacity, st);
   hr::launch_attention(w.q, kv->k, kv->v, b->cu_seqlens, b->start_pos, b->cache_slot, b->used_keys, b->n_seq,
                        b->max_seqlen, Hq, Hkv, dh, kv->capacity, d->causal != 0, w.attn, fp8,
                        fp8 ? 1.0f / L->as_o : 1.f, st);
@@ -246,7 +229,6 @@ hr_status hr_prefill_layer(const hr_dims* dims, const hr_layer* layer, const hr_
   if (ws_bytes < need_ws) return fail(HR_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need_ws);
   Ws w;
   ws_layout(dims, batch->total_tokens, &w, static_cast<uint8_t*>(ws));
-  if (batch->total_tokens <= kSmallT) hr::launch_zero_i32(w.ctr, w.n_ctr, stream);
   return run_layer(dims, layer, batch, h, kv, w, false, stream);
 }
 
@@ -293,7 +275,7 @@ hr_status hr_prefill_stack(const hr_dims* dims, const hr_layer* layers, const hr
   const hr_layer& L0 = layers[0];
   const bool fp8 = L0.wtype == HR_FP8_E4M3;
   hr::launch_embed_rmsnorm(ids, embed, x_embeds, T, D, L0.in_norm_w, dims->rms_eps, h_out, w.x, fp8,
-                           fp8 ? 1.0f / L0.as_qkv : 1.f, stream, w.ctr, w.n_ctr);
+                           fp8 ? 1.0f / L0.as_qkv : 1.f, stream);
   for (int l = 0; l < dims->n_layers; ++l)
     HR_TRY(run_layer(dims, &layers[l], batch, h_out, &kv[l], w, l == 0, stream));
   if (want_head)

@@ -9,7 +9,9 @@
 //
 // Two kernels:
 //  * skinny (M <= 64): weight streaming.  A workgroup owns 16 output columns
-//    (16 gate + 16 up for SwiGLU) and its wavefronts split K; every lane streams
+//    (16 gate + 16 up for SwiGLU; 32 for the bf16 and residual epilogues at
+//    M <= 16, so each activation fragment serves twice the weight rows) and
+//    its wavefronts split K; every lane streams
 //    32 contiguous bytes of a weight row per step (16 rows x 128 B per wave, so
 //    whole cache lines), the activation rows come from L2.  Cross-workgroup
 //    split-K (grid.y) is allowed for the residual epilogue, reduced with fp32
@@ -82,20 +84,6 @@ __device__ __forceinline__ floatx16 mma32(const u32x4 (&a)[NC], const u32x4 (&b)
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
-// Small-M (<= 64 rows) fusion of QKV + q/k RMSNorm + RoPE + KV write: the
-// product is kept in fp32 and the last workgroup of each head applies the
-// per-head norm and rotation and writes q or the cache rows of that head (one
-// launch instead of two).
-struct RopeTail {
-  float* qkv32;       // [M, (Hq+2Hkv) d] fp32 product
-  const uint16_t* qw;
-  const uint16_t* kw;
-  float theta, eps;
-  const int32_t *cu, *start_pos, *cache_slot, *used_keys;
-  int n_seq, causal, Hq, Hkv, d, capacity;
-  uint16_t *q_out, *kc, *vc;
-};
-
 struct EpiArgs {
   int epi;            // hr_epilogue
   void* out;          // bf16 [M,N] | fp32 [M,N] (+=) | act [M,F] | fp32 logits
@@ -106,103 +94,7 @@ struct EpiArgs {
   int out_fp8;        // SwiGLU output in e4m3
   int F;              // SwiGLU width (gate rows [0,F), up rows [F,2F))
   int hilo_rows;      // head: rows [0,h) hold hi, [h,2h) lo terms; out = hi + lo
-  int* counter;       // QKV tail: arrival counters (zero on entry, reset on exit)
-  RopeTail rope;
 };
-
-// Cross-workgroup hand-off without cache-wide fences.  On gfx950 the L2 is
-// private to each XCD, so a device-scope fence costs a whole-L2 writeback
-// (release) and invalidate (acquire) -- per workgroup, tens of microseconds
-// for a grid, and the invalidate makes every other resident workgroup on the
-// XCD re-fetch its operands.  Instead every value handed to another
-// workgroup is written and read with device-scope atomic stores and loads
-// (write-through / coherent accesses), fp32 atomic adds are coherent by
-// construction, and ordering is the completion wait of each wavefront's
-// stores (vmcnt 0) before the workgroup barrier that precedes the counter
-// increment: the last arrival sees every other workgroup's values.
-__device__ __forceinline__ void coherent_store(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float coherent_load(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// true in exactly one workgroup per `total` arrivals on *ctr (all threads)
-__device__ __forceinline__ bool last_arrival(int* ctr, int total) {
-  __shared__ int s_last;
-  // gfx9 s_waitcnt: vmcnt 0 (bits 3:0 and 15:14), expcnt 7, lgkmcnt 15
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  if (threadIdx.x == 0)
-    s_last = (__hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == total - 1) ? 1 : 0;
-  __syncthreads();
-  return s_last != 0;
-}
-
-// The tail below runs in one workgroup after every other one has finished, so
-// it is pure latency: every value it needs is requested before the first one
-// is used (no load waits on another load).
-
-// q/k RMSNorm + rotate-half RoPE + cache write of head row `r` for the M rows.
-// Work items (token, j) with j < d/2 own the RoPE pair (j, j + d/2); a token's
-// d/2 items are consecutive lanes, so the head norm is a d/2-lane butterfly.
-// Each thread takes up to kRopeItems items with all their loads in flight.
-constexpr int kRopeItems = 8;
-
-__device__ void rope_head_tail(int r, int M, const RopeTail& t, int nthreads) {
-  const int d = t.d, half = d >> 1;
-  const int j = threadIdx.x % half;                   // nthreads is a multiple of d/2
-  const int n_rows = t.Hq + 2 * t.Hkv;
-  const bool is_q = r < t.Hq, is_k = !is_q && r < t.Hq + t.Hkv;
-  const int n_items = M * half;
-  const double inv_freq = exp2(-double(2 * j) / double(d) * log2(double(t.theta)));
-  const float w0 = is_q ? bf2f(t.qw[j]) : (is_k ? bf2f(t.kw[j]) : 1.f);
-  const float w1 = is_q ? bf2f(t.qw[j + half]) : (is_k ? bf2f(t.kw[j + half]) : 1.f);
-  for (int base = 0; base < n_items; base += nthreads * kRopeItems) {
-    float x0[kRopeItems], x1[kRopeItems];
-    int pos[kRopeItems], wkv[kRopeItems];
-    size_t crow[kRopeItems];
-#pragma unroll
-    for (int it = 0; it < kRopeItems; ++it) {
-      const int item = base + it * nthreads + threadIdx.x;
-      const int m = item / half;
-      const bool ok = item < n_items;
-      const float* src = t.qkv32 + size_t(ok ? m : 0) * n_rows * d + size_t(r) * d;
-      x0[it] = ok ? coherent_load(src + j) : 0.f;
-      x1[it] = ok ? coherent_load(src + j + half) : 0.f;
-      const int s = ok ? find_seq(t.cu, t.n_seq, m) : 0;
-      const int i = m - t.cu[s];
-      pos[it] = t.start_pos[s] + i;
-      wkv[it] = ok && (t.causal || i < t.used_keys[s]);
-      crow[it] = size_t(t.cache_slot[s]) * t.capacity + pos[it];
-    }
-#pragma unroll
-    for (int it = 0; it < kRopeItems; ++it) {
-      const int item = base + it * nthreads + threadIdx.x;
-      const float ss = group_sum(x0[it] * x0[it] + x1[it] * x1[it], half);
-      if (item >= n_items) continue;
-      const int m = item / half;
-      if (is_q || is_k) {
-        const float inv = 1.0f / __builtin_sqrtf(ss / float(d) + t.eps);
-        const float a = x0[it] * inv * w0, b = x1[it] * inv * w1;
-        // angle p * theta^(-2j/d) in float64, reduced to [-pi, pi] before the
-        // fp32 sincos
-        const double phi = double(pos[it]) * inv_freq;
-        const double k2 = __builtin_rint(phi * 0.15915494309189535);
-        const float red = float(__builtin_fma(-k2, 6.283185307179586, phi));
-        float sn, cs;
-        sincosf(red, &sn, &cs);
-        const float y0 = a * cs - b * sn, y1 = b * cs + a * sn;
-        uint16_t* dst = is_q ? t.q_out + (size_t(m) * t.Hq + r) * d : t.kc + (crow[it] * t.Hkv + (r - t.Hq)) * d;
-        if (is_q || wkv[it]) { dst[j] = uint16_t(f2bf(y0)); dst[j + half] = uint16_t(f2bf(y1)); }
-      } else if (wkv[it]) {
-        uint16_t* dst = t.vc + (crow[it] * t.Hkv + (r - t.Hq - t.Hkv)) * d;
-        dst[j] = uint16_t(f2bf(x0[it]));
-        dst[j + half] = uint16_t(f2bf(x1[it]));
-      }
-    }
-  }
-}
 
 // value of one product element after the dtype scale
 template <bool FP8>
@@ -212,13 +104,16 @@ __device__ __forceinline__ float scaled(const EpiArgs& e, float acc, int n) {
 }
 
 // ============================================================== skinny kernel
-template <int WAVES, int MB, int EPI, bool FP8>
+// CB: 16-column blocks per workgroup (non-SwiGLU epilogues); SwiGLU always
+// takes the gate block and the matching up block
+template <int WAVES, int MB, int EPI, bool FP8, int U, int CB>
 __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, int M, int N, int K_bytes,
     EpiArgs e) {
-  constexpr int NB = (EPI == HR_EPI_SWIGLU) ? 2 : 1;   // gate and up column blocks
+  constexpr int NB = (EPI == HR_EPI_SWIGLU) ? 2 : CB;  // weight row blocks per workgroup
+  static_assert(EPI != HR_EPI_HEAD || CB == 1, "head epilogue: one column block");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int cb = blockIdx.x;                           // 16-column block
+  const int cb = blockIdx.x;
   const int g = lane >> 4, rc = lane & 15;
   // weight rows this lane streams
   int wrow[NB];
@@ -229,8 +124,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
     wok[0] = true;
     wok[NB - 1] = true;
   } else {
-    wrow[0] = cb * 16 + rc;
-    wok[0] = wrow[0] < N;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      wrow[nb] = (cb * NB + nb) * 16 + rc;
+      wok[nb] = wrow[nb] < N;
+    }
   }
   const int steps = K_bytes >> 7;                      // 128-byte K steps
   const int ksplit = gridDim.y, kz = blockIdx.y;
@@ -243,25 +141,27 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
     for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  constexpr int U = 4;
-  int s = s_lo + wave;
-  for (; s + (U - 1) * WAVES < s_hi; s += U * WAVES) {
+  // U steps of 128 bytes per wave in flight; the last batch is predicated, so
+  // a wave whose share is at most U steps issues all its loads at once
+  for (int s = s_lo + wave; s < s_hi; s += U * WAVES) {
     u32x4 bw[U][NB][2], ax[U][MB][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const size_t kb = size_t(s + u * WAVES) * 128 + g * 32;
+      const int st = s + u * WAVES;
+      const bool sok = st < s_hi;
+      const size_t kb = size_t(sok ? st : s) * 128 + g * 32;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const u32x4* p = reinterpret_cast<const u32x4*>(w + size_t(wrow[nb]) * K_bytes + kb);
-        bw[u][nb][0] = wok[nb] ? p[0] : zero;
-        bw[u][nb][1] = wok[nb] ? p[1] : zero;
+        bw[u][nb][0] = (wok[nb] && sok) ? p[0] : zero;
+        bw[u][nb][1] = (wok[nb] && sok) ? p[1] : zero;
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int row = mb * 16 + rc;
         const u32x4* p = reinterpret_cast<const u32x4*>(x + size_t(row) * K_bytes + kb);
-        ax[u][mb][0] = row < M ? p[0] : zero;
-        ax[u][mb][1] = row < M ? p[1] : zero;
+        ax[u][mb][0] = (row < M && sok) ? p[0] : zero;
+        ax[u][mb][1] = (row < M && sok) ? p[1] : zero;
       }
     }
 #pragma unroll
@@ -273,30 +173,6 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
           acc[nb][mb] = mma16<FP8>(ax[u][mb][0], bw[u][nb][0], acc[nb][mb]);
           acc[nb][mb] = mma16<FP8>(ax[u][mb][1], bw[u][nb][1], acc[nb][mb]);
         }
-  }
-  for (; s < s_hi; s += WAVES) {
-    const size_t kb = size_t(s) * 128 + g * 32;
-    u32x4 bw[NB][2], ax[MB][2];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(w + size_t(wrow[nb]) * K_bytes + kb);
-      bw[nb][0] = wok[nb] ? p[0] : zero;
-      bw[nb][1] = wok[nb] ? p[1] : zero;
-    }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int row = mb * 16 + rc;
-      const u32x4* p = reinterpret_cast<const u32x4*>(x + size_t(row) * K_bytes + kb);
-      ax[mb][0] = row < M ? p[0] : zero;
-      ax[mb][1] = row < M ? p[1] : zero;
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        acc[nb][mb] = mma16<FP8>(ax[mb][0], bw[nb][0], acc[nb][mb]);
-        acc[nb][mb] = mma16<FP8>(ax[mb][1], bw[nb][1], acc[nb][mb]);
-      }
   }
 
   // fixed-order reduction of the wavefront partials
@@ -316,8 +192,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
       v[nb] = t;
     }
     const int row = mb * 16 + 4 * (ln >> 4) + r;
-    const int col = cb * 16 + (ln & 15);
     if constexpr (EPI == HR_EPI_SWIGLU) {
+      const int col = cb * 16 + (ln & 15);
       if (row < M) {
         const float gt = scaled<FP8>(e, v[0], col);
         const float up = scaled<FP8>(e, v[NB - 1], e.F + col);
@@ -327,19 +203,21 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
         else
           static_cast<uint16_t*>(e.out)[size_t(row) * e.ldo + col] = uint16_t(f2bf(a));
       }
-    } else if (col < N) {
+    } else {
+#pragma unroll
+     for (int nb = 0; nb < NB; ++nb) {
+      const int col = (cb * NB + nb) * 16 + (ln & 15);
+      if (col >= N) continue;
       if constexpr (EPI == HR_EPI_BF16) {
         if (row < M)
           static_cast<uint16_t*>(e.out)[size_t(row) * e.ldo + col] =
-              uint16_t(f2bf(scaled<FP8>(e, v[0], col)));
+              uint16_t(f2bf(scaled<FP8>(e, v[nb], col)));
       } else if constexpr (EPI == HR_EPI_RESIDUAL) {
         if (row < M) {
           float* o = static_cast<float*>(e.out) + size_t(row) * e.ldo + col;
-          if (ksplit == 1) *o += scaled<FP8>(e, v[0], col);
-          else unsafeAtomicAdd(o, scaled<FP8>(e, v[0], col));
+          if (ksplit == 1) *o += scaled<FP8>(e, v[nb], col);
+          else unsafeAtomicAdd(o, scaled<FP8>(e, v[nb], col));
         }
-      } else if constexpr (EPI == HR_EPI_QKV_ROPE) {
-        if (row < M) coherent_store(e.rope.qkv32 + size_t(row) * e.ldo + col, scaled<FP8>(e, v[0], col));
       } else {  // HR_EPI_HEAD: fp32 logits = hi-row product + lo-row product
         if (row < e.hilo_rows) {
           const int r2 = row + e.hilo_rows;   // the lo term of the same sequence
@@ -351,14 +229,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
           static_cast<float*>(e.out)[size_t(row) * e.ldo + col] = v[0] + lo;
         }
       }
-    }
-  }
-  if constexpr (EPI == HR_EPI_QKV_ROPE) {
-    const int blocks_per_head = e.rope.d / 16;
-    const int head = cb / blocks_per_head;
-    if (last_arrival(e.counter + head, blocks_per_head * gridDim.y)) {
-      rope_head_tail(head, M, e.rope, WAVES * 64);
-      if (threadIdx.x == 0) __hip_atomic_store(e.counter + head, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+     }
     }
   }
 }
@@ -641,19 +512,36 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
 }
 
 // ============================================================== dispatch
+// 16-column blocks per workgroup for the bf16 / residual epilogues at M <= 16:
+// two blocks read each activation fragment for twice the weight rows
+constexpr int kSkinnyCB = 2;
+
+template <int EPI>
+constexpr int skinny_cb(int mb) { return (mb == 1 && (EPI == HR_EPI_BF16 || EPI == HR_EPI_RESIDUAL)) ? kSkinnyCB : 1; }
+
 template <int EPI, bool FP8>
 static void skinny(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
                    int blocks, int ksplit, hipStream_t st) {
   dim3 grid(blocks, ksplit);
   const int mb = (M + 15) / 16;
-  if (EPI == HR_EPI_SWIGLU) {
-    if (mb == 1) gemm_skinny_kernel<8, 1, EPI, FP8><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
-    else if (mb == 2) gemm_skinny_kernel<4, 2, EPI, FP8><<<grid, 256, 0, st>>>(x, w, M, N, Kb, e);
-    else gemm_skinny_kernel<4, 4, EPI, FP8><<<grid, 256, 0, st>>>(x, w, M, N, Kb, e);
+  // 128-byte steps per wave (8 waves, the largest split)
+  const int steps = Kb / 128;
+  const int spw = ((steps + ksplit - 1) / ksplit + 7) / 8;
+  constexpr int CB1 = (EPI == HR_EPI_BF16 || EPI == HR_EPI_RESIDUAL) ? kSkinnyCB : 1;
+  constexpr int NB1 = (EPI == HR_EPI_SWIGLU) ? 2 : CB1;
+  if (mb == 1) {
+    // all of a wave's steps in one batch when they fit (5 steps x NB = 1 block
+    // measured faster than 4 + 1; at NB = 2 the 5-step batch costs occupancy)
+    if (spw <= 2) gemm_skinny_kernel<8, 1, EPI, FP8, 2, CB1><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
+    else if (spw == 3) gemm_skinny_kernel<8, 1, EPI, FP8, 3, CB1><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
+    else if (spw == 5 && NB1 == 1) gemm_skinny_kernel<8, 1, EPI, FP8, 5, CB1><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
+    else gemm_skinny_kernel<8, 1, EPI, FP8, 4, CB1><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
+  } else if (EPI == HR_EPI_SWIGLU) {
+    if (mb == 2) gemm_skinny_kernel<4, 2, EPI, FP8, 4, 1><<<grid, 256, 0, st>>>(x, w, M, N, Kb, e);
+    else gemm_skinny_kernel<4, 4, EPI, FP8, 4, 1><<<grid, 256, 0, st>>>(x, w, M, N, Kb, e);
   } else {
-    if (mb == 1) gemm_skinny_kernel<8, 1, EPI, FP8><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
-    else if (mb == 2) gemm_skinny_kernel<8, 2, EPI, FP8><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
-    else gemm_skinny_kernel<4, 4, EPI, FP8><<<grid, 256, 0, st>>>(x, w, M, N, Kb, e);
+    if (mb == 2) gemm_skinny_kernel<8, 2, EPI, FP8, 4, 1><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
+    else gemm_skinny_kernel<4, 4, EPI, FP8, 4, 1><<<grid, 256, 0, st>>>(x, w, M, N, Kb, e);
   }
 }
 
@@ -741,9 +629,10 @@ void launch_linear(const void* x, const void* w, const float* w_scale, float x_s
   const uint8_t* xb = static_cast<const uint8_t*>(x);
   const uint8_t* wb = static_cast<const uint8_t*>(w);
   const int ncols = (epi == HR_EPI_SWIGLU) ? N / 2 : N;
-  const int blocks = (ncols + 15) / 16;
 #define HR_DISPATCH(EPI_)                                                                     \
   if (M <= 64) {                                                                              \
+    const int cbw = 16 * skinny_cb<EPI_>((M + 15) / 16);                                      \
+    const int blocks = (ncols + cbw - 1) / cbw;                                               \
     int ks = 1;                                                                               \
     if (EPI_ == HR_EPI_RESIDUAL && blocks < 256) ks = (512 + blocks - 1) / blocks;            \
     if (ks > Kb / 128) ks = Kb / 128;                                                         \
@@ -757,28 +646,6 @@ void launch_linear(const void* x, const void* w, const float* w_scale, float x_s
   else if (epi == HR_EPI_RESIDUAL) { HR_DISPATCH(HR_EPI_RESIDUAL) }
   else { HR_DISPATCH(HR_EPI_SWIGLU) }
 #undef HR_DISPATCH
-}
-
-// Small-M (<= 64) QKV + q/k norm + RoPE + KV write: x . W_qkv^T -> fp32
-// qkv32 -> per-head tails.
-void launch_qkv_rope(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8, int M,
-                     int N, int K, float* qkv32, int* counters, const QkvRopeParams& p, hipStream_t st) {
-  EpiArgs e{};
-  e.epi = HR_EPI_QKV_ROPE;
-  e.x_scale = x_scale;
-  e.w_scale = w_scale;
-  e.ldo = N;
-  e.counter = counters;
-  e.rope = RopeTail{qkv32, static_cast<const uint16_t*>(p.qw), static_cast<const uint16_t*>(p.kw), p.theta,
-                    p.eps, p.cu, p.start_pos, p.cache_slot, p.used_keys, p.n_seq, p.causal ? 1 : 0, p.Hq,
-                    p.Hkv, p.d, p.capacity, static_cast<uint16_t*>(p.q_out), static_cast<uint16_t*>(p.kc),
-                    static_cast<uint16_t*>(p.vc)};
-  const int Kb = fp8 ? K : 2 * K;
-  const int blocks = N / 16;
-  const uint8_t* xb = static_cast<const uint8_t*>(x);
-  const uint8_t* wb = static_cast<const uint8_t*>(w);
-  if (fp8) skinny<HR_EPI_QKV_ROPE, true>(xb, wb, M, N, Kb, e, blocks, 1, st);
-  else skinny<HR_EPI_QKV_ROPE, false>(xb, wb, M, N, Kb, e, blocks, 1, st);
 }
 
 // Head: zsplit bf16 [2n, D] (hi rows then lo rows), W bf16 [N, D] -> fp32 [n, N]

@@ -9,17 +9,7 @@
 namespace hr {
 
 constexpr int HR_EPI_HEAD = 3;        // internal: fp32 logits from hi/lo bf16 rows
-constexpr int HR_EPI_QKV_ROPE = 5;    // internal: fp32 QKV, then per-head norm + RoPE + KV write
 
-struct QkvRopeParams {
-  const void *qw, *kw;
-  float theta, eps;
-  const int32_t *cu, *start_pos, *cache_slot, *used_keys;
-  int n_seq;
-  bool causal;
-  int Hq, Hkv, d, capacity;
-  void *q_out, *kc, *vc;
-};
 
 void launch_codebook_step(int B, int K, int V, int bos, int eoc, bool f32, const void* logits,
                           int32_t* frame, uint8_t* eoc_seen, uint8_t* done, int32_t* codes,
@@ -28,10 +18,9 @@ void launch_codebook_step(int B, int K, int V, int bos, int eoc, bool f32, const
 
 void launch_embed_rmsnorm(const int32_t* ids, const void* embed, const void* x_embeds, int T, int D,
                           const void* w, float eps, float* h_out, void* x_out, bool fp8,
-                          float inv_scale, hipStream_t st, int* zero_ctr = nullptr,
-                          int n_zero = 0);
+                          float inv_scale, hipStream_t st);
 void launch_rmsnorm(const float* h, int T, int D, const void* w, float eps, void* x_out, bool fp8,
-                    float inv_scale, hipStream_t st, int* zero_ctr = nullptr, int n_zero = 0);
+                    float inv_scale, hipStream_t st);
 void launch_final_split(const float* h, const int32_t* cu, int seq0, int n, int D, const void* w,
                         float eps, int n_rows, void* zsplit, hipStream_t st);
 void launch_quant_weight(const void* w, int N, int K, uint8_t* w8, float* scale, hipStream_t st);
@@ -62,8 +51,5 @@ void launch_linear(const void* x, const void* w, const float* w_scale, float x_s
                    int M, int N, int K, int epi, void* out, float out_scale, hipStream_t st);
 void launch_head_gemm(const void* zsplit, int n, const void* w, int N, int D, float* out,
                       hipStream_t st);
-void launch_qkv_rope(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8, int M,
-                     int N, int K, float* qkv32, int* counters, const QkvRopeParams& p, hipStream_t st);
-void launch_zero_i32(int* p, int n, hipStream_t st);
 
 }  // namespace hr

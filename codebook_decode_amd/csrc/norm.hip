@@ -54,15 +54,18 @@ template <int MODE>
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
     const float* __restrict__ h_in, const int32_t* __restrict__ ids,
     const uint16_t* __restrict__ rows_bf16, float* __restrict__ h_out, int D,
-    const uint16_t* __restrict__ w, float eps, void* __restrict__ x_out, int fp8, float inv_scale,
-    int* __restrict__ zero_ctr, int n_zero) {
+    const uint16_t* __restrict__ w, float eps, void* __restrict__ x_out, int fp8, float inv_scale) {
   __shared__ float red[kNormThreads / 64];
   const int t = blockIdx.x;
   const int n8 = D >> 3;
-  // the first kernel of a layer call clears the arrival counters of the fused
-  // projections that follow it on the stream
-  if (t == 0)
-    for (int i = threadIdx.x; i < n_zero; i += kNormThreads) zero_ctr[i] = 0;
+  // the norm weights are requested first: they are not on the path that waits
+  // for the row's sum of squares
+  u32x4 wq[kNormMaxPerThread];
+#pragma unroll
+  for (int c = 0; c < kNormMaxPerThread; ++c) {
+    const int i8 = threadIdx.x + c * kNormThreads;
+    wq[c] = i8 < n8 ? reinterpret_cast<const u32x4*>(w)[i8] : u32x4{0u, 0u, 0u, 0u};
+  }
   float v[kNormMaxPerThread][8];
   float ss = 0.f;
   const uint16_t* src16 = nullptr;
@@ -95,12 +98,11 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
   for (int c = 0; c < kNormMaxPerThread; ++c) {
     int i8 = threadIdx.x + c * kNormThreads;
     if (i8 < n8) {
-      u32x4 wq = reinterpret_cast<const u32x4*>(w)[i8];
       float y[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        y[2 * j] = v[c][2 * j] * r * bf_lo(wq[j]);
-        y[2 * j + 1] = v[c][2 * j + 1] * r * bf_hi(wq[j]);
+        y[2 * j] = v[c][2 * j] * r * bf_lo(wq[c][j]);
+        y[2 * j + 1] = v[c][2 * j + 1] * r * bf_hi(wq[c][j]);
       }
       store_x8(x_out, size_t(t) * n8 + i8, y, fp8 != 0, inv_scale);
     }
@@ -173,29 +175,22 @@ __global__ __launch_bounds__(kNormThreads) void quant_weight_kernel(
 
 void launch_embed_rmsnorm(const int32_t* ids, const void* embed, const void* x_embeds, int T, int D,
                           const void* w, float eps, float* h_out, void* x_out, bool fp8,
-                          float inv_scale, hipStream_t st, int* zero_ctr, int n_zero) {
+                          float inv_scale, hipStream_t st) {
   const uint16_t* w16 = static_cast<const uint16_t*>(w);
   if (ids)
     rmsnorm_kernel<1><<<T, kNormThreads, 0, st>>>(nullptr, ids, static_cast<const uint16_t*>(embed),
-                                                  h_out, D, w16, eps, x_out, fp8, inv_scale, zero_ctr,
-                                                  n_zero);
+                                                  h_out, D, w16, eps, x_out, fp8, inv_scale);
   else
     rmsnorm_kernel<2><<<T, kNormThreads, 0, st>>>(nullptr, nullptr,
                                                   static_cast<const uint16_t*>(x_embeds), h_out, D,
-                                                  w16, eps, x_out, fp8, inv_scale, zero_ctr, n_zero);
+                                                  w16, eps, x_out, fp8, inv_scale);
 }
-
-__global__ void zero_i32_kernel(int* __restrict__ p, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
-}
-
-void launch_zero_i32(int* p, int n, hipStream_t st) { zero_i32_kernel<<<1, 256, 0, st>>>(p, n); }
 
 void launch_rmsnorm(const float* h, int T, int D, const void* w, float eps, void* x_out, bool fp8,
-                    float inv_scale, hipStream_t st, int* zero_ctr, int n_zero) {
+                    float inv_scale, hipStream_t st) {
   rmsnorm_kernel<0><<<T, kNormThreads, 0, st>>>(h, nullptr, nullptr, nullptr, D,
                                                 static_cast<const uint16_t*>(w), eps, x_out, fp8,
-                                                inv_scale, zero_ctr, n_zero);
+                                                inv_scale);
 }
 
 void launch_final_split(const float* h, const int32_t* cu, int seq0, int n, int D, const void* w,

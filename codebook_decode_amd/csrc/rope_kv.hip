@@ -5,7 +5,8 @@
 // the same over both halves of head_dim, so pair (m, m + d/2) turns together)
 // and `run` (split the merged QKV rows, rotate, write the cache).
 //
-// A workgroup of 256 threads takes kRopeTok tokens.  First the per-token angle
+// A workgroup of 256 threads takes tpb <= kRopeTok tokens (1 for small
+// batches, so the rows of a 13-token prompt spread over 13 workgroups).  First the per-token angle
 // tables: p * theta^(-2m/d) for m < d/2, the frequency and the angle in
 // float64, reduced to [-pi, pi] in float64, its sine and cosine taken in fp32,
 // kept in LDS.  Then every head row of those tokens is handled by d/16 lanes, lane c
@@ -29,13 +30,20 @@ __device__ __forceinline__ float bf_at(const u32x4& v, int i) {   // element i <
 }
 
 // theta^(-2m/d), m < d/2, in float64: computed once on the host per launch and
-// passed by value (kernel argument memory), so no workgroup spends time on it
+// passed by value (kernel-argument memory), so no workgroup spends time on it
 struct RopeFreq {
   double inv[64];
 };
 
+static RopeFreq rope_freq(int d, float theta) {
+  RopeFreq f{};
+  for (int m = 0; m < d / 2 && m < 64; ++m)
+    f.inv[m] = std::exp2(-double(2 * m) / double(d) * std::log2(double(theta)));
+  return f;
+}
+
 __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
-    const uint16_t* __restrict__ qkv, int T, int Hq, int Hkv, int d, const RopeFreq freq, float eps,
+    const uint16_t* __restrict__ qkv, int T, int tpb, int Hq, int Hkv, int d, const RopeFreq freq, float eps,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ start_pos,
     const int32_t* __restrict__ cache_slot, const int32_t* __restrict__ used_keys, int n_seq,
     int causal, const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
@@ -45,10 +53,42 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
   __shared__ long long s_crow[kRopeTok];     // cache row (slot * capacity + position)
   __shared__ int s_wkv[kRopeTok];
   const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * kRopeTok;
-  const int nt = min(kRopeTok, T - t0);
+  const int t0 = blockIdx.x * tpb;
+  const int nt = min(tpb, T - t0);
   const int half = d >> 1;
   const int n_rows = Hq + 2 * Hkv;
+
+  const int L = d >> 4;                       // lanes per head row
+  const int c = tid % L;                      // this lane's 8-pair chunk
+  const int per_round = 256 / L;
+  const int total = nt * n_rows;
+  const int step = per_round * kRopeRows;
+
+  // head rows of one round of kRopeRows x per_round rows
+  u32x4 lo[kRopeRows], hi[kRopeRows];
+  auto load_round = [&](int base) {
+#pragma unroll
+    for (int k = 0; k < kRopeRows; ++k) {
+      const int rr = base + k * per_round;
+      if (rr < total) {
+        const int tt = rr / n_rows, r = rr % n_rows;
+        const uint16_t* src = qkv + size_t(t0 + tt) * n_rows * d + size_t(r) * d;
+        lo[k] = *reinterpret_cast<const u32x4*>(src + 8 * c);
+        hi[k] = *reinterpret_cast<const u32x4*>(src + half + 8 * c);
+      } else {
+        lo[k] = u32x4{0u, 0u, 0u, 0u};
+        hi[k] = lo[k];
+      }
+    }
+  };
+  // the first round's rows and this lane's norm weights are requested before
+  // the tables are built, so their latency overlaps the tables'
+  int base = tid / L;
+  load_round(base);
+  const u32x4 wq0 = *reinterpret_cast<const u32x4*>(qw + 8 * c);
+  const u32x4 wq1 = *reinterpret_cast<const u32x4*>(qw + half + 8 * c);
+  const u32x4 wk0 = *reinterpret_cast<const u32x4*>(kw + 8 * c);
+  const u32x4 wk1 = *reinterpret_cast<const u32x4*>(kw + half + 8 * c);
 
   // token positions, cache rows, whether K/V are written
   if (tid < nt) {
@@ -75,31 +115,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
   }
   __syncthreads();
 
-  const int L = d >> 4;                       // lanes per head row
-  const int c = tid % L;                      // this lane's 8-pair chunk
-  const int per_round = 256 / L;
-  const int total = nt * n_rows;
-  // this lane's norm weights (chunk c of each half), bf16 pairs
-  const u32x4 wq0 = *reinterpret_cast<const u32x4*>(qw + 8 * c);
-  const u32x4 wq1 = *reinterpret_cast<const u32x4*>(qw + half + 8 * c);
-  const u32x4 wk0 = *reinterpret_cast<const u32x4*>(kw + 8 * c);
-  const u32x4 wk1 = *reinterpret_cast<const u32x4*>(kw + half + 8 * c);
-
-  for (int base = tid / L; base < total; base += per_round * kRopeRows) {
-    u32x4 lo[kRopeRows], hi[kRopeRows];
-#pragma unroll
-    for (int k = 0; k < kRopeRows; ++k) {
-      const int rr = base + k * per_round;
-      if (rr < total) {
-        const int tt = rr / n_rows, r = rr % n_rows;
-        const uint16_t* src = qkv + size_t(t0 + tt) * n_rows * d + size_t(r) * d;
-        lo[k] = *reinterpret_cast<const u32x4*>(src + 8 * c);
-        hi[k] = *reinterpret_cast<const u32x4*>(src + half + 8 * c);
-      } else {
-        lo[k] = u32x4{0u, 0u, 0u, 0u};
-        hi[k] = lo[k];
-      }
-    }
+  for (; base < total; base += step) {
+    if (base != tid / L) load_round(base);
 #pragma unroll
     for (int k = 0; k < kRopeRows; ++k) {
       const int rr = base + k * per_round;
@@ -151,11 +168,13 @@ void launch_qknorm_rope_kv(const void* qkv, int T, int Hq, int Hkv, int d, float
                            const int32_t* used_keys, int n_seq, bool causal, const void* qw,
                            const void* kw, void* q_out, void* kc, void* vc, int capacity,
                            hipStream_t st) {
-  const int blocks = (T + kRopeTok - 1) / kRopeTok;
-  RopeFreq freq;
-  for (int m = 0; m < d / 2; ++m) freq.inv[m] = std::exp2(-double(2 * m) / double(d) * std::log2(double(theta)));
+  // tokens per workgroup: 1 below 512 tokens (latency: every row in flight
+  // at once), up to kRopeTok for large batches (fewer angle tables)
+  const int tpb = T < 512 ? 1 : (T < 1024 ? 2 : kRopeTok);
+  const int blocks = (T + tpb - 1) / tpb;
+  const RopeFreq freq = rope_freq(d, theta);
   qknorm_rope_kv_kernel<<<blocks, 256, 0, st>>>(
-      static_cast<const uint16_t*>(qkv), T, Hq, Hkv, d, freq, eps, cu, start_pos, cache_slot,
+      static_cast<const uint16_t*>(qkv), T, tpb, Hq, Hkv, d, freq, eps, cu, start_pos, cache_slot,
       used_keys, n_seq, causal ? 1 : 0, static_cast<const uint16_t*>(qw),
       static_cast<const uint16_t*>(kw), static_cast<uint16_t*>(q_out), static_cast<uint16_t*>(kc),
       static_cast<uint16_t*>(vc), capacity);

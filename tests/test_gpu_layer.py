@@ -148,7 +148,7 @@ def test_layer_prefill_then_continuation(H):
 FP8_CASES = [
     # name, used rows P, rows, causal
     ("fp8_p512_pad544_noncausal", 512, 544, False),   # tiled GEMMs
-    ("fp8_p40_pad48_noncausal", 40, 48, False),       # fused small-batch projections
+    ("fp8_p40_pad48_noncausal", 40, 48, False),       # small-batch (skinny) projections
     ("fp8_p13_causal", 13, 13, True),
 ]
 

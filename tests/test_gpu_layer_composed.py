@@ -1,15 +1,13 @@
-"""The fused small-batch layer path (T <= 64) against the same layer composed
-from the step-level entry points (one kernel per step).
+"""hr_prefill_layer / hr_prefill_stack at small batches against the same layer
+composed from the step-level entry points of include/hr_ops.h (one call per
+step), on new tokens every repetition.
 
-On the fused path the QKV projection keeps its product in fp32 and its last
-workgroup per head applies the q/k norm, RoPE and cache write (values cross
-workgroups inside one kernel).  A missed hand-off (a workgroup reading a value
-before another one's write is visible) reads the previous call's data, so
-every repetition here uses new inputs: a stale read then shows up as an O(1)
-difference.  The two paths round at different points (the composed one
-rounds QKV to bf16), so they are two samples of the bf16 storage noise, whose
-distance from the exact layer is 0.038-0.049 on this layer: the bar is
-cosine >= 0.9999 and max |diff| <= 0.1 per layer.
+Both run the same kernels; the residual projections add split-K partials into
+h with fp32 atomics, whose order varies, so the two are two samples of the
+bf16/fp32 rounding noise (0.04-0.05 from the exact layer on this layer): the
+bar is cosine >= 0.9999 and max |diff| <= 0.1 per layer.  A layer call that
+skipped, reordered or mis-addressed a step (a stale workspace region, a cache
+row written to the wrong slot) shows up as an O(1) difference.
 """
 import numpy as np
 import pytest
@@ -18,7 +16,7 @@ import synth
 
 pytestmark = pytest.mark.gpu
 
-REPS = 10
+REPS = 3
 
 
 @pytest.fixture(scope="module")
@@ -36,7 +34,7 @@ def layers(H):
 
 
 def composed_layer(H, m, dims, batch, dl, h, kv, T):
-    """One layer from the step-level entries (no fused hand-offs)."""
+    """One layer from the step-level entries."""
     import torch
     D, F, A, NQKV = m.hidden, m.ffn, m.attn_width, m.qkv_rows
     bf = dict(dtype=torch.bfloat16, device="cuda")
@@ -61,7 +59,7 @@ def close(name, got, ref, n_layers=1):
 
 
 @pytest.mark.parametrize("T", [1, 13, 40, 64])
-def test_fused_layer_matches_composed_steps(H, layers, T):
+def test_layer_matches_composed_steps(H, layers, T):
     """hr_prefill_layer at T tokens (one sequence), REPS times on new tokens."""
     import torch
     from gpu_util import bits_of, dev, log
@@ -73,7 +71,7 @@ def test_fused_layer_matches_composed_steps(H, layers, T):
     b = H.Batch([0, T], [0], [0])
     ws = workspace(H, dims, H.HR_BF16, T)
     for r in range(REPS):
-        log(f"fused layer T={T} repetition {r}")
+        log(f"layer T={T} repetition {r}")
         ids = synth.prompt_ids(m, T, seq=100 + r)
         h0 = synth.embed_rows(m, ids)
         h_init = synth.bf16_bits_to_f32(h0)
@@ -89,7 +87,7 @@ def test_fused_layer_matches_composed_steps(H, layers, T):
         assert np.all(bits_of(kf)[T:] == 0x7FC0), "stray cache write"
 
 
-def test_fused_stack_two_layers_matches_composed_steps(H, layers):
+def test_stack_two_layers_matches_composed_steps(H, layers):
     """hr_prefill_stack over two layers at 13 tokens, REPS times."""
     import torch
     from gpu_util import dev, dev_bf16, log
@@ -103,7 +101,7 @@ def test_fused_stack_two_layers_matches_composed_steps(H, layers):
     ws = workspace(H, dims, H.HR_BF16, T)
     dims1 = dims_of(H, m, True, 1)
     for r in range(REPS):
-        log(f"fused 2-layer stack repetition {r}")
+        log(f"2-layer stack repetition {r}")
         ids = synth.prompt_ids(m, T, seq=200 + r)
         h = torch.empty((T, m.hidden), dtype=torch.float32, device="cuda")
         caches = [kv_cache(m, 1, cap) for _ in range(2)]
