@@ -236,24 +236,27 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
 
 // ============================================================== tiled kernel
 // BM x BN output tile per workgroup of WM x WN wavefronts; each wavefront owns a
-// (BM/WM) x (BN/WN) sub-tile of 16x16 MFMA blocks.  K advances in 64-byte slabs
-// (32 bf16 or 64 e4m3 values) copied global -> LDS directly
-// (global_load_lds_dwordx4: lane i of a wave writes 16 B at LDS base + 16 i)
-// through a ring of STAGES slabs.  A slab holds BM rows of A and BN rows of B,
-// 64 bytes each; 16-byte chunk c of row r sits at LDS chunk c ^ ((r >> 1) & 3),
-// so the 8 lanes of one ds_read_b128 phase (8 rows, one logical chunk) hit 8
-// distinct 16-byte bank groups (measured: zero bank conflicts).  The swizzle is
-// applied on the global side: each lane fetches the chunk its LDS slot must
-// hold.  One barrier per slab: after it every wave's copies of slab s have
+// (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.  K advances in 64-byte slabs
+// (32 bf16 or 64 e4m3 values; 128-byte slabs for some small-M shapes) copied
+// global -> LDS directly (global_load_lds_dwordx4: lane i of a wave writes 16 B
+// at LDS base + 16 i) through a ring of STAGES slabs.  A slab holds BM rows of
+// A and BN rows of B; the 16-byte chunks of a row are XOR-swizzled (swz below)
+// so that every 16-lane phase of a fragment read hits 16 distinct bank groups
+// (SQ_LDS_BANK_CONFLICT reads 0).  The swizzle is applied on the global side:
+// each lane fetches the chunk its LDS slot must hold.  One barrier per slab:
+// after it every wave's copies of slab s have
 // landed and every wave is done with slab s-1, whose slot is refilled with slab
 // s+STAGES-1.
-// LDS chunk swizzle for slabs of SB bytes per row: 64-byte rows pair up in a
-// 128-byte bank line, so chunk c of row r sits at c ^ ((r >> 1) & 3); 128-byte
-// rows fill the bank line alone: c ^ (r & 7).
+// LDS chunk swizzle for slabs of SB bytes per row.  gfx950's LDS has 64 banks
+// of 4 bytes (a 256-byte bank line) and serves a ds_read_b128 16 lanes at a
+// time; the 16 lanes of one phase read one logical chunk of 16 consecutive
+// rows, so those must fall in 16 distinct 16-byte bank groups.  64-byte rows
+// (4 to a bank line) put chunk c of row r at c ^ ((r >> 2) & 3); 128-byte rows
+// (2 to a bank line) at c ^ ((r >> 1) & 7).
 template <int SB>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (SB == 64) return (row >> 1) & 3;
-  else return row & 7;
+  if constexpr (SB == 64) return (row >> 2) & 3;
+  else return (row >> 1) & 7;
 }
 
 __device__ __forceinline__ void lds_copy16(const uint8_t* g, uint8_t* lds_base) {
