@@ -271,6 +271,43 @@ def varlen_batch(H, m, layers, shared, reps=3):
             "ms": round(sec * 1e3, 3), "tok_s": round(T / sec, 1)}
 
 
+def decode_steps(H, m, dev_layers, layers, shared, B, cached, reps=5):
+    """One batched decode step (hr_decode_step: the 36-layer stack over one new
+    row per stream at position `cached`, the head, the codebook step), B
+    streams whose caches hold `cached` rows (zeros: the values do not change
+    the work).  HBM floor: the weights + head once, plus every stream's K/V
+    rows of every layer."""
+    import torch
+    from gpu_util import dev
+    from model_util import dims_of
+    K, V, D = m.n_codebooks, m.cb_vocab, m.hidden
+    cap = cached + 64
+    dims = dims_of(H, m, True, len(layers))
+    kvt = [(torch.zeros((B * cap, m.n_kv_heads, m.head_dim), dtype=torch.bfloat16, device="cuda"),
+            torch.zeros((B * cap, m.n_kv_heads, m.head_dim), dtype=torch.bfloat16, device="cuda"))
+           for _ in layers]
+    kvs = [H.make_kv(k, v, cap, B) for k, v in kvt]
+    b = H.Batch(np.arange(B + 1), [cached] * B, np.arange(B))
+    emb = (torch.randn((B, D), device="cuda") * 0.02).to(torch.bfloat16)
+    logits = torch.empty((B, K * V), dtype=torch.float32, device="cuda")
+    frame = dev(np.full(B, 20, np.int32))
+    seen, done = torch.zeros((B, K), dtype=torch.uint8, device="cuda"), torch.zeros(B, dtype=torch.uint8,
+                                                                                      device="cuda")
+    codes = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    ws = torch.empty(H.hr_decode_workspace_bytes(dims, H.HR_BF16, B), dtype=torch.uint8, device="cuda")
+
+    def call():
+        H.hr_decode_step(dims, layers, b, emb, kvs, shared["final"], shared["head"], K, V, m.bos_id, m.eoc_id,
+                         logits, frame, seen, done, codes, None, 0, shared["cb"], emb, ws)
+    sec = time_events(call, reps, warm=1)
+    kv_bytes = len(layers) * B * (cached + 1) * m.n_kv_heads * m.head_dim * 2 * 2
+    weight_bytes = sum(sum(t.numel() * t.element_size() for t in dl.values()) for dl in dev_layers)
+    bytes_ = weight_bytes + K * V * D * 2 + kv_bytes
+    del kvt
+    return {"B": B, "cached_rows": cached, "ms_per_step": round(sec * 1e3, 4),
+            "frames_per_s": round(B / sec, 1), "bytes": int(bytes_), "roofline": hbm(bytes_, sec)}
+
+
 def codebook_steps(H, m, shared, B=64, reps=100):
     """The delayed-codebook step at B streams, 8 x 1026, bf16 logits."""
     import torch
@@ -447,6 +484,9 @@ def main():
         out["fp8_layer"] = fp8_layer(H, m, dev_layers[0])
         out["varlen32"] = varlen_batch(H, m, layers, shared)
         out["codebook_b64"] = codebook_steps(H, m, shared)
+        log("timing decode steps (B=64 over 512 cached rows, B=1 over 2047)")
+        out["decode_b64"] = decode_steps(H, m, dev_layers, layers, shared, 64, 512)
+        out["decode_b1"] = decode_steps(H, m, dev_layers, layers, shared, 1, 2047)
         out["hbm_sweep"] = hbm_sweep(H, m, shared)
         torch.cuda.synchronize()
     if not args.no_cpu:

@@ -146,7 +146,14 @@ hr_status check_layer(const hr_dims* d, const hr_layer* L, int idx) {
 
 struct Ws {
   uint8_t *x, *qkv, *q, *attn, *act, *head;
+  float *part_o, *part_ml;   // key-chunk partials of the split attention (null: no split)
 };
+
+// Batches of up to kAttnSplitT rows may split long attention rows into key
+// chunks (decode steps and short continuations of long cached prefixes).
+constexpr int kAttnSplitT = 256;
+constexpr int kAttnSlots = 8;      // key chunks per query block at most
+constexpr int kAttnChunk = 4;      // 64-key tiles per chunk at least
 
 size_t ws_layout(const hr_dims* d, int32_t T, Ws* w, uint8_t* base) {
   const size_t D = d->hidden, F = d->ffn, A = size_t(d->n_q_heads) * d->head_dim;
@@ -165,8 +172,43 @@ size_t ws_layout(const hr_dims* d, int32_t T, Ws* w, uint8_t* base) {
   tmp.attn = take(t * A * 2);
   tmp.act = take(t * F * 2);
   tmp.head = take(size_t(64) * D * 2);
+  tmp.part_o = tmp.part_ml = nullptr;
+  if (t > 0 && t <= size_t(kAttnSplitT)) {
+    tmp.part_o = reinterpret_cast<float*>(take(size_t(kAttnSlots) * t * A * 4));
+    tmp.part_ml = reinterpret_cast<float*>(take(size_t(kAttnSlots) * t * d->n_q_heads * 8));
+  }
   if (w) *w = tmp;
   return off;
+}
+
+// Split attention rows into key chunks when the unsplit grid (query blocks x
+// kv heads x sequences) leaves most CUs idle and the longest row spans at least
+// 2 chunks: a decode step of a few streams over long caches, or a short
+// continuation.  Row lengths come from the host mirrors of the batch.
+// Measured (8 kv heads x 128): one query after 2040 cached keys 54.8 -> 23.9
+// us, 13 queries after 2000 keys 55.1 -> 26.0 us (4-tile chunks); a prefill
+// from position 0 or a decode step of 64 streams is faster unsplit.
+hr::AttnSplit attn_split(const hr_dims* d, const hr_batch* b, const Ws& w) {
+  hr::AttnSplit sp;
+  if (!w.part_o) return sp;
+  const int qpw = hr::attention_qpw(d->n_q_heads, d->n_kv_heads);
+  long long wgs = 0;
+  int max_keys = 0;
+  for (int s = 0; s < b->n_seq; ++s) {
+    const int len = b->h_cu_seqlens[s + 1] - b->h_cu_seqlens[s];
+    wgs += (long long)((len + qpw - 1) / qpw) * d->n_kv_heads;
+    const int keys = d->causal ? b->h_start_pos[s] + len : b->h_used_keys[s];
+    if (keys > max_keys) max_keys = keys;
+  }
+  const int max_tiles = (max_keys + 63) / 64;
+  if (wgs >= 128 || max_tiles < 2 * kAttnChunk) return sp;
+  sp.chunk_tiles = kAttnChunk;
+  const int want = (max_tiles + kAttnChunk - 1) / kAttnChunk;
+  sp.n_slots = want < kAttnSlots ? want : kAttnSlots;
+  sp.part_o = w.part_o;
+  sp.part_ml = w.part_ml;
+  sp.T = b->total_tokens;
+  return sp;
 }
 
 // one layer's kernels over buffers already validated.  `x_ready`: w.x already
@@ -176,6 +218,7 @@ hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_batch* b, floa
   const int T = b->total_tokens, D = d->hidden, F = d->ffn, Hq = d->n_q_heads, Hkv = d->n_kv_heads;
   const int dh = d->head_dim, A = Hq * dh, NQKV = (Hq + 2 * Hkv) * dh;
   const bool fp8 = L->wtype == HR_FP8_E4M3;
+  const hr::AttnSplit split = attn_split(d, b, w);
   if (!x_ready)
     hr::launch_rmsnorm(h, T, D, L->in_norm_w, d->rms_eps, w.x, fp8, fp8 ? 1.0f / L->as_qkv : 1.f, st);
   hr::launch_linear(w.x, L->w_qkv, L->ws_qkv, L->as_qkv, fp8, T, NQKV, D, HR_EPI_BF16, w.qkv, 0.f, st);
@@ -184,7 +227,7 @@ hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_batch* b, floa
                             w.q, kv->k, kv->v, kv->capacity, st);
   hr::launch_attention(w.q, kv->k, kv->v, b->cu_seqlens, b->start_pos, b->cache_slot, b->used_keys, b->n_seq,
                        b->max_seqlen, Hq, Hkv, dh, kv->capacity, d->causal != 0, w.attn, fp8,
-                       fp8 ? 1.0f / L->as_o : 1.f, st);
+                       fp8 ? 1.0f / L->as_o : 1.f, st, &split);
   hr::launch_linear(w.attn, L->w_o, L->ws_o, L->as_o, fp8, T, D, A, HR_EPI_RESIDUAL, h, 0.f, st);
   hr::launch_rmsnorm(h, T, D, L->post_norm_w, d->rms_eps, w.x, fp8, fp8 ? 1.0f / L->as_gu : 1.f, st);
   hr::launch_linear(w.x, L->w_gu, L->ws_gu, L->as_gu, fp8, T, 2 * F, D, HR_EPI_SWIGLU, w.act,
@@ -232,11 +275,15 @@ hr_status hr_prefill_layer(const hr_dims* dims, const hr_layer* layer, const hr_
   return run_layer(dims, layer, batch, h, kv, w, false, stream);
 }
 
-hr_status hr_prefill_stack(const hr_dims* dims, const hr_layer* layers, const hr_batch* batch,
-                           const int32_t* ids, const void* embed, int32_t vocab, const void* x_embeds,
-                           const hr_kv* kv, const void* final_norm_w, const void* head_w,
-                           int32_t n_codebooks, int32_t cb_vocab, float* h_out, float* logits_out,
-                           void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// every check of hr_prefill_stack, before anything is launched
+hr_status check_stack(const hr_dims* dims, const hr_layer* layers, const hr_batch* batch, const int32_t* ids,
+                      const void* embed, int32_t vocab, const void* x_embeds, const hr_kv* kv,
+                      const void* final_norm_w, const void* head_w, int32_t n_codebooks, int32_t cb_vocab,
+                      const float* logits_out) {
   HR_TRY(check_dims(dims));
   if (dims->n_layers <= 0) return fail(HR_EINVAL, "n_layers must be > 0");
   if (!layers || !kv) return fail(HR_EINVAL, "layers and kv arrays are required");
@@ -253,10 +300,9 @@ hr_status hr_prefill_stack(const hr_dims* dims, const hr_layer* layers, const hr
     HR_TRY(need(x_embeds, "x_embeds (ids is NULL)"));
   }
   HR_TRY(need(final_norm_w, "final_norm_w"));
-  const bool want_head = head_w != nullptr && logits_out != nullptr;
   if ((head_w != nullptr) != (logits_out != nullptr))
     return fail(HR_EINVAL, "head_w and logits_out must both be given or both NULL");
-  if (want_head) {
+  if (head_w) {
     HR_TRY(need(head_w, "head_w"));
     HR_TRY(need(logits_out, "logits_out"));
     if (n_codebooks <= 0 || cb_vocab <= 0) return fail(HR_EINVAL, "n_codebooks and cb_vocab must be > 0");
@@ -264,13 +310,14 @@ hr_status hr_prefill_stack(const hr_dims* dims, const hr_layer* layers, const hr
       if (batch->h_cu_seqlens[s + 1] <= batch->h_cu_seqlens[s])
         return fail(HR_EINVAL, "sequence %d is empty: no last row for the head", s);
   }
-  if (batch->total_tokens == 0) return HR_OK;
-  HR_TRY(need(h_out, "h_out"));
-  HR_TRY(need(ws, "ws"));
-  const size_t need_ws = ws_layout(dims, batch->total_tokens, nullptr, nullptr);
-  if (ws_bytes < need_ws) return fail(HR_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need_ws);
-  Ws w;
-  ws_layout(dims, batch->total_tokens, &w, static_cast<uint8_t*>(ws));
+  return HR_OK;
+}
+
+// the stack's kernels over validated arguments and a laid-out workspace
+hr_status enqueue_stack(const hr_dims* dims, const hr_layer* layers, const hr_batch* batch, const int32_t* ids,
+                        const void* embed, const void* x_embeds, const hr_kv* kv, const void* final_norm_w,
+                        const void* head_w, int32_t n_codebooks, int32_t cb_vocab, float* h_out,
+                        float* logits_out, const Ws& w, hipStream_t stream) {
   const int T = batch->total_tokens, D = dims->hidden;
   const hr_layer& L0 = layers[0];
   const bool fp8 = L0.wtype == HR_FP8_E4M3;
@@ -278,16 +325,17 @@ hr_status hr_prefill_stack(const hr_dims* dims, const hr_layer* layers, const hr
                            fp8 ? 1.0f / L0.as_qkv : 1.f, stream);
   for (int l = 0; l < dims->n_layers; ++l)
     HR_TRY(run_layer(dims, &layers[l], batch, h_out, &kv[l], w, l == 0, stream));
-  if (want_head)
+  if (head_w)
     HR_TRY(run_head(h_out, batch, D, final_norm_w, dims->rms_eps, head_w, n_codebooks, cb_vocab, logits_out,
                     w.head, stream));
   return check_launch("prefill stack");
 }
 
-hr_status hr_codebook_step(int32_t B, int32_t K, int32_t V, int32_t bos_id, int32_t eoc_id,
-                           int32_t logits_is_fp32, const void* logits, int32_t* frame, uint8_t* eoc_seen,
-                           uint8_t* done, int32_t* codes, int32_t* aligned, int32_t max_frames,
-                           const void* cb_embed, int32_t D, void* emb_out, hipStream_t stream) {
+// every check of hr_codebook_step
+hr_status check_codebook(int32_t B, int32_t K, int32_t V, int32_t bos_id, int32_t eoc_id, const void* logits,
+                         const int32_t* frame, const uint8_t* eoc_seen, const uint8_t* done, const int32_t* codes,
+                         const int32_t* aligned, int32_t max_frames, const void* cb_embed, int32_t D,
+                         const void* emb_out) {
   if (B < 0 || K <= 0 || V < 2 || D <= 0) return fail(HR_EINVAL, "bad sizes B=%d K=%d V=%d D=%d", B, K, V, D);
   if (K > 1024) return fail(HR_EUNSUPPORTED, "K = %d > 1024 codebooks", K);
   if (D % 8) return fail(HR_EINVAL, "D = %d is not a multiple of 8", D);
@@ -298,6 +346,84 @@ hr_status hr_codebook_step(int32_t B, int32_t K, int32_t V, int32_t bos_id, int3
   if (aligned && max_frames <= 0) return fail(HR_EINVAL, "max_frames must be > 0 when aligned is given");
   HR_TRY(need(cb_embed, "cb_embed"));
   HR_TRY(need(emb_out, "emb_out"));
+  return HR_OK;
+}
+
+// decode workspace: the prefill workspace of B rows, then h fp32 [B, D]
+size_t decode_ws_layout(const hr_dims* d, int32_t B, Ws* w, float** h, uint8_t* base) {
+  const size_t off = ws_layout(d, B, w, base);
+  if (h) *h = base ? reinterpret_cast<float*>(base + off) : nullptr;
+  return off + up256(size_t(B) * d->hidden * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+hr_status hr_prefill_stack(const hr_dims* dims, const hr_layer* layers, const hr_batch* batch,
+                           const int32_t* ids, const void* embed, int32_t vocab, const void* x_embeds,
+                           const hr_kv* kv, const void* final_norm_w, const void* head_w,
+                           int32_t n_codebooks, int32_t cb_vocab, float* h_out, float* logits_out,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  HR_TRY(check_stack(dims, layers, batch, ids, embed, vocab, x_embeds, kv, final_norm_w, head_w, n_codebooks,
+                     cb_vocab, logits_out));
+  if (batch->total_tokens == 0) return HR_OK;
+  HR_TRY(need(h_out, "h_out"));
+  HR_TRY(need(ws, "ws"));
+  const size_t need_ws = ws_layout(dims, batch->total_tokens, nullptr, nullptr);
+  if (ws_bytes < need_ws) return fail(HR_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need_ws);
+  Ws w;
+  ws_layout(dims, batch->total_tokens, &w, static_cast<uint8_t*>(ws));
+  return enqueue_stack(dims, layers, batch, ids, embed, x_embeds, kv, final_norm_w, head_w, n_codebooks, cb_vocab,
+                       h_out, logits_out, w, stream);
+}
+
+size_t hr_decode_workspace_bytes(const hr_dims* dims, hr_wtype wtype, int32_t B) {
+  (void)wtype;
+  if (!dims || B < 0) return 0;
+  return decode_ws_layout(dims, B, nullptr, nullptr, nullptr);
+}
+
+hr_status hr_decode_step(const hr_dims* dims, const hr_layer* layers, const hr_batch* batch, const void* x_embeds,
+                         const hr_kv* kv, const void* final_norm_w, const void* head_w, int32_t n_codebooks,
+                         int32_t cb_vocab, int32_t bos_id, int32_t eoc_id, float* logits_out, int32_t* frame,
+                         uint8_t* eoc_seen, uint8_t* done, int32_t* codes, int32_t* aligned, int32_t max_frames,
+                         const void* cb_embed, void* emb_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!dims) return fail(HR_EINVAL, "dims is NULL");
+  if (!dims->causal) return fail(HR_EUNSUPPORTED, "a decode step attends causally (dims->causal = 0)");
+  if (!batch) return fail(HR_EINVAL, "batch is NULL");
+  if (!head_w || !logits_out) return fail(HR_EINVAL, "a decode step needs head_w and logits_out");
+  HR_TRY(check_stack(dims, layers, batch, nullptr, nullptr, 0, x_embeds, kv, final_norm_w, head_w, n_codebooks,
+                     cb_vocab, logits_out));
+  const int B = batch->n_seq;
+  if (batch->total_tokens != B)
+    return fail(HR_EINVAL, "a decode step takes one row per stream (total_tokens %d, n_seq %d)",
+                batch->total_tokens, B);
+  for (int s = 0; s < B; ++s)
+    if (batch->h_cu_seqlens[s + 1] - batch->h_cu_seqlens[s] != 1)
+      return fail(HR_EINVAL, "stream %d has %d rows; a decode step takes one", s,
+                  batch->h_cu_seqlens[s + 1] - batch->h_cu_seqlens[s]);
+  HR_TRY(check_codebook(B, n_codebooks, cb_vocab, bos_id, eoc_id, logits_out, frame, eoc_seen, done, codes,
+                        aligned, max_frames, cb_embed, dims->hidden, emb_out));
+  HR_TRY(need(ws, "ws"));
+  const size_t need_ws = decode_ws_layout(dims, B, nullptr, nullptr, nullptr);
+  if (ws_bytes < need_ws) return fail(HR_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need_ws);
+  Ws w;
+  float* h = nullptr;
+  decode_ws_layout(dims, B, &w, &h, static_cast<uint8_t*>(ws));
+  HR_TRY(enqueue_stack(dims, layers, batch, nullptr, nullptr, x_embeds, kv, final_norm_w, head_w, n_codebooks,
+                       cb_vocab, h, logits_out, w, stream));
+  hr::launch_codebook_step(B, n_codebooks, cb_vocab, bos_id, eoc_id, true, logits_out, frame, eoc_seen, done,
+                           codes, aligned, max_frames, cb_embed, dims->hidden, emb_out, stream);
+  return check_launch("decode step");
+}
+
+hr_status hr_codebook_step(int32_t B, int32_t K, int32_t V, int32_t bos_id, int32_t eoc_id,
+                           int32_t logits_is_fp32, const void* logits, int32_t* frame, uint8_t* eoc_seen,
+                           uint8_t* done, int32_t* codes, int32_t* aligned, int32_t max_frames,
+                           const void* cb_embed, int32_t D, void* emb_out, hipStream_t stream) {
+  HR_TRY(check_codebook(B, K, V, bos_id, eoc_id, logits, frame, eoc_seen, done, codes, aligned, max_frames,
+                        cb_embed, D, emb_out));
   if (B == 0) return HR_OK;
   hr::launch_codebook_step(B, K, V, bos_id, eoc_id, logits_is_fp32 != 0, logits, frame, eoc_seen, done, codes,
                            aligned, max_frames, cb_embed, D, emb_out, stream);

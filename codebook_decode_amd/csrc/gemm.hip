@@ -8,7 +8,10 @@
 // out = x [M, K] . W [N, K]^T, W row-major [out, in] as stored.
 //
 // Two kernels:
-//  * skinny (M <= 64): weight streaming.  A workgroup owns 16 output columns
+//  * skinny (M <= 16; the head GEMM up to 64 rows): weight streaming.  Above 16
+//    rows the tiled kernel wins (M = 64, the layer's four projections: 93 us
+//    tiled against 129 us skinny, whose activation traffic per workgroup is
+//    M / 16 times its weight traffic).  A workgroup owns 16 output columns
 //    (16 gate + 16 up for SwiGLU; 32 for the bf16 and residual epilogues at
 //    M <= 16, so each activation fragment serves twice the weight rows) and
 //    its wavefronts split K; every lane streams
@@ -584,7 +587,8 @@ static void tiled_fill(const uint8_t* x, const uint8_t* w, int M, int N, int Kb,
 
 // Tile configuration of the large-M GEMM, per projection and M range, from
 // sweeps of 12-13 tile shapes, slab depths and split-K factors on MI355X with
-// the 4B layer's shapes (M = 128, 256, 512, 4192 bf16; M = 544 e4m3).  Small M
+// the 4B layer's shapes (M = 128, 256, 512, 4192 bf16; M = 544 e4m3; M = 32
+// and 64, the batched decode step, from a sweep of 4).  Small M
 // wants small tiles (more workgroups than CUs: QKV at M = 128 runs 39 -> 20 us
 // going from 128x128 to 64x64 tiles with 128-byte slabs); large M wants the
 // 256x256 tile (LDS traffic per MFMA).  Split-K fills the grid for the
@@ -594,6 +598,7 @@ static void tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, cons
                   hipStream_t st) {
   const int K_el = FP8 ? Kb : Kb / 2;
   if constexpr (EPI == HR_EPI_SWIGLU) {
+    if (M <= 64) return tiled_fill<EPI, FP8, 64, 128, 2, 2, 6, 128>(x, w, M, N, Kb, e, st);
     if (M > 384) return tiled_fill<EPI, FP8, 256, 256, 4, 2, 4>(x, w, M, N, Kb, e, st);
     if (M > 128) return tiled_fill<EPI, FP8, 256, 128, 4, 2, 4>(x, w, M, N, Kb, e, st);
     return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4, 128>(x, w, M, N, Kb, e, st);
@@ -601,6 +606,7 @@ static void tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, cons
     if (M > 1024) return tiled_fill<EPI, FP8, 256, 256, 4, 2, 4>(x, w, M, N, Kb, e, st);
     if (M > 384) return tiled_fill<EPI, FP8, 64, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
     if (M > 128) return tiled_fill<EPI, FP8, 128, 64, 2, 2, 6, 128>(x, w, M, N, Kb, e, st);
+    if (M <= 64) return tiled_fill<EPI, FP8, 64, 32, 2, 1, 8, 128>(x, w, M, N, Kb, e, st);
     return tiled_fill<EPI, FP8, 64, 64, 2, 2, 8, 128>(x, w, M, N, Kb, e, st);
   } else {
     if constexpr (FP8) {
@@ -612,6 +618,7 @@ static void tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, cons
       return tiled_fill<EPI, FP8, 128, 64, 2, 2, 4>(x, w, M, N, Kb, e, st, 3);
     }
     if (M > 128) return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
+    if (M <= 64 && K_el >= 8192) return tiled_fill<EPI, FP8, 64, 64, 2, 2, 8, 128>(x, w, M, N, Kb, e, st);
     if (K_el >= 8192) return tiled_fill<EPI, FP8, 128, 64, 2, 2, 4>(x, w, M, N, Kb, e, st);
     return tiled_fill<EPI, FP8, 64, 64, 2, 2, 4>(x, w, M, N, Kb, e, st);
   }
@@ -633,7 +640,7 @@ void launch_linear(const void* x, const void* w, const float* w_scale, float x_s
   const uint8_t* wb = static_cast<const uint8_t*>(w);
   const int ncols = (epi == HR_EPI_SWIGLU) ? N / 2 : N;
 #define HR_DISPATCH(EPI_)                                                                     \
-  if (M <= 64) {                                                                              \
+  if (M <= 16) {                                                                              \
     const int cbw = 16 * skinny_cb<EPI_>((M + 15) / 16);                                      \
     const int blocks = (ncols + cbw - 1) / cbw;                                               \
     int ks = 1;                                                                               \

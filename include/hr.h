@@ -179,6 +179,34 @@ hr_status hr_codebook_step(int32_t B, int32_t K, int32_t V, int32_t bos_id, int3
                            int32_t max_frames, const void* cb_embed, int32_t D, void* emb_out,
                            hipStream_t stream);
 
+/* One batched autoregressive decode step of B streams (the step that follows
+ * the prefill, one new row per stream): the stack over x_embeds at each
+ * stream's next position (its cache rows [0, start_pos] are attended
+ * causally; long rows over few streams are split into key chunks), the audio
+ * head on the new rows into logits_out, then the delayed-codebook step on
+ * those logits, which writes this step's codes and the next step's input rows.
+ *  batch       B sequences of one row each: cu_seqlens = {0, 1, ..., B},
+ *              start_pos[b] = the position of stream b's new row (its cached
+ *              length), cache_slot[b]; host mirrors as for the prefill.
+ *  x_embeds    bf16 [B, D]: the new rows' input embeddings (for the step after
+ *              a prefill: the codebook-embedding sum of its first codes).
+ *  logits_out  fp32 [B, K, V]: the head's logits of this step (output).
+ *  frame, eoc_seen, done, codes, aligned, max_frames, cb_embed: as in
+ *              hr_codebook_step (D = dims->hidden).
+ *  emb_out     bf16 [B, D]: the next step's x_embeds; may be the x_embeds buffer.
+ *  ws          device scratch of at least hr_decode_workspace_bytes(dims, wtype, B).
+ * HR_EUNSUPPORTED if dims->causal is 0; HR_EINVAL if a stream has other than one
+ * row, head_w or logits_out is NULL, or on any check of hr_prefill_stack or
+ * hr_codebook_step.  Nothing is launched when a check fails. */
+size_t hr_decode_workspace_bytes(const hr_dims* dims, hr_wtype wtype, int32_t B);
+hr_status hr_decode_step(const hr_dims* dims, const hr_layer* layers, const hr_batch* batch,
+                         const void* x_embeds, const hr_kv* kv, const void* final_norm_w,
+                         const void* head_w, int32_t n_codebooks, int32_t cb_vocab, int32_t bos_id,
+                         int32_t eoc_id, float* logits_out, int32_t* frame, uint8_t* eoc_seen,
+                         uint8_t* done, int32_t* codes, int32_t* aligned, int32_t max_frames,
+                         const void* cb_embed, void* emb_out, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
 const char* hr_last_error(void);
 
 #ifdef __cplusplus

@@ -212,3 +212,42 @@ def test_attention_chunked_validation(ct, slots, ws, ws_bytes, status):
                                   ct, slots, ws, ws_bytes, None)
     assert st == status, (st, H.hr_last_error())
     assert H.hr_attention_chunked_workspace_bytes(d, 300, 4) >= 4 * 300 * 32 * (128 * 4 + 8)
+
+
+@pytest.mark.parametrize("case,status", [
+    ("noncausal", H.HR_EUNSUPPORTED), ("two_rows", H.HR_EINVAL), ("no_head", H.HR_EINVAL),
+    ("bos_eq_eoc", H.HR_EINVAL), ("workspace", H.HR_EWORKSPACE), ("misaligned_emb", H.HR_EALIGN),
+    ("capacity", H.HR_ECAPACITY), ("wtype_mix", H.HR_EINVAL),
+])
+def test_decode_step_validation(case, status):
+    lib = H.lib()
+    d = dims()
+    Ls = (H.HrLayer * 2)(layer(), layer())
+    Ks = (H.HrKv * 2)(kv(), kv())
+    b = batch([1, 1, 1], starts=[10, 200, 5])
+    head, emb, bos, ws_bytes = FAKE, FAKE, 1024, 1 << 40
+    if case == "noncausal":
+        d, b = dims(causal=False), batch([1, 1, 1], used=[1, 1, 1])
+    elif case == "two_rows":
+        b = batch([1, 2, 1], starts=[10, 200, 5])
+    elif case == "no_head":
+        head = None
+    elif case == "bos_eq_eoc":
+        bos = 1025
+    elif case == "workspace":
+        ws_bytes = H.hr_decode_workspace_bytes(d, H.HR_BF16, 3) - 1
+    elif case == "misaligned_emb":
+        emb = MISALIGNED
+    elif case == "capacity":
+        b = batch([1, 1, 1], starts=[2048, 200, 5])
+    elif case == "wtype_mix":
+        Ls = (H.HrLayer * 2)(layer(), layer(wtype=H.HR_FP8_E4M3, ws_qkv=FAKE, ws_o=FAKE, ws_gu=FAKE,
+                                           ws_down=FAKE, as_qkv=1.0, as_o=1.0, as_gu=1.0, as_down=1.0))
+    st = lib.hr_decode_step(ctypes.byref(d), Ls, ctypes.byref(b.c), FAKE, Ks, FAKE, head, 8, 1026, bos, 1025, FAKE,
+                            FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, emb, FAKE, ws_bytes, None)
+    assert st == status, (case, st, H.hr_last_error())
+
+
+def test_decode_workspace_holds_the_prefill_workspace():
+    d = dims()
+    assert H.hr_decode_workspace_bytes(d, H.HR_BF16, 64) >= H.hr_workspace_bytes(d, H.HR_BF16, 64) + 64 * 2560 * 4
