@@ -181,16 +181,18 @@ size_t ws_layout(const hr_dims* d, int32_t T, Ws* w, uint8_t* base) {
   return off;
 }
 
-// Split attention rows into key chunks when the unsplit grid (query blocks x
-// kv heads x sequences) leaves most CUs idle and the longest row spans at least
-// 2 chunks: a decode step of a few streams over long caches, or a short
-// continuation.  Row lengths come from the host mirrors of the batch.
-// Measured (8 kv heads x 128): one query after 2040 cached keys 54.8 -> 23.9
-// us, 13 queries after 2000 keys 55.1 -> 26.0 us (4-tile chunks); a prefill
-// from position 0 or a decode step of 64 streams is faster unsplit.
-hr::AttnSplit attn_split(const hr_dims* d, const hr_batch* b, const Ws& w) {
+// Attention launch plan from the batch's host row lengths (start_pos + len).
+// Key chunks: when the unsplit grid (query blocks x kv heads x sequences)
+// leaves most CUs idle and the longest row spans at least 2 chunks (a decode
+// step of a few streams over long caches, a short continuation); needs the
+// partial buffers of the workspace (w).  Measured (8 kv heads x 128): one
+// query after 2040 cached keys 54.8 -> 23.9 us, 13 queries after 2000 keys
+// 55.1 -> 26.0 us (4-tile chunks); a prefill from position 0 or a decode step
+// of 64 streams is faster unsplit.  Two wave groups per block (interleaved
+// key tiles) when the grid is still below one workgroup per CU and a block
+// has at least 4 tiles.
+hr::AttnSplit attn_plan(const hr_dims* d, const hr_batch* b, const Ws* w) {
   hr::AttnSplit sp;
-  if (!w.part_o) return sp;
   const int qpw = hr::attention_qpw(d->n_q_heads, d->n_kv_heads);
   long long wgs = 0;
   int max_keys = 0;
@@ -201,13 +203,19 @@ hr::AttnSplit attn_split(const hr_dims* d, const hr_batch* b, const Ws& w) {
     if (keys > max_keys) max_keys = keys;
   }
   const int max_tiles = (max_keys + 63) / 64;
-  if (wgs >= 128 || max_tiles < 2 * kAttnChunk) return sp;
-  sp.chunk_tiles = kAttnChunk;
-  const int want = (max_tiles + kAttnChunk - 1) / kAttnChunk;
-  sp.n_slots = want < kAttnSlots ? want : kAttnSlots;
-  sp.part_o = w.part_o;
-  sp.part_ml = w.part_ml;
-  sp.T = b->total_tokens;
+  int block_tiles = max_tiles;
+  if (w && w->part_o && wgs < 128 && max_tiles >= 2 * kAttnChunk) {
+    sp.chunk_tiles = kAttnChunk;
+    const int want = (max_tiles + kAttnChunk - 1) / kAttnChunk;
+    sp.n_slots = want < kAttnSlots ? want : kAttnSlots;
+    sp.part_o = w->part_o;
+    sp.part_ml = w->part_ml;
+    sp.T = b->total_tokens;
+    wgs *= sp.n_slots;
+    block_tiles = (max_tiles + sp.n_slots - 1) / sp.n_slots;
+    if (block_tiles < kAttnChunk) block_tiles = kAttnChunk;
+  }
+  if (wgs < 256 && block_tiles >= 4) sp.groups = 2;
   return sp;
 }
 
@@ -218,7 +226,7 @@ hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_batch* b, floa
   const int T = b->total_tokens, D = d->hidden, F = d->ffn, Hq = d->n_q_heads, Hkv = d->n_kv_heads;
   const int dh = d->head_dim, A = Hq * dh, NQKV = (Hq + 2 * Hkv) * dh;
   const bool fp8 = L->wtype == HR_FP8_E4M3;
-  const hr::AttnSplit split = attn_split(d, b, w);
+  const hr::AttnSplit split = attn_plan(d, b, &w);
   if (!x_ready)
     hr::launch_rmsnorm(h, T, D, L->in_norm_w, d->rms_eps, w.x, fp8, fp8 ? 1.0f / L->as_qkv : 1.f, st);
   hr::launch_linear(w.x, L->w_qkv, L->ws_qkv, L->as_qkv, fp8, T, NQKV, D, HR_EPI_BF16, w.qkv, 0.f, st);
@@ -515,10 +523,11 @@ hr_status hr_attention(const hr_dims* dims, const hr_batch* batch, const void* q
   HR_TRY(need(out, "out"));
   if (out_type == HR_FP8_E4M3 && !(out_scale > 0.f)) return fail(HR_EINVAL, "out_scale must be > 0");
   if (batch->total_tokens == 0) return HR_OK;
+  const hr::AttnSplit plan = attn_plan(dims, batch, nullptr);
   hr::launch_attention(q, kv->k, kv->v, batch->cu_seqlens, batch->start_pos, batch->cache_slot, batch->used_keys,
                        batch->n_seq, batch->max_seqlen, dims->n_q_heads, dims->n_kv_heads, dims->head_dim,
                        kv->capacity, dims->causal != 0, out, out_type == HR_FP8_E4M3,
-                       out_type == HR_FP8_E4M3 ? 1.0f / out_scale : 1.f, stream);
+                       out_type == HR_FP8_E4M3 ? 1.0f / out_scale : 1.f, stream, &plan);
   return check_launch("attention");
 }
 

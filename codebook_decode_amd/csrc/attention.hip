@@ -49,8 +49,12 @@ __device__ __forceinline__ void chunk_plan(int n_tiles, int chunk_tiles, int n_s
   n_chunks = (n_tiles + ct - 1) / ct;
 }
 
-template <int DH, int GROUP>
-__global__ __launch_bounds__(256, 2) void attention_kernel(
+// NG groups of 4 wavefronts: group n takes key tiles kt0 + n, kt0 + n + NG, ...
+// of the same queries, with its own K/V buffers; the groups' running
+// (max, sum, output) are merged through LDS at the end.  NG = 2 gives a long
+// row two wavefronts per SIMD that hide each other's latencies.
+template <int DH, int GROUP, int NG>
+__global__ __launch_bounds__(256 * NG, 2 / NG) void attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ start_pos,
     const int32_t* __restrict__ cache_slot, const int32_t* __restrict__ used_keys, int Hq, int Hkv,
@@ -65,8 +69,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
   constexpr int KPT = KCH / 256;              // K chunks per thread
   constexpr int VPT = KCH / 2 / 256;          // V key-pair units per thread (2 loads each)
   static_assert(KPT >= 1 && VPT >= 1, "tile / thread mapping");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[AKT * K_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[DH * VT_LD];
+  constexpr int kGroupLds = AKT * K_LD + DH * VT_LD;   // elements of one group's K and V^T tiles
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NG * kGroupLds];
 
   const int s = blockIdx.z, g = blockIdx.y;
   const int len = cu[s + 1] - cu[s];
@@ -78,7 +82,11 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
   const int tok0 = cu[s];
   const int start = start_pos[s];
   const size_t base = size_t(cache_slot[s]) * capacity;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int grp = int(threadIdx.x) >> 8;            // key-tile group
+  const int tid = threadIdx.x & 255, wave = tid >> 6;   // within the group
+  uint16_t* sK = smem + grp * kGroupLds;
+  uint16_t* sVt = sK + AKT * K_LD;
   const int hg = wave % GROUP, qsub = wave / GROUP;
   const int hh = g * GROUP + hg;
   const int half = lane >> 5, r32 = lane & 31;
@@ -164,13 +172,16 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
   float m_run = -__builtin_inff();
   float l_part = 0.f;
 
-  if (kt0 < kt1) fetch(kt0 * AKT);
-  for (int kt = kt0; kt < kt1; ++kt) {
+  if (kt0 + grp < kt1) fetch((kt0 + grp) * AKT);
+  for (int kb = kt0; kb < kt1; kb += NG) {
+    const int kt = kb + grp;
+    const bool have = kt < kt1;      // the other group may still have a tile
     const int k0 = kt * AKT;
     __syncthreads();                 // every wave is done with the previous tile
-    stage();
+    if (have) stage();
     __syncthreads();
-    if (kt + 1 < kt1) fetch(k0 + AKT);   // in flight during this tile's math
+    if (kt + NG < kt1) fetch(k0 + NG * AKT);   // in flight during this tile's math
+    if (!have) continue;
 
     // scores of 2 blocks of 32 keys
     floatx16 sc[2];
@@ -252,6 +263,39 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
       }
   }
 
+  if constexpr (NG > 1) {
+    // merge the groups' partial softmaxes into group 0 (through the now idle
+    // tile buffers: 4 waves x 64 lanes x (2 + 16 NDB) floats per group)
+    constexpr int kVals = 2 + 16 * NDB;
+    static_assert(size_t(NG - 1) * 256 * kVals * 4 <= sizeof(smem), "merge buffer");
+    float* xch = reinterpret_cast<float*>(smem);
+    __syncthreads();
+    if (grp > 0) {
+      float* my = xch + (size_t(grp - 1) * 256 + tid) * kVals;
+      my[0] = m_run;
+      my[1] = l_part;
+#pragma unroll
+      for (int j = 0; j < NDB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) my[2 + 16 * j + r] = o[j][r];
+    }
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int g2 = 1; g2 < NG; ++g2) {
+      const float* ot = xch + (size_t(g2 - 1) * 256 + tid) * kVals;
+      const float m2 = ot[0];
+      const float mm = fmaxf(m_run, m2);
+      const float a1 = (m_run == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
+      const float a2 = (m2 == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(m2 - mm);
+      l_part = l_part * a1 + ot[1] * a2;
+#pragma unroll
+      for (int j = 0; j < NDB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[j][r] = o[j][r] * a1 + ot[2 + 16 * j + r] * a2;
+      m_run = mm;
+    }
+  }
   float l = l_part + __shfl_xor(l_part, 32, kWave);
   if (!qok) return;
   if (split) {
@@ -341,11 +385,18 @@ static void launch_attn_t(const void* q, const void* kc, const void* vc, const i
   const int slots = sp_cfg.chunk_tiles > 0 ? sp_cfg.n_slots : 1;
   dim3 grid(n_qb * slots, Hkv, n_seq);
   const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf(float(DH));
-  attention_kernel<DH, GROUP><<<grid, 256, 0, st>>>(
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
-      static_cast<const uint16_t*>(vc), cu, sp, slot, used, Hq, Hkv, cap, causal ? 1 : 0,
-      scale_log2, out, fp8 ? 1 : 0, out_inv, sp_cfg.chunk_tiles, slots, sp_cfg.part_o,
-      reinterpret_cast<float2_t*>(sp_cfg.part_ml), sp_cfg.T);
+  if (sp_cfg.groups == 2)
+    attention_kernel<DH, GROUP, 2><<<grid, 512, 0, st>>>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
+        static_cast<const uint16_t*>(vc), cu, sp, slot, used, Hq, Hkv, cap, causal ? 1 : 0,
+        scale_log2, out, fp8 ? 1 : 0, out_inv, sp_cfg.chunk_tiles, slots, sp_cfg.part_o,
+        reinterpret_cast<float2_t*>(sp_cfg.part_ml), sp_cfg.T);
+  else
+    attention_kernel<DH, GROUP, 1><<<grid, 256, 0, st>>>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
+        static_cast<const uint16_t*>(vc), cu, sp, slot, used, Hq, Hkv, cap, causal ? 1 : 0,
+        scale_log2, out, fp8 ? 1 : 0, out_inv, sp_cfg.chunk_tiles, slots, sp_cfg.part_o,
+        reinterpret_cast<float2_t*>(sp_cfg.part_ml), sp_cfg.T);
   if (sp_cfg.chunk_tiles > 0)
     attention_merge_kernel<DH><<<sp_cfg.T, 256, 0, st>>>(cu, sp, used, n_seq, Hq, causal ? 1 : 0, QPW,
                                                          sp_cfg.chunk_tiles, slots, sp_cfg.part_o,

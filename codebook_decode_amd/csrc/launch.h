@@ -35,6 +35,7 @@ void launch_qknorm_rope_kv(const void* qkv, int T, int Hq, int Hkv, int d, float
 // blocks with more than chunk_tiles 64-key tiles write fp32 partials per chunk
 // (n_slots chunk slots at most) and a merge kernel combines them.
 struct AttnSplit {
+  int groups = 1;           // wave groups interleaving the key tiles of a block (1 or 2)
   int chunk_tiles = 0;      // 0: no split
   int n_slots = 1;
   float* part_o = nullptr;  // [n_slots, T, Hq, d]
