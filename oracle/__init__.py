@@ -23,9 +23,13 @@ rounded to bf16).  Sources, cited by page title and section:
   ``_quantize`` and the per-call ``run`` of ``_make_run``): RMSNorm with eps
   1e-6, rotate-half RoPE, attention over exactly the used keys, static
   per-tensor activation scales ``amax / FP8_MAX``.
+* vLLM-Omni pull request 8226 (Higgs Audio v3 streaming on Model Runner V2),
+  Purpose and Test Plan: temperature / top-k / top-p sampling of the codebook
+  rows with per-request seeded exponential noise.
 
 Modules: ``numerics`` (bf16 widen/round, e4m3 codec), ``prefill`` (layer, stack,
 head), ``codebook`` (delayed-codebook step), ``fp8`` (weight/activation scales,
-calibration, fake-quant layer).
+calibration, fake-quant layer), ``sampling`` (Philox4x64-10 noise and the row
+sampler), ``policy`` (the step with sampling and the termination policies).
 """
-from . import numerics, prefill, codebook, fp8  # noqa: F401
+from . import numerics, prefill, codebook, fp8, sampling, policy  # noqa: F401

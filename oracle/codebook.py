@@ -74,11 +74,16 @@ def codebook_step(logits: np.ndarray, frame: np.ndarray, eoc_seen: np.ndarray, d
             frame[b] = t + 1
             done[b] = 1 if all(eoc_seen[b, k] for k in range(K)) else 0
         codes[b] = c
-        acc = cb_embed_f32[0 * V + c[0]].astype(np.float32).copy()
-        for k in range(1, K):
-            acc = (acc + cb_embed_f32[k * V + c[k]].astype(np.float32)).astype(np.float32)
-        emb[b] = f32_to_bf16(acc)
+        emb[b] = embed_sum(cb_embed_f32, c, V)
     return codes, emb
+
+
+def embed_sum(cb_embed_f32: np.ndarray, c, V: int) -> np.ndarray:
+    """bf16 bits of the fp32 sum, in codebook order, of rows k * V + c[k]."""
+    acc = cb_embed_f32[0 * V + c[0]].astype(np.float32).copy()
+    for k in range(1, len(c)):
+        acc = (acc + cb_embed_f32[k * V + c[k]].astype(np.float32)).astype(np.float32)
+    return f32_to_bf16(acc)
 
 
 def top2_margin(logits: np.ndarray) -> np.ndarray:

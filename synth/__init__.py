@@ -32,6 +32,7 @@ SEED_CALIB = 7           # the fixed FP8 calibration prompt
 SEED_LENGTHS = 2024      # varlen prompt lengths
 SEED_LOGITS = 99         # codebook-step logits
 SEED_STATE = 5           # codebook-step initial frame counters
+SEED_SAMPLING = 42       # per-stream sampling settings and generator keys
 
 # tensor ids inside a model's seed space
 T_EMBED, T_IN_NORM, T_POST_NORM, T_Q_NORM, T_K_NORM = 0, 1, 2, 3, 4
@@ -296,3 +297,22 @@ def codebook_state(B: int, K: int, frame_hi: int = 16, seed: int = SEED_STATE) -
     return {"frame": g.integers(0, frame_hi, B, dtype=np.int64).astype(np.int32),
             "eoc_seen": np.zeros((B, K), np.uint8),
             "done": np.zeros(B, np.uint8)}
+
+
+def sampling_settings(B: int, seed: int = SEED_SAMPLING, serving: bool = False) -> dict:
+    """Per-stream sampling settings: temperature fp32, top_k int32, top_p fp32 and
+    a 64-bit generator key (uint64) per stream.  ``serving``: every stream at
+    temperature 1, top-k 50, top-p 0.95 (the serving runs' settings); else a mix
+    that covers greedy (T = 0), top-k off / 1 / 50 / 200 / all, top-p off / 0.95 / 0.5 / 0
+    and temperatures 0.7 / 1.0 / 1.3."""
+    g = _stream(seed, B, 1 if serving else 0)
+    keys = g.integers(0, 2 ** 63, B, dtype=np.int64).astype(np.uint64) * np.uint64(2) + \
+        g.integers(0, 2, B, dtype=np.int64).astype(np.uint64)
+    if serving:
+        return {"temperature": np.ones(B, np.float32), "top_k": np.full(B, 50, np.int32),
+                "top_p": np.full(B, 0.95, np.float32), "seed": keys}
+    i = np.arange(B)
+    return {"temperature": np.array([0.0, 0.7, 1.0, 1.3], np.float32)[i % 4],
+            "top_k": np.array([0, 1, 50, 200, 1 << 20], np.int32)[i % 5],
+            "top_p": np.array([1.0, 0.95, 0.5, 0.95, 0.0, 0.95, 1.0], np.float32)[i % 7],
+            "seed": keys}
