@@ -328,6 +328,37 @@ def codebook_steps(H, m, shared, B=64, reps=100):
     return {"B": B, "us_per_step": round(sec * 1e6, 2), "bytes": int(bytes_), "roofline": hbm(bytes_, sec)}
 
 
+def codebook_policy_steps(H, m, shared, B=64, reps=100):
+    """The sampled codebook step at B streams, 8 x 1026, bf16 logits, serving
+    settings (temperature 1, top-k 50, top-p 0.95, per-stream Philox keys), with
+    the EOC cascade and the repeated-code guard (limit 64) on.  The streams' frame
+    counters advance every call, so each call draws fresh noise."""
+    import torch
+    import synth
+    from gpu_util import dev, dev_bf16
+    K, V, D = m.n_codebooks, m.cb_vocab, m.hidden
+    logits = dev_bf16(synth.codebook_logits(B, K, V, 0, m.eoc_id))
+    st = synth.codebook_state(B, K)
+    frame, seen, done = dev(st["frame"]), dev(st["eoc_seen"]), dev(st["done"])
+    codes = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    emb = torch.empty((B, D), dtype=torch.bfloat16, device="cuda")
+    sp = synth.sampling_settings(B, serving=True)
+    end = dev(np.full(B, -1, np.int32))
+    last = dev(np.full((B, K), -1, np.int32))
+    run = dev(np.zeros(B, np.int32))
+    pol = H.make_policy(temperature=dev(sp["temperature"]), top_k=dev(sp["top_k"]), top_p=dev(sp["top_p"]),
+                        seed=dev(sp["seed"].view(np.int64)), eoc_cascade=True, repeat_limit=64, end_frame=end,
+                        last_codes=last, repeat_run=run)
+
+    def call():
+        H.hr_codebook_step_policy(B, K, V, m.bos_id, m.eoc_id, logits, frame, seen, done, codes, None, 0,
+                                  shared["cb"], D, emb, pol)
+    sec = time_events(call, reps)
+    bytes_ = B * (K * V * 2 + K * D * 2 + D * 2 + K * 4 + K + 8 + 16 + K * 8 + 8)
+    return {"B": B, "us_per_step": round(sec * 1e6, 2), "bytes": int(bytes_), "roofline": hbm(bytes_, sec),
+            "settings": "T 1, top-k 50, top-p 0.95, EOC cascade, repeat guard 64"}
+
+
 def hbm_sweep(H, m, shared):
     """The memory-bound kernels where their bytes outgrow launch latency:
     RMSNorm (6 B per element), q/k norm + RoPE + KV write (24.6 KB per token),
@@ -358,6 +389,8 @@ def hbm_sweep(H, m, shared):
     for B in (4096, 16384):
         r = codebook_steps(H, m, shared, B=B, reps=10)
         out[f"codebook_B{B}"] = {"us": r["us_per_step"], "roofline": r["roofline"]}
+    r = codebook_policy_steps(H, m, shared, B=4096, reps=10)
+    out["codebook_sampled_B4096"] = {"us": r["us_per_step"], "roofline": r["roofline"]}
     return out
 
 
@@ -484,6 +517,7 @@ def main():
         out["fp8_layer"] = fp8_layer(H, m, dev_layers[0])
         out["varlen32"] = varlen_batch(H, m, layers, shared)
         out["codebook_b64"] = codebook_steps(H, m, shared)
+        out["codebook_sampled_b64"] = codebook_policy_steps(H, m, shared)
         log("timing decode steps (B=64 over 512 cached rows, B=1 over 2047)")
         out["decode_b64"] = decode_steps(H, m, dev_layers, layers, shared, 64, 512)
         out["decode_b1"] = decode_steps(H, m, dev_layers, layers, shared, 1, 2047)

@@ -438,6 +438,45 @@ hr_status hr_codebook_step(int32_t B, int32_t K, int32_t V, int32_t bos_id, int3
   return check_launch("codebook step");
 }
 
+hr_status hr_codebook_step_policy(int32_t B, int32_t K, int32_t V, int32_t bos_id, int32_t eoc_id,
+                                  int32_t logits_is_fp32, const void* logits, int32_t* frame, uint8_t* eoc_seen,
+                                  uint8_t* done, int32_t* codes, int32_t* aligned, int32_t max_frames,
+                                  const void* cb_embed, int32_t D, void* emb_out, const hr_step_policy* policy,
+                                  hipStream_t stream) {
+  HR_TRY(check_codebook(B, K, V, bos_id, eoc_id, logits, frame, eoc_seen, done, codes, aligned, max_frames,
+                        cb_embed, D, emb_out));
+  if (V > 2048) return fail(HR_EUNSUPPORTED, "V = %d > 2048 ids per codebook for the policy step", V);
+  hr::StepPolicy p;
+  if (policy) {
+    p.temperature = policy->temperature;
+    p.top_k = policy->top_k;
+    p.top_p = policy->top_p;
+    p.seed = policy->seed;
+    p.eoc_cascade = policy->eoc_cascade != 0;
+    p.repeat_limit = policy->repeat_limit;
+    p.end_frame = policy->end_frame;
+    p.last_codes = policy->last_codes;
+    p.repeat_run = policy->repeat_run;
+    if (p.temperature && !p.seed) return fail(HR_EINVAL, "temperature given without seed");
+    if (p.seed && (reinterpret_cast<uintptr_t>(p.seed) & 7))
+      return fail(HR_EALIGN, "seed is not 8-byte aligned");
+    if (p.repeat_limit < 0 || p.repeat_limit == 1)
+      return fail(HR_EINVAL, "repeat_limit %d: 0 (off) or >= 2", p.repeat_limit);
+    if ((p.eoc_cascade || p.repeat_limit) && !p.end_frame)
+      return fail(HR_EINVAL, "end_frame is required by the cascade and the stop guard");
+    if (p.repeat_limit && (!p.last_codes || !p.repeat_run))
+      return fail(HR_EINVAL, "last_codes and repeat_run are required by the stop guard");
+  }
+  if (B == 0) return HR_OK;
+  if (!p.temperature && !p.eoc_cascade && !p.repeat_limit)   // greedy, no policy: the plain step's kernel
+    hr::launch_codebook_step(B, K, V, bos_id, eoc_id, logits_is_fp32 != 0, logits, frame, eoc_seen, done, codes,
+                             aligned, max_frames, cb_embed, D, emb_out, stream);
+  else
+    hr::launch_codebook_policy(B, K, V, bos_id, eoc_id, logits_is_fp32 != 0, logits, frame, eoc_seen, done, codes,
+                               aligned, max_frames, cb_embed, D, emb_out, p, stream);
+  return check_launch("codebook policy step");
+}
+
 // ------------------------------------------------------------------ step-level entries (hr_ops.h)
 hr_status hr_embed_rmsnorm(const int32_t* ids, const void* embed, int32_t vocab, const void* x_embeds,
                            int32_t T, int32_t D, const void* norm_w, float eps, float* h_out, void* x_out,

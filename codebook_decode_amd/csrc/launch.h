@@ -16,6 +16,23 @@ void launch_codebook_step(int B, int K, int V, int bos, int eoc, bool f32, const
                           int32_t* aligned, int max_frames, const void* cb_embed, int D,
                           void* emb_out, hipStream_t st);
 
+// per-stream sampling and termination policies (fields as hr_step_policy)
+struct StepPolicy {
+  const float* temperature = nullptr;
+  const int32_t* top_k = nullptr;
+  const float* top_p = nullptr;
+  const uint64_t* seed = nullptr;
+  int eoc_cascade = 0;
+  int repeat_limit = 0;
+  int32_t* end_frame = nullptr;
+  int32_t* last_codes = nullptr;
+  int32_t* repeat_run = nullptr;
+};
+void launch_codebook_policy(int B, int K, int V, int bos, int eoc, bool f32, const void* logits,
+                            int32_t* frame, uint8_t* eoc_seen, uint8_t* done, int32_t* codes,
+                            int32_t* aligned, int max_frames, const void* cb_embed, int D,
+                            void* emb_out, const StepPolicy& pol, hipStream_t st);
+
 void launch_embed_rmsnorm(const int32_t* ids, const void* embed, const void* x_embeds, int T, int D,
                           const void* w, float eps, float* h_out, void* x_out, bool fp8,
                           float inv_scale, hipStream_t st);

@@ -51,6 +51,12 @@ class HrBatch(ctypes.Structure):
                 ("h_used_keys", c_vp)]
 
 
+class HrStepPolicy(ctypes.Structure):
+    _fields_ = [("temperature", c_vp), ("top_k", c_vp), ("top_p", c_vp), ("seed", c_vp),
+                ("eoc_cascade", c_i32), ("repeat_limit", c_i32), ("end_frame", c_vp),
+                ("last_codes", c_vp), ("repeat_run", c_vp)]
+
+
 class HrError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
@@ -80,6 +86,9 @@ def lib() -> ctypes.CDLL:
                                          c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
             "hr_codebook_step": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp,
                                          c_vp, c_vp, c_i32, c_vp, c_i32, c_vp, c_vp]),
+            "hr_codebook_step_policy": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp,
+                                                c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp, P(HrStepPolicy),
+                                                c_vp]),
             "hr_decode_workspace_bytes": (c_sz, [P(HrDims), c_i32, c_i32]),
             "hr_decode_step": (c_i32, [P(HrDims), P(HrLayer), P(HrBatch), c_vp, P(HrKv), c_vp, c_vp, c_i32, c_i32,
                                        c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp,
@@ -235,6 +244,25 @@ def hr_codebook_step(B, K, V, bos_id, eoc_id, logits, frame, eoc_seen, done, cod
     _check(lib().hr_codebook_step(B, K, V, bos_id, eoc_id, f32, ptr(logits), ptr(frame), ptr(eoc_seen),
                                   ptr(done), ptr(codes), ptr(aligned), max_frames, ptr(cb_embed), D,
                                   ptr(emb_out), stream if stream is not None else current_stream()))
+
+
+def make_policy(temperature=None, top_k=None, top_p=None, seed=None, eoc_cascade=False, repeat_limit=0,
+                end_frame=None, last_codes=None, repeat_run=None) -> HrStepPolicy:
+    """hr_step_policy over device tensors (kept alive on the returned struct)."""
+    pol = HrStepPolicy(ptr(temperature), ptr(top_k), ptr(top_p), ptr(seed), 1 if eoc_cascade else 0,
+                       int(repeat_limit), ptr(end_frame), ptr(last_codes), ptr(repeat_run))
+    pol._tensors = (temperature, top_k, top_p, seed, end_frame, last_codes, repeat_run)
+    return pol
+
+
+def hr_codebook_step_policy(B, K, V, bos_id, eoc_id, logits, frame, eoc_seen, done, codes, aligned, max_frames,
+                            cb_embed, D, emb_out, policy=None, stream=None) -> None:
+    import torch
+    f32 = 1 if logits.dtype == torch.float32 else 0
+    _check(lib().hr_codebook_step_policy(B, K, V, bos_id, eoc_id, f32, ptr(logits), ptr(frame), ptr(eoc_seen),
+                                         ptr(done), ptr(codes), ptr(aligned), max_frames, ptr(cb_embed), D,
+                                         ptr(emb_out), ctypes.byref(policy) if policy is not None else None,
+                                         stream if stream is not None else current_stream()))
 
 
 def hr_embed_rmsnorm(ids, embed, vocab, x_embeds, T, D, norm_w, eps, h_out, x_out, x_type=HR_BF16,

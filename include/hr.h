@@ -179,6 +179,62 @@ hr_status hr_codebook_step(int32_t B, int32_t K, int32_t V, int32_t bos_id, int3
                            int32_t max_frames, const void* cb_embed, int32_t D, void* emb_out,
                            hipStream_t stream);
 
+/* Per-stream sampling and termination policies for hr_codebook_step_policy.
+ * Sampling (vLLM-Omni pull request 8226, Higgs Audio v3 streaming on Model
+ * Runner V2, Purpose and Test Plan: temperature / top-k / top-p with per-request
+ * seeded exponential noise).  All arrays are device memory of B entries, read
+ * only; NULL means the default for every stream.
+ *  temperature  fp32: > 0 samples from softmax(logits / T); <= 0 (or NULL) is
+ *               the greedy argmax of hr_codebook_step.
+ *  top_k        int32: keep the logits >= the k-th largest (ties at the k-th
+ *               value stay); <= 0, >= V or NULL: off.
+ *  top_p        fp32: order the survivors by logit (equal logits by lower id)
+ *               and keep each while the softmax mass ahead of it is below p;
+ *               >= 1 or NULL: off; <= 0 keeps the first only.
+ *  seed         uint64: the stream's Philox4x64-10 key (seed, 0); row k at
+ *               step t (= frame) draws counter block (t, k, v / 4, 0), word
+ *               v % 4 for id v, u = (top 23 bits + 1/2) / 2^23; the winner is
+ *               the kept id with the largest z - ln(-ln u) (lowest id on
+ *               equality).  Required when temperature is given.
+ * Termination (FlashRT pull request 141, Summary and Root cause: delayed EOC
+ * for every codebook; a deterministic stop guard for repeated-code loops).  An
+ * end frame e >= 0 forces codebook k to EOC at every step t >= e + k.
+ *  eoc_cascade  1: when an open stream (e < 0) emits EOC in codebooks k1..kn
+ *               at step t, e = t - max(k).
+ *  repeat_limit 0: off; >= 2: an open stream counts consecutive steps whose K
+ *               codes equal the previous step's (a new run counts 1) and sets
+ *               e = t + 1 when the count reaches the limit.
+ *  end_frame    int32 [B] in/out, -1 while open; required by either rule.
+ *  last_codes   int32 [B, K] in/out (start at -1) and repeat_run int32 [B]
+ *               in/out (start at 0): the guard's state, required by it. */
+typedef struct {
+  const float* temperature;
+  const int32_t* top_k;
+  const float* top_p;
+  const uint64_t* seed;
+  int32_t eoc_cascade;
+  int32_t repeat_limit;
+  int32_t* end_frame;
+  int32_t* last_codes;
+  int32_t* repeat_run;
+} hr_step_policy;
+
+/* hr_codebook_step with the policies above (policy NULL: all defaults, the
+ * same codes as hr_codebook_step).  Per stream that is not done, with t = frame
+ * and e = end_frame (-1 without one): codebook k emits BOS while t < k, EOC if
+ * it already emitted EOC, EOC if e >= 0 and t >= e + k, else its row's choice
+ * (greedy or sampled); then the guard and the cascade may set e (the smaller
+ * of their candidates), frame = t + 1, done = every codebook has emitted EOC.
+ * Arguments as for hr_codebook_step.  HR_EUNSUPPORTED if V > 2048; HR_EINVAL on
+ * the checks of hr_codebook_step, temperature without seed, repeat_limit of 1
+ * or below 0, or a missing state array; HR_EALIGN if seed is not 8-byte
+ * aligned.  Calls that overlap on one stream state race. */
+hr_status hr_codebook_step_policy(int32_t B, int32_t K, int32_t V, int32_t bos_id, int32_t eoc_id,
+                                  int32_t logits_is_fp32, const void* logits, int32_t* frame,
+                                  uint8_t* eoc_seen, uint8_t* done, int32_t* codes, int32_t* aligned,
+                                  int32_t max_frames, const void* cb_embed, int32_t D, void* emb_out,
+                                  const hr_step_policy* policy, hipStream_t stream);
+
 /* One batched autoregressive decode step of B streams (the step that follows
  * the prefill, one new row per stream): the stack over x_embeds at each
  * stream's next position (its cache rows [0, start_pos] are attended

@@ -197,6 +197,29 @@ def test_codebook_misaligned_logits_refused():
     assert st == H.HR_EALIGN
 
 
+@pytest.mark.parametrize("case,status", [
+    ({"V": 2049}, H.HR_EUNSUPPORTED),
+    ({"temperature": FAKE}, H.HR_EINVAL),                        # temperature without seed
+    ({"temperature": FAKE, "seed": FAKE + 4}, H.HR_EALIGN),
+    ({"repeat_limit": 1, "end_frame": FAKE, "last_codes": FAKE, "repeat_run": FAKE}, H.HR_EINVAL),
+    ({"repeat_limit": -2, "end_frame": FAKE, "last_codes": FAKE, "repeat_run": FAKE}, H.HR_EINVAL),
+    ({"eoc_cascade": 1}, H.HR_EINVAL),                           # no end_frame
+    ({"repeat_limit": 4, "end_frame": FAKE}, H.HR_EINVAL),       # no guard state
+    ({"repeat_limit": 4, "end_frame": FAKE, "last_codes": FAKE}, H.HR_EINVAL),
+    ({"bos": 1026}, H.HR_EINVAL),                                # the plain step's checks still apply
+])
+def test_codebook_policy_validation(case, status):
+    lib = H.lib()
+    c = dict(case)
+    V = c.pop("V", 1026)
+    bos = c.pop("bos", V - 2)
+    pol = H.HrStepPolicy(c.get("temperature"), None, None, c.get("seed"), c.get("eoc_cascade", 0),
+                         c.get("repeat_limit", 0), c.get("end_frame"), c.get("last_codes"), c.get("repeat_run"))
+    st = lib.hr_codebook_step_policy(4, 8, V, bos, V - 1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, 2560,
+                                     FAKE, ctypes.byref(pol), None)
+    assert st == status, (st, H.hr_last_error())
+
+
 @pytest.mark.parametrize("ct,slots,ws,ws_bytes,status", [
     (0, 4, FAKE, 1 << 40, H.HR_EINVAL),           # chunk_tiles < 1
     (2, 0, FAKE, 1 << 40, H.HR_EINVAL),           # no slot
