@@ -536,6 +536,60 @@ hr_status hr_linear(const void* x, const void* w, const float* w_scale, float x_
   return check_launch("linear");
 }
 
+hr_status hr_quantize_mxfp4(const void* x, int32_t x_is_fp32, int32_t M, int32_t K, const float* col_scale,
+                            const float* row_scale, uint8_t* codes, uint8_t* scales, int32_t ld_scales,
+                            hipStream_t stream) {
+  if (M < 0 || K <= 0 || K % 128) return fail(HR_EINVAL, "bad M=%d / K=%d (a multiple of 128)", M, K);
+  if (ld_scales < M || ld_scales % 4) return fail(HR_EINVAL, "ld_scales %d: >= M and a multiple of 4", ld_scales);
+  HR_TRY(need(x, "x"));
+  HR_TRY(need(codes, "codes"));
+  HR_TRY(need(scales, "scales"));
+  if (M == 0) return HR_OK;
+  hr::launch_quant_mx(x, x_is_fp32 != 0, M, K, col_scale, row_scale, codes, scales, ld_scales, stream);
+  return check_launch("quantize mxfp4");
+}
+
+hr_status hr_rmsnorm_mxfp4(const float* h, int32_t T, int32_t D, const void* norm_w, float eps,
+                           const float* col_scale, uint8_t* codes, uint8_t* scales, int32_t ld_scales,
+                           hipStream_t stream) {
+  if (T < 0 || D <= 0 || D % 128 || D > 8192) return fail(HR_EINVAL, "bad T=%d / D=%d", T, D);
+  if (ld_scales < T || ld_scales % 4) return fail(HR_EINVAL, "ld_scales %d: >= T and a multiple of 4", ld_scales);
+  HR_TRY(need(h, "h"));
+  HR_TRY(need(norm_w, "norm_w"));
+  HR_TRY(need(codes, "codes"));
+  HR_TRY(need(scales, "scales"));
+  if (T == 0) return HR_OK;
+  hr::launch_rmsnorm_mx(h, T, D, norm_w, col_scale, eps, codes, scales, ld_scales, stream);
+  return check_launch("rmsnorm mxfp4");
+}
+
+hr_status hr_linear_mxfp4(const uint8_t* x, const uint8_t* x_scales, int32_t ld_x_scales, const uint8_t* w,
+                          const uint8_t* w_scales, int32_t M, int32_t N, int32_t K, hr_epilogue epi, void* out,
+                          uint8_t* out_scales, int32_t ld_out_scales, hipStream_t stream) {
+  if (M < 0 || N <= 0 || K <= 0 || K % 128) return fail(HR_EINVAL, "bad M=%d N=%d K=%d (K a multiple of 128)", M, N, K);
+  if (epi != HR_EPI_RESIDUAL && epi != HR_EPI_SWIGLU) return fail(HR_EINVAL, "MXFP4: residual or SwiGLU epilogue");
+  if (epi == HR_EPI_RESIDUAL && N % 256) return fail(HR_EUNSUPPORTED, "N = %d must be a multiple of 256", N);
+  if (epi == HR_EPI_SWIGLU && N % 256) return fail(HR_EUNSUPPORTED, "N = 2F = %d: F a multiple of 128", N);
+  const int32_t Mr = (M + 255) / 256 * 256;
+  if (ld_x_scales < Mr || ld_x_scales % 4) return fail(HR_EINVAL, "ld_x_scales %d < %d", ld_x_scales, Mr);
+  if (uint64_t(M > N ? M : N) * (K / 2) >= (uint64_t(1) << 31))
+    return fail(HR_EUNSUPPORTED, "an operand of %d x %d or %d x %d exceeds 2 GB", M, K, N, K);
+  HR_TRY(need(x, "x"));
+  HR_TRY(need(x_scales, "x_scales"));
+  HR_TRY(need(w, "w"));
+  HR_TRY(need(w_scales, "w_scales"));
+  HR_TRY(need(out, "out"));
+  if (epi == HR_EPI_SWIGLU) {
+    HR_TRY(need(out_scales, "out_scales"));
+    if (ld_out_scales < Mr || ld_out_scales % 4)
+      return fail(HR_EINVAL, "ld_out_scales %d < %d", ld_out_scales, Mr);
+  }
+  if (M == 0) return HR_OK;
+  hr::launch_linear_mx(x, x_scales, ld_x_scales, w, w_scales, M, N, K, epi, out, out_scales, ld_out_scales,
+                       stream);
+  return check_launch("linear mxfp4");
+}
+
 hr_status hr_qknorm_rope_kv(const hr_dims* dims, const hr_batch* batch, const void* qkv, const void* q_norm_w,
                             const void* k_norm_w, void* q_out, const hr_kv* kv, hipStream_t stream) {
   HR_TRY(check_dims(dims));

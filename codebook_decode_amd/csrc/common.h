@@ -70,6 +70,32 @@ __device__ __forceinline__ float e4m3_to_f(uint32_t c) {
   return (c & 0x80u) ? -v : v;
 }
 
+// ---------------------------------------------------------------- MXFP4 (OCP MX)
+// Shared exponent of a 32-element block with the given max |v|: floor(log2
+// amax) - 2 (2 = the exponent of E2M1's largest value 6), clamped to
+// [-127, 127]; -127 for a zero (or subnormal) amax.  The scale byte is e + 127.
+__device__ __forceinline__ int mx_block_exp(float amax) {
+  const int ex = int((__float_as_uint(amax) >> 23) & 0xFFu);
+  if (ex == 0) return -127;
+  const int e = ex - 127 - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+// E2M1 code of y (nearest, ties to the even code, saturating at 6): the
+// midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 between the magnitudes
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6 go to codes 0, 2, 2, 4, 4, 6, 6
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+  const float a = fabsf(y);
+  uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+             : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  if (c != 0u && (__float_as_uint(y) >> 31)) c |= 8u;
+  return c;
+}
+// byte offset of block kb of row r in the slab-interleaved scale layout
+// [K / 128][ld][4] (the 4 blocks of one 128-element K slab of a row together)
+__device__ __forceinline__ size_t mx_scale_off(int r, int kb, int ld) {
+  return (size_t(kb >> 2) * size_t(ld) + size_t(r)) * 4 + (kb & 3);
+}
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -85,6 +85,30 @@ __device__ __forceinline__ floatx16 mma32(const u32x4 (&a)[NC], const u32x4 (&b)
   }
 }
 
+// MXFP4 32 x 32 block over one 128-value K slab: chunk m (16 B = 32 E2M1
+// values of k-half h of MFMA m) feeds v_mfma_scale_f32_32x32x64_f8f6f4 with
+// format 4 (E2M1) on both sides; the lane's scale dword holds the E8M0 bytes
+// of blocks 0..3 of the slab for its row, and MFMA m takes block 2m + h (lane
+// layout and scale semantics checked on the device against a CPU model)
+__device__ __forceinline__ floatx16 mma32_mx(const u32x4 (&a)[2], const u32x4 (&b)[2], uint32_t sa, uint32_t sb,
+                                             int h, floatx16 c) {
+  typedef int intx8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    // E2M1 operands use the low 4 dwords of the 8-dword tuple; the high half is
+    // not read, so it holds the other chunk (no zero registers, fewer moves)
+    const int o = 1 - m;
+    intx8 av = {int(a[m][0]), int(a[m][1]), int(a[m][2]), int(a[m][3]),
+                int(a[o][0]), int(a[o][1]), int(a[o][2]), int(a[o][3])};
+    intx8 bv = {int(b[m][0]), int(b[m][1]), int(b[m][2]), int(b[m][3]),
+                int(b[o][0]), int(b[o][1]), int(b[o][2]), int(b[o][3])};
+    const int sh = 8 * (2 * m + h);
+    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 0, int((sa >> sh) & 0xFFu), 0,
+                                                        int((sb >> sh) & 0xFFu));
+  }
+  return c;
+}
+
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
 struct EpiArgs {
@@ -97,6 +121,12 @@ struct EpiArgs {
   int out_fp8;        // SwiGLU output in e4m3
   int F;              // SwiGLU width (gate rows [0,F), up rows [F,2F))
   int hilo_rows;      // head: rows [0,h) hold hi, [h,2h) lo terms; out = hi + lo
+  // MXFP4 operands: block scales in the slab-interleaved layout [K/128][ld][4]
+  const uint8_t* mx_sa;  // A scales, ld = mx_lda (M rounded up to the 256-row tile)
+  const uint8_t* mx_sb;  // B scales, ld = N
+  int mx_lda;
+  uint8_t* mx_out_s;     // SwiGLU MXFP4 output: scales of the [M, F] product, ld = mx_ldo
+  int mx_ldo;
 };
 
 // value of one product element after the dtype scale
@@ -322,18 +352,25 @@ struct TileCfg {
   static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "tile shape");
 };
 
-template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int SB>
+// MX: E2M1 operands with E8M0 block scales (FP8 false).  The scales ride the
+// slab ring: per slab, wave 0 copies the A tile's 256 rows x 4 scale bytes and
+// wave 1 the B tile's (1 KB each), so those two waves issue one copy more per
+// slab and wait for one more.
+template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int SB, bool MX = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, int M, int N, int K_bytes,
     int tiles_m, int n_tiles, EpiArgs e) {
   using C = TileCfg<BM, BN, WM, WN, STAGES, SB>;
   constexpr int IM = C::kIM, JN = C::kJN, LPS = C::kLPS, NC = C::kChunks / 2;
   static_assert(EPI != HR_EPI_SWIGLU || JN % 2 == 0, "SwiGLU waves hold gate/up block pairs");
+  static_assert(!MX || (!FP8 && BM == 256 && BN == 256 && SB == 64 && WM * WN >= 2),
+                "MXFP4: 256 x 256 tiles of 128-value (64-byte) slabs");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* sA = smem;                                   // [STAGES][BM rows][64 B]
   uint8_t* sB = smem + STAGES * C::kSlabA;              // [STAGES][BN rows][64 B]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
+  uint8_t* sS = smem + STAGES * (C::kSlabA + C::kSlabB);   // MX: [STAGES][A 1 KB | B 1 KB] scales
   // XCD-aware order: consecutive workgroup ids go round-robin over the 8 XCDs;
   // give each XCD a contiguous run of tiles so the m-tiles that share a weight
   // tile are served by one L2
@@ -379,6 +416,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
       src[j] = uint32_t(br) * uint32_t(K_bytes) + lc * 16;
     }
   }
+  // MX scale copies: lane l carries rows 4l .. 4l+3 (4 bytes each) of the
+  // A tile (wave 0) or of the B tile (wave 1, rows mapped as the B copies)
+  uint32_t s_src = 0, s_ld = 0;
+  if constexpr (MX) {
+    if (wave == 0) {
+      s_src = uint32_t(m0 + 4 * lane) * 4u;
+      s_ld = uint32_t(e.mx_lda) * 4u;
+    } else if (wave == 1) {
+      const int row = 4 * lane;
+      int br;
+      if constexpr (EPI == HR_EPI_SWIGLU) {
+        const int blk = row >> 5, off = row & 31;
+        const int a0 = (n0 >> 1) + (blk >> 1) * 32 + off;
+        br = (blk & 1) ? e.F + a0 : a0;
+      } else {
+        br = n0 + row;
+      }
+      s_src = uint32_t(br) * 4u;
+      s_ld = uint32_t(N) * 4u;
+    }
+  }
   const int slabs_total = K_bytes / SB;
   const int kz = blockIdx.z, ksplit = gridDim.z;
   const int sl0 = (slabs_total * kz) / ksplit, sl1 = (slabs_total * (kz + 1)) / ksplit;
@@ -391,6 +449,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
       const bool is_a = dst_off[j] < STAGES * C::kSlabA;
       lds_copy16((is_a ? x : w) + src[j] + ko, smem + dst_off[j] + stage * (is_a ? C::kSlabA : C::kSlabB));
     }
+    if constexpr (MX) {
+      if (wave < 2)
+        lds_copy16((wave == 0 ? e.mx_sa : e.mx_sb) + size_t(slab) * s_ld + s_src, sS + stage * 2048 + wave * 1024);
+    }
+  };
+  // wait until `pending` slabs issued after the needed one may still be in flight
+  auto wait_slabs = [&](int pending) {
+    if (MX && wave < 2) wait_stages<LPS + 1, STAGES>(pending);
+    else wait_stages<LPS, STAGES>(pending);
   };
 
   floatx16 acc[IM][JN];
@@ -412,9 +479,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
   const int a_row0 = wm * (BM / WM) + r32, b_row0 = wn * (BN / WN) + r32;
   auto chunk_of = [&](int c) { return FP8 ? 4 * (c >> 1) + 2 * h + (c & 1) : 2 * c + h; };
   typedef u32x4 Frag[NC];
-  auto read_frags = [&](int stage, Frag (&fa)[IM], Frag (&fb)[JN]) {
+  auto read_frags = [&](int stage, Frag (&fa)[IM], Frag (&fb)[JN], uint32_t (&sa)[IM], uint32_t (&sb)[JN]) {
     const uint8_t* A = sA + stage * C::kSlabA;
     const uint8_t* B = sB + stage * C::kSlabB;
+    if constexpr (MX) {
+      const uint8_t* S = sS + stage * 2048;
+#pragma unroll
+      for (int i = 0; i < IM; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(S + (a_row0 + i * 32) * 4);
+#pragma unroll
+      for (int j = 0; j < JN; ++j) sb[j] = *reinterpret_cast<const uint32_t*>(S + 1024 + (b_row0 + j * 32) * 4);
+    }
 #pragma unroll
     for (int j = 0; j < JN; ++j) {
       const int r = b_row0 + j * 32;
@@ -430,11 +504,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
         fa[i][c] = *reinterpret_cast<const u32x4*>(A + r * SB + ((chunk_of(c) ^ swz<SB>(r)) << 4));
     }
   };
-  auto mma_slab = [&](const Frag (&fa)[IM], const Frag (&fb)[JN]) {
+  auto mma_slab = [&](const Frag (&fa)[IM], const Frag (&fb)[JN], const uint32_t (&sa)[IM],
+                      const uint32_t (&sb)[JN]) {
 #pragma unroll
     for (int i = 0; i < IM; ++i)
 #pragma unroll
-      for (int j = 0; j < JN; ++j) acc[i][j] = mma32<FP8, NC>(fa[i], fb[j], acc[i][j]);
+      for (int j = 0; j < JN; ++j) {
+        if constexpr (MX) acc[i][j] = mma32_mx(fa[i], fb[j], sa[i], sb[j], h, acc[i][j]);
+        else acc[i][j] = mma32<FP8, NC>(fa[i], fb[j], acc[i][j]);
+      }
   };
   // Software pipeline: the fragments of slab it+1 are read from LDS while the
   // MFMAs of slab it run, so LDS latency hides behind MFMA work.  Slab it+1
@@ -442,26 +520,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
   // during the wait.  Slot (it-1) % STAGES is refilled after the barrier of
   // iteration it: every wave's reads from it happened in iteration it-2.
   Frag fa0[IM], fb0[JN], fa1[IM], fb1[JN];
+  uint32_t sa0[IM], sb0[JN], sa1[IM], sb1[JN];
   if (n_slabs > 0) {
-    wait_stages<LPS, STAGES>(min(STAGES - 2, n_slabs - 1));
+    wait_slabs(min(STAGES - 2, n_slabs - 1));
     lds_barrier();
-    read_frags(0, fa0, fb0);
+    read_frags(0, fa0, fb0, sa0, sb0);
   }
   int it = 0;
-  constexpr int kReads = (IM + JN) * NC, kMfma = IM * JN * (FP8 ? NC / 2 : NC);
-  auto step = [&](Frag (&fa)[IM], Frag (&fb)[JN], Frag (&fan)[IM], Frag (&fbn)[JN]) {
+  constexpr int kReads = (IM + JN) * (NC + (MX ? 1 : 0)), kMfma = IM * JN * (FP8 ? NC / 2 : NC);
+  auto step = [&](Frag (&fa)[IM], Frag (&fb)[JN], uint32_t (&sa)[IM], uint32_t (&sb)[JN], Frag (&fan)[IM],
+                  Frag (&fbn)[JN], uint32_t (&san)[IM], uint32_t (&sbn)[JN]) {
     // this slab's fragments were read one MFMA burst ago: settle them here so
     // no wait lands between the next slab's reads and these MFMAs
     wait_lds();
-    wait_stages<LPS, STAGES>(min(STAGES - 3, n_slabs - 2 - it));
+    wait_slabs(min(STAGES - 3, n_slabs - 2 - it));
     lds_barrier();
     if (it + STAGES - 1 < n_slabs) issue(sl0 + it + STAGES - 1, (it + STAGES - 1) % STAGES);
     // the next slab's fragments (after the last slab: a stale slot, never
     // used), issued one-for-one between this slab's MFMAs: issue is in order,
     // so a burst of LDS reads stalled behind the copies into LDS would
     // otherwise leave the matrix pipe idle (10% on the gate/up GEMM at M=512)
-    read_frags((it + 1) % STAGES, fan, fbn);
-    mma_slab(fa, fb);
+    read_frags((it + 1) % STAGES, fan, fbn, san, sbn);
+    mma_slab(fa, fb, sa, sb);
 #pragma unroll
     for (int q = 0; q < (kReads < kMfma ? kReads : kMfma); ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
@@ -473,12 +553,40 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
   };
   // unrolled by two so the current / next fragment sets are fixed registers
   while (it < n_slabs) {
-    step(fa0, fb0, fa1, fb1);
-    if (it < n_slabs) step(fa1, fb1, fa0, fb0);
+    step(fa0, fb0, sa0, sb0, fa1, fb1, sa1, sb1);
+    if (it < n_slabs) step(fa1, fb1, sa1, sb1, fa0, fb0, sa0, sb0);
   }
 
   // epilogue: 32x32 accumulator layout, lane holds column lane % 32 and rows
   // 8 (r / 4) + 4 (lane / 32) + r % 4 of its block, r = 0..15
+  if constexpr (MX && EPI == HR_EPI_SWIGLU) {
+    // silu(g) * u of one row's 32 columns of a gate/up block pair is one MX
+    // block of the down projection's input: its amax over the 32 lanes of the
+    // half-wave, the shared exponent, E2M1 codes, two per byte (lane pairs)
+    uint8_t* oc = static_cast<uint8_t*>(e.out);
+#pragma unroll
+    for (int i = 0; i < IM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * (BM / WM) + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+#pragma unroll
+        for (int jj = 0; jj < JN / 2; ++jj) {
+          const int cb = (n0 >> 1) + (wn * (JN / 2) + jj) * 32;     // first column of the block
+          const float a = silu(acc[i][2 * jj][r]) * acc[i][2 * jj + 1][r];
+          float am = fabsf(a);
+#pragma unroll
+          for (int m = 1; m < 32; m <<= 1) am = fmaxf(am, __shfl_xor(am, m, kWave));
+          const int ex = mx_block_exp(am);
+          const uint32_t code = e2m1_code(ldexpf(a, -ex));
+          const uint32_t hi = __shfl_xor(code, 1, kWave);
+          if (row < M && cb < e.F) {
+            if ((r32 & 1) == 0) oc[size_t(row) * (e.F / 2) + ((cb + r32) >> 1)] = uint8_t(code | (hi << 4));
+            if (r32 == 0) e.mx_out_s[mx_scale_off(row, cb >> 5, e.mx_ldo)] = uint8_t(ex + 127);
+          }
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < IM; ++i) {
 #pragma unroll
@@ -551,28 +659,29 @@ static void skinny(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, con
   }
 }
 
-template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int SB>
+template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int SB, bool MX = false>
 static void tiled_cfg(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
                       int ksplit, hipStream_t st) {
   using C = TileCfg<BM, BN, WM, WN, STAGES, SB>;
+  constexpr size_t kLds = C::kLds + (MX ? size_t(STAGES) * 2048 : 0);
   const int tiles_m = (M + BM - 1) / BM;
   const int ncols = (EPI == HR_EPI_SWIGLU) ? 2 * e.F : N;
   const int tiles_n = (ncols + BN - 1) / BN;
   const int n_tiles = tiles_m * tiles_n;
-  auto kern = gemm_tiled_kernel<EPI, FP8, BM, BN, WM, WN, STAGES, SB>;
+  auto kern = gemm_tiled_kernel<EPI, FP8, BM, BN, WM, WN, STAGES, SB, MX>;
   static bool lds_raised = false;  // above the 64 KB default dynamic-LDS limit
-  if (C::kLds > 65536 && !lds_raised) {
+  if (kLds > 65536 && !lds_raised) {
     hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                        int(C::kLds));
+                        int(kLds));
     lds_raised = true;
   }
   dim3 grid(n_tiles, 1, ksplit);
-  kern<<<grid, C::kThreads, C::kLds, st>>>(x, w, M, N, Kb, tiles_m, n_tiles, e);
+  kern<<<grid, C::kThreads, kLds, st>>>(x, w, M, N, Kb, tiles_m, n_tiles, e);
 }
 
 // Launch with a split-K factor that fills the 256 CUs for the residual
 // projections (fp32 atomics into h), or the given one.
-template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int SB = 64>
+template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int SB = 64, bool MX = false>
 static void tiled_fill(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
                        hipStream_t st, int ks_force = 0) {
   const int ncols = (EPI == HR_EPI_SWIGLU) ? 2 * e.F : N;
@@ -582,7 +691,7 @@ static void tiled_fill(const uint8_t* x, const uint8_t* w, int M, int N, int Kb,
   if (EPI == HR_EPI_RESIDUAL && ks_force > 0) ks = ks_force;
   const int max_ks = Kb / SB / 4 > 0 ? Kb / SB / 4 : 1;   // >= 4 slabs per split
   if (ks > max_ks) ks = max_ks;
-  tiled_cfg<EPI, FP8, BM, BN, WM, WN, STAGES, SB>(x, w, M, N, Kb, e, ks, st);
+  tiled_cfg<EPI, FP8, BM, BN, WM, WN, STAGES, SB, MX>(x, w, M, N, Kb, e, ks, st);
 }
 
 // Tile configuration of the large-M GEMM, per projection and M range, from
@@ -656,6 +765,28 @@ void launch_linear(const void* x, const void* w, const float* w_scale, float x_s
   else if (epi == HR_EPI_RESIDUAL) { HR_DISPATCH(HR_EPI_RESIDUAL) }
   else { HR_DISPATCH(HR_EPI_SWIGLU) }
 #undef HR_DISPATCH
+}
+
+// MXFP4 x MXFP4: x codes [M, K/2] with scales (ld lda), w codes [N, K/2] with
+// scales (ld N); RESIDUAL adds into fp32 out [M, N]; SWIGLU (N = 2F) writes the
+// MXFP4 product: codes [M, F/2] into out, scales (ld ldo) into out_scales.
+// Every M runs 256 x 256 tiles.
+void launch_linear_mx(const uint8_t* x, const uint8_t* x_scales, int lda, const uint8_t* w,
+                      const uint8_t* w_scales, int M, int N, int K, int epi, void* out, uint8_t* out_scales,
+                      int ldo, hipStream_t st) {
+  EpiArgs e{};
+  e.epi = epi;
+  e.out = out;
+  e.ldo = N;
+  e.F = N / 2;
+  e.mx_sa = x_scales;
+  e.mx_sb = w_scales;
+  e.mx_lda = lda;
+  e.mx_out_s = out_scales;
+  e.mx_ldo = ldo;
+  const int Kb = K / 2;
+  if (epi == HR_EPI_SWIGLU) tiled_fill<HR_EPI_SWIGLU, false, 256, 256, 4, 2, 4, 64, true>(x, w, M, N, Kb, e, st);
+  else tiled_fill<HR_EPI_RESIDUAL, false, 256, 256, 4, 2, 4, 64, true>(x, w, M, N, Kb, e, st);
 }
 
 // Head: zsplit bf16 [2n, D] (hi rows then lo rows), W bf16 [N, D] -> fp32 [n, N]

@@ -41,6 +41,12 @@ void launch_rmsnorm(const float* h, int T, int D, const void* w, float eps, void
 void launch_final_split(const float* h, const int32_t* cu, int seq0, int n, int D, const void* w,
                         float eps, int n_rows, void* zsplit, hipStream_t st);
 void launch_quant_weight(const void* w, int N, int K, uint8_t* w8, float* scale, hipStream_t st);
+// MXFP4: codes [M, K/2] (two per byte, element 2i low), scales in the
+// slab-interleaved layout [K/128][ld_s][4] (ld_s >= M)
+void launch_quant_mx(const void* x, bool f32, int M, int K, const float* col, const float* row_scale,
+                     uint8_t* codes, uint8_t* scales, int ld_s, hipStream_t st);
+void launch_rmsnorm_mx(const float* h, int T, int D, const void* w, const float* col, float eps,
+                       uint8_t* codes, uint8_t* scales, int ld_s, hipStream_t st);
 
 void launch_qknorm_rope_kv(const void* qkv, int T, int Hq, int Hkv, int d, float theta, float eps,
                            const int32_t* cu, const int32_t* start_pos, const int32_t* cache_slot,
@@ -67,6 +73,9 @@ void launch_attention(const void* q, const void* kc, const void* vc, const int32
 
 void launch_linear(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8,
                    int M, int N, int K, int epi, void* out, float out_scale, hipStream_t st);
+void launch_linear_mx(const uint8_t* x, const uint8_t* x_scales, int lda, const uint8_t* w,
+                      const uint8_t* w_scales, int M, int N, int K, int epi, void* out, uint8_t* out_scales,
+                      int ldo, hipStream_t st);
 void launch_head_gemm(const void* zsplit, int n, const void* w, int N, int D, float* out,
                       hipStream_t st);
 

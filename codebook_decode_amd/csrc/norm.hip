@@ -6,6 +6,10 @@
 //   final_split   : z = RMS(h[last row of s]) * w in fp32, stored as two bf16
 //                   terms hi = bf16(z), lo = bf16(z - hi) for the head GEMM
 //   quant_weight  : per-output-channel E4M3 packing of a bf16 weight
+//   MXFP4 (OCP MX: E2M1 values, one E8M0 scale per 32 consecutive K values):
+//   quant_mx      : weight packing w' = (w * col) * row, or activation rows
+//                   x' = x * col, one thread per 32-value block
+//   rmsnorm_mx    : x = RMS(h) * w * col straight to MXFP4 (4 threads per block)
 // The fp32 residual h is read once into registers (one row per workgroup,
 // 8 elements per thread, 128-bit accesses); the row sum of squares is a
 // wavefront butterfly plus a cross-wave LDS step.
@@ -201,6 +205,142 @@ void launch_final_split(const float* h, const int32_t* cu, int seq0, int n, int 
 
 void launch_quant_weight(const void* w, int N, int K, uint8_t* w8, float* scale, hipStream_t st) {
   quant_weight_kernel<<<N, kNormThreads, 0, st>>>(static_cast<const uint16_t*>(w), K, w8, scale);
+}
+
+// ---------------------------------------------------------------- MXFP4
+// Encode 32 values (one block) held by one thread: codes (16 B, element 2i in
+// the low nibble of byte i) and the scale byte.
+__device__ __forceinline__ void mx_encode32(const float* v, u32x4& codes, uint32_t& sbyte) {
+  float am = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
+  const int e = mx_block_exp(am);
+  sbyte = uint32_t(e + 127);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t wd = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wd |= e2m1_code(ldexpf(v[8 * q + i], -e)) << (4 * i);
+    codes[q] = wd;
+  }
+}
+
+// One thread per (row, block).  SRC 0: bf16 rows, 1: fp32 rows.  v = x * col
+// (one binary32 rounding) then * row (a second one), as the packing contract.
+template <int SRC>
+__global__ __launch_bounds__(256) void quant_mx_kernel(const void* __restrict__ x, int M, int K,
+                                                       const float* __restrict__ col,
+                                                       const float* __restrict__ row_scale,
+                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                       int ld_s) {
+  const int nb = K >> 5;
+  const size_t id = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (id >= size_t(M) * nb) return;
+  const int r = int(id / nb), kb = int(id % nb);
+  float v[32];
+  if (SRC == 0) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + size_t(r) * K + kb * 32);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 t = p[q];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { v[8 * q + 2 * j] = bf_lo(t[j]); v[8 * q + 2 * j + 1] = bf_hi(t[j]); }
+    }
+  } else {
+    const floatx4* p = reinterpret_cast<const floatx4*>(static_cast<const float*>(x) + size_t(r) * K + kb * 32);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const floatx4 t = p[q];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[4 * q + j] = t[j];
+    }
+  }
+  if (col) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = v[i] * col[kb * 32 + i];
+  }
+  if (row_scale) {
+    const float rs = row_scale[r];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = v[i] * rs;
+  }
+  u32x4 c;
+  uint32_t sb;
+  mx_encode32(v, c, sb);
+  reinterpret_cast<u32x4*>(codes + size_t(r) * (K / 2))[kb] = c;
+  scales[mx_scale_off(r, kb, ld_s)] = uint8_t(sb);
+}
+
+// x = RMS(h) * w * col -> MXFP4.  One row per workgroup, 8 values per thread
+// (as rmsnorm_kernel); the 4 threads of a 32-value block are adjacent lanes.
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_mx_kernel(
+    const float* __restrict__ h, int D, const uint16_t* __restrict__ w, const float* __restrict__ col,
+    float eps, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int ld_s) {
+  __shared__ float red[kNormThreads / 64];
+  const int t = blockIdx.x;
+  const int n8 = D >> 3;
+  float v[kNormMaxPerThread][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < kNormMaxPerThread; ++c) {
+    const int i8 = threadIdx.x + c * kNormThreads;
+    if (i8 < n8) {
+      const floatx4* p = reinterpret_cast<const floatx4*>(h + size_t(t) * D) + 2 * i8;
+      const floatx4 a = p[0], b = p[1];
+      v[c][0] = a[0]; v[c][1] = a[1]; v[c][2] = a[2]; v[c][3] = a[3];
+      v[c][4] = b[0]; v[c][5] = b[1]; v[c][6] = b[2]; v[c][7] = b[3];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss += v[c][j] * v[c][j];
+    }
+  }
+  const float tot = block_sum(ss, red);
+  const float r = 1.0f / __builtin_sqrtf(tot / float(D) + eps);
+#pragma unroll
+  for (int c = 0; c < kNormMaxPerThread; ++c) {
+    const int i8 = threadIdx.x + c * kNormThreads;
+    if (c * kNormThreads >= n8) break;            // uniform: every lane of the block takes part below
+    const bool ok = i8 < n8;
+    float y[8];
+    float am = 0.f;
+    if (ok) {
+      const u32x4 wq = reinterpret_cast<const u32x4*>(w)[i8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y[2 * j] = v[c][2 * j] * r * bf_lo(wq[j]);
+        y[2 * j + 1] = v[c][2 * j + 1] * r * bf_hi(wq[j]);
+      }
+      if (col) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = y[j] * col[8 * i8 + j];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(y[j]));
+    }
+    am = fmaxf(am, __shfl_xor(am, 1, kWave));
+    am = fmaxf(am, __shfl_xor(am, 2, kWave));
+    if (ok) {
+      const int e = mx_block_exp(am);
+      uint32_t wd = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wd |= e2m1_code(ldexpf(y[j], -e)) << (4 * j);
+      reinterpret_cast<uint32_t*>(codes + size_t(t) * (D / 2))[i8] = wd;
+      if ((i8 & 3) == 0) scales[mx_scale_off(t, i8 >> 2, ld_s)] = uint8_t(e + 127);
+    }
+  }
+}
+
+void launch_quant_mx(const void* x, bool f32, int M, int K, const float* col, const float* row_scale,
+                     uint8_t* codes, uint8_t* scales, int ld_s, hipStream_t st) {
+  const size_t n = size_t(M) * (K / 32);
+  const int grid = int((n + 255) / 256);
+  if (f32) quant_mx_kernel<1><<<grid, 256, 0, st>>>(x, M, K, col, row_scale, codes, scales, ld_s);
+  else quant_mx_kernel<0><<<grid, 256, 0, st>>>(x, M, K, col, row_scale, codes, scales, ld_s);
+}
+
+void launch_rmsnorm_mx(const float* h, int T, int D, const void* w, const float* col, float eps,
+                       uint8_t* codes, uint8_t* scales, int ld_s, hipStream_t st) {
+  rmsnorm_mx_kernel<<<T, kNormThreads, 0, st>>>(h, D, static_cast<const uint16_t*>(w), col, eps, codes, scales,
+                                                ld_s);
 }
 
 }  // namespace hr

@@ -106,6 +106,10 @@ def lib() -> ctypes.CDLL:
             "hr_head_logits": (c_i32, [c_vp, P(HrBatch), c_i32, c_vp, c_f32, c_vp, c_i32, c_i32, c_vp, c_vp,
                                        c_sz, c_vp]),
             "hr_quantize_weight_e4m3": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp]),
+            "hr_quantize_mxfp4": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp]),
+            "hr_rmsnorm_mxfp4": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_f32, c_vp, c_vp, c_vp, c_i32, c_vp]),
+            "hr_linear_mxfp4": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp,
+                                        c_i32, c_vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -319,3 +323,27 @@ def hr_head_logits(h, batch: Batch, D, final_norm_w, eps, head_w, n_codebooks, c
 def hr_quantize_weight_e4m3(w, N, K, w8, scale, stream=None) -> None:
     _check(lib().hr_quantize_weight_e4m3(ptr(w), N, K, ptr(w8), ptr(scale),
                                          stream if stream is not None else current_stream()))
+
+
+def mx_scale_bytes(rows: int, K: int) -> int:
+    """Bytes of an MXFP4 scale array of ``rows`` rows (ld = rows) over K."""
+    return (K // 128) * rows * 4
+
+
+def hr_quantize_mxfp4(x, M, K, codes, scales, ld_scales, col_scale=None, row_scale=None, stream=None) -> None:
+    import torch
+    f32 = 1 if x.dtype == torch.float32 else 0
+    _check(lib().hr_quantize_mxfp4(ptr(x), f32, M, K, ptr(col_scale), ptr(row_scale), ptr(codes), ptr(scales),
+                                   ld_scales, stream if stream is not None else current_stream()))
+
+
+def hr_rmsnorm_mxfp4(h, T, D, norm_w, eps, codes, scales, ld_scales, col_scale=None, stream=None) -> None:
+    _check(lib().hr_rmsnorm_mxfp4(ptr(h), T, D, ptr(norm_w), eps, ptr(col_scale), ptr(codes), ptr(scales),
+                                  ld_scales, stream if stream is not None else current_stream()))
+
+
+def hr_linear_mxfp4(x, x_scales, ld_x_scales, w, w_scales, M, N, K, epi, out, out_scales=None, ld_out_scales=0,
+                    stream=None) -> None:
+    _check(lib().hr_linear_mxfp4(ptr(x), ptr(x_scales), ld_x_scales, ptr(w), ptr(w_scales), M, N, K, epi,
+                                 ptr(out), ptr(out_scales), ld_out_scales,
+                                 stream if stream is not None else current_stream()))

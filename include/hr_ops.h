@@ -95,6 +95,49 @@ hr_status hr_head_logits(const float* h, const hr_batch* batch, int32_t D, const
 hr_status hr_quantize_weight_e4m3(const void* w, int32_t N, int32_t K, uint8_t* w8, float* scale,
                                   hipStream_t stream);
 
+/* ---- MXFP4 band of the O and FFN projections (NEXT-4) -------------------
+ * flashrt-structures 0.2.0, prefill_tower/fp8_chain.py: the FP4 band table (the
+ * FFN pair and the attention output projection in 4-bit with dynamic block
+ * scales, QKV unchanged), _awq_scale (per-input-channel pre-scale s; the GEMM
+ * columns carry s, the tensor feeding the GEMM carries 1/s) and
+ * _interleave_gu_rows (the down projection's 1/s folded into the up rows).  On
+ * gfx950 the format is OCP MX FP4: E2M1 values (0, 0.5, 1, 1.5, 2, 3, 4, 6 and
+ * negatives; nearest, ties to the even code, saturating at 6), one E8M0 scale
+ * 2^e per 32 consecutive values along K, e = floor(log2 max|v|) - 2 clamped to
+ * [-127, 127] (byte e + 127; an all-zero block gets byte 0).
+ * Layouts: codes u8 [rows, K/2], element 2i in the low nibble of byte i;
+ * scales u8 in the slab-interleaved layout [K/128][ld][4] (block kb of row r at
+ * ((kb/4) * ld + r) * 4 + kb % 4), ld >= rows.  K must be a multiple of 128;
+ * codes and scales 16-byte aligned. */
+
+/* Quantise rows: v = x[r, k] * col_scale[k] * row_scale[r] (each product one
+ * binary32 rounding, in that order; a NULL vector is 1), then MX blocks.
+ * x bf16 or fp32 (x_is_fp32) [M, K].  Weights: col_scale = AWQ s of the input
+ * channels, row_scale = 1/s of the down projection on the up rows.
+ * Activations: col_scale = 1/s.  HR_EINVAL on sizes or ld_scales < M. */
+hr_status hr_quantize_mxfp4(const void* x, int32_t x_is_fp32, int32_t M, int32_t K, const float* col_scale,
+                            const float* row_scale, uint8_t* codes, uint8_t* scales, int32_t ld_scales,
+                            hipStream_t stream);
+
+/* x = RMS(h; norm_w) * col_scale straight to MXFP4 (the gate/up input with its
+ * 1/s).  h fp32 [T, D], D a multiple of 128 and <= 8192. */
+hr_status hr_rmsnorm_mxfp4(const float* h, int32_t T, int32_t D, const void* norm_w, float eps,
+                           const float* col_scale, uint8_t* codes, uint8_t* scales, int32_t ld_scales,
+                           hipStream_t stream);
+
+/* MXFP4 GEMM y = x w^T with fp32 accumulation of the scaled E2M1 products.
+ *  x codes [M, K/2] with scales (ld_x_scales >= M rounded up to 256: the
+ *  256-row tiles read whole scale rows; rows >= M are ignored), w codes
+ *  [N, K/2] with scales (ld N).
+ *  HR_EPI_RESIDUAL: out fp32 [M, N] += y (N a multiple of 256).
+ *  HR_EPI_SWIGLU: N = 2F, w rows [gate; up]; act = silu(gate) * up goes out as
+ *  MXFP4: codes [M, F/2] into out, scales into out_scales with ld_out_scales
+ *  (>= M rounded up to 256, so the result can feed this call as x); F a
+ *  multiple of 128. */
+hr_status hr_linear_mxfp4(const uint8_t* x, const uint8_t* x_scales, int32_t ld_x_scales, const uint8_t* w,
+                          const uint8_t* w_scales, int32_t M, int32_t N, int32_t K, hr_epilogue epi, void* out,
+                          uint8_t* out_scales, int32_t ld_out_scales, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

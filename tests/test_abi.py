@@ -220,6 +220,25 @@ def test_codebook_policy_validation(case, status):
     assert st == status, (st, H.hr_last_error())
 
 
+def test_mxfp4_validation():
+    lib = H.lib()
+    # K not a multiple of 128; ld below M
+    assert lib.hr_quantize_mxfp4(FAKE, 0, 4, 96, None, None, FAKE, FAKE, 4, None) == H.HR_EINVAL
+    assert lib.hr_quantize_mxfp4(FAKE, 0, 8, 128, None, None, FAKE, FAKE, 4, None) == H.HR_EINVAL
+    assert lib.hr_rmsnorm_mxfp4(FAKE, 4, 200, FAKE, 1e-6, None, FAKE, FAKE, 4, None) == H.HR_EINVAL
+    lin = lib.hr_linear_mxfp4
+    # x scales must cover the 256-row tiles; N multiple of 256; bf16 epilogue refused
+    assert lin(FAKE, FAKE, 100, FAKE, FAKE, 100, 256, 256, H.HR_EPI_RESIDUAL, FAKE, None, 0, None) == H.HR_EINVAL
+    assert lin(FAKE, FAKE, 256, FAKE, FAKE, 100, 384, 256, H.HR_EPI_RESIDUAL, FAKE, None, 0, None) == \
+        H.HR_EUNSUPPORTED
+    assert lin(FAKE, FAKE, 256, FAKE, FAKE, 100, 256, 256, H.HR_EPI_BF16, FAKE, None, 0, None) == H.HR_EINVAL
+    assert lin(FAKE, FAKE, 256, FAKE, FAKE, 100, 512, 256, H.HR_EPI_SWIGLU, FAKE, None, 0, None) == H.HR_EINVAL
+    assert lin(FAKE, FAKE, 256, FAKE, FAKE, 100, 512, 256, H.HR_EPI_SWIGLU, FAKE, FAKE, 128, None) == H.HR_EINVAL
+    assert lin(FAKE, FAKE, 256, FAKE, FAKE, 100, 512, 200, H.HR_EPI_SWIGLU, FAKE, FAKE, 256, None) == H.HR_EINVAL
+    assert lin(FAKE + 4, FAKE, 256, FAKE, FAKE, 100, 512, 256, H.HR_EPI_SWIGLU, FAKE, FAKE, 256, None) == \
+        H.HR_EALIGN
+
+
 @pytest.mark.parametrize("ct,slots,ws,ws_bytes,status", [
     (0, 4, FAKE, 1 << 40, H.HR_EINVAL),           # chunk_tiles < 1
     (2, 0, FAKE, 1 << 40, H.HR_EINVAL),           # no slot

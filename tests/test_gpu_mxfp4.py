@@ -1,0 +1,182 @@
+"""MXFP4 (OCP MX) operations on the GPU against the oracle.
+
+* Weight and activation quantisation: codes and scale bytes bit-exact (both
+  sides quantise the same binary32 values).
+* RMSNorm straight to MXFP4: the GPU's fp32 norm and the oracle's float64 one
+  differ in the last bits, so a code may move by one step where a value sits on
+  a rounding boundary; everything else is equal.
+* The MXFP4 GEMM (residual epilogue): fp32 accumulation of exactly
+  representable scaled products, against the float64 blocked product.
+* The gate/up GEMM with the SwiGLU epilogue writing MXFP4: as for the norm,
+  codes equal up to one-step moves at boundaries, scales up to binade edges.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import mxfp4 as mx
+from oracle import numerics as nx
+from oracle import prefill as op
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def H():
+    import codebook_decode_amd.hr as H
+    H.lib()
+    return H
+
+
+def slab_layout(scales_rk: np.ndarray, ld: int) -> np.ndarray:
+    """[R, K/32] scale bytes -> the slab-interleaved [K/128][ld][4] layout."""
+    R, nb = scales_rk.shape
+    out = np.zeros((nb // 4, ld, 4), np.uint8)
+    out[:, :R, :] = scales_rk.reshape(R, nb // 4, 4).transpose(1, 0, 2)
+    return out
+
+
+def from_slab_layout(buf: np.ndarray, R: int, K: int, ld: int) -> np.ndarray:
+    return buf.reshape(K // 128, ld, 4)[:, :R, :].transpose(1, 0, 2).reshape(R, K // 32)
+
+
+def dev_mx(codes_rk: np.ndarray, scales_rk: np.ndarray, ld: int):
+    from gpu_util import dev
+    return dev(mx.pack_codes(codes_rk)), dev(slab_layout(scales_rk, ld).reshape(-1))
+
+
+def _empty_mx(R, K, ld):
+    import torch
+    return (torch.zeros((R, K // 2), dtype=torch.uint8, device="cuda"),
+            torch.zeros((K // 128) * ld * 4, dtype=torch.uint8, device="cuda"))
+
+
+@pytest.mark.parametrize("N,K,with_row", [(512, 2560, True), (256, 4096, False), (768, 256, True)])
+def test_weight_quantisation_bit_exact(H, N, K, with_row):
+    import torch
+    from gpu_util import log, dev, dev_bf16
+    rng = np.random.default_rng(N + K)
+    wb = nx.f32_to_bf16((rng.standard_normal((N, K)) * 0.02 * np.exp(rng.normal(0, 1, (N, 1)))).astype(np.float32))
+    col = rng.uniform(0.25, 4.0, K).astype(np.float32)
+    row = rng.uniform(0.25, 4.0, N).astype(np.float32) if with_row else None
+    log(f"mxfp4 weight quantisation N={N} K={K}")
+    codes, scales = _empty_mx(N, K, N)
+    H.hr_quantize_mxfp4(dev_bf16(wb), N, K, codes, scales, N, col_scale=dev(col),
+                        row_scale=dev(row) if row is not None else None)
+    torch.cuda.synchronize()
+    rc, rs = mx.pack_weight(nx.bf16_to_f32(wb), col, row)
+    np.testing.assert_array_equal(codes.cpu().numpy(), mx.pack_codes(rc))
+    np.testing.assert_array_equal(from_slab_layout(scales.cpu().numpy(), N, K, N), rs)
+
+
+@pytest.mark.parametrize("M,K,f32", [(13, 4096, False), (300, 2560, True), (512, 4096, False)])
+def test_activation_quantisation_bit_exact(H, M, K, f32):
+    import torch
+    from gpu_util import log, dev, dev_bf16
+    rng = np.random.default_rng(M * 7 + K)
+    x = (rng.standard_normal((M, K)) * np.exp(rng.normal(0, 2, (M, 1)))).astype(np.float32)
+    x[0, :64] = 0.0                                        # an all-zero block
+    x[1 % M, 32:64] = np.float32(2.0 ** -140)              # subnormal block maximum
+    col = rng.uniform(0.25, 4.0, K).astype(np.float32)
+    if f32:
+        d_x = dev(x)
+        xv = x
+    else:
+        bits = nx.f32_to_bf16(x)
+        d_x = dev_bf16(bits)
+        xv = nx.bf16_to_f32(bits)
+    ld = (M + 255) // 256 * 256
+    log(f"mxfp4 activation quantisation M={M} K={K} f32={f32}")
+    codes, scales = _empty_mx(M, K, ld)
+    H.hr_quantize_mxfp4(d_x, M, K, codes, scales, ld, col_scale=dev(col))
+    torch.cuda.synchronize()
+    rc, rs = mx.quantize_blocks((xv * col[None, :]).astype(np.float32).astype(np.float64))
+    np.testing.assert_array_equal(codes.cpu().numpy(), mx.pack_codes(rc))
+    np.testing.assert_array_equal(from_slab_layout(scales.cpu().numpy(), M, K, ld), rs)
+
+
+def _one_step_close(gc, gs, rc, rs, what):
+    """Codes equal except one-step moves of a value that sat on a boundary
+    (<= 0.5% of the values), scale bytes equal except for blocks whose max sat on
+    a binade edge (<= 0.5% of the blocks)."""
+    gv = mx.e2m1_decode(gc)
+    rv = mx.e2m1_decode(rc)
+    same_scale = np.repeat(gs == rs, 32, axis=-1)
+    diff = (gv != rv) & same_scale
+    frac = diff.mean()
+    mags = np.abs(rv[diff])
+    step = np.where(mags < 2, 0.5, np.where(mags < 4, 1.0, 2.0))
+    assert np.all(np.abs(gv[diff] - rv[diff]) <= step + 1e-12), f"{what}: a code moved by more than one step"
+    assert frac <= 5e-3, f"{what}: {frac:.2e} of the codes differ"
+    assert (gs != rs).mean() <= 5e-3, f"{what}: {(gs != rs).mean():.2e} of the scales differ"
+    return frac
+
+
+@pytest.mark.parametrize("T,D", [(7, 256), (300, 2560)])
+def test_rmsnorm_mxfp4(H, T, D):
+    import torch
+    from gpu_util import log, dev, dev_bf16
+    rng = np.random.default_rng(T + D)
+    h = (rng.standard_normal((T, D)) * 3).astype(np.float32)
+    w = nx.f32_to_bf16((1 + 0.1 * rng.standard_normal(D)).astype(np.float32))
+    col = rng.uniform(0.25, 4.0, D).astype(np.float32)
+    ld = (T + 255) // 256 * 256
+    log(f"rmsnorm mxfp4 T={T} D={D}")
+    codes, scales = _empty_mx(T, D, ld)
+    H.hr_rmsnorm_mxfp4(dev(h), T, D, dev_bf16(w), 1e-6, codes, scales, ld, col_scale=dev(col))
+    torch.cuda.synchronize()
+    x = op.rms_norm(h.astype(np.float64), nx.bf16_to_f64(w), 1e-6) * col.astype(np.float64)[None, :]
+    rc, rs = mx.quantize_blocks(x)
+    gc = mx.unpack_codes(codes.cpu().numpy())
+    gs = from_slab_layout(scales.cpu().numpy(), T, D, ld)
+    _one_step_close(gc, gs, rc, rs, "rmsnorm")
+
+
+def _random_mx(rng, R, K, lo=118, hi=132):
+    codes = rng.integers(0, 16, (R, K)).astype(np.uint8)
+    scales = rng.integers(lo, hi, (R, K // 32)).astype(np.uint8)
+    return codes, scales
+
+
+@pytest.mark.parametrize("M,N,K", [(13, 512, 2560), (300, 2560, 4096), (512, 256, 9728), (600, 768, 256)])
+def test_linear_mxfp4_residual(H, M, N, K):
+    import torch
+    from gpu_util import log, dev
+    rng = np.random.default_rng(M + N + K)
+    xc, xs = _random_mx(rng, M, K)
+    wc, ws = _random_mx(rng, N, K)
+    ld = (M + 255) // 256 * 256
+    h0 = rng.standard_normal((M, N)).astype(np.float32)
+    out = dev(h0.copy())
+    dx, dxs = dev_mx(xc, xs, ld)
+    dw, dws = dev_mx(wc, ws, N)
+    log(f"linear mxfp4 residual M={M} N={N} K={K}")
+    H.hr_linear_mxfp4(dx, dxs, ld, dw, dws, M, N, K, H.HR_EPI_RESIDUAL, out)
+    torch.cuda.synchronize()
+    ref = h0.astype(np.float64) + mx.mx_matmul(xc, xs, wc, ws)
+    got = out.cpu().numpy().astype(np.float64)
+    scale = np.abs(mx.dequantize_blocks(xc, xs)) @ np.abs(mx.dequantize_blocks(wc, ws)).T + np.abs(h0)
+    err = np.abs(got - ref) / (scale + 1e-30)
+    assert err.max() < 2e-5, err.max()        # fp32 sums of K/64 MFMA partials
+
+
+@pytest.mark.parametrize("M,F,K", [(13, 256, 2560), (512, 768, 2560), (300, 9728, 2560)])
+def test_linear_mxfp4_swiglu_to_mxfp4(H, M, F, K):
+    import torch
+    from gpu_util import log
+    rng = np.random.default_rng(M + F)
+    xc, xs = _random_mx(rng, M, K, 120, 126)
+    wc, ws = _random_mx(rng, 2 * F, K, 112, 118)
+    ld = (M + 255) // 256 * 256
+    dx, dxs = dev_mx(xc, xs, ld)
+    dw, dws = dev_mx(wc, ws, 2 * F)
+    oc, os_ = _empty_mx(M, F, ld)
+    log(f"linear mxfp4 swiglu M={M} F={F} K={K}")
+    H.hr_linear_mxfp4(dx, dxs, ld, dw, dws, M, 2 * F, K, H.HR_EPI_SWIGLU, oc, os_, ld)
+    torch.cuda.synchronize()
+    gu = mx.mx_matmul(xc, xs, wc, ws)
+    act = op.silu(gu[:, :F]) * gu[:, F:]
+    rc, rs = mx.quantize_blocks(act)
+    gc = mx.unpack_codes(oc.cpu().numpy())
+    gs = from_slab_layout(os_.cpu().numpy(), M, F, ld)
+    _one_step_close(gc, gs, rc, rs, "swiglu")
