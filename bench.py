@@ -30,6 +30,7 @@ METRIC = "prefill ms/prompt at P=13, prompt tok/s at P=512; % of MFMA/HBM roofli
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
+FP4_PEAK_TFLOPS = 10100.0     # dense E2M1 (MXFP4) MFMA
 
 
 def log(msg):
@@ -241,6 +242,33 @@ def fp8_layer(H, m, dev_layer, reps=20):
     return {"workload": "fp8_layer_d2560_p512_pad544 (non-causal over 512 used keys)",
             "us_per_layer_wall": round(sec * 1e6, 2), "e4m3_gflop": round(e4m3_flops / 1e9, 2),
             "attention_gflop_bf16": round(attn_flops / 1e9, 2), "floor_us": round(t_floor * 1e6, 2),
+            "frac_of_floor": round(t_floor / sec, 4)}
+
+
+def mxfp4_layer(H, m, dev_layer, reps=20):
+    """The MXFP4 band of one 4B layer at P = 512, causal: O, gate/up and down
+    on E2M1 operands with E8M0 block scales (weights packed on the device; AWQ
+    vectors of 1: the timing does not depend on their values), QKV and
+    attention bf16."""
+    import synth
+    from gpu_util import dev
+    from model_util import dims_of, kv_cache, mx_pack, workspace
+    P, cap = 512, 512
+    dl, mxd = mx_pack(H, dev_layer, m)
+    layer = H.make_layer(dl, H.HR_MXFP4, mx=mxd)
+    dims = dims_of(H, m, True, 1)
+    kc, vc = kv_cache(m, 1, cap, poison=False)
+    kv = H.make_kv(kc, vc, cap, 1)
+    b = H.Batch([0, P], [0], [0])
+    h = dev(synth.bf16_bits_to_f32(synth.embed_rows(m, synth.prompt_ids(m, P))))
+    ws = workspace(H, dims, H.HR_MXFP4, P)
+    sec = time_events(lambda: H.hr_prefill_layer(dims, layer, b, h, kv, ws), reps)
+    fp4_flops = 2.0 * P * (m.attn_width * m.hidden + 2 * m.ffn * m.hidden + m.ffn * m.hidden)
+    bf16_flops = 2.0 * P * m.hidden * m.qkv_rows + 2.0 * 2 * m.n_q_heads * m.head_dim * P * P / 2
+    t_floor = fp4_flops / (FP4_PEAK_TFLOPS * 1e12) + bf16_flops / (BF16_PEAK_TFLOPS * 1e12)
+    return {"workload": "mxfp4_layer_d2560_p512 (causal; O, gate/up, down MXFP4)",
+            "us_per_layer_wall": round(sec * 1e6, 2), "fp4_gflop": round(fp4_flops / 1e9, 2),
+            "bf16_gflop": round(bf16_flops / 1e9, 2), "floor_us": round(t_floor * 1e6, 2),
             "frac_of_floor": round(t_floor / sec, 4)}
 
 
@@ -515,6 +543,7 @@ def main():
                        "roofline": hbm(weight_bytes + head_bytes, sec128)}
         out["layer_d2560"] = layer_rotated(H, m, dev_layers)
         out["fp8_layer"] = fp8_layer(H, m, dev_layers[0])
+        out["mxfp4_layer"] = mxfp4_layer(H, m, dev_layers[0])
         out["varlen32"] = varlen_batch(H, m, layers, shared)
         out["codebook_b64"] = codebook_steps(H, m, shared)
         out["codebook_sampled_b64"] = codebook_policy_steps(H, m, shared)

@@ -124,7 +124,8 @@ hr_status check_batch(const hr_dims* d, const hr_batch* b, const hr_kv* kv) {
 
 hr_status check_layer(const hr_dims* d, const hr_layer* L, int idx) {
   if (!L) return fail(HR_EINVAL, "layer %d is NULL", idx);
-  if (L->wtype != HR_BF16 && L->wtype != HR_FP8_E4M3) return fail(HR_EINVAL, "layer %d: bad wtype", idx);
+  if (L->wtype != HR_BF16 && L->wtype != HR_FP8_E4M3 && L->wtype != HR_MXFP4)
+    return fail(HR_EINVAL, "layer %d: bad wtype", idx);
   const void* ptrs[] = {L->in_norm_w, L->post_norm_w, L->q_norm_w, L->k_norm_w,
                         L->w_qkv,     L->w_o,         L->w_gu,     L->w_down};
   const char* names[] = {"in_norm_w", "post_norm_w", "q_norm_w", "k_norm_w", "w_qkv", "w_o", "w_gu", "w_down"};
@@ -140,13 +141,24 @@ hr_status check_layer(const hr_dims* d, const hr_layer* L, int idx) {
       if (!(v > 0.f) || !std::isfinite(v))
         return fail(HR_EINVAL, "layer %d: FP8 activation scales must be finite and > 0", idx);
   }
-  (void)d;
+  if (L->wtype == HR_MXFP4) {
+    const uint8_t* sc[] = {L->mx_o_s, L->mx_gu_s, L->mx_down_s};
+    for (const uint8_t* p : sc) {
+      if (!p) return fail(HR_EINVAL, "layer %d: MXFP4 block scales missing", idx);
+      if (!aligned16(p)) return fail(HR_EALIGN, "layer %d: MXFP4 block scales not 16-byte aligned", idx);
+    }
+    const int A = d->n_q_heads * d->head_dim;
+    if (d->hidden % 256 || A % 128 || d->ffn % 128)
+      return fail(HR_EUNSUPPORTED, "layer %d: MXFP4 needs D %% 256, Hq d %% 128, F %% 128 == 0", idx);
+  }
   return HR_OK;
 }
 
 struct Ws {
   uint8_t *x, *qkv, *q, *attn, *act, *head;
   float *part_o, *part_ml;   // key-chunk partials of the split attention (null: no split)
+  uint8_t *mx_s1, *mx_s2;    // MXFP4 block scales: O / gate-up input, down input (ld mx_ld)
+  int mx_ld;                 // rows of the scale layouts: T rounded up to the 256-row tile
 };
 
 // Batches of up to kAttnSplitT rows may split long attention rows into key
@@ -172,6 +184,10 @@ size_t ws_layout(const hr_dims* d, int32_t T, Ws* w, uint8_t* base) {
   tmp.attn = take(t * A * 2);
   tmp.act = take(t * F * 2);
   tmp.head = take(size_t(64) * D * 2);
+  // MXFP4 band: the codes reuse x (O / gate-up input) and act (down input)
+  tmp.mx_ld = int((t + 255) / 256 * 256);
+  tmp.mx_s1 = take(((D > A ? D : A) / 128) * size_t(tmp.mx_ld) * 4);
+  tmp.mx_s2 = take((F / 128) * size_t(tmp.mx_ld) * 4);
   tmp.part_o = tmp.part_ml = nullptr;
   if (t > 0 && t <= size_t(kAttnSplitT)) {
     tmp.part_o = reinterpret_cast<float*>(take(size_t(kAttnSlots) * t * A * 4));
@@ -225,7 +241,7 @@ hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_batch* b, floa
                     const Ws& w, bool x_ready, hipStream_t st) {
   const int T = b->total_tokens, D = d->hidden, F = d->ffn, Hq = d->n_q_heads, Hkv = d->n_kv_heads;
   const int dh = d->head_dim, A = Hq * dh, NQKV = (Hq + 2 * Hkv) * dh;
-  const bool fp8 = L->wtype == HR_FP8_E4M3;
+  const bool fp8 = L->wtype == HR_FP8_E4M3, mx = L->wtype == HR_MXFP4;
   const hr::AttnSplit split = attn_plan(d, b, &w);
   if (!x_ready)
     hr::launch_rmsnorm(h, T, D, L->in_norm_w, d->rms_eps, w.x, fp8, fp8 ? 1.0f / L->as_qkv : 1.f, st);
@@ -236,6 +252,19 @@ hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_batch* b, floa
   hr::launch_attention(w.q, kv->k, kv->v, b->cu_seqlens, b->start_pos, b->cache_slot, b->used_keys, b->n_seq,
                        b->max_seqlen, Hq, Hkv, dh, kv->capacity, d->causal != 0, w.attn, fp8,
                        fp8 ? 1.0f / L->as_o : 1.f, st, &split);
+  if (mx) {
+    // O, gate/up and down on MXFP4: per-row block quantisation of each input
+    // (1/s applied first), the gate/up epilogue writing the down input
+    const uint8_t* wo = static_cast<const uint8_t*>(L->w_o);
+    hr::launch_quant_mx(w.attn, false, T, A, L->awq_inv_o, nullptr, w.x, w.mx_s1, w.mx_ld, st);
+    hr::launch_linear_mx(w.x, w.mx_s1, w.mx_ld, wo, L->mx_o_s, T, D, A, HR_EPI_RESIDUAL, h, nullptr, 0, st);
+    hr::launch_rmsnorm_mx(h, T, D, L->post_norm_w, L->awq_inv_gu, d->rms_eps, w.x, w.mx_s1, w.mx_ld, st);
+    hr::launch_linear_mx(w.x, w.mx_s1, w.mx_ld, static_cast<const uint8_t*>(L->w_gu), L->mx_gu_s, T, 2 * F, D,
+                         HR_EPI_SWIGLU, w.act, w.mx_s2, w.mx_ld, st);
+    hr::launch_linear_mx(w.act, w.mx_s2, w.mx_ld, static_cast<const uint8_t*>(L->w_down), L->mx_down_s, T, D, F,
+                         HR_EPI_RESIDUAL, h, nullptr, 0, st);
+    return check_launch("prefill layer (MXFP4)");
+  }
   hr::launch_linear(w.attn, L->w_o, L->ws_o, L->as_o, fp8, T, D, A, HR_EPI_RESIDUAL, h, 0.f, st);
   hr::launch_rmsnorm(h, T, D, L->post_norm_w, d->rms_eps, w.x, fp8, fp8 ? 1.0f / L->as_gu : 1.f, st);
   hr::launch_linear(w.x, L->w_gu, L->ws_gu, L->as_gu, fp8, T, 2 * F, D, HR_EPI_SWIGLU, w.act,

@@ -111,6 +111,21 @@ __device__ __forceinline__ floatx16 mma32_mx(const u32x4 (&a)[2], const u32x4 (&
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+// value of lane (lane ^ 1) / (lane ^ 2) / the 8-lane mirror / the 16-lane
+// mirror, by DPP (no LDS-pipe shuffle)
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) { return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false); }
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) { return __int_as_float(dpp_i<CTRL>(__float_as_int(v))); }
+// max over the 32 lanes of a half-wave: quad swaps, 8- and 16-lane mirrors, then lane ^ 16
+__device__ __forceinline__ float half_wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xb1>(v));     // quad_perm(1, 0, 3, 2)
+  v = fmaxf(v, dpp_f<0x4e>(v));     // quad_perm(2, 3, 0, 1)
+  v = fmaxf(v, dpp_f<0x141>(v));    // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));    // row_mirror
+  return fmaxf(v, __shfl_xor(v, 16, kWave));
+}
+
 struct EpiArgs {
   int epi;            // hr_epilogue
   void* out;          // bf16 [M,N] | fp32 [M,N] (+=) | act [M,F] | fp32 logits
@@ -353,9 +368,10 @@ struct TileCfg {
 };
 
 // MX: E2M1 operands with E8M0 block scales (FP8 false).  The scales ride the
-// slab ring: per slab, wave 0 copies the A tile's 256 rows x 4 scale bytes and
-// wave 1 the B tile's (1 KB each), so those two waves issue one copy more per
-// slab and wait for one more.
+// slab ring: per slab the tile's BM + BN rows x 4 scale bytes (A rows, then B
+// rows) go in kSc 1-KB copies, copy c by wave c (lane l: rows 4l .. 4l+3 of
+// that KB; lanes past the last row repeat row 0 into the pad), so those waves
+// issue one copy more per slab and wait for one more.
 template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int SB, bool MX = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, int M, int N, int K_bytes,
@@ -363,14 +379,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
   using C = TileCfg<BM, BN, WM, WN, STAGES, SB>;
   constexpr int IM = C::kIM, JN = C::kJN, LPS = C::kLPS, NC = C::kChunks / 2;
   static_assert(EPI != HR_EPI_SWIGLU || JN % 2 == 0, "SwiGLU waves hold gate/up block pairs");
-  static_assert(!MX || (!FP8 && BM == 256 && BN == 256 && SB == 64 && WM * WN >= 2),
-                "MXFP4: 256 x 256 tiles of 128-value (64-byte) slabs");
+  constexpr int kSc = MX ? (BM + BN + 255) / 256 : 0;   // scale copies per slab
+  static_assert(!MX || (!FP8 && SB == 64 && WM * WN >= kSc), "MXFP4: 128-value (64-byte) slabs");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* sA = smem;                                   // [STAGES][BM rows][64 B]
   uint8_t* sB = smem + STAGES * C::kSlabA;              // [STAGES][BN rows][64 B]
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
-  uint8_t* sS = smem + STAGES * (C::kSlabA + C::kSlabB);   // MX: [STAGES][A 1 KB | B 1 KB] scales
+  uint8_t* sS = smem + STAGES * (C::kSlabA + C::kSlabB);   // MX: [STAGES][kSc KB: A rows, B rows] scales
   // XCD-aware order: consecutive workgroup ids go round-robin over the 8 XCDs;
   // give each XCD a contiguous run of tiles so the m-tiles that share a weight
   // tile are served by one L2
@@ -416,15 +432,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
       src[j] = uint32_t(br) * uint32_t(K_bytes) + lc * 16;
     }
   }
-  // MX scale copies: lane l carries rows 4l .. 4l+3 (4 bytes each) of the
-  // A tile (wave 0) or of the B tile (wave 1, rows mapped as the B copies)
+  // MX scale copy of this wave (wave < kSc): lane l carries combined rows
+  // q = 256 wave + 4l .. +3 (4 bytes each): A rows below BM, then B rows
+  // (mapped as the B copies), past BM + BN a repeat of A row 0
   uint32_t s_src = 0, s_ld = 0;
+  bool s_is_a = true;
   if constexpr (MX) {
-    if (wave == 0) {
-      s_src = uint32_t(m0 + 4 * lane) * 4u;
+    const int q = 256 * wave + 4 * lane;
+    if (q < BM || q >= BM + BN) {
+      s_src = uint32_t(m0 + (q < BM ? q : 0)) * 4u;
       s_ld = uint32_t(e.mx_lda) * 4u;
-    } else if (wave == 1) {
-      const int row = 4 * lane;
+    } else {
+      const int row = q - BM;
       int br;
       if constexpr (EPI == HR_EPI_SWIGLU) {
         const int blk = row >> 5, off = row & 31;
@@ -435,6 +454,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
       }
       s_src = uint32_t(br) * 4u;
       s_ld = uint32_t(N) * 4u;
+      s_is_a = false;
     }
   }
   const int slabs_total = K_bytes / SB;
@@ -450,13 +470,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
       lds_copy16((is_a ? x : w) + src[j] + ko, smem + dst_off[j] + stage * (is_a ? C::kSlabA : C::kSlabB));
     }
     if constexpr (MX) {
-      if (wave < 2)
-        lds_copy16((wave == 0 ? e.mx_sa : e.mx_sb) + size_t(slab) * s_ld + s_src, sS + stage * 2048 + wave * 1024);
+      if (wave < kSc)
+        lds_copy16((s_is_a ? e.mx_sa : e.mx_sb) + size_t(slab) * s_ld + s_src, sS + stage * (kSc * 1024) + wave * 1024);
     }
   };
   // wait until `pending` slabs issued after the needed one may still be in flight
   auto wait_slabs = [&](int pending) {
-    if (MX && wave < 2) wait_stages<LPS + 1, STAGES>(pending);
+    if (MX && wave < kSc) wait_stages<LPS + 1, STAGES>(pending);
     else wait_stages<LPS, STAGES>(pending);
   };
 
@@ -483,11 +503,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
     const uint8_t* A = sA + stage * C::kSlabA;
     const uint8_t* B = sB + stage * C::kSlabB;
     if constexpr (MX) {
-      const uint8_t* S = sS + stage * 2048;
+      const uint8_t* S = sS + stage * (kSc * 1024);
 #pragma unroll
       for (int i = 0; i < IM; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(S + (a_row0 + i * 32) * 4);
 #pragma unroll
-      for (int j = 0; j < JN; ++j) sb[j] = *reinterpret_cast<const uint32_t*>(S + 1024 + (b_row0 + j * 32) * 4);
+      for (int j = 0; j < JN; ++j) sb[j] = *reinterpret_cast<const uint32_t*>(S + (BM + b_row0 + j * 32) * 4);
     }
 #pragma unroll
     for (int j = 0; j < JN; ++j) {
@@ -573,12 +593,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
         for (int jj = 0; jj < JN / 2; ++jj) {
           const int cb = (n0 >> 1) + (wn * (JN / 2) + jj) * 32;     // first column of the block
           const float a = silu(acc[i][2 * jj][r]) * acc[i][2 * jj + 1][r];
-          float am = fabsf(a);
-#pragma unroll
-          for (int m = 1; m < 32; m <<= 1) am = fmaxf(am, __shfl_xor(am, m, kWave));
-          const int ex = mx_block_exp(am);
+          const int ex = mx_block_exp(half_wave_max(fabsf(a)));
           const uint32_t code = e2m1_code(ldexpf(a, -ex));
-          const uint32_t hi = __shfl_xor(code, 1, kWave);
+          const uint32_t hi = uint32_t(dpp_i<0xb1>(int(code)));
           if (row < M && cb < e.F) {
             if ((r32 & 1) == 0) oc[size_t(row) * (e.F / 2) + ((cb + r32) >> 1)] = uint8_t(code | (hi << 4));
             if (r32 == 0) e.mx_out_s[mx_scale_off(row, cb >> 5, e.mx_ldo)] = uint8_t(ex + 127);
@@ -663,7 +680,7 @@ template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int SB,
 static void tiled_cfg(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
                       int ksplit, hipStream_t st) {
   using C = TileCfg<BM, BN, WM, WN, STAGES, SB>;
-  constexpr size_t kLds = C::kLds + (MX ? size_t(STAGES) * 2048 : 0);
+  constexpr size_t kLds = C::kLds + (MX ? size_t(STAGES) * 1024 * ((BM + BN + 255) / 256) : 0);
   const int tiles_m = (M + BM - 1) / BM;
   const int ncols = (EPI == HR_EPI_SWIGLU) ? 2 * e.F : N;
   const int tiles_n = (ncols + BN - 1) / BN;
@@ -770,7 +787,6 @@ void launch_linear(const void* x, const void* w, const float* w_scale, float x_s
 // MXFP4 x MXFP4: x codes [M, K/2] with scales (ld lda), w codes [N, K/2] with
 // scales (ld N); RESIDUAL adds into fp32 out [M, N]; SWIGLU (N = 2F) writes the
 // MXFP4 product: codes [M, F/2] into out, scales (ld ldo) into out_scales.
-// Every M runs 256 x 256 tiles.
 void launch_linear_mx(const uint8_t* x, const uint8_t* x_scales, int lda, const uint8_t* w,
                       const uint8_t* w_scales, int M, int N, int K, int epi, void* out, uint8_t* out_scales,
                       int ldo, hipStream_t st) {
@@ -786,7 +802,8 @@ void launch_linear_mx(const uint8_t* x, const uint8_t* x_scales, int lda, const 
   e.mx_ldo = ldo;
   const int Kb = K / 2;
   if (epi == HR_EPI_SWIGLU) tiled_fill<HR_EPI_SWIGLU, false, 256, 256, 4, 2, 4, 64, true>(x, w, M, N, Kb, e, st);
-  else tiled_fill<HR_EPI_RESIDUAL, false, 256, 256, 4, 2, 4, 64, true>(x, w, M, N, Kb, e, st);
+  else if (M > 1024) tiled_fill<HR_EPI_RESIDUAL, false, 256, 256, 4, 2, 4, 64, true>(x, w, M, N, Kb, e, st);
+  else tiled_fill<HR_EPI_RESIDUAL, false, 128, 64, 4, 1, 4, 64, true>(x, w, M, N, Kb, e, st);
 }
 
 // Head: zsplit bf16 [2n, D] (hi rows then lo rows), W bf16 [N, D] -> fp32 [n, N]

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libhr.so")
 
 HR_OK, HR_EINVAL, HR_EUNSUPPORTED, HR_ECAPACITY = 0, -1, -2, -3
 HR_EBOUND, HR_EWORKSPACE, HR_EALIGN, HR_EHIP = -4, -5, -6, -7
-HR_BF16, HR_FP8_E4M3 = 0, 1
+HR_BF16, HR_FP8_E4M3, HR_MXFP4 = 0, 1, 2
 HR_EPI_BF16, HR_EPI_RESIDUAL, HR_EPI_SWIGLU = 0, 1, 2
 STATUS_NAMES = {0: "HR_OK", -1: "HR_EINVAL", -2: "HR_EUNSUPPORTED", -3: "HR_ECAPACITY",
                 -4: "HR_EBOUND", -5: "HR_EWORKSPACE", -6: "HR_EALIGN", -7: "HR_EHIP"}
@@ -37,7 +37,9 @@ class HrLayer(ctypes.Structure):
                 ("in_norm_w", c_vp), ("post_norm_w", c_vp), ("q_norm_w", c_vp), ("k_norm_w", c_vp),
                 ("w_qkv", c_vp), ("w_o", c_vp), ("w_gu", c_vp), ("w_down", c_vp),
                 ("ws_qkv", c_vp), ("ws_o", c_vp), ("ws_gu", c_vp), ("ws_down", c_vp),
-                ("as_qkv", c_f32), ("as_o", c_f32), ("as_gu", c_f32), ("as_down", c_f32)]
+                ("as_qkv", c_f32), ("as_o", c_f32), ("as_gu", c_f32), ("as_down", c_f32),
+                ("mx_o_s", c_vp), ("mx_gu_s", c_vp), ("mx_down_s", c_vp), ("awq_inv_o", c_vp),
+                ("awq_inv_gu", c_vp)]
 
 
 class HrKv(ctypes.Structure):
@@ -189,8 +191,11 @@ def make_kv(k, v, capacity: int, n_slots: int) -> HrKv:
     return kv
 
 
-def make_layer(t: dict, wtype: int = HR_BF16, scales: dict | None = None, wscales: dict | None = None) -> HrLayer:
-    """``t``: device tensors in_norm, post_norm, q_norm, k_norm, w_qkv, w_o, w_gu, w_down."""
+def make_layer(t: dict, wtype: int = HR_BF16, scales: dict | None = None, wscales: dict | None = None,
+               mx: dict | None = None) -> HrLayer:
+    """``t``: device tensors in_norm, post_norm, q_norm, k_norm, w_qkv, w_o, w_gu, w_down.
+    MXFP4: ``t`` holds the packed codes of w_o / w_gu / w_down and ``mx`` their
+    scales (``o_s``, ``gu_s``, ``down_s``) and the 1/s vectors (``inv_o``, ``inv_gu``)."""
     L = HrLayer()
     L.wtype = wtype
     L.in_norm_w, L.post_norm_w = ptr(t["in_norm"]), ptr(t["post_norm"])
@@ -200,7 +205,10 @@ def make_layer(t: dict, wtype: int = HR_BF16, scales: dict | None = None, wscale
         L.ws_qkv, L.ws_o = ptr(wscales["qkv"]), ptr(wscales["o"])
         L.ws_gu, L.ws_down = ptr(wscales["gu"]), ptr(wscales["dn"])
         L.as_qkv, L.as_o, L.as_gu, L.as_down = (scales["qkv"], scales["o"], scales["gu"], scales["dn"])
-    L._tensors = (t, wscales)     # raw pointers above: keep the weights alive with the struct
+    if wtype == HR_MXFP4:
+        L.mx_o_s, L.mx_gu_s, L.mx_down_s = ptr(mx["o_s"]), ptr(mx["gu_s"]), ptr(mx["down_s"])
+        L.awq_inv_o, L.awq_inv_gu = ptr(mx.get("inv_o")), ptr(mx.get("inv_gu"))
+    L._tensors = (t, wscales, mx)     # raw pointers above: keep the weights alive with the struct
     return L
 
 

@@ -57,7 +57,7 @@ typedef enum {
   HR_EHIP = -7           /* a HIP launch error                                   */
 } hr_status;
 
-typedef enum { HR_BF16 = 0, HR_FP8_E4M3 = 1 } hr_wtype;
+typedef enum { HR_BF16 = 0, HR_FP8_E4M3 = 1, HR_MXFP4 = 2 } hr_wtype;
 
 /* Shapes of the decoder.  Supported: head_dim in {64, 128};
  * n_q_heads / n_kv_heads in {1, 2, 4}; hidden, ffn multiples of 64. */
@@ -81,6 +81,16 @@ typedef struct {
  *         W[n, k] ~= ws[n] * e4m3(w[n, k]); as_* are the static per-tensor
  *         activation scales (host floats): the GEMM input x is quantised as
  *         e4m3(x / as) and the product is rescaled by as * ws[n].
+ *  MXFP4: the band of flashrt-structures 0.2.0 prefill_tower/fp8_chain.py (the
+ *         FP4 band table: O and the FFN pair in 4-bit with dynamic block
+ *         scales, QKV unchanged) in gfx950's OCP MX form (hr_ops.h): w_qkv is
+ *         bf16; w_o, w_gu, w_down are E2M1 codes [N, K/2] packed by
+ *         hr_quantize_mxfp4 with the AWQ scales of their input channels
+ *         (and 1/s of the down projection on the up rows), their block scales
+ *         in mx_*_s (slab-interleaved, ld = N); awq_inv_o / awq_inv_gu are the
+ *         1/s vectors applied to the attention output and the FFN input before
+ *         they are quantised per row (NULL: 1).  D a multiple of 256, Hq d and
+ *         F multiples of 128.
  * Row order of w_qkv: q heads, then k heads, then v heads ([(Hq+2Hkv)d, D]).
  * Row order of w_gu: the gate projection, then the up projection ([2F, D]). */
 typedef struct {
@@ -98,6 +108,11 @@ typedef struct {
   const float* ws_gu;       /* FP8 only: [2F] */
   const float* ws_down;     /* FP8 only: [D] */
   float as_qkv, as_o, as_gu, as_down;  /* FP8 only, > 0 */
+  const uint8_t* mx_o_s;     /* MXFP4 only: block scales of w_o    [Hq d/128][D][4] */
+  const uint8_t* mx_gu_s;    /* MXFP4 only: block scales of w_gu   [D/128][2F][4] */
+  const uint8_t* mx_down_s;  /* MXFP4 only: block scales of w_down [F/128][D][4] */
+  const float* awq_inv_o;    /* MXFP4 only: fp32 [Hq d] or NULL */
+  const float* awq_inv_gu;   /* MXFP4 only: fp32 [D] or NULL */
 } hr_layer;
 
 /* KV cache of one layer: bf16 [n_slots * capacity, Hkv, d]; position p of the

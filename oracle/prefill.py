@@ -116,7 +116,7 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
 
 def prefill_layer(m, lw: dict, batch: dict, h: np.ndarray, kc: np.ndarray, vc: np.ndarray,
                   causal: bool = True, used_keys=None, taps: dict | None = None,
-                  linear=None, store=None) -> np.ndarray:
+                  linear=None, store=None, store_ffn: bool = True) -> np.ndarray:
     """One decoder layer over a packed batch; returns the new residual h[T, D].
 
     ``m``: model shapes (hidden, n_q_heads, n_kv_heads, head_dim, ffn, rope_theta,
@@ -131,7 +131,9 @@ def prefill_layer(m, lw: dict, batch: dict, h: np.ndarray, kc: np.ndarray, vc: n
     ``round_bf16``) is applied wherever a bf16 implementation stores an
     intermediate: the two norm outputs, the QKV product, the normed and rotated
     q / k, the attention probabilities fed to P.V, the attention output and the
-    SwiGLU product (a diagnostic of bf16 storage; default: no rounding).
+    SwiGLU product (a diagnostic of bf16 storage; default: no rounding);
+    ``store_ffn=False`` leaves the two FFN inputs (post-attention norm output,
+    SwiGLU product) unrounded, for a chain that quantises them from fp32.
     """
     D, Hq, Hkv, d = m.hidden, m.n_q_heads, m.n_kv_heads, m.head_dim
     F, eps, theta = m.ffn, m.rms_eps, m.rope_theta
@@ -175,9 +177,10 @@ def prefill_layer(m, lw: dict, batch: dict, h: np.ndarray, kc: np.ndarray, vc: n
                                    visible, st)
     o = st(o.reshape(T, Hq * d))
     h = h + lin("o", o, lw["w_o"])
-    x_post = st(rms_norm(h, lw["post_norm"], eps))
+    st_ffn = st if store_ffn else _identity
+    x_post = st_ffn(rms_norm(h, lw["post_norm"], eps))
     gu = lin("gu", x_post, lw["w_gu"])
-    act = st(silu(gu[:, :F]) * gu[:, F:])
+    act = st_ffn(silu(gu[:, :F]) * gu[:, F:])
     h = h + lin("dn", act, lw["w_down"])
     if taps is not None:
         taps.update(qkv=x_in, o=o, gu=x_post, dn=act)

@@ -32,6 +32,33 @@ def fp8_pack(H, dl: dict, m) -> tuple:
     return out, scales
 
 
+def mx_pack(H, dl: dict, m, awq: dict | None = None) -> tuple:
+    """MXFP4 weights of O, gate/up and down packed on the device by
+    hr_quantize_mxfp4 (AWQ vectors ``awq`` = {"o", "gu", "dn"} of s; None: 1).
+    Returns (device weights dict with the codes in place of w_o / w_gu / w_down,
+    the make_layer ``mx`` dict of scales and 1/s vectors)."""
+    import torch
+    from gpu_util import dev
+    D, F, A = m.hidden, m.ffn, m.n_q_heads * m.head_dim
+    out = dict(dl)
+    mxd = {}
+    s = inv = None
+    if awq is not None:
+        s = {k: np.asarray(v, np.float64).astype(np.float32) for k, v in awq.items()}
+        inv = {k: (1.0 / np.asarray(v, np.float64)).astype(np.float32) for k, v in awq.items()}
+    row_gu = np.concatenate([np.ones(F, np.float32), inv["dn"]]) if inv is not None else None
+    for name, key, N, K, site, row in (("w_o", "o_s", D, A, "o", None), ("w_gu", "gu_s", 2 * F, D, "gu", row_gu),
+                                       ("w_down", "down_s", D, F, "dn", None)):
+        c = torch.zeros((N, K // 2), dtype=torch.uint8, device="cuda")
+        sc = torch.zeros((K // 128) * N * 4, dtype=torch.uint8, device="cuda")
+        H.hr_quantize_mxfp4(dl[name], N, K, c, sc, N, col_scale=dev(s[site]) if s is not None else None,
+                            row_scale=dev(row) if row is not None else None)
+        out[name], mxd[key] = c, sc
+    mxd["inv_o"] = dev(inv["o"]) if inv is not None else None
+    mxd["inv_gu"] = dev(inv["gu"]) if inv is not None else None
+    return out, mxd
+
+
 def dims_of(H, m, causal=True, n_layers=None):
     return H.make_dims(m.hidden, m.n_q_heads, m.n_kv_heads, m.head_dim, m.ffn,
                        n_layers if n_layers is not None else m.n_layers, m.rope_theta, m.rms_eps, causal)

@@ -180,3 +180,71 @@ def test_linear_mxfp4_swiglu_to_mxfp4(H, M, F, K):
     gc = mx.unpack_codes(oc.cpu().numpy())
     gs = from_slab_layout(os_.cpu().numpy(), M, F, ld)
     _one_step_close(gc, gs, rc, rs, "swiglu")
+
+
+MX_LAYER_CASES = [
+    ("tiny_d256_p6", synth.TINY, 6, 64),
+    ("layer_d2560_p13", synth.QWEN3_4B, 13, 64),
+    ("layer_d2560_p512", synth.QWEN3_4B, 512, 512),
+]
+
+
+@pytest.mark.parametrize("name,m,P,cap", MX_LAYER_CASES, ids=[c[0] for c in MX_LAYER_CASES])
+def test_layer_mxfp4(H, name, m, P, cap):
+    """The MXFP4 band of a layer (O, gate/up, down on MXFP4, QKV and attention
+    bf16), causal prefill of P rows, weights packed on the device with AWQ
+    scales from the fixed 32-token calibration prompt.
+
+    The bar is the method's own accuracy: the layer's update h' - h against the
+    unquantised layer no worse than the oracle's MXFP4 layer (same packed
+    weights) minus 2e-3.  Element-level agreement with the oracle's MXFP4 layer
+    cannot be tight: a 4-bit code moves wherever an activation sits near one of
+    its rounding boundaries, and bf16-level differences move enough of them
+    that the oracle's own MXFP4 layer with and without bf16 storage of the
+    attention path agrees only to cosine 0.979 (P = 13) / 0.972 (P = 128); the
+    GPU is held to 0.96 against the oracle that stores as the kernels do.  The
+    quantisers (bit-exact) and the MXFP4 GEMMs are checked element by element
+    in the tests above.  K/V cache rows (the bf16 part) at the bf16 bar."""
+    import torch
+    from gpu_util import cosine, dev, log
+    from model_util import dims_of, kv_cache, mx_pack, upload_layer, workspace
+    log(f"mxfp4 layer {name}")
+    bits = synth.layer_tensors(m, 0)
+    lw = op.widen_layer(bits)
+    h_cal = nx.bf16_to_f64(synth.embed_rows(m, synth.calibration_ids(m, 32)))
+    awq = mx.calibrate_awq(m, lw, h_cal)
+    dl = upload_layer(bits)
+    dlm, mxd = mx_pack(H, dl, m, awq)
+    torch.cuda.synchronize()
+    pk = mx.pack_layer({k: v.astype(np.float32) for k, v in lw.items()}, awq)
+    np.testing.assert_array_equal(dlm["w_down"].cpu().numpy(), mx.pack_codes(pk["packed"]["dn"][0]))
+    np.testing.assert_array_equal(dlm["w_gu"].cpu().numpy(), mx.pack_codes(pk["packed"]["gu"][0]))
+    layer = H.make_layer(dlm, H.HR_MXFP4, mx=mxd)
+    ids = synth.prompt_ids(m, P)
+    h0 = nx.bf16_to_f64(synth.embed_rows(m, ids))
+    kc, vc = kv_cache(m, 1, cap)
+    dims = dims_of(H, m, True, 1)
+    b = H.Batch([0, P], [0], [0])
+    h = dev(np.ascontiguousarray(h0, dtype=np.float32))
+    ws_ = workspace(H, dims, H.HR_MXFP4, P)
+    H.hr_prefill_layer(dims, layer, b, h, H.make_kv(kc, vc, cap, 1), ws_)
+    torch.cuda.synchronize()
+    hg = h.cpu().numpy().astype(np.float64)
+    ob = {"cu_seqlens": [0, P], "start_pos": [0], "cache_slot": [0], "capacity": cap}
+    kr, vr = op.new_cache(m, 1, cap)
+    h_exact = op.prefill_layer(m, lw, ob, h0, kr, vr, True, None)
+    # the oracle's MXFP4 layer with the bf16 part of the chain stored as the
+    # kernels store it: the attention output is quantised from bf16 on both sides
+    h_mx = mx.mx_layer(m, lw, pk, ob, h0, *op.new_cache(m, 1, cap), True, None, store=op.round_bf16)
+    h_mx_exact = mx.mx_layer(m, lw, pk, ob, h0, *op.new_cache(m, 1, cap), True, None)
+    d_g, d_mx, d_ex = hg - h0, h_mx - h0, h_exact - h0
+    c_or, c_ex, c_method = cosine(d_g, d_mx), cosine(d_g, d_ex), cosine(h_mx_exact - h0, d_ex)
+    log(f"  update cos: vs MXFP4 oracle {c_or:.6f}; vs unquantised {c_ex:.6f} "
+        f"(MXFP4 oracle vs unquantised {c_method:.6f})")
+    assert np.all(np.isfinite(hg))
+    assert c_or >= 0.96, c_or
+    assert c_ex >= c_method - 2e-3, (c_ex, c_method)
+    from gpu_util import bits_of
+    ck = cosine(nx.bf16_to_f64(bits_of(kc)[:P]), kr[:P])
+    log(f"  K cache cos {ck:.7f}")
+    assert ck >= 0.9999
