@@ -520,6 +520,7 @@ hr_status hr_embed_rmsnorm(const int32_t* ids, const void* embed, int32_t vocab,
   HR_TRY(need(norm_w, "norm_w"));
   HR_TRY(need(h_out, "h_out"));
   HR_TRY(need(x_out, "x_out"));
+  if (x_type != HR_BF16 && x_type != HR_FP8_E4M3) return fail(HR_EINVAL, "x_type: bf16 or e4m3");
   if (x_type == HR_FP8_E4M3 && !(x_scale > 0.f)) return fail(HR_EINVAL, "x_scale must be > 0");
   if (T == 0) return HR_OK;
   hr::launch_embed_rmsnorm(ids, embed, x_embeds, T, D, norm_w, eps, h_out, x_out, x_type == HR_FP8_E4M3,
@@ -533,6 +534,7 @@ hr_status hr_rmsnorm(const float* h, int32_t T, int32_t D, const void* norm_w, f
   HR_TRY(need(h, "h"));
   HR_TRY(need(norm_w, "norm_w"));
   HR_TRY(need(x_out, "x_out"));
+  if (x_type != HR_BF16 && x_type != HR_FP8_E4M3) return fail(HR_EINVAL, "x_type: bf16 or e4m3");
   if (x_type == HR_FP8_E4M3 && !(x_scale > 0.f)) return fail(HR_EINVAL, "x_scale must be > 0");
   if (T == 0) return HR_OK;
   hr::launch_rmsnorm(h, T, D, norm_w, eps, x_out, x_type == HR_FP8_E4M3,
@@ -643,6 +645,7 @@ hr_status hr_attention(const hr_dims* dims, const hr_batch* batch, const void* q
   HR_TRY(check_batch(dims, batch, kv));
   HR_TRY(need(q, "q"));
   HR_TRY(need(out, "out"));
+  if (out_type != HR_BF16 && out_type != HR_FP8_E4M3) return fail(HR_EINVAL, "out_type: bf16 or e4m3");
   if (out_type == HR_FP8_E4M3 && !(out_scale > 0.f)) return fail(HR_EINVAL, "out_scale must be > 0");
   if (batch->total_tokens == 0) return HR_OK;
   const hr::AttnSplit plan = attn_plan(dims, batch, nullptr);
@@ -667,6 +670,7 @@ hr_status hr_attention_chunked(const hr_dims* dims, const hr_batch* batch, const
   HR_TRY(check_batch(dims, batch, kv));
   HR_TRY(need(q, "q"));
   HR_TRY(need(out, "out"));
+  if (out_type != HR_BF16 && out_type != HR_FP8_E4M3) return fail(HR_EINVAL, "out_type: bf16 or e4m3");
   if (out_type == HR_FP8_E4M3 && !(out_scale > 0.f)) return fail(HR_EINVAL, "out_scale must be > 0");
   if (chunk_tiles < 1 || n_slots < 1 || n_slots > 64)
     return fail(HR_EINVAL, "chunk_tiles must be >= 1 and n_slots in [1, 64] (got %d, %d)", chunk_tiles, n_slots);

@@ -222,6 +222,8 @@ def test_codebook_policy_validation(case, status):
 
 def test_mxfp4_validation():
     lib = H.lib()
+    # the bf16 / e4m3 entries refuse the MXFP4 type
+    assert lib.hr_rmsnorm(FAKE, 4, 256, FAKE, 1e-6, FAKE, H.HR_MXFP4, 1.0, None) == H.HR_EINVAL
     # K not a multiple of 128; ld below M
     assert lib.hr_quantize_mxfp4(FAKE, 0, 4, 96, None, None, FAKE, FAKE, 4, None) == H.HR_EINVAL
     assert lib.hr_quantize_mxfp4(FAKE, 0, 8, 128, None, None, FAKE, FAKE, 4, None) == H.HR_EINVAL
