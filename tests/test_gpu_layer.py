@@ -105,6 +105,9 @@ CASES = [
     ("layer_d2560_p6", synth.QWEN3_4B, [6], [0], [0], 2048),
     ("layer_d2560_p13", synth.QWEN3_4B, [13], [0], [0], 2048),
     ("layer_d2560_varlen_t200", synth.QWEN3_4B, [100, 37, 63], [0, 0, 0], [1, 2, 0], 128),
+    # the P = 512 prefill of the throughput measurement (256 x 256 gate/up tiles,
+    # two wave groups per attention block)
+    ("layer_d2560_p512", synth.QWEN3_4B, [512], [0], [0], 512),
 ]
 
 
