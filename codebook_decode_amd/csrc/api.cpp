@@ -147,6 +147,8 @@ hr_status check_layer(const hr_dims* d, const hr_layer* L, int idx) {
       if (!p) return fail(HR_EINVAL, "layer %d: MXFP4 block scales missing", idx);
       if (!aligned16(p)) return fail(HR_EALIGN, "layer %d: MXFP4 block scales not 16-byte aligned", idx);
     }
+    if ((L->awq_inv_o && !aligned16(L->awq_inv_o)) || (L->awq_inv_gu && !aligned16(L->awq_inv_gu)))
+      return fail(HR_EALIGN, "layer %d: AWQ vectors not 16-byte aligned", idx);
     const int A = d->n_q_heads * d->head_dim;
     if (d->hidden % 256 || A % 128 || d->ffn % 128)
       return fail(HR_EUNSUPPORTED, "layer %d: MXFP4 needs D %% 256, Hq d %% 128, F %% 128 == 0", idx);
@@ -575,6 +577,7 @@ hr_status hr_quantize_mxfp4(const void* x, int32_t x_is_fp32, int32_t M, int32_t
   HR_TRY(need(x, "x"));
   HR_TRY(need(codes, "codes"));
   HR_TRY(need(scales, "scales"));
+  if (col_scale && !aligned16(col_scale)) return fail(HR_EALIGN, "col_scale is not 16-byte aligned");
   if (M == 0) return HR_OK;
   hr::launch_quant_mx(x, x_is_fp32 != 0, M, K, col_scale, row_scale, codes, scales, ld_scales, stream);
   return check_launch("quantize mxfp4");
@@ -589,6 +592,7 @@ hr_status hr_rmsnorm_mxfp4(const float* h, int32_t T, int32_t D, const void* nor
   HR_TRY(need(norm_w, "norm_w"));
   HR_TRY(need(codes, "codes"));
   HR_TRY(need(scales, "scales"));
+  if (col_scale && !aligned16(col_scale)) return fail(HR_EALIGN, "col_scale is not 16-byte aligned");
   if (T == 0) return HR_OK;
   hr::launch_rmsnorm_mx(h, T, D, norm_w, col_scale, eps, codes, scales, ld_scales, stream);
   return check_launch("rmsnorm mxfp4");

@@ -256,8 +256,13 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const void* __restrict__ 
     }
   }
   if (col) {
+    const floatx4* c4 = reinterpret_cast<const floatx4*>(col + kb * 32);   // 16-byte aligned (checked)
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = v[i] * col[kb * 32 + i];
+    for (int q = 0; q < 8; ++q) {
+      const floatx4 c = c4[q];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[4 * q + j] = v[4 * q + j] * c[j];
+    }
   }
   if (row_scale) {
     const float rs = row_scale[r];
@@ -310,8 +315,10 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_mx_kernel(
         y[2 * j + 1] = v[c][2 * j + 1] * r * bf_hi(wq[j]);
       }
       if (col) {
+        const floatx4* c4 = reinterpret_cast<const floatx4*>(col + 8 * i8);   // 16-byte aligned (checked)
+        const floatx4 c0 = c4[0], c1 = c4[1];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) y[j] = y[j] * col[8 * i8 + j];
+        for (int j = 0; j < 4; ++j) { y[j] = y[j] * c0[j]; y[4 + j] = y[4 + j] * c1[j]; }
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(y[j]));

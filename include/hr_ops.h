@@ -108,7 +108,7 @@ hr_status hr_quantize_weight_e4m3(const void* w, int32_t N, int32_t K, uint8_t* 
  * Layouts: codes u8 [rows, K/2], element 2i in the low nibble of byte i;
  * scales u8 in the slab-interleaved layout [K/128][ld][4] (block kb of row r at
  * ((kb/4) * ld + r) * 4 + kb % 4), ld >= rows.  K must be a multiple of 128;
- * codes and scales 16-byte aligned. */
+ * codes, scales and the scale vectors 16-byte aligned. */
 
 /* Quantise rows: v = x[r, k] * col_scale[k] * row_scale[r] (each product one
  * binary32 rounding, in that order; a NULL vector is 1), then MX blocks.
