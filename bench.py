@@ -547,8 +547,9 @@ def main():
         out["varlen32"] = varlen_batch(H, m, layers, shared)
         out["codebook_b64"] = codebook_steps(H, m, shared)
         out["codebook_sampled_b64"] = codebook_policy_steps(H, m, shared)
-        log("timing decode steps (B=64 over 512 cached rows, B=1 over 2047)")
+        log("timing decode steps (B=64 over 512 cached rows, B=16 and B=1 over 2047)")
         out["decode_b64"] = decode_steps(H, m, dev_layers, layers, shared, 64, 512)
+        out["decode_b16"] = decode_steps(H, m, dev_layers, layers, shared, 16, 2047)
         out["decode_b1"] = decode_steps(H, m, dev_layers, layers, shared, 1, 2047)
         out["hbm_sweep"] = hbm_sweep(H, m, shared)
         torch.cuda.synchronize()

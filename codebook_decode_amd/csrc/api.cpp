@@ -166,8 +166,10 @@ struct Ws {
 // Batches of up to kAttnSplitT rows may split long attention rows into key
 // chunks (decode steps and short continuations of long cached prefixes).
 constexpr int kAttnSplitT = 256;
-constexpr int kAttnSlots = 8;      // key chunks per query block at most
-constexpr int kAttnChunk = 4;      // 64-key tiles per chunk at least
+constexpr int kAttnSlots = 4;      // key chunks per query block at most
+constexpr int kAttnMinChunk = 8;   // 64-key tiles per chunk of the longest row at least
+constexpr int kAttnChunk = 4;      // 64-key tiles per chunk of shorter rows at least
+constexpr long long kAttnSplitGrid = 512;   // workgroups of a split grid at most
 
 size_t ws_layout(const hr_dims* d, int32_t T, Ws* w, uint8_t* base) {
   const size_t D = d->hidden, F = d->ffn, A = size_t(d->n_q_heads) * d->head_dim;
@@ -200,15 +202,18 @@ size_t ws_layout(const hr_dims* d, int32_t T, Ws* w, uint8_t* base) {
 }
 
 // Attention launch plan from the batch's host row lengths (start_pos + len).
-// Key chunks: when the unsplit grid (query blocks x kv heads x sequences)
-// leaves most CUs idle and the longest row spans at least 2 chunks (a decode
-// step of a few streams over long caches, a short continuation); needs the
-// partial buffers of the workspace (w).  Measured (8 kv heads x 128): one
-// query after 2040 cached keys 54.8 -> 23.9 us, 13 queries after 2000 keys
-// 55.1 -> 26.0 us (4-tile chunks); a prefill from position 0 or a decode step
-// of 64 streams is faster unsplit.  Two wave groups per block (interleaved
-// key tiles) when the grid is still below one workgroup per CU and a block
-// has at least 4 tiles.
+// Key chunks: when the unsplit grid (query blocks x kv heads x sequences) is
+// small against the CUs and the longest row is long, each query block takes 2
+// or 4 key chunks of at least 8 tiles (64 keys each), the most that keep the
+// grid within 512 workgroups; needs the partial buffers of the workspace (w).
+// Measured (8 kv heads x 128, one query per stream after 2040 cached keys):
+// 1 stream 44.6 -> 25.4 us, 8 streams 48.6 -> 29.1, 16 streams 49.2 -> 36.2
+// (4 chunks), 32 streams 57.7 -> 51.8 (2 chunks); 8 chunks of 4 tiles were
+// never faster by more than 5% and up to 1.6x slower (the combine step and
+// the per-chunk start-up grow with the count); a prefill from position 0,
+// 48 or more streams, or rows under 16 tiles run unsplit.  Two wave groups
+// per block (interleaved key tiles) when the grid is still below one
+// workgroup per CU and a block has at least 4 tiles.
 hr::AttnSplit attn_plan(const hr_dims* d, const hr_batch* b, const Ws* w) {
   hr::AttnSplit sp;
   const int qpw = hr::attention_qpw(d->n_q_heads, d->n_kv_heads);
@@ -222,16 +227,17 @@ hr::AttnSplit attn_plan(const hr_dims* d, const hr_batch* b, const Ws* w) {
   }
   const int max_tiles = (max_keys + 63) / 64;
   int block_tiles = max_tiles;
-  if (w && w->part_o && wgs < 128 && max_tiles >= 2 * kAttnChunk) {
+  int slots = 1;
+  for (int c = 2; c <= kAttnSlots; c *= 2)
+    if (wgs * c <= kAttnSplitGrid && (max_tiles + c - 1) / c >= kAttnMinChunk) slots = c;
+  if (w && w->part_o && slots > 1) {
     sp.chunk_tiles = kAttnChunk;
-    const int want = (max_tiles + kAttnChunk - 1) / kAttnChunk;
-    sp.n_slots = want < kAttnSlots ? want : kAttnSlots;
+    sp.n_slots = slots;
     sp.part_o = w->part_o;
     sp.part_ml = w->part_ml;
     sp.T = b->total_tokens;
     wgs *= sp.n_slots;
     block_tiles = (max_tiles + sp.n_slots - 1) / sp.n_slots;
-    if (block_tiles < kAttnChunk) block_tiles = kAttnChunk;
   }
   if (wgs < 256 && block_tiles >= 4) sp.groups = 2;
   return sp;
