@@ -243,6 +243,19 @@ hr::AttnSplit attn_plan(const hr_dims* d, const hr_batch* b, const Ws* w) {
   return sp;
 }
 
+// The fused short-prompt path applies when every sequence starts at position
+// 0 and has at most kSmallRows rows (its keys are its own rows): returns the
+// longest sequence's rows then, else -1.
+int small_prompt(const hr_batch* b) {
+  int longest = 0;
+  for (int s = 0; s < b->n_seq; ++s) {
+    const int len = b->h_cu_seqlens[s + 1] - b->h_cu_seqlens[s];
+    if (b->h_start_pos[s] != 0 || len > hr::kSmallRows) return -1;
+    if (len > longest) longest = len;
+  }
+  return longest;
+}
+
 // one layer's kernels over buffers already validated.  `x_ready`: w.x already
 // holds RMSNorm_in(h) of this layer.
 hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_batch* b, float* h, const hr_kv* kv,
@@ -254,12 +267,18 @@ hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_batch* b, floa
   if (!x_ready)
     hr::launch_rmsnorm(h, T, D, L->in_norm_w, d->rms_eps, w.x, fp8, fp8 ? 1.0f / L->as_qkv : 1.f, st);
   hr::launch_linear(w.x, L->w_qkv, L->ws_qkv, L->as_qkv, fp8, T, NQKV, D, HR_EPI_BF16, w.qkv, 0.f, st);
-  hr::launch_qknorm_rope_kv(w.qkv, T, Hq, Hkv, dh, d->rope_theta, d->rms_eps, b->cu_seqlens, b->start_pos,
-                            b->cache_slot, b->used_keys, b->n_seq, d->causal != 0, L->q_norm_w, L->k_norm_w,
-                            w.q, kv->k, kv->v, kv->capacity, st);
-  hr::launch_attention(w.q, kv->k, kv->v, b->cu_seqlens, b->start_pos, b->cache_slot, b->used_keys, b->n_seq,
-                       b->max_seqlen, Hq, Hkv, dh, kv->capacity, d->causal != 0, w.attn, fp8,
-                       fp8 ? 1.0f / L->as_o : 1.f, st, &split);
+  if (const int small = small_prompt(b); small >= 0) {
+    hr::launch_rope_attn_small(w.qkv, b->n_seq, small, Hq, Hkv, dh, d->rope_theta, d->rms_eps, b->cu_seqlens,
+                               b->cache_slot, b->used_keys, d->causal != 0, L->q_norm_w, L->k_norm_w, kv->k, kv->v,
+                               kv->capacity, w.attn, fp8, fp8 ? 1.0f / L->as_o : 1.f, st);
+  } else {
+    hr::launch_qknorm_rope_kv(w.qkv, T, Hq, Hkv, dh, d->rope_theta, d->rms_eps, b->cu_seqlens, b->start_pos,
+                              b->cache_slot, b->used_keys, b->n_seq, d->causal != 0, L->q_norm_w, L->k_norm_w,
+                              w.q, kv->k, kv->v, kv->capacity, st);
+    hr::launch_attention(w.q, kv->k, kv->v, b->cu_seqlens, b->start_pos, b->cache_slot, b->used_keys, b->n_seq,
+                         b->max_seqlen, Hq, Hkv, dh, kv->capacity, d->causal != 0, w.attn, fp8,
+                         fp8 ? 1.0f / L->as_o : 1.f, st, &split);
+  }
   if (mx) {
     // O, gate/up and down on MXFP4: per-row block quantisation of each input
     // (1/s applied first), the gate/up epilogue writing the down input
@@ -664,6 +683,30 @@ hr_status hr_attention(const hr_dims* dims, const hr_batch* batch, const void* q
                        kv->capacity, dims->causal != 0, out, out_type == HR_FP8_E4M3,
                        out_type == HR_FP8_E4M3 ? 1.0f / out_scale : 1.f, stream, &plan);
   return check_launch("attention");
+}
+
+hr_status hr_qknorm_rope_attention(const hr_dims* dims, const hr_batch* batch, const void* qkv,
+                                   const void* q_norm_w, const void* k_norm_w, const hr_kv* kv, void* out,
+                                   hr_wtype out_type, float out_scale, hipStream_t stream) {
+  HR_TRY(check_dims(dims));
+  HR_TRY(check_kv(dims, kv, "kv"));
+  HR_TRY(check_batch(dims, batch, kv));
+  HR_TRY(need(qkv, "qkv"));
+  HR_TRY(need(q_norm_w, "q_norm_w"));
+  HR_TRY(need(k_norm_w, "k_norm_w"));
+  HR_TRY(need(out, "out"));
+  if (out_type != HR_BF16 && out_type != HR_FP8_E4M3) return fail(HR_EINVAL, "out_type: bf16 or e4m3");
+  if (out_type == HR_FP8_E4M3 && !(out_scale > 0.f)) return fail(HR_EINVAL, "out_scale must be > 0");
+  const int longest = small_prompt(batch);
+  if (longest < 0)
+    return fail(HR_EUNSUPPORTED, "every sequence must start at position 0 with at most %d rows", hr::kSmallRows);
+  if (batch->total_tokens == 0) return HR_OK;
+  hr::launch_rope_attn_small(qkv, batch->n_seq, longest, dims->n_q_heads, dims->n_kv_heads, dims->head_dim,
+                             dims->rope_theta, dims->rms_eps, batch->cu_seqlens, batch->cache_slot,
+                             batch->used_keys, dims->causal != 0, q_norm_w, k_norm_w, kv->k, kv->v, kv->capacity,
+                             out, out_type == HR_FP8_E4M3, out_type == HR_FP8_E4M3 ? 1.0f / out_scale : 1.f,
+                             stream);
+  return check_launch("qknorm_rope_attention");
 }
 
 size_t hr_attention_chunked_workspace_bytes(const hr_dims* dims, int32_t total_tokens, int32_t n_slots) {

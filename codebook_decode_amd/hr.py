@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
             "hr_linear": (c_i32, [c_vp, c_vp, c_vp, c_f32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_f32, c_vp]),
             "hr_qknorm_rope_kv": (c_i32, [P(HrDims), P(HrBatch), c_vp, c_vp, c_vp, c_vp, P(HrKv), c_vp]),
             "hr_attention": (c_i32, [P(HrDims), P(HrBatch), c_vp, P(HrKv), c_vp, c_i32, c_f32, c_vp]),
+            "hr_qknorm_rope_attention": (c_i32, [P(HrDims), P(HrBatch), c_vp, c_vp, c_vp, P(HrKv), c_vp, c_i32,
+                                                 c_f32, c_vp]),
             "hr_attention_chunked_workspace_bytes": (c_sz, [P(HrDims), c_i32, c_i32]),
             "hr_attention_chunked": (c_i32, [P(HrDims), P(HrBatch), c_vp, P(HrKv), c_vp, c_i32, c_f32, c_i32,
                                              c_i32, c_vp, c_sz, c_vp]),
@@ -303,6 +305,13 @@ def hr_qknorm_rope_kv(dims, batch: Batch, qkv, q_norm_w, k_norm_w, q_out, kv: Hr
 def hr_attention(dims, batch: Batch, q, kv: HrKv, out, out_type=HR_BF16, out_scale=1.0, stream=None) -> None:
     _check(lib().hr_attention(ctypes.byref(dims), ctypes.byref(batch.c), ptr(q), ctypes.byref(kv), ptr(out),
                               out_type, out_scale, stream if stream is not None else current_stream()))
+
+
+def hr_qknorm_rope_attention(dims, batch: Batch, qkv, q_norm_w, k_norm_w, kv: HrKv, out, out_type=HR_BF16,
+                             out_scale=1.0, stream=None) -> None:
+    _check(lib().hr_qknorm_rope_attention(ctypes.byref(dims), ctypes.byref(batch.c), ptr(qkv), ptr(q_norm_w),
+                                          ptr(k_norm_w), ctypes.byref(kv), ptr(out), out_type, out_scale,
+                                          stream if stream is not None else current_stream()))
 
 
 def hr_attention_chunked_workspace_bytes(dims, total_tokens: int, n_slots: int) -> int:

@@ -57,6 +57,16 @@ hr_status hr_qknorm_rope_kv(const hr_dims* dims, const hr_batch* batch, const vo
                             const void* q_norm_w, const void* k_norm_w, void* q_out,
                             const hr_kv* kv, hipStream_t stream);
 
+/* Steps A3 and A4 in one launch for short prompts: the q/k norm + RoPE + KV
+ * write of hr_qknorm_rope_kv (the cache receives the same values) followed by
+ * the attention of hr_attention, out bf16 or e4m3(o / out_scale) [T, Hq*d],
+ * without writing q anywhere.  Every sequence must start at position 0 and
+ * hold at most 32 rows (HR_EUNSUPPORTED otherwise): its keys are then its own
+ * rows.  The layer entries take this path by themselves for such batches. */
+hr_status hr_qknorm_rope_attention(const hr_dims* dims, const hr_batch* batch, const void* qkv,
+                                   const void* q_norm_w, const void* k_norm_w, const hr_kv* kv, void* out,
+                                   hr_wtype out_type, float out_scale, hipStream_t stream);
+
 /* GQA attention over the cache (step A4): out [T, Hq*d] with
  * o_h = softmax(q_h K_g^T / sqrt(d)) V_g, g = h / (Hq/Hkv), over the causal
  * window or the used keys (dims->causal).  bf16 out, or e4m3(o / out_scale). */

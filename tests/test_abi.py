@@ -259,6 +259,25 @@ def test_attention_chunked_validation(ct, slots, ws, ws_bytes, status):
 
 
 @pytest.mark.parametrize("case,status", [
+    ("continuation", H.HR_EUNSUPPORTED),        # a sequence past position 0
+    ("long", H.HR_EUNSUPPORTED),                # 33 rows
+    ("out_type", H.HR_EINVAL),
+    ("fp8_scale", H.HR_EINVAL),
+    ("no_out", H.HR_EINVAL),
+])
+def test_qknorm_rope_attention_validation(case, status):
+    lib = H.lib()
+    d, k = dims(), kv()
+    b = batch([13, 33] if case == "long" else [13, 5], starts=[0, 7] if case == "continuation" else None)
+    out_type = {"out_type": H.HR_MXFP4, "fp8_scale": H.HR_FP8_E4M3}.get(case, H.HR_BF16)
+    scale = 0.0 if case == "fp8_scale" else 1.0
+    out = None if case == "no_out" else FAKE
+    st = lib.hr_qknorm_rope_attention(ctypes.byref(d), ctypes.byref(b.c), FAKE, FAKE, FAKE, ctypes.byref(k), out,
+                                      out_type, scale, None)
+    assert st == status, (st, H.hr_last_error())
+
+
+@pytest.mark.parametrize("case,status", [
     ("noncausal", H.HR_EUNSUPPORTED), ("two_rows", H.HR_EINVAL), ("no_head", H.HR_EINVAL),
     ("bos_eq_eoc", H.HR_EINVAL), ("workspace", H.HR_EWORKSPACE), ("misaligned_emb", H.HR_EALIGN),
     ("capacity", H.HR_ECAPACITY), ("wtype_mix", H.HR_EINVAL),

@@ -226,6 +226,73 @@ def test_qknorm_rope_kv(H, model, lens, starts, slots, cap):
     assert np.all(kcb[~written] == BF16_NAN) and np.all(vcb[~written] == BF16_NAN)
 
 
+# ------------------------------------------------------------------ A3 + A4 fused (short prompts)
+# Every sequence from position 0 with at most 32 rows: the cache must hold the
+# bits hr_qknorm_rope_kv writes (the same arithmetic), and the output must be
+# the attention of the q it produces over those keys (oracle on the bf16 q, k,
+# v, as for hr_attention).  Cases: one 13-token prompt; a packed batch with a
+# 1-row and a full 32-row prompt in permuted cache slots; the tiny model (d 64,
+# 2 query heads per kv head); non-causal used keys with pads (their K/V left
+# unwritten) and an e4m3 output.
+@pytest.mark.parametrize("model,lens,slots,causal,used,fp8", [
+    (synth.QWEN3_4B, [13], [0], True, None, False),
+    (synth.QWEN3_4B, [1, 32, 7], [2, 0, 1], True, None, False),
+    (synth.TINY, [6, 20], [1, 0], True, None, False),
+    (synth.QWEN3_4B, [13, 20], [0, 1], False, [10, 20], True),
+])
+def test_qknorm_rope_attention(H, model, lens, slots, causal, used, fp8):
+    import torch
+    from gpu_util import BF16_NAN, bits_of, dev_bf16, f64_of_bf16, log, poisoned_bf16
+    m = model
+    log(f"qknorm_rope_attention {m.name} lens={lens} causal={causal} fp8={fp8}")
+    T, n, cap = sum(lens), len(lens), 40
+    Hq, Hkv, d = m.n_q_heads, m.n_kv_heads, m.head_dim
+    qkv = dev_bf16(seeded_bf16((T, m.qkv_rows), (23, T, d), 1.0))
+    qw = dev_bf16(seeded_bf16((d,), (24, d), 0.1, 1.0))
+    kw = dev_bf16(seeded_bf16((d,), (25, d), 0.1, 1.0))
+    b = H.Batch(np.concatenate([[0], np.cumsum(lens)]), [0] * n, slots, used)
+    dims = _dims(H, m, causal)
+    caches = [(poisoned_bf16((n * cap, Hkv, d)), poisoned_bf16((n * cap, Hkv, d))) for _ in range(2)]
+    out_scale = 0.01
+    otype = H.HR_FP8_E4M3 if fp8 else H.HR_BF16
+    outs = [torch.full((T, Hq * d), 0x7F, dtype=torch.uint8, device="cuda") if fp8 else
+            torch.full((T, Hq * d), float("nan"), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    H.hr_qknorm_rope_attention(dims, b, qkv, qw, kw, H.make_kv(*caches[0], cap, n), outs[0], otype, out_scale)
+    q_out = poisoned_bf16((T, Hq, d))
+    kv1 = H.make_kv(*caches[1], cap, n)
+    H.hr_qknorm_rope_kv(dims, b, qkv, qw, kw, q_out, kv1)
+    H.hr_attention(dims, b, q_out, kv1, outs[1], otype, out_scale)
+    torch.cuda.synchronize()
+    for c0, c1 in zip(*caches):
+        np.testing.assert_array_equal(bits_of(c0), bits_of(c1))
+    kcb = bits_of(caches[0][0])
+    if not causal:      # pad rows past the used keys keep the poison
+        for s in range(n):
+            assert np.all(kcb[slots[s] * cap + used[s]:slots[s] * cap + cap] == BF16_NAN)
+    if fp8:
+        got = nx.e4m3_decode(outs[0].cpu().numpy()).reshape(T, Hq, d) * out_scale
+    else:
+        got = f64_of_bf16(outs[0]).reshape(T, Hq, d)
+    assert np.all(np.isfinite(got))
+    qv = f64_of_bf16(q_out)
+    kv_, vv = f64_of_bf16(caches[1][0]), f64_of_bf16(caches[1][1])
+    cu = b.h_cu
+    grp = Hq // Hkv
+    for s in range(n):
+        a, e = cu[s], cu[s + 1]
+        nk = lens[s] if causal else used[s]
+        vis = (np.arange(nk)[None, :] <= np.arange(lens[s])[:, None]) if causal else np.ones((lens[s], nk), bool)
+        rows = slice(slots[s] * cap, slots[s] * cap + nk)
+        for hh in range(Hq):
+            g = hh // grp
+            ref = op.attention(qv[a:e, hh], kv_[rows, g], vv[rows, g], vis)
+            err = np.abs(got[a:e, hh] - ref)
+            if fp8:
+                assert np.all(err <= 2.0 ** -4 * np.abs(ref) + 2.0 ** -9 * out_scale + 4e-3), (s, hh, float(err.max()))
+            else:
+                assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 4e-3), (s, hh, float(err.max()))
+
+
 # ----------------------------------------------------------------------------- A4
 @pytest.mark.parametrize("Hq,Hkv,d,lens,starts,causal,used", [
     (32, 8, 128, [13], [0], True, None),
