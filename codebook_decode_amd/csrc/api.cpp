@@ -167,9 +167,18 @@ struct Ws {
 // chunks (decode steps and short continuations of long cached prefixes).
 constexpr int kAttnSplitT = 256;
 constexpr int kAttnSlots = 4;      // key chunks per query block at most
+constexpr int kDecodeSlotRows = 256;        // partial rows (chunks x tokens) reserved for decode steps at least
+constexpr int kDecodeMaxSlots = 8;          // key chunks of a decode row at most
+constexpr long long kDecodeGrid = 512;      // workgroups a decode step's chunking aims at
 constexpr int kAttnMinChunk = 8;   // 64-key tiles per chunk of the longest row at least
 constexpr int kAttnChunk = 4;      // 64-key tiles per chunk of shorter rows at least
 constexpr long long kAttnSplitGrid = 512;   // workgroups of a split grid at most
+
+// rows (key chunk x token) of the attention partials in the workspace
+size_t part_rows(size_t t) {
+  const size_t r = size_t(kAttnSlots) * t;
+  return r > size_t(kDecodeSlotRows) ? r : size_t(kDecodeSlotRows);
+}
 
 size_t ws_layout(const hr_dims* d, int32_t T, Ws* w, uint8_t* base) {
   const size_t D = d->hidden, F = d->ffn, A = size_t(d->n_q_heads) * d->head_dim;
@@ -194,8 +203,9 @@ size_t ws_layout(const hr_dims* d, int32_t T, Ws* w, uint8_t* base) {
   tmp.mx_s2 = take((F / 128) * size_t(tmp.mx_ld) * 4);
   tmp.part_o = tmp.part_ml = nullptr;
   if (t > 0 && t <= size_t(kAttnSplitT)) {
-    tmp.part_o = reinterpret_cast<float*>(take(size_t(kAttnSlots) * t * A * 4));
-    tmp.part_ml = reinterpret_cast<float*>(take(size_t(kAttnSlots) * t * d->n_q_heads * 8));
+    const size_t rows = part_rows(t);
+    tmp.part_o = reinterpret_cast<float*>(take(rows * A * 4));
+    tmp.part_ml = reinterpret_cast<float*>(take(rows * d->n_q_heads * 8));
   }
   if (w) *w = tmp;
   return off;
@@ -214,7 +224,52 @@ size_t ws_layout(const hr_dims* d, int32_t T, Ws* w, uint8_t* base) {
 // 48 or more streams, or rows under 16 tiles run unsplit.  Two wave groups
 // per block (interleaved key tiles) when the grid is still below one
 // workgroup per CU and a block has at least 4 tiles.
+// Every sequence one row (a decode step)?
+bool one_row_batch(const hr_batch* b) {
+  for (int s = 0; s < b->n_seq; ++s)
+    if (b->h_cu_seqlens[s + 1] - b->h_cu_seqlens[s] != 1) return false;
+  return true;
+}
+
+// Decode steps (one row per sequence) take decode_attention_kernel; with the
+// workspace's partial buffers the keys are cut into chunks of ct 64-key tiles:
+// the larger of 1/8 of the longest row and what keeps the grid (every chunk of
+// every kv head of every stream) near kDecodeGrid workgroups; one chunk when
+// that leaves fewer than 2.  Measured (8 kv heads x 128, µs; the rule's pick
+// in brackets): 1 stream over 2041 keys 41.5 unsplit, [12.9] with 8 chunks of
+// 4 tiles, 13.6 with 16 of 2; 16 streams 50.2 unsplit, [28.5] with 4 chunks of
+// 8, 31.3 with 8 of 4; 32 streams [47.5] with 2 chunks, 52.0 unsplit; 64
+// streams over 512 keys [25.2] unsplit, 33.6 with 2 chunks.
+hr::AttnSplit decode_plan(const hr_dims* d, const hr_batch* b, const Ws* w) {
+  hr::AttnSplit sp;
+  sp.decode = true;
+  if (!w || !w->part_o) return sp;
+  long long units = 0;
+  int max_tiles = 0;
+  for (int s = 0; s < b->n_seq; ++s) {
+    const int keys = d->causal ? b->h_start_pos[s] + 1 : b->h_used_keys[s];
+    const int tiles = (keys + 63) / 64;
+    units += (long long)tiles * d->n_kv_heads;
+    if (tiles > max_tiles) max_tiles = tiles;
+  }
+  int ct = int((units + kDecodeGrid - 1) / kDecodeGrid);
+  const int by_len = (max_tiles + kDecodeMaxSlots - 1) / kDecodeMaxSlots;
+  if (ct < by_len) ct = by_len;
+  if (ct < 1) ct = 1;
+  const int want = (max_tiles + ct - 1) / ct;
+  int cap = int(part_rows(size_t(b->total_tokens)) / size_t(b->total_tokens));
+  if (cap > kDecodeMaxSlots) cap = kDecodeMaxSlots;
+  if (want < 2 || cap < 2) return sp;
+  sp.chunk_tiles = ct;
+  sp.n_slots = want < cap ? want : cap;
+  sp.part_o = w->part_o;
+  sp.part_ml = w->part_ml;
+  sp.T = b->total_tokens;
+  return sp;
+}
+
 hr::AttnSplit attn_plan(const hr_dims* d, const hr_batch* b, const Ws* w) {
+  if (one_row_batch(b)) return decode_plan(d, b, w);
   hr::AttnSplit sp;
   const int qpw = hr::attention_qpw(d->n_q_heads, d->n_kv_heads);
   long long wgs = 0;
@@ -734,6 +789,7 @@ hr_status hr_attention_chunked(const hr_dims* dims, const hr_batch* batch, const
   if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(HR_EALIGN, "workspace must be 256-byte aligned");
   const size_t t = size_t(batch->total_tokens), Hq = size_t(dims->n_q_heads);
   hr::AttnSplit sp;
+  sp.decode = one_row_batch(batch);
   sp.chunk_tiles = chunk_tiles;
   sp.n_slots = n_slots;
   sp.part_o = static_cast<float*>(ws);

@@ -334,8 +334,9 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void attention_kernel(
 }
 
 // Combine the key-chunk partials of the split query blocks:
-// o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c, M = max_c m_c.
-// One workgroup per token; rows of unsplit query blocks were written final.
+// o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c, M = max_c m_c, taken as
+// one pass with a running maximum.  Grid (token, 256 (head, 4-dim) units per
+// workgroup); rows of unsplit query blocks were written final.
 template <int DH>
 __global__ __launch_bounds__(256) void attention_merge_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ start_pos, const int32_t* __restrict__ used_keys,
@@ -349,30 +350,193 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(
   int ct, nch;
   chunk_plan((n_keys + AKT - 1) / AKT, chunk_tiles, n_slots, ct, nch);
   if (nch <= 1) return;
-  for (int u = threadIdx.x; u < Hq * (DH / 4); u += 256) {
-    const int h = u / (DH / 4), d4 = u % (DH / 4);
-    float M = -__builtin_inff();
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, part_ml[(size_t(c) * T + t) * Hq + h][0]);
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    float L = 0.f;
-    for (int c = 0; c < nch; ++c) {
-      const size_t prow = (size_t(c) * T + t) * Hq + h;
-      const float2_t ml = part_ml[prow];
-      const float wgt = (ml[0] == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(ml[0] - M);
-      L += wgt * ml[1];
-      acc += wgt * *reinterpret_cast<const floatx4*>(part_o + prow * DH + 4 * d4);
+  // thread: one head and 4 output dims; one pass over the chunks with a
+  // running maximum (unrolled, so the chunks' loads are in flight together)
+  const int u = blockIdx.y * 256 + threadIdx.x;
+  if (u >= Hq * (DH / 4)) return;
+  const int h = u / (DH / 4), d4 = u % (DH / 4);
+  float M = -__builtin_inff(), L = 0.f;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int c = 0; c < nch; ++c) {
+    const size_t prow = (size_t(c) * T + t) * Hq + h;
+    const float2_t ml = part_ml[prow];
+    const floatx4 o = *reinterpret_cast<const floatx4*>(part_o + prow * DH + 4 * d4);
+    const float mn = fmaxf(M, ml[0]);
+    const float a = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M - mn);
+    const float b = ml[0] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(ml[0] - mn);
+    L = L * a + b * ml[1];
+    acc = acc * a + b * o;
+    M = mn;
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  const size_t orow = (size_t(t) * Hq + h) * DH + 4 * d4;
+  const float y0 = acc[0] * inv, y1 = acc[1] * inv, y2 = acc[2] * inv, y3 = acc[3] * inv;
+  if (out_fp8) {
+    *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(out) + orow) =
+        f2e4m3(y0 * out_inv) | (f2e4m3(y1 * out_inv) << 8) | (f2e4m3(y2 * out_inv) << 16) |
+        (f2e4m3(y3 * out_inv) << 24);
+  } else {
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow) = u32x2{pack_bf2(y0, y1), pack_bf2(y2, y3)};
+  }
+}
+
+// ============================================================ decode attention
+// One query row per sequence (a decode step).  Workgroup = (key chunk, kv
+// head, sequence), 4 waves.  The chunk's keys are dealt KPW to a wave
+// instruction, DH/8 lanes per key (lane: 8 dims), so K and V come in as
+// row-contiguous 16-byte loads, U steps of them in flight per wave; the G query
+// heads of the kv head sit in registers.  A key's score is a DPP sum over its
+// lanes (rows of 16 lanes, or half rows for DH 64); each lane keeps an online
+// softmax (max and sum in base 2, its 8 output dims) per head over the keys of
+// its lane row, rescaling once per batch of U keys; the workgroup's 4 * KPW row
+// states are combined through LDS.  A sequence whose keys form one chunk gets
+// its output written here; otherwise the chunk writes (max, sum) and the
+// unnormalised output for attention_merge_kernel, with the chunk plan and the
+// partial layout of attention_kernel.  Keys past the chunk's end read the
+// chunk's last key (in bounds) and score -inf.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+template <int DH, int G>
+__global__ __launch_bounds__(256) void decode_attention_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ start_pos, const int32_t* __restrict__ cache_slot,
+    const int32_t* __restrict__ used_keys, int Hq, int Hkv, int cap, int causal, float scale_log2,
+    void* __restrict__ out, int out_fp8, float out_inv, int chunk_tiles, int n_slots, float* __restrict__ part_o,
+    float2_t* __restrict__ part_ml, int T) {
+  constexpr int LPK = DH / 8;          // lanes per key
+  constexpr int KPW = 64 / LPK;        // keys per wave instruction (lane rows)
+  constexpr int KPS = 4 * KPW;         // keys per workgroup step
+  constexpr int NR = 4 * KPW;          // row states per workgroup
+  constexpr int U = 4;                 // steps per batch
+  __shared__ float s_ml[G][NR][2];
+  __shared__ float s_o[G][NR][DH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int t = cu[s];
+  const int n_keys = causal ? start_pos[s] + 1 : used_keys[s];
+  int ct, nch;
+  chunk_plan((n_keys + AKT - 1) / AKT, chunk_tiles, n_slots, ct, nch);
+  if (c >= nch) return;                                 // whole workgroup
+  const int k0 = c * ct * AKT, k1 = min(n_keys, k0 + ct * AKT);
+  const int r = lane / LPK, d8 = lane % LPK;
+  const int R = wave * KPW + r;
+  const size_t crow = size_t(cache_slot[s]) * cap;
+
+  float qf[G][8];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(q + (size_t(t) * Hq + g * G + hh) * DH + 8 * d8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[hh][e] = (e & 1) ? bf_hi(v[e >> 1]) : bf_lo(v[e >> 1]);
+  }
+  float m[G], l[G], o[G][8];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    m[hh] = -__builtin_inff();
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
+  }
+  const int n_steps = (k1 - k0 + KPS - 1) / KPS;
+  for (int s0 = 0; s0 < n_steps; s0 += U) {
+    u32x4 kv[U], vv[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = k0 + (s0 + u) * KPS + wave * KPW + r;
+      ok[u] = j < k1;
+      const size_t row = (crow + (ok[u] ? j : k1 - 1)) * Hkv + g;
+      kv[u] = *reinterpret_cast<const u32x4*>(kc + row * DH + 8 * d8);
+      vv[u] = *reinterpret_cast<const u32x4*>(vc + row * DH + 8 * d8);
     }
-    const float inv = L > 0.f ? 1.0f / L : 0.f;
-    const size_t orow = (size_t(t) * Hq + h) * DH + 4 * d4;
-    const float y0 = acc[0] * inv, y1 = acc[1] * inv, y2 = acc[2] * inv, y3 = acc[3] * inv;
-    if (out_fp8) {
-      *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(out) + orow) =
-          f2e4m3(y0 * out_inv) | (f2e4m3(y1 * out_inv) << 8) | (f2e4m3(y2 * out_inv) << 16) |
-          (f2e4m3(y3 * out_inv) << 24);
-    } else {
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow) = u32x2{pack_bf2(y0, y1), pack_bf2(y2, y3)};
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float x[U];
+      float mb = -__builtin_inff();
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot += qf[hh][e] * ((e & 1) ? bf_hi(kv[u][e >> 1]) : bf_lo(kv[u][e >> 1]));
+        dot = dpp_add<0xb1>(dot);                        // quad_perm [1,0,3,2]
+        dot = dpp_add<0x4e>(dot);                        // quad_perm [2,3,0,1]
+        dot = dpp_add<0x141>(dot);                       // row_half_mirror: 8 lanes
+        if constexpr (LPK == 16) dot = dpp_add<0x140>(dot);   // row_mirror: 16 lanes
+        x[u] = ok[u] ? dot * scale_log2 : -__builtin_inff();
+        mb = fmaxf(mb, x[u]);
+      }
+      const float mn = fmaxf(m[hh], mb);
+      if (mn == -__builtin_inff()) continue;             // nothing unmasked yet in this lane row
+      const float sc = __builtin_amdgcn_exp2f(m[hh] - mn);   // 0 when m was -inf
+      l[hh] *= sc;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[hh][e] *= sc;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float p = __builtin_amdgcn_exp2f(x[u] - mn);   // 0 for masked keys
+        l[hh] += p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[hh][e] += p * ((e & 1) ? bf_hi(vv[u][e >> 1]) : bf_lo(vv[u][e >> 1]));
+      }
+      m[hh] = mn;
     }
   }
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    if (d8 == 0) {
+      s_ml[hh][R][0] = m[hh];
+      s_ml[hh][R][1] = l[hh];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_o[hh][R][8 * d8 + e] = o[hh][e];
+  }
+  __syncthreads();
+  for (int u = tid; u < G * DH; u += 256) {
+    const int hh = u / DH, d = u % DH;
+    float M = -__builtin_inff();
+    for (int i = 0; i < NR; ++i) M = fmaxf(M, s_ml[hh][i][0]);
+    float L = 0.f, O = 0.f;
+    for (int i = 0; i < NR; ++i) {
+      const float mi = s_ml[hh][i][0];
+      const float w = mi == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mi - M);
+      L += w * s_ml[hh][i][1];
+      O += w * s_o[hh][i][d];
+    }
+    const int hq = g * G + hh;
+    if (nch == 1) {
+      const float y = O / L;
+      const size_t orow = (size_t(t) * Hq + hq) * DH + d;
+      if (out_fp8) static_cast<uint8_t*>(out)[orow] = uint8_t(f2e4m3(y * out_inv));
+      else static_cast<uint16_t*>(out)[orow] = uint16_t(f2bf(y));
+    } else {
+      const size_t prow = (size_t(c) * T + t) * Hq + hq;
+      part_o[prow * DH + d] = O;
+      if (d == 0) part_ml[prow] = float2_t{M, L};
+    }
+  }
+}
+
+template <int DH, int GROUP>
+static void launch_decode_t(const void* q, const void* kc, const void* vc, const int32_t* cu, const int32_t* sp,
+                            const int32_t* slot, const int32_t* used, int n_seq, int Hq, int Hkv, int cap,
+                            bool causal, void* out, bool fp8, float out_inv, const AttnSplit& cfg, hipStream_t st) {
+  const int slots = cfg.chunk_tiles > 0 ? cfg.n_slots : 1;
+  const dim3 grid(slots, Hkv, n_seq);
+  const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf(float(DH));
+  decode_attention_kernel<DH, GROUP><<<grid, 256, 0, st>>>(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), cu, sp,
+      slot, used, Hq, Hkv, cap, causal ? 1 : 0, scale_log2, out, fp8 ? 1 : 0, out_inv, cfg.chunk_tiles, slots,
+      cfg.part_o, reinterpret_cast<float2_t*>(cfg.part_ml), cfg.T);
+  if (cfg.chunk_tiles > 0)
+    attention_merge_kernel<DH><<<dim3(cfg.T, (Hq * (DH / 4) + 255) / 256), 256, 0, st>>>(
+        cu, sp, used, n_seq, Hq, causal ? 1 : 0, 1, cfg.chunk_tiles,
+                                                      slots, cfg.part_o,
+                                                      reinterpret_cast<const float2_t*>(cfg.part_ml), cfg.T, out,
+                                                      fp8 ? 1 : 0, out_inv);
 }
 
 template <int DH, int GROUP>
@@ -398,7 +562,8 @@ static void launch_attn_t(const void* q, const void* kc, const void* vc, const i
         scale_log2, out, fp8 ? 1 : 0, out_inv, sp_cfg.chunk_tiles, slots, sp_cfg.part_o,
         reinterpret_cast<float2_t*>(sp_cfg.part_ml), sp_cfg.T);
   if (sp_cfg.chunk_tiles > 0)
-    attention_merge_kernel<DH><<<sp_cfg.T, 256, 0, st>>>(cu, sp, used, n_seq, Hq, causal ? 1 : 0, QPW,
+    attention_merge_kernel<DH><<<dim3(sp_cfg.T, (Hq * (DH / 4) + 255) / 256), 256, 0, st>>>(
+        cu, sp, used, n_seq, Hq, causal ? 1 : 0, QPW,
                                                          sp_cfg.chunk_tiles, slots, sp_cfg.part_o,
                                                          reinterpret_cast<const float2_t*>(sp_cfg.part_ml),
                                                          sp_cfg.T, out, fp8 ? 1 : 0, out_inv);
@@ -415,8 +580,12 @@ void launch_attention(const void* q, const void* kc, const void* vc, const int32
   const AttnSplit& cfg = split ? *split : none;
 #define HR_ATT(DH_, G_)                                                                         \
   if (d == DH_ && group == G_) {                                                                \
-    launch_attn_t<DH_, G_>(q, kc, vc, cu, sp, slot, used, n_seq, max_len, Hq, Hkv, cap, causal, \
-                           out, fp8, out_inv, cfg, st);                                         \
+    if (cfg.decode)                                                                             \
+      launch_decode_t<DH_, G_>(q, kc, vc, cu, sp, slot, used, n_seq, Hq, Hkv, cap, causal, out, \
+                               fp8, out_inv, cfg, st);                                          \
+    else                                                                                        \
+      launch_attn_t<DH_, G_>(q, kc, vc, cu, sp, slot, used, n_seq, max_len, Hq, Hkv, cap,       \
+                             causal, out, fp8, out_inv, cfg, st);                               \
     return;                                                                                     \
   }
   HR_ATT(128, 4) HR_ATT(128, 2) HR_ATT(128, 1) HR_ATT(64, 4) HR_ATT(64, 2) HR_ATT(64, 1)

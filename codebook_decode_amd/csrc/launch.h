@@ -66,6 +66,7 @@ void launch_rope_attn_small(const void* qkv, int n_seq, int max_len, int Hq, int
 // blocks with more than chunk_tiles 64-key tiles write fp32 partials per chunk
 // (n_slots chunk slots at most) and a merge kernel combines them.
 struct AttnSplit {
+  bool decode = false;      // one row per sequence: decode_attention_kernel (+ merge when chunked)
   int groups = 1;           // wave groups interleaving the key tiles of a block (1 or 2)
   int chunk_tiles = 0;      // 0: no split
   int n_slots = 1;

@@ -9,7 +9,9 @@ the audio head and the delayed-codebook step.
 * hr_decode_step on the tiny model, three streams prefilled with different
   prompt lengths, six steps: each step's logits against the oracle's, codes
   and the codebook-embedding sum bit-exact (the free-running comparison stops
-  at the first near-tie the two sides resolve differently), stream state equal.
+  at the first near-tie the two sides resolve differently: a top-2 margin
+  below 1e-3 or below twice that row's logit error, the gap such an error can
+  close), stream state equal.
 * hr_decode_step on two 4B layers over four streams with long seeded caches:
   logits against the oracle (exact and with bf16 storage rounding), codes
   equal wherever bf16 storage cannot flip them (margin >= 3x the bf16 chain's
@@ -149,7 +151,12 @@ def test_decode_step_tiny_batched(H):
         gcodes = codes.cpu().numpy()
         diff = gcodes != ocodes
         if np.any(diff):
-            assert np.all(margin[diff] < 1e-3), f"step {t}: codes differ outside the margin exemption"
+            # a logit error of at most e per element can swap the top two only
+            # when their gap is below 2e: the 1e-3 exemption widens to twice the
+            # row's own logit error, which the logits check above bounds
+            row_err = np.max(np.abs(logits.cpu().numpy().reshape(B, K, V).astype(np.float64) - olog), axis=-1)
+            exempt = np.maximum(1e-3, 2.0 * row_err)
+            assert np.all(margin[diff] < exempt[diff]), f"step {t}: codes differ outside the margin exemption"
             log(f"step {t}: codes differ on a near-tie; stopping the free-running comparison")
             return
         np.testing.assert_array_equal(bits_of(emb), oemb)

@@ -300,6 +300,11 @@ def test_qknorm_rope_attention(H, model, lens, slots, causal, used, fp8):
     (4, 2, 64, [6, 70], [0, 10], True, None),
     (8, 8, 64, [33], [0], True, None),
     (32, 8, 128, [100], [0], False, [90]),
+    # one row per sequence (decode steps: the decode kernel, one chunk per row)
+    (32, 8, 128, [1, 1, 1], [0, 700, 2000], True, None),
+    (4, 2, 64, [1, 1], [5, 130], True, None),
+    (8, 8, 64, [1], [300], True, None),
+    (32, 8, 128, [1, 1], [0, 0], False, [1, 1]),
 ])
 def test_attention(H, Hq, Hkv, d, lens, starts, causal, used):
     _attention_case(H, Hq, Hkv, d, lens, starts, causal, used)
@@ -316,6 +321,13 @@ def test_attention(H, Hq, Hkv, d, lens, starts, causal, used):
     (4, 2, 64, [200, 7, 90], [0, 0, 600], True, None, 2, 3, False),
     (8, 8, 64, [130], [0], True, None, 1, 64, False),
     (32, 8, 128, [256], [0], True, None, 1, 4, True),
+    # decode steps cut into chunks and merged: one-tile chunks up to the slot
+    # cap (a 32-tile row over 16 slots: 2-tile chunks), a row shorter than one
+    # chunk written directly beside split ones, a ragged last chunk, GQA 2 and 1
+    (32, 8, 128, [1, 1, 1], [0, 700, 2000], True, None, 1, 16, False),
+    (32, 8, 128, [1, 1, 1, 1], [63, 64, 1000, 2046], True, None, 4, 4, True),
+    (4, 2, 64, [1, 1], [60, 900], True, None, 2, 8, False),
+    (8, 8, 64, [1, 1], [129, 1500], True, None, 3, 64, False),
 ])
 def test_attention_chunked(H, Hq, Hkv, d, lens, starts, causal, used, ct, slots, fp8):
     _attention_case(H, Hq, Hkv, d, lens, starts, causal, used, chunked=(ct, slots), fp8=fp8)
