@@ -322,7 +322,11 @@ hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_batch* b, floa
   if (!x_ready)
     hr::launch_rmsnorm(h, T, D, L->in_norm_w, d->rms_eps, w.x, fp8, fp8 ? 1.0f / L->as_qkv : 1.f, st);
   hr::launch_linear(w.x, L->w_qkv, L->ws_qkv, L->as_qkv, fp8, T, NQKV, D, HR_EPI_BF16, w.qkv, 0.f, st);
-  if (const int small = small_prompt(b); small >= 0) {
+  if (split.decode && d->causal) {
+    hr::launch_decode_rope_attention(w.qkv, L->q_norm_w, L->k_norm_w, d->rope_theta, d->rms_eps, kv->k, kv->v,
+                                     b->cu_seqlens, b->start_pos, b->cache_slot, b->n_seq, Hq, Hkv, dh,
+                                     kv->capacity, w.attn, fp8, fp8 ? 1.0f / L->as_o : 1.f, split, st);
+  } else if (const int small = small_prompt(b); small >= 0) {
     hr::launch_rope_attn_small(w.qkv, b->n_seq, small, Hq, Hkv, dh, d->rope_theta, d->rms_eps, b->cu_seqlens,
                                b->cache_slot, b->used_keys, d->causal != 0, L->q_norm_w, L->k_norm_w, kv->k, kv->v,
                                kv->capacity, w.attn, fp8, fp8 ? 1.0f / L->as_o : 1.f, st);

@@ -25,6 +25,7 @@
 // computed.  Probabilities feed the MFMA in bf16; sums and rescaling stay fp32.
 #include "common.h"
 #include "launch.h"
+#include "rope_math.h"
 
 namespace hr {
 
@@ -395,18 +396,31 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(
 // unnormalised output for attention_merge_kernel, with the chunk plan and the
 // partial layout of attention_kernel.  Keys past the chunk's end read the
 // chunk's last key (in bounds) and score -inf.
+// ROPE: q points at the merged QKV rows and step A3 happens here too: wave 0
+// norms and rotates the G query rows of the stream's new token (rope_pairs,
+// the arithmetic of qknorm_rope_kv_kernel, q rounded to bf16 as that kernel
+// stores it) into LDS, and the workgroup of the last chunk also the new k row
+// and the v row, writes both to the cache row start_pos and uses them from
+// LDS for that key (its cache row is being written by the same launch).
+struct RopeArgs {
+  const void* qw;
+  const void* kw;
+  float theta, eps;
+};
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_add(float v) {
   return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
-template <int DH, int G>
+template <int DH, int G, bool ROPE>
 __global__ __launch_bounds__(256) void decode_attention_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ start_pos, const int32_t* __restrict__ cache_slot,
     const int32_t* __restrict__ used_keys, int Hq, int Hkv, int cap, int causal, float scale_log2,
     void* __restrict__ out, int out_fp8, float out_inv, int chunk_tiles, int n_slots, float* __restrict__ part_o,
-    float2_t* __restrict__ part_ml, int T) {
+    float2_t* __restrict__ part_ml, int T, const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
+    const RopeFreq freq, float eps) {
   constexpr int LPK = DH / 8;          // lanes per key
   constexpr int KPW = 64 / LPK;        // keys per wave instruction (lane rows)
   constexpr int KPS = 4 * KPW;         // keys per workgroup step
@@ -425,11 +439,57 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
   const int r = lane / LPK, d8 = lane % LPK;
   const int R = wave * KPW + r;
   const size_t crow = size_t(cache_slot[s]) * cap;
+  const int p_new = n_keys - 1;                          // ROPE: the new token's key
+
+  __shared__ float s_cs[DH / 2], s_sn[DH / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t s_qr[ROPE ? G : 1][DH];
+  __shared__ __attribute__((aligned(16))) uint16_t s_kn[ROPE ? DH : 8], s_vn[ROPE ? DH : 8];
+  if constexpr (ROPE) {
+    constexpr int HALF = DH / 2, L = DH / 16;            // rope layout: L lanes per head row
+    const bool last = c == nch - 1;
+    if (tid < HALF) rope_angle(p_new, freq.inv[tid], s_cs[tid], s_sn[tid]);
+    __syncthreads();
+    if (wave == 0) {
+      const int row = lane / L, c8 = lane % L;
+      const int n_rows = G + (last ? 2 : 0);
+      const int rr = row < n_rows ? row : 0;             // spare lanes repeat row 0 (group_sum needs them)
+      const int head = rr < G ? g * G + rr : (rr == G ? Hq + g : Hq + Hkv + g);
+      const uint16_t* src = q + (size_t(t) * (Hq + 2 * Hkv) + head) * DH;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(src + 8 * c8);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(src + HALF + 8 * c8);
+      const uint16_t* nw = rr < G ? qw : kw;
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(nw + 8 * c8);
+      const u32x4 w1 = *reinterpret_cast<const u32x4*>(nw + HALF + 8 * c8);
+      const float ss = group_sum(pairs_sumsq(lo, hi), L);
+      if (row < n_rows) {
+        const size_t cdst = ((crow + p_new) * Hkv + g) * DH;
+        if (rr <= G) {
+          const float inv = 1.0f / __builtin_sqrtf(ss / float(DH) + eps);
+          u32x4 o0, o1;
+          rope_pairs(lo, hi, w0, w1, inv, &s_cs[8 * c8], &s_sn[8 * c8], o0, o1);
+          uint16_t* dst = rr < G ? &s_qr[rr < G ? rr : 0][0] : &s_kn[0];
+          *reinterpret_cast<u32x4*>(dst + 8 * c8) = o0;
+          *reinterpret_cast<u32x4*>(dst + HALF + 8 * c8) = o1;
+          if (rr == G) {
+            *reinterpret_cast<u32x4*>(kc + cdst + 8 * c8) = o0;
+            *reinterpret_cast<u32x4*>(kc + cdst + HALF + 8 * c8) = o1;
+          }
+        } else {
+          *reinterpret_cast<u32x4*>(&s_vn[8 * c8]) = lo;
+          *reinterpret_cast<u32x4*>(&s_vn[HALF + 8 * c8]) = hi;
+          *reinterpret_cast<u32x4*>(vc + cdst + 8 * c8) = lo;
+          *reinterpret_cast<u32x4*>(vc + cdst + HALF + 8 * c8) = hi;
+        }
+      }
+    }
+    __syncthreads();
+  }
 
   float qf[G][8];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(q + (size_t(t) * Hq + g * G + hh) * DH + 8 * d8);
+    const u32x4 v = ROPE ? *reinterpret_cast<const u32x4*>(&s_qr[ROPE ? hh : 0][8 * d8])
+                         : *reinterpret_cast<const u32x4*>(q + (size_t(t) * Hq + g * G + hh) * DH + 8 * d8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) qf[hh][e] = (e & 1) ? bf_hi(v[e >> 1]) : bf_lo(v[e >> 1]);
   }
@@ -452,6 +512,14 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
       const size_t row = (crow + (ok[u] ? j : k1 - 1)) * Hkv + g;
       kv[u] = *reinterpret_cast<const u32x4*>(kc + row * DH + 8 * d8);
       vv[u] = *reinterpret_cast<const u32x4*>(vc + row * DH + 8 * d8);
+      if constexpr (ROPE) {
+        // the new key: from LDS (the load above may race with its own write
+        // and is discarded)
+        if (j == p_new) {
+          kv[u] = *reinterpret_cast<const u32x4*>(&s_kn[8 * d8]);
+          vv[u] = *reinterpret_cast<const u32x4*>(&s_vn[8 * d8]);
+        }
+      }
     }
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
@@ -523,14 +591,25 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
 template <int DH, int GROUP>
 static void launch_decode_t(const void* q, const void* kc, const void* vc, const int32_t* cu, const int32_t* sp,
                             const int32_t* slot, const int32_t* used, int n_seq, int Hq, int Hkv, int cap,
-                            bool causal, void* out, bool fp8, float out_inv, const AttnSplit& cfg, hipStream_t st) {
+                            bool causal, void* out, bool fp8, float out_inv, const AttnSplit& cfg, hipStream_t st,
+                            const RopeArgs* rope = nullptr) {
   const int slots = cfg.chunk_tiles > 0 ? cfg.n_slots : 1;
   const dim3 grid(slots, Hkv, n_seq);
   const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf(float(DH));
-  decode_attention_kernel<DH, GROUP><<<grid, 256, 0, st>>>(
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), cu, sp,
-      slot, used, Hq, Hkv, cap, causal ? 1 : 0, scale_log2, out, fp8 ? 1 : 0, out_inv, cfg.chunk_tiles, slots,
-      cfg.part_o, reinterpret_cast<float2_t*>(cfg.part_ml), cfg.T);
+  // kc and vc are written only on the RoPE path (the new token's row)
+  uint16_t* kcw = static_cast<uint16_t*>(const_cast<void*>(kc));
+  uint16_t* vcw = static_cast<uint16_t*>(const_cast<void*>(vc));
+  if (rope)
+    decode_attention_kernel<DH, GROUP, true><<<grid, 256, 0, st>>>(
+        static_cast<const uint16_t*>(q), kcw, vcw, cu, sp, slot, used, Hq, Hkv, cap, causal ? 1 : 0, scale_log2,
+        out, fp8 ? 1 : 0, out_inv, cfg.chunk_tiles, slots, cfg.part_o, reinterpret_cast<float2_t*>(cfg.part_ml),
+        cfg.T, static_cast<const uint16_t*>(rope->qw), static_cast<const uint16_t*>(rope->kw),
+        rope_freq(DH, rope->theta), rope->eps);
+  else
+    decode_attention_kernel<DH, GROUP, false><<<grid, 256, 0, st>>>(
+        static_cast<const uint16_t*>(q), kcw, vcw, cu, sp, slot, used, Hq, Hkv, cap, causal ? 1 : 0, scale_log2,
+        out, fp8 ? 1 : 0, out_inv, cfg.chunk_tiles, slots, cfg.part_o, reinterpret_cast<float2_t*>(cfg.part_ml),
+        cfg.T, nullptr, nullptr, RopeFreq{}, 0.f);
   if (cfg.chunk_tiles > 0)
     attention_merge_kernel<DH><<<dim3(cfg.T, (Hq * (DH / 4) + 255) / 256), 256, 0, st>>>(
         cu, sp, used, n_seq, Hq, causal ? 1 : 0, 1, cfg.chunk_tiles,
@@ -570,6 +649,22 @@ static void launch_attn_t(const void* q, const void* kc, const void* vc, const i
 }
 
 int attention_qpw(int Hq, int Hkv) { return 32 * (4 / (Hq / Hkv)); }
+
+void launch_decode_rope_attention(const void* qkv, const void* qw, const void* kw, float theta, float eps,
+                                  void* kc, void* vc, const int32_t* cu, const int32_t* sp, const int32_t* slot,
+                                  int n_seq, int Hq, int Hkv, int d, int cap, void* out, bool fp8, float out_inv,
+                                  const AttnSplit& cfg, hipStream_t st) {
+  const int group = Hq / Hkv;
+  const RopeArgs rope{qw, kw, theta, eps};
+#define HR_DEC(DH_, G_)                                                                         \
+  if (d == DH_ && group == G_) {                                                                \
+    launch_decode_t<DH_, G_>(qkv, kc, vc, cu, sp, slot, nullptr, n_seq, Hq, Hkv, cap, true, out, \
+                             fp8, out_inv, cfg, st, &rope);                                     \
+    return;                                                                                     \
+  }
+  HR_DEC(128, 4) HR_DEC(128, 2) HR_DEC(128, 1) HR_DEC(64, 4) HR_DEC(64, 2) HR_DEC(64, 1)
+#undef HR_DEC
+}
 
 void launch_attention(const void* q, const void* kc, const void* vc, const int32_t* cu,
                       const int32_t* sp, const int32_t* slot, const int32_t* used, int n_seq,

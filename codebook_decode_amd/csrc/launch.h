@@ -80,6 +80,13 @@ void launch_attention(const void* q, const void* kc, const void* vc, const int32
                       int max_len, int Hq, int Hkv, int d, int cap, bool causal, void* out, bool fp8,
                       float out_inv, hipStream_t st, const AttnSplit* split = nullptr);
 
+// Decode steps (one row per sequence, causal): step A3 (q/k norm, RoPE, the new
+// row's K/V write) inside the decode attention launch; qkv = the merged QKV rows.
+void launch_decode_rope_attention(const void* qkv, const void* qw, const void* kw, float theta, float eps,
+                                  void* kc, void* vc, const int32_t* cu, const int32_t* sp, const int32_t* slot,
+                                  int n_seq, int Hq, int Hkv, int d, int cap, void* out, bool fp8, float out_inv,
+                                  const AttnSplit& cfg, hipStream_t st);
+
 void launch_linear(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8,
                    int M, int N, int K, int epi, void* out, float out_scale, hipStream_t st);
 void launch_linear_mx(const uint8_t* x, const uint8_t* x_scales, int lda, const uint8_t* w,

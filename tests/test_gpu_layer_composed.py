@@ -113,3 +113,47 @@ def test_stack_two_layers_matches_composed_steps(H, layers):
             composed_layer(H, m, dims1, b, dls[l], hc, H.make_kv(kc, vc, cap, 1), T)
         torch.cuda.synchronize()
         close("hidden after 2 layers", h.cpu().numpy(), hc.cpu().numpy(), n_layers=2)
+
+
+@pytest.mark.parametrize("starts,slots", [
+    ([37, 700, 1500, 2046], [1, 3, 0, 2]),      # split into key chunks (the layer's workspace)
+    ([0, 5, 63, 64], [0, 1, 2, 3]),             # one chunk each; a stream at position 0
+])
+def test_decode_layer_matches_composed_steps(H, layers, starts, slots):
+    """A decode step (one row per stream over seeded caches): the layer, which
+    norms and rotates q / k and writes the new K/V row inside the decode
+    attention launch, against the composed steps (hr_qknorm_rope_kv, then
+    hr_attention).  The new cache rows must hold the same bits, every other
+    row must be untouched, the hidden within the bar above."""
+    import torch
+    from gpu_util import bits_of, dev, dev_bf16, log
+    from model_util import dims_of, workspace
+    m, dls = layers
+    B, cap = len(starts), 2048
+    dims = dims_of(H, m, True, 1)
+    layer = H.make_layer(dls[0])
+    b = H.Batch(np.arange(B + 1), starts, slots)
+    ws = workspace(H, dims, H.HR_BF16, B)
+    shape = (B * cap, m.n_kv_heads, m.head_dim)
+    kb = np.full(shape, 0x7FC0, np.uint16)
+    vb = np.full(shape, 0x7FC0, np.uint16)
+    for s, (sp, slot) in enumerate(zip(starts, slots)):
+        if sp:
+            kb[slot * cap: slot * cap + sp] = synth.normal_bf16((sp,) + shape[1:], (60, 0, s), 1.0)
+            vb[slot * cap: slot * cap + sp] = synth.normal_bf16((sp,) + shape[1:], (60, 1, s), 1.0)
+    for r in range(REPS):
+        log(f"decode layer starts={starts} repetition {r}")
+        h_init = synth.bf16_bits_to_f32(synth.embed_rows(m, synth.prompt_ids(m, B, seq=300 + r)))
+        hf, hc = dev(h_init.copy()), dev(h_init.copy())
+        kf, vf, kc, vc = dev_bf16(kb), dev_bf16(vb), dev_bf16(kb), dev_bf16(vb)
+        H.hr_prefill_layer(dims, layer, b, hf, H.make_kv(kf, vf, cap, B), ws)
+        composed_layer(H, m, dims, b, dls[0], hc, H.make_kv(kc, vc, cap, B), B)
+        torch.cuda.synchronize()
+        close("hidden", hf.cpu().numpy(), hc.cpu().numpy())
+        np.testing.assert_array_equal(bits_of(kf), bits_of(kc))
+        np.testing.assert_array_equal(bits_of(vf), bits_of(vc))
+        new_rows = [slot * cap + sp for sp, slot in zip(starts, slots)]
+        kfb = bits_of(kf)
+        assert not np.any(kfb[new_rows] == 0x7FC0), "new K rows not written"
+        kfb[new_rows] = kb[new_rows]
+        np.testing.assert_array_equal(kfb, kb)      # nothing else written
