@@ -718,7 +718,11 @@ static void tiled_fill(const uint8_t* x, const uint8_t* w, int M, int N, int Kb,
 // wants small tiles (more workgroups than CUs: QKV at M = 128 runs 39 -> 20 us
 // going from 128x128 to 64x64 tiles with 128-byte slabs); large M wants the
 // 256x256 tile (LDS traffic per MFMA).  Split-K fills the grid for the
-// residual projections.
+// residual projections.  Re-swept at M = 512 once the LDS swizzle and the
+// interleaved fragment reads were in: bf16 QKV and O on 128x128 tiles of 8
+// waves with 128-byte slabs (QKV 32.6 us against 48.8 on 64x128, O 27.5
+// against 34.1 on 128x64; gate/up and down keep their tiles, every
+// alternative tried was slower).
 template <int EPI, bool FP8>
 static void tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
                   hipStream_t st) {
@@ -730,7 +734,10 @@ static void tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, cons
     return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4, 128>(x, w, M, N, Kb, e, st);
   } else if constexpr (EPI == HR_EPI_BF16) {
     if (M > 1024) return tiled_fill<EPI, FP8, 256, 256, 4, 2, 4>(x, w, M, N, Kb, e, st);
-    if (M > 384) return tiled_fill<EPI, FP8, 64, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
+    if (M > 384) {
+      if constexpr (FP8) return tiled_fill<EPI, FP8, 64, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
+      else return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st);
+    }
     if (M > 128) return tiled_fill<EPI, FP8, 128, 64, 2, 2, 6, 128>(x, w, M, N, Kb, e, st);
     if (M <= 64) return tiled_fill<EPI, FP8, 64, 32, 2, 1, 8, 128>(x, w, M, N, Kb, e, st);
     return tiled_fill<EPI, FP8, 64, 64, 2, 2, 8, 128>(x, w, M, N, Kb, e, st);
@@ -741,7 +748,7 @@ static void tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, cons
     if (M > 1024) return tiled_fill<EPI, FP8, 256, 256, 4, 2, 4>(x, w, M, N, Kb, e, st);
     if (M > 384) {
       if (K_el >= 8192) return tiled_fill<EPI, FP8, 256, 128, 4, 2, 4>(x, w, M, N, Kb, e, st, 6);
-      return tiled_fill<EPI, FP8, 128, 64, 2, 2, 4>(x, w, M, N, Kb, e, st, 3);
+      return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st, 3);
     }
     if (M > 128) return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
     if (M <= 64 && K_el >= 8192) return tiled_fill<EPI, FP8, 64, 64, 2, 2, 8, 128>(x, w, M, N, Kb, e, st);
