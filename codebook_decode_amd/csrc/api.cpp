@@ -140,6 +140,9 @@ hr_status check_layer(const hr_dims* d, const hr_layer* L, int idx) {
     for (float v : a)
       if (!(v > 0.f) || !std::isfinite(v))
         return fail(HR_EINVAL, "layer %d: FP8 activation scales must be finite and > 0", idx);
+    // e4m3 GEMMs step K in slabs of up to 128 values
+    if (d->hidden % 128 || d->ffn % 128 || (d->n_q_heads * d->head_dim) % 128)
+      return fail(HR_EUNSUPPORTED, "layer %d: FP8 needs D, F and Hq d to be multiples of 128", idx);
   }
   if (L->wtype == HR_MXFP4) {
     const uint8_t* sc[] = {L->mx_o_s, L->mx_gu_s, L->mx_down_s};

@@ -79,6 +79,7 @@ def call_layer(d, L, b, kvv, ws_bytes=1 << 40, h=FAKE, ws=FAKE):
     ("used_missing", H.HR_EINVAL), ("cu_not_monotone", H.HR_EINVAL), ("workspace", H.HR_EWORKSPACE),
     ("misaligned_h", H.HR_EALIGN), ("fp8_scale", H.HR_EINVAL), ("noncausal_start", H.HR_EUNSUPPORTED),
     ("weight_4gb", H.HR_EUNSUPPORTED), ("activation_4gb", H.HR_EUNSUPPORTED),
+    ("fp8_k64", H.HR_EUNSUPPORTED),
 ])
 def test_prefill_layer_validation(case, status):
     d, L, b, k = dims(), layer(), batch([13]), kv()
@@ -112,6 +113,10 @@ def test_prefill_layer_validation(case, status):
     elif case == "fp8_scale":
         L = layer(wtype=H.HR_FP8_E4M3, ws_qkv=FAKE, ws_o=FAKE, ws_gu=FAKE, ws_down=FAKE,
                   as_qkv=1.0, as_o=0.0, as_gu=1.0, as_down=1.0)
+    elif case == "fp8_k64":                          # e4m3 K steps of 128 values: F = 9664 is not one
+        d = dims(ffn=9664)
+        L = layer(wtype=H.HR_FP8_E4M3, ws_qkv=FAKE, ws_o=FAKE, ws_gu=FAKE, ws_down=FAKE,
+                  as_qkv=1.0, as_o=1.0, as_gu=1.0, as_down=1.0)
     elif case == "noncausal_start":
         d, b = dims(causal=False), batch([13], starts=[4], used=[13])
     elif case == "weight_4gb":                       # 2F x D bf16 gate/up >= 4 GB
