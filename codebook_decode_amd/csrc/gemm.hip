@@ -813,9 +813,12 @@ void launch_linear_mx(const uint8_t* x, const uint8_t* x_scales, int lda, const 
   e.mx_out_s = out_scales;
   e.mx_ldo = ldo;
   const int Kb = K / 2;
-  if (epi == HR_EPI_SWIGLU) tiled_fill<HR_EPI_SWIGLU, false, 256, 256, 4, 2, 4, 64, true>(x, w, M, N, Kb, e, st);
+  // tiles from a sweep of the MXFP4 layer at P = 512: gate/up 128 x 128 on 8
+  // waves (the layer 166 -> 156 us against 256 x 256), O and down 64 x 128
+  // (-> 153 us against 128 x 64; 128 x 128 and 64 x 64 slower)
+  if (epi == HR_EPI_SWIGLU) tiled_fill<HR_EPI_SWIGLU, false, 128, 128, 4, 2, 4, 64, true>(x, w, M, N, Kb, e, st);
   else if (M > 1024) tiled_fill<HR_EPI_RESIDUAL, false, 256, 256, 4, 2, 4, 64, true>(x, w, M, N, Kb, e, st);
-  else tiled_fill<HR_EPI_RESIDUAL, false, 128, 64, 4, 1, 4, 64, true>(x, w, M, N, Kb, e, st);
+  else tiled_fill<HR_EPI_RESIDUAL, false, 64, 128, 2, 2, 4, 64, true>(x, w, M, N, Kb, e, st);
 }
 
 // Head: zsplit bf16 [2n, D] (hi rows then lo rows), W bf16 [N, D] -> fp32 [n, N]
