@@ -721,9 +721,11 @@ static void tiled_fill(const uint8_t* x, const uint8_t* w, int M, int N, int Kb,
 // residual projections.  Re-swept at M = 512 once the LDS swizzle and the
 // interleaved fragment reads were in: bf16 QKV and O on 128x128 tiles of 8
 // waves with 128-byte slabs (QKV 32.6 us against 48.8 on 64x128, O 27.5
-// against 34.1 on 128x64, e4m3 QKV at M = 544 22.5 against 30.7; gate/up and
-// down keep their tiles, every alternative tried was slower, as were e4m3 O and
-// down on 128x128); at M = 4096 the residual projections on the
+// against 34.1 on 128x64; gate/up and down keep their tiles, every alternative
+// tried was slower); e4m3 at M = 544: QKV and gate/up on the same 128x128
+// tiles (22.5 against 30.7 us on 64x128, 58.1 against 60.3 on 256x256), O and
+// down on 64x64 with 128-byte slabs (26.1 / 44.6 against 28.8 / 46.0 on
+// 128x64); at M = 4096 the residual projections on the
 // same 128x128 tiles (O 140 us against 156 on 256x256, down 284 against 289,
 // QKV stays on 256x256: 153 against 177); at M = 128 gate/up on 8 waves (35.9
 // against 38.0 us), down 128x64 and O 64x64 with 128-byte slabs (32.5 / 14.1
@@ -734,7 +736,10 @@ static void tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, cons
   const int K_el = FP8 ? Kb : Kb / 2;
   if constexpr (EPI == HR_EPI_SWIGLU) {
     if (M <= 64) return tiled_fill<EPI, FP8, 64, 128, 2, 2, 6, 128>(x, w, M, N, Kb, e, st);
-    if (M > 384) return tiled_fill<EPI, FP8, 256, 256, 4, 2, 4>(x, w, M, N, Kb, e, st);
+    if (M > 384) {
+      if constexpr (FP8) return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st);
+      else return tiled_fill<EPI, FP8, 256, 256, 4, 2, 4>(x, w, M, N, Kb, e, st);
+    }
     if (M > 128) return tiled_fill<EPI, FP8, 256, 128, 4, 2, 4>(x, w, M, N, Kb, e, st);
     return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st);
   } else if constexpr (EPI == HR_EPI_BF16) {
@@ -745,7 +750,7 @@ static void tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, cons
     return tiled_fill<EPI, FP8, 64, 64, 2, 2, 8, 128>(x, w, M, N, Kb, e, st);
   } else {
     if constexpr (FP8) {
-      if (M > 128) return tiled_fill<EPI, FP8, 128, 64, 4, 1, 4>(x, w, M, N, Kb, e, st);
+      if (M > 128) return tiled_fill<EPI, FP8, 64, 64, 2, 2, 4, 128>(x, w, M, N, Kb, e, st);
     }
     if (M > 1024) return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st);
     if (M > 384) {
