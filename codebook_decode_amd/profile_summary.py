@@ -26,7 +26,7 @@ def short(name: str) -> str:
 
 def render(path: str, title: str, command: str, notes: list) -> str:
     rows = list(csv.DictReader(open(path)))
-    out = [f"# {title}", "", "Command (repository root on the GPU box):", "", f"    {command}", ""]
+    out = [f"# {title}", "", "Command (repository root on the MI355X host):", "", f"    {command}", ""]
     out += notes + [""] if notes else []
     out += ["| kernel | calls | total us | avg us | min us | max us | % |", "|---|---:|---:|---:|---:|---:|---:|"]
     for r in rows:
@@ -75,7 +75,7 @@ def render_traffic(fetch_csv: str, write_csv: str, fetch_cmd: str, write_cmd: st
     algo = 19456 * 2560 * 2 + 512 * 2560 * 2 + 512 * 9728 * 2
     lines = [
         "# HBM traffic of the gate/up GEMM, M = 512 (512 x 19456 x 2560, bf16, SwiGLU epilogue)", "",
-        "Commands (repository root on the GPU box; one counter set per run):", "",
+        "Commands (repository root on the MI355X host; one counter set per run):", "",
         f"    {fetch_cmd}", f"    {write_cmd}", "",
         "`codebook_decode_amd.traffic_probe` launches the GEMM on 3 distinct weight matrices, then a plain "
         "256 MiB device copy twice. The copy's readings against the 256 MiB it must read and write give the "
