@@ -6,6 +6,8 @@ the audio head and the delayed-codebook step.
   rows (seeded values): 4 streams x 8 kv heads give 32 query blocks, the
   longest row spans 30 key tiles, so the layer splits the rows into key
   chunks and merges the partials.  Per-layer bf16 checks as for the prefill.
+* The FP8 layer on the same kind of decode step (the attention output in
+  e4m3), at the FP8 bar against the unquantised and the fake-quant oracle.
 * hr_decode_step on the tiny model, three streams prefilled with different
   prompt lengths, six steps: each step's logits against the oracle's, codes
   and the codebook-embedding sum bit-exact (the free-running comparison stops
@@ -74,6 +76,45 @@ def test_layer_decode_rows_over_long_caches(H):
     he, _, _ = oracle_layer(m, bits, lens, starts, slots, cap, h0, caches=(ek, ev), store=op.round_bf16)
     check_hidden("hidden", hg, hr, he)
     compare_caches(kcg, vcg, kcr, vcr)
+
+
+def test_layer_decode_fp8_rows_over_long_caches(H):
+    """The FP8 layer on a decode step (one row per stream over seeded caches):
+    the new rows' q/k norm, RoPE and K/V write inside the decode attention
+    launch, its output quantised to e4m3 for the O projection.  Held to the FP8
+    bar against the unquantised and the fake-quant oracle."""
+    import torch
+    from gpu_util import bits_of, cosine, log
+    from model_util import fp8_pack, upload_layer
+    from oracle import fp8 as of
+    from test_gpu_layer import check_fp8, fp8_scales, oracle_layer, run_gpu_layer
+    m = synth.QWEN3_4B.with_layers(1)
+    lens, starts, slots, cap = [1, 1, 1, 1], [1900, 700, 1200, 460], [0, 1, 2, 3], 2048
+    log(f"fp8 decode rows over long caches: starts {starts}")
+    bits = synth.layer_tensors(m, 0)
+    lw = op.widen_layer(bits)
+    scales, = fp8_scales(m, [lw])
+    kb, vb = seeded_prefix(m, starts, slots, cap, (78,))
+    h0 = nx.bf16_to_f64(synth.embed_rows(m, synth.prompt_ids(m, 4, seq=6)))
+    import codebook_decode_amd.hr as HH
+    w8, ws = fp8_pack(HH, upload_layer(bits), m)
+    torch.cuda.synchronize()
+    (gk, gv), (ok, ov) = caches_from_bits(kb, vb)
+    hg, kcg, vcg = run_gpu_layer(H, m, bits, lens, starts, slots, cap, h0, caches=(gk, gv),
+                                 fp8=(scales, (w8, ws)))
+    hr, kcr, vcr = oracle_layer(m, bits, lens, starts, slots, cap, h0, caches=(ok, ov))
+    _, (fk, fv) = caches_from_bits(kb, vb)
+    packed = of.pack_layer({k: v.astype(np.float32) for k, v in lw.items()})
+    ob = {"cu_seqlens": np.arange(5), "start_pos": starts, "cache_slot": slots, "capacity": cap}
+    hf = of.fp8_layer(m, lw, scales, packed, ob, h0, fk, fv, True, None)
+    check_fp8("fp8 decode hidden", hg, hr, hf)
+    rows = [sl * cap + sp for sp, sl in zip(starts, slots)]
+    kgb = bits_of(kcg)
+    ck = cosine(nx.bf16_to_f64(kgb[rows]), kcr[rows])
+    log(f"  fp8 decode new K rows cos = {ck:.6f}")
+    assert ck >= 0.998
+    kgb[rows] = kb[rows]
+    np.testing.assert_array_equal(kgb, kb)                  # no other row written
 
 
 def _oracle_decode(m, lw_of, starts, slots, cap, x_rows, caches, wf, wh, store=None):
