@@ -293,3 +293,108 @@ def test_stack_composes_layers_and_final_norm():
         h = op.prefill_layer(m, lws[l], b, h, kc, vc)
     np.testing.assert_array_equal(hL, h)
     np.testing.assert_array_equal(z, op.rms_norm(h, wf))
+
+
+# ----------------------------------------------------------------------------- per-head q/k norm
+def _scalar_qk_attention(m, lw, h, start):
+    """Independent scalar evaluation of steps 1-6 of the layer for one causal
+    sequence at positions start, start+1, ... ("Stabilize Higgs Audio
+    termination and prefill", Summary: q/k norm + RoPE, then attention).
+    Per head, over its d values: RMS with its own weight (q_norm for query
+    heads, k_norm for key heads), THEN the rotation, written as the complex
+    product (x_m + i x_{m+d/2}) * exp(i p theta^(-2m/d)).  Returns the rotated
+    keys [T][Hkv][d] and the attention outputs [T][Hq][d] as Python floats."""
+    import cmath
+    D, Hq, Hkv, d = m.hidden, m.n_q_heads, m.n_kv_heads, m.head_dim
+    eps, theta, half = m.rms_eps, m.rope_theta, m.head_dim // 2
+    T = h.shape[0]
+    W = [[float(v) for v in row] for row in lw["w_qkv"]]
+
+    def rms(vals, w):
+        ms = math.fsum(v * v for v in vals) / len(vals)
+        inv = 1.0 / math.sqrt(ms + eps)
+        return [v * inv * float(wj) for v, wj in zip(vals, w)]
+
+    def rotate(vals, p):
+        out = [0.0] * d
+        for mm in range(half):
+            z = complex(vals[mm], vals[mm + half]) * cmath.exp(1j * p * theta ** (-2.0 * mm / d))
+            out[mm], out[mm + half] = z.real, z.imag
+        return out
+
+    qs, ks, vs = [], [], []
+    for t in range(T):
+        x = rms([float(v) for v in h[t]], lw["in_norm"])
+        row = [math.fsum(x[j] * W[n][j] for j in range(D)) for n in range(len(W))]
+        p = start + t
+        qs.append([rotate(rms(row[hh * d:(hh + 1) * d], lw["q_norm"]), p) for hh in range(Hq)])
+        kb = Hq * d
+        ks.append([rotate(rms(row[kb + g * d:kb + (g + 1) * d], lw["k_norm"]), p) for g in range(Hkv)])
+        vb = (Hq + Hkv) * d
+        vs.append([row[vb + g * d:vb + (g + 1) * d] for g in range(Hkv)])
+    outs = []
+    for i in range(T):
+        per_head = []
+        for hh in range(Hq):
+            g = hh // (Hq // Hkv)
+            sc = [math.fsum(a * b for a, b in zip(qs[i][hh], ks[j][g])) / math.sqrt(d) for j in range(i + 1)]
+            mx = max(sc)
+            e = [math.exp(s - mx) for s in sc]
+            tot = math.fsum(e)
+            per_head.append([math.fsum(e[j] * vs[j][g][c] for j in range(i + 1)) / tot for c in range(d)])
+        outs.append(per_head)
+    return ks, outs
+
+
+def test_qk_norm_per_head_with_own_weight_before_rope():
+    """Cache keys and attention outputs of a 5-token prompt against the scalar
+    evaluation above, with q_norm and k_norm far apart (a swapped weight, a
+    norm across heads, a norm after the rotation or a dropped norm each move
+    the result by orders of magnitude more than the tolerance)."""
+    m = Dims(rope_theta=10.0)
+    lw = rand_layer(m, seed=21, scale=0.4)
+    g = np.random.default_rng(22)
+    lw["q_norm"] = 1.0 + 0.6 * g.standard_normal(m.head_dim)
+    lw["k_norm"] = 0.5 + 0.4 * g.standard_normal(m.head_dim)
+    T = 5
+    h = g.standard_normal((T, m.hidden))
+    kc, vc = op.new_cache(m, 1, 16)
+    taps = {}
+    op.prefill_layer(m, lw, batch_of([T], 16), h, kc, vc, True, taps=taps)
+    ks, outs = _scalar_qk_attention(m, lw, h, 0)
+    np.testing.assert_allclose(kc[:T], np.array(ks), rtol=1e-11, atol=1e-12)
+    o = taps["o"].reshape(T, m.n_q_heads, m.head_dim)
+    np.testing.assert_allclose(o, np.array(outs), rtol=1e-10, atol=1e-11)
+
+
+def test_qk_norm_removes_the_scale_of_each_head_alone():
+    """Scaling the W_qkv rows of ONE query head (or one key head) by c > 0
+    leaves the layer output unchanged when the RMSNorm runs per head (eps 0);
+    a norm over all heads at once would let that head's scale move the
+    others."""
+    m = Dims(rms_eps=0.0, rope_theta=100.0)
+    lw = rand_layer(m, seed=23)
+    d, Hq = m.head_dim, m.n_q_heads
+    ref, *_ = run_layer(m, lw, [6])
+    for rows in (slice(1 * d, 2 * d), slice((Hq + 1) * d, (Hq + 2) * d)):   # q head 1, k head 1
+        lw2 = {k: v.copy() for k, v in lw.items()}
+        lw2["w_qkv"][rows] *= 3.7
+        got, *_ = run_layer(m, lw2, [6])
+        np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-11)
+    # the v rows carry no norm: the same scale on a value head changes the output
+    lw3 = {k: v.copy() for k, v in lw.items()}
+    lw3["w_qkv"][(Hq + 2) * d:(Hq + 3) * d] *= 3.7
+    got, *_ = run_layer(m, lw3, [6])
+    assert np.max(np.abs(got - ref)) > 1e-3
+
+
+def test_qk_norm_weights_are_not_interchangeable():
+    m = Dims(rope_theta=10.0)
+    lw = rand_layer(m, seed=24)
+    lw["q_norm"] = np.linspace(0.3, 1.9, m.head_dim)
+    lw["k_norm"] = np.linspace(1.7, 0.2, m.head_dim)
+    ref, kc_ref, *_ = run_layer(m, lw, [5])
+    lw2 = dict(lw, q_norm=lw["k_norm"], k_norm=lw["q_norm"])
+    got, kc_got, *_ = run_layer(m, lw2, [5])
+    assert np.max(np.abs(got - ref)) > 1e-3
+    assert np.max(np.abs(kc_got[:5] - kc_ref[:5])) > 1e-2
