@@ -148,15 +148,17 @@ def gemm_gu_launches(H, m, P, dev_layers):
 def gemm_traffic():
     """Bytes per launch of the gate/up GEMM from the committed FETCH_SIZE /
     WRITE_SIZE summary, if it was taken on the current GEMM source (else None)."""
+    import hashlib
     import re
-    from codebook_decode_amd.profile_summary import source_digest
     path = os.path.join(ROOT, "profiles", "gemm_gateup_m512_traffic.md")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
     m_t = re.search(r"traffic_bytes_per_launch: (\d+)", txt)
     m_h = re.search(r"gemm_source_sha256: ([0-9a-f]+)", txt)
-    if not m_t or not m_h or m_h.group(1) != source_digest():
+    src = os.path.join(ROOT, "codebook_decode_amd", "csrc", "gemm.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if not m_t or not m_h or m_h.group(1) != digest:
         return None
     return int(m_t.group(1))
 
