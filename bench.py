@@ -135,8 +135,8 @@ def time_kernel_events(fn_list, reps=3):
 def gemm_gu_launches(H, m, P, dev_layers):
     """The gate/up + SwiGLU GEMM of the P-row prefill, one launch per layer's weights."""
     import torch
-    x = torch.randn((P, m.hidden), device="cuda").to(torch.bfloat16)
-    out = torch.empty((P, m.ffn), dtype=torch.bfloat16, device="cuda")
+    x = torch.randn((P, m.hidden), device="cuda").to(torch.float16)
+    out = torch.empty((P, m.ffn), dtype=torch.float16, device="cuda")
     fns = []
     for dl in dev_layers:
         w = dl["w_gu"]
@@ -391,29 +391,30 @@ def codebook_policy_steps(H, m, shared, B=64, reps=100):
 
 def hbm_sweep(H, m, shared):
     """The memory-bound kernels where their bytes outgrow launch latency:
-    RMSNorm (6 B per element), q/k norm + RoPE + KV write (24.6 KB per token),
-    codebook step (62.5 KB per stream)."""
+    RMSNorm (6 B per element: fp32 in, fp16 out), q/k norm + RoPE + KV write
+    (36.9 KB per token: fp32 QKV row in, fp16 q and bf16 K/V out), codebook
+    step (62.5 KB per stream)."""
     import torch
     from model_util import dims_of
     out = {}
     D = m.hidden
     for T in (4096, 65536):
         h = torch.randn((T, D), device="cuda")
-        x = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+        x = torch.empty((T, D), dtype=torch.float16, device="cuda")
         sec = time_events(lambda: H.hr_rmsnorm(h, T, D, shared["final"], m.rms_eps, x), 10)
         out[f"rmsnorm_T{T}"] = {"us": round(sec * 1e6, 2), "roofline": hbm(6 * T * D, sec)}
         del h, x
     for T in (4096, 32768):
         dims = dims_of(H, m, True, 1)
-        qkv = (torch.randn((T, m.qkv_rows), device="cuda") * 0.5).to(torch.bfloat16)
-        q = torch.empty((T, m.attn_width), dtype=torch.bfloat16, device="cuda")
+        qkv = torch.randn((T, m.qkv_rows), device="cuda") * 0.5
+        q = torch.empty((T, m.attn_width), dtype=torch.float16, device="cuda")
         kc = torch.empty((T, m.n_kv_heads, m.head_dim), dtype=torch.bfloat16, device="cuda")
         vc = torch.empty_like(kc)
         b = H.Batch([0, T], [0], [0])
         kv = H.make_kv(kc, vc, T, 1)
         qn = shared["final"][:m.head_dim]
         sec = time_events(lambda: H.hr_qknorm_rope_kv(dims, b, qkv, qn, qn, q, kv), 10)
-        bytes_ = T * (m.qkv_rows * 2 + m.attn_width * 2 + 2 * m.n_kv_heads * m.head_dim * 2)
+        bytes_ = T * (m.qkv_rows * 4 + m.attn_width * 2 + 2 * m.n_kv_heads * m.head_dim * 2)
         out[f"qknorm_rope_kv_T{T}"] = {"us": round(sec * 1e6, 2), "roofline": hbm(bytes_, sec)}
         del qkv, q, kc, vc
     for B in (4096, 16384):

@@ -161,6 +161,7 @@ hr_status check_layer(const hr_dims* d, const hr_layer* L, int idx) {
 
 struct Ws {
   uint8_t *x, *qkv, *q, *attn, *act, *head;
+  float* part;               // split-K partials of the O / down projections [ks][T][D] (null: none needed)
   float *part_o, *part_ml;   // key-chunk partials of the split attention (null: no split)
   uint8_t *mx_s1, *mx_s2;    // MXFP4 block scales: O / gate-up input, down input (ld mx_ld)
   int mx_ld;                 // rows of the scale layouts: T rounded up to the 256-row tile
@@ -183,6 +184,29 @@ size_t part_rows(size_t t) {
   return r > size_t(kDecodeSlotRows) ? r : size_t(kDecodeSlotRows);
 }
 
+// Largest split-K factor the residual projections (O: K = Hq d, down: K = F;
+// N = D, M = T rows) take in any weight format: the partial buffer holds that
+// many [T, D] fp32 slices.
+int residual_ks(const hr_dims* d, int32_t T) {
+  if (T <= 0) return 1;
+  const int D = d->hidden, A = d->n_q_heads * d->head_dim, F = d->ffn;
+  int ks = 1;
+  for (int K : {A, F}) {
+    for (bool fp8 : {false, true}) {
+      if (fp8 && K % 128) continue;
+      const int k = hr::launch_linear(nullptr, nullptr, nullptr, 1.f, fp8, T, D, K, HR_EPI_RESIDUAL, nullptr, 0.f,
+                                      nullptr, false, nullptr);
+      ks = k > ks ? k : ks;
+    }
+    if (D % 256 == 0 && K % 128 == 0) {
+      const int k = hr::launch_linear_mx(nullptr, nullptr, 0, nullptr, nullptr, T, D, K, HR_EPI_RESIDUAL, nullptr,
+                                         nullptr, 0, nullptr, false, nullptr);
+      ks = k > ks ? k : ks;
+    }
+  }
+  return ks;
+}
+
 size_t ws_layout(const hr_dims* d, int32_t T, Ws* w, uint8_t* base) {
   const size_t D = d->hidden, F = d->ffn, A = size_t(d->n_q_heads) * d->head_dim;
   const size_t NQKV = size_t(d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
@@ -195,7 +219,7 @@ size_t ws_layout(const hr_dims* d, int32_t T, Ws* w, uint8_t* base) {
   };
   Ws tmp;
   tmp.x = take(t * (D > A ? D : A) * 2);
-  tmp.qkv = take(t * NQKV * 2);
+  tmp.qkv = take(t * NQKV * 4);     // fp32: the q/k norm reads unrounded projections
   tmp.q = take(t * A * 2);
   tmp.attn = take(t * A * 2);
   tmp.act = take(t * F * 2);
@@ -204,6 +228,8 @@ size_t ws_layout(const hr_dims* d, int32_t T, Ws* w, uint8_t* base) {
   tmp.mx_ld = int((t + 255) / 256 * 256);
   tmp.mx_s1 = take(((D > A ? D : A) / 128) * size_t(tmp.mx_ld) * 4);
   tmp.mx_s2 = take((F / 128) * size_t(tmp.mx_ld) * 4);
+  const int ks = residual_ks(d, T);
+  tmp.part = ks > 1 ? reinterpret_cast<float*>(take(size_t(ks) * t * D * 4)) : nullptr;
   tmp.part_o = tmp.part_ml = nullptr;
   if (t > 0 && t <= size_t(kAttnSplitT)) {
     const size_t rows = part_rows(t);
@@ -314,51 +340,83 @@ int small_prompt(const hr_batch* b) {
   return longest;
 }
 
+// Input norm of a layer in its format: fp16 for the bf16 and MXFP4 bands
+// (their QKV GEMM takes fp16 activations), e4m3 with the layer's QKV scale.
+void in_norm_mode(const hr_layer* L, int* mode, float* inv) {
+  const bool fp8 = L->wtype == HR_FP8_E4M3;
+  *mode = fp8 ? hr::kNormE4M3 : hr::kNormF16;
+  *inv = fp8 ? 1.0f / L->as_qkv : 1.f;
+}
+
 // one layer's kernels over buffers already validated.  `x_ready`: w.x already
-// holds RMSNorm_in(h) of this layer.
-hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_batch* b, float* h, const hr_kv* kv,
-                    const Ws& w, bool x_ready, hipStream_t st) {
+// holds RMSNorm_in(h) of this layer.  `next`: the following layer (its input
+// norm is fused with this layer's last residual add), or null: the residual
+// is completed alone.
+hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_layer* next, const hr_batch* b, float* h,
+                    const hr_kv* kv, const Ws& w, bool x_ready, hipStream_t st) {
   const int T = b->total_tokens, D = d->hidden, F = d->ffn, Hq = d->n_q_heads, Hkv = d->n_kv_heads;
   const int dh = d->head_dim, A = Hq * dh, NQKV = (Hq + 2 * Hkv) * dh;
   const bool fp8 = L->wtype == HR_FP8_E4M3, mx = L->wtype == HR_MXFP4;
+  const float eps = d->rms_eps;
   const hr::AttnSplit split = attn_plan(d, b, &w);
-  if (!x_ready)
-    hr::launch_rmsnorm(h, T, D, L->in_norm_w, d->rms_eps, w.x, fp8, fp8 ? 1.0f / L->as_qkv : 1.f, st);
-  hr::launch_linear(w.x, L->w_qkv, L->ws_qkv, L->as_qkv, fp8, T, NQKV, D, HR_EPI_BF16, w.qkv, 0.f, st);
+  if (!x_ready) {
+    int mode;
+    float inv;
+    in_norm_mode(L, &mode, &inv);
+    hr::launch_residual_norm(h, nullptr, 0, T, D, L->in_norm_w, eps, mode, w.x, inv, nullptr, nullptr, 0, st);
+  }
+  hr::launch_linear(w.x, L->w_qkv, L->ws_qkv, L->as_qkv, fp8, T, NQKV, D, HR_EPI_F32, w.qkv, 0.f, nullptr, true,
+                    st);
   if (split.decode && d->causal) {
-    hr::launch_decode_rope_attention(w.qkv, L->q_norm_w, L->k_norm_w, d->rope_theta, d->rms_eps, kv->k, kv->v,
+    hr::launch_decode_rope_attention(w.qkv, L->q_norm_w, L->k_norm_w, d->rope_theta, eps, kv->k, kv->v,
                                      b->cu_seqlens, b->start_pos, b->cache_slot, b->n_seq, Hq, Hkv, dh,
                                      kv->capacity, w.attn, fp8, fp8 ? 1.0f / L->as_o : 1.f, split, st);
   } else if (const int small = small_prompt(b); small >= 0) {
-    hr::launch_rope_attn_small(w.qkv, b->n_seq, small, Hq, Hkv, dh, d->rope_theta, d->rms_eps, b->cu_seqlens,
+    hr::launch_rope_attn_small(w.qkv, b->n_seq, small, Hq, Hkv, dh, d->rope_theta, eps, b->cu_seqlens,
                                b->cache_slot, b->used_keys, d->causal != 0, L->q_norm_w, L->k_norm_w, kv->k, kv->v,
                                kv->capacity, w.attn, fp8, fp8 ? 1.0f / L->as_o : 1.f, st);
   } else {
-    hr::launch_qknorm_rope_kv(w.qkv, T, Hq, Hkv, dh, d->rope_theta, d->rms_eps, b->cu_seqlens, b->start_pos,
+    hr::launch_qknorm_rope_kv(w.qkv, T, Hq, Hkv, dh, d->rope_theta, eps, b->cu_seqlens, b->start_pos,
                               b->cache_slot, b->used_keys, b->n_seq, d->causal != 0, L->q_norm_w, L->k_norm_w,
                               w.q, kv->k, kv->v, kv->capacity, st);
     hr::launch_attention(w.q, kv->k, kv->v, b->cu_seqlens, b->start_pos, b->cache_slot, b->used_keys, b->n_seq,
                          b->max_seqlen, Hq, Hkv, dh, kv->capacity, d->causal != 0, w.attn, fp8,
                          fp8 ? 1.0f / L->as_o : 1.f, st, &split);
   }
+  // after the down projection: the residual completed, fused with the next
+  // layer's input norm (or alone after the last layer)
+  int next_mode = hr::kNormNone;
+  float next_inv = 1.f;
+  if (next) in_norm_mode(next, &next_mode, &next_inv);
+  const void* next_w = next ? next->in_norm_w : nullptr;
   if (mx) {
     // O, gate/up and down on MXFP4: per-row block quantisation of each input
     // (1/s applied first), the gate/up epilogue writing the down input
     const uint8_t* wo = static_cast<const uint8_t*>(L->w_o);
-    hr::launch_quant_mx(w.attn, false, T, A, L->awq_inv_o, nullptr, w.x, w.mx_s1, w.mx_ld, st);
-    hr::launch_linear_mx(w.x, w.mx_s1, w.mx_ld, wo, L->mx_o_s, T, D, A, HR_EPI_RESIDUAL, h, nullptr, 0, st);
-    hr::launch_rmsnorm_mx(h, T, D, L->post_norm_w, L->awq_inv_gu, d->rms_eps, w.x, w.mx_s1, w.mx_ld, st);
+    hr::launch_quant_mx(w.attn, 2, T, A, L->awq_inv_o, nullptr, w.x, w.mx_s1, w.mx_ld, st);
+    int ks = hr::launch_linear_mx(w.x, w.mx_s1, w.mx_ld, wo, L->mx_o_s, T, D, A, HR_EPI_RESIDUAL, h, nullptr, 0,
+                                  w.part, true, st);
+    hr::launch_residual_norm(h, w.part, ks > 1 ? ks : 0, T, D, L->post_norm_w, eps, hr::kNormMX, w.x, 1.f,
+                             L->awq_inv_gu, w.mx_s1, w.mx_ld, st);
     hr::launch_linear_mx(w.x, w.mx_s1, w.mx_ld, static_cast<const uint8_t*>(L->w_gu), L->mx_gu_s, T, 2 * F, D,
-                         HR_EPI_SWIGLU, w.act, w.mx_s2, w.mx_ld, st);
-    hr::launch_linear_mx(w.act, w.mx_s2, w.mx_ld, static_cast<const uint8_t*>(L->w_down), L->mx_down_s, T, D, F,
-                         HR_EPI_RESIDUAL, h, nullptr, 0, st);
+                         HR_EPI_SWIGLU, w.act, w.mx_s2, w.mx_ld, nullptr, true, st);
+    ks = hr::launch_linear_mx(w.act, w.mx_s2, w.mx_ld, static_cast<const uint8_t*>(L->w_down), L->mx_down_s, T, D,
+                              F, HR_EPI_RESIDUAL, h, nullptr, 0, w.part, true, st);
+    hr::launch_residual_norm(h, w.part, ks > 1 ? ks : 0, T, D, next_w, eps, next_mode, w.x, next_inv, nullptr,
+                             nullptr, 0, st);
     return check_launch("prefill layer (MXFP4)");
   }
-  hr::launch_linear(w.attn, L->w_o, L->ws_o, L->as_o, fp8, T, D, A, HR_EPI_RESIDUAL, h, 0.f, st);
-  hr::launch_rmsnorm(h, T, D, L->post_norm_w, d->rms_eps, w.x, fp8, fp8 ? 1.0f / L->as_gu : 1.f, st);
+  int ks = hr::launch_linear(w.attn, L->w_o, L->ws_o, L->as_o, fp8, T, D, A, HR_EPI_RESIDUAL, h, 0.f, w.part, true,
+                             st);
+  hr::launch_residual_norm(h, w.part, ks > 1 ? ks : 0, T, D, L->post_norm_w, eps,
+                           fp8 ? hr::kNormE4M3 : hr::kNormF16, w.x, fp8 ? 1.0f / L->as_gu : 1.f, nullptr, nullptr, 0,
+                           st);
   hr::launch_linear(w.x, L->w_gu, L->ws_gu, L->as_gu, fp8, T, 2 * F, D, HR_EPI_SWIGLU, w.act,
-                    fp8 ? L->as_down : 0.f, st);
-  hr::launch_linear(w.act, L->w_down, L->ws_down, L->as_down, fp8, T, D, F, HR_EPI_RESIDUAL, h, 0.f, st);
+                    fp8 ? L->as_down : 0.f, nullptr, true, st);
+  ks = hr::launch_linear(w.act, L->w_down, L->ws_down, L->as_down, fp8, T, D, F, HR_EPI_RESIDUAL, h, 0.f, w.part,
+                         true, st);
+  hr::launch_residual_norm(h, w.part, ks > 1 ? ks : 0, T, D, next_w, eps, next_mode, w.x, next_inv, nullptr, nullptr,
+                           0, st);
   return check_launch("prefill layer");
 }
 
@@ -398,7 +456,7 @@ hr_status hr_prefill_layer(const hr_dims* dims, const hr_layer* layer, const hr_
   if (ws_bytes < need_ws) return fail(HR_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need_ws);
   Ws w;
   ws_layout(dims, batch->total_tokens, &w, static_cast<uint8_t*>(ws));
-  return run_layer(dims, layer, batch, h, kv, w, false, stream);
+  return run_layer(dims, layer, nullptr, batch, h, kv, w, false, stream);
 }
 
 }  // extern "C"
@@ -449,8 +507,11 @@ hr_status enqueue_stack(const hr_dims* dims, const hr_layer* layers, const hr_ba
   const bool fp8 = L0.wtype == HR_FP8_E4M3;
   hr::launch_embed_rmsnorm(ids, embed, x_embeds, T, D, L0.in_norm_w, dims->rms_eps, h_out, w.x, fp8,
                            fp8 ? 1.0f / L0.as_qkv : 1.f, stream);
+  // every layer's input norm after the first is fused into the previous
+  // layer's last residual add
   for (int l = 0; l < dims->n_layers; ++l)
-    HR_TRY(run_layer(dims, &layers[l], batch, h_out, &kv[l], w, l == 0, stream));
+    HR_TRY(run_layer(dims, &layers[l], l + 1 < dims->n_layers ? &layers[l + 1] : nullptr, batch, h_out, &kv[l], w,
+                     true, stream));
   if (head_w)
     HR_TRY(run_head(h_out, batch, D, final_norm_w, dims->rms_eps, head_w, n_codebooks, cb_vocab, logits_out,
                     w.head, stream));
@@ -609,7 +670,7 @@ hr_status hr_embed_rmsnorm(const int32_t* ids, const void* embed, int32_t vocab,
   HR_TRY(need(norm_w, "norm_w"));
   HR_TRY(need(h_out, "h_out"));
   HR_TRY(need(x_out, "x_out"));
-  if (x_type != HR_BF16 && x_type != HR_FP8_E4M3) return fail(HR_EINVAL, "x_type: bf16 or e4m3");
+  if (x_type != HR_F16 && x_type != HR_FP8_E4M3) return fail(HR_EINVAL, "x_type: HR_F16 or HR_FP8_E4M3");
   if (x_type == HR_FP8_E4M3 && !(x_scale > 0.f)) return fail(HR_EINVAL, "x_scale must be > 0");
   if (T == 0) return HR_OK;
   hr::launch_embed_rmsnorm(ids, embed, x_embeds, T, D, norm_w, eps, h_out, x_out, x_type == HR_FP8_E4M3,
@@ -623,7 +684,7 @@ hr_status hr_rmsnorm(const float* h, int32_t T, int32_t D, const void* norm_w, f
   HR_TRY(need(h, "h"));
   HR_TRY(need(norm_w, "norm_w"));
   HR_TRY(need(x_out, "x_out"));
-  if (x_type != HR_BF16 && x_type != HR_FP8_E4M3) return fail(HR_EINVAL, "x_type: bf16 or e4m3");
+  if (x_type != HR_F16 && x_type != HR_FP8_E4M3) return fail(HR_EINVAL, "x_type: HR_F16 or HR_FP8_E4M3");
   if (x_type == HR_FP8_E4M3 && !(x_scale > 0.f)) return fail(HR_EINVAL, "x_scale must be > 0");
   if (T == 0) return HR_OK;
   hr::launch_rmsnorm(h, T, D, norm_w, eps, x_out, x_type == HR_FP8_E4M3,
@@ -631,11 +692,27 @@ hr_status hr_rmsnorm(const float* h, int32_t T, int32_t D, const void* norm_w, f
   return check_launch("rmsnorm");
 }
 
+size_t hr_linear_workspace_bytes(hr_wtype wtype, int32_t M, int32_t N, int32_t K, hr_epilogue epi) {
+  if (epi != HR_EPI_RESIDUAL || M <= 0 || N <= 0 || K <= 0) return 0;
+  int ks = 1;
+  if (wtype == HR_MXFP4) {
+    if (K % 128) return 0;
+    ks = hr::launch_linear_mx(nullptr, nullptr, 0, nullptr, nullptr, M, N, K, HR_EPI_RESIDUAL, nullptr, nullptr, 0,
+                              nullptr, false, nullptr);
+  } else {
+    const bool fp8 = wtype == HR_FP8_E4M3;
+    if (K % (fp8 ? 128 : 64)) return 0;
+    ks = hr::launch_linear(nullptr, nullptr, nullptr, 1.f, fp8, M, N, K, HR_EPI_RESIDUAL, nullptr, 0.f, nullptr,
+                           false, nullptr);
+  }
+  return ks > 1 ? up256(size_t(ks) * size_t(M) * size_t(N) * 4) : 0;
+}
+
 hr_status hr_linear(const void* x, const void* w, const float* w_scale, float x_scale, hr_wtype wtype,
-                    int32_t M, int32_t N, int32_t K, hr_epilogue epi, void* out, float out_scale,
-                    hipStream_t stream) {
+                    int32_t M, int32_t N, int32_t K, hr_epilogue epi, void* out, float out_scale, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
   if (M < 0 || N <= 0 || K <= 0) return fail(HR_EINVAL, "bad M=%d N=%d K=%d", M, N, K);
-  if (epi != HR_EPI_BF16 && epi != HR_EPI_RESIDUAL && epi != HR_EPI_SWIGLU) return fail(HR_EINVAL, "bad epilogue");
+  if (epi != HR_EPI_F32 && epi != HR_EPI_RESIDUAL && epi != HR_EPI_SWIGLU) return fail(HR_EINVAL, "bad epilogue");
   if (wtype != HR_BF16 && wtype != HR_FP8_E4M3) return fail(HR_EINVAL, "bad wtype");
   const bool fp8 = wtype == HR_FP8_E4M3;
   if (K % (fp8 ? 128 : 64)) return fail(HR_EUNSUPPORTED, "K = %d must be a multiple of %d", K, fp8 ? 128 : 64);
@@ -651,22 +728,53 @@ hr_status hr_linear(const void* x, const void* w, const float* w_scale, float x_
     if (!(x_scale > 0.f)) return fail(HR_EINVAL, "FP8 needs x_scale > 0");
     if (epi == HR_EPI_SWIGLU && !(out_scale > 0.f)) return fail(HR_EINVAL, "FP8 SwiGLU needs out_scale > 0");
   }
+  const size_t need_ws = hr_linear_workspace_bytes(wtype, M, N, K, epi);
+  if (need_ws) {
+    if (!ws || ws_bytes < need_ws)
+      return fail(HR_EWORKSPACE, "linear workspace needs %zu bytes, got %zu", need_ws, ws ? ws_bytes : size_t(0));
+    HR_TRY(need(ws, "ws"));
+  }
   if (M == 0) return HR_OK;
-  hr::launch_linear(x, w, w_scale, x_scale, fp8, M, N, K, epi, out, out_scale, stream);
+  const int ks = hr::launch_linear(x, w, w_scale, x_scale, fp8, M, N, K, epi, out, out_scale,
+                                   static_cast<float*>(ws), true, stream);
+  if (epi == HR_EPI_RESIDUAL && ks > 1)
+    hr::launch_residual_sum(static_cast<float*>(out), static_cast<const float*>(ws), ks, size_t(M) * size_t(N),
+                            stream);
   return check_launch("linear");
 }
 
-hr_status hr_quantize_mxfp4(const void* x, int32_t x_is_fp32, int32_t M, int32_t K, const float* col_scale,
+hr_status hr_residual_rmsnorm(float* h, const float* partials, int32_t n_partials, int32_t T, int32_t D,
+                              const void* norm_w, float eps, void* x_out, hr_wtype x_type, float x_scale,
+                              hipStream_t stream) {
+  if (T < 0 || D <= 0 || D % 8 || D > 8192) return fail(HR_EINVAL, "bad T=%d / D=%d", T, D);
+  if (n_partials < 0) return fail(HR_EINVAL, "n_partials %d < 0", n_partials);
+  HR_TRY(need(h, "h"));
+  if (n_partials > 0) HR_TRY(need(partials, "partials"));
+  if (x_out) {
+    HR_TRY(need(x_out, "x_out"));
+    HR_TRY(need(norm_w, "norm_w"));
+    if (x_type != HR_F16 && x_type != HR_FP8_E4M3) return fail(HR_EINVAL, "x_type: HR_F16 or HR_FP8_E4M3");
+    if (x_type == HR_FP8_E4M3 && !(x_scale > 0.f)) return fail(HR_EINVAL, "x_scale must be > 0");
+  }
+  if (T == 0) return HR_OK;
+  const int mode = !x_out ? hr::kNormNone : (x_type == HR_FP8_E4M3 ? hr::kNormE4M3 : hr::kNormF16);
+  hr::launch_residual_norm(h, partials, n_partials, T, D, norm_w, eps, mode, x_out,
+                           x_type == HR_FP8_E4M3 ? 1.0f / x_scale : 1.f, nullptr, nullptr, 0, stream);
+  return check_launch("residual_rmsnorm");
+}
+
+hr_status hr_quantize_mxfp4(const void* x, int32_t x_format, int32_t M, int32_t K, const float* col_scale,
                             const float* row_scale, uint8_t* codes, uint8_t* scales, int32_t ld_scales,
                             hipStream_t stream) {
   if (M < 0 || K <= 0 || K % 128) return fail(HR_EINVAL, "bad M=%d / K=%d (a multiple of 128)", M, K);
   if (ld_scales < M || ld_scales % 4) return fail(HR_EINVAL, "ld_scales %d: >= M and a multiple of 4", ld_scales);
+  if (x_format < 0 || x_format > 2) return fail(HR_EINVAL, "x_format %d: 0 bf16, 1 fp32, 2 fp16", x_format);
   HR_TRY(need(x, "x"));
   HR_TRY(need(codes, "codes"));
   HR_TRY(need(scales, "scales"));
   if (col_scale && !aligned16(col_scale)) return fail(HR_EALIGN, "col_scale is not 16-byte aligned");
   if (M == 0) return HR_OK;
-  hr::launch_quant_mx(x, x_is_fp32 != 0, M, K, col_scale, row_scale, codes, scales, ld_scales, stream);
+  hr::launch_quant_mx(x, x_format, M, K, col_scale, row_scale, codes, scales, ld_scales, stream);
   return check_launch("quantize mxfp4");
 }
 
@@ -687,7 +795,8 @@ hr_status hr_rmsnorm_mxfp4(const float* h, int32_t T, int32_t D, const void* nor
 
 hr_status hr_linear_mxfp4(const uint8_t* x, const uint8_t* x_scales, int32_t ld_x_scales, const uint8_t* w,
                           const uint8_t* w_scales, int32_t M, int32_t N, int32_t K, hr_epilogue epi, void* out,
-                          uint8_t* out_scales, int32_t ld_out_scales, hipStream_t stream) {
+                          uint8_t* out_scales, int32_t ld_out_scales, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
   if (M < 0 || N <= 0 || K <= 0 || K % 128) return fail(HR_EINVAL, "bad M=%d N=%d K=%d (K a multiple of 128)", M, N, K);
   if (epi != HR_EPI_RESIDUAL && epi != HR_EPI_SWIGLU) return fail(HR_EINVAL, "MXFP4: residual or SwiGLU epilogue");
   if (epi == HR_EPI_RESIDUAL && N % 256) return fail(HR_EUNSUPPORTED, "N = %d must be a multiple of 256", N);
@@ -706,9 +815,18 @@ hr_status hr_linear_mxfp4(const uint8_t* x, const uint8_t* x_scales, int32_t ld_
     if (ld_out_scales < Mr || ld_out_scales % 4)
       return fail(HR_EINVAL, "ld_out_scales %d < %d", ld_out_scales, Mr);
   }
+  const size_t need_ws = hr_linear_workspace_bytes(HR_MXFP4, M, N, K, epi);
+  if (need_ws) {
+    if (!ws || ws_bytes < need_ws)
+      return fail(HR_EWORKSPACE, "linear workspace needs %zu bytes, got %zu", need_ws, ws ? ws_bytes : size_t(0));
+    HR_TRY(need(ws, "ws"));
+  }
   if (M == 0) return HR_OK;
-  hr::launch_linear_mx(x, x_scales, ld_x_scales, w, w_scales, M, N, K, epi, out, out_scales, ld_out_scales,
-                       stream);
+  const int ks = hr::launch_linear_mx(x, x_scales, ld_x_scales, w, w_scales, M, N, K, epi, out, out_scales,
+                                      ld_out_scales, static_cast<float*>(ws), true, stream);
+  if (epi == HR_EPI_RESIDUAL && ks > 1)
+    hr::launch_residual_sum(static_cast<float*>(out), static_cast<const float*>(ws), ks, size_t(M) * size_t(N),
+                            stream);
   return check_launch("linear mxfp4");
 }
 
@@ -736,7 +854,7 @@ hr_status hr_attention(const hr_dims* dims, const hr_batch* batch, const void* q
   HR_TRY(check_batch(dims, batch, kv));
   HR_TRY(need(q, "q"));
   HR_TRY(need(out, "out"));
-  if (out_type != HR_BF16 && out_type != HR_FP8_E4M3) return fail(HR_EINVAL, "out_type: bf16 or e4m3");
+  if (out_type != HR_F16 && out_type != HR_FP8_E4M3) return fail(HR_EINVAL, "out_type: HR_F16 or HR_FP8_E4M3");
   if (out_type == HR_FP8_E4M3 && !(out_scale > 0.f)) return fail(HR_EINVAL, "out_scale must be > 0");
   if (batch->total_tokens == 0) return HR_OK;
   const hr::AttnSplit plan = attn_plan(dims, batch, nullptr);
@@ -757,7 +875,7 @@ hr_status hr_qknorm_rope_attention(const hr_dims* dims, const hr_batch* batch, c
   HR_TRY(need(q_norm_w, "q_norm_w"));
   HR_TRY(need(k_norm_w, "k_norm_w"));
   HR_TRY(need(out, "out"));
-  if (out_type != HR_BF16 && out_type != HR_FP8_E4M3) return fail(HR_EINVAL, "out_type: bf16 or e4m3");
+  if (out_type != HR_F16 && out_type != HR_FP8_E4M3) return fail(HR_EINVAL, "out_type: HR_F16 or HR_FP8_E4M3");
   if (out_type == HR_FP8_E4M3 && !(out_scale > 0.f)) return fail(HR_EINVAL, "out_scale must be > 0");
   const int longest = small_prompt(batch);
   if (longest < 0)
@@ -785,7 +903,7 @@ hr_status hr_attention_chunked(const hr_dims* dims, const hr_batch* batch, const
   HR_TRY(check_batch(dims, batch, kv));
   HR_TRY(need(q, "q"));
   HR_TRY(need(out, "out"));
-  if (out_type != HR_BF16 && out_type != HR_FP8_E4M3) return fail(HR_EINVAL, "out_type: bf16 or e4m3");
+  if (out_type != HR_F16 && out_type != HR_FP8_E4M3) return fail(HR_EINVAL, "out_type: HR_F16 or HR_FP8_E4M3");
   if (out_type == HR_FP8_E4M3 && !(out_scale > 0.f)) return fail(HR_EINVAL, "out_scale must be > 0");
   if (chunk_tiles < 1 || n_slots < 1 || n_slots > 64)
     return fail(HR_EINVAL, "chunk_tiles must be >= 1 and n_slots in [1, 64] (got %d, %d)", chunk_tiles, n_slots);

@@ -10,7 +10,8 @@
 //
 // Workgroup = (query block, kv head g, sequence), 4 wavefronts sharing every
 // K/V tile: the GROUP query heads of g, times 4/GROUP blocks of 32 positions.
-// Per 64-key tile, with v_mfma_f32_32x32x16_bf16:
+// Per 64-key tile, with v_mfma_f32_32x32x16_f16 (q in fp16; the bf16 K and V
+// rows convert exactly to fp16 as they are staged in LDS):
 //   S^T = K . Q^T  (A = 32 keys x 16 d from LDS, B = the wave's 32 queries,
 //                   kept in registers) -> lane l holds query l%32 and keys
 //                   8(r/4) + 4(l/32) + r%4, r = 0..15, of each 32-key block;
@@ -22,7 +23,7 @@
 //                   so P goes from the score accumulator to the B operand with no
 //                   lane exchange; V is staged transposed in LDS.
 // The next tile's K and V are fetched into registers while the current tile is
-// computed.  Probabilities feed the MFMA in bf16; sums and rescaling stay fp32.
+// computed.  Probabilities feed the MFMA in fp16; sums and rescaling stay fp32.
 #include "common.h"
 #include "launch.h"
 #include "rope_math.h"
@@ -32,9 +33,9 @@ namespace hr {
 constexpr int AKT = 64;        // keys per tile
 constexpr int VT_LD = 72;      // padded key stride of the transposed V tile (elements)
 
-__device__ __forceinline__ floatx16 mfma32_bf16(u32x4 a, u32x4 b, floatx16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+__device__ __forceinline__ floatx16 mfma32_f16(u32x4 a, u32x4 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
 // Key chunks of a query block with n_tiles 64-key tiles: at least chunk_tiles
@@ -149,13 +150,13 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void attention_kernel(
     for (int j = 0; j < KPT; ++j) {
       const int c = tid + 256 * j;
       const int key = c / (DH / 8), d8 = c % (DH / 8);
-      *reinterpret_cast<u32x4*>(sK + key * K_LD + d8 * 8) = rk[j];
+      *reinterpret_cast<u32x4*>(sK + key * K_LD + d8 * 8) = bf8_to_f16x8(rk[j]);
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int u = tid + 256 * j;
       const int key = 2 * (u % (AKT / 2)), d8 = u / (AKT / 2);
-      const u32x4 a = rv[j][0], b = rv[j][1];
+      const u32x4 a = bf8_to_f16x8(rv[j][0]), b = bf8_to_f16x8(rv[j][1]);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         *reinterpret_cast<uint32_t*>(sVt + (d8 * 8 + 2 * w) * VT_LD + key) = (a[w] & 0xFFFFu) | (b[w] << 16);
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void attention_kernel(
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const u32x4 kf = *reinterpret_cast<const u32x4*>(sK + (blk * 32 + r32) * K_LD + ks * 16 + half * 8);
-        a = mfma32_bf16(kf, qf[ks], a);
+        a = mfma32_f16(kf, qf[ks], a);
       }
       sc[blk] = a;
     }
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void attention_kernel(
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[blk][r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32, kWave)) * scale_log2;   // scale > 0: max commutes
     // The reference max m_run moves only when a tile exceeds it by more than
-    // 8 (base 2): probabilities then stay <= 2^8, well inside bf16 and fp32
+    // 8 (base 2): probabilities then stay <= 2^8, well inside fp16 and fp32
     // range at unchanged relative precision, and most tiles skip rescaling
     // the accumulators (the result o / l does not depend on the reference).
     const bool grow = mt > m_run + 8.0f;
@@ -248,10 +249,10 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void attention_kernel(
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         u32x4 pb;
-        pb[0] = pack_bf2_hw(sc[blk][8 * kk + 0], sc[blk][8 * kk + 1]);
-        pb[1] = pack_bf2_hw(sc[blk][8 * kk + 2], sc[blk][8 * kk + 3]);
-        pb[2] = pack_bf2_hw(sc[blk][8 * kk + 4], sc[blk][8 * kk + 5]);
-        pb[3] = pack_bf2_hw(sc[blk][8 * kk + 6], sc[blk][8 * kk + 7]);
+        pb[0] = pack_f16x2(sc[blk][8 * kk + 0], sc[blk][8 * kk + 1]);
+        pb[1] = pack_f16x2(sc[blk][8 * kk + 2], sc[blk][8 * kk + 3]);
+        pb[2] = pack_f16x2(sc[blk][8 * kk + 4], sc[blk][8 * kk + 5]);
+        pb[3] = pack_f16x2(sc[blk][8 * kk + 6], sc[blk][8 * kk + 7]);
         const int kb = blk * 32 + kk * 16 + 4 * half;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void attention_kernel(
           const u32x2 x0 = *reinterpret_cast<const u32x2*>(vrow + kb);
           const u32x2 x1 = *reinterpret_cast<const u32x2*>(vrow + kb + 8);
           const u32x4 va = {x0[0], x0[1], x1[0], x1[1]};
-          o[db] = mfma32_bf16(va, pb, o[db]);
+          o[db] = mfma32_f16(va, pb, o[db]);
         }
       }
   }
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void attention_kernel(
                            (f2e4m3(y2 * out_inv) << 16) | (f2e4m3(y3 * out_inv) << 24);
         *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(out) + orow + d0) = w;
       } else {
-        const u32x2 w = {pack_bf2_hw(y0, y1), pack_bf2_hw(y2, y3)};
+        const u32x2 w = {pack_f16x2(y0, y1), pack_f16x2(y2, y3)};
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow + d0) = w;
       }
     }
@@ -378,7 +379,7 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(
         f2e4m3(y0 * out_inv) | (f2e4m3(y1 * out_inv) << 8) | (f2e4m3(y2 * out_inv) << 16) |
         (f2e4m3(y3 * out_inv) << 24);
   } else {
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow) = u32x2{pack_bf2(y0, y1), pack_bf2(y2, y3)};
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow) = u32x2{pack_f16x2(y0, y1), pack_f16x2(y2, y3)};
   }
 }
 
@@ -396,10 +397,10 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(
 // unnormalised output for attention_merge_kernel, with the chunk plan and the
 // partial layout of attention_kernel.  Keys past the chunk's end read the
 // chunk's last key (in bounds) and score -inf.
-// ROPE: q points at the merged QKV rows and step A3 happens here too: wave 0
-// norms and rotates the G query rows of the stream's new token (rope_pairs,
-// the arithmetic of qknorm_rope_kv_kernel, q rounded to bf16 as that kernel
-// stores it) into LDS, and the workgroup of the last chunk also the new k row
+// ROPE: q points at the fp32 merged QKV rows and step A3 happens here too:
+// wave 0 norms and rotates the G query rows of the stream's new token
+// (rope_pairs, the arithmetic of qknorm_rope_kv_kernel, q rounded to fp16 as
+// that kernel stores it) into LDS, and the workgroup of the last chunk also the new k row
 // and the v row, writes both to the cache row start_pos and uses them from
 // LDS for that key (its cache row is being written by the same launch).
 struct RopeArgs {
@@ -415,7 +416,7 @@ __device__ __forceinline__ float dpp_add(float v) {
 
 template <int DH, int G, bool ROPE>
 __global__ __launch_bounds__(256) void decode_attention_kernel(
-    const uint16_t* __restrict__ q, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
+    const void* __restrict__ q, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ start_pos, const int32_t* __restrict__ cache_slot,
     const int32_t* __restrict__ used_keys, int Hq, int Hkv, int cap, int causal, float scale_log2,
     void* __restrict__ out, int out_fp8, float out_inv, int chunk_tiles, int n_slots, float* __restrict__ part_o,
@@ -454,9 +455,9 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
       const int n_rows = G + (last ? 2 : 0);
       const int rr = row < n_rows ? row : 0;             // spare lanes repeat row 0 (group_sum needs them)
       const int head = rr < G ? g * G + rr : (rr == G ? Hq + g : Hq + Hkv + g);
-      const uint16_t* src = q + (size_t(t) * (Hq + 2 * Hkv) + head) * DH;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(src + 8 * c8);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(src + HALF + 8 * c8);
+      const float* src = static_cast<const float*>(q) + (size_t(t) * (Hq + 2 * Hkv) + head) * DH;
+      const F8 lo = load_f8(src + 8 * c8);
+      const F8 hi = load_f8(src + HALF + 8 * c8);
       const uint16_t* nw = rr < G ? qw : kw;
       const u32x4 w0 = *reinterpret_cast<const u32x4*>(nw + 8 * c8);
       const u32x4 w1 = *reinterpret_cast<const u32x4*>(nw + HALF + 8 * c8);
@@ -465,8 +466,10 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
         const size_t cdst = ((crow + p_new) * Hkv + g) * DH;
         if (rr <= G) {
           const float inv = 1.0f / __builtin_sqrtf(ss / float(DH) + eps);
-          u32x4 o0, o1;
-          rope_pairs(lo, hi, w0, w1, inv, &s_cs[8 * c8], &s_sn[8 * c8], o0, o1);
+          F8 r0, r1;
+          rope_pairs(lo, hi, w0, w1, inv, &s_cs[8 * c8], &s_sn[8 * c8], r0, r1);
+          const u32x4 o0 = rr < G ? pack8_f16(r0) : pack8_bf16(r0);
+          const u32x4 o1 = rr < G ? pack8_f16(r1) : pack8_bf16(r1);
           uint16_t* dst = rr < G ? &s_qr[rr < G ? rr : 0][0] : &s_kn[0];
           *reinterpret_cast<u32x4*>(dst + 8 * c8) = o0;
           *reinterpret_cast<u32x4*>(dst + HALF + 8 * c8) = o1;
@@ -475,10 +478,11 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
             *reinterpret_cast<u32x4*>(kc + cdst + HALF + 8 * c8) = o1;
           }
         } else {
-          *reinterpret_cast<u32x4*>(&s_vn[8 * c8]) = lo;
-          *reinterpret_cast<u32x4*>(&s_vn[HALF + 8 * c8]) = hi;
-          *reinterpret_cast<u32x4*>(vc + cdst + 8 * c8) = lo;
-          *reinterpret_cast<u32x4*>(vc + cdst + HALF + 8 * c8) = hi;
+          const u32x4 v0 = pack8_bf16(lo), v1 = pack8_bf16(hi);
+          *reinterpret_cast<u32x4*>(&s_vn[8 * c8]) = v0;
+          *reinterpret_cast<u32x4*>(&s_vn[HALF + 8 * c8]) = v1;
+          *reinterpret_cast<u32x4*>(vc + cdst + 8 * c8) = v0;
+          *reinterpret_cast<u32x4*>(vc + cdst + HALF + 8 * c8) = v1;
         }
       }
     }
@@ -489,9 +493,10 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     const u32x4 v = ROPE ? *reinterpret_cast<const u32x4*>(&s_qr[ROPE ? hh : 0][8 * d8])
-                         : *reinterpret_cast<const u32x4*>(q + (size_t(t) * Hq + g * G + hh) * DH + 8 * d8);
+                         : *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(q) +
+                                                           (size_t(t) * Hq + g * G + hh) * DH + 8 * d8);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qf[hh][e] = (e & 1) ? bf_hi(v[e >> 1]) : bf_lo(v[e >> 1]);
+    for (int e = 0; e < 8; ++e) qf[hh][e] = h_at(v, e);
   }
   float m[G], l[G], o[G][8];
 #pragma unroll
@@ -579,7 +584,7 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
       const float y = O / L;
       const size_t orow = (size_t(t) * Hq + hq) * DH + d;
       if (out_fp8) static_cast<uint8_t*>(out)[orow] = uint8_t(f2e4m3(y * out_inv));
-      else static_cast<uint16_t*>(out)[orow] = uint16_t(f2bf(y));
+      else static_cast<uint16_t*>(out)[orow] = uint16_t(f2h(y));
     } else {
       const size_t prow = (size_t(c) * T + t) * Hq + hq;
       part_o[prow * DH + d] = O;
@@ -601,13 +606,13 @@ static void launch_decode_t(const void* q, const void* kc, const void* vc, const
   uint16_t* vcw = static_cast<uint16_t*>(const_cast<void*>(vc));
   if (rope)
     decode_attention_kernel<DH, GROUP, true><<<grid, 256, 0, st>>>(
-        static_cast<const uint16_t*>(q), kcw, vcw, cu, sp, slot, used, Hq, Hkv, cap, causal ? 1 : 0, scale_log2,
+        q, kcw, vcw, cu, sp, slot, used, Hq, Hkv, cap, causal ? 1 : 0, scale_log2,
         out, fp8 ? 1 : 0, out_inv, cfg.chunk_tiles, slots, cfg.part_o, reinterpret_cast<float2_t*>(cfg.part_ml),
         cfg.T, static_cast<const uint16_t*>(rope->qw), static_cast<const uint16_t*>(rope->kw),
         rope_freq(DH, rope->theta), rope->eps);
   else
     decode_attention_kernel<DH, GROUP, false><<<grid, 256, 0, st>>>(
-        static_cast<const uint16_t*>(q), kcw, vcw, cu, sp, slot, used, Hq, Hkv, cap, causal ? 1 : 0, scale_log2,
+        q, kcw, vcw, cu, sp, slot, used, Hq, Hkv, cap, causal ? 1 : 0, scale_log2,
         out, fp8 ? 1 : 0, out_inv, cfg.chunk_tiles, slots, cfg.part_o, reinterpret_cast<float2_t*>(cfg.part_ml),
         cfg.T, nullptr, nullptr, RopeFreq{}, 0.f);
   if (cfg.chunk_tiles > 0)

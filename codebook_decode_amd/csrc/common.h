@@ -37,6 +37,34 @@ __device__ __forceinline__ uint32_t pack_bf2_hw(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
+// ---------------------------------------------------------------- IEEE binary16
+// Activations of the bf16-weight band are fp16 (11-bit significand): 8x less
+// rounding error than bf16 at the same MFMA rate.  bf16 weights enter the fp16
+// MFMAs converted in registers; that conversion is exact for every bf16 value
+// of magnitude in [2^-17, 2^16) (fp16 keeps all 8 significand bits there, down
+// to its subnormals); smaller ones round to the nearest multiple of 2^-24, and
+// 2^16 or more would overflow (outside the weights this band accepts).
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float h_lo(uint32_t w) { return float(__builtin_bit_cast(f16x2_t, w)[0]); }
+__device__ __forceinline__ float h_hi(uint32_t w) { return float(__builtin_bit_cast(f16x2_t, w)[1]); }
+// two fp32 -> packed fp16, nearest even (v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  f2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+}
+__device__ __forceinline__ uint32_t f2h(float f) {        // one fp32 -> fp16 bits, nearest even
+  return uint32_t(__builtin_bit_cast(uint16_t, _Float16(f)));
+}
+// 8 bf16 -> 8 fp16 (3 VALU per pair: two widenings by bit shift, one packed convert)
+__device__ __forceinline__ uint32_t bf2_to_f16x2(uint32_t w) {
+  return pack_f16x2(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
+}
+__device__ __forceinline__ u32x4 bf8_to_f16x8(u32x4 v) {
+  return u32x4{bf2_to_f16x2(v[0]), bf2_to_f16x2(v[1]), bf2_to_f16x2(v[2]), bf2_to_f16x2(v[3])};
+}
+
 // ---------------------------------------------------------------- OCP E4M3
 // fp32 -> e4m3fn code: nearest even, magnitudes beyond 448 saturate to 448.
 // Normal E4M3 values are (1 + m/8) 2^(e-7), e in 1..15; subnormals m 2^-9.

@@ -44,19 +44,24 @@ __device__ __forceinline__ floatx4 mfma_fp8(uint32_t a0, uint32_t a1, uint32_t b
   long b = (long)(((unsigned long)b1 << 32) | b0);
   return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
 }
-// 16 bytes of A times 16 bytes of B along k: one bf16 MFMA or two fp8 MFMAs.
-template <bool FP8>
+// 16 bytes of A times 16 bytes of B along k: one fp16 MFMA (B already in
+// fp16), one bf16 MFMA, or two fp8 MFMAs.
+template <bool FP8, bool F16>
 __device__ __forceinline__ floatx4 mma16(u32x4 a, u32x4 b, floatx4 c) {
   if constexpr (FP8) {
     c = mfma_fp8(a[0], a[1], b[0], b[1], c);
     return mfma_fp8(a[2], a[3], b[2], b[3], c);
+  } else if constexpr (F16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                  0, 0, 0);
   } else {
     return mfma_bf16(a, b, c);
   }
 }
 
 // 32 x 32 output block over one K slab: NC 16-byte chunks of its row of A and
-// of B per lane.  bf16: chunk c feeds one v_mfma_f32_32x32x16_bf16; e4m3:
+// of B per lane.  fp16 (A fp16, B converted from bf16 before the call): chunk c
+// feeds one v_mfma_f32_32x32x16_f16; e4m3:
 // chunks (2m, 2m+1) feed one v_mfma_scale_f32_32x32x64_f8f6f4 (format 0 = e4m3
 // on both sides, unit scale) on those 32 contiguous bytes.  The 32x32 forms
 // issue at twice the rate of the 16x16 ones on gfx950 (measured 2.16 vs 1.24
@@ -79,8 +84,8 @@ __device__ __forceinline__ floatx16 mma32(const u32x4 (&a)[NC], const u32x4 (&b)
   } else {
 #pragma unroll
     for (int m = 0; m < NC; ++m)
-      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[m]), __builtin_bit_cast(bf16x8, b[m]),
-                                                  c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[m]), __builtin_bit_cast(f16x8, b[m]),
+                                                 c, 0, 0, 0);
     return c;
   }
 }
@@ -128,7 +133,7 @@ __device__ __forceinline__ float half_wave_max(float v) {
 
 struct EpiArgs {
   int epi;            // hr_epilogue
-  void* out;          // bf16 [M,N] | fp32 [M,N] (+=) | act [M,F] | fp32 logits
+  void* out;          // fp32 [M,N] | fp32 [M,N] (+=) | act [M,F] | fp32 logits
   int ldo;            // leading dimension of out (elements)
   float x_scale;      // FP8: activation scale
   const float* w_scale;  // FP8: per-output-channel weight scale (N)
@@ -136,6 +141,13 @@ struct EpiArgs {
   int out_fp8;        // SwiGLU output in e4m3
   int F;              // SwiGLU width (gate rows [0,F), up rows [F,2F))
   int hilo_rows;      // head: rows [0,h) hold hi, [h,2h) lo terms; out = hi + lo
+  // RESIDUAL with split-K (ksplit > 1): split kz writes its fp32 partial to
+  // part + kz * part_stride (row-major, ld = ldo) with plain stores; the caller
+  // sums the splits in a fixed order (residual_norm_kernel).  ksplit == 1 adds
+  // into out in place (one writer per element).  No atomics: the result does
+  // not depend on the order in which workgroups finish.
+  float* part;
+  size_t part_stride;
   // MXFP4 operands: block scales in the slab-interleaved layout [K/128][ld][4]
   const uint8_t* mx_sa;  // A scales, ld = mx_lda (M rounded up to the 256-row tile)
   const uint8_t* mx_sb;  // B scales, ld = N
@@ -160,6 +172,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
     EpiArgs e) {
   constexpr int NB = (EPI == HR_EPI_SWIGLU) ? 2 : CB;  // weight row blocks per workgroup
   static_assert(EPI != HR_EPI_HEAD || CB == 1, "head epilogue: one column block");
+  // fp16 activations times bf16 weights converted to fp16; the head's split
+  // bf16 rows (hi + lo) meet the bf16 weights directly
+  constexpr bool kF16 = !FP8 && EPI != HR_EPI_HEAD;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cb = blockIdx.x;
   const int g = lane >> 4, rc = lane & 15;
@@ -215,12 +230,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb) {
+        const u32x4 b0 = kF16 ? bf8_to_f16x8(bw[u][nb][0]) : bw[u][nb][0];
+        const u32x4 b1 = kF16 ? bf8_to_f16x8(bw[u][nb][1]) : bw[u][nb][1];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          acc[nb][mb] = mma16<FP8>(ax[u][mb][0], bw[u][nb][0], acc[nb][mb]);
-          acc[nb][mb] = mma16<FP8>(ax[u][mb][1], bw[u][nb][1], acc[nb][mb]);
+          acc[nb][mb] = mma16<FP8, kF16>(ax[u][mb][0], b0, acc[nb][mb]);
+          acc[nb][mb] = mma16<FP8, kF16>(ax[u][mb][1], b1, acc[nb][mb]);
         }
+      }
   }
 
   // fixed-order reduction of the wavefront partials
@@ -249,22 +267,20 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
         if (e.out_fp8)
           static_cast<uint8_t*>(e.out)[size_t(row) * e.ldo + col] = uint8_t(f2e4m3(a * e.out_inv));
         else
-          static_cast<uint16_t*>(e.out)[size_t(row) * e.ldo + col] = uint16_t(f2bf(a));
+          static_cast<uint16_t*>(e.out)[size_t(row) * e.ldo + col] = uint16_t(f2h(a));
       }
     } else {
 #pragma unroll
      for (int nb = 0; nb < NB; ++nb) {
       const int col = (cb * NB + nb) * 16 + (ln & 15);
       if (col >= N) continue;
-      if constexpr (EPI == HR_EPI_BF16) {
-        if (row < M)
-          static_cast<uint16_t*>(e.out)[size_t(row) * e.ldo + col] =
-              uint16_t(f2bf(scaled<FP8>(e, v[nb], col)));
+      if constexpr (EPI == HR_EPI_F32) {
+        if (row < M) static_cast<float*>(e.out)[size_t(row) * e.ldo + col] = scaled<FP8>(e, v[nb], col);
       } else if constexpr (EPI == HR_EPI_RESIDUAL) {
         if (row < M) {
           float* o = static_cast<float*>(e.out) + size_t(row) * e.ldo + col;
           if (ksplit == 1) *o += scaled<FP8>(e, v[nb], col);
-          else unsafeAtomicAdd(o, scaled<FP8>(e, v[nb], col));
+          else e.part[size_t(kz) * e.part_stride + size_t(row) * e.ldo + col] = scaled<FP8>(e, v[nb], col);
         }
       } else {  // HR_EPI_HEAD: fp32 logits = hi-row product + lo-row product
         if (row < e.hilo_rows) {
@@ -553,6 +569,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
     // this slab's fragments were read one MFMA burst ago: settle them here so
     // no wait lands between the next slab's reads and these MFMAs
     wait_lds();
+    // fp16 mode: the bf16 weight fragments to fp16 once per slab (each serves
+    // IM MFMAs), while this wave's next copies may still be landing
+    if constexpr (!FP8 && !MX) {
+#pragma unroll
+      for (int j = 0; j < JN; ++j)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) fb[j][c] = bf8_to_f16x8(fb[j][c]);
+    }
     wait_slabs(min(STAGES - 3, n_slabs - 2 - it));
     lds_barrier();
     if (it + STAGES - 1 < n_slabs) issue(sl0 + it + STAGES - 1, (it + STAGES - 1) % STAGES);
@@ -621,7 +645,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
             if (e.out_fp8)
               static_cast<uint8_t*>(e.out)[size_t(row) * e.ldo + col] = uint8_t(f2e4m3(a * e.out_inv));
             else
-              static_cast<uint16_t*>(e.out)[size_t(row) * e.ldo + col] = uint16_t(f2bf(a));
+              static_cast<uint16_t*>(e.out)[size_t(row) * e.ldo + col] = uint16_t(f2h(a));
           }
         }
       } else {
@@ -630,11 +654,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
           const int col = n0 + wn * (BN / WN) + j * 32 + r32;
           if (col >= N) continue;
           const float v = scaled<FP8>(e, acc[i][j][r], col);
-          if constexpr (EPI == HR_EPI_BF16) {
-            static_cast<uint16_t*>(e.out)[size_t(row) * e.ldo + col] = uint16_t(f2bf(v));
+          if constexpr (EPI == HR_EPI_F32) {
+            static_cast<float*>(e.out)[size_t(row) * e.ldo + col] = v;
           } else {
-            float* o = static_cast<float*>(e.out) + size_t(row) * e.ldo + col;
-            if (ksplit == 1) *o += v; else unsafeAtomicAdd(o, v);
+            if (ksplit == 1) static_cast<float*>(e.out)[size_t(row) * e.ldo + col] += v;
+            else e.part[size_t(kz) * e.part_stride + size_t(row) * e.ldo + col] = v;
           }
         }
       }
@@ -648,7 +672,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
 constexpr int kSkinnyCB = 2;
 
 template <int EPI>
-constexpr int skinny_cb(int mb) { return (mb == 1 && (EPI == HR_EPI_BF16 || EPI == HR_EPI_RESIDUAL)) ? kSkinnyCB : 1; }
+constexpr int skinny_cb(int mb) { return (mb == 1 && (EPI == HR_EPI_F32 || EPI == HR_EPI_RESIDUAL)) ? kSkinnyCB : 1; }
 
 template <int EPI, bool FP8>
 static void skinny(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
@@ -658,7 +682,7 @@ static void skinny(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, con
   // 128-byte steps per wave (8 waves, the largest split)
   const int steps = Kb / 128;
   const int spw = ((steps + ksplit - 1) / ksplit + 7) / 8;
-  constexpr int CB1 = (EPI == HR_EPI_BF16 || EPI == HR_EPI_RESIDUAL) ? kSkinnyCB : 1;
+  constexpr int CB1 = (EPI == HR_EPI_F32 || EPI == HR_EPI_RESIDUAL) ? kSkinnyCB : 1;
   constexpr int NB1 = (EPI == HR_EPI_SWIGLU) ? 2 : CB1;
   if (mb == 1) {
     // all of a wave's steps in one batch when they fit (5 steps x NB = 1 block
@@ -696,11 +720,12 @@ static void tiled_cfg(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, 
   kern<<<grid, C::kThreads, kLds, st>>>(x, w, M, N, Kb, tiles_m, n_tiles, e);
 }
 
-// Launch with a split-K factor that fills the 256 CUs for the residual
-// projections (fp32 atomics into h), or the given one.
+// Split-K factor that fills the 256 CUs for the residual projections (the
+// splits' partials are summed by the caller), or the given one; launched only
+// when `go` (otherwise this only plans the factor).
 template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int SB = 64, bool MX = false>
-static void tiled_fill(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
-                       hipStream_t st, int ks_force = 0) {
+static int tiled_fill(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
+                      hipStream_t st, bool go, int ks_force = 0) {
   const int ncols = (EPI == HR_EPI_SWIGLU) ? 2 * e.F : N;
   const int tiles = ((M + BM - 1) / BM) * ((ncols + BN - 1) / BN);
   int ks = 1;
@@ -708,7 +733,8 @@ static void tiled_fill(const uint8_t* x, const uint8_t* w, int M, int N, int Kb,
   if (EPI == HR_EPI_RESIDUAL && ks_force > 0) ks = ks_force;
   const int max_ks = Kb / SB / 4 > 0 ? Kb / SB / 4 : 1;   // >= 4 slabs per split
   if (ks > max_ks) ks = max_ks;
-  tiled_cfg<EPI, FP8, BM, BN, WM, WN, STAGES, SB, MX>(x, w, M, N, Kb, e, ks, st);
+  if (go) tiled_cfg<EPI, FP8, BM, BN, WM, WN, STAGES, SB, MX>(x, w, M, N, Kb, e, ks, st);
+  return ks;
 }
 
 // Tile configuration of the large-M GEMM, per projection and M range, from
@@ -731,41 +757,42 @@ static void tiled_fill(const uint8_t* x, const uint8_t* w, int M, int N, int Kb,
 // against 38.0 us), down 128x64 and O 64x64 with 128-byte slabs (32.5 / 14.1
 // against 34.7 / 17.0).
 template <int EPI, bool FP8>
-static void tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
-                  hipStream_t st) {
+static int tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
+                 hipStream_t st, bool go) {
   const int K_el = FP8 ? Kb : Kb / 2;
   if constexpr (EPI == HR_EPI_SWIGLU) {
-    if (M <= 64) return tiled_fill<EPI, FP8, 64, 128, 2, 2, 6, 128>(x, w, M, N, Kb, e, st);
+    if (M <= 64) return tiled_fill<EPI, FP8, 64, 128, 2, 2, 6, 128>(x, w, M, N, Kb, e, st, go);
     if (M > 384) {
-      if constexpr (FP8) return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st);
-      else return tiled_fill<EPI, FP8, 256, 256, 4, 2, 4>(x, w, M, N, Kb, e, st);
+      if constexpr (FP8) return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st, go);
+      else return tiled_fill<EPI, FP8, 256, 256, 4, 2, 4>(x, w, M, N, Kb, e, st, go);
     }
-    if (M > 128) return tiled_fill<EPI, FP8, 256, 128, 4, 2, 4>(x, w, M, N, Kb, e, st);
-    return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st);
-  } else if constexpr (EPI == HR_EPI_BF16) {
-    if (M > 1024) return tiled_fill<EPI, FP8, 256, 256, 4, 2, 4>(x, w, M, N, Kb, e, st);
-    if (M > 384) return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st);
-    if (M > 128) return tiled_fill<EPI, FP8, 128, 64, 2, 2, 6, 128>(x, w, M, N, Kb, e, st);
-    if (M <= 64) return tiled_fill<EPI, FP8, 64, 32, 2, 1, 8, 128>(x, w, M, N, Kb, e, st);
-    return tiled_fill<EPI, FP8, 64, 64, 2, 2, 8, 128>(x, w, M, N, Kb, e, st);
+    if (M > 128) return tiled_fill<EPI, FP8, 256, 128, 4, 2, 4>(x, w, M, N, Kb, e, st, go);
+    return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st, go);
+  } else if constexpr (EPI == HR_EPI_F32) {
+    if (M > 1024) return tiled_fill<EPI, FP8, 256, 256, 4, 2, 4>(x, w, M, N, Kb, e, st, go);
+    if (M > 384) return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st, go);
+    if (M > 128) return tiled_fill<EPI, FP8, 128, 64, 2, 2, 6, 128>(x, w, M, N, Kb, e, st, go);
+    if (M <= 64) return tiled_fill<EPI, FP8, 64, 32, 2, 1, 8, 128>(x, w, M, N, Kb, e, st, go);
+    return tiled_fill<EPI, FP8, 64, 64, 2, 2, 8, 128>(x, w, M, N, Kb, e, st, go);
   } else {
     if constexpr (FP8) {
-      if (M > 128) return tiled_fill<EPI, FP8, 64, 64, 2, 2, 4, 128>(x, w, M, N, Kb, e, st);
+      if (M > 128) return tiled_fill<EPI, FP8, 64, 64, 2, 2, 4, 128>(x, w, M, N, Kb, e, st, go);
     }
-    if (M > 1024) return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st);
+    if (M > 1024) return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st, go);
     if (M > 384) {
-      if (K_el >= 8192) return tiled_fill<EPI, FP8, 256, 128, 4, 2, 4>(x, w, M, N, Kb, e, st, 6);
-      return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st, 3);
+      if (K_el >= 8192) return tiled_fill<EPI, FP8, 256, 128, 4, 2, 4>(x, w, M, N, Kb, e, st, go, 6);
+      return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st, go, 3);
     }
-    if (M > 128) return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4>(x, w, M, N, Kb, e, st);
-    if (M <= 64 && K_el >= 8192) return tiled_fill<EPI, FP8, 64, 64, 2, 2, 8, 128>(x, w, M, N, Kb, e, st);
-    if (K_el >= 8192) return tiled_fill<EPI, FP8, 128, 64, 4, 1, 4, 128>(x, w, M, N, Kb, e, st);
-    return tiled_fill<EPI, FP8, 64, 64, 2, 2, 4, 128>(x, w, M, N, Kb, e, st);
+    if (M > 128) return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4>(x, w, M, N, Kb, e, st, go);
+    if (M <= 64 && K_el >= 8192) return tiled_fill<EPI, FP8, 64, 64, 2, 2, 8, 128>(x, w, M, N, Kb, e, st, go);
+    if (K_el >= 8192) return tiled_fill<EPI, FP8, 128, 64, 4, 1, 4, 128>(x, w, M, N, Kb, e, st, go);
+    return tiled_fill<EPI, FP8, 64, 64, 2, 2, 4, 128>(x, w, M, N, Kb, e, st, go);
   }
 }
 
-void launch_linear(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8,
-                   int M, int N, int K, int epi, void* out, float out_scale, hipStream_t st) {
+int launch_linear(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8,
+                  int M, int N, int K, int epi, void* out, float out_scale, float* part, bool go,
+                  hipStream_t st) {
   EpiArgs e{};
   e.epi = epi;
   e.out = out;
@@ -775,10 +802,13 @@ void launch_linear(const void* x, const void* w, const float* w_scale, float x_s
   e.out_inv = out_scale > 0.f ? 1.0f / out_scale : 1.0f;
   e.F = N / 2;
   e.ldo = (epi == HR_EPI_SWIGLU) ? N / 2 : N;
+  e.part = part;
+  e.part_stride = size_t(M) * size_t(N);
   const int Kb = fp8 ? K : 2 * K;
   const uint8_t* xb = static_cast<const uint8_t*>(x);
   const uint8_t* wb = static_cast<const uint8_t*>(w);
   const int ncols = (epi == HR_EPI_SWIGLU) ? N / 2 : N;
+  int ks = 1;
   // small batches: the residual projections split K over about 384 workgroups
   // (1.5 per CU; measured at T = 13 against 256, 512 and 768: O 8.2 us against
   // 8.7 / 8.8 / 8.7, down 14.6 against 16.7 / 15.0 / 14.9)
@@ -786,27 +816,27 @@ void launch_linear(const void* x, const void* w, const float* w_scale, float x_s
   if (M <= 16) {                                                                              \
     const int cbw = 16 * skinny_cb<EPI_>((M + 15) / 16);                                      \
     const int blocks = (ncols + cbw - 1) / cbw;                                               \
-    int ks = 1;                                                                               \
     if (EPI_ == HR_EPI_RESIDUAL && blocks < 256) ks = (384 + blocks - 1) / blocks;            \
     if (ks > Kb / 128) ks = Kb / 128;                                                         \
-    if (fp8) skinny<EPI_, true>(xb, wb, M, N, Kb, e, blocks, ks, st);                         \
-    else skinny<EPI_, false>(xb, wb, M, N, Kb, e, blocks, ks, st);                            \
+    if (go && fp8) skinny<EPI_, true>(xb, wb, M, N, Kb, e, blocks, ks, st);                   \
+    else if (go) skinny<EPI_, false>(xb, wb, M, N, Kb, e, blocks, ks, st);                    \
   } else {                                                                                    \
-    if (fp8) tiled<EPI_, true>(xb, wb, M, N, Kb, e, st);                                      \
-    else tiled<EPI_, false>(xb, wb, M, N, Kb, e, st);                                         \
+    ks = fp8 ? tiled<EPI_, true>(xb, wb, M, N, Kb, e, st, go)                                 \
+             : tiled<EPI_, false>(xb, wb, M, N, Kb, e, st, go);                               \
   }
-  if (epi == HR_EPI_BF16) { HR_DISPATCH(HR_EPI_BF16) }
+  if (epi == HR_EPI_F32) { HR_DISPATCH(HR_EPI_F32) }
   else if (epi == HR_EPI_RESIDUAL) { HR_DISPATCH(HR_EPI_RESIDUAL) }
   else { HR_DISPATCH(HR_EPI_SWIGLU) }
 #undef HR_DISPATCH
+  return ks;
 }
 
 // MXFP4 x MXFP4: x codes [M, K/2] with scales (ld lda), w codes [N, K/2] with
 // scales (ld N); RESIDUAL adds into fp32 out [M, N]; SWIGLU (N = 2F) writes the
 // MXFP4 product: codes [M, F/2] into out, scales (ld ldo) into out_scales.
-void launch_linear_mx(const uint8_t* x, const uint8_t* x_scales, int lda, const uint8_t* w,
-                      const uint8_t* w_scales, int M, int N, int K, int epi, void* out, uint8_t* out_scales,
-                      int ldo, hipStream_t st) {
+int launch_linear_mx(const uint8_t* x, const uint8_t* x_scales, int lda, const uint8_t* w,
+                     const uint8_t* w_scales, int M, int N, int K, int epi, void* out, uint8_t* out_scales,
+                     int ldo, float* part, bool go, hipStream_t st) {
   EpiArgs e{};
   e.epi = epi;
   e.out = out;
@@ -817,13 +847,16 @@ void launch_linear_mx(const uint8_t* x, const uint8_t* x_scales, int lda, const 
   e.mx_lda = lda;
   e.mx_out_s = out_scales;
   e.mx_ldo = ldo;
+  e.part = part;
+  e.part_stride = size_t(M) * size_t(N);
   const int Kb = K / 2;
   // tiles from a sweep of the MXFP4 layer at P = 512: gate/up 128 x 128 on 8
   // waves (the layer 166 -> 156 us against 256 x 256), O and down 64 x 128
   // (-> 153 us against 128 x 64; 128 x 128 and 64 x 64 slower)
-  if (epi == HR_EPI_SWIGLU) tiled_fill<HR_EPI_SWIGLU, false, 128, 128, 4, 2, 4, 64, true>(x, w, M, N, Kb, e, st);
-  else if (M > 1024) tiled_fill<HR_EPI_RESIDUAL, false, 256, 256, 4, 2, 4, 64, true>(x, w, M, N, Kb, e, st);
-  else tiled_fill<HR_EPI_RESIDUAL, false, 64, 128, 2, 2, 4, 64, true>(x, w, M, N, Kb, e, st);
+  if (epi == HR_EPI_SWIGLU)
+    return tiled_fill<HR_EPI_SWIGLU, false, 128, 128, 4, 2, 4, 64, true>(x, w, M, N, Kb, e, st, go);
+  if (M > 1024) return tiled_fill<HR_EPI_RESIDUAL, false, 256, 256, 4, 2, 4, 64, true>(x, w, M, N, Kb, e, st, go);
+  return tiled_fill<HR_EPI_RESIDUAL, false, 64, 128, 2, 2, 4, 64, true>(x, w, M, N, Kb, e, st, go);
 }
 
 // Head: zsplit bf16 [2n, D] (hi rows then lo rows), W bf16 [N, D] -> fp32 [n, N]

@@ -43,7 +43,8 @@ void launch_final_split(const float* h, const int32_t* cu, int seq0, int n, int 
 void launch_quant_weight(const void* w, int N, int K, uint8_t* w8, float* scale, hipStream_t st);
 // MXFP4: codes [M, K/2] (two per byte, element 2i low), scales in the
 // slab-interleaved layout [K/128][ld_s][4] (ld_s >= M)
-void launch_quant_mx(const void* x, bool f32, int M, int K, const float* col, const float* row_scale,
+// fmt: 0 bf16, 1 fp32, 2 fp16 rows
+void launch_quant_mx(const void* x, int fmt, int M, int K, const float* col, const float* row_scale,
                      uint8_t* codes, uint8_t* scales, int ld_s, hipStream_t st);
 void launch_rmsnorm_mx(const float* h, int T, int D, const void* w, const float* col, float eps,
                        uint8_t* codes, uint8_t* scales, int ld_s, hipStream_t st);
@@ -87,11 +88,27 @@ void launch_decode_rope_attention(const void* qkv, const void* qw, const void* k
                                   int n_seq, int Hq, int Hkv, int d, int cap, void* out, bool fp8, float out_inv,
                                   const AttnSplit& cfg, hipStream_t st);
 
-void launch_linear(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8,
-                   int M, int N, int K, int epi, void* out, float out_scale, hipStream_t st);
-void launch_linear_mx(const uint8_t* x, const uint8_t* x_scales, int lda, const uint8_t* w,
-                      const uint8_t* w_scales, int M, int N, int K, int epi, void* out, uint8_t* out_scales,
-                      int ldo, hipStream_t st);
+// Projections.  Return the split-K factor ks of the launch (1 unless the
+// epilogue is HR_EPI_RESIDUAL).  RESIDUAL with ks > 1 writes ks fp32 partials
+// [ks][M][N] to `part` instead of touching `out`; the caller reduces them
+// (launch_residual_norm).  go == false: plan only (return ks, launch nothing).
+int launch_linear(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8,
+                  int M, int N, int K, int epi, void* out, float out_scale, float* part, bool go,
+                  hipStream_t st);
+int launch_linear_mx(const uint8_t* x, const uint8_t* x_scales, int lda, const uint8_t* w,
+                     const uint8_t* w_scales, int M, int N, int K, int epi, void* out, uint8_t* out_scales,
+                     int ldo, float* part, bool go, hipStream_t st);
+
+// h[t] += sum over kz = 0..ks-1 of part[kz][t] (in that order; ks = 0: no
+// add), then, when out_mode != kNormNone, x = RMS(h[t]) * w (* col for MX)
+// in the out_mode format.  One workgroup per row.
+enum NormOut { kNormNone = 0, kNormF16 = 1, kNormE4M3 = 2, kNormMX = 3 };
+// the residual add alone over a flat array of n elements (n % 8 == 0), in the
+// order and arithmetic of launch_residual_norm
+void launch_residual_sum(float* h, const float* part, int ks, size_t n, hipStream_t st);
+void launch_residual_norm(float* h, const float* part, int ks, int T, int D, const void* w, float eps,
+                          int out_mode, void* x_out, float inv_scale, const float* col, uint8_t* mx_scales,
+                          int mx_ld, hipStream_t st);
 void launch_head_gemm(const void* zsplit, int n, const void* w, int N, int D, float* out,
                       hipStream_t st);
 

@@ -3,6 +3,7 @@
 // weight; eps 1e-6):
 //   embed_rmsnorm : h = widen(embed[id]) (or given bf16 rows); x = RMS(h) * w
 //   rmsnorm       : x = RMS(h) * w from the fp32 residual
+//   (x in fp16, the GEMM input of the bf16-weight band, or e4m3)
 //   final_split   : z = RMS(h[last row of s]) * w in fp32, stored as two bf16
 //                   terms hi = bf16(z), lo = bf16(z - hi) for the head GEMM
 //   quant_weight  : per-output-channel E4M3 packing of a bf16 weight
@@ -32,7 +33,7 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
-// Write 8 normalised values as bf16 (16 B) or e4m3 (8 B).
+// Write 8 normalised values as fp16 (16 B) or e4m3 (8 B).
 __device__ __forceinline__ void store_x8(void* x_out, size_t idx8, const float* y, bool fp8,
                                          float inv_scale) {
   if (fp8) {
@@ -48,7 +49,7 @@ __device__ __forceinline__ void store_x8(void* x_out, size_t idx8, const float* 
   } else {
     u32x4 o;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = pack_bf2(y[2 * j], y[2 * j + 1]);
+    for (int j = 0; j < 4; ++j) o[j] = pack_f16x2(y[2 * j], y[2 * j + 1]);
     reinterpret_cast<u32x4*>(x_out)[idx8] = o;
   }
 }
@@ -110,6 +111,154 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
       }
       store_x8(x_out, size_t(t) * n8 + i8, y, fp8 != 0, inv_scale);
     }
+  }
+}
+
+// Fused residual add + RMSNorm (steps A6, A9): h[t] += part[0][t] + ... +
+// part[ks-1][t] (the split-K partials of the O or down projection, summed in
+// split order, then added to h: a fixed order, so the result is the same on
+// every run), then x = RMS(h[t]) * w in the OUT format: fp16, e4m3(x * inv),
+// MXFP4 of x * col (OCP MX blocks of 32, the 4 threads of a block adjacent
+// lanes), or nothing (the last layer's residual).  ks = 0: the plain RMSNorm
+// of h.  One row per workgroup, 8 values per thread, 128-bit accesses.
+template <int OUT>
+__global__ __launch_bounds__(kNormThreads) void residual_norm_kernel(
+    float* __restrict__ h, const float* __restrict__ part, int ks, size_t part_stride, int D,
+    const uint16_t* __restrict__ w, float eps, void* __restrict__ x_out, float inv_scale,
+    const float* __restrict__ col, uint8_t* __restrict__ mx_scales, int mx_ld) {
+  __shared__ float red[kNormThreads / 64];
+  const int t = blockIdx.x;
+  const int n8 = D >> 3;
+  u32x4 wq[kNormMaxPerThread];
+  if constexpr (OUT != kNormNone) {
+#pragma unroll
+    for (int c = 0; c < kNormMaxPerThread; ++c) {
+      const int i8 = threadIdx.x + c * kNormThreads;
+      wq[c] = i8 < n8 ? reinterpret_cast<const u32x4*>(w)[i8] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  float v[kNormMaxPerThread][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < kNormMaxPerThread; ++c) {
+    const int i8 = threadIdx.x + c * kNormThreads;
+    if (i8 < n8) {
+      floatx4* hp = reinterpret_cast<floatx4*>(h + size_t(t) * D) + 2 * i8;
+      floatx4 a = hp[0], b = hp[1];
+      if (ks > 0) {
+        const floatx4* pp = reinterpret_cast<const floatx4*>(part + size_t(t) * D) + 2 * i8;
+        floatx4 sa = pp[0], sb = pp[1];
+        for (int kz = 1; kz < ks; ++kz) {
+          const floatx4* q = reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(pp) + kz * part_stride);
+          sa += q[0];
+          sb += q[1];
+        }
+        a += sa;
+        b += sb;
+        hp[0] = a;
+        hp[1] = b;
+      }
+      v[c][0] = a[0]; v[c][1] = a[1]; v[c][2] = a[2]; v[c][3] = a[3];
+      v[c][4] = b[0]; v[c][5] = b[1]; v[c][6] = b[2]; v[c][7] = b[3];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss += v[c][j] * v[c][j];
+    }
+  }
+  if constexpr (OUT == kNormNone) return;
+  const float tot = block_sum(ss, red);
+  const float r = 1.0f / __builtin_sqrtf(tot / float(D) + eps);
+#pragma unroll
+  for (int c = 0; c < kNormMaxPerThread; ++c) {
+    const int i8 = threadIdx.x + c * kNormThreads;
+    if constexpr (OUT == kNormMX) {
+      if (c * kNormThreads >= n8) break;            // uniform: every lane of a block takes part below
+    }
+    const bool ok = i8 < n8;
+    float y[8];
+    if (ok) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y[2 * j] = v[c][2 * j] * r * bf_lo(wq[c][j]);
+        y[2 * j + 1] = v[c][2 * j + 1] * r * bf_hi(wq[c][j]);
+      }
+    }
+    if constexpr (OUT == kNormMX) {
+      float am = 0.f;
+      if (ok) {
+        if (col) {
+          const floatx4* c4 = reinterpret_cast<const floatx4*>(col + 8 * i8);   // 16-byte aligned (checked)
+          const floatx4 c0 = c4[0], c1 = c4[1];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) { y[j] = y[j] * c0[j]; y[4 + j] = y[4 + j] * c1[j]; }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(y[j]));
+      }
+      am = fmaxf(am, __shfl_xor(am, 1, kWave));
+      am = fmaxf(am, __shfl_xor(am, 2, kWave));
+      if (ok) {
+        const int e = mx_block_exp(am);
+        uint32_t wd = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wd |= e2m1_code(ldexpf(y[j], -e)) << (4 * j);
+        reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(x_out) + size_t(t) * (D / 2))[i8] = wd;
+        if ((i8 & 3) == 0) mx_scales[mx_scale_off(t, i8 >> 2, mx_ld)] = uint8_t(e + 127);
+      }
+    } else {
+      if (ok) store_x8(x_out, size_t(t) * n8 + i8, y, OUT == kNormE4M3, inv_scale);
+    }
+  }
+}
+
+// The residual add alone over a flat [n] array (n a multiple of 8): h[i] +=
+// part[0][i] + ... + part[ks-1][i], the same order and operations as
+// residual_norm_kernel, so both give the same bits.
+__global__ __launch_bounds__(256) void residual_sum_kernel(float* __restrict__ h, const float* __restrict__ part,
+                                                           int ks, size_t n) {
+  const size_t n8 = n >> 3;
+  for (size_t i8 = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i8 < n8; i8 += size_t(gridDim.x) * blockDim.x) {
+    floatx4* hp = reinterpret_cast<floatx4*>(h) + 2 * i8;
+    const floatx4* pp = reinterpret_cast<const floatx4*>(part) + 2 * i8;
+    floatx4 sa = pp[0], sb = pp[1];
+    for (int kz = 1; kz < ks; ++kz) {
+      const floatx4* q = reinterpret_cast<const floatx4*>(part + kz * n) + 2 * i8;
+      sa += q[0];
+      sb += q[1];
+    }
+    hp[0] = hp[0] + sa;
+    hp[1] = hp[1] + sb;
+  }
+}
+
+void launch_residual_sum(float* h, const float* part, int ks, size_t n, hipStream_t st) {
+  if (ks <= 0 || n == 0) return;
+  const size_t n8 = n >> 3;
+  const size_t blocks = (n8 + 255) / 256;
+  residual_sum_kernel<<<unsigned(blocks < 4096 ? blocks : 4096), 256, 0, st>>>(h, part, ks, n);
+}
+
+void launch_residual_norm(float* h, const float* part, int ks, int T, int D, const void* w, float eps,
+                          int out_mode, void* x_out, float inv_scale, const float* col, uint8_t* mx_scales,
+                          int mx_ld, hipStream_t st) {
+  const size_t stride = size_t(T) * size_t(D);
+  const uint16_t* w16 = static_cast<const uint16_t*>(w);
+  if (out_mode == kNormNone && ks <= 0) return;
+  switch (out_mode) {
+    case kNormNone:
+      residual_norm_kernel<kNormNone><<<T, kNormThreads, 0, st>>>(h, part, ks, stride, D, w16, eps, x_out, inv_scale,
+                                                                   col, mx_scales, mx_ld);
+      break;
+    case kNormE4M3:
+      residual_norm_kernel<kNormE4M3><<<T, kNormThreads, 0, st>>>(h, part, ks, stride, D, w16, eps, x_out, inv_scale,
+                                                                   col, mx_scales, mx_ld);
+      break;
+    case kNormMX:
+      residual_norm_kernel<kNormMX><<<T, kNormThreads, 0, st>>>(h, part, ks, stride, D, w16, eps, x_out, inv_scale,
+                                                                 col, mx_scales, mx_ld);
+      break;
+    default:
+      residual_norm_kernel<kNormF16><<<T, kNormThreads, 0, st>>>(h, part, ks, stride, D, w16, eps, x_out, inv_scale,
+                                                                  col, mx_scales, mx_ld);
   }
 }
 
@@ -192,9 +341,9 @@ void launch_embed_rmsnorm(const int32_t* ids, const void* embed, const void* x_e
 
 void launch_rmsnorm(const float* h, int T, int D, const void* w, float eps, void* x_out, bool fp8,
                     float inv_scale, hipStream_t st) {
-  rmsnorm_kernel<0><<<T, kNormThreads, 0, st>>>(h, nullptr, nullptr, nullptr, D,
-                                                static_cast<const uint16_t*>(w), eps, x_out, fp8,
-                                                inv_scale);
+  // the fused kernel with no partials: the same arithmetic as after a residual add
+  launch_residual_norm(const_cast<float*>(h), nullptr, 0, T, D, w, eps, fp8 ? kNormE4M3 : kNormF16, x_out, inv_scale,
+                       nullptr, nullptr, 0, st);
 }
 
 void launch_final_split(const float* h, const int32_t* cu, int seq0, int n, int D, const void* w,
@@ -225,7 +374,7 @@ __device__ __forceinline__ void mx_encode32(const float* v, u32x4& codes, uint32
   }
 }
 
-// One thread per (row, block).  SRC 0: bf16 rows, 1: fp32 rows.  v = x * col
+// One thread per (row, block).  SRC 0: bf16 rows, 1: fp32 rows, 2: fp16 rows.  v = x * col
 // (one binary32 rounding) then * row (a second one), as the packing contract.
 template <int SRC>
 __global__ __launch_bounds__(256) void quant_mx_kernel(const void* __restrict__ x, int M, int K,
@@ -245,6 +394,14 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const void* __restrict__ 
       const u32x4 t = p[q];
 #pragma unroll
       for (int j = 0; j < 4; ++j) { v[8 * q + 2 * j] = bf_lo(t[j]); v[8 * q + 2 * j + 1] = bf_hi(t[j]); }
+    }
+  } else if (SRC == 2) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + size_t(r) * K + kb * 32);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 t = p[q];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { v[8 * q + 2 * j] = h_lo(t[j]); v[8 * q + 2 * j + 1] = h_hi(t[j]); }
     }
   } else {
     const floatx4* p = reinterpret_cast<const floatx4*>(static_cast<const float*>(x) + size_t(r) * K + kb * 32);
@@ -276,78 +433,18 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const void* __restrict__ 
   scales[mx_scale_off(r, kb, ld_s)] = uint8_t(sb);
 }
 
-// x = RMS(h) * w * col -> MXFP4.  One row per workgroup, 8 values per thread
-// (as rmsnorm_kernel); the 4 threads of a 32-value block are adjacent lanes.
-__global__ __launch_bounds__(kNormThreads) void rmsnorm_mx_kernel(
-    const float* __restrict__ h, int D, const uint16_t* __restrict__ w, const float* __restrict__ col,
-    float eps, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int ld_s) {
-  __shared__ float red[kNormThreads / 64];
-  const int t = blockIdx.x;
-  const int n8 = D >> 3;
-  float v[kNormMaxPerThread][8];
-  float ss = 0.f;
-#pragma unroll
-  for (int c = 0; c < kNormMaxPerThread; ++c) {
-    const int i8 = threadIdx.x + c * kNormThreads;
-    if (i8 < n8) {
-      const floatx4* p = reinterpret_cast<const floatx4*>(h + size_t(t) * D) + 2 * i8;
-      const floatx4 a = p[0], b = p[1];
-      v[c][0] = a[0]; v[c][1] = a[1]; v[c][2] = a[2]; v[c][3] = a[3];
-      v[c][4] = b[0]; v[c][5] = b[1]; v[c][6] = b[2]; v[c][7] = b[3];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ss += v[c][j] * v[c][j];
-    }
-  }
-  const float tot = block_sum(ss, red);
-  const float r = 1.0f / __builtin_sqrtf(tot / float(D) + eps);
-#pragma unroll
-  for (int c = 0; c < kNormMaxPerThread; ++c) {
-    const int i8 = threadIdx.x + c * kNormThreads;
-    if (c * kNormThreads >= n8) break;            // uniform: every lane of the block takes part below
-    const bool ok = i8 < n8;
-    float y[8];
-    float am = 0.f;
-    if (ok) {
-      const u32x4 wq = reinterpret_cast<const u32x4*>(w)[i8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        y[2 * j] = v[c][2 * j] * r * bf_lo(wq[j]);
-        y[2 * j + 1] = v[c][2 * j + 1] * r * bf_hi(wq[j]);
-      }
-      if (col) {
-        const floatx4* c4 = reinterpret_cast<const floatx4*>(col + 8 * i8);   // 16-byte aligned (checked)
-        const floatx4 c0 = c4[0], c1 = c4[1];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { y[j] = y[j] * c0[j]; y[4 + j] = y[4 + j] * c1[j]; }
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(y[j]));
-    }
-    am = fmaxf(am, __shfl_xor(am, 1, kWave));
-    am = fmaxf(am, __shfl_xor(am, 2, kWave));
-    if (ok) {
-      const int e = mx_block_exp(am);
-      uint32_t wd = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) wd |= e2m1_code(ldexpf(y[j], -e)) << (4 * j);
-      reinterpret_cast<uint32_t*>(codes + size_t(t) * (D / 2))[i8] = wd;
-      if ((i8 & 3) == 0) scales[mx_scale_off(t, i8 >> 2, ld_s)] = uint8_t(e + 127);
-    }
-  }
-}
-
-void launch_quant_mx(const void* x, bool f32, int M, int K, const float* col, const float* row_scale,
+void launch_quant_mx(const void* x, int fmt, int M, int K, const float* col, const float* row_scale,
                      uint8_t* codes, uint8_t* scales, int ld_s, hipStream_t st) {
   const size_t n = size_t(M) * (K / 32);
   const int grid = int((n + 255) / 256);
-  if (f32) quant_mx_kernel<1><<<grid, 256, 0, st>>>(x, M, K, col, row_scale, codes, scales, ld_s);
+  if (fmt == 1) quant_mx_kernel<1><<<grid, 256, 0, st>>>(x, M, K, col, row_scale, codes, scales, ld_s);
+  else if (fmt == 2) quant_mx_kernel<2><<<grid, 256, 0, st>>>(x, M, K, col, row_scale, codes, scales, ld_s);
   else quant_mx_kernel<0><<<grid, 256, 0, st>>>(x, M, K, col, row_scale, codes, scales, ld_s);
 }
 
 void launch_rmsnorm_mx(const float* h, int T, int D, const void* w, const float* col, float eps,
                        uint8_t* codes, uint8_t* scales, int ld_s, hipStream_t st) {
-  rmsnorm_mx_kernel<<<T, kNormThreads, 0, st>>>(h, D, static_cast<const uint16_t*>(w), col, eps, codes, scales,
-                                                ld_s);
+  launch_residual_norm(const_cast<float*>(h), nullptr, 0, T, D, w, eps, kNormMX, codes, 1.f, col, scales, ld_s, st);
 }
 
 }  // namespace hr

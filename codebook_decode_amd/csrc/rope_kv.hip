@@ -11,10 +11,11 @@
 // float64, reduced to [-pi, pi] in float64, its sine and cosine taken in fp32,
 // kept in LDS.  Then every head row of those tokens is handled by d/16 lanes, lane c
 // owning the 8 RoPE pairs (8c + i, d/2 + 8c + i), i < 8: it reads the two
-// 16-byte halves straight from the merged QKV row (the d/16 lanes of a row
-// read 2 x d bytes, whole 128-byte lines), the head's sum of squares is a
-// butterfly over those lanes, and the results leave as 16-byte stores.  Rows
-// are dealt to the threads in rounds of 256 / (d/16), kRopeRows rounds in flight.
+// 32-byte pieces straight from the fp32 merged QKV row (the d/16 lanes of a
+// row read 4 x d bytes, whole 128-byte lines), the head's sum of squares is a
+// butterfly over those lanes, and the results leave as 16-byte stores: q in
+// fp16, k and v in bf16 (the cache), each value rounded once.  Rows are dealt
+// to the threads in rounds of 256 / (d/16), kRopeRows rounds in flight.
 #include <cmath>
 
 #include "common.h"
@@ -27,7 +28,7 @@ constexpr int kRopeTok = 4;     // tokens per workgroup
 constexpr int kRopeRows = 3;    // head-row rounds with loads in flight per thread
 
 __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
-    const uint16_t* __restrict__ qkv, int T, int tpb, int Hq, int Hkv, int d, const RopeFreq freq, float eps,
+    const float* __restrict__ qkv, int T, int tpb, int Hq, int Hkv, int d, const RopeFreq freq, float eps,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ start_pos,
     const int32_t* __restrict__ cache_slot, const int32_t* __restrict__ used_keys, int n_seq,
     int causal, const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
@@ -49,18 +50,18 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
   const int step = per_round * kRopeRows;
 
   // head rows of one round of kRopeRows x per_round rows
-  u32x4 lo[kRopeRows], hi[kRopeRows];
+  F8 lo[kRopeRows], hi[kRopeRows];
   auto load_round = [&](int base) {
 #pragma unroll
     for (int k = 0; k < kRopeRows; ++k) {
       const int rr = base + k * per_round;
       if (rr < total) {
         const int tt = rr / n_rows, r = rr % n_rows;
-        const uint16_t* src = qkv + size_t(t0 + tt) * n_rows * d + size_t(r) * d;
-        lo[k] = *reinterpret_cast<const u32x4*>(src + 8 * c);
-        hi[k] = *reinterpret_cast<const u32x4*>(src + half + 8 * c);
+        const float* src = qkv + size_t(t0 + tt) * n_rows * d + size_t(r) * d;
+        lo[k] = load_f8(src + 8 * c);
+        hi[k] = load_f8(src + half + 8 * c);
       } else {
-        lo[k] = u32x4{0u, 0u, 0u, 0u};
+        lo[k] = F8{floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
         hi[k] = lo[k];
       }
     }
@@ -106,17 +107,17 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
         const bool is_q = r < Hq;
         if (!is_q && !s_wkv[tt]) continue;
         const float inv = 1.0f / __builtin_sqrtf(ss / float(d) + eps);
-        u32x4 o0, o1;
+        F8 o0, o1;
         rope_pairs(lo[k], hi[k], is_q ? wq0 : wk0, is_q ? wq1 : wk1, inv, &s_cos[tt][8 * c], &s_sin[tt][8 * c],
                    o0, o1);
         uint16_t* dst = is_q ? q_out + (size_t(t) * Hq + r) * d
                              : kc + (size_t(s_crow[tt]) * Hkv + (r - Hq)) * d;
-        *reinterpret_cast<u32x4*>(dst + 8 * c) = o0;
-        *reinterpret_cast<u32x4*>(dst + half + 8 * c) = o1;
+        *reinterpret_cast<u32x4*>(dst + 8 * c) = is_q ? pack8_f16(o0) : pack8_bf16(o0);
+        *reinterpret_cast<u32x4*>(dst + half + 8 * c) = is_q ? pack8_f16(o1) : pack8_bf16(o1);
       } else if (s_wkv[tt]) {
         uint16_t* dst = vc + (size_t(s_crow[tt]) * Hkv + (r - Hq - Hkv)) * d;
-        *reinterpret_cast<u32x4*>(dst + 8 * c) = lo[k];
-        *reinterpret_cast<u32x4*>(dst + half + 8 * c) = hi[k];
+        *reinterpret_cast<u32x4*>(dst + 8 * c) = pack8_bf16(lo[k]);
+        *reinterpret_cast<u32x4*>(dst + half + 8 * c) = pack8_bf16(hi[k]);
       }
     }
   }
@@ -135,7 +136,7 @@ void launch_qknorm_rope_kv(const void* qkv, int T, int Hq, int Hkv, int d, float
   const int blocks = (T + tpb - 1) / tpb;
   const RopeFreq freq = rope_freq(d, theta);
   qknorm_rope_kv_kernel<<<blocks, 256, 0, st>>>(
-      static_cast<const uint16_t*>(qkv), T, tpb, Hq, Hkv, d, freq, eps, cu, start_pos, cache_slot,
+      static_cast<const float*>(qkv), T, tpb, Hq, Hkv, d, freq, eps, cu, start_pos, cache_slot,
       used_keys, n_seq, causal ? 1 : 0, static_cast<const uint16_t*>(qw),
       static_cast<const uint16_t*>(kw), static_cast<uint16_t*>(q_out), static_cast<uint16_t*>(kc),
       static_cast<uint16_t*>(vc), capacity);
@@ -157,7 +158,8 @@ void launch_qknorm_rope_kv(const void* qkv, int T, int Hq, int Hkv, int d, float
 // exact row max; the max and the sum are DPP reductions within rows of 16
 // lanes and a fixed-order combination of the 4 rows.  P V: lane l owns output
 // dims 2l and 2l + 1 and takes each probability from lane j by readlane.  The
-// output is o / l rounded once (bf16, or e4m3 of o / l times out_inv).
+// output is o / l rounded once (fp16, or e4m3 of o / l times out_inv).  q is
+// held in fp16 and k, v in bf16, the values the separate kernels store.
 // Causal: keys j <= i; otherwise keys j < used_keys[s].
 template <int CTRL>
 __device__ __forceinline__ float dpp_row(float v) {
@@ -187,7 +189,7 @@ constexpr int kSmallWaves = 8;
 
 template <int D, int NQ>
 __global__ __launch_bounds__(64 * kSmallWaves) void rope_attn_small_kernel(
-    const uint16_t* __restrict__ qkv, int Hq, int Hkv, const RopeFreq freq, float eps,
+    const float* __restrict__ qkv, int Hq, int Hkv, const RopeFreq freq, float eps,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ cache_slot, const int32_t* __restrict__ used_keys,
     int causal, const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw, uint16_t* __restrict__ kc,
     uint16_t* __restrict__ vc, int capacity, float scale_log2, void* __restrict__ out, int out_fp8,
@@ -213,18 +215,18 @@ __global__ __launch_bounds__(64 * kSmallWaves) void rope_attn_small_kernel(
   const int c = tid % L;
 
   // rows rr < 3 len: q of token rr, then k of token rr - len, then v
-  u32x4 lo[NR], hi[NR];
+  F8 lo[NR], hi[NR];
 #pragma unroll
   for (int k = 0; k < NR; ++k) {
     const int rr = tid / L + k * PER;
     if (rr < 3 * len) {
       const int kind = rr / len, i = rr - kind * len;
       const int head = kind == 0 ? hq : (kind == 1 ? Hq + g : Hq + Hkv + g);
-      const uint16_t* src = qkv + (size_t(t0 + i) * n_rows + head) * D;
-      lo[k] = *reinterpret_cast<const u32x4*>(src + 8 * c);
-      hi[k] = *reinterpret_cast<const u32x4*>(src + HALF + 8 * c);
+      const float* src = qkv + (size_t(t0 + i) * n_rows + head) * D;
+      lo[k] = load_f8(src + 8 * c);
+      hi[k] = load_f8(src + HALF + 8 * c);
     } else {
-      lo[k] = u32x4{0u, 0u, 0u, 0u};
+      lo[k] = F8{floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
       hi[k] = lo[k];
     }
   }
@@ -247,9 +249,11 @@ __global__ __launch_bounds__(64 * kSmallWaves) void rope_attn_small_kernel(
     const bool kv_row = write_kv && (causal || i < n_keys);
     if (kind < 2) {
       const float inv = 1.0f / __builtin_sqrtf(ss / float(D) + eps);
-      u32x4 o0, o1;
+      F8 r0, r1;
       rope_pairs(lo[k], hi[k], kind == 0 ? wq0 : wk0, kind == 0 ? wq1 : wk1, inv, &s_cos[i][8 * c],
-                 &s_sin[i][8 * c], o0, o1);
+                 &s_sin[i][8 * c], r0, r1);
+      const u32x4 o0 = kind == 0 ? pack8_f16(r0) : pack8_bf16(r0);
+      const u32x4 o1 = kind == 0 ? pack8_f16(r1) : pack8_bf16(r1);
       uint16_t* row = kind == 0 ? &s_q[i][0] : &s_k[i][0];
       *reinterpret_cast<u32x4*>(row + 8 * c) = o0;
       *reinterpret_cast<u32x4*>(row + HALF + 8 * c) = o1;
@@ -259,12 +263,13 @@ __global__ __launch_bounds__(64 * kSmallWaves) void rope_attn_small_kernel(
         *reinterpret_cast<u32x4*>(dst + HALF + 8 * c) = o1;
       }
     } else {
-      *reinterpret_cast<u32x4*>(&s_v[i][8 * c]) = lo[k];
-      *reinterpret_cast<u32x4*>(&s_v[i][HALF + 8 * c]) = hi[k];
+      const u32x4 v0 = pack8_bf16(lo[k]), v1 = pack8_bf16(hi[k]);
+      *reinterpret_cast<u32x4*>(&s_v[i][8 * c]) = v0;
+      *reinterpret_cast<u32x4*>(&s_v[i][HALF + 8 * c]) = v1;
       if (kv_row) {
         uint16_t* dst = vc + (size_t(crow0 + i) * Hkv + g) * D;
-        *reinterpret_cast<u32x4*>(dst + 8 * c) = lo[k];
-        *reinterpret_cast<u32x4*>(dst + HALF + 8 * c) = hi[k];
+        *reinterpret_cast<u32x4*>(dst + 8 * c) = v0;
+        *reinterpret_cast<u32x4*>(dst + HALF + 8 * c) = v1;
       }
     }
   }
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void rope_attn_small_kernel(
     for (int e = 0; e < 8; ++e) {
       const float kf = bf_at(kv, e);
 #pragma unroll
-      for (int qi = 0; qi < NQ; ++qi) acc[qi] += bf_at(qv[qi], e) * kf;
+      for (int qi = 0; qi < NQ; ++qi) acc[qi] += h_at(qv[qi], e) * kf;
     }
   }
   float p[NQ], inv_l[NQ];
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void rope_attn_small_kernel(
           *reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(out) + orow) =
               uint16_t(f2e4m3(y0 * out_inv) | (f2e4m3(y1 * out_inv) << 8));
         else
-          *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + orow) = pack_bf2(y0, y1);
+          *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + orow) = pack_f16x2(y0, y1);
       }
     }
   }
@@ -346,7 +351,7 @@ void launch_rope_attn_small(const void* qkv, int n_seq, int max_len, int Hq, int
   const dim3 grid(Hq, n_seq);
   auto go = [&](auto kern) {
     kern<<<grid, 64 * kSmallWaves, 0, st>>>(
-        static_cast<const uint16_t*>(qkv), Hq, Hkv, freq, eps, cu, cache_slot, used_keys, causal ? 1 : 0,
+        static_cast<const float*>(qkv), Hq, Hkv, freq, eps, cu, cache_slot, used_keys, causal ? 1 : 0,
         static_cast<const uint16_t*>(qw), static_cast<const uint16_t*>(kw), static_cast<uint16_t*>(kc),
         static_cast<uint16_t*>(vc), capacity, scale_log2, out, fp8 ? 1 : 0, out_inv);
   };

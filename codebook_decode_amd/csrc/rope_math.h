@@ -14,37 +14,50 @@ namespace hr {
 __device__ __forceinline__ float bf_at(const u32x4& v, int i) {   // element i < 8 (i constant)
   return (i & 1) ? bf_hi(v[i >> 1]) : bf_lo(v[i >> 1]);
 }
+__device__ __forceinline__ float h_at(const u32x4& v, int i) {    // fp16 element i < 8 (i constant)
+  return (i & 1) ? h_hi(v[i >> 1]) : h_lo(v[i >> 1]);
+}
+
+// 8 consecutive fp32 values of a head row (two 16-byte loads)
+struct F8 {
+  floatx4 a, b;
+  __device__ __forceinline__ float operator[](int i) const { return i < 4 ? a[i] : b[i - 4]; }
+};
+__device__ __forceinline__ F8 load_f8(const float* p) {
+  return F8{reinterpret_cast<const floatx4*>(p)[0], reinterpret_cast<const floatx4*>(p)[1]};
+}
+__device__ __forceinline__ u32x4 pack8_bf16(const F8& v) {      // nearest even (the cache format)
+  return u32x4{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7])};
+}
+__device__ __forceinline__ u32x4 pack8_f16(const F8& v) {       // nearest even (q for the attention)
+  return u32x4{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]), pack_f16x2(v[6], v[7])};
+}
 
 // sum of squares of a lane's 8 pairs of a head row
-__device__ __forceinline__ float pairs_sumsq(const u32x4& lo, const u32x4& hi) {
+__device__ __forceinline__ float pairs_sumsq(const F8& lo, const F8& hi) {
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float a = bf_at(lo, i), b = bf_at(hi, i);
-    ss += a * a + b * b;
-  }
+  for (int i = 0; i < 8; ++i) ss += lo[i] * lo[i] + hi[i] * hi[i];
   return ss;
 }
 
-// a lane's 8 RoPE pairs (m, m + d/2), m = 8c + i: RMSNorm scale inv and norm
-// weights (w0: first half, w1: second half), then the rotation by the angles
-// cs[i], sn[i]; bf16 results
-__device__ __forceinline__ void rope_pairs(const u32x4& lo, const u32x4& hi, const u32x4& w0, const u32x4& w1,
-                                           float inv, const float* cs, const float* sn, u32x4& o0, u32x4& o1) {
+// a lane's 8 RoPE pairs (m, m + d/2), m = 8c + i, of an fp32 head row: RMSNorm
+// scale inv and bf16 norm weights (w0: first half, w1: second half), then the
+// rotation by the angles cs[i], sn[i]; fp32 results (the caller rounds them
+// once, to bf16 for the cache or fp16 for q)
+__device__ __forceinline__ void rope_pairs(const F8& lo, const F8& hi, const u32x4& w0, const u32x4& w1,
+                                           float inv, const float* cs, const float* sn, F8& o0, F8& o1) {
+  float y0[8], y1[8];
 #pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    float y0[2], y1[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float a = bf_at(lo, i + e) * inv * bf_at(w0, i + e);
-      const float b = bf_at(hi, i + e) * inv * bf_at(w1, i + e);
-      const float c = cs[i + e], s = sn[i + e];
-      y0[e] = a * c - b * s;
-      y1[e] = b * c + a * s;
-    }
-    o0[i / 2] = pack_bf2(y0[0], y0[1]);
-    o1[i / 2] = pack_bf2(y1[0], y1[1]);
+  for (int i = 0; i < 8; ++i) {
+    const float a = lo[i] * inv * bf_at(w0, i);
+    const float b = hi[i] * inv * bf_at(w1, i);
+    const float c = cs[i], s = sn[i];
+    y0[i] = a * c - b * s;
+    y1[i] = b * c + a * s;
   }
+  o0 = F8{floatx4{y0[0], y0[1], y0[2], y0[3]}, floatx4{y0[4], y0[5], y0[6], y0[7]}};
+  o1 = F8{floatx4{y1[0], y1[1], y1[2], y1[3]}, floatx4{y1[4], y1[5], y1[6], y1[7]}};
 }
 
 // angle of pair m at position p: p * theta^(-2m/d) in float64, reduced to

@@ -17,8 +17,9 @@ LIB_PATH = os.path.join(_HERE, "libhr.so")
 
 HR_OK, HR_EINVAL, HR_EUNSUPPORTED, HR_ECAPACITY = 0, -1, -2, -3
 HR_EBOUND, HR_EWORKSPACE, HR_EALIGN, HR_EHIP = -4, -5, -6, -7
-HR_BF16, HR_FP8_E4M3, HR_MXFP4 = 0, 1, 2
-HR_EPI_BF16, HR_EPI_RESIDUAL, HR_EPI_SWIGLU = 0, 1, 2
+HR_BF16, HR_FP8_E4M3, HR_MXFP4, HR_F16 = 0, 1, 2, 3
+HR_EPI_F32, HR_EPI_RESIDUAL, HR_EPI_SWIGLU = 0, 1, 2
+MX_SRC_BF16, MX_SRC_F32, MX_SRC_F16 = 0, 1, 2
 STATUS_NAMES = {0: "HR_OK", -1: "HR_EINVAL", -2: "HR_EUNSUPPORTED", -3: "HR_ECAPACITY",
                 -4: "HR_EBOUND", -5: "HR_EWORKSPACE", -6: "HR_EALIGN", -7: "HR_EHIP"}
 
@@ -98,7 +99,10 @@ def lib() -> ctypes.CDLL:
             "hr_embed_rmsnorm": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_vp, c_f32, c_vp, c_vp,
                                          c_i32, c_f32, c_vp]),
             "hr_rmsnorm": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_f32, c_vp, c_i32, c_f32, c_vp]),
-            "hr_linear": (c_i32, [c_vp, c_vp, c_vp, c_f32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_f32, c_vp]),
+            "hr_linear_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
+            "hr_linear": (c_i32, [c_vp, c_vp, c_vp, c_f32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_f32, c_vp, c_sz,
+                                  c_vp]),
+            "hr_residual_rmsnorm": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_f32, c_vp, c_i32, c_f32, c_vp]),
             "hr_qknorm_rope_kv": (c_i32, [P(HrDims), P(HrBatch), c_vp, c_vp, c_vp, c_vp, P(HrKv), c_vp]),
             "hr_attention": (c_i32, [P(HrDims), P(HrBatch), c_vp, P(HrKv), c_vp, c_i32, c_f32, c_vp]),
             "hr_qknorm_rope_attention": (c_i32, [P(HrDims), P(HrBatch), c_vp, c_vp, c_vp, P(HrKv), c_vp, c_i32,
@@ -113,7 +117,7 @@ def lib() -> ctypes.CDLL:
             "hr_quantize_mxfp4": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp]),
             "hr_rmsnorm_mxfp4": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_f32, c_vp, c_vp, c_vp, c_i32, c_vp]),
             "hr_linear_mxfp4": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp,
-                                        c_i32, c_vp]),
+                                        c_i32, c_vp, c_sz, c_vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -279,21 +283,34 @@ def hr_codebook_step_policy(B, K, V, bos_id, eoc_id, logits, frame, eoc_seen, do
                                          stream if stream is not None else current_stream()))
 
 
-def hr_embed_rmsnorm(ids, embed, vocab, x_embeds, T, D, norm_w, eps, h_out, x_out, x_type=HR_BF16,
+def hr_embed_rmsnorm(ids, embed, vocab, x_embeds, T, D, norm_w, eps, h_out, x_out, x_type=HR_F16,
                      x_scale=1.0, stream=None) -> None:
     _check(lib().hr_embed_rmsnorm(ptr(ids), ptr(embed), vocab, ptr(x_embeds), T, D, ptr(norm_w), eps,
                                   ptr(h_out), ptr(x_out), x_type, x_scale,
                                   stream if stream is not None else current_stream()))
 
 
-def hr_rmsnorm(h, T, D, norm_w, eps, x_out, x_type=HR_BF16, x_scale=1.0, stream=None) -> None:
+def hr_rmsnorm(h, T, D, norm_w, eps, x_out, x_type=HR_F16, x_scale=1.0, stream=None) -> None:
     _check(lib().hr_rmsnorm(ptr(h), T, D, ptr(norm_w), eps, ptr(x_out), x_type, x_scale,
                             stream if stream is not None else current_stream()))
 
 
-def hr_linear(x, w, w_scale, x_scale, wtype, M, N, K, epi, out, out_scale=0.0, stream=None) -> None:
+def hr_linear_workspace_bytes(wtype, M, N, K, epi) -> int:
+    return lib().hr_linear_workspace_bytes(wtype, M, N, K, epi)
+
+
+def hr_linear(x, w, w_scale, x_scale, wtype, M, N, K, epi, out, out_scale=0.0, ws=None, stream=None) -> None:
+    """``ws``: device scratch of hr_linear_workspace_bytes(...) bytes (a torch
+    tensor) when that is non-zero (the split-K partials of HR_EPI_RESIDUAL)."""
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().hr_linear(ptr(x), ptr(w), ptr(w_scale), x_scale, wtype, M, N, K, epi, ptr(out), out_scale,
-                           stream if stream is not None else current_stream()))
+                           ptr(ws), nbytes, stream if stream is not None else current_stream()))
+
+
+def hr_residual_rmsnorm(h, partials, n_partials, T, D, norm_w, eps, x_out, x_type=HR_F16, x_scale=1.0,
+                        stream=None) -> None:
+    _check(lib().hr_residual_rmsnorm(ptr(h), ptr(partials), n_partials, T, D, ptr(norm_w), eps, ptr(x_out), x_type,
+                                     x_scale, stream if stream is not None else current_stream()))
 
 
 def hr_qknorm_rope_kv(dims, batch: Batch, qkv, q_norm_w, k_norm_w, q_out, kv: HrKv, stream=None) -> None:
@@ -302,12 +319,12 @@ def hr_qknorm_rope_kv(dims, batch: Batch, qkv, q_norm_w, k_norm_w, q_out, kv: Hr
                                    stream if stream is not None else current_stream()))
 
 
-def hr_attention(dims, batch: Batch, q, kv: HrKv, out, out_type=HR_BF16, out_scale=1.0, stream=None) -> None:
+def hr_attention(dims, batch: Batch, q, kv: HrKv, out, out_type=HR_F16, out_scale=1.0, stream=None) -> None:
     _check(lib().hr_attention(ctypes.byref(dims), ctypes.byref(batch.c), ptr(q), ctypes.byref(kv), ptr(out),
                               out_type, out_scale, stream if stream is not None else current_stream()))
 
 
-def hr_qknorm_rope_attention(dims, batch: Batch, qkv, q_norm_w, k_norm_w, kv: HrKv, out, out_type=HR_BF16,
+def hr_qknorm_rope_attention(dims, batch: Batch, qkv, q_norm_w, k_norm_w, kv: HrKv, out, out_type=HR_F16,
                              out_scale=1.0, stream=None) -> None:
     _check(lib().hr_qknorm_rope_attention(ctypes.byref(dims), ctypes.byref(batch.c), ptr(qkv), ptr(q_norm_w),
                                           ptr(k_norm_w), ctypes.byref(kv), ptr(out), out_type, out_scale,
@@ -319,7 +336,7 @@ def hr_attention_chunked_workspace_bytes(dims, total_tokens: int, n_slots: int) 
 
 
 def hr_attention_chunked(dims, batch: Batch, q, kv: HrKv, out, chunk_tiles: int, n_slots: int, ws,
-                         out_type=HR_BF16, out_scale=1.0, stream=None) -> None:
+                         out_type=HR_F16, out_scale=1.0, stream=None) -> None:
     _check(lib().hr_attention_chunked(ctypes.byref(dims), ctypes.byref(batch.c), ptr(q), ctypes.byref(kv), ptr(out),
                                       out_type, out_scale, chunk_tiles, n_slots, ptr(ws),
                                       ws.numel() * ws.element_size(),
@@ -349,8 +366,8 @@ def mx_scale_bytes(rows: int, K: int) -> int:
 
 def hr_quantize_mxfp4(x, M, K, codes, scales, ld_scales, col_scale=None, row_scale=None, stream=None) -> None:
     import torch
-    f32 = 1 if x.dtype == torch.float32 else 0
-    _check(lib().hr_quantize_mxfp4(ptr(x), f32, M, K, ptr(col_scale), ptr(row_scale), ptr(codes), ptr(scales),
+    fmt = {torch.bfloat16: MX_SRC_BF16, torch.float32: MX_SRC_F32, torch.float16: MX_SRC_F16}[x.dtype]
+    _check(lib().hr_quantize_mxfp4(ptr(x), fmt, M, K, ptr(col_scale), ptr(row_scale), ptr(codes), ptr(scales),
                                    ld_scales, stream if stream is not None else current_stream()))
 
 
@@ -360,7 +377,15 @@ def hr_rmsnorm_mxfp4(h, T, D, norm_w, eps, codes, scales, ld_scales, col_scale=N
 
 
 def hr_linear_mxfp4(x, x_scales, ld_x_scales, w, w_scales, M, N, K, epi, out, out_scales=None, ld_out_scales=0,
-                    stream=None) -> None:
+                    ws=None, stream=None) -> None:
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().hr_linear_mxfp4(ptr(x), ptr(x_scales), ld_x_scales, ptr(w), ptr(w_scales), M, N, K, epi,
-                                 ptr(out), ptr(out_scales), ld_out_scales,
+                                 ptr(out), ptr(out_scales), ld_out_scales, ptr(ws), nbytes,
                                  stream if stream is not None else current_stream()))
+
+
+def linear_ws(wtype, M, N, K, epi):
+    """A device workspace for hr_linear / hr_linear_mxfp4 (None when none is needed)."""
+    import torch
+    n = hr_linear_workspace_bytes(wtype, M, N, K, epi)
+    return torch.empty(n, dtype=torch.uint8, device="cuda") if n else None

@@ -57,7 +57,10 @@ typedef enum {
   HR_EHIP = -7           /* a HIP launch error                                   */
 } hr_status;
 
-typedef enum { HR_BF16 = 0, HR_FP8_E4M3 = 1, HR_MXFP4 = 2 } hr_wtype;
+/* Number formats.  Weights: HR_BF16, HR_FP8_E4M3, HR_MXFP4.  HR_F16 (IEEE
+ * binary16) names the activations of the bf16-weight band where a step entry
+ * of hr_ops.h takes an activation type. */
+typedef enum { HR_BF16 = 0, HR_FP8_E4M3 = 1, HR_MXFP4 = 2, HR_F16 = 3 } hr_wtype;
 
 /* Shapes of the decoder.  Supported: head_dim in {64, 128};
  * n_q_heads / n_kv_heads in {1, 2, 4}; hidden, ffn multiples of 64. */
@@ -76,7 +79,14 @@ typedef struct {
 } hr_dims;
 
 /* One decoder layer: device pointers, weights row-major [out, in].
- *  bf16:  w_* are bf16.
+ *  bf16:  w_* are bf16.  The activations between the kernels are fp16 (the
+ *         norm outputs, the attention output, the SwiGLU product; 11-bit
+ *         significand), the merged QKV rows fp32, the residual fp32 and the KV
+ *         cache bf16; the GEMMs and attention run fp16 MFMAs (weights and
+ *         cache rows converted exactly in registers) with fp32 accumulation.
+ *         bf16 activations would hold the layer only to about 4e-2 of the
+ *         exact result on 4B-class shapes (the bf16 storage points alone), the
+ *         fp16 ones to about 1e-2, at the same MFMA rate.
  *  FP8:   w_* are e4m3 codes with per-output-channel fp32 scales ws_* so that
  *         W[n, k] ~= ws[n] * e4m3(w[n, k]); as_* are the static per-tensor
  *         activation scales (host floats): the GEMM input x is quantised as

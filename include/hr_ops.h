@@ -20,37 +20,62 @@ extern "C" {
 
 /* Embedding lookup + input RMSNorm (steps A0, A1).
  * h_out[t] = embed[ids[t]] widened to fp32 (x_embeds[t] when ids == NULL);
- * x_out[t] = h[t] * (mean(h[t]^2) + eps)^-1/2 * norm_w, stored bf16, or as
- * e4m3(x / x_scale) when x_type == HR_FP8_E4M3.  D a multiple of 8. */
+ * x_out[t] = h[t] * (mean(h[t]^2) + eps)^-1/2 * norm_w, stored fp16
+ * (x_type == HR_F16, the input of the bf16-weight band's GEMMs) or as
+ * e4m3(x / x_scale) (x_type == HR_FP8_E4M3).  D a multiple of 8. */
 hr_status hr_embed_rmsnorm(const int32_t* ids, const void* embed, int32_t vocab,
                            const void* x_embeds, int32_t T, int32_t D, const void* norm_w,
                            float eps, float* h_out, void* x_out, hr_wtype x_type, float x_scale,
                            hipStream_t stream);
 
 /* RMSNorm of the fp32 residual (steps A6, A9): x_out[t] = RMS(h[t]) * norm_w,
- * bf16 or e4m3(x / x_scale).  (The residual add itself is fused into the
- * epilogue of the O and down projections, HR_EPI_RESIDUAL.) */
+ * fp16 (HR_F16) or e4m3(x / x_scale) (HR_FP8_E4M3).  (The residual add itself
+ * is fused into the epilogue of the O and down projections, HR_EPI_RESIDUAL.) */
 hr_status hr_rmsnorm(const float* h, int32_t T, int32_t D, const void* norm_w, float eps,
                      void* x_out, hr_wtype x_type, float x_scale, hipStream_t stream);
 
 typedef enum {
-  HR_EPI_BF16 = 0,      /* out bf16 [M, N] = x W^T                               */
+  HR_EPI_F32 = 0,       /* out fp32 [M, N] = x W^T  (the merged QKV rows)        */
   HR_EPI_RESIDUAL = 1,  /* out fp32 [M, N] += x W^T  (residual add)              */
   HR_EPI_SWIGLU = 2     /* N = 2F (gate rows, then up rows); out [M, F] =
-                           silu(g) * u, bf16, or e4m3(./out_scale) in FP8 mode  */
+                           silu(g) * u, fp16, or e4m3(./out_scale) in FP8 mode  */
 } hr_epilogue;
 
-/* Projection (steps A2, A5, A7, A8): x [M, K] times W [N, K]^T.
- *  bf16:  x and w bf16; w_scale ignored.
- *  FP8:   x and w e4m3; the product is scaled by x_scale * w_scale[n].
+/* Projection (steps A2, A5, A7, A8): x [M, K] times W [N, K]^T, fp32
+ * accumulation.
+ * HR_EPI_RESIDUAL may split K over workgroups to fill the GPU; the splits'
+ * fp32 partials then go to ws (hr_linear_workspace_bytes: 0 when no split is
+ * taken) and are added to out in split order, h + (p0 + p1 + ...): the
+ * result does not depend on the order in which workgroups finish, and equals
+ * bit for bit what the layer entries compute (there the add is fused with the
+ * next RMSNorm, hr_residual_rmsnorm).  HR_EWORKSPACE if ws is too small.
+ *  wtype HR_BF16:     x fp16, w bf16 (each weight enters the fp16 MFMA
+ *                     converted exactly: bf16 values of magnitude 2^-17 to
+ *                     2^16 are fp16 values; smaller ones round to a multiple
+ *                     of 2^-24); w_scale ignored.
+ *  wtype HR_FP8_E4M3: x and w e4m3; the product is scaled by
+ *                     x_scale * w_scale[n].
  * K a multiple of 64, N a multiple of 16 (32 for SWIGLU). */
+size_t hr_linear_workspace_bytes(hr_wtype wtype, int32_t M, int32_t N, int32_t K, hr_epilogue epi);
 hr_status hr_linear(const void* x, const void* w, const float* w_scale, float x_scale,
                     hr_wtype wtype, int32_t M, int32_t N, int32_t K, hr_epilogue epi, void* out,
-                    float out_scale, hipStream_t stream);
+                    float out_scale, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Fused residual add + RMSNorm (steps A6, A9; the fused residual-add +
+ * RMSNorm (+ quantise) of flashrt-structures prefill_tower/fp8_chain.py, `run`):
+ * h[t] += p[0][t] + ... + p[n-1][t] with p[k] = partials + k*T*D (the split-K
+ * partials of a residual projection, summed in that order, then added to h;
+ * n_partials = 0: no add), then x_out[t] = RMS(h[t]) * norm_w as fp16
+ * (HR_F16) or e4m3(x / x_scale); x_out NULL: the add alone.  h fp32 [T, D],
+ * D a multiple of 8 and <= 8192. */
+hr_status hr_residual_rmsnorm(float* h, const float* partials, int32_t n_partials, int32_t T, int32_t D,
+                              const void* norm_w, float eps, void* x_out, hr_wtype x_type, float x_scale,
+                              hipStream_t stream);
 
 /* Per-head q/k RMSNorm + rotate-half RoPE + KV-cache write (step A3).
- * qkv bf16 [T, (Hq+2Hkv)d] -> q_out bf16 [T, Hq, d] (normed, rotated);
- * cache rows slot*capacity + start_pos + i receive k (normed, rotated) and v.
+ * qkv fp32 [T, (Hq+2Hkv)d] -> q_out fp16 [T, Hq, d] (normed, rotated);
+ * cache rows slot*capacity + start_pos + i receive k (normed, rotated) and v,
+ * each rounded once to bf16.
  * RoPE angle of pair (m, m + d/2) at position p: p * theta^(-2m/d).
  * Non-causal batches skip the cache write of pad rows i >= used_keys[s]. */
 hr_status hr_qknorm_rope_kv(const hr_dims* dims, const hr_batch* batch, const void* qkv,
@@ -59,7 +84,8 @@ hr_status hr_qknorm_rope_kv(const hr_dims* dims, const hr_batch* batch, const vo
 
 /* Steps A3 and A4 in one launch for short prompts: the q/k norm + RoPE + KV
  * write of hr_qknorm_rope_kv (the cache receives the same values) followed by
- * the attention of hr_attention, out bf16 or e4m3(o / out_scale) [T, Hq*d],
+ * the attention of hr_attention, out fp16 (HR_F16) or e4m3(o / out_scale)
+ * [T, Hq*d],
  * without writing q anywhere.  Every sequence must start at position 0 and
  * hold at most 32 rows (HR_EUNSUPPORTED otherwise): its keys are then its own
  * rows.  The layer entries take this path by themselves for such batches. */
@@ -67,9 +93,11 @@ hr_status hr_qknorm_rope_attention(const hr_dims* dims, const hr_batch* batch, c
                                    const void* q_norm_w, const void* k_norm_w, const hr_kv* kv, void* out,
                                    hr_wtype out_type, float out_scale, hipStream_t stream);
 
-/* GQA attention over the cache (step A4): out [T, Hq*d] with
- * o_h = softmax(q_h K_g^T / sqrt(d)) V_g, g = h / (Hq/Hkv), over the causal
- * window or the used keys (dims->causal).  bf16 out, or e4m3(o / out_scale). */
+/* GQA attention over the cache (step A4): q fp16 [T, Hq, d], out [T, Hq*d]
+ * with o_h = softmax(q_h K_g^T / sqrt(d)) V_g, g = h / (Hq/Hkv), over the
+ * causal window or the used keys (dims->causal).  Scores and P V run as fp16
+ * MFMAs with fp32 accumulation (the bf16 cache rows convert exactly); out fp16
+ * (HR_F16) or e4m3(o / out_scale) (HR_FP8_E4M3). */
 hr_status hr_attention(const hr_dims* dims, const hr_batch* batch, const void* q, const hr_kv* kv,
                        void* out, hr_wtype out_type, float out_scale, hipStream_t stream);
 
@@ -122,10 +150,11 @@ hr_status hr_quantize_weight_e4m3(const void* w, int32_t N, int32_t K, uint8_t* 
 
 /* Quantise rows: v = x[r, k] * col_scale[k] * row_scale[r] (each product one
  * binary32 rounding, in that order; a NULL vector is 1), then MX blocks.
- * x bf16 or fp32 (x_is_fp32) [M, K].  Weights: col_scale = AWQ s of the input
+ * x [M, K] in the format x_format: 0 bf16 (weights), 1 fp32, 2 fp16 (the
+ * attention output of the MXFP4 band).  Weights: col_scale = AWQ s of the input
  * channels, row_scale = 1/s of the down projection on the up rows.
  * Activations: col_scale = 1/s.  HR_EINVAL on sizes or ld_scales < M. */
-hr_status hr_quantize_mxfp4(const void* x, int32_t x_is_fp32, int32_t M, int32_t K, const float* col_scale,
+hr_status hr_quantize_mxfp4(const void* x, int32_t x_format, int32_t M, int32_t K, const float* col_scale,
                             const float* row_scale, uint8_t* codes, uint8_t* scales, int32_t ld_scales,
                             hipStream_t stream);
 
@@ -136,6 +165,8 @@ hr_status hr_rmsnorm_mxfp4(const float* h, int32_t T, int32_t D, const void* nor
                            hipStream_t stream);
 
 /* MXFP4 GEMM y = x w^T with fp32 accumulation of the scaled E2M1 products.
+ *  ws / ws_bytes: the split-K partials of HR_EPI_RESIDUAL, as for hr_linear
+ *  (hr_linear_workspace_bytes(HR_MXFP4, ...)).
  *  x codes [M, K/2] with scales (ld_x_scales >= M rounded up to 256: the
  *  256-row tiles read whole scale rows; rows >= M are ignored), w codes
  *  [N, K/2] with scales (ld N).
@@ -146,7 +177,8 @@ hr_status hr_rmsnorm_mxfp4(const float* h, int32_t T, int32_t D, const void* nor
  *  multiple of 128. */
 hr_status hr_linear_mxfp4(const uint8_t* x, const uint8_t* x_scales, int32_t ld_x_scales, const uint8_t* w,
                           const uint8_t* w_scales, int32_t M, int32_t N, int32_t K, hr_epilogue epi, void* out,
-                          uint8_t* out_scales, int32_t ld_out_scales, hipStream_t stream);
+                          uint8_t* out_scales, int32_t ld_out_scales, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

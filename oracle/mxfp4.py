@@ -190,13 +190,8 @@ def mx_linear(pk: dict):
     return lin
 
 
-def mx_layer(m, lw: dict, pk: dict, batch: dict, h, kc, vc, causal: bool = True, used_keys=None,
-             store=None) -> np.ndarray:
+def mx_layer(m, lw: dict, pk: dict, batch: dict, h, kc, vc, causal: bool = True, used_keys=None) -> np.ndarray:
     """The layer with O, gate/up and down on MXFP4 operands (QKV and attention
-    unchanged).  ``store`` (e.g. ``prefill.round_bf16``) rounds the bf16 part of
-    the chain where a bf16 implementation stores it (norm output, QKV, q / k,
-    P, attention output): the attention output is quantised from its stored
-    value, the FFN inputs straight from their full-precision values."""
+    unchanged): each GEMM input is quantised from its full-precision value."""
     from .prefill import prefill_layer
-    return prefill_layer(m, lw, batch, h, kc, vc, causal, used_keys, linear=mx_linear(pk), store=store,
-                         store_ffn=False)
+    return prefill_layer(m, lw, batch, h, kc, vc, causal, used_keys, linear=mx_linear(pk))

@@ -34,7 +34,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .numerics import bf16_to_f64, f32_to_bf16
+from .numerics import bf16_to_f64
 
 
 # ------------------------------------------------------------------ elementwise pieces
@@ -74,21 +74,15 @@ def softmax(scores: np.ndarray) -> np.ndarray:
     return e / np.sum(e, axis=-1, keepdims=True)
 
 
-def attention(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, visible: np.ndarray,
-              store=None) -> np.ndarray:
+def attention(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, visible: np.ndarray) -> np.ndarray:
     """One head: q[n, d] over keys[j, d] / vals[j, d]; ``visible[i, j]`` masks.
 
     o[i] = sum_j softmax_j(q_i . k_j / sqrt(d)) v_j over the visible j.
-    ``store`` (diagnostic) rounds the unnormalised probabilities exp(s - max)
-    before they weight the values; the normaliser keeps the unrounded sum.
     """
     d = q.shape[-1]
     s = q @ keys.T / np.sqrt(d)
     s = np.where(visible, s, -np.inf)
-    if store is None:
-        return softmax(s) @ vals
-    e = np.exp(s - np.max(s, axis=-1, keepdims=True))
-    return (store(e) @ vals) / np.sum(e, axis=-1, keepdims=True)
+    return softmax(s) @ vals
 
 
 # ------------------------------------------------------------------ weights
@@ -103,20 +97,9 @@ def dense(x: np.ndarray, w: np.ndarray) -> np.ndarray:
 
 
 # ------------------------------------------------------------------ one layer
-def _identity(x):
-    return x
-
-
-def round_bf16(x: np.ndarray) -> np.ndarray:
-    """x rounded to the nearest bfloat16 value (ties to even), as float64."""
-    x = np.asarray(x, dtype=np.float64)
-    f32 = x.astype(np.float32)
-    return bf16_to_f64(f32_to_bf16(f32))
-
-
 def prefill_layer(m, lw: dict, batch: dict, h: np.ndarray, kc: np.ndarray, vc: np.ndarray,
                   causal: bool = True, used_keys=None, taps: dict | None = None,
-                  linear=None, store=None, store_ffn: bool = True) -> np.ndarray:
+                  linear=None) -> np.ndarray:
     """One decoder layer over a packed batch; returns the new residual h[T, D].
 
     ``m``: model shapes (hidden, n_q_heads, n_kv_heads, head_dim, ffn, rope_theta,
@@ -127,25 +110,18 @@ def prefill_layer(m, lw: dict, batch: dict, h: np.ndarray, kc: np.ndarray, vc: n
     sees [0, used_keys[s]) and rows i >= used_keys[s] are pads (not written to
     the cache, outputs unspecified).  ``taps`` (optional dict) receives the four
     GEMM inputs (``qkv``, ``o``, ``gu``, ``dn``).  ``linear(site, x, W)`` replaces
-    the plain product (used by the FP8 fake-quant diagnostic).  ``store`` (e.g.
-    ``round_bf16``) is applied wherever a bf16 implementation stores an
-    intermediate: the two norm outputs, the QKV product, the normed and rotated
-    q / k, the attention probabilities fed to P.V, the attention output and the
-    SwiGLU product (a diagnostic of bf16 storage; default: no rounding);
-    ``store_ffn=False`` leaves the two FFN inputs (post-attention norm output,
-    SwiGLU product) unrounded, for a chain that quantises them from fp32.
+    the plain product (used by the FP8 and MXFP4 fake-quant diagnostics).
     """
     D, Hq, Hkv, d = m.hidden, m.n_q_heads, m.n_kv_heads, m.head_dim
     F, eps, theta = m.ffn, m.rms_eps, m.rope_theta
     lin = linear or (lambda site, x, w: dense(x, w))
-    st = store or _identity
     cu = np.asarray(batch["cu_seqlens"])
     cap = int(batch["capacity"])
     group = Hq // Hkv
     h = np.array(h, dtype=np.float64, copy=True)
     T = h.shape[0]
-    x_in = st(rms_norm(h, lw["in_norm"], eps))
-    qkv = st(lin("qkv", x_in, lw["w_qkv"]))
+    x_in = rms_norm(h, lw["in_norm"], eps)
+    qkv = lin("qkv", x_in, lw["w_qkv"])
     q = qkv[:, :Hq * d].reshape(T, Hq, d)
     k = qkv[:, Hq * d:(Hq + Hkv) * d].reshape(T, Hkv, d)
     v = qkv[:, (Hq + Hkv) * d:].reshape(T, Hkv, d)
@@ -160,8 +136,8 @@ def prefill_layer(m, lw: dict, batch: dict, h: np.ndarray, kc: np.ndarray, vc: n
         sp = int(batch["start_pos"][s])
         base = int(batch["cache_slot"][s]) * cap
         pos = sp + np.arange(n)
-        qs = st(apply_rope(q[a:b], pos, theta))
-        ks = st(apply_rope(k[a:b], pos, theta))
+        qs = apply_rope(q[a:b], pos, theta)
+        ks = apply_rope(k[a:b], pos, theta)
         n_write = n if causal else int(used_keys[s])
         kc[base + sp: base + sp + n_write] = ks[:n_write]
         vc[base + sp: base + sp + n_write] = v[a:a + n_write]
@@ -173,14 +149,12 @@ def prefill_layer(m, lw: dict, batch: dict, h: np.ndarray, kc: np.ndarray, vc: n
             visible = np.ones((n, n_keys), dtype=bool)
         for hh in range(Hq):
             g = hh // group
-            o[a:b, hh] = attention(qs[:, hh], kc[base:base + n_keys, g], vc[base:base + n_keys, g],
-                                   visible, st)
-    o = st(o.reshape(T, Hq * d))
+            o[a:b, hh] = attention(qs[:, hh], kc[base:base + n_keys, g], vc[base:base + n_keys, g], visible)
+    o = o.reshape(T, Hq * d)
     h = h + lin("o", o, lw["w_o"])
-    st_ffn = st if store_ffn else _identity
-    x_post = st_ffn(rms_norm(h, lw["post_norm"], eps))
+    x_post = rms_norm(h, lw["post_norm"], eps)
     gu = lin("gu", x_post, lw["w_gu"])
-    act = st_ffn(silu(gu[:, :F]) * gu[:, F:])
+    act = silu(gu[:, :F]) * gu[:, F:]
     h = h + lin("dn", act, lw["w_down"])
     if taps is not None:
         taps.update(qkv=x_in, o=o, gu=x_post, dn=act)

@@ -8,6 +8,7 @@ import numpy as np
 import torch
 
 BF16_NAN = 0x7FC0
+F16_NAN = 0x7E00
 
 
 def log(msg: str) -> None:
@@ -18,6 +19,16 @@ def log(msg: str) -> None:
 def dev_bf16(bits: np.ndarray) -> torch.Tensor:
     t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
     return t.view(torch.bfloat16).to("cuda")
+
+
+def dev_f16(a: np.ndarray) -> torch.Tensor:
+    """float16 array (values already rounded by numpy, nearest even) -> device."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float16)).to("cuda")
+
+
+def seeded_f16(shape, seed, std=1.0) -> np.ndarray:
+    """Seeded normal draws rounded to fp16 (the activation format of the bf16-weight band)."""
+    return (np.random.default_rng(seed).standard_normal(shape) * std).astype(np.float16)
 
 
 def dev_u8(a: np.ndarray) -> torch.Tensor:
@@ -37,8 +48,15 @@ def f64_of_bf16(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
+f64_of = f64_of_bf16      # any float tensor (bf16, fp16, fp32) -> float64 host array
+
+
 def poisoned_bf16(shape) -> torch.Tensor:
     return torch.full(shape, BF16_NAN, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+
+
+def poisoned_f16(shape) -> torch.Tensor:
+    return torch.full(shape, F16_NAN, dtype=torch.int16, device="cuda").view(torch.float16)
 
 
 def cosine(a, b) -> float:
@@ -62,3 +80,9 @@ def assert_bf16_close(got, ref, rel=2.0 ** -8, abs_=1e-6, what=""):
     bad = err > bound
     assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} elements out of tolerance; "
                            f"worst err {float(err.max()):.3g}")
+
+
+def assert_f16_close(got, ref, rel=2.0 ** -10, abs_=1e-7, what=""):
+    """An fp16 store (half-ulp 2^-11 relative; 2^-25 absolute in the subnormal
+    range) of a value computed in fp32."""
+    assert_bf16_close(got, ref, rel=rel, abs_=abs_, what=what)

@@ -186,13 +186,32 @@ def test_codebook_misaligned_embedding_refused():
 def test_linear_validation():
     lib = H.lib()
     # an operand of 4 GB or more (32-bit byte offsets in the tiled GEMM)
-    assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_BF16, 65536, 64, 32768, 0, FAKE, 0.0, None) == \
+    assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_BF16, 65536, 64, 32768, 0, FAKE, 0.0, None, 0, None) == \
         H.HR_EUNSUPPORTED
-    assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_BF16, 4, 16, 48, 0, FAKE, 0.0, None) == H.HR_EUNSUPPORTED
-    assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_BF16, 4, 24, 64, 0, FAKE, 0.0, None) == H.HR_EUNSUPPORTED
-    assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_FP8_E4M3, 4, 16, 128, 0, FAKE, 0.0, None) == H.HR_EINVAL
-    assert lib.hr_linear(FAKE, FAKE, FAKE, 1.0, H.HR_FP8_E4M3, 4, 32, 128, 2, FAKE, 0.0, None) == H.HR_EINVAL
-    assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_BF16, 4, 16, 64, 7, FAKE, 0.0, None) == H.HR_EINVAL
+    assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_BF16, 4, 16, 48, 0, FAKE, 0.0, None, 0, None) == H.HR_EUNSUPPORTED
+    assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_BF16, 4, 24, 64, 0, FAKE, 0.0, None, 0, None) == H.HR_EUNSUPPORTED
+    assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_FP8_E4M3, 4, 16, 128, 0, FAKE, 0.0, None, 0, None) == H.HR_EINVAL
+    assert lib.hr_linear(FAKE, FAKE, FAKE, 1.0, H.HR_FP8_E4M3, 4, 32, 128, 2, FAKE, 0.0, None, 0, None) == H.HR_EINVAL
+    assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_BF16, 4, 16, 64, 7, FAKE, 0.0, None, 0, None) == H.HR_EINVAL
+    # a residual projection that splits K needs the partial workspace
+    assert H.hr_linear_workspace_bytes(H.HR_BF16, 13, 2560, 9728, H.HR_EPI_RESIDUAL) > 0
+    assert H.hr_linear_workspace_bytes(H.HR_BF16, 13, 2560, 9728, H.HR_EPI_F32) == 0
+    assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_BF16, 13, 2560, 9728, 1, FAKE, 0.0, None, 0, None) == \
+        H.HR_EWORKSPACE
+    assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_BF16, 13, 2560, 9728, 1, FAKE, 0.0, FAKE, 100, None) == \
+        H.HR_EWORKSPACE
+
+
+def test_residual_rmsnorm_validation():
+    lib = H.lib()
+    f = lib.hr_residual_rmsnorm
+    assert f(FAKE, FAKE, -1, 4, 256, FAKE, 1e-6, FAKE, H.HR_F16, 1.0, None) == H.HR_EINVAL
+    assert f(FAKE, None, 2, 4, 256, FAKE, 1e-6, FAKE, H.HR_F16, 1.0, None) == H.HR_EINVAL      # partials missing
+    assert f(FAKE, FAKE, 2, 4, 250, FAKE, 1e-6, FAKE, H.HR_F16, 1.0, None) == H.HR_EINVAL      # D % 8
+    assert f(FAKE, FAKE, 2, 4, 256, FAKE, 1e-6, FAKE, H.HR_BF16, 1.0, None) == H.HR_EINVAL     # x fp16 or e4m3
+    assert f(FAKE, FAKE, 2, 4, 256, FAKE, 1e-6, FAKE, H.HR_FP8_E4M3, 0.0, None) == H.HR_EINVAL
+    assert f(FAKE, FAKE, 2, 4, 256, None, 1e-6, FAKE, H.HR_F16, 1.0, None) == H.HR_EINVAL      # norm weight
+    assert f(MISALIGNED, FAKE, 2, 4, 256, FAKE, 1e-6, FAKE, H.HR_F16, 1.0, None) == H.HR_EALIGN
 
 
 def test_codebook_misaligned_logits_refused():
@@ -229,20 +248,24 @@ def test_mxfp4_validation():
     lib = H.lib()
     # the bf16 / e4m3 entries refuse the MXFP4 type
     assert lib.hr_rmsnorm(FAKE, 4, 256, FAKE, 1e-6, FAKE, H.HR_MXFP4, 1.0, None) == H.HR_EINVAL
+    # norm outputs are fp16 (the bf16-weight band) or e4m3
+    assert lib.hr_rmsnorm(FAKE, 4, 256, FAKE, 1e-6, FAKE, H.HR_BF16, 1.0, None) == H.HR_EINVAL
     # K not a multiple of 128; ld below M
     assert lib.hr_quantize_mxfp4(FAKE, 0, 4, 96, None, None, FAKE, FAKE, 4, None) == H.HR_EINVAL
     assert lib.hr_quantize_mxfp4(FAKE, 0, 8, 128, None, None, FAKE, FAKE, 4, None) == H.HR_EINVAL
     assert lib.hr_rmsnorm_mxfp4(FAKE, 4, 200, FAKE, 1e-6, None, FAKE, FAKE, 4, None) == H.HR_EINVAL
     lin = lib.hr_linear_mxfp4
     # x scales must cover the 256-row tiles; N multiple of 256; bf16 epilogue refused
-    assert lin(FAKE, FAKE, 100, FAKE, FAKE, 100, 256, 256, H.HR_EPI_RESIDUAL, FAKE, None, 0, None) == H.HR_EINVAL
-    assert lin(FAKE, FAKE, 256, FAKE, FAKE, 100, 384, 256, H.HR_EPI_RESIDUAL, FAKE, None, 0, None) == \
+    assert lin(FAKE, FAKE, 100, FAKE, FAKE, 100, 256, 256, H.HR_EPI_RESIDUAL, FAKE, None, 0, None, 0, None) == H.HR_EINVAL
+    assert lin(FAKE, FAKE, 256, FAKE, FAKE, 100, 384, 256, H.HR_EPI_RESIDUAL, FAKE, None, 0, None, 0, None) == \
         H.HR_EUNSUPPORTED
-    assert lin(FAKE, FAKE, 256, FAKE, FAKE, 100, 256, 256, H.HR_EPI_BF16, FAKE, None, 0, None) == H.HR_EINVAL
-    assert lin(FAKE, FAKE, 256, FAKE, FAKE, 100, 512, 256, H.HR_EPI_SWIGLU, FAKE, None, 0, None) == H.HR_EINVAL
-    assert lin(FAKE, FAKE, 256, FAKE, FAKE, 100, 512, 256, H.HR_EPI_SWIGLU, FAKE, FAKE, 128, None) == H.HR_EINVAL
-    assert lin(FAKE, FAKE, 256, FAKE, FAKE, 100, 512, 200, H.HR_EPI_SWIGLU, FAKE, FAKE, 256, None) == H.HR_EINVAL
-    assert lin(FAKE + 4, FAKE, 256, FAKE, FAKE, 100, 512, 256, H.HR_EPI_SWIGLU, FAKE, FAKE, 256, None) == \
+    assert lin(FAKE, FAKE, 256, FAKE, FAKE, 100, 256, 256, H.HR_EPI_F32, FAKE, None, 0, None, 0, None) == H.HR_EINVAL
+    # the quantiser's source format is 0 (bf16), 1 (fp32) or 2 (fp16)
+    assert lib.hr_quantize_mxfp4(FAKE, 3, 4, 128, None, None, FAKE, FAKE, 4, None) == H.HR_EINVAL
+    assert lin(FAKE, FAKE, 256, FAKE, FAKE, 100, 512, 256, H.HR_EPI_SWIGLU, FAKE, None, 0, None, 0, None) == H.HR_EINVAL
+    assert lin(FAKE, FAKE, 256, FAKE, FAKE, 100, 512, 256, H.HR_EPI_SWIGLU, FAKE, FAKE, 128, None, 0, None) == H.HR_EINVAL
+    assert lin(FAKE, FAKE, 256, FAKE, FAKE, 100, 512, 200, H.HR_EPI_SWIGLU, FAKE, FAKE, 256, None, 0, None) == H.HR_EINVAL
+    assert lin(FAKE + 4, FAKE, 256, FAKE, FAKE, 100, 512, 256, H.HR_EPI_SWIGLU, FAKE, FAKE, 256, None, 0, None) == \
         H.HR_EALIGN
 
 
@@ -257,7 +280,7 @@ def test_mxfp4_validation():
 def test_attention_chunked_validation(ct, slots, ws, ws_bytes, status):
     lib = H.lib()
     d, b, k = dims(), batch([300]), kv()
-    st = lib.hr_attention_chunked(ctypes.byref(d), ctypes.byref(b.c), FAKE, ctypes.byref(k), FAKE, H.HR_BF16, 1.0,
+    st = lib.hr_attention_chunked(ctypes.byref(d), ctypes.byref(b.c), FAKE, ctypes.byref(k), FAKE, H.HR_F16, 1.0,
                                   ct, slots, ws, ws_bytes, None)
     assert st == status, (st, H.hr_last_error())
     assert H.hr_attention_chunked_workspace_bytes(d, 300, 4) >= 4 * 300 * 32 * (128 * 4 + 8)
@@ -267,6 +290,7 @@ def test_attention_chunked_validation(ct, slots, ws, ws_bytes, status):
     ("continuation", H.HR_EUNSUPPORTED),        # a sequence past position 0
     ("long", H.HR_EUNSUPPORTED),                # 33 rows
     ("out_type", H.HR_EINVAL),
+    ("out_bf16", H.HR_EINVAL),                  # activations of the bf16-weight band are fp16
     ("fp8_scale", H.HR_EINVAL),
     ("no_out", H.HR_EINVAL),
 ])
@@ -274,7 +298,7 @@ def test_qknorm_rope_attention_validation(case, status):
     lib = H.lib()
     d, k = dims(), kv()
     b = batch([13, 33] if case == "long" else [13, 5], starts=[0, 7] if case == "continuation" else None)
-    out_type = {"out_type": H.HR_MXFP4, "fp8_scale": H.HR_FP8_E4M3}.get(case, H.HR_BF16)
+    out_type = {"out_type": H.HR_MXFP4, "fp8_scale": H.HR_FP8_E4M3, "out_bf16": H.HR_BF16}.get(case, H.HR_F16)
     scale = 0.0 if case == "fp8_scale" else 1.0
     out = None if case == "no_out" else FAKE
     st = lib.hr_qknorm_rope_attention(ctypes.byref(d), ctypes.byref(b.c), FAKE, FAKE, FAKE, ctypes.byref(k), out,

@@ -1,12 +1,10 @@
 """hr_prefill_stack captured in a HIP graph (torch.cuda.CUDAGraph on a side
 stream) and replayed: every replay, with eager work and synchronisations of
-the program in between, must give what the eager call gives.  The library
-records kernels only (no memset nodes); the residual projections add split-K
-partials with fp32 atomics, whose order varies, so hidden states, logits and
-the caches of later layers are held to the bar of two samples of that rounding
-noise (cosine >= 0.9999, max |diff| <= 0.1 per layer); the first layer's KV
-cache, which depends on the embedding rows alone, must be equal bit for bit,
-and no row past the prompt may be written.
+the program in between, must give what the eager call gives, bit for bit:
+the library records kernels only (no memset nodes) and every reduction runs in
+a fixed order (split-K partials summed in split order), so hidden state,
+logits and every layer's KV cache repeat exactly; no row past the prompt may
+be written.
 """
 import numpy as np
 import pytest
@@ -26,7 +24,7 @@ def H():
 @pytest.mark.parametrize("P", [13, 512])
 def test_stack_graph_replays_match_eager(H, P):
     import torch
-    from gpu_util import bits_of, cosine, dev, dev_bf16, log, max_abs
+    from gpu_util import bits_of, dev, dev_bf16, log, max_abs
     from model_util import dims_of, kv_cache, upload_layer, workspace
     m = synth.QWEN3_4B
     n_layers = 2
@@ -72,18 +70,11 @@ def test_stack_graph_replays_match_eager(H, P):
         torch.cuda.synchronize()
         hg, lg = h.cpu().numpy(), logits.cpu().numpy()
         assert np.all(np.isfinite(hg)) and np.all(np.isfinite(lg)), r
-        ch, ah = cosine(hg, h_ref), max_abs(hg, h_ref)
-        cl, al = cosine(lg, l_ref), max_abs(lg, l_ref)
-        log(f"  replay {r}: hidden cos={ch:.8f} max={ah:.3g}; logits cos={cl:.8f} max={al:.3g}")
-        assert ch >= 1.0 - 1e-4 * n_layers and ah <= 0.1 * n_layers, (r, ch, ah)
-        assert cl >= 1.0 - 1e-4 * n_layers and al <= 0.1 * n_layers, (r, cl, al)
-        # layer 0's K/V come from the embedding rows alone: the same bits; later
-        # layers read a hidden state that went through the atomics
-        np.testing.assert_array_equal(bits_of(caches[0][0]), kv_ref[0][0])
-        np.testing.assert_array_equal(bits_of(caches[0][1]), kv_ref[0][1])
-        for (k, v), (kr, vr) in list(zip(caches, kv_ref))[1:]:
+        log(f"  replay {r}: hidden max diff {max_abs(hg, h_ref):.3g}; logits max diff {max_abs(lg, l_ref):.3g}")
+        np.testing.assert_array_equal(hg, h_ref)
+        np.testing.assert_array_equal(lg, l_ref)
+        for (k, v), (kr, vr) in zip(caches, kv_ref):
             for t, ref in ((k, kr), (v, vr)):
-                got = t[:P].float().cpu().numpy()
-                exp = torch.from_numpy(ref[:P].view(np.int16)).view(torch.bfloat16).float().numpy()
-                assert cosine(got, exp) >= 0.9999 and max_abs(got, exp) <= 0.1, r
-                assert np.all(bits_of(t)[P:] == 0x7FC0)
+                b_ = bits_of(t)
+                np.testing.assert_array_equal(b_[:P], ref[:P])
+                assert np.all(b_[P:] == 0x7FC0)

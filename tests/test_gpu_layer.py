@@ -1,16 +1,8 @@
 """hr_prefill_layer / hr_prefill_stack on the GPU against the float64 oracle.
 
-bf16, per layer, for the hidden state and every written K/V cache row:
-  * cosine >= 0.9999 against the exact oracle;
-  * max |err| against the exact oracle <= max(3e-2, 1.5 x the distance of the
-    oracle run with bf16 rounding at the kernels' storage points (norm
-    outputs, QKV, q/k, P, attention output, SwiGLU product) from the exact
-    oracle).  Rounding the GEMM inputs to bf16 alone costs about 0.026 on the
-    4B layer at P=13 and the whole bf16 chain 0.038 (0.044 at 200 rows), so
-    3e-2 is below what bf16 operands reach on these inputs; the GPU's own
-    rounding is a different sample of the same noise (fp32 values reach
-    different near-ties than float64 ones), so it is held to the same scale,
-    not to the emulation element by element.  Measured values are logged.
+bf16 weights (the band computes with fp16 activations), per layer, for the
+hidden state and every written K/V cache row, against the exact float64
+oracle: cosine >= 0.9999 and max |err| <= 3e-2.  Measured values are logged.
 Cache rows outside the batch stay NaN.
 FP8: the GPU's cosine against the unquantised layer must be no worse (minus
 1e-3) than the oracle's fake-quant layer's (same scales, same packed weights:
@@ -48,14 +40,9 @@ def check(name, got, ref, cos_min=COS_MIN, abs_max=ABS_MAX):
     assert a <= abs_max, f"{name}: max abs {a}"
 
 
-def check_hidden(name, got, exact, emul):
-    """The three bf16 checks of the module docstring."""
-    from gpu_util import cosine, log, max_abs
-    c, a, e, floor = cosine(got, exact), max_abs(got, exact), max_abs(got, emul), max_abs(emul, exact)
-    log(f"  {name}: cos={c:.7f} max_abs={a:.3g} vs_bf16_chain={e:.3g} bf16_chain_floor={floor:.3g}")
-    assert np.all(np.isfinite(got)), f"{name}: non-finite"
-    assert c >= COS_MIN, f"{name}: cosine {c}"
-    assert a <= max(ABS_MAX, 1.5 * floor), f"{name}: max abs {a} (floor {floor})"
+def check_hidden(name, got, exact):
+    """The bf16-band bars of the module docstring."""
+    check(name, got, exact)
 
 
 def run_gpu_layer(H, m, bits, lens, starts, slots, cap, h0, causal=True, used=None, caches=None,
@@ -82,12 +69,12 @@ def run_gpu_layer(H, m, bits, lens, starts, slots, cap, h0, causal=True, used=No
     return h.cpu().numpy().astype(np.float64), kc, vc
 
 
-def oracle_layer(m, bits, lens, starts, slots, cap, h0, causal=True, used=None, caches=None, store=None):
+def oracle_layer(m, bits, lens, starts, slots, cap, h0, causal=True, used=None, caches=None):
     n_slots = max(slots) + 1
     kc, vc = caches if caches is not None else op.new_cache(m, n_slots, cap)
     b = {"cu_seqlens": np.concatenate([[0], np.cumsum(lens)]), "start_pos": starts, "cache_slot": slots,
          "capacity": cap}
-    h = op.prefill_layer(m, op.widen_layer(bits), b, h0, kc, vc, causal, used, store=store)
+    h = op.prefill_layer(m, op.widen_layer(bits), b, h0, kc, vc, causal, used)
     return h, kc, vc
 
 
@@ -105,9 +92,14 @@ CASES = [
     ("layer_d2560_p6", synth.QWEN3_4B, [6], [0], [0], 2048),
     ("layer_d2560_p13", synth.QWEN3_4B, [13], [0], [0], 2048),
     ("layer_d2560_varlen_t200", synth.QWEN3_4B, [100, 37, 63], [0, 0, 0], [1, 2, 0], 128),
+    # 17-64 and 65-128 rows: the small-M tiles of every projection (down at K 9728)
+    ("layer_d2560_p40", synth.QWEN3_4B, [40], [0], [0], 64),
+    ("layer_d2560_p128", synth.QWEN3_4B, [128], [0], [0], 128),
     # the P = 512 prefill of the throughput measurement (256 x 256 gate/up tiles,
     # two wave groups per attention block)
     ("layer_d2560_p512", synth.QWEN3_4B, [512], [0], [0], 512),
+    # above 1024 rows: the large-M tiles (varlen batches)
+    ("layer_d2560_varlen_t1100", synth.QWEN3_4B, [600, 500], [0, 0], [0, 1], 600),
 ]
 
 
@@ -120,8 +112,7 @@ def test_layer_bf16(H, name, m, lens, starts, slots, cap):
     h0 = nx.bf16_to_f64(synth.embed_rows(m, ids))
     hg, kcg, vcg = run_gpu_layer(H, m, bits, lens, starts, slots, cap, h0)
     hr, kcr, vcr = oracle_layer(m, bits, lens, starts, slots, cap, h0)
-    he, _, _ = oracle_layer(m, bits, lens, starts, slots, cap, h0, store=op.round_bf16)
-    check_hidden("hidden", hg, hr, he)
+    check_hidden("hidden", hg, hr)
     compare_caches(kcg, vcg, kcr, vcr)
 
 
@@ -141,10 +132,7 @@ def test_layer_prefill_then_continuation(H):
     g2, kcg, vcg = run_gpu_layer(H, m, bits, [3], [10], [0], cap, h0[10:], caches=caches)
     r1, *_ = oracle_layer(m, bits, [10], [0], [0], cap, h0[:10], caches=ocaches)
     r2, kcr, vcr = oracle_layer(m, bits, [3], [10], [0], cap, h0[10:], caches=ocaches)
-    ecaches = op.new_cache(m, 1, cap)
-    e1, *_ = oracle_layer(m, bits, [10], [0], [0], cap, h0[:10], caches=ecaches, store=op.round_bf16)
-    e2, *_ = oracle_layer(m, bits, [3], [10], [0], cap, h0[10:], caches=ecaches, store=op.round_bf16)
-    check_hidden("hidden", np.concatenate([g1, g2]), np.concatenate([r1, r2]), np.concatenate([e1, e2]))
+    check_hidden("hidden", np.concatenate([g1, g2]), np.concatenate([r1, r2]))
     compare_caches(kcg, vcg, kcr, vcr)
 
 

@@ -1,13 +1,17 @@
-"""hr_prefill_layer / hr_prefill_stack at small batches against the same layer
-composed from the step-level entry points of include/hr_ops.h (one call per
-step), on new tokens every repetition.
+"""hr_prefill_layer / hr_prefill_stack against the same layer composed from the
+step-level entry points of include/hr_ops.h (one call per step), on new tokens
+every repetition.
 
-Both run the same kernels; the residual projections add split-K partials into
-h with fp32 atomics, whose order varies, so the two are two samples of the
-bf16/fp32 rounding noise (0.04-0.05 from the exact layer on this layer): the
-bar is cosine >= 0.9999 and max |diff| <= 0.1 per layer.  A layer call that
-skipped, reordered or mis-addressed a step (a stale workspace region, a cache
-row written to the wrong slot) shows up as an O(1) difference.
+Both run the same kernels in the same configuration, and every reduction is in
+a fixed order (the residual projections' split-K partials are summed in split
+order, no atomics), so hidden state and caches must be equal bit for bit: a
+layer call that skipped, reordered or mis-addressed a step (a stale workspace
+region, a cache row written to the wrong slot) or a result that changed from
+run to run fails.  The one exception is a decode step over long caches, where
+the layer entry splits the attention into key chunks (its workspace holds the
+partials) and the composed steps run it unsplit: there the bar is the per-layer
+bf16-band bar (cosine >= 0.9999, max |diff| <= 3e-2), and the cache rows must
+still be equal bit for bit.
 """
 import numpy as np
 import pytest
@@ -33,29 +37,40 @@ def layers(H):
     return m, [upload_layer(synth.layer_tensors(m, l)) for l in range(2)]
 
 
-def composed_layer(H, m, dims, batch, dl, h, kv, T):
-    """One layer from the step-level entries."""
+def composed_layer(H, m, dims, batch, dl, h, kv, T, fused_short=False):
+    """One layer from the step-level entries (activations fp16, QKV rows
+    fp32).  ``fused_short``: steps A3 + A4 through hr_qknorm_rope_attention,
+    the launch the layer entries take for prompts of at most 32 rows from
+    position 0 (unless every sequence has one row: a decode step)."""
     import torch
     D, F, A, NQKV = m.hidden, m.ffn, m.attn_width, m.qkv_rows
-    bf = dict(dtype=torch.bfloat16, device="cuda")
-    x, qkv = torch.empty((T, D), **bf), torch.empty((T, NQKV), **bf)
-    q, attn, act = torch.empty((T, A), **bf), torch.empty((T, A), **bf), torch.empty((T, F), **bf)
+    ws_o = H.linear_ws(H.HR_BF16, T, D, A, H.HR_EPI_RESIDUAL)
+    ws_d = H.linear_ws(H.HR_BF16, T, D, F, H.HR_EPI_RESIDUAL)
+    hf = dict(dtype=torch.float16, device="cuda")
+    x, qkv = torch.empty((T, D), **hf), torch.empty((T, NQKV), dtype=torch.float32, device="cuda")
+    q, attn, act = torch.empty((T, A), **hf), torch.empty((T, A), **hf), torch.empty((T, F), **hf)
     H.hr_rmsnorm(h, T, D, dl["in_norm"], m.rms_eps, x)
-    H.hr_linear(x, dl["w_qkv"], None, 1.0, H.HR_BF16, T, NQKV, D, H.HR_EPI_BF16, qkv)
-    H.hr_qknorm_rope_kv(dims, batch, qkv, dl["q_norm"], dl["k_norm"], q, kv)
-    H.hr_attention(dims, batch, q, kv, attn)
-    H.hr_linear(attn, dl["w_o"], None, 1.0, H.HR_BF16, T, D, A, H.HR_EPI_RESIDUAL, h)
+    H.hr_linear(x, dl["w_qkv"], None, 1.0, H.HR_BF16, T, NQKV, D, H.HR_EPI_F32, qkv)
+    if fused_short:
+        H.hr_qknorm_rope_attention(dims, batch, qkv, dl["q_norm"], dl["k_norm"], kv, attn)
+    else:
+        H.hr_qknorm_rope_kv(dims, batch, qkv, dl["q_norm"], dl["k_norm"], q, kv)
+        H.hr_attention(dims, batch, q, kv, attn)
+    H.hr_linear(attn, dl["w_o"], None, 1.0, H.HR_BF16, T, D, A, H.HR_EPI_RESIDUAL, h, ws=ws_o)
     H.hr_rmsnorm(h, T, D, dl["post_norm"], m.rms_eps, x)
     H.hr_linear(x, dl["w_gu"], None, 1.0, H.HR_BF16, T, 2 * F, D, H.HR_EPI_SWIGLU, act)
-    H.hr_linear(act, dl["w_down"], None, 1.0, H.HR_BF16, T, D, F, H.HR_EPI_RESIDUAL, h)
+    H.hr_linear(act, dl["w_down"], None, 1.0, H.HR_BF16, T, D, F, H.HR_EPI_RESIDUAL, h, ws=ws_d)
 
 
-def close(name, got, ref, n_layers=1):
+def close(name, got, ref, exact=True):
     from gpu_util import cosine, log, max_abs
     c, a = cosine(got, ref), max_abs(got, ref)
     log(f"  {name}: cos={c:.8f} max_abs={a:.3g}")
     assert np.all(np.isfinite(got)), name
-    assert c >= 1.0 - 1e-4 * n_layers and a <= 0.1 * n_layers, (name, c, a)
+    if exact:
+        np.testing.assert_array_equal(np.asarray(got), np.asarray(ref), err_msg=name)
+    else:
+        assert c >= 0.9999 and a <= 3e-2, (name, c, a)
 
 
 @pytest.mark.parametrize("T", [1, 13, 40, 64, 512])
@@ -79,7 +94,7 @@ def test_layer_matches_composed_steps(H, layers, T):
         kf, vf = kv_cache(m, 1, cap)
         kc, vc = kv_cache(m, 1, cap)
         H.hr_prefill_layer(dims, layer, b, hf, H.make_kv(kf, vf, cap, 1), ws)
-        composed_layer(H, m, dims, b, dls[0], hc, H.make_kv(kc, vc, cap, 1), T)
+        composed_layer(H, m, dims, b, dls[0], hc, H.make_kv(kc, vc, cap, 1), T, fused_short=1 < T <= 32)
         torch.cuda.synchronize()
         close("hidden", hf.cpu().numpy(), hc.cpu().numpy())
         close("K cache", kf[:T].float().cpu().numpy(), kc[:T].float().cpu().numpy())
@@ -110,9 +125,9 @@ def test_stack_two_layers_matches_composed_steps(H, layers):
         hc = dev(synth.bf16_bits_to_f32(synth.embed_rows(m, ids)))
         for l in range(2):
             kc, vc = kv_cache(m, 1, cap)
-            composed_layer(H, m, dims1, b, dls[l], hc, H.make_kv(kc, vc, cap, 1), T)
+            composed_layer(H, m, dims1, b, dls[l], hc, H.make_kv(kc, vc, cap, 1), T, fused_short=True)
         torch.cuda.synchronize()
-        close("hidden after 2 layers", h.cpu().numpy(), hc.cpu().numpy(), n_layers=2)
+        close("hidden after 2 layers", h.cpu().numpy(), hc.cpu().numpy())
 
 
 @pytest.mark.parametrize("starts,slots", [
@@ -149,7 +164,7 @@ def test_decode_layer_matches_composed_steps(H, layers, starts, slots):
         H.hr_prefill_layer(dims, layer, b, hf, H.make_kv(kf, vf, cap, B), ws)
         composed_layer(H, m, dims, b, dls[0], hc, H.make_kv(kc, vc, cap, B), B)
         torch.cuda.synchronize()
-        close("hidden", hf.cpu().numpy(), hc.cpu().numpy())
+        close("hidden", hf.cpu().numpy(), hc.cpu().numpy(), exact=starts[-1] < 64)
         np.testing.assert_array_equal(bits_of(kf), bits_of(kc))
         np.testing.assert_array_equal(bits_of(vf), bits_of(vc))
         new_rows = [slot * cap + sp for sp, slot in zip(starts, slots)]

@@ -1,6 +1,8 @@
 """Each prefill step on the GPU against the float64 oracle, on seeded inputs,
 through the C ABI (include/hr_ops.h).  Sizes span several tiles with ragged
-tails; caches and outputs are NaN-poisoned to catch unwritten or stray writes."""
+tails; caches and outputs are NaN-poisoned to catch unwritten or stray writes.
+Activation formats of the bf16-weight band: norm outputs, q, the attention
+output and the SwiGLU product fp16; merged QKV rows fp32; caches bf16."""
 import numpy as np
 import pytest
 
@@ -27,27 +29,27 @@ def seeded_bf16(shape, key, std=1.0, mean=0.0):
 @pytest.mark.parametrize("T,D", [(13, 2560), (300, 256), (1, 2560)])
 def test_embed_rmsnorm_and_rmsnorm(H, T, D):
     import torch
-    from gpu_util import assert_bf16_close, dev, dev_bf16, f64_of_bf16, log
+    from gpu_util import assert_f16_close, dev, dev_bf16, f64_of, log
     log(f"embed_rmsnorm T={T} D={D}")
     vocab = 4096
     E = seeded_bf16((vocab, D), (1, D), 0.02)
     w = seeded_bf16((D,), (2, D), 0.1, 1.0)
     ids = np.random.default_rng(T).integers(0, vocab, T).astype(np.int32)
     h = torch.empty((T, D), dtype=torch.float32, device="cuda")
-    x = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    x = torch.empty((T, D), dtype=torch.float16, device="cuda")
     H.hr_embed_rmsnorm(dev(ids), dev_bf16(E), vocab, None, T, D, dev_bf16(w), 1e-6, h, x)
     torch.cuda.synchronize()
     rows = nx.bf16_to_f64(E[ids])
     np.testing.assert_array_equal(h.cpu().numpy().astype(np.float64), rows)     # exact widening
     ref = op.rms_norm(rows, nx.bf16_to_f64(w), 1e-6)
-    assert_bf16_close(f64_of_bf16(x), ref, what="embed_rmsnorm x")
+    assert_f16_close(f64_of(x), ref, what="embed_rmsnorm x")
     # plain RMSNorm of an fp32 residual with larger spread
     hr = (np.random.default_rng(5).standard_normal((T, D)) * 7).astype(np.float32)
-    x2 = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    x2 = torch.empty((T, D), dtype=torch.float16, device="cuda")
     H.hr_rmsnorm(dev(hr), T, D, dev_bf16(w), 1e-6, x2)
     torch.cuda.synchronize()
-    assert_bf16_close(f64_of_bf16(x2), op.rms_norm(hr.astype(np.float64), nx.bf16_to_f64(w), 1e-6),
-                      what="rmsnorm x")
+    assert_f16_close(f64_of(x2), op.rms_norm(hr.astype(np.float64), nx.bf16_to_f64(w), 1e-6),
+                     what="rmsnorm x")
 
 
 def test_rmsnorm_fp8_output(H):
@@ -73,7 +75,7 @@ def test_rmsnorm_fp8_output(H):
 # ----------------------------------------------------------------------------- A2 / A5 / A7 / A8
 def _linear_case(H, M, N, K, epi, fp8=False, seed=0):
     import torch
-    from gpu_util import dev, dev_bf16, dev_u8, f64_of_bf16, log
+    from gpu_util import dev, dev_bf16, dev_f16, dev_u8, f64_of, log, seeded_f16
     log(f"linear M={M} N={N} K={K} epi={epi} fp8={fp8}")
     rng = np.random.default_rng(seed)
     if fp8:
@@ -87,24 +89,30 @@ def _linear_case(H, M, N, K, epi, fp8=False, seed=0):
         dx, dw, dws = dev_u8(codes_x), dev_u8(codes_w), dev(ws)
         wtype = H.HR_FP8_E4M3
     else:
-        xb = seeded_bf16((M, K), (10, M, K, seed), 1.0)
+        # fp16 activations (seeded normals rounded to fp16) times bf16 weights
+        xh = seeded_f16((M, K), 1000 * M + K + seed, 1.0)
         wb = seeded_bf16((N, K), (11, N, K, seed), 0.02)
-        xv, wv = nx.bf16_to_f64(xb), nx.bf16_to_f64(wb)
-        dx, dw, dws, xs = dev_bf16(xb), dev_bf16(wb), None, 1.0
+        xv, wv = xh.astype(np.float64), nx.bf16_to_f64(wb)
+        dx, dw, dws, xs = dev_f16(xh), dev_bf16(wb), None, 1.0
         wtype = H.HR_BF16
     ref = xv @ wv.T
-    if epi == H.HR_EPI_BF16:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    if epi == H.HR_EPI_F32:
+        out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
         H.hr_linear(dx, dw, dws, xs, wtype, M, N, K, epi, out)
         torch.cuda.synchronize()
-        got = f64_of_bf16(out)
-        scale = np.sqrt(np.sum(np.abs(xv) ** 2, 1))[:, None] * np.sqrt(np.sum(wv ** 2, 1))[None, :]
+        got = out.cpu().numpy().astype(np.float64)
         err = np.abs(got - ref)
-        assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-5 * scale), float(err.max())
+        if fp8:
+            absdot = np.abs(xv) @ np.abs(wv).T
+            assert np.all(err <= 2.0 ** -11 * absdot + 1e-12), float(np.max(err / absdot))
+        else:
+            # exact products, fp32 accumulation
+            scale = np.sqrt(np.sum(xv ** 2, 1))[:, None] * np.sqrt(np.sum(wv ** 2, 1))[None, :]
+            assert np.all(err <= 1e-5 * scale), float(err.max())
     elif epi == H.HR_EPI_RESIDUAL:
         h0 = np.random.default_rng(seed + 1).standard_normal((M, N)).astype(np.float32)
         h = dev(h0)
-        H.hr_linear(dx, dw, dws, xs, wtype, M, N, K, epi, h)
+        H.hr_linear(dx, dw, dws, xs, wtype, M, N, K, epi, h, ws=H.linear_ws(wtype, M, N, K, epi))
         torch.cuda.synchronize()
         got = h.cpu().numpy().astype(np.float64)
         want = h0 + ref
@@ -124,7 +132,7 @@ def _linear_case(H, M, N, K, epi, fp8=False, seed=0):
         if fp8:
             out = torch.empty((M, F), dtype=torch.uint8, device="cuda")
         else:
-            out = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+            out = torch.empty((M, F), dtype=torch.float16, device="cuda")
         H.hr_linear(dx, dw, dws, xs, wtype, M, N, K, epi, out, out_scale if fp8 else 0.0)
         torch.cuda.synchronize()
         act = op.silu(ref[:, :F]) * ref[:, F:]
@@ -145,29 +153,37 @@ def _linear_case(H, M, N, K, epi, fp8=False, seed=0):
             assert np.all(np.abs(got - sat) <= bound * 1.01), float(np.max(np.abs(got - sat) / bound))
             log(f"fp8 SwiGLU codes differing from the float64 quantisation: {float((got != want).mean()):.4f}")
         else:
-            got = f64_of_bf16(out)
+            got = f64_of(out)
             gs = np.sqrt(np.sum(xv ** 2, 1))[:, None] * np.sqrt(np.sum(wv[:F] ** 2, 1) + np.sum(wv[F:] ** 2, 1))[None, :]
-            assert np.all(np.abs(got - act) <= 2.0 ** -8 * np.abs(act) + 1e-4 * gs), float(np.abs(got - act).max())
+            assert np.all(np.abs(got - act) <= 2.0 ** -10 * np.abs(act) + 1e-4 * gs), float(np.abs(got - act).max())
 
 
 @pytest.mark.parametrize("M", [1, 13, 16])
 def test_linear_skinny_bf16(H, M):
-    _linear_case(H, M, 6144, 2560, H.HR_EPI_BF16, seed=M)
+    _linear_case(H, M, 6144, 2560, H.HR_EPI_F32, seed=M)
     _linear_case(H, M, 2560, 4096, H.HR_EPI_RESIDUAL, seed=M)
     _linear_case(H, M, 2 * 768, 256, H.HR_EPI_SWIGLU, seed=M)
 
 
 @pytest.mark.parametrize("M", [17, 40, 64, 65, 200, 544])
 def test_linear_tiled_bf16(H, M):
-    _linear_case(H, M, 512, 2560, H.HR_EPI_BF16, seed=M)
+    _linear_case(H, M, 512, 2560, H.HR_EPI_F32, seed=M)
     _linear_case(H, M, 256, 768, H.HR_EPI_RESIDUAL, seed=M)
     _linear_case(H, M, 2560, 1024, H.HR_EPI_RESIDUAL, seed=M + 1)
     _linear_case(H, M, 2 * 768, 256, H.HR_EPI_SWIGLU, seed=M)
 
 
+# the down projection's shapes (N 2560, K 9728) at every row range whose tile
+# the dispatch picks differently: 17-64 rows, 65-128 (the 128-row prefill),
+# 129-384, 385-1024 (the 512-row prefill, split-K 6) and above 1024
+@pytest.mark.parametrize("M", [17, 64, 65, 128, 129, 512, 1100])
+def test_linear_down_shapes(H, M):
+    _linear_case(H, M, 2560, 9728, H.HR_EPI_RESIDUAL, seed=M + 7)
+
+
 @pytest.mark.parametrize("M", [13, 200])
 def test_linear_fp8(H, M):
-    _linear_case(H, M, 512, 1024, H.HR_EPI_BF16, fp8=True, seed=M)
+    _linear_case(H, M, 512, 1024, H.HR_EPI_F32, fp8=True, seed=M)
     _linear_case(H, M, 256, 512, H.HR_EPI_RESIDUAL, fp8=True, seed=M)
     _linear_case(H, M, 2 * 256, 512, H.HR_EPI_SWIGLU, fp8=True, seed=M)
 
@@ -176,7 +192,84 @@ def test_linear_rejects_bad_shapes(H):
     import torch
     x = torch.zeros(64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(H.HrError, match="HR_EUNSUPPORTED"):
-        H.hr_linear(x, x, None, 1.0, H.HR_BF16, 1, 16, 48, H.HR_EPI_BF16, x)
+        H.hr_linear(x, x, None, 1.0, H.HR_BF16, 1, 16, 48, H.HR_EPI_F32, x)
+
+
+# ----------------------------------------------------------------------------- A6 / A9 fused
+@pytest.mark.parametrize("T,D,ks,fmt", [(13, 2560, 5, "f16"), (512, 2560, 6, "f16"), (300, 256, 1, "e4m3"),
+                                        (7, 2560, 0, "f16"), (40, 2560, 3, "none")])
+def test_residual_rmsnorm(H, T, D, ks, fmt):
+    """h += p0 + ... + p_{ks-1} (split order), then RMS(h) * w in fp16 / e4m3
+    (or nothing), against float64; run twice on the same inputs the bits must
+    repeat; hr_linear's residual path (the same order) plus hr_rmsnorm give
+    the same bits as the fused call."""
+    import torch
+    from gpu_util import assert_f16_close, dev, dev_bf16, f64_of, log
+    log(f"residual_rmsnorm T={T} D={D} ks={ks} {fmt}")
+    rng = np.random.default_rng(T * 31 + ks)
+    h0 = (rng.standard_normal((T, D)) * 20).astype(np.float32)
+    parts = (rng.standard_normal((max(ks, 1), T, D)) * 2).astype(np.float32)
+    w = seeded_bf16((D,), (4, D), 0.1, 1.0)
+    a = 0.05
+    xtype = {"f16": H.HR_F16, "e4m3": H.HR_FP8_E4M3, "none": H.HR_F16}[fmt]
+    outs = []
+    for rep in range(2):
+        h = dev(h0.copy())
+        x = None if fmt == "none" else torch.empty((T, D), dtype=torch.uint8 if fmt == "e4m3" else torch.float16,
+                                                   device="cuda")
+        H.hr_residual_rmsnorm(h, dev(parts), ks, T, D, dev_bf16(w), 1e-6, x, xtype, a)
+        torch.cuda.synchronize()
+        outs.append((h.cpu().numpy(), None if x is None else x.cpu().numpy()))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    if fmt != "none":
+        np.testing.assert_array_equal(outs[0][1], outs[1][1])
+    # the sum in split order, in fp32 (the contract), then added to h
+    s = parts[0].copy() if ks > 0 else np.zeros((T, D), np.float32)
+    for k in range(1, ks):
+        s = (s + parts[k]).astype(np.float32)
+    want_h = (h0 + s).astype(np.float32) if ks > 0 else h0
+    np.testing.assert_array_equal(outs[0][0], want_h)
+    if fmt == "none":
+        return
+    ref = op.rms_norm(want_h.astype(np.float64), nx.bf16_to_f64(w), 1e-6)
+    if fmt == "f16":
+        assert_f16_close(outs[0][1].astype(np.float64), ref, what="fused x")
+        # the same bits through the separate residual add and norm entries
+        h2 = dev(want_h)
+        x2 = torch.empty((T, D), dtype=torch.float16, device="cuda")
+        H.hr_rmsnorm(h2, T, D, dev_bf16(w), 1e-6, x2)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(x2.cpu().numpy(), outs[0][1])
+    else:
+        got = nx.e4m3_decode(outs[0][1])
+        want = nx.e4m3_round(ref / a)
+        diff = got != want
+        assert diff.mean() < 1e-3
+        step = np.abs(want) * 2.0 ** -3 + 2.0 ** -9
+        assert np.all(np.abs(got - want)[diff] <= step[diff])
+
+
+def test_linear_residual_is_deterministic(H):
+    """A split-K residual projection (down at 13 and 512 rows) gives the same
+    bits on every call."""
+    import torch
+    from gpu_util import dev, dev_bf16, dev_f16, log, seeded_f16
+    for M in (13, 512):
+        N, K = 2560, 9728
+        log(f"residual determinism M={M}")
+        x = dev_f16(seeded_f16((M, K), 77 + M, 1.0))
+        w = dev_bf16(seeded_bf16((N, K), (12, M), 0.02))
+        h0 = np.random.default_rng(M).standard_normal((M, N)).astype(np.float32)
+        ws = H.linear_ws(H.HR_BF16, M, N, K, H.HR_EPI_RESIDUAL)
+        assert ws is not None, "expected a split-K launch"
+        res = []
+        for _ in range(3):
+            h = dev(h0.copy())
+            H.hr_linear(x, w, None, 1.0, H.HR_BF16, M, N, K, H.HR_EPI_RESIDUAL, h, ws=ws)
+            torch.cuda.synchronize()
+            res.append(h.cpu().numpy())
+        np.testing.assert_array_equal(res[0], res[1])
+        np.testing.assert_array_equal(res[0], res[2])
 
 
 # ----------------------------------------------------------------------------- A3
@@ -192,22 +285,22 @@ def _dims(H, m, causal=True):
 ])
 def test_qknorm_rope_kv(H, model, lens, starts, slots, cap):
     import torch
-    from gpu_util import BF16_NAN, bits_of, dev_bf16, f64_of_bf16, log, poisoned_bf16
+    from gpu_util import BF16_NAN, bits_of, dev, dev_bf16, f64_of, log, poisoned_bf16, poisoned_f16
     m = model
     log(f"qknorm_rope_kv {m.name} lens={lens} starts={starts}")
     T = sum(lens)
     Hq, Hkv, d = m.n_q_heads, m.n_kv_heads, m.head_dim
-    qkv = seeded_bf16((T, m.qkv_rows), (20, T, d), 1.0)
+    qkv = np.random.default_rng(20 + T + d).standard_normal((T, m.qkv_rows)).astype(np.float32)
     qw = seeded_bf16((d,), (21, d), 0.1, 1.0)
     kw = seeded_bf16((d,), (22, d), 0.1, 1.0)
     n_slots = max(slots) + 1
     kc, vc = poisoned_bf16((n_slots * cap, Hkv, d)), poisoned_bf16((n_slots * cap, Hkv, d))
-    q_out = poisoned_bf16((T, Hq, d))
+    q_out = poisoned_f16((T, Hq, d))
     b = H.Batch(np.concatenate([[0], np.cumsum(lens)]), starts, slots)
-    H.hr_qknorm_rope_kv(_dims(H, m), b, dev_bf16(qkv), dev_bf16(qw), dev_bf16(kw), q_out,
+    H.hr_qknorm_rope_kv(_dims(H, m), b, dev(qkv), dev_bf16(qw), dev_bf16(kw), q_out,
                         H.make_kv(kc, vc, cap, n_slots))
     torch.cuda.synchronize()
-    x = nx.bf16_to_f64(qkv)
+    x = qkv.astype(np.float64)
     cu = b.h_cu
     kcb, vcb = bits_of(kc), bits_of(vc)
     written = np.zeros(n_slots * cap, bool)
@@ -219,17 +312,18 @@ def test_qknorm_rope_kv(H, model, lens, starts, slots, cap):
                           m.rope_theta)
         rows = slots[s] * cap + pos
         written[rows] = True
-        from gpu_util import assert_bf16_close
-        assert_bf16_close(f64_of_bf16(q_out[a:e]), q, abs_=1e-5, what="q")
+        from gpu_util import assert_bf16_close, assert_f16_close
+        assert_f16_close(f64_of(q_out[a:e]), q, abs_=1e-5, what="q")
         assert_bf16_close(nx.bf16_to_f64(kcb[rows]), k, abs_=1e-5, what="k cache")
-        np.testing.assert_array_equal(vcb[rows], qkv[a:e, (Hq + Hkv) * d:].reshape(-1, Hkv, d))   # v copied
+        # v: the fp32 projection rounded once to bf16 (nearest even)
+        np.testing.assert_array_equal(vcb[rows], nx.f32_to_bf16(qkv[a:e, (Hq + Hkv) * d:]).reshape(-1, Hkv, d))
     assert np.all(kcb[~written] == BF16_NAN) and np.all(vcb[~written] == BF16_NAN)
 
 
 # ------------------------------------------------------------------ A3 + A4 fused (short prompts)
 # Every sequence from position 0 with at most 32 rows: the cache must hold the
 # bits hr_qknorm_rope_kv writes (the same arithmetic), and the output must be
-# the attention of the q it produces over those keys (oracle on the bf16 q, k,
+# the attention of the q it produces over those keys (oracle on the fp16 q, bf16 k,
 # v, as for hr_attention).  Cases: one 13-token prompt; a packed batch with a
 # 1-row and a full 32-row prompt in permuted cache slots; the tiny model (d 64,
 # 2 query heads per kv head); non-causal used keys with pads (their K/V left
@@ -242,23 +336,23 @@ def test_qknorm_rope_kv(H, model, lens, starts, slots, cap):
 ])
 def test_qknorm_rope_attention(H, model, lens, slots, causal, used, fp8):
     import torch
-    from gpu_util import BF16_NAN, bits_of, dev_bf16, f64_of_bf16, log, poisoned_bf16
+    from gpu_util import BF16_NAN, bits_of, dev, dev_bf16, f64_of, log, poisoned_bf16, poisoned_f16
     m = model
     log(f"qknorm_rope_attention {m.name} lens={lens} causal={causal} fp8={fp8}")
     T, n, cap = sum(lens), len(lens), 40
     Hq, Hkv, d = m.n_q_heads, m.n_kv_heads, m.head_dim
-    qkv = dev_bf16(seeded_bf16((T, m.qkv_rows), (23, T, d), 1.0))
+    qkv = dev(np.random.default_rng(23 + T + d).standard_normal((T, m.qkv_rows)).astype(np.float32))
     qw = dev_bf16(seeded_bf16((d,), (24, d), 0.1, 1.0))
     kw = dev_bf16(seeded_bf16((d,), (25, d), 0.1, 1.0))
     b = H.Batch(np.concatenate([[0], np.cumsum(lens)]), [0] * n, slots, used)
     dims = _dims(H, m, causal)
     caches = [(poisoned_bf16((n * cap, Hkv, d)), poisoned_bf16((n * cap, Hkv, d))) for _ in range(2)]
     out_scale = 0.01
-    otype = H.HR_FP8_E4M3 if fp8 else H.HR_BF16
+    otype = H.HR_FP8_E4M3 if fp8 else H.HR_F16
     outs = [torch.full((T, Hq * d), 0x7F, dtype=torch.uint8, device="cuda") if fp8 else
-            torch.full((T, Hq * d), float("nan"), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+            torch.full((T, Hq * d), float("nan"), dtype=torch.float16, device="cuda") for _ in range(2)]
     H.hr_qknorm_rope_attention(dims, b, qkv, qw, kw, H.make_kv(*caches[0], cap, n), outs[0], otype, out_scale)
-    q_out = poisoned_bf16((T, Hq, d))
+    q_out = poisoned_f16((T, Hq, d))
     kv1 = H.make_kv(*caches[1], cap, n)
     H.hr_qknorm_rope_kv(dims, b, qkv, qw, kw, q_out, kv1)
     H.hr_attention(dims, b, q_out, kv1, outs[1], otype, out_scale)
@@ -272,10 +366,10 @@ def test_qknorm_rope_attention(H, model, lens, slots, causal, used, fp8):
     if fp8:
         got = nx.e4m3_decode(outs[0].cpu().numpy()).reshape(T, Hq, d) * out_scale
     else:
-        got = f64_of_bf16(outs[0]).reshape(T, Hq, d)
+        got = f64_of(outs[0]).reshape(T, Hq, d)
     assert np.all(np.isfinite(got))
-    qv = f64_of_bf16(q_out)
-    kv_, vv = f64_of_bf16(caches[1][0]), f64_of_bf16(caches[1][1])
+    qv = f64_of(q_out)
+    kv_, vv = f64_of(caches[1][0]), f64_of(caches[1][1])
     cu = b.h_cu
     grp = Hq // Hkv
     for s in range(n):
@@ -288,9 +382,9 @@ def test_qknorm_rope_attention(H, model, lens, slots, causal, used, fp8):
             ref = op.attention(qv[a:e, hh], kv_[rows, g], vv[rows, g], vis)
             err = np.abs(got[a:e, hh] - ref)
             if fp8:
-                assert np.all(err <= 2.0 ** -4 * np.abs(ref) + 2.0 ** -9 * out_scale + 4e-3), (s, hh, float(err.max()))
+                assert np.all(err <= 2.0 ** -4 * np.abs(ref) + 2.0 ** -9 * out_scale + 2e-3), (s, hh, float(err.max()))
             else:
-                assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 4e-3), (s, hh, float(err.max()))
+                assert np.all(err <= 2.0 ** -10 * np.abs(ref) + 2e-3), (s, hh, float(err.max()))
 
 
 # ----------------------------------------------------------------------------- A4
@@ -335,12 +429,12 @@ def test_attention_chunked(H, Hq, Hkv, d, lens, starts, causal, used, ct, slots,
 
 def _attention_case(H, Hq, Hkv, d, lens, starts, causal, used, chunked=None, fp8=False):
     import torch
-    from gpu_util import dev_bf16, f64_of_bf16, log
+    from gpu_util import dev_bf16, dev_f16, f64_of, log, seeded_f16
     log(f"attention Hq={Hq} Hkv={Hkv} d={d} lens={lens} causal={causal} chunked={chunked} fp8={fp8}")
     cap = max(s + l for s, l in zip(starts, lens)) + 3
     n = len(lens)
     T = sum(lens)
-    q = seeded_bf16((T, Hq, d), (30, T, Hq, d), 1.0)
+    q = seeded_f16((T, Hq, d), 30 + T * Hq + d, 1.0)
     kc = seeded_bf16((n * cap, Hkv, d), (31, cap, Hkv, d), 1.0)
     vc = seeded_bf16((n * cap, Hkv, d), (32, cap, Hkv, d), 1.0)
     b = H.Batch(np.concatenate([[0], np.cumsum(lens)]), starts, list(range(n)), used)
@@ -351,21 +445,21 @@ def _attention_case(H, Hq, Hkv, d, lens, starts, causal, used, chunked=None, fp8
     if fp8:
         out = torch.full((T, Hq * d), 0x7F, dtype=torch.uint8, device="cuda")      # e4m3 NaN
     else:
-        out = torch.full((T, Hq * d), float("nan"), dtype=torch.bfloat16, device="cuda")
-    otype = H.HR_FP8_E4M3 if fp8 else H.HR_BF16
+        out = torch.full((T, Hq * d), float("nan"), dtype=torch.float16, device="cuda")
+    otype = H.HR_FP8_E4M3 if fp8 else H.HR_F16
     if chunked:
         ct, slots = chunked
         nb = H.hr_attention_chunked_workspace_bytes(dims, T, slots)
         ws = torch.full((nb // 4,), float("nan"), dtype=torch.float32, device="cuda")
-        H.hr_attention_chunked(dims, b, dev_bf16(q), kvd, out, ct, slots, ws, otype, out_scale)
+        H.hr_attention_chunked(dims, b, dev_f16(q), kvd, out, ct, slots, ws, otype, out_scale)
     else:
-        H.hr_attention(dims, b, dev_bf16(q), kvd, out, otype, out_scale)
+        H.hr_attention(dims, b, dev_f16(q), kvd, out, otype, out_scale)
     torch.cuda.synchronize()
     if fp8:
         got = nx.e4m3_decode(out.cpu().numpy()).reshape(T, Hq, d) * out_scale
     else:
-        got = f64_of_bf16(out).reshape(T, Hq, d)
-    qv, kv_, vv = nx.bf16_to_f64(q), nx.bf16_to_f64(kc), nx.bf16_to_f64(vc)
+        got = f64_of(out).reshape(T, Hq, d)
+    qv, kv_, vv = q.astype(np.float64), nx.bf16_to_f64(kc), nx.bf16_to_f64(vc)
     cu = b.h_cu
     grp = Hq // Hkv
     for s in range(n):
@@ -381,10 +475,12 @@ def _attention_case(H, Hq, Hkv, d, lens, starts, causal, used, chunked=None, fp8
             g = hh // grp
             ref = op.attention(qv[a:e, hh], kv_[s * cap:s * cap + nk, g], vv[s * cap:s * cap + nk, g], vis)
             err = np.abs(got[a:e, hh] - ref)
-            if fp8:     # e4m3 keeps 3 mantissa bits: half a step of 2^-3 relative, plus the bf16 path's error
-                assert np.all(err <= 2.0 ** -4 * np.abs(ref) + 2.0 ** -9 * out_scale + 4e-3), (s, hh, float(err.max()))
+            # fp16 output: half an ulp (2^-11 relative) plus the fp16 probabilities
+            # of P V (2^-11 relative each, at most 2^-11 max|v| in the mean)
+            if fp8:     # e4m3 keeps 3 mantissa bits: half a step of 2^-3 relative
+                assert np.all(err <= 2.0 ** -4 * np.abs(ref) + 2.0 ** -9 * out_scale + 2e-3), (s, hh, float(err.max()))
             else:
-                assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 4e-3), (s, hh, float(err.max()))
+                assert np.all(err <= 2.0 ** -10 * np.abs(ref) + 2e-3), (s, hh, float(err.max()))
 
 
 # ----------------------------------------------------------------------------- A9 final + A10
