@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "hr.h"
@@ -571,11 +572,16 @@ size_t hr_decode_workspace_bytes(const hr_dims* dims, hr_wtype wtype, int32_t B)
   return decode_ws_layout(dims, B, nullptr, nullptr, nullptr);
 }
 
-hr_status hr_decode_step(const hr_dims* dims, const hr_layer* layers, const hr_batch* batch, const void* x_embeds,
-                         const hr_kv* kv, const void* final_norm_w, const void* head_w, int32_t n_codebooks,
-                         int32_t cb_vocab, int32_t bos_id, int32_t eoc_id, float* logits_out, int32_t* frame,
-                         uint8_t* eoc_seen, uint8_t* done, int32_t* codes, int32_t* aligned, int32_t max_frames,
-                         const void* cb_embed, void* emb_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// every check of a decode step except the workspace's
+hr_status check_decode(const hr_dims* dims, const hr_layer* layers, const hr_batch* batch, const void* x_embeds,
+                       const hr_kv* kv, const void* final_norm_w, const void* head_w, int32_t n_codebooks,
+                       int32_t cb_vocab, int32_t bos_id, int32_t eoc_id, float* logits_out, int32_t* frame,
+                       uint8_t* eoc_seen, uint8_t* done, int32_t* codes, int32_t* aligned, int32_t max_frames,
+                       const void* cb_embed, void* emb_out) {
   if (!dims) return fail(HR_EINVAL, "dims is NULL");
   if (!dims->causal) return fail(HR_EUNSUPPORTED, "a decode step attends causally (dims->causal = 0)");
   if (!batch) return fail(HR_EINVAL, "batch is NULL");
@@ -592,9 +598,16 @@ hr_status hr_decode_step(const hr_dims* dims, const hr_layer* layers, const hr_b
                   batch->h_cu_seqlens[s + 1] - batch->h_cu_seqlens[s]);
   HR_TRY(check_codebook(B, n_codebooks, cb_vocab, bos_id, eoc_id, logits_out, frame, eoc_seen, done, codes,
                         aligned, max_frames, cb_embed, dims->hidden, emb_out));
-  HR_TRY(need(ws, "ws"));
-  const size_t need_ws = decode_ws_layout(dims, B, nullptr, nullptr, nullptr);
-  if (ws_bytes < need_ws) return fail(HR_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need_ws);
+  return HR_OK;
+}
+
+// the decode step's kernels over validated arguments and a large enough workspace
+hr_status enqueue_decode(const hr_dims* dims, const hr_layer* layers, const hr_batch* batch, const void* x_embeds,
+                         const hr_kv* kv, const void* final_norm_w, const void* head_w, int32_t n_codebooks,
+                         int32_t cb_vocab, int32_t bos_id, int32_t eoc_id, float* logits_out, int32_t* frame,
+                         uint8_t* eoc_seen, uint8_t* done, int32_t* codes, int32_t* aligned, int32_t max_frames,
+                         const void* cb_embed, void* emb_out, void* ws, hipStream_t stream) {
+  const int B = batch->n_seq;
   Ws w;
   float* h = nullptr;
   decode_ws_layout(dims, B, &w, &h, static_cast<uint8_t*>(ws));
@@ -603,6 +616,77 @@ hr_status hr_decode_step(const hr_dims* dims, const hr_layer* layers, const hr_b
   hr::launch_codebook_step(B, n_codebooks, cb_vocab, bos_id, eoc_id, true, logits_out, frame, eoc_seen, done,
                            codes, aligned, max_frames, cb_embed, dims->hidden, emb_out, stream);
   return check_launch("decode step");
+}
+
+// Scratch of hr_decode_step_noalloc: a file-scope device array (each GPU the
+// library runs on holds its own copy until the process ends).  In host code
+// `scratch` names a host-side stand-in, never the device memory: its address
+// on a device comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = size_t(32) << 20;   // 4B-class decode steps of up to 128 streams (27 MiB)
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hr_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(HR_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(HR_EUNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(HR_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hr_status hr_decode_step(const hr_dims* dims, const hr_layer* layers, const hr_batch* batch, const void* x_embeds,
+                         const hr_kv* kv, const void* final_norm_w, const void* head_w, int32_t n_codebooks,
+                         int32_t cb_vocab, int32_t bos_id, int32_t eoc_id, float* logits_out, int32_t* frame,
+                         uint8_t* eoc_seen, uint8_t* done, int32_t* codes, int32_t* aligned, int32_t max_frames,
+                         const void* cb_embed, void* emb_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  HR_TRY(check_decode(dims, layers, batch, x_embeds, kv, final_norm_w, head_w, n_codebooks, cb_vocab, bos_id, eoc_id,
+                      logits_out, frame, eoc_seen, done, codes, aligned, max_frames, cb_embed, emb_out));
+  HR_TRY(need(ws, "ws"));
+  const size_t need_ws = decode_ws_layout(dims, batch->n_seq, nullptr, nullptr, nullptr);
+  if (ws_bytes < need_ws) return fail(HR_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need_ws);
+  return enqueue_decode(dims, layers, batch, x_embeds, kv, final_norm_w, head_w, n_codebooks, cb_vocab, bos_id,
+                        eoc_id, logits_out, frame, eoc_seen, done, codes, aligned, max_frames, cb_embed, emb_out, ws,
+                        stream);
+}
+
+size_t hr_decode_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+hr_status hr_decode_step_noalloc(const hr_dims* dims, const hr_layer* layers, const hr_batch* batch,
+                                 const void* x_embeds, const hr_kv* kv, const void* final_norm_w, const void* head_w,
+                                 int32_t n_codebooks, int32_t cb_vocab, int32_t bos_id, int32_t eoc_id,
+                                 float* logits_out, int32_t* frame, uint8_t* eoc_seen, uint8_t* done, int32_t* codes,
+                                 int32_t* aligned, int32_t max_frames, const void* cb_embed, void* emb_out,
+                                 hipStream_t stream) {
+  HR_TRY(check_decode(dims, layers, batch, x_embeds, kv, final_norm_w, head_w, n_codebooks, cb_vocab, bos_id, eoc_id,
+                      logits_out, frame, eoc_seen, done, codes, aligned, max_frames, cb_embed, emb_out));
+  const size_t need_ws = decode_ws_layout(dims, batch->n_seq, nullptr, nullptr, nullptr);
+  if (need_ws > kScratchBytes)
+    return fail(HR_EWORKSPACE, "a decode step of %d streams needs %zu bytes of scratch; the allocation-free entry "
+                "holds %zu (hr_decode_step with a caller workspace has no such limit)",
+                batch->n_seq, need_ws, kScratchBytes);
+  void* ws = nullptr;
+  HR_TRY(scratch_of_current_device(&ws));
+  // every scratch region is written before it is read within the call
+  // (split-K partials, attention partials, activations), so nothing is cleared
+  return enqueue_decode(dims, layers, batch, x_embeds, kv, final_norm_w, head_w, n_codebooks, cb_vocab, bos_id,
+                        eoc_id, logits_out, frame, eoc_seen, done, codes, aligned, max_frames, cb_embed, emb_out, ws,
+                        stream);
 }
 
 hr_status hr_codebook_step(int32_t B, int32_t K, int32_t V, int32_t bos_id, int32_t eoc_id,

@@ -93,6 +93,10 @@ def lib() -> ctypes.CDLL:
                                                 c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp, P(HrStepPolicy),
                                                 c_vp]),
             "hr_decode_workspace_bytes": (c_sz, [P(HrDims), c_i32, c_i32]),
+            "hr_decode_noalloc_scratch_bytes": (c_sz, []),
+            "hr_decode_step_noalloc": (c_i32, [P(HrDims), P(HrLayer), P(HrBatch), c_vp, P(HrKv), c_vp, c_vp, c_i32,
+                                               c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp,
+                                               c_vp, c_vp]),
             "hr_decode_step": (c_i32, [P(HrDims), P(HrLayer), P(HrBatch), c_vp, P(HrKv), c_vp, c_vp, c_i32, c_i32,
                                        c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp,
                                        c_sz, c_vp]),
@@ -253,6 +257,22 @@ def hr_decode_step(dims, layers: list, batch: Batch, x_embeds, kvs: list, final_
                                 ptr(eoc_seen), ptr(done), ptr(codes), ptr(aligned), max_frames, ptr(cb_embed),
                                 ptr(emb_out), ptr(ws), ws.numel() * ws.element_size(),
                                 stream if stream is not None else current_stream()))
+
+
+def hr_decode_noalloc_scratch_bytes() -> int:
+    return lib().hr_decode_noalloc_scratch_bytes()
+
+
+def hr_decode_step_noalloc(dims, layers: list, batch: Batch, x_embeds, kvs: list, final_norm_w, head_w,
+                           n_codebooks, cb_vocab, bos_id, eoc_id, logits_out, frame, eoc_seen, done, codes, aligned,
+                           max_frames, cb_embed, emb_out, stream=None) -> None:
+    L = (HrLayer * len(layers))(*layers)
+    K = (HrKv * len(kvs))(*kvs)
+    _check(lib().hr_decode_step_noalloc(ctypes.byref(dims), L, ctypes.byref(batch.c), ptr(x_embeds), K,
+                                        ptr(final_norm_w), ptr(head_w), n_codebooks, cb_vocab, bos_id, eoc_id,
+                                        ptr(logits_out), ptr(frame), ptr(eoc_seen), ptr(done), ptr(codes), ptr(aligned),
+                                        max_frames, ptr(cb_embed), ptr(emb_out),
+                                        stream if stream is not None else current_stream()))
 
 
 def hr_codebook_step(B, K, V, bos_id, eoc_id, logits, frame, eoc_seen, done, codes, aligned, max_frames,

@@ -288,6 +288,24 @@ hr_status hr_decode_step(const hr_dims* dims, const hr_layer* layers, const hr_b
                          const void* cb_embed, void* emb_out, void* ws, size_t ws_bytes,
                          hipStream_t stream);
 
+/* hr_decode_step without the workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and results, with their
+ * scratch in a fixed device array of hr_decode_noalloc_scratch_bytes() (32 MiB)
+ * that the library holds on each GPU it runs on until the process ends.  The
+ * call allocates and frees nothing.  HR_EWORKSPACE when the step's scratch
+ * (hr_decode_workspace_bytes) exceeds that size: up to 128 streams of the
+ * 4B-class shape.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (two streams, two host threads) race and must be
+ * serialised by the caller.  Other checks and errors as hr_decode_step. */
+size_t hr_decode_noalloc_scratch_bytes(void);
+hr_status hr_decode_step_noalloc(const hr_dims* dims, const hr_layer* layers, const hr_batch* batch,
+                                 const void* x_embeds, const hr_kv* kv, const void* final_norm_w,
+                                 const void* head_w, int32_t n_codebooks, int32_t cb_vocab, int32_t bos_id,
+                                 int32_t eoc_id, float* logits_out, int32_t* frame, uint8_t* eoc_seen,
+                                 uint8_t* done, int32_t* codes, int32_t* aligned, int32_t max_frames,
+                                 const void* cb_embed, void* emb_out, hipStream_t stream);
+
 const char* hr_last_error(void);
 
 #ifdef __cplusplus

@@ -343,3 +343,27 @@ def test_decode_step_validation(case, status):
 def test_decode_workspace_holds_the_prefill_workspace():
     d = dims()
     assert H.hr_decode_workspace_bytes(d, H.HR_BF16, 64) >= H.hr_workspace_bytes(d, H.HR_BF16, 64) + 64 * 2560 * 4
+
+
+def test_decode_noalloc_validation():
+    """The allocation-free decode step runs hr_decode_step's checks, and refuses
+    a batch whose scratch exceeds its fixed array before touching the device."""
+    lib = H.lib()
+    assert H.hr_decode_noalloc_scratch_bytes() == 32 << 20
+    d = dims()
+    Ls = (H.HrLayer * 2)(layer(), layer())
+    Ks = (H.HrKv * 2)(kv(), kv())
+    call = lambda dd, b, bos=1024: lib.hr_decode_step_noalloc(
+        ctypes.byref(dd), Ls, ctypes.byref(b.c), FAKE, Ks, FAKE, FAKE, 8, 1026, bos, 1025, FAKE, FAKE, FAKE, FAKE,
+        FAKE, None, 0, FAKE, FAKE, None)
+    assert call(dims(causal=False), batch([1, 1], used=[1, 1])) == H.HR_EUNSUPPORTED
+    assert call(d, batch([1, 2], starts=[3, 4])) == H.HR_EINVAL
+    assert call(d, batch([1, 1], starts=[3, 4]), bos=1025) == H.HR_EINVAL
+    big = 300                                   # 4B-shape scratch of 300 streams > 32 MiB
+    assert H.hr_decode_workspace_bytes(d, H.HR_BF16, big) > 32 << 20
+    Kbig = (H.HrKv * 2)(kv(n_slots=big), kv(n_slots=big))
+    bb = batch([1] * big, starts=[3] * big)          # kept alive: the struct points at its host arrays
+    st = lib.hr_decode_step_noalloc(ctypes.byref(d), Ls, ctypes.byref(bb.c), FAKE,
+                                    Kbig, FAKE, FAKE, 8, 1026, 1024, 1025, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE,
+                                    FAKE, None)
+    assert st == H.HR_EWORKSPACE, H.hr_last_error()
