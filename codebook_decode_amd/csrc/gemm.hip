@@ -756,6 +756,12 @@ static int tiled_fill(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, 
 // QKV stays on 256x256: 153 against 177); at M = 128 gate/up on 8 waves (35.9
 // against 38.0 us), down 128x64 and O 64x64 with 128-byte slabs (32.5 / 14.1
 // against 34.7 / 17.0).
+// bf16 weights reach the fp16 MFMAs converted in registers, once per B
+// fragment and slab, so the 8-wave tiles stand their waves 2 x 4 (each wave
+// 2x the A rows and half the B columns of a 4 x 2 layout: half the
+// conversions for the same LDS reads): at 512 rows QKV 36.9 -> 31.7 us,
+// O 31.4 -> 28.7, gate/up 95.4 -> 87.2, down 52.1 -> 49.0 (weights rotated
+// through 4 copies).  The e4m3 tiles keep their layout (no conversion).
 template <int EPI, bool FP8>
 static int tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
                  hipStream_t st, bool go) {
@@ -764,13 +770,13 @@ static int tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const
     if (M <= 64) return tiled_fill<EPI, FP8, 64, 128, 2, 2, 6, 128>(x, w, M, N, Kb, e, st, go);
     if (M > 384) {
       if constexpr (FP8) return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st, go);
-      else return tiled_fill<EPI, FP8, 256, 256, 4, 2, 4>(x, w, M, N, Kb, e, st, go);
+      else return tiled_fill<EPI, FP8, 256, 256, 2, 4, 4>(x, w, M, N, Kb, e, st, go);
     }
     if (M > 128) return tiled_fill<EPI, FP8, 256, 128, 4, 2, 4>(x, w, M, N, Kb, e, st, go);
     return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st, go);
   } else if constexpr (EPI == HR_EPI_F32) {
-    if (M > 1024) return tiled_fill<EPI, FP8, 256, 256, 4, 2, 4>(x, w, M, N, Kb, e, st, go);
-    if (M > 384) return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st, go);
+    if (M > 1024) return tiled_fill<EPI, FP8, 256, 256, 2, 4, 4>(x, w, M, N, Kb, e, st, go);
+    if (M > 384) return tiled_fill<EPI, FP8, 128, 128, 2, 4, 4, 128>(x, w, M, N, Kb, e, st, go);
     if (M > 128) return tiled_fill<EPI, FP8, 128, 64, 2, 2, 6, 128>(x, w, M, N, Kb, e, st, go);
     if (M <= 64) return tiled_fill<EPI, FP8, 64, 32, 2, 1, 8, 128>(x, w, M, N, Kb, e, st, go);
     return tiled_fill<EPI, FP8, 64, 64, 2, 2, 8, 128>(x, w, M, N, Kb, e, st, go);
@@ -778,10 +784,10 @@ static int tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const
     if constexpr (FP8) {
       if (M > 128) return tiled_fill<EPI, FP8, 64, 64, 2, 2, 4, 128>(x, w, M, N, Kb, e, st, go);
     }
-    if (M > 1024) return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st, go);
+    if (M > 1024) return tiled_fill<EPI, FP8, 128, 128, 2, 4, 4, 128>(x, w, M, N, Kb, e, st, go);
     if (M > 384) {
-      if (K_el >= 8192) return tiled_fill<EPI, FP8, 256, 128, 4, 2, 4>(x, w, M, N, Kb, e, st, go, 6);
-      return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st, go, 3);
+      if (K_el >= 8192) return tiled_fill<EPI, FP8, 256, 128, 2, 4, 4>(x, w, M, N, Kb, e, st, go, 6);
+      return tiled_fill<EPI, FP8, 128, 128, 2, 4, 4, 128>(x, w, M, N, Kb, e, st, go, 3);
     }
     if (M > 128) return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4>(x, w, M, N, Kb, e, st, go);
     if (M <= 64 && K_el >= 8192) return tiled_fill<EPI, FP8, 64, 64, 2, 2, 8, 128>(x, w, M, N, Kb, e, st, go);
