@@ -1,9 +1,16 @@
 """Build libhr.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-    python -m codebook_decode_amd.build        # writes codebook_decode_amd/libhr.so
+    python -m codebook_decode_amd.build          # writes codebook_decode_amd/libhr.so
+    python -m codebook_decode_amd.build --asan   # writes codebook_decode_amd/libhr_asan.so
 
 Objects go to codebook_decode_amd/_build/ (git-ignored); the shared library
 sits next to the Python binding that loads it.
+
+--asan: the host code (the C ABI's validation and launch sequencing) built
+with AddressSanitizer and UndefinedBehaviorSanitizer; the GPU code is built as
+usual (the sanitizers apply to the host pass only).  Load it through the
+binding with HR_LIB=<path> and the ASan runtime preloaded (asan_runtime()
+gives its path), e.g. to run tests/test_abi.py on the CPU.
 """
 from __future__ import annotations
 
@@ -19,6 +26,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhr.so")
+LIB_ASAN = os.path.join(PKG, "libhr_asan.so")
+BUILD_ASAN = os.path.join(PKG, "_build_asan")
+# host-pass sanitizers (each -fsanitize= right after -Xarch_host: host code only)
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+              "-fno-omit-frame-pointer", "-g", "-shared-libsan"]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -42,33 +54,43 @@ def _hipcc() -> str:
     return h
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, asan: bool = False) -> str:
+    obj = os.path.join(BUILD_ASAN if asan else BUILD, os.path.basename(src) + ".o")
+    flags = FLAGS + (ASAN_FLAGS if asan else [])
+    cmd = [_hipcc(), *flags, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [_hipcc(), *FLAGS, "-x", "hip", "-c", src, "-o", obj]
+        cmd = [_hipcc(), *flags, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every source and link libhr.so; always rebuilds."""
-    os.makedirs(BUILD, exist_ok=True)
+def asan_runtime() -> str:
+    """Path of the ASan runtime the sanitizer build links against (to preload)."""
+    r = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def build(verbose: bool = True, asan: bool = False) -> str:
+    """Compile every source and link libhr.so (or libhr_asan.so); always rebuilds."""
+    os.makedirs(BUILD_ASAN if asan else BUILD, exist_ok=True)
     srcs = sources()
     with ThreadPoolExecutor(min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda f: _compile(f, asan), srcs))
+    lib = LIB_ASAN if asan else LIB
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    if asan:
+        cmd += ["-fsanitize=address,undefined", "-shared-libsan"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources", file=sys.stderr)
-    return LIB
+        print(f"built {lib} from {len(srcs)} sources", file=sys.stderr)
+    return lib
 
 
 if __name__ == "__main__":
-    build()
+    build(asan="--asan" in sys.argv[1:])

@@ -13,7 +13,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libhr.so")
+# HR_LIB selects another build of the same library (the host-sanitizer build)
+LIB_PATH = os.environ.get("HR_LIB") or os.path.join(_HERE, "libhr.so")
 
 HR_OK, HR_EINVAL, HR_EUNSUPPORTED, HR_ECAPACITY = 0, -1, -2, -3
 HR_EBOUND, HR_EWORKSPACE, HR_EALIGN, HR_EHIP = -4, -5, -6, -7

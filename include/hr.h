@@ -60,7 +60,13 @@ typedef enum {
 /* Number formats.  Weights: HR_BF16, HR_FP8_E4M3, HR_MXFP4.  HR_F16 (IEEE
  * binary16) names the activations of the bf16-weight band where a step entry
  * of hr_ops.h takes an activation type. */
-typedef enum { HR_BF16 = 0, HR_FP8_E4M3 = 1, HR_MXFP4 = 2, HR_F16 = 3 } hr_wtype;
+typedef enum {
+  HR_BF16 = 0, HR_FP8_E4M3 = 1, HR_MXFP4 = 2, HR_F16 = 3,
+  /* range markers, never valid arguments: they give the type the whole int32
+     range, so any value a caller passes is a value of the type that the
+     checks reject (HR_EINVAL), not undefined behaviour */
+  HR_WTYPE_RANGE_MIN_ = INT32_MIN, HR_WTYPE_RANGE_MAX_ = INT32_MAX
+} hr_wtype;
 
 /* Shapes of the decoder.  Supported: head_dim in {64, 128};
  * n_q_heads / n_kv_heads in {1, 2, 4}; hidden, ffn multiples of 64. */

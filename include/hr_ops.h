@@ -37,8 +37,9 @@ hr_status hr_rmsnorm(const float* h, int32_t T, int32_t D, const void* norm_w, f
 typedef enum {
   HR_EPI_F32 = 0,       /* out fp32 [M, N] = x W^T  (the merged QKV rows)        */
   HR_EPI_RESIDUAL = 1,  /* out fp32 [M, N] += x W^T  (residual add)              */
-  HR_EPI_SWIGLU = 2     /* N = 2F (gate rows, then up rows); out [M, F] =
+  HR_EPI_SWIGLU = 2,    /* N = 2F (gate rows, then up rows); out [M, F] =
                            silu(g) * u, fp16, or e4m3(./out_scale) in FP8 mode  */
+  HR_EPI_RANGE_MIN_ = INT32_MIN, HR_EPI_RANGE_MAX_ = INT32_MAX   /* range markers, as for hr_wtype */
 } hr_epilogue;
 
 /* Projection (steps A2, A5, A7, A8): x [M, K] times W [N, K]^T, fp32

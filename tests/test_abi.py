@@ -367,3 +367,13 @@ def test_decode_noalloc_validation():
                                     Kbig, FAKE, FAKE, 8, 1026, 1024, 1025, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE,
                                     FAKE, None)
     assert st == H.HR_EWORKSPACE, H.hr_last_error()
+
+
+def test_one_hip_runtime_in_the_process():
+    """libhr and torch share one HIP runtime: after the library is loaded, the
+    process maps exactly one libamdhip64 (two runtimes in one process broke
+    tensor and stream interop)."""
+    H.lib()
+    maps = open("/proc/self/maps").read()
+    libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(libs) == 1, libs
