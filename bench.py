@@ -389,9 +389,10 @@ def codebook_policy_steps(H, m, shared, B=64, reps=100):
             "settings": "T 1, top-k 50, top-p 0.95, EOC cascade, repeat guard 64"}
 
 
-def hbm_sweep(H, m, shared):
+def hbm_sweep(H, m, shared, reps=10):
     """The memory-bound kernels where their bytes outgrow launch latency:
-    RMSNorm (6 B per element: fp32 in, fp16 out), q/k norm + RoPE + KV write
+    RMSNorm (6 B per element: fp32 in, fp16 out), the fused residual add +
+    RMSNorm (14 B per element), q/k norm + RoPE + KV write
     (36.9 KB per token: fp32 QKV row in, fp16 q and bf16 K/V out), codebook
     step (62.5 KB per stream)."""
     import torch
@@ -401,9 +402,17 @@ def hbm_sweep(H, m, shared):
     for T in (4096, 65536):
         h = torch.randn((T, D), device="cuda")
         x = torch.empty((T, D), dtype=torch.float16, device="cuda")
-        sec = time_events(lambda: H.hr_rmsnorm(h, T, D, shared["final"], m.rms_eps, x), 10)
+        sec = time_events(lambda: H.hr_rmsnorm(h, T, D, shared["final"], m.rms_eps, x), reps)
         out[f"rmsnorm_T{T}"] = {"us": round(sec * 1e6, 2), "roofline": hbm(6 * T * D, sec)}
         del h, x
+    # fused residual add + RMSNorm: h and one split's partial in, h and x out (14 B per element)
+    for T in (4096, 16384):
+        h = torch.randn((T, D), device="cuda")
+        part = torch.randn((1, T, D), device="cuda")
+        x = torch.empty((T, D), dtype=torch.float16, device="cuda")
+        sec = time_events(lambda: H.hr_residual_rmsnorm(h, part, 1, T, D, shared["final"], m.rms_eps, x), reps)
+        out[f"residual_rmsnorm_T{T}"] = {"us": round(sec * 1e6, 2), "roofline": hbm(14 * T * D, sec)}
+        del h, part, x
     for T in (4096, 32768):
         dims = dims_of(H, m, True, 1)
         qkv = torch.randn((T, m.qkv_rows), device="cuda") * 0.5
@@ -413,23 +422,27 @@ def hbm_sweep(H, m, shared):
         b = H.Batch([0, T], [0], [0])
         kv = H.make_kv(kc, vc, T, 1)
         qn = shared["final"][:m.head_dim]
-        sec = time_events(lambda: H.hr_qknorm_rope_kv(dims, b, qkv, qn, qn, q, kv), 10)
+        sec = time_events(lambda: H.hr_qknorm_rope_kv(dims, b, qkv, qn, qn, q, kv), reps)
         bytes_ = T * (m.qkv_rows * 4 + m.attn_width * 2 + 2 * m.n_kv_heads * m.head_dim * 2)
         out[f"qknorm_rope_kv_T{T}"] = {"us": round(sec * 1e6, 2), "roofline": hbm(bytes_, sec)}
         del qkv, q, kc, vc
     for B in (4096, 16384):
-        r = codebook_steps(H, m, shared, B=B, reps=10)
+        r = codebook_steps(H, m, shared, B=B, reps=reps)
         out[f"codebook_B{B}"] = {"us": r["us_per_step"], "roofline": r["roofline"]}
-    r = codebook_policy_steps(H, m, shared, B=4096, reps=10)
+    r = codebook_policy_steps(H, m, shared, B=4096, reps=reps)
     out["codebook_sampled_B4096"] = {"us": r["us_per_step"], "roofline": r["roofline"]}
     return out
 
 
-def cpu_baseline(m, P, host_layers):
-    """The float64 oracle on the P-token prefill of the whole stack (every layer
-    given in ``host_layers``, scaled to m.n_layers if fewer), plus final norm
-    and head on the last row.  Weight widening is outside the timed part."""
+def cpu_baseline(m, P, host_layers, shared_host):
+    """The float64 oracle, timed on the host cores on a bounded sample of the
+    same workloads: the P-token prefill of the whole stack (every layer given
+    in ``host_layers``, scaled to m.n_layers if fewer) plus final norm and head
+    on the last row (the headline value, prompt tok/s); the same at P = 13
+    (ms per prompt); and the delayed-codebook step on 64 streams x 8 x 1026
+    bf16 logits (us per step).  Weight widening is outside the timed parts."""
     import synth
+    from oracle import codebook as oc
     from oracle import prefill as op
     from oracle import numerics as nx
     try:
@@ -437,30 +450,65 @@ def cpu_baseline(m, P, host_layers):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    ids = synth.prompt_ids(m, P)
-    h = nx.bf16_to_f64(synth.embed_rows(m, ids))
-    b = {"cu_seqlens": [0, P], "start_pos": [0], "cache_slot": [0], "capacity": P}
-    t_layers = 0.0
-    n_sample_layers = len(host_layers)
-    for bits in host_layers:
-        lw = op.widen_layer(bits)
-        kc, vc = op.new_cache(m, 1, P)
+    wh = nx.bf16_to_f64(shared_host["head"])
+    wf = nx.bf16_to_f64(shared_host["final"])
+
+    def stack_time(P_):
+        ids = synth.prompt_ids(m, P_)
+        h = nx.bf16_to_f64(synth.embed_rows(m, ids))
+        b = {"cu_seqlens": [0, P_], "start_pos": [0], "cache_slot": [0], "capacity": P_}
+        t_layers = 0.0
+        for bits in host_layers:
+            lw = op.widen_layer(bits)
+            kc, vc = op.new_cache(m, 1, P_)
+            t0 = time.perf_counter()
+            h = op.prefill_layer(m, lw, b, h, kc, vc)
+            t_layers += time.perf_counter() - t0
+            del lw
         t0 = time.perf_counter()
-        h = op.prefill_layer(m, lw, b, h, kc, vc)
-        t_layers += time.perf_counter() - t0
-        del lw
-    wh = nx.bf16_to_f64(synth.head_weight(m))
-    wf = nx.bf16_to_f64(synth.final_norm(m))
+        z = op.final_norm(m, h, wf)
+        op.head_logits(z[-1:], wh, m.n_codebooks, m.cb_vocab)
+        t_head = time.perf_counter() - t0
+        return t_layers / len(host_layers) * m.n_layers + t_head, t_layers
+
+    per_prompt, t_l = stack_time(P)
+    per13, t13 = stack_time(13)
+    # codebook step, B = 64
+    B, K, V = 64, m.n_codebooks, m.cb_vocab
+    logits = nx.bf16_to_f64(synth.codebook_logits(B, K, V, 0, m.eoc_id))
+    st = synth.codebook_state(B, K)
+    cb32 = nx.bf16_to_f32(shared_host["cb"])
     t0 = time.perf_counter()
-    z = op.final_norm(m, h, wf)
-    op.head_logits(z[-1:], wh, m.n_codebooks, m.cb_vocab)
-    t_head = time.perf_counter() - t0
-    per_prompt = t_layers / n_sample_layers * m.n_layers + t_head
+    oc.codebook_step(logits, st["frame"].copy(), st["eoc_seen"].copy(), st["done"].copy(), m.bos_id, m.eoc_id, cb32)
+    t_cb = time.perf_counter() - t0
+    n = len(host_layers)
     return {"value": round(P / per_prompt, 3), "unit": "prompt tok/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_sample_layers} of {m.n_layers} layers of the P={P} prefill in float64 "
-                      f"({t_layers:.1f} s of layer compute), scaled x{m.n_layers / n_sample_layers:g}, "
-                      f"plus final norm + head on the last row",
-            "ms_per_prompt": round(per_prompt * 1e3, 1)}
+            "sample": f"{n} of {m.n_layers} layers of the P={P} prefill in float64 ({t_l:.1f} s of layer compute), "
+                      f"scaled x{m.n_layers / n:g}, plus final norm + head on the last row; the same at P=13 "
+                      f"({t13:.1f} s); one codebook step of 64 streams x {K} x {V}",
+            "ms_per_prompt": round(per_prompt * 1e3, 1),
+            "p13_ms_per_prompt": round(per13 * 1e3, 1),
+            "codebook_b64_us_per_step": round(t_cb * 1e6, 1)}
+
+
+def probe(H, m, layers, shared, dev_layers):
+    """Launches for the counter runs (rocprofv3 --pmc): three P=512 stack
+    steps, the FP8 layer, the memory-bound kernels at sweep sizes and a
+    256 MiB device copy whose counter readings calibrate the byte counters."""
+    import torch
+    st = Stack(H, m, 512, dev_layers, layers, shared)
+    for _ in range(3):
+        st.step()
+    torch.cuda.synchronize()
+    del st
+    fp8_layer(H, m, dev_layers[0], reps=2)
+    sweep = hbm_sweep(H, m, shared, reps=2)
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return sweep
 
 
 def main():
@@ -472,6 +520,8 @@ def main():
     ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
     ap.add_argument("--layers", type=int, default=36)
     ap.add_argument("--headline-only", action="store_true", help="skip the other measurement rows")
+    ap.add_argument("--probe", action="store_true",
+                    help="only the launches the rocprofv3 counter runs read (no timing line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path is built and "
@@ -489,7 +539,11 @@ def main():
     shared = {"embed": dev_bf16(synth.embed_table(m)), "final": dev_bf16(synth.final_norm(m)),
               "head": dev_bf16(synth.head_weight(m)), "cb": dev_bf16(synth.codebook_embed(m))}
     log(f"embedding / head tables ready in {time.time() - t0:.1f} s")
-    dev_layers, layers, host_layers = build_model(H, m, m.n_layers, keep_host=not args.no_cpu)
+    dev_layers, layers, host_layers = build_model(H, m, m.n_layers, keep_host=not args.no_cpu and not args.probe)
+    if args.probe:
+        probe(H, m, layers, shared, dev_layers)
+        log("probe launches done")
+        return
 
     # headline: P = 512
     P = 512
@@ -558,7 +612,9 @@ def main():
         torch.cuda.synchronize()
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(m, P, host_layers)
+        out["cpu_baseline"] = cpu_baseline(m, P, host_layers,
+                                           {"head": synth.head_weight(m), "final": synth.final_norm(m),
+                                            "cb": synth.codebook_embed(m)})
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -762,6 +762,12 @@ static int tiled_fill(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, 
 // conversions for the same LDS reads): at 512 rows QKV 36.9 -> 31.7 us,
 // O 31.4 -> 28.7, gate/up 95.4 -> 87.2, down 52.1 -> 49.0 (weights rotated
 // through 4 copies).  The e4m3 tiles keep their layout (no conversion).
+// Re-swept with fp16 activations at 64, 128 and 4274 rows: the down projection
+// (K 9728) at up to 128 rows takes the O projection's 64 x 64 tiles with 4
+// stages (2 workgroups per CU): 30.1 -> 20.8 us at 64 rows, 38.8 -> 28.3 at
+// 128; every other tile stayed (256 x 128 residual tiles above 1024 rows won
+// alone, O 165.7 -> 159.3 and down 330.0 -> 303.8 us at 4274 rows, but the
+// 36-layer varlen batch got slower with them: 46.3 -> 49.8 ms).
 template <int EPI, bool FP8>
 static int tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
                  hipStream_t st, bool go) {
@@ -790,8 +796,6 @@ static int tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const
       return tiled_fill<EPI, FP8, 128, 128, 2, 4, 4, 128>(x, w, M, N, Kb, e, st, go, 3);
     }
     if (M > 128) return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4>(x, w, M, N, Kb, e, st, go);
-    if (M <= 64 && K_el >= 8192) return tiled_fill<EPI, FP8, 64, 64, 2, 2, 8, 128>(x, w, M, N, Kb, e, st, go);
-    if (K_el >= 8192) return tiled_fill<EPI, FP8, 128, 64, 4, 1, 4, 128>(x, w, M, N, Kb, e, st, go);
     return tiled_fill<EPI, FP8, 64, 64, 2, 2, 4, 128>(x, w, M, N, Kb, e, st, go);
   }
 }
