@@ -150,7 +150,7 @@ def gemm_traffic():
     WRITE_SIZE summary, if it was taken on the current GEMM source (else None)."""
     import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", "gemm_gateup_m512_traffic.md")
+    path = os.path.join(ROOT, "profiles", "gemm_attention_p512_counters.md")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
