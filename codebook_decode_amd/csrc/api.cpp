@@ -324,7 +324,14 @@ hr::AttnSplit attn_plan(const hr_dims* d, const hr_batch* b, const Ws* w) {
     wgs *= sp.n_slots;
     block_tiles = (max_tiles + sp.n_slots - 1) / sp.n_slots;
   }
-  if (wgs < 256 && block_tiles >= 4) sp.groups = 2;
+  // a grid short of the 256 CUs splits each KV head's query heads over two
+  // workgroups (P = 512, one sequence: 128 -> 256 workgroups)
+  const int group = d->n_q_heads / d->n_kv_heads;
+  if (wgs < 256 && group % 2 == 0) {
+    sp.head_split = 2;
+    wgs *= 2;
+  }
+  if (wgs < 512 && block_tiles >= 4) sp.groups = 2;
   return sp;
 }
 

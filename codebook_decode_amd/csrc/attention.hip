@@ -51,12 +51,16 @@ __device__ __forceinline__ void chunk_plan(int n_tiles, int chunk_tiles, int n_s
   n_chunks = (n_tiles + ct - 1) / ct;
 }
 
-// NG groups of 4 wavefronts: group n takes key tiles kt0 + n, kt0 + n + NG, ...
+// NG groups of wavefronts: group n takes key tiles kt0 + n, kt0 + n + NG, ...
 // of the same queries, with its own K/V buffers; the groups' running
 // (max, sum, output) are merged through LDS at the end.  NG = 2 gives a long
-// row two wavefronts per SIMD that hide each other's latencies.
-template <int DH, int GROUP, int NG>
-__global__ __launch_bounds__(256 * NG, 2 / NG) void attention_kernel(
+// row two wavefronts per SIMD that hide each other's latencies.  HSPLIT = 2
+// gives each of two workgroups half the GROUP query heads of a KV head (each
+// stages the same K/V tiles): twice the workgroups, half the work per CU for
+// grids that would leave CUs idle.
+template <int DH, int GROUP, int NG, int HSPLIT = 1>
+__global__ __launch_bounds__(64 * (GROUP / HSPLIT) * (4 / GROUP) * NG) __attribute__((amdgpu_waves_per_eu(2)))
+void attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ start_pos,
     const int32_t* __restrict__ cache_slot, const int32_t* __restrict__ used_keys, int Hq, int Hkv,
@@ -64,17 +68,20 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void attention_kernel(
     int chunk_tiles, int n_slots, float* __restrict__ part_o, float2_t* __restrict__ part_ml, int T) {
   constexpr int QSUB = 4 / GROUP;             // 32-query sub-blocks per workgroup
   constexpr int QPW = 32 * QSUB;
+  constexpr int HPW = GROUP / HSPLIT;         // query heads per workgroup
+  constexpr int GT = 64 * HPW * QSUB;         // threads of one key-tile group
+  static_assert(GROUP % HSPLIT == 0, "heads split evenly");
   constexpr int K_LD = DH + 8;                // padded row of the K tile (elements)
   constexpr int NKS = DH / 16;                // 16-wide d steps of the score MFMA
   constexpr int NDB = DH / 32;                // 32-wide d blocks of the output
   constexpr int KCH = AKT * (DH / 8);         // 16-byte chunks of a K (or V) tile
-  constexpr int KPT = KCH / 256;              // K chunks per thread
-  constexpr int VPT = KCH / 2 / 256;          // V key-pair units per thread (2 loads each)
+  constexpr int KPT = KCH / GT;               // K chunks per thread
+  constexpr int VPT = KCH / 2 / GT;           // V key-pair units per thread (2 loads each)
   static_assert(KPT >= 1 && VPT >= 1, "tile / thread mapping");
   constexpr int kGroupLds = AKT * K_LD + DH * VT_LD;   // elements of one group's K and V^T tiles
   __shared__ __attribute__((aligned(16))) uint16_t smem[NG * kGroupLds];
 
-  const int s = blockIdx.z, g = blockIdx.y;
+  const int s = blockIdx.z, g = int(blockIdx.y) / HSPLIT, hsel = int(blockIdx.y) % HSPLIT;
   const int len = cu[s + 1] - cu[s];
   // blockIdx.x = (query block, key chunk slot); longest causal rows first
   const int qb = gridDim.x / n_slots - 1 - int(blockIdx.x) / n_slots;
@@ -85,12 +92,12 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void attention_kernel(
   const int start = start_pos[s];
   const size_t base = size_t(cache_slot[s]) * capacity;
   const int lane = threadIdx.x & 63;
-  const int grp = int(threadIdx.x) >> 8;            // key-tile group
-  const int tid = threadIdx.x & 255, wave = tid >> 6;   // within the group
+  const int grp = int(threadIdx.x) / GT;            // key-tile group
+  const int tid = int(threadIdx.x) % GT, wave = tid >> 6;   // within the group
   uint16_t* sK = smem + grp * kGroupLds;
   uint16_t* sVt = sK + AKT * K_LD;
-  const int hg = wave % GROUP, qsub = wave / GROUP;
-  const int hh = g * GROUP + hg;
+  const int hg = wave % HPW, qsub = wave / HPW;
+  const int hh = g * GROUP + hsel * HPW + hg;
   const int half = lane >> 5, r32 = lane & 31;
   const int iq = i0 + qsub * 32 + r32;        // this lane's query (sequence-relative)
   const bool qok = iq < len;
@@ -106,15 +113,15 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void attention_kernel(
   const int kt0 = ck * ct;
   const int kt1 = min(n_tiles_all, kt0 + ct);
 
-  // the wave's queries as the B operand: query r32, d = 16 ks + 8 half + [0,8)
+  // the wave's queries as the B operand: query r32, d = 16 ks + 8 half + [0,8).
+  // A lane past the block's end takes the sequence's first query instead (its
+  // finite results are never stored); no select on the loaded values, so the
+  // first K/V fetch below issues while these loads are in flight.
   u32x4 qf[NKS];
   {
     const uint16_t* qrow = q + (size_t(tok0 + (qok ? iq : 0)) * Hq + hh) * DH;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qrow + ks * 16 + half * 8);
-      qf[ks] = qok ? v : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qrow + ks * 16 + half * 8);
   }
 
   // K/V tile fetch into registers: K chunk c -> (key c / (DH/8), d8 c % (DH/8));
@@ -129,14 +136,14 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void attention_kernel(
   auto fetch = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const int c = tid + 256 * j;
+      const int c = tid + GT * j;
       const int key = c / (DH / 8), d8 = c % (DH / 8);
       const int row = min(k0 + key, last_key);
       rk[j] = *reinterpret_cast<const u32x4*>(kbase + size_t(row) * row_stride + d8 * 8);
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-      const int u = tid + 256 * j;
+      const int u = tid + GT * j;
       const int key = 2 * (u % (AKT / 2)), d8 = u / (AKT / 2);
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
@@ -148,13 +155,13 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void attention_kernel(
   auto stage = [&]() {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const int c = tid + 256 * j;
+      const int c = tid + GT * j;
       const int key = c / (DH / 8), d8 = c % (DH / 8);
       *reinterpret_cast<u32x4*>(sK + key * K_LD + d8 * 8) = bf8_to_f16x8(rk[j]);
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-      const int u = tid + 256 * j;
+      const int u = tid + GT * j;
       const int key = 2 * (u % (AKT / 2)), d8 = u / (AKT / 2);
       const u32x4 a = bf8_to_f16x8(rv[j][0]), b = bf8_to_f16x8(rv[j][1]);
 #pragma unroll
@@ -267,13 +274,13 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void attention_kernel(
 
   if constexpr (NG > 1) {
     // merge the groups' partial softmaxes into group 0 (through the now idle
-    // tile buffers: 4 waves x 64 lanes x (2 + 16 NDB) floats per group)
+    // tile buffers: GT lanes x (2 + 16 NDB) floats per group)
     constexpr int kVals = 2 + 16 * NDB;
-    static_assert(size_t(NG - 1) * 256 * kVals * 4 <= sizeof(smem), "merge buffer");
+    static_assert(size_t(NG - 1) * GT * kVals * 4 <= sizeof(smem), "merge buffer");
     float* xch = reinterpret_cast<float*>(smem);
     __syncthreads();
     if (grp > 0) {
-      float* my = xch + (size_t(grp - 1) * 256 + tid) * kVals;
+      float* my = xch + (size_t(grp - 1) * GT + tid) * kVals;
       my[0] = m_run;
       my[1] = l_part;
 #pragma unroll
@@ -285,7 +292,7 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void attention_kernel(
     if (grp > 0) return;
 #pragma unroll
     for (int g2 = 1; g2 < NG; ++g2) {
-      const float* ot = xch + (size_t(g2 - 1) * 256 + tid) * kVals;
+      const float* ot = xch + (size_t(g2 - 1) * GT + tid) * kVals;
       const float m2 = ot[0];
       const float mm = fmaxf(m_run, m2);
       const float a1 = (m_run == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
@@ -631,20 +638,30 @@ static void launch_attn_t(const void* q, const void* kc, const void* vc, const i
   constexpr int QPW = 32 * (4 / GROUP);
   const int n_qb = (max_len + QPW - 1) / QPW;
   const int slots = sp_cfg.chunk_tiles > 0 ? sp_cfg.n_slots : 1;
-  dim3 grid(n_qb * slots, Hkv, n_seq);
+  // head split only where the group divides (GROUP 2 and 4)
+  const int hsplit = (sp_cfg.head_split == 2 && GROUP % 2 == 0) ? 2 : 1;
+  dim3 grid(n_qb * slots, Hkv * hsplit, n_seq);
   const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf(float(DH));
-  if (sp_cfg.groups == 2)
-    attention_kernel<DH, GROUP, 2><<<grid, 512, 0, st>>>(
-        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
-        static_cast<const uint16_t*>(vc), cu, sp, slot, used, Hq, Hkv, cap, causal ? 1 : 0,
-        scale_log2, out, fp8 ? 1 : 0, out_inv, sp_cfg.chunk_tiles, slots, sp_cfg.part_o,
-        reinterpret_cast<float2_t*>(sp_cfg.part_ml), sp_cfg.T);
-  else
-    attention_kernel<DH, GROUP, 1><<<grid, 256, 0, st>>>(
-        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
-        static_cast<const uint16_t*>(vc), cu, sp, slot, used, Hq, Hkv, cap, causal ? 1 : 0,
-        scale_log2, out, fp8 ? 1 : 0, out_inv, sp_cfg.chunk_tiles, slots, sp_cfg.part_o,
-        reinterpret_cast<float2_t*>(sp_cfg.part_ml), sp_cfg.T);
+#define HR_ATT_LAUNCH(NG_, HS_)                                                                  \
+  attention_kernel<DH, GROUP, NG_, HS_><<<grid, 64 * (GROUP / HS_) * (4 / GROUP) * NG_, 0, st>>>( \
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),                         \
+      static_cast<const uint16_t*>(vc), cu, sp, slot, used, Hq, Hkv, cap, causal ? 1 : 0,        \
+      scale_log2, out, fp8 ? 1 : 0, out_inv, sp_cfg.chunk_tiles, slots, sp_cfg.part_o,          \
+      reinterpret_cast<float2_t*>(sp_cfg.part_ml), sp_cfg.T)
+  if constexpr (GROUP % 2 == 0) {
+    if (hsplit == 2) {
+      if (sp_cfg.groups == 2) HR_ATT_LAUNCH(2, 2);
+      else HR_ATT_LAUNCH(1, 2);
+    } else if (sp_cfg.groups == 2) {
+      HR_ATT_LAUNCH(2, 1);
+    } else {
+      HR_ATT_LAUNCH(1, 1);
+    }
+  } else {
+    if (sp_cfg.groups == 2) HR_ATT_LAUNCH(2, 1);
+    else HR_ATT_LAUNCH(1, 1);
+  }
+#undef HR_ATT_LAUNCH
   if (sp_cfg.chunk_tiles > 0)
     attention_merge_kernel<DH><<<dim3(sp_cfg.T, (Hq * (DH / 4) + 255) / 256), 256, 0, st>>>(
         cu, sp, used, n_seq, Hq, causal ? 1 : 0, QPW,

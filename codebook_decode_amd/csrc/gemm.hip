@@ -375,11 +375,17 @@ struct TileCfg {
   static constexpr int kJN = BN / WN / 32;                  // 32-col blocks per wave
   static constexpr int kChunks = SB / 16;                   // 16-byte chunks per row
   static constexpr int kRowsPerCopy = 1024 / SB;            // rows per 1 KB wave copy
-  static constexpr int kCopies = (BM + BN) / kRowsPerCopy;  // 1 KB wave copies per slab
-  static constexpr int kLPS = kCopies / (WM * WN);          // copies per wave per slab
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kCopies = (BM + BN) / kRowsPerCopy;  // 1 KB copies per slab
+  static constexpr int kFull = kCopies / kWaves;            // whole copies per wave
+  static constexpr int kRem = kCopies % kWaves;             // left over: one partial copy per wave
+  static constexpr int kPartLanes = kRem * 64 / kWaves;     // lanes of each wave's partial copy
+  static constexpr int kLPS = kFull + (kRem ? 1 : 0);       // copy instructions per wave per slab
   static constexpr int kSlabA = BM * SB, kSlabB = BN * SB;
   static constexpr size_t kLds = size_t(STAGES) * (kSlabA + kSlabB);
-  static_assert(kCopies % (WM * WN) == 0, "copies must split evenly over the waves");
+  static_assert(BM % kRowsPerCopy == 0 && BN % kRowsPerCopy == 0, "whole copies per operand");
+  static_assert(kRem * 64 % kWaves == 0, "left-over copies split evenly over the waves");
+  static_assert(kRem == 0 || kFull * kWaves >= BM / kRowsPerCopy, "partial copies lie in B");
   static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "tile shape");
 };
 
@@ -396,7 +402,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
   constexpr int IM = C::kIM, JN = C::kJN, LPS = C::kLPS, NC = C::kChunks / 2;
   static_assert(EPI != HR_EPI_SWIGLU || JN % 2 == 0, "SwiGLU waves hold gate/up block pairs");
   constexpr int kSc = MX ? (BM + BN + 255) / 256 : 0;   // scale copies per slab
-  static_assert(!MX || (!FP8 && SB == 64 && WM * WN >= kSc), "MXFP4: 128-value (64-byte) slabs");
+  static_assert(!MX || (!FP8 && SB == 64 && WM * WN >= kSc && C::kRem == 0), "MXFP4: 128-value (64-byte) slabs");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* sA = smem;                                   // [STAGES][BM rows][64 B]
   uint8_t* sB = smem + STAGES * C::kSlabA;              // [STAGES][BN rows][64 B]
@@ -404,10 +410,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
   const int wm = wave / WN, wn = wave % WN;
   uint8_t* sS = smem + STAGES * (C::kSlabA + C::kSlabB);   // MX: [STAGES][kSc KB: A rows, B rows] scales
   // XCD-aware order: consecutive workgroup ids go round-robin over the 8 XCDs;
-  // give each XCD a contiguous run of tiles so the m-tiles that share a weight
-  // tile are served by one L2
+  // give each XCD a contiguous run of tiles (XCD x: n/8 of them, one more for
+  // x < n % 8) so the m-tiles that share a weight tile are served by one L2
   int bid = blockIdx.x;
-  if (n_tiles % 8 == 0) bid = (bid % 8) * (n_tiles / 8) + bid / 8;
+  {
+    const int q8 = n_tiles >> 3, r8 = n_tiles & 7, xcd = bid & 7;
+    bid = xcd * q8 + min(xcd, r8) + (bid >> 3);
+  }
   // grouped order: runs of GM m-tiles sweep n together, so the tiles running
   // at once on one XCD share a few A and B panels in its L2
   constexpr int GM = 4;
@@ -418,20 +427,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
   const int tm = first_m + in_group % gm, tn = in_group / gm;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // this wave's LPS 1-KB copies per slab: copy q covers 1024/SB rows of A or of
-  // B; lane i fills LDS chunk 64 q' + i of that operand.  Sources are 32-bit
-  // byte offsets from x or w (the host keeps both operands under 2 GB).
+  // this wave's LPS copies per slab over the slab's 16-byte chunks (A rows,
+  // then B rows): whole copy j takes chunks 64 (wave + j waves) + lane; when
+  // the copies do not split evenly, the left-over ones (all in B) are shared
+  // out as one partial copy per wave of kPartLanes lanes.  Lane i of a copy
+  // fills LDS chunk (first chunk of the copy) + i of its operand.  Sources are
+  // 32-bit byte offsets from x or w (the host keeps both operands under 2 GB).
   uint32_t src[LPS];
   int dst_off[LPS];
 #pragma unroll
   for (int j = 0; j < LPS; ++j) {
-    const int q = wave + j * (WM * WN);
-    const bool is_a = q < BM / C::kRowsPerCopy;
-    const int qq = is_a ? q : q - BM / C::kRowsPerCopy;
-    const int chunk = qq * 64 + lane;
+    const bool part = C::kRem > 0 && j == C::kFull;
+    const int first = part ? C::kFull * C::kWaves * 64 + wave * C::kPartLanes : (wave + j * C::kWaves) * 64;
+    const int ln = part ? min(lane, C::kPartLanes - 1) : lane;
+    const bool is_a = first < BM * C::kChunks;
+    const int op_first = is_a ? first : first - BM * C::kChunks;   // first chunk within the operand
+    const int chunk = op_first + ln;
     const int row = chunk / C::kChunks, pc = chunk % C::kChunks;
     const int lc = pc ^ swz<SB>(row);
-    dst_off[j] = is_a ? qq * 1024 : STAGES * C::kSlabA + qq * 1024;
+    dst_off[j] = is_a ? op_first * 16 : STAGES * C::kSlabA + op_first * 16;
     if (is_a) {
       src[j] = uint32_t(min(m0 + row, M - 1)) * uint32_t(K_bytes) + lc * 16;
     } else {
@@ -483,6 +497,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
 #pragma unroll
     for (int j = 0; j < LPS; ++j) {
       const bool is_a = dst_off[j] < STAGES * C::kSlabA;
+      // a partial copy keeps lanes [0, kPartLanes) (lane 0 is always active, so
+      // every wave issues LPS copies and the vmcnt waits below stay uniform)
+      if (C::kRem > 0 && j == C::kFull && lane >= C::kPartLanes) continue;
       lds_copy16((is_a ? x : w) + src[j] + ko, smem + dst_off[j] + stage * (is_a ? C::kSlabA : C::kSlabB));
     }
     if constexpr (MX) {
@@ -504,13 +521,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // The ring always has STAGES - 1 slabs in flight ahead of the one being
-  // consumed: past the last slab a copy repeats the last slab into a slot that
-  // is never read again, so every wait below has the same count.
-  if (n_slabs > 0) {
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) issue(sl0 + min(s, n_slabs - 1), s);
-  }
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < n_slabs) issue(sl0 + s, s);
 
   // a lane reads row (lane % 32) of each 32-row block, NC chunks of the slab:
   // bf16 chunk 2c + h feeds k-step c; e4m3 chunks 4m + 2h + {0, 1} feed MFMA m
@@ -562,7 +575,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
   Frag fa0[IM], fb0[JN], fa1[IM], fb1[JN];
   uint32_t sa0[IM], sb0[JN], sa1[IM], sb1[JN];
   if (n_slabs > 0) {
-    wait_slabs(STAGES - 2);
+    wait_slabs(min(STAGES - 2, n_slabs - 1));
     lds_barrier();
     read_frags(0, fa0, fb0, sa0, sb0);
   }
@@ -581,19 +594,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
 #pragma unroll
         for (int c = 0; c < NC; ++c) fb[j][c] = bf8_to_f16x8(fb[j][c]);
     }
-    wait_slabs(STAGES - 3);
+    wait_slabs(min(STAGES - 3, n_slabs - 2 - it));
     lds_barrier();
+    // refill the slot of slab it - 1 (every wave finished reading it before
+    // this barrier).  Issued here, ahead of the MFMAs: placed after them (in
+    // program order) the copies ran a slab later, which measured a wash in the
+    // 36-layer stack (QKV and O 0.2-0.4 us faster, the weight-streaming down
+    // projection 1.5 us slower) though faster in isolation
+    if (it + STAGES - 1 < n_slabs) issue(sl0 + it + STAGES - 1, (it + STAGES - 1) % STAGES);
     // the next slab's fragments (after the last slab: a stale slot, never
     // used), issued one-for-one between this slab's MFMAs: issue is in order,
     // so a burst of LDS reads stalled behind the copies into LDS would
     // otherwise leave the matrix pipe idle (10% on the gate/up GEMM at M=512)
     read_frags((it + 1) % STAGES, fan, fbn, san, sbn);
     mma_slab(fa, fb, sa, sb);
-    // refill the slot of slab it - 1 (every wave finished reading it before
-    // this iteration's barrier); placed after the MFMAs in program order, the
-    // copies issue behind most of them instead of stalling the first ones
-    // (M = 512: QKV 31.1 -> 28.9 us, O 27.9 -> 26.3, down 49.5 -> 48.2)
-    issue(sl0 + min(it + STAGES - 1, n_slabs - 1), (it + STAGES - 1) % STAGES);
 #pragma unroll
     for (int q = 0; q < (kReads < kMfma ? kReads : kMfma); ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
@@ -608,7 +622,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
     step(fa0, fb0, sa0, sb0, fa1, fb1, sa1, sb1);
     if (it < n_slabs) step(fa1, fb1, sa1, sb1, fa0, fb0, sa0, sb0);
   }
-  wait_vm<0>();   // the trailing repeat copies land before the workgroup ends
 
   // epilogue: 32x32 accumulator layout, lane holds column lane % 32 and rows
   // 8 (r / 4) + 4 (lane / 32) + r % 4 of its block, r = 0..15

@@ -69,6 +69,7 @@ void launch_rope_attn_small(const void* qkv, int n_seq, int max_len, int Hq, int
 struct AttnSplit {
   bool decode = false;      // one row per sequence: decode_attention_kernel (+ merge when chunked)
   int groups = 1;           // wave groups interleaving the key tiles of a block (1 or 2)
+  int head_split = 1;       // workgroups sharing a KV head's query heads (1 or 2)
   int chunk_tiles = 0;      // 0: no split
   int n_slots = 1;
   float* part_o = nullptr;  // [n_slots, T, Hq, d]
