@@ -37,24 +37,37 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def build_model(H, m, n_layers, keep_host=False):
-    """Seeded weights of every layer, uploaded; returns device tensors, structs
-    and (keep_host) the host bf16 bit patterns for the CPU oracle."""
+def weight_shapes(m):
+    return {"w_qkv": (m.qkv_rows, m.hidden), "w_o": (m.hidden, m.attn_width), "w_gu": (2 * m.ffn, m.hidden),
+            "w_down": (m.hidden, m.ffn)}
+
+
+def build_model(H, m, n_layers, keep_host=False, packed=True):
+    """Seeded bf16 weights of every layer, uploaded; with `packed` also their
+    hr_pack_weight form (prepared once here, outside every timed region).
+    Returns the bf16 device tensors, the packed ones (or None), the layer
+    structs of the timed path and (keep_host) the host bf16 bit patterns for
+    the CPU oracle."""
     import torch
     import synth
     from model_util import upload_layer
-    layers, dev_layers, host = [], [], []
+    layers, dev_layers, pk_layers, host = [], [], [], []
     t0 = time.time()
     for l in range(n_layers):
         bits = synth.layer_tensors(m, l)
         dl = upload_layer(bits)
         dev_layers.append(dl)
-        layers.append(H.make_layer(dl))
+        if packed:
+            dp = H.pack_layer_weights(dl, weight_shapes(m))
+            pk_layers.append(dp)
+            layers.append(H.make_layer(dp, H.HR_F16_PACKED))
+        else:
+            layers.append(H.make_layer(dl))
         if keep_host:
             host.append(bits)
     torch.cuda.synchronize()
-    log(f"weights of {n_layers} layers drawn and uploaded in {time.time() - t0:.1f} s")
-    return dev_layers, layers, host
+    log(f"weights of {n_layers} layers drawn, uploaded{' and packed' if packed else ''} in {time.time() - t0:.1f} s")
+    return dev_layers, (pk_layers if packed else None), layers, host
 
 
 class Stack:
@@ -132,15 +145,16 @@ def time_kernel_events(fn_list, reps=3):
     return start.elapsed_time(end) / 1e3 / n
 
 
-def gemm_gu_launches(H, m, P, dev_layers):
-    """The gate/up + SwiGLU GEMM of the P-row prefill, one launch per layer's weights."""
+def gemm_gu_launches(H, m, P, dev_layers, wtype):
+    """The gate/up + SwiGLU GEMM of the P-row prefill, one launch per layer's
+    weights (in the timed path's format)."""
     import torch
     x = torch.randn((P, m.hidden), device="cuda").to(torch.float16)
     out = torch.empty((P, m.ffn), dtype=torch.float16, device="cuda")
     fns = []
     for dl in dev_layers:
         w = dl["w_gu"]
-        fns.append(lambda w=w: H.hr_linear(x, w, None, 1.0, H.HR_BF16, P, 2 * m.ffn, m.hidden, H.HR_EPI_SWIGLU,
+        fns.append(lambda w=w: H.hr_linear(x, w, None, 1.0, wtype, P, 2 * m.ffn, m.hidden, H.HR_EPI_SWIGLU,
                                            out))
     return fns
 
@@ -184,8 +198,8 @@ def hbm(bytes_, sec):
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def layer_rotated(H, m, dev_layers, lens=(6, 13), copies=4, reps=40):
-    """One bf16 layer at P tokens, rotating through `copies` layers' weights
+def layer_rotated(H, m, dev_layers, lens=(6, 13), copies=4, reps=40, wtype=None):
+    """One layer at P tokens, rotating through `copies` layers' weights
     (807 MB > the 256 MB MALL, so every call streams its weights from HBM)."""
     import torch
     import synth
@@ -193,7 +207,8 @@ def layer_rotated(H, m, dev_layers, lens=(6, 13), copies=4, reps=40):
     from model_util import dims_of, kv_cache, workspace
     dims = dims_of(H, m, True, 1)
     cap = 2048
-    layers = [H.make_layer(dl) for dl in dev_layers[:copies]]
+    wtype = H.HR_BF16 if wtype is None else wtype
+    layers = [H.make_layer(dl, wtype) for dl in dev_layers[:copies]]
     kvt = [kv_cache(m, 1, cap, poison=False) for _ in range(copies)]
     kvs = [H.make_kv(k, v, cap, 1) for k, v in kvt]
     weight_bytes = sum(t.numel() * t.element_size() for t in dev_layers[0].values())
@@ -520,6 +535,8 @@ def main():
     ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
     ap.add_argument("--layers", type=int, default=36)
     ap.add_argument("--headline-only", action="store_true", help="skip the other measurement rows")
+    ap.add_argument("--weights", choices=("packed", "bf16"), default="packed",
+                    help="timed path: bf16 weights packed once by hr_pack_weight (the same products) or as stored")
     ap.add_argument("--probe", action="store_true",
                     help="only the launches the rocprofv3 counter runs read (no timing line)")
     args = ap.parse_args()
@@ -539,7 +556,12 @@ def main():
     shared = {"embed": dev_bf16(synth.embed_table(m)), "final": dev_bf16(synth.final_norm(m)),
               "head": dev_bf16(synth.head_weight(m)), "cb": dev_bf16(synth.codebook_embed(m))}
     log(f"embedding / head tables ready in {time.time() - t0:.1f} s")
-    dev_layers, layers, host_layers = build_model(H, m, m.n_layers, keep_host=not args.no_cpu and not args.probe)
+    packed = args.weights == "packed"
+    dev_layers, pk_layers, layers, host_layers = build_model(H, m, m.n_layers,
+                                                             keep_host=not args.no_cpu and not args.probe,
+                                                             packed=packed)
+    wtype = H.HR_F16_PACKED if packed else H.HR_BF16
+    run_layers = pk_layers if packed else dev_layers      # device weights of the timed path
     if args.probe:
         probe(H, m, layers, shared, dev_layers)
         log("probe launches done")
@@ -559,7 +581,7 @@ def main():
     weight_bytes = sum(sum(t.numel() * t.element_size() for t in dl.values()) for dl in dev_layers)
     head_bytes = shared["head"].numel() * 2
     # dominant kernel at P=512: the gate/up GEMM (49% of the layer's FLOPs)
-    fns = gemm_gu_launches(H, m, P, dev_layers)
+    fns = gemm_gu_launches(H, m, P, run_layers, wtype)
     t_gu = time_kernel_events(fns)
     flops_gu = 2.0 * P * m.hidden * 2 * m.ffn
     achieved = flops_gu / t_gu / 1e12
@@ -571,12 +593,15 @@ def main():
         "metric": METRIC, "value": round(tok_s, 1), "unit": "prompt tok/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "numerics": ("bf16 weights (" + ("packed once to fp16 by hr_pack_weight: the same values, bit-identical "
+                     "results to the unpacked path" if packed else "as stored") + "); fp16 activations into fp16 "
+                     "MFMAs with fp32 accumulation; fp32 residual; bf16 KV cache"),
         "data": "synthetic (seeded N(0,0.02) weights, uniform token ids)",
         "config": {"workload": f"stack{m.n_layers}_d2560_p512: Qwen3-style 4B decoder stack, {m.n_layers} layers, "
                                "hidden 2560, 32/8 heads x 128, SwiGLU 9728, single prompt P=512, causal, "
                                "KV cache 2048, audio head 8 x 1026 + delayed-codebook step",
-                   "prompt_len": P, "layers": m.n_layers, "graph": bool(args.graph)},
-        "roofline": {"bound": "mfma", "kernel": "gemm_tiled SwiGLU (gate/up 512 x 19456 x 2560)",
+                   "prompt_len": P, "layers": m.n_layers, "graph": bool(args.graph), "weights": args.weights},
+        "roofline": {"bound": "mfma", "kernel": f"gemm_tiled SwiGLU (gate/up 512 x 19456 x 2560, {args.weights} weights)",
                      "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": gemm_traffic(),
                      "avg_launch_us": round(t_gu * 1e6, 2)},
@@ -598,7 +623,13 @@ def main():
         del st128
         out["p128"] = {"ms_per_prompt": round(sec128 * 1e3, 4),
                        "roofline": hbm(weight_bytes + head_bytes, sec128)}
-        out["layer_d2560"] = layer_rotated(H, m, dev_layers)
+        out["layer_d2560"] = layer_rotated(H, m, run_layers, wtype=wtype)
+        if packed:
+            # the same stack on the weights as stored (bf16, converted in registers)
+            st_b = Stack(H, m, P, dev_layers, [H.make_layer(dl) for dl in dev_layers], shared)
+            sec_b = time_steps(st_b.step, args.steps, args.warmup, args.graph)
+            del st_b
+            out["stack_p512_bf16_layout"] = {"ms_per_step": round(sec_b * 1e3, 4), "tok_s": round(P / sec_b, 1)}
         out["fp8_layer"] = fp8_layer(H, m, dev_layers[0])
         out["mxfp4_layer"] = mxfp4_layer(H, m, dev_layers[0])
         out["varlen32"] = varlen_batch(H, m, layers, shared)

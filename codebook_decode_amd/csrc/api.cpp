@@ -125,7 +125,7 @@ hr_status check_batch(const hr_dims* d, const hr_batch* b, const hr_kv* kv) {
 
 hr_status check_layer(const hr_dims* d, const hr_layer* L, int idx) {
   if (!L) return fail(HR_EINVAL, "layer %d is NULL", idx);
-  if (L->wtype != HR_BF16 && L->wtype != HR_FP8_E4M3 && L->wtype != HR_MXFP4)
+  if (L->wtype != HR_BF16 && L->wtype != HR_FP8_E4M3 && L->wtype != HR_MXFP4 && L->wtype != HR_F16_PACKED)
     return fail(HR_EINVAL, "layer %d: bad wtype", idx);
   const void* ptrs[] = {L->in_norm_w, L->post_norm_w, L->q_norm_w, L->k_norm_w,
                         L->w_qkv,     L->w_o,         L->w_gu,     L->w_down};
@@ -195,7 +195,7 @@ int residual_ks(const hr_dims* d, int32_t T) {
   for (int K : {A, F}) {
     for (bool fp8 : {false, true}) {
       if (fp8 && K % 128) continue;
-      const int k = hr::launch_linear(nullptr, nullptr, nullptr, 1.f, fp8, T, D, K, HR_EPI_RESIDUAL, nullptr, 0.f,
+      const int k = hr::launch_linear(nullptr, nullptr, nullptr, 1.f, fp8, false, T, D, K, HR_EPI_RESIDUAL, nullptr, 0.f,
                                       nullptr, false, nullptr);
       ks = k > ks ? k : ks;
     }
@@ -364,7 +364,7 @@ hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_layer* next, c
                     const hr_kv* kv, const Ws& w, bool x_ready, hipStream_t st) {
   const int T = b->total_tokens, D = d->hidden, F = d->ffn, Hq = d->n_q_heads, Hkv = d->n_kv_heads;
   const int dh = d->head_dim, A = Hq * dh, NQKV = (Hq + 2 * Hkv) * dh;
-  const bool fp8 = L->wtype == HR_FP8_E4M3, mx = L->wtype == HR_MXFP4;
+  const bool fp8 = L->wtype == HR_FP8_E4M3, mx = L->wtype == HR_MXFP4, pk = L->wtype == HR_F16_PACKED;
   const float eps = d->rms_eps;
   const hr::AttnSplit split = attn_plan(d, b, &w);
   if (!x_ready) {
@@ -373,7 +373,7 @@ hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_layer* next, c
     in_norm_mode(L, &mode, &inv);
     hr::launch_residual_norm(h, nullptr, 0, T, D, L->in_norm_w, eps, mode, w.x, inv, nullptr, nullptr, 0, st);
   }
-  hr::launch_linear(w.x, L->w_qkv, L->ws_qkv, L->as_qkv, fp8, T, NQKV, D, HR_EPI_F32, w.qkv, 0.f, nullptr, true,
+  hr::launch_linear(w.x, L->w_qkv, L->ws_qkv, L->as_qkv, fp8, pk, T, NQKV, D, HR_EPI_F32, w.qkv, 0.f, nullptr, true,
                     st);
   if (split.decode && d->causal) {
     hr::launch_decode_rope_attention(w.qkv, L->q_norm_w, L->k_norm_w, d->rope_theta, eps, kv->k, kv->v,
@@ -414,15 +414,15 @@ hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_layer* next, c
                              nullptr, 0, st);
     return check_launch("prefill layer (MXFP4)");
   }
-  int ks = hr::launch_linear(w.attn, L->w_o, L->ws_o, L->as_o, fp8, T, D, A, HR_EPI_RESIDUAL, h, 0.f, w.part, true,
-                             st);
+  int ks = hr::launch_linear(w.attn, L->w_o, L->ws_o, L->as_o, fp8, pk, T, D, A, HR_EPI_RESIDUAL, h, 0.f, w.part,
+                             true, st);
   hr::launch_residual_norm(h, w.part, ks > 1 ? ks : 0, T, D, L->post_norm_w, eps,
                            fp8 ? hr::kNormE4M3 : hr::kNormF16, w.x, fp8 ? 1.0f / L->as_gu : 1.f, nullptr, nullptr, 0,
                            st);
-  hr::launch_linear(w.x, L->w_gu, L->ws_gu, L->as_gu, fp8, T, 2 * F, D, HR_EPI_SWIGLU, w.act,
+  hr::launch_linear(w.x, L->w_gu, L->ws_gu, L->as_gu, fp8, pk, T, 2 * F, D, HR_EPI_SWIGLU, w.act,
                     fp8 ? L->as_down : 0.f, nullptr, true, st);
-  ks = hr::launch_linear(w.act, L->w_down, L->ws_down, L->as_down, fp8, T, D, F, HR_EPI_RESIDUAL, h, 0.f, w.part,
-                         true, st);
+  ks = hr::launch_linear(w.act, L->w_down, L->ws_down, L->as_down, fp8, pk, T, D, F, HR_EPI_RESIDUAL, h, 0.f,
+                         w.part, true, st);
   hr::launch_residual_norm(h, w.part, ks > 1 ? ks : 0, T, D, next_w, eps, next_mode, w.x, next_inv, nullptr, nullptr,
                            0, st);
   return check_launch("prefill layer");
@@ -793,8 +793,8 @@ size_t hr_linear_workspace_bytes(hr_wtype wtype, int32_t M, int32_t N, int32_t K
   } else {
     const bool fp8 = wtype == HR_FP8_E4M3;
     if (K % (fp8 ? 128 : 64)) return 0;
-    ks = hr::launch_linear(nullptr, nullptr, nullptr, 1.f, fp8, M, N, K, HR_EPI_RESIDUAL, nullptr, 0.f, nullptr,
-                           false, nullptr);
+    ks = hr::launch_linear(nullptr, nullptr, nullptr, 1.f, fp8, false, M, N, K, HR_EPI_RESIDUAL, nullptr, 0.f,
+                           nullptr, false, nullptr);
   }
   return ks > 1 ? up256(size_t(ks) * size_t(M) * size_t(N) * 4) : 0;
 }
@@ -804,13 +804,15 @@ hr_status hr_linear(const void* x, const void* w, const float* w_scale, float x_
                     size_t ws_bytes, hipStream_t stream) {
   if (M < 0 || N <= 0 || K <= 0) return fail(HR_EINVAL, "bad M=%d N=%d K=%d", M, N, K);
   if (epi != HR_EPI_F32 && epi != HR_EPI_RESIDUAL && epi != HR_EPI_SWIGLU) return fail(HR_EINVAL, "bad epilogue");
-  if (wtype != HR_BF16 && wtype != HR_FP8_E4M3) return fail(HR_EINVAL, "bad wtype");
-  const bool fp8 = wtype == HR_FP8_E4M3;
+  if (wtype != HR_BF16 && wtype != HR_FP8_E4M3 && wtype != HR_F16_PACKED) return fail(HR_EINVAL, "bad wtype");
+  const bool fp8 = wtype == HR_FP8_E4M3, pk = wtype == HR_F16_PACKED;
   if (K % (fp8 ? 128 : 64)) return fail(HR_EUNSUPPORTED, "K = %d must be a multiple of %d", K, fp8 ? 128 : 64);
   if (uint64_t(M > N ? M : N) * K * (fp8 ? 1 : 2) >= (uint64_t(1) << 32))
     return fail(HR_EUNSUPPORTED, "an operand of %d x %d or %d x %d exceeds 4 GB", M, K, N, K);
   if (N % 16 || (epi == HR_EPI_SWIGLU && N % 32))
     return fail(HR_EUNSUPPORTED, "N = %d must be a multiple of 16 (32 for SwiGLU)", N);
+  if (pk && epi == HR_EPI_SWIGLU && N % 64)
+    return fail(HR_EUNSUPPORTED, "packed gate/up: N = %d must be a multiple of 64", N);
   HR_TRY(need(x, "x"));
   HR_TRY(need(w, "w"));
   HR_TRY(need(out, "out"));
@@ -826,12 +828,29 @@ hr_status hr_linear(const void* x, const void* w, const float* w_scale, float x_
     HR_TRY(need(ws, "ws"));
   }
   if (M == 0) return HR_OK;
-  const int ks = hr::launch_linear(x, w, w_scale, x_scale, fp8, M, N, K, epi, out, out_scale,
+  const int ks = hr::launch_linear(x, w, w_scale, x_scale, fp8, pk, M, N, K, epi, out, out_scale,
                                    static_cast<float*>(ws), true, stream);
   if (epi == HR_EPI_RESIDUAL && ks > 1)
     hr::launch_residual_sum(static_cast<float*>(out), static_cast<const float*>(ws), ks, size_t(M) * size_t(N),
                             stream);
   return check_launch("linear");
+}
+
+hr_status hr_pack_weight(const void* w, int32_t N, int32_t K, int32_t gate_up, void* out, hipStream_t stream) {
+  if (N <= 0 || K <= 0 || K % 32) return fail(HR_EINVAL, "bad N=%d / K=%d (K a multiple of 32)", N, K);
+  if (gate_up != 0 && gate_up != 1) return fail(HR_EINVAL, "gate_up must be 0 or 1");
+  if (gate_up && N % 64) return fail(HR_EUNSUPPORTED, "gate/up: N = 2F = %d must be a multiple of 64", N);
+  if (uint64_t(N) * uint64_t(K) * 2 >= (uint64_t(1) << 31))
+    return fail(HR_EUNSUPPORTED, "a %d x %d weight exceeds 2 GB", N, K);
+  HR_TRY(need(w, "w"));
+  HR_TRY(need(out, "out"));
+  const uintptr_t a = reinterpret_cast<uintptr_t>(w), o = reinterpret_cast<uintptr_t>(out);
+  const uintptr_t bytes = uintptr_t(N) * uintptr_t(K) * 2;
+  if (a < o + bytes && o < a + bytes) return fail(HR_EINVAL, "out overlaps w");
+  const int rc = hr::launch_pack_weight(w, N, K, gate_up != 0, out, stream);
+  if (rc < 0) return fail(HR_EHIP, "pack weight: %s", hipGetErrorString(hipGetLastError()));
+  if (rc > 0) return fail(HR_EINVAL, "a weight is outside the fp16 range (|w| >= 65520, inf or NaN)");
+  return HR_OK;
 }
 
 hr_status hr_residual_rmsnorm(float* h, const float* partials, int32_t n_partials, int32_t T, int32_t D,

@@ -28,6 +28,7 @@
 //    by global_load_lds (no register round trip) through a multi-stage ring,
 //    XOR-swizzled so fragment reads are free of bank conflicts, one barrier per
 //    slab, fragment reads of the next slab interleaved with this slab's MFMAs.
+#include <algorithm>
 #include "common.h"
 #include "launch.h"
 
@@ -166,12 +167,15 @@ __device__ __forceinline__ float scaled(const EpiArgs& e, float acc, int n) {
 // ============================================================== skinny kernel
 // CB: 16-column blocks per workgroup (non-SwiGLU epilogues); SwiGLU always
 // takes the gate block and the matching up block
-template <int WAVES, int MB, int EPI, bool FP8, int U, int CB>
+// PK: fp16 weights in the slab-major layout of pack_weight_kernel (a lane's
+// 32 bytes of a 128-byte step lie in 64-byte slab 2 step + g / 2 of its row).
+template <int WAVES, int MB, int EPI, bool FP8, int U, int CB, bool PK = false>
 __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, int M, int N, int K_bytes,
     EpiArgs e) {
   constexpr int NB = (EPI == HR_EPI_SWIGLU) ? 2 : CB;  // weight row blocks per workgroup
   static_assert(EPI != HR_EPI_HEAD || CB == 1, "head epilogue: one column block");
+  static_assert(!PK || (!FP8 && EPI != HR_EPI_HEAD), "packed weights: fp16 projections");
   // fp16 activations times bf16 weights converted to fp16; the head's split
   // bf16 rows (hi + lo) meet the bf16 weights directly
   constexpr bool kF16 = !FP8 && EPI != HR_EPI_HEAD;
@@ -191,6 +195,18 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
     for (int nb = 0; nb < NB; ++nb) {
       wrow[nb] = (cb * NB + nb) * 16 + rc;
       wok[nb] = wrow[nb] < N;
+    }
+  }
+  // packed rows: the gate/up rows interleave in 32-row blocks (gate rows
+  // 32p.., then up rows 32p..); other matrices keep their row order
+  int prow[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    if constexpr (EPI == HR_EPI_SWIGLU) {
+      const int a = cb * 16 + rc;
+      prow[nb] = (a >> 5) * 64 + (nb ? 32 : 0) + (a & 31);
+    } else {
+      prow[nb] = wrow[nb];
     }
   }
   const int steps = K_bytes >> 7;                      // 128-byte K steps
@@ -215,7 +231,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
       const size_t kb = size_t(sok ? st : s) * 128 + g * 32;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(w + size_t(wrow[nb]) * K_bytes + kb);
+        const u32x4* p;
+        if constexpr (PK)
+          p = reinterpret_cast<const u32x4*>(
+              w + (size_t(2 * (sok ? st : s) + (g >> 1)) * size_t(N) + size_t(prow[nb])) * 64 + (g & 1) * 32);
+        else
+          p = reinterpret_cast<const u32x4*>(w + size_t(wrow[nb]) * K_bytes + kb);
         bw[u][nb][0] = (wok[nb] && sok) ? p[0] : zero;
         bw[u][nb][1] = (wok[nb] && sok) ? p[1] : zero;
       }
@@ -231,8 +252,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_skinny_kernel(
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const u32x4 b0 = kF16 ? bf8_to_f16x8(bw[u][nb][0]) : bw[u][nb][0];
-        const u32x4 b1 = kF16 ? bf8_to_f16x8(bw[u][nb][1]) : bw[u][nb][1];
+        const u32x4 b0 = (kF16 && !PK) ? bf8_to_f16x8(bw[u][nb][0]) : bw[u][nb][0];
+        const u32x4 b1 = (kF16 && !PK) ? bf8_to_f16x8(bw[u][nb][1]) : bw[u][nb][1];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           acc[nb][mb] = mma16<FP8, kF16>(ax[u][mb][0], b0, acc[nb][mb]);
@@ -394,10 +415,13 @@ struct TileCfg {
 // rows) go in kSc 1-KB copies, copy c by wave c (lane l: rows 4l .. 4l+3 of
 // that KB; lanes past the last row repeat row 0 into the pad), so those waves
 // issue one copy more per slab and wait for one more.
-template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int SB, bool MX = false>
+// PK: fp16 weights in the slab-major layout of pack_weight_kernel (no
+// conversion; a B tile's rows of one 64-byte slab are one contiguous run).
+template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int SB, bool MX = false, bool PK = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, int M, int N, int K_bytes,
     int tiles_m, int n_tiles, EpiArgs e) {
+  static_assert(!PK || (!FP8 && !MX), "packed weights are fp16");
   using C = TileCfg<BM, BN, WM, WN, STAGES, SB>;
   constexpr int IM = C::kIM, JN = C::kJN, LPS = C::kLPS, NC = C::kChunks / 2;
   static_assert(EPI != HR_EPI_SWIGLU || JN % 2 == 0, "SwiGLU waves hold gate/up block pairs");
@@ -450,16 +474,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
       src[j] = uint32_t(min(m0 + row, M - 1)) * uint32_t(K_bytes) + lc * 16;
     } else {
       int br;
-      if constexpr (EPI == HR_EPI_SWIGLU) {
+      if constexpr (EPI == HR_EPI_SWIGLU && !PK) {
         // 32-row blocks of the B tile alternate gate / up rows of the same
         // activation columns, so each wave holds a gate block and its up block
+        // (packed weights hold their rows in that order already)
         const int blk = row >> 5, off = row & 31;
         const int a0 = min((n0 >> 1) + (blk >> 1) * 32 + off, e.F - 1);   // act column
         br = (blk & 1) ? e.F + a0 : a0;
       } else {
         br = min(n0 + row, N - 1);
       }
-      src[j] = uint32_t(br) * uint32_t(K_bytes) + lc * 16;
+      if constexpr (PK)   // chunk lc of the row: 64-byte slab lc / 4 of this SB-byte slab
+        src[j] = uint32_t(lc >> 2) * uint32_t(N) * 64u + uint32_t(br) * 64u + (lc & 3) * 16;
+      else
+        src[j] = uint32_t(br) * uint32_t(K_bytes) + lc * 16;
     }
   }
   // MX scale copy of this wave (wave < kSc): lane l carries combined rows
@@ -494,13 +522,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
 
   auto issue = [&](int slab, int stage) {
     const size_t ko = size_t(slab) * SB;
+    // packed weights: slab-major, N rows x 64 bytes per 64-byte slab
+    const size_t kob = PK ? size_t(slab) * (SB / 64) * size_t(N) * 64 : ko;
 #pragma unroll
     for (int j = 0; j < LPS; ++j) {
       const bool is_a = dst_off[j] < STAGES * C::kSlabA;
       // a partial copy keeps lanes [0, kPartLanes) (lane 0 is always active, so
       // every wave issues LPS copies and the vmcnt waits below stay uniform)
       if (C::kRem > 0 && j == C::kFull && lane >= C::kPartLanes) continue;
-      lds_copy16((is_a ? x : w) + src[j] + ko, smem + dst_off[j] + stage * (is_a ? C::kSlabA : C::kSlabB));
+      lds_copy16((is_a ? x : w) + src[j] + (is_a ? ko : kob),
+                 smem + dst_off[j] + stage * (is_a ? C::kSlabA : C::kSlabB));
     }
     if constexpr (MX) {
       if (wave < kSc)
@@ -588,7 +619,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
     wait_lds();
     // fp16 mode: the bf16 weight fragments to fp16 once per slab (each serves
     // IM MFMAs), while this wave's next copies may still be landing
-    if constexpr (!FP8 && !MX) {
+    if constexpr (!FP8 && !MX && !PK) {
 #pragma unroll
       for (int j = 0; j < JN; ++j)
 #pragma unroll
@@ -696,7 +727,7 @@ constexpr int kSkinnyCB = 2;
 template <int EPI>
 constexpr int skinny_cb(int mb) { return (mb == 1 && (EPI == HR_EPI_F32 || EPI == HR_EPI_RESIDUAL)) ? kSkinnyCB : 1; }
 
-template <int EPI, bool FP8>
+template <int EPI, bool FP8, bool PK = false>
 static void skinny(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
                    int blocks, int ksplit, hipStream_t st) {
   dim3 grid(blocks, ksplit);
@@ -709,20 +740,20 @@ static void skinny(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, con
   if (mb == 1) {
     // all of a wave's steps in one batch when they fit (5 steps x NB = 1 block
     // measured faster than 4 + 1; at NB = 2 the 5-step batch costs occupancy)
-    if (spw <= 2) gemm_skinny_kernel<8, 1, EPI, FP8, 2, CB1><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
-    else if (spw == 3) gemm_skinny_kernel<8, 1, EPI, FP8, 3, CB1><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
-    else if (spw == 5 && NB1 == 1) gemm_skinny_kernel<8, 1, EPI, FP8, 5, CB1><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
-    else gemm_skinny_kernel<8, 1, EPI, FP8, 4, CB1><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
+    if (spw <= 2) gemm_skinny_kernel<8, 1, EPI, FP8, 2, CB1, PK><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
+    else if (spw == 3) gemm_skinny_kernel<8, 1, EPI, FP8, 3, CB1, PK><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
+    else if (spw == 5 && NB1 == 1) gemm_skinny_kernel<8, 1, EPI, FP8, 5, CB1, PK><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
+    else gemm_skinny_kernel<8, 1, EPI, FP8, 4, CB1, PK><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
   } else if (EPI == HR_EPI_SWIGLU) {
-    if (mb == 2) gemm_skinny_kernel<4, 2, EPI, FP8, 4, 1><<<grid, 256, 0, st>>>(x, w, M, N, Kb, e);
-    else gemm_skinny_kernel<4, 4, EPI, FP8, 4, 1><<<grid, 256, 0, st>>>(x, w, M, N, Kb, e);
+    if (mb == 2) gemm_skinny_kernel<4, 2, EPI, FP8, 4, 1, PK><<<grid, 256, 0, st>>>(x, w, M, N, Kb, e);
+    else gemm_skinny_kernel<4, 4, EPI, FP8, 4, 1, PK><<<grid, 256, 0, st>>>(x, w, M, N, Kb, e);
   } else {
-    if (mb == 2) gemm_skinny_kernel<8, 2, EPI, FP8, 4, 1><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
-    else gemm_skinny_kernel<4, 4, EPI, FP8, 4, 1><<<grid, 256, 0, st>>>(x, w, M, N, Kb, e);
+    if (mb == 2) gemm_skinny_kernel<8, 2, EPI, FP8, 4, 1, PK><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
+    else gemm_skinny_kernel<4, 4, EPI, FP8, 4, 1, PK><<<grid, 256, 0, st>>>(x, w, M, N, Kb, e);
   }
 }
 
-template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int SB, bool MX = false>
+template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int SB, bool MX = false, bool PK = false>
 static void tiled_cfg(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
                       int ksplit, hipStream_t st) {
   using C = TileCfg<BM, BN, WM, WN, STAGES, SB>;
@@ -731,7 +762,7 @@ static void tiled_cfg(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, 
   const int ncols = (EPI == HR_EPI_SWIGLU) ? 2 * e.F : N;
   const int tiles_n = (ncols + BN - 1) / BN;
   const int n_tiles = tiles_m * tiles_n;
-  auto kern = gemm_tiled_kernel<EPI, FP8, BM, BN, WM, WN, STAGES, SB, MX>;
+  auto kern = gemm_tiled_kernel<EPI, FP8, BM, BN, WM, WN, STAGES, SB, MX, PK>;
   if (kLds > 65536) {
     // above the 64 KB default dynamic-LDS limit: raised once per kernel (a
     // thread-safe static); a refusal surfaces as the launch's error
@@ -746,7 +777,7 @@ static void tiled_cfg(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, 
 // Split-K factor that fills the 256 CUs for the residual projections (the
 // splits' partials are summed by the caller), or the given one; launched only
 // when `go` (otherwise this only plans the factor).
-template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int SB = 64, bool MX = false>
+template <int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int SB = 64, bool MX = false, bool PK = false>
 static int tiled_fill(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
                       hipStream_t st, bool go, int ks_force = 0) {
   const int ncols = (EPI == HR_EPI_SWIGLU) ? 2 * e.F : N;
@@ -756,7 +787,7 @@ static int tiled_fill(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, 
   if (EPI == HR_EPI_RESIDUAL && ks_force > 0) ks = ks_force;
   const int max_ks = Kb / SB / 4 > 0 ? Kb / SB / 4 : 1;   // >= 4 slabs per split
   if (ks > max_ks) ks = max_ks;
-  if (go) tiled_cfg<EPI, FP8, BM, BN, WM, WN, STAGES, SB, MX>(x, w, M, N, Kb, e, ks, st);
+  if (go) tiled_cfg<EPI, FP8, BM, BN, WM, WN, STAGES, SB, MX, PK>(x, w, M, N, Kb, e, ks, st);
   return ks;
 }
 
@@ -791,39 +822,39 @@ static int tiled_fill(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, 
 // 128; every other tile stayed (256 x 128 residual tiles above 1024 rows won
 // alone, O 165.7 -> 159.3 and down 330.0 -> 303.8 us at 4274 rows, but the
 // 36-layer varlen batch got slower with them: 46.3 -> 49.8 ms).
-template <int EPI, bool FP8>
+template <int EPI, bool FP8, bool PK>
 static int tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const EpiArgs& e,
                  hipStream_t st, bool go) {
   const int K_el = FP8 ? Kb : Kb / 2;
   if constexpr (EPI == HR_EPI_SWIGLU) {
-    if (M <= 64) return tiled_fill<EPI, FP8, 64, 128, 2, 2, 6, 128>(x, w, M, N, Kb, e, st, go);
+    if (M <= 64) return tiled_fill<EPI, FP8, 64, 128, 2, 2, 6, 128, false, PK>(x, w, M, N, Kb, e, st, go);
     if (M > 384) {
-      if constexpr (FP8) return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st, go);
-      else return tiled_fill<EPI, FP8, 256, 256, 2, 4, 4>(x, w, M, N, Kb, e, st, go);
+      if constexpr (FP8) return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128, false, PK>(x, w, M, N, Kb, e, st, go);
+      else return tiled_fill<EPI, FP8, 256, 256, 2, 4, 4, 64, false, PK>(x, w, M, N, Kb, e, st, go);
     }
-    if (M > 128) return tiled_fill<EPI, FP8, 256, 128, 4, 2, 4>(x, w, M, N, Kb, e, st, go);
-    return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128>(x, w, M, N, Kb, e, st, go);
+    if (M > 128) return tiled_fill<EPI, FP8, 256, 128, 4, 2, 4, 64, false, PK>(x, w, M, N, Kb, e, st, go);
+    return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128, false, PK>(x, w, M, N, Kb, e, st, go);
   } else if constexpr (EPI == HR_EPI_F32) {
-    if (M > 1024) return tiled_fill<EPI, FP8, 256, 256, 2, 4, 4>(x, w, M, N, Kb, e, st, go);
-    if (M > 384) return tiled_fill<EPI, FP8, 128, 128, 2, 4, 4, 128>(x, w, M, N, Kb, e, st, go);
-    if (M > 128) return tiled_fill<EPI, FP8, 128, 64, 2, 2, 6, 128>(x, w, M, N, Kb, e, st, go);
-    if (M <= 64) return tiled_fill<EPI, FP8, 64, 32, 2, 1, 8, 128>(x, w, M, N, Kb, e, st, go);
-    return tiled_fill<EPI, FP8, 64, 64, 2, 2, 8, 128>(x, w, M, N, Kb, e, st, go);
+    if (M > 1024) return tiled_fill<EPI, FP8, 256, 256, 2, 4, 4, 64, false, PK>(x, w, M, N, Kb, e, st, go);
+    if (M > 384) return tiled_fill<EPI, FP8, 128, 128, 2, 4, 4, 128, false, PK>(x, w, M, N, Kb, e, st, go);
+    if (M > 128) return tiled_fill<EPI, FP8, 128, 64, 2, 2, 6, 128, false, PK>(x, w, M, N, Kb, e, st, go);
+    if (M <= 64) return tiled_fill<EPI, FP8, 64, 32, 2, 1, 8, 128, false, PK>(x, w, M, N, Kb, e, st, go);
+    return tiled_fill<EPI, FP8, 64, 64, 2, 2, 8, 128, false, PK>(x, w, M, N, Kb, e, st, go);
   } else {
     if constexpr (FP8) {
-      if (M > 128) return tiled_fill<EPI, FP8, 64, 64, 2, 2, 4, 128>(x, w, M, N, Kb, e, st, go);
+      if (M > 128) return tiled_fill<EPI, FP8, 64, 64, 2, 2, 4, 128, false, PK>(x, w, M, N, Kb, e, st, go);
     }
-    if (M > 1024) return tiled_fill<EPI, FP8, 128, 128, 2, 4, 4, 128>(x, w, M, N, Kb, e, st, go);
+    if (M > 1024) return tiled_fill<EPI, FP8, 128, 128, 2, 4, 4, 128, false, PK>(x, w, M, N, Kb, e, st, go);
     if (M > 384) {
-      if (K_el >= 8192) return tiled_fill<EPI, FP8, 256, 128, 2, 4, 4>(x, w, M, N, Kb, e, st, go, 6);
-      return tiled_fill<EPI, FP8, 128, 128, 2, 4, 4, 128>(x, w, M, N, Kb, e, st, go, 3);
+      if (K_el >= 8192) return tiled_fill<EPI, FP8, 256, 128, 2, 4, 4, 64, false, PK>(x, w, M, N, Kb, e, st, go, 6);
+      return tiled_fill<EPI, FP8, 128, 128, 2, 4, 4, 128, false, PK>(x, w, M, N, Kb, e, st, go, 3);
     }
-    if (M > 128) return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4>(x, w, M, N, Kb, e, st, go);
-    return tiled_fill<EPI, FP8, 64, 64, 2, 2, 4, 128>(x, w, M, N, Kb, e, st, go);
+    if (M > 128) return tiled_fill<EPI, FP8, 128, 128, 2, 2, 4, 64, false, PK>(x, w, M, N, Kb, e, st, go);
+    return tiled_fill<EPI, FP8, 64, 64, 2, 2, 4, 128, false, PK>(x, w, M, N, Kb, e, st, go);
   }
 }
 
-int launch_linear(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8,
+int launch_linear(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8, bool packed,
                   int M, int N, int K, int epi, void* out, float out_scale, float* part, bool go,
                   hipStream_t st) {
   EpiArgs e{};
@@ -852,10 +883,12 @@ int launch_linear(const void* x, const void* w, const float* w_scale, float x_sc
     if (EPI_ == HR_EPI_RESIDUAL && blocks < 256) ks = (384 + blocks - 1) / blocks;            \
     if (ks > Kb / 128) ks = Kb / 128;                                                         \
     if (go && fp8) skinny<EPI_, true>(xb, wb, M, N, Kb, e, blocks, ks, st);                   \
+    else if (go && packed) skinny<EPI_, false, true>(xb, wb, M, N, Kb, e, blocks, ks, st);     \
     else if (go) skinny<EPI_, false>(xb, wb, M, N, Kb, e, blocks, ks, st);                    \
   } else {                                                                                    \
-    ks = fp8 ? tiled<EPI_, true>(xb, wb, M, N, Kb, e, st, go)                                 \
-             : tiled<EPI_, false>(xb, wb, M, N, Kb, e, st, go);                               \
+    ks = fp8 ? tiled<EPI_, true, false>(xb, wb, M, N, Kb, e, st, go)                          \
+             : packed ? tiled<EPI_, false, true>(xb, wb, M, N, Kb, e, st, go)                 \
+                      : tiled<EPI_, false, false>(xb, wb, M, N, Kb, e, st, go);               \
   }
   if (epi == HR_EPI_F32) { HR_DISPATCH(HR_EPI_F32) }
   else if (epi == HR_EPI_RESIDUAL) { HR_DISPATCH(HR_EPI_RESIDUAL) }
@@ -890,6 +923,56 @@ int launch_linear_mx(const uint8_t* x, const uint8_t* x_scales, int lda, const u
     return tiled_fill<HR_EPI_SWIGLU, false, 128, 128, 4, 2, 4, 64, true>(x, w, M, N, Kb, e, st, go);
   if (M > 1024) return tiled_fill<HR_EPI_RESIDUAL, false, 256, 256, 4, 2, 4, 64, true>(x, w, M, N, Kb, e, st, go);
   return tiled_fill<HR_EPI_RESIDUAL, false, 64, 128, 2, 2, 4, 64, true>(x, w, M, N, Kb, e, st, go);
+}
+
+// ============================================================== weight packing
+// Packed fp16 weights: W [N, K] bf16 row-major -> P [K/32][N][32] fp16: each
+// 64-byte run is one row's slab of 32 K values, so the rows of a tile for one
+// slab are one contiguous run.  gate_up (W = [gate; up], N = 2F): packed row
+// 64 p + 32 u + r holds row u F + 32 p + r, the 32-row gate / up block order
+// the SwiGLU tiles consume.  The values are converted as the bf16 path does in
+// registers (bf8_to_f16x8: exact for |w| in [2^-17, 65504], round to nearest
+// even below), so a packed layer computes the same products in the same order;
+// a non-finite result (|w| >= 65520, inf or NaN) sets *bad.
+__global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t* __restrict__ w, int N, int K, int gate_up,
+                                                          uint16_t* __restrict__ out, unsigned int* __restrict__ bad) {
+  const size_t n_chunks = size_t(N) * size_t(K / 8);
+  unsigned int nonfinite = 0;
+  for (size_t c = size_t(blockIdx.x) * 256 + threadIdx.x; c < n_chunks; c += size_t(gridDim.x) * 256) {
+    const int q = int(c & 3);                 // 8-value quarter of the 64-byte run
+    const size_t run = c >> 2;
+    const int pr = int(run % size_t(N)), sl = int(run / size_t(N));
+    int row = pr;
+    if (gate_up) {
+      const int F = N / 2;
+      row = ((pr >> 5) & 1) * F + 32 * (pr >> 6) + (pr & 31);
+    }
+    const u32x4 h = bf8_to_f16x8(*reinterpret_cast<const u32x4*>(w + size_t(row) * K + size_t(sl) * 32 + q * 8));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      nonfinite |= ((h[i] & 0x7C00u) == 0x7C00u) | (((h[i] >> 16) & 0x7C00u) == 0x7C00u);
+    *reinterpret_cast<u32x4*>(out + c * 8) = h;
+  }
+  if (nonfinite) atomicOr(bad, 1u);
+}
+
+int launch_pack_weight(const void* w, int N, int K, bool gate_up, void* out, hipStream_t st) {
+  unsigned int* bad = nullptr;
+  if (hipMalloc(&bad, sizeof(unsigned int)) != hipSuccess) return -1;
+  unsigned int h_bad = 0;
+  int rc = -1;
+  const size_t n_chunks = size_t(N) * size_t(K / 8);
+  const int blocks = int(std::min<size_t>((n_chunks + 255) / 256, 16384));
+  if (hipMemcpyAsync(bad, &h_bad, sizeof(h_bad), hipMemcpyHostToDevice, st) == hipSuccess) {
+    pack_weight_kernel<<<blocks, 256, 0, st>>>(static_cast<const uint16_t*>(w), N, K, gate_up ? 1 : 0,
+                                                static_cast<uint16_t*>(out), bad);
+    if (hipGetLastError() == hipSuccess &&
+        hipMemcpyAsync(&h_bad, bad, sizeof(h_bad), hipMemcpyDeviceToHost, st) == hipSuccess &&
+        hipStreamSynchronize(st) == hipSuccess)
+      rc = h_bad ? 1 : 0;
+  }
+  (void)hipFree(bad);
+  return rc;
 }
 
 // Head: zsplit bf16 [2n, D] (hi rows then lo rows), W bf16 [N, D] -> fp32 [n, N]

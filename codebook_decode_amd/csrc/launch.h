@@ -93,9 +93,13 @@ void launch_decode_rope_attention(const void* qkv, const void* qw, const void* k
 // epilogue is HR_EPI_RESIDUAL).  RESIDUAL with ks > 1 writes ks fp32 partials
 // [ks][M][N] to `part` instead of touching `out`; the caller reduces them
 // (launch_residual_norm).  go == false: plan only (return ks, launch nothing).
-int launch_linear(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8,
+// packed: w is fp16 in the slab-major layout of launch_pack_weight (fp8 false)
+int launch_linear(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8, bool packed,
                   int M, int N, int K, int epi, void* out, float out_scale, float* part, bool go,
                   hipStream_t st);
+// bf16 W [N, K] -> packed fp16 (slab-major [K/32][N][32], gate_up: 32-row
+// gate / up blocks); synchronous; 0 ok, 1 a non-finite fp16 value, -1 HIP error
+int launch_pack_weight(const void* w, int N, int K, bool gate_up, void* out, hipStream_t st);
 int launch_linear_mx(const uint8_t* x, const uint8_t* x_scales, int lda, const uint8_t* w,
                      const uint8_t* w_scales, int M, int N, int K, int epi, void* out, uint8_t* out_scales,
                      int ldo, float* part, bool go, hipStream_t st);

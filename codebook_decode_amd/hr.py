@@ -18,7 +18,7 @@ LIB_PATH = os.environ.get("HR_LIB") or os.path.join(_HERE, "libhr.so")
 
 HR_OK, HR_EINVAL, HR_EUNSUPPORTED, HR_ECAPACITY = 0, -1, -2, -3
 HR_EBOUND, HR_EWORKSPACE, HR_EALIGN, HR_EHIP = -4, -5, -6, -7
-HR_BF16, HR_FP8_E4M3, HR_MXFP4, HR_F16 = 0, 1, 2, 3
+HR_BF16, HR_FP8_E4M3, HR_MXFP4, HR_F16, HR_F16_PACKED = 0, 1, 2, 3, 4
 HR_EPI_F32, HR_EPI_RESIDUAL, HR_EPI_SWIGLU = 0, 1, 2
 MX_SRC_BF16, MX_SRC_F32, MX_SRC_F16 = 0, 1, 2
 STATUS_NAMES = {0: "HR_OK", -1: "HR_EINVAL", -2: "HR_EUNSUPPORTED", -3: "HR_ECAPACITY",
@@ -105,6 +105,7 @@ def lib() -> ctypes.CDLL:
                                          c_i32, c_f32, c_vp]),
             "hr_rmsnorm": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_f32, c_vp, c_i32, c_f32, c_vp]),
             "hr_linear_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
+            "hr_pack_weight": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
             "hr_linear": (c_i32, [c_vp, c_vp, c_vp, c_f32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_f32, c_vp, c_sz,
                                   c_vp]),
             "hr_residual_rmsnorm": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_f32, c_vp, c_i32, c_f32, c_vp]),
@@ -318,6 +319,25 @@ def hr_rmsnorm(h, T, D, norm_w, eps, x_out, x_type=HR_F16, x_scale=1.0, stream=N
 
 def hr_linear_workspace_bytes(wtype, M, N, K, epi) -> int:
     return lib().hr_linear_workspace_bytes(wtype, M, N, K, epi)
+
+
+def hr_pack_weight(w, N, K, gate_up, out, stream=None) -> None:
+    """bf16 w [N, K] -> ``out`` (N * K * 2 bytes) for HR_F16_PACKED layers."""
+    _check(lib().hr_pack_weight(ptr(w), N, K, int(gate_up), ptr(out),
+                                stream if stream is not None else current_stream()))
+
+
+def pack_layer_weights(t: dict, shapes: dict) -> dict:
+    """Copy of layer dict ``t`` with w_qkv / w_o / w_gu / w_down replaced by
+    their packed forms; ``shapes[name] = (N, K)``."""
+    import torch
+    out = dict(t)
+    for name in ("w_qkv", "w_o", "w_gu", "w_down"):
+        N, K = shapes[name]
+        p = torch.empty((N, K), dtype=torch.float16, device=t[name].device)
+        hr_pack_weight(t[name], N, K, name == "w_gu", p)
+        out[name] = p
+    return out
 
 
 def hr_linear(x, w, w_scale, x_scale, wtype, M, N, K, epi, out, out_scale=0.0, ws=None, stream=None) -> None:

@@ -57,11 +57,13 @@ typedef enum {
   HR_EHIP = -7           /* a HIP launch error                                   */
 } hr_status;
 
-/* Number formats.  Weights: HR_BF16, HR_FP8_E4M3, HR_MXFP4.  HR_F16 (IEEE
- * binary16) names the activations of the bf16-weight band where a step entry
- * of hr_ops.h takes an activation type. */
+/* Number formats.  Weights: HR_BF16, HR_FP8_E4M3, HR_MXFP4, HR_F16_PACKED.
+ * HR_F16 (IEEE binary16) names the activations of the bf16-weight band where a
+ * step entry of hr_ops.h takes an activation type.  HR_F16_PACKED: bf16
+ * weights prepared once by hr_pack_weight (fp16 values in a slab-major
+ * layout); a layer of them computes exactly what the HR_BF16 layer computes. */
 typedef enum {
-  HR_BF16 = 0, HR_FP8_E4M3 = 1, HR_MXFP4 = 2, HR_F16 = 3,
+  HR_BF16 = 0, HR_FP8_E4M3 = 1, HR_MXFP4 = 2, HR_F16 = 3, HR_F16_PACKED = 4,
   /* range markers, never valid arguments: they give the type the whole int32
      range, so any value a caller passes is a value of the type that the
      checks reject (HR_EINVAL), not undefined behaviour */
@@ -84,7 +86,8 @@ typedef struct {
                              i >= used_keys[s] are trailing pads            */
 } hr_dims;
 
-/* One decoder layer: device pointers, weights row-major [out, in].
+/* One decoder layer: device pointers, weights row-major [out, in] (packed
+ * layers: the layout of hr_pack_weight).
  *  bf16:  w_* are bf16.  The activations between the kernels are fp16 (the
  *         norm outputs, the attention output, the SwiGLU product; 11-bit
  *         significand), the merged QKV rows fp32, the residual fp32 and the KV
@@ -158,6 +161,25 @@ typedef struct {
   const int32_t* h_cache_slot;
   const int32_t* h_used_keys;
 } hr_batch;
+
+/* Prepares one bf16 weight matrix of a layer for HR_F16_PACKED (once, at
+ * load).  The four projection GEMMs of the chain ("Stabilize Higgs Audio
+ * termination and prefill", Summary) stream these matrices; the layout serves
+ * their tiles:
+ *  w    bf16 [N, K] row-major (device), K a multiple of 32;
+ *  out  device buffer of N * K * 2 bytes, not overlapping w: fp16 values in
+ *       the slab-major layout out[K/32][N][32] (each 64-byte run is one row's
+ *       32 consecutive K values, so the rows of a tile for one K slab are one
+ *       contiguous run);
+ *  gate_up 1 for w_gu ([gate; up], N = 2F, F a multiple of 32): packed row
+ *       64 p + 32 u + r holds row u F + 32 p + r (32-row blocks alternate gate
+ *       and up rows of the same activation columns); 0 for w_qkv, w_o, w_down.
+ * The conversion is the one the HR_BF16 kernels make in registers (exact for
+ * |w| in [2^-17, 65504], round to nearest even below 2^-17), so a layer of
+ * packed weights computes the same products in the same order.  A weight
+ * that does not fit fp16 (|w| >= 65520, inf, NaN) returns HR_EINVAL.  The
+ * call synchronises `stream` (it reads back that check). */
+hr_status hr_pack_weight(const void* w, int32_t N, int32_t K, int32_t gate_up, void* out, hipStream_t stream);
 
 /* Bytes of scratch the prefill calls need for `total_tokens` rows. */
 size_t hr_workspace_bytes(const hr_dims* dims, hr_wtype wtype, int32_t total_tokens);

@@ -56,6 +56,9 @@ typedef enum {
  *                     of 2^-24); w_scale ignored.
  *  wtype HR_FP8_E4M3: x and w e4m3; the product is scaled by
  *                     x_scale * w_scale[n].
+ *  wtype HR_F16_PACKED: x fp16, w written by hr_pack_weight (gate_up = 1 for
+ *                     SWIGLU, N then a multiple of 64); bit for bit the
+ *                     HR_BF16 result of the unpacked weights; w_scale ignored.
  * K a multiple of 64, N a multiple of 16 (32 for SWIGLU). */
 size_t hr_linear_workspace_bytes(hr_wtype wtype, int32_t M, int32_t N, int32_t K, hr_epilogue epi);
 hr_status hr_linear(const void* x, const void* w, const float* w_scale, float x_scale,

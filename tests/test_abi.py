@@ -202,6 +202,23 @@ def test_linear_validation():
         H.HR_EWORKSPACE
 
 
+def test_pack_weight_validation():
+    lib = H.lib()
+    f = lib.hr_pack_weight
+    assert f(FAKE, 64, 48, 0, FAKE + (1 << 20), None) == H.HR_EINVAL          # K % 32
+    assert f(FAKE, 0, 64, 0, FAKE + (1 << 20), None) == H.HR_EINVAL
+    assert f(FAKE, 96, 64, 1, FAKE + (1 << 20), None) == H.HR_EUNSUPPORTED    # gate/up: N % 64
+    assert f(FAKE, 64, 64, 2, FAKE + (1 << 20), None) == H.HR_EINVAL          # gate_up flag 0 / 1
+    assert f(None, 64, 64, 0, FAKE, None) == H.HR_EINVAL
+    assert f(FAKE, 64, 64, 0, MISALIGNED, None) == H.HR_EALIGN
+    assert f(FAKE, 64, 64, 0, FAKE + 4096, None) == H.HR_EINVAL               # out overlaps w
+    assert f(FAKE, 65536, 32768, 0, FAKE + (1 << 40), None) == H.HR_EUNSUPPORTED   # >= 2 GB
+    # a packed layer and hr_linear accept the format, with the gate/up rule
+    assert lib.hr_linear(FAKE, FAKE, None, 1.0, H.HR_F16_PACKED, 4, 96, 64, 2, FAKE, 0.0, None, 0, None) == \
+        H.HR_EUNSUPPORTED
+    assert lib.hr_linear(FAKE, FAKE, None, 1.0, 5, 4, 64, 64, 0, FAKE, 0.0, None, 0, None) == H.HR_EINVAL
+
+
 def test_residual_rmsnorm_validation():
     lib = H.lib()
     f = lib.hr_residual_rmsnorm

@@ -197,3 +197,44 @@ def test_varlen32_stack36(H, model_36):
     m = model_36[0]
     w = synth.workloads()["varlen32_stack36_d2560"]
     _teacher_forced_and_free(H, model_36, w.prompt_lens, w.capacity, "varlen32")
+
+
+@pytest.mark.timeout(600)
+def test_stack36_p512_packed_equals_bf16(H, model_36):
+    """The 36-layer stack with its weights packed by hr_pack_weight (the
+    format the benchmark times) gives the bf16 stack's hidden states, logits
+    and KV caches bit for bit."""
+    import torch
+    from gpu_util import dev, log
+    from model_util import dims_of, kv_cache, workspace
+    m, host, devl, sh = model_36
+    shapes = {"w_qkv": (m.qkv_rows, m.hidden), "w_o": (m.hidden, m.attn_width), "w_gu": (2 * m.ffn, m.hidden),
+              "w_down": (m.hidden, m.ffn)}
+    P, cap = 512, 1024
+    K, V = m.n_codebooks, m.cb_vocab
+    ids = dev(synth.prompt_ids(m, P))
+    b = H.Batch([0, P], [0], [0])
+    dims = dims_of(H, m, True)
+    res = []
+    for packed in (False, True):
+        if packed:
+            dls = [H.pack_layer_weights(d, shapes) for d in devl]
+            layers = [H.make_layer(d, H.HR_F16_PACKED) for d in dls]
+            wtype = H.HR_F16_PACKED
+        else:
+            dls, layers, wtype = devl, [H.make_layer(d) for d in devl], H.HR_BF16
+        kvs = [kv_cache(m, 1, cap, poison=False) for _ in range(m.n_layers)]
+        h_out = torch.empty((P, m.hidden), dtype=torch.float32, device="cuda")
+        logits = torch.empty((1, K * V), dtype=torch.float32, device="cuda")
+        H.hr_prefill_stack(dims, layers, b, ids, sh["embed"], m.vocab, None, [H.make_kv(k, v, cap, 1) for k, v in kvs],
+                           sh["d_final"], sh["d_head"], K, V, h_out, logits, workspace(H, dims, wtype, P))
+        torch.cuda.synchronize()
+        log(f"stack P=512 packed={packed} done")
+        res.append((h_out.cpu().numpy(), logits.cpu().numpy(),
+                    kvs[-1][0].cpu().view(torch.int16).numpy(), kvs[-1][1].cpu().view(torch.int16).numpy()))
+        del kvs
+        if packed:
+            del dls, layers
+    for a, b_ in zip(res[0], res[1]):
+        np.testing.assert_array_equal(a, b_)
+
