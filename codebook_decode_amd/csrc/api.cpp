@@ -193,9 +193,11 @@ int residual_ks(const hr_dims* d, int32_t T) {
   const int D = d->hidden, A = d->n_q_heads * d->head_dim, F = d->ffn;
   int ks = 1;
   for (int K : {A, F}) {
-    for (bool fp8 : {false, true}) {
+    // bf16, e4m3, packed fp16 (each format plans its own tiles)
+    for (int f = 0; f < 3; ++f) {
+      const bool fp8 = f == 1, pk = f == 2;
       if (fp8 && K % 128) continue;
-      const int k = hr::launch_linear(nullptr, nullptr, nullptr, 1.f, fp8, false, T, D, K, HR_EPI_RESIDUAL, nullptr, 0.f,
+      const int k = hr::launch_linear(nullptr, nullptr, nullptr, 1.f, fp8, pk, T, D, K, HR_EPI_RESIDUAL, nullptr, 0.f,
                                       nullptr, false, nullptr);
       ks = k > ks ? k : ks;
     }
@@ -791,9 +793,10 @@ size_t hr_linear_workspace_bytes(hr_wtype wtype, int32_t M, int32_t N, int32_t K
     ks = hr::launch_linear_mx(nullptr, nullptr, 0, nullptr, nullptr, M, N, K, HR_EPI_RESIDUAL, nullptr, nullptr, 0,
                               nullptr, false, nullptr);
   } else {
-    const bool fp8 = wtype == HR_FP8_E4M3;
+    const bool fp8 = wtype == HR_FP8_E4M3, pk = wtype == HR_F16_PACKED;
     if (K % (fp8 ? 128 : 64)) return 0;
-    ks = hr::launch_linear(nullptr, nullptr, nullptr, 1.f, fp8, false, M, N, K, HR_EPI_RESIDUAL, nullptr, 0.f,
+    // the plan of the format that will run (its split factor sizes the partials)
+    ks = hr::launch_linear(nullptr, nullptr, nullptr, 1.f, fp8, pk, M, N, K, HR_EPI_RESIDUAL, nullptr, 0.f,
                            nullptr, false, nullptr);
   }
   return ks > 1 ? up256(size_t(ks) * size_t(M) * size_t(N) * 4) : 0;
