@@ -962,23 +962,24 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t* __rest
   if (nonfinite) atomicOr(bad, 1u);
 }
 
+// the non-finite flag of pack_weight_kernel: one word per GPU (file scope, no
+// allocation); packs that overlap on one GPU share it
+__device__ unsigned int g_pack_bad;
+
 int launch_pack_weight(const void* w, int N, int K, bool gate_up, void* out, hipStream_t st) {
   unsigned int* bad = nullptr;
-  if (hipMalloc(&bad, sizeof(unsigned int)) != hipSuccess) return -1;
+  if (hipGetSymbolAddress(reinterpret_cast<void**>(&bad), HIP_SYMBOL(g_pack_bad)) != hipSuccess) return -1;
   unsigned int h_bad = 0;
-  int rc = -1;
   const size_t n_chunks = size_t(N) * size_t(K / 8);
   const int blocks = int(std::min<size_t>((n_chunks + 255) / 256, 16384));
-  if (hipMemcpyAsync(bad, &h_bad, sizeof(h_bad), hipMemcpyHostToDevice, st) == hipSuccess) {
-    pack_weight_kernel<<<blocks, 256, 0, st>>>(static_cast<const uint16_t*>(w), N, K, gate_up ? 1 : 0,
-                                                static_cast<uint16_t*>(out), bad);
-    if (hipGetLastError() == hipSuccess &&
-        hipMemcpyAsync(&h_bad, bad, sizeof(h_bad), hipMemcpyDeviceToHost, st) == hipSuccess &&
-        hipStreamSynchronize(st) == hipSuccess)
-      rc = h_bad ? 1 : 0;
-  }
-  (void)hipFree(bad);
-  return rc;
+  if (hipMemcpyAsync(bad, &h_bad, sizeof(h_bad), hipMemcpyHostToDevice, st) != hipSuccess) return -1;
+  pack_weight_kernel<<<blocks, 256, 0, st>>>(static_cast<const uint16_t*>(w), N, K, gate_up ? 1 : 0,
+                                              static_cast<uint16_t*>(out), bad);
+  if (hipGetLastError() != hipSuccess ||
+      hipMemcpyAsync(&h_bad, bad, sizeof(h_bad), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return -1;
+  return h_bad ? 1 : 0;
 }
 
 // Head: zsplit bf16 [2n, D] (hi rows then lo rows), W bf16 [N, D] -> fp32 [n, N]

@@ -25,13 +25,17 @@
  *    so bounds are checked, never assumed (HR_EBOUND).
  *
  * Conventions for every call:
- *  - All tensors are row-major and live in device memory owned by the caller;
- *    the library never allocates, frees or reads device memory on the host.
+ *  - All tensors are row-major (packed weights: the layout of hr_pack_weight)
+ *    and live in device memory owned by the caller; the library never
+ *    allocates or frees device memory, and reads none on the host except the
+ *    one-word range check of hr_pack_weight.
  *  - bf16 tensors are passed as `const void*` (IEEE bfloat16 bit patterns);
  *    e4m3 tensors as OCP FP8 E4M3 (e4m3fn) bytes.
  *  - Every check runs on the host before the first launch; a call that
- *    returns a non-OK status has enqueued nothing.  Work is enqueued on
- *    `stream` in order; the call returns without synchronising.
+ *    returns a non-OK status has enqueued nothing (hr_pack_weight's range
+ *    check, which needs the data, is the exception: it reports after the
+ *    pack).  Work is enqueued on `stream` in order; the call returns without
+ *    synchronising (hr_pack_weight does synchronise).
  *  - Device pointers must be 16-byte aligned (HR_EALIGN otherwise).
  *  - hr_last_error() returns a thread-local message for the last failure.
  */
@@ -177,8 +181,10 @@ typedef struct {
  * The conversion is the one the HR_BF16 kernels make in registers (exact for
  * |w| in [2^-17, 65504], round to nearest even below 2^-17), so a layer of
  * packed weights computes the same products in the same order.  A weight
- * that does not fit fp16 (|w| >= 65520, inf, NaN) returns HR_EINVAL.  The
- * call synchronises `stream` (it reads back that check). */
+ * that does not fit fp16 (|w| >= 65520, inf, NaN) returns HR_EINVAL.  Unlike
+ * the other entries this one synchronises `stream` (it reads that check back
+ * from a one-word flag each GPU holds; packs that overlap on one GPU race on
+ * it).  It allocates nothing. */
 hr_status hr_pack_weight(const void* w, int32_t N, int32_t K, int32_t gate_up, void* out, hipStream_t stream);
 
 /* Bytes of scratch the prefill calls need for `total_tokens` rows. */
