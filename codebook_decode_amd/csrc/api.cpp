@@ -162,6 +162,7 @@ hr_status check_layer(const hr_dims* d, const hr_layer* L, int idx) {
 
 struct Ws {
   uint8_t *x, *qkv, *q, *attn, *act, *head;
+  float* rope;               // RoPE angle table [T][d] of the QKV epilogue (cos, then sin)
   float* part;               // split-K partials of the O / down projections [ks][T][D] (null: none needed)
   float *part_o, *part_ml;   // key-chunk partials of the split attention (null: no split)
   uint8_t *mx_s1, *mx_s2;    // MXFP4 block scales: O / gate-up input, down input (ld mx_ld)
@@ -227,6 +228,7 @@ size_t ws_layout(const hr_dims* d, int32_t T, Ws* w, uint8_t* base) {
   tmp.attn = take(t * A * 2);
   tmp.act = take(t * F * 2);
   tmp.head = take(size_t(64) * D * 2);
+  tmp.rope = reinterpret_cast<float*>(take(t * size_t(d->head_dim) * 4));
   // MXFP4 band: the codes reuse x (O / gate-up input) and act (down input)
   tmp.mx_ld = int((t + 255) / 256 * 256);
   tmp.mx_s1 = take(((D > A ? D : A) / 128) * size_t(tmp.mx_ld) * 4);
@@ -350,6 +352,16 @@ int small_prompt(const hr_batch* b) {
   return longest;
 }
 
+// Step A3 in the QKV GEMM's epilogue (hr::launch_qkv_rope) for batches that
+// take the separate q/k-norm + RoPE step (not a decode step, not a short
+// prompt) with 385-1024 rows: one launch and no fp32 QKV round trip instead of
+// two (P = 512: the 8.4 us step).  Its angle table is built once per call.
+bool qkv_rope_fused(const hr_dims* d, const hr_batch* b) {
+  if (one_row_batch(b) && d->causal) return false;
+  if (small_prompt(b) >= 0) return false;
+  return hr::qkv_rope_fits(b->total_tokens, d->head_dim);
+}
+
 // Input norm of a layer in its format: fp16 for the bf16 and MXFP4 bands
 // (their QKV GEMM takes fp16 activations), e4m3 with the layer's QKV scale.
 void in_norm_mode(const hr_layer* L, int* mode, float* inv) {
@@ -375,8 +387,15 @@ hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_layer* next, c
     in_norm_mode(L, &mode, &inv);
     hr::launch_residual_norm(h, nullptr, 0, T, D, L->in_norm_w, eps, mode, w.x, inv, nullptr, nullptr, 0, st);
   }
-  hr::launch_linear(w.x, L->w_qkv, L->ws_qkv, L->as_qkv, fp8, pk, T, NQKV, D, HR_EPI_F32, w.qkv, 0.f, nullptr, true,
-                    st);
+  const bool fused_qkv = qkv_rope_fused(d, b);
+  if (fused_qkv) {
+    const hr::QkvRope qr{w.q, kv->k, kv->v, b->cu_seqlens, b->start_pos, b->cache_slot, b->used_keys, b->n_seq,
+                         d->causal, kv->capacity, Hq, Hkv, dh, L->q_norm_w, L->k_norm_w, eps, w.rope};
+    hr::launch_qkv_rope(w.x, L->w_qkv, L->ws_qkv, L->as_qkv, fp8, pk, T, D, qr, st);
+  } else {
+    hr::launch_linear(w.x, L->w_qkv, L->ws_qkv, L->as_qkv, fp8, pk, T, NQKV, D, HR_EPI_F32, w.qkv, 0.f, nullptr,
+                      true, st);
+  }
   if (split.decode && d->causal) {
     hr::launch_decode_rope_attention(w.qkv, L->q_norm_w, L->k_norm_w, d->rope_theta, eps, kv->k, kv->v,
                                      b->cu_seqlens, b->start_pos, b->cache_slot, b->n_seq, Hq, Hkv, dh,
@@ -386,9 +405,10 @@ hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_layer* next, c
                                b->cache_slot, b->used_keys, d->causal != 0, L->q_norm_w, L->k_norm_w, kv->k, kv->v,
                                kv->capacity, w.attn, fp8, fp8 ? 1.0f / L->as_o : 1.f, st);
   } else {
-    hr::launch_qknorm_rope_kv(w.qkv, T, Hq, Hkv, dh, d->rope_theta, eps, b->cu_seqlens, b->start_pos,
-                              b->cache_slot, b->used_keys, b->n_seq, d->causal != 0, L->q_norm_w, L->k_norm_w,
-                              w.q, kv->k, kv->v, kv->capacity, st);
+    if (!fused_qkv)
+      hr::launch_qknorm_rope_kv(w.qkv, T, Hq, Hkv, dh, d->rope_theta, eps, b->cu_seqlens, b->start_pos,
+                                b->cache_slot, b->used_keys, b->n_seq, d->causal != 0, L->q_norm_w, L->k_norm_w,
+                                w.q, kv->k, kv->v, kv->capacity, st);
     hr::launch_attention(w.q, kv->k, kv->v, b->cu_seqlens, b->start_pos, b->cache_slot, b->used_keys, b->n_seq,
                          b->max_seqlen, Hq, Hkv, dh, kv->capacity, d->causal != 0, w.attn, fp8,
                          fp8 ? 1.0f / L->as_o : 1.f, st, &split);
@@ -466,6 +486,9 @@ hr_status hr_prefill_layer(const hr_dims* dims, const hr_layer* layer, const hr_
   if (ws_bytes < need_ws) return fail(HR_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need_ws);
   Ws w;
   ws_layout(dims, batch->total_tokens, &w, static_cast<uint8_t*>(ws));
+  if (qkv_rope_fused(dims, batch))
+    hr::launch_rope_table(batch->cu_seqlens, batch->start_pos, batch->n_seq, batch->total_tokens, dims->head_dim,
+                          dims->rope_theta, w.rope, stream);
   return run_layer(dims, layer, nullptr, batch, h, kv, w, false, stream);
 }
 
@@ -517,6 +540,9 @@ hr_status enqueue_stack(const hr_dims* dims, const hr_layer* layers, const hr_ba
   const bool fp8 = L0.wtype == HR_FP8_E4M3;
   hr::launch_embed_rmsnorm(ids, embed, x_embeds, T, D, L0.in_norm_w, dims->rms_eps, h_out, w.x, fp8,
                            fp8 ? 1.0f / L0.as_qkv : 1.f, stream);
+  if (qkv_rope_fused(dims, batch))   // the angles are the same for every layer
+    hr::launch_rope_table(batch->cu_seqlens, batch->start_pos, batch->n_seq, T, dims->head_dim, dims->rope_theta,
+                          w.rope, stream);
   // every layer's input norm after the first is fused into the previous
   // layer's last residual add
   for (int l = 0; l < dims->n_layers; ++l)

@@ -31,6 +31,7 @@
 #include <algorithm>
 #include "common.h"
 #include "launch.h"
+#include "rope_math.h"
 
 
 namespace hr {
@@ -150,6 +151,7 @@ struct EpiArgs {
   float* part;
   size_t part_stride;
   // MXFP4 operands: block scales in the slab-interleaved layout [K/128][ld][4]
+  QkvRope qr;            // HR_EPI_QKV_ROPE: where step A3 writes, its weights and tables
   const uint8_t* mx_sa;  // A scales, ld = mx_lda (M rounded up to the 256-row tile)
   const uint8_t* mx_sb;  // B scales, ld = N
   int mx_lda;
@@ -656,6 +658,76 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
 
   // epilogue: 32x32 accumulator layout, lane holds column lane % 32 and rows
   // 8 (r / 4) + 4 (lane / 32) + r % 4 of its block, r = 0..15
+  if constexpr (EPI == HR_EPI_QKV_ROPE) {
+    // Step A3 on the tile's fp32 rows: the tile (after the dtype scale) goes
+    // to LDS, then every (row, head) is handled as qknorm_rope_kv_kernel
+    // handles it — d/16 lanes, lane c owning the RoPE pairs (8c + i,
+    // d/2 + 8c + i), the head's sum of squares a butterfly over those lanes,
+    // the same rounding — so q and the cache receive the same bits.
+    static_assert(!MX && BN % 64 == 0, "whole heads of 64 or 128 per tile");
+    constexpr int LDT = BN + 4;                      // padded fp32 row of the tile in LDS
+    static_assert(size_t(BM) * LDT * 4 <= C::kLds, "the tile fits the slab ring");
+    float* sT = reinterpret_cast<float*>(smem);
+    wait_vm<0>();
+    __syncthreads();                                 // every wave is done with the ring
+#pragma unroll
+    for (int i = 0; i < IM; ++i)
+#pragma unroll
+      for (int j = 0; j < JN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = wm * (BM / WM) + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int cl = wn * (BN / WN) + j * 32 + r32;
+          sT[rl * LDT + cl] = scaled<FP8>(e, acc[i][j][r], n0 + cl);
+        }
+    __syncthreads();
+    const QkvRope& q = e.qr;
+    const int d = q.d, half = d >> 1, L = d >> 4;
+    const int heads = BN / d, items = BM * heads * L;
+    const int c = tid % L;
+    const uint16_t* qw = static_cast<const uint16_t*>(q.qw);
+    const uint16_t* kw = static_cast<const uint16_t*>(q.kw);
+    const u32x4 wq0 = *reinterpret_cast<const u32x4*>(qw + 8 * c);
+    const u32x4 wq1 = *reinterpret_cast<const u32x4*>(qw + half + 8 * c);
+    const u32x4 wk0 = *reinterpret_cast<const u32x4*>(kw + 8 * c);
+    const u32x4 wk1 = *reinterpret_cast<const u32x4*>(kw + half + 8 * c);
+    // rounds of C::kThreads items, every lane in every round (the butterfly)
+    for (int base = 0; base < items; base += C::kThreads) {
+      const int it = base + tid;
+      const bool ok = it < items;
+      const int rh = ok ? it / L : 0;
+      const int rl = rh / heads, hi = rh % heads;
+      const float* row = sT + rl * LDT + hi * d;
+      const F8 lo = F8{*reinterpret_cast<const floatx4*>(row + 8 * c), *reinterpret_cast<const floatx4*>(row + 8 * c + 4)};
+      const F8 up = F8{*reinterpret_cast<const floatx4*>(row + half + 8 * c),
+                       *reinterpret_cast<const floatx4*>(row + half + 8 * c + 4)};
+      const float ss = group_sum(pairs_sumsq(lo, up), L);
+      const int t = m0 + rl;
+      if (!ok || t >= M) continue;
+      const int hidx = (n0 + hi * d) / d;            // head among q, k, v heads
+      const int sq = find_seq(q.cu, q.n_seq, t);
+      const int ti = t - q.cu[sq];
+      const bool wkv = q.causal || ti < q.used_keys[sq];
+      const long long crow = (long long)q.cache_slot[sq] * q.capacity + q.start_pos[sq] + ti;
+      if (hidx < q.Hq + q.Hkv) {
+        const bool is_q = hidx < q.Hq;
+        if (!is_q && !wkv) continue;
+        const float inv = 1.0f / __builtin_sqrtf(ss / float(d) + q.eps);
+        const float* cs = q.rope + size_t(t) * d + 8 * c;
+        F8 o0, o1;
+        rope_pairs(lo, up, is_q ? wq0 : wk0, is_q ? wq1 : wk1, inv, cs, cs + half, o0, o1);
+        uint16_t* dst = is_q ? static_cast<uint16_t*>(q.q_out) + (size_t(t) * q.Hq + hidx) * d
+                             : static_cast<uint16_t*>(q.kc) + (size_t(crow) * q.Hkv + (hidx - q.Hq)) * d;
+        *reinterpret_cast<u32x4*>(dst + 8 * c) = is_q ? pack8_f16(o0) : pack8_bf16(o0);
+        *reinterpret_cast<u32x4*>(dst + half + 8 * c) = is_q ? pack8_f16(o1) : pack8_bf16(o1);
+      } else if (wkv) {
+        uint16_t* dst = static_cast<uint16_t*>(q.vc) + (size_t(crow) * q.Hkv + (hidx - q.Hq - q.Hkv)) * d;
+        *reinterpret_cast<u32x4*>(dst + 8 * c) = pack8_bf16(lo);
+        *reinterpret_cast<u32x4*>(dst + half + 8 * c) = pack8_bf16(up);
+      }
+    }
+    return;
+  }
   if constexpr (MX && EPI == HR_EPI_SWIGLU) {
     // silu(g) * u of one row's 32 columns of a gate/up block pair is one MX
     // block of the down projection's input: its amax over the 32 lanes of the
@@ -901,6 +973,30 @@ int launch_linear(const void* x, const void* w, const float* w_scale, float x_sc
   else { HR_DISPATCH(HR_EPI_SWIGLU) }
 #undef HR_DISPATCH
   return ks;
+}
+
+bool qkv_rope_fits(int M, int d) { return M > 384 && M <= 1024 && (d == 64 || d == 128); }
+
+// 128 x 128 tiles (the F32 table's choice for these rows): a tile column
+// block is one head of 128 or two of 64
+bool launch_qkv_rope(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8, bool packed,
+                     int M, int K, const QkvRope& qr, hipStream_t st) {
+  if (!qkv_rope_fits(M, qr.d)) return false;
+  EpiArgs e{};
+  e.epi = HR_EPI_QKV_ROPE;
+  e.x_scale = x_scale;
+  e.w_scale = w_scale;
+  e.qr = qr;
+  const int N = (qr.Hq + 2 * qr.Hkv) * qr.d;
+  e.ldo = N;
+  const int Kb = fp8 ? K : 2 * K;
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  const uint8_t* wb = static_cast<const uint8_t*>(w);
+  constexpr int E = HR_EPI_QKV_ROPE;
+  if (fp8) tiled_cfg<E, true, 128, 128, 2, 4, 4, 128>(xb, wb, M, N, Kb, e, 1, st);
+  else if (packed) tiled_cfg<E, false, 128, 128, 2, 4, 4, 128, false, true>(xb, wb, M, N, Kb, e, 1, st);
+  else tiled_cfg<E, false, 128, 128, 2, 4, 4, 128>(xb, wb, M, N, Kb, e, 1, st);
+  return true;
 }
 
 // MXFP4 x MXFP4: x codes [M, K/2] with scales (ld lda), w codes [N, K/2] with

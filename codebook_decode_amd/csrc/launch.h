@@ -9,6 +9,7 @@
 namespace hr {
 
 constexpr int HR_EPI_HEAD = 3;        // internal: fp32 logits from hi/lo bf16 rows
+constexpr int HR_EPI_QKV_ROPE = 5;    // internal: merged QKV rows -> q/k norm + RoPE + KV write
 
 
 void launch_codebook_step(int B, int K, int V, int bos, int eoc, bool f32, const void* logits,
@@ -97,6 +98,33 @@ void launch_decode_rope_attention(const void* qkv, const void* qw, const void* k
 int launch_linear(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8, bool packed,
                   int M, int N, int K, int epi, void* out, float out_scale, float* part, bool go,
                   hipStream_t st);
+// Merged QKV projection with step A3 in its epilogue: the fp32 rows of each
+// 128-column tile (whole heads) are normed (q / k, own weights), rotated and
+// written as the separate step writes them (q fp16 [T, Hq, d], K / V rows bf16
+// into the cache), with the angles from launch_rope_table's table.  Takes
+// 384 < M <= 1024 and d in {64, 128}; returns false (nothing launched)
+// otherwise.
+struct QkvRope {
+  void* q_out;
+  void* kc;
+  void* vc;
+  const int32_t* cu;
+  const int32_t* start_pos;
+  const int32_t* cache_slot;
+  const int32_t* used_keys;
+  int n_seq, causal, capacity, Hq, Hkv, d;
+  const void* qw;
+  const void* kw;
+  float eps;
+  const float* rope;   // [T][d]: cos of pairs m < d/2, then their sin
+};
+bool qkv_rope_fits(int M, int d);
+bool launch_qkv_rope(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8, bool packed,
+                     int M, int K, const QkvRope& qr, hipStream_t st);
+// the RoPE angle table of a batch: tab[t][m] = cos, tab[t][d/2 + m] = sin of
+// position(t) * theta^(-2m/d) (the same arithmetic as the q/k norm kernels)
+void launch_rope_table(const int32_t* cu, const int32_t* start_pos, int n_seq, int T, int d, float theta,
+                       float* tab, hipStream_t st);
 // bf16 W [N, K] -> packed fp16 (slab-major [K/32][N][32], gate_up: 32-row
 // gate / up blocks); synchronous; 0 ok, 1 a non-finite fp16 value, -1 HIP error
 int launch_pack_weight(const void* w, int N, int K, bool gate_up, void* out, hipStream_t st);

@@ -123,6 +123,30 @@ __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
   }
 }
 
+// The angle table of a batch for the QKV epilogue (launch_qkv_rope): one
+// thread per (token, pair m), the same angle arithmetic as the table of
+// qknorm_rope_kv_kernel, so both paths rotate by the same bits.
+__global__ __launch_bounds__(256) void rope_table_kernel(const int32_t* __restrict__ cu,
+                                                         const int32_t* __restrict__ start_pos, int n_seq, int T,
+                                                         int half, const RopeFreq freq, float* __restrict__ tab) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= T * half) return;
+  const int t = idx / half, m = idx % half;
+  const int s = find_seq(cu, n_seq, t);
+  const int p = start_pos[s] + (t - cu[s]);
+  float cs, sn;
+  rope_angle(p, freq.inv[m], cs, sn);
+  tab[size_t(t) * 2 * half + m] = cs;
+  tab[size_t(t) * 2 * half + half + m] = sn;
+}
+
+void launch_rope_table(const int32_t* cu, const int32_t* start_pos, int n_seq, int T, int d, float theta,
+                       float* tab, hipStream_t st) {
+  const int half = d / 2;
+  const RopeFreq freq = rope_freq(d, theta);
+  rope_table_kernel<<<(T * half + 255) / 256, 256, 0, st>>>(cu, start_pos, n_seq, T, half, freq, tab);
+}
+
 void launch_qknorm_rope_kv(const void* qkv, int T, int Hq, int Hkv, int d, float theta, float eps,
                            const int32_t* cu, const int32_t* start_pos, const int32_t* cache_slot,
                            const int32_t* used_keys, int n_seq, bool causal, const void* qw,

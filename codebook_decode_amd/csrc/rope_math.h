@@ -33,11 +33,20 @@ __device__ __forceinline__ u32x4 pack8_f16(const F8& v) {       // nearest even 
   return u32x4{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]), pack_f16x2(v[6], v[7])};
 }
 
+// The arithmetic below is spelled out operation by operation (explicit fmaf,
+// no contraction): these helpers are inlined into several kernels, and a
+// compiler free to fuse a multiply into an add could fuse them differently in
+// each, so the cache rows and q would differ between paths in the last bit.
+
 // sum of squares of a lane's 8 pairs of a head row
 __device__ __forceinline__ float pairs_sumsq(const F8& lo, const F8& hi) {
+#pragma clang fp contract(off)
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ss += lo[i] * lo[i] + hi[i] * hi[i];
+  for (int i = 0; i < 8; ++i) {
+    ss = __builtin_fmaf(lo[i], lo[i], ss);
+    ss = __builtin_fmaf(hi[i], hi[i], ss);
+  }
   return ss;
 }
 
@@ -47,14 +56,15 @@ __device__ __forceinline__ float pairs_sumsq(const F8& lo, const F8& hi) {
 // once, to bf16 for the cache or fp16 for q)
 __device__ __forceinline__ void rope_pairs(const F8& lo, const F8& hi, const u32x4& w0, const u32x4& w1,
                                            float inv, const float* cs, const float* sn, F8& o0, F8& o1) {
+#pragma clang fp contract(off)
   float y0[8], y1[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float a = lo[i] * inv * bf_at(w0, i);
-    const float b = hi[i] * inv * bf_at(w1, i);
+    const float a = (lo[i] * inv) * bf_at(w0, i);
+    const float b = (hi[i] * inv) * bf_at(w1, i);
     const float c = cs[i], s = sn[i];
-    y0[i] = a * c - b * s;
-    y1[i] = b * c + a * s;
+    y0[i] = __builtin_fmaf(a, c, -(b * s));
+    y1[i] = __builtin_fmaf(b, c, a * s);
   }
   o0 = F8{floatx4{y0[0], y0[1], y0[2], y0[3]}, floatx4{y0[4], y0[5], y0[6], y0[7]}};
   o1 = F8{floatx4{y1[0], y1[1], y1[2], y1[3]}, floatx4{y1[4], y1[5], y1[6], y1[7]}};
