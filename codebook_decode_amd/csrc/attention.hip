@@ -182,6 +182,12 @@ void attention_kernel(
   float l_part = 0.f;
 
   if (kt0 + grp < kt1) fetch((kt0 + grp) * AKT);
+  // q and the first tile land before the loop (the first staging needs the
+  // tile anyway).  Without this explicit wait the compiler, seeing the q loads
+  // possibly in flight at the loop head, guards the score MFMAs of every tile
+  // with waits that also cover the next tile's prefetch (vmcnt(7) .. vmcnt(0)
+  // right after the prefetch issues), serialising each fetch with the math.
+  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));   // vmcnt(0) only
   for (int kb = kt0; kb < kt1; kb += NG) {
     const int kt = kb + grp;
     const bool have = kt < kt1;      // the other group may still have a tile

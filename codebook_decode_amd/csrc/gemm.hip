@@ -150,6 +150,9 @@ struct EpiArgs {
   // not depend on the order in which workgroups finish.
   float* part;
   size_t part_stride;
+  // F32 / RESIDUAL / fp16 SwiGLU outputs may be stored as 16-byte row chunks
+  // (out and part 16-byte aligned, the output width and ldo whole chunks)
+  int vec_store;
   // MXFP4 operands: block scales in the slab-interleaved layout [K/128][ld][4]
   QkvRope qr;            // HR_EPI_QKV_ROPE: where step A3 writes, its weights and tables
   const uint8_t* mx_sa;  // A scales, ld = mx_lda (M rounded up to the 256-row tile)
@@ -753,6 +756,75 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
       }
     return;
   }
+  // Row-chunk stores through LDS: a lane's accumulators hold one column of
+  // 16 rows, so direct stores write 4 (fp32) or 2 (fp16) bytes per lane and
+  // instruction.  Instead each pass of 32 rows per wave row (IM passes) goes to
+  // LDS as the tile's output rows, then every thread stores 16-byte chunks of
+  // them (a wave instruction covers whole rows): a quarter to an eighth of
+  // the store instructions.  Same values, same bits as the direct stores.
+  if constexpr (!MX && (EPI == HR_EPI_F32 || EPI == HR_EPI_RESIDUAL || EPI == HR_EPI_SWIGLU)) {
+    if (e.vec_store) {
+      constexpr bool SG = EPI == HR_EPI_SWIGLU;
+      constexpr int EB = SG ? 2 : 4;                   // output bytes per element
+      constexpr int CO = SG ? BN / 2 : BN;             // output columns of the tile
+      constexpr int PR = 32 * WM;                      // tile rows per pass
+      constexpr int LDR = CO * EB + 32;                // padded LDS row (bytes): the two half-waves
+                                                       // (rows 4 apart) land on distinct banks
+      constexpr int CPR = CO * EB / 16;                // 16-byte chunks per row
+      static_assert(size_t(PR) * LDR <= C::kLds, "a pass fits the slab ring");
+      static_assert((CO * EB) % 64 == 0, "whole 64-byte row segments");
+      const int col0 = SG ? (n0 >> 1) : n0;            // first output column of the tile
+      const int ncol = SG ? e.F : N;
+      uint8_t* sE = smem;
+      wait_vm<0>();                                     // no copy into the ring in flight
+#pragma unroll
+      for (int i = 0; i < IM; ++i) {
+        __syncthreads();                                // the ring (or the previous pass) is free
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int lr = wm * 32 + 8 * (r >> 2) + 4 * h + (r & 3);   // row within the pass
+          if constexpr (SG) {
+#pragma unroll
+            for (int jj = 0; jj < JN / 2; ++jj) {
+              const int cl = (wn * (JN / 2) + jj) * 32 + r32;
+              const int col = col0 + cl;
+              const int cg = min(col, e.F - 1);
+              const float gt = scaled<FP8>(e, acc[i][2 * jj][r], cg);
+              const float up = scaled<FP8>(e, acc[i][2 * jj + 1][r], e.F + cg);
+              *reinterpret_cast<uint16_t*>(sE + lr * LDR + cl * 2) = uint16_t(f2h(silu(gt) * up));
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < JN; ++j) {
+              const int cl = wn * (BN / WN) + j * 32 + r32;
+              *reinterpret_cast<float*>(sE + lr * LDR + cl * 4) = scaled<FP8>(e, acc[i][j][r], min(n0 + cl, N - 1));
+            }
+          }
+        }
+        __syncthreads();
+        for (int c = tid; c < PR * CPR; c += C::kThreads) {
+          const int lr = c / CPR, ch = c % CPR;
+          const int row = m0 + (lr >> 5) * (BM / WM) + i * 32 + (lr & 31);
+          const int col = col0 + ch * (16 / EB);
+          if (row >= M || col >= ncol) continue;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(sE + lr * LDR + ch * 16);
+          if constexpr (SG) {
+            *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(e.out) + size_t(row) * e.ldo + col) = v;
+          } else if constexpr (EPI == HR_EPI_F32) {
+            *reinterpret_cast<u32x4*>(static_cast<float*>(e.out) + size_t(row) * e.ldo + col) = v;
+          } else if (ksplit == 1) {
+            floatx4* o = reinterpret_cast<floatx4*>(static_cast<float*>(e.out) + size_t(row) * e.ldo + col);
+            const floatx4 a = __builtin_bit_cast(floatx4, v);
+            const floatx4 b = *o;
+            *o = floatx4{b[0] + a[0], b[1] + a[1], b[2] + a[2], b[3] + a[3]};
+          } else {
+            *reinterpret_cast<u32x4*>(e.part + size_t(kz) * e.part_stride + size_t(row) * e.ldo + col) = v;
+          }
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < IM; ++i) {
 #pragma unroll
@@ -946,6 +1018,13 @@ int launch_linear(const void* x, const void* w, const float* w_scale, float x_sc
   e.ldo = (epi == HR_EPI_SWIGLU) ? N / 2 : N;
   e.part = part;
   e.part_stride = size_t(M) * size_t(N);
+  {
+    const int eb = (epi == HR_EPI_SWIGLU) ? 2 : 4;
+    const int width = (epi == HR_EPI_SWIGLU) ? N / 2 : N;
+    const bool al = reinterpret_cast<uintptr_t>(out) % 16 == 0 && reinterpret_cast<uintptr_t>(part) % 16 == 0;
+    e.vec_store = (epi == HR_EPI_F32 || epi == HR_EPI_RESIDUAL || (epi == HR_EPI_SWIGLU && !fp8)) && al &&
+                  (width * eb) % 16 == 0 && (e.ldo * eb) % 16 == 0;
+  }
   const int Kb = fp8 ? K : 2 * K;
   const uint8_t* xb = static_cast<const uint8_t*>(x);
   const uint8_t* wb = static_cast<const uint8_t*>(w);
