@@ -92,7 +92,7 @@ void attention_kernel(
   const int start = start_pos[s];
   const size_t base = size_t(cache_slot[s]) * capacity;
   const int lane = threadIdx.x & 63;
-  const int grp = int(threadIdx.x) / GT;            // key-tile group
+  const int grp = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / GT);   // key-tile group (wave-uniform)
   const int tid = int(threadIdx.x) % GT, wave = tid >> 6;   // within the group
   uint16_t* sK = smem + grp * kGroupLds;
   uint16_t* sVt = sK + AKT * K_LD;
@@ -133,7 +133,29 @@ void attention_kernel(
   const uint16_t* vbase = vc + (base * Hkv + g) * DH;
   const size_t row_stride = size_t(Hkv) * DH;
   const int last_key = n_keys - 1;
+  // A thread's chunk j is its chunk 0 moved by a uniform step: KROWS rows
+  // for K, VCOLS elements for V.  So a tile inside the keys is fetched from a
+  // uniform base plus one byte offset per thread (scalar base + vector offset
+  // addressing: no per-load address arithmetic).
+  static_assert(GT % (DH / 8) == 0 && GT % (AKT / 2) == 0, "uniform chunk steps");
+  constexpr int KROWS = GT / (DH / 8);
+  constexpr int VCOLS = GT / (AKT / 2) * 8;
+  const uint32_t k_off = (uint32_t(tid / (DH / 8)) * uint32_t(row_stride) + uint32_t(tid % (DH / 8)) * 8) * 2;
+  const uint32_t v_off = (uint32_t(2 * (tid % (AKT / 2))) * uint32_t(row_stride) + uint32_t(tid / (AKT / 2)) * 8) * 2;
   auto fetch = [&](int k0) {
+    if (k0 + AKT <= n_keys) {          // uniform: no row of the tile past the keys
+      const uint8_t* kt = reinterpret_cast<const uint8_t*>(kbase + size_t(k0) * row_stride);
+      const uint8_t* vt = reinterpret_cast<const uint8_t*>(vbase + size_t(k0) * row_stride);
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        rk[j] = *reinterpret_cast<const u32x4*>(kt + size_t(j) * KROWS * row_stride * 2 + k_off);
+#pragma unroll
+      for (int j = 0; j < VPT; ++j)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          rv[j][e] = *reinterpret_cast<const u32x4*>(vt + (size_t(e) * row_stride + j * VCOLS) * 2 + v_off);
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int c = tid + GT * j;
