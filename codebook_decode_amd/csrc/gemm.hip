@@ -151,7 +151,10 @@ struct EpiArgs {
   float* part;
   size_t part_stride;
   // F32 / RESIDUAL / fp16 SwiGLU outputs may be stored as 16-byte row chunks
-  // (out and part 16-byte aligned, the output width and ldo whole chunks)
+  // (out and part 16-byte aligned, the output width and ldo whole chunks:
+  // always so through the entry points, which require aligned buffers and N
+  // a multiple of 16; the element-wise stores remain for the e4m3 SwiGLU
+  // output and the MXFP4 residual tiles)
   int vec_store;
   // MXFP4 operands: block scales in the slab-interleaved layout [K/128][ld][4]
   QkvRope qr;            // HR_EPI_QKV_ROPE: where step A3 writes, its weights and tables

@@ -175,8 +175,9 @@ def test_linear_tiled_bf16(H, M):
 
 # the down projection's shapes (N 2560, K 9728) at every row range whose tile
 # the dispatch picks differently: 17-64 rows, 65-128 (the 128-row prefill),
-# 129-384, 385-1024 (the 512-row prefill, split-K 6) and above 1024
-@pytest.mark.parametrize("M", [17, 64, 65, 128, 129, 512, 1100])
+# 129-384, 385-576 (the 512-row prefill, 128 x 128 tiles split 3), 577-1024
+# (256 x 128 split 6) and above 1024
+@pytest.mark.parametrize("M", [17, 64, 65, 128, 129, 512, 600, 1100])
 def test_linear_down_shapes(H, M):
     _linear_case(H, M, 2560, 9728, H.HR_EPI_RESIDUAL, seed=M + 7)
 
