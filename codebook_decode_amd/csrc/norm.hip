@@ -121,40 +121,75 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
 // MXFP4 of x * col (OCP MX blocks of 32, the 4 threads of a block adjacent
 // lanes), or nothing (the last layer's residual).  ks = 0: the plain RMSNorm
 // of h.  One row per workgroup, 8 values per thread, 128-bit accesses.
-template <int OUT>
+template <int OUT, int CPT>
 __global__ __launch_bounds__(kNormThreads) void residual_norm_kernel(
     float* __restrict__ h, const float* __restrict__ part, int ks, size_t part_stride, int D,
     const uint16_t* __restrict__ w, float eps, void* __restrict__ x_out, float inv_scale,
     const float* __restrict__ col, uint8_t* __restrict__ mx_scales, int mx_ld) {
+  // CPT: chunks of 8 values per thread (D <= 2048 CPT)
   __shared__ float red[kNormThreads / 64];
   const int t = blockIdx.x;
   const int n8 = D >> 3;
-  u32x4 wq[kNormMaxPerThread];
+  u32x4 wq[CPT];
   if constexpr (OUT != kNormNone) {
 #pragma unroll
-    for (int c = 0; c < kNormMaxPerThread; ++c) {
+    for (int c = 0; c < CPT; ++c) {
       const int i8 = threadIdx.x + c * kNormThreads;
       wq[c] = i8 < n8 ? reinterpret_cast<const u32x4*>(w)[i8] : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  float v[kNormMaxPerThread][8];
-  float ss = 0.f;
+  // h and every partial of the thread's chunks are requested before any sum
+  // (KB partials per batch): the loads overlap instead of one memory round
+  // trip per partial and chunk.  The sums keep the split order, h + (p0 + p1 + ...).
+  constexpr int KB = 4;
+  floatx4 ha[CPT], hb[CPT], sa[CPT], sb[CPT];
 #pragma unroll
-  for (int c = 0; c < kNormMaxPerThread; ++c) {
+  for (int c = 0; c < CPT; ++c) {
     const int i8 = threadIdx.x + c * kNormThreads;
     if (i8 < n8) {
-      floatx4* hp = reinterpret_cast<floatx4*>(h + size_t(t) * D) + 2 * i8;
-      floatx4 a = hp[0], b = hp[1];
-      if (ks > 0) {
-        const floatx4* pp = reinterpret_cast<const floatx4*>(part + size_t(t) * D) + 2 * i8;
-        floatx4 sa = pp[0], sb = pp[1];
-        for (int kz = 1; kz < ks; ++kz) {
-          const floatx4* q = reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(pp) + kz * part_stride);
-          sa += q[0];
-          sb += q[1];
+      const floatx4* hp = reinterpret_cast<const floatx4*>(h + size_t(t) * D) + 2 * i8;
+      ha[c] = hp[0];
+      hb[c] = hp[1];
+    }
+  }
+  for (int kz0 = 0; kz0 < ks; kz0 += KB) {
+    floatx4 qa[KB][CPT], qb[KB][CPT];
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int i8 = threadIdx.x + c * kNormThreads;
+        if (kz0 + u < ks && i8 < n8) {
+          const floatx4* q = reinterpret_cast<const floatx4*>(part + size_t(kz0 + u) * part_stride + size_t(t) * D) + 2 * i8;
+          qa[u][c] = q[0];
+          qb[u][c] = q[1];
         }
-        a += sa;
-        b += sb;
+      }
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        if (kz0 + u >= ks) continue;
+        if (kz0 + u == 0) {
+          sa[c] = qa[u][c];
+          sb[c] = qb[u][c];
+        } else {
+          sa[c] += qa[u][c];
+          sb[c] += qb[u][c];
+        }
+      }
+  }
+  float v[CPT][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int i8 = threadIdx.x + c * kNormThreads;
+    if (i8 < n8) {
+      floatx4 a = ha[c], b = hb[c];
+      if (ks > 0) {
+        a += sa[c];
+        b += sb[c];
+        floatx4* hp = reinterpret_cast<floatx4*>(h + size_t(t) * D) + 2 * i8;
         hp[0] = a;
         hp[1] = b;
       }
@@ -168,7 +203,7 @@ __global__ __launch_bounds__(kNormThreads) void residual_norm_kernel(
   const float tot = block_sum(ss, red);
   const float r = 1.0f / __builtin_sqrtf(tot / float(D) + eps);
 #pragma unroll
-  for (int c = 0; c < kNormMaxPerThread; ++c) {
+  for (int c = 0; c < CPT; ++c) {
     const int i8 = threadIdx.x + c * kNormThreads;
     if constexpr (OUT == kNormMX) {
       if (c * kNormThreads >= n8) break;            // uniform: every lane of a block takes part below
@@ -218,15 +253,28 @@ __global__ __launch_bounds__(256) void residual_sum_kernel(float* __restrict__ h
   const size_t n8 = n >> 3;
   for (size_t i8 = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i8 < n8; i8 += size_t(gridDim.x) * blockDim.x) {
     floatx4* hp = reinterpret_cast<floatx4*>(h) + 2 * i8;
-    const floatx4* pp = reinterpret_cast<const floatx4*>(part) + 2 * i8;
-    floatx4 sa = pp[0], sb = pp[1];
-    for (int kz = 1; kz < ks; ++kz) {
-      const floatx4* q = reinterpret_cast<const floatx4*>(part + kz * n) + 2 * i8;
-      sa += q[0];
-      sb += q[1];
+    const floatx4 ha = hp[0], hb = hp[1];
+    // all partials of a batch requested before the sums (split order kept)
+    constexpr int KB = 4;
+    floatx4 sa, sb;
+    for (int kz0 = 0; kz0 < ks; kz0 += KB) {
+      floatx4 qa[KB], qb[KB];
+#pragma unroll
+      for (int u = 0; u < KB; ++u)
+        if (kz0 + u < ks) {
+          const floatx4* q = reinterpret_cast<const floatx4*>(part + size_t(kz0 + u) * n) + 2 * i8;
+          qa[u] = q[0];
+          qb[u] = q[1];
+        }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        if (kz0 + u >= ks) continue;
+        if (kz0 + u == 0) { sa = qa[u]; sb = qb[u]; }
+        else { sa += qa[u]; sb += qb[u]; }
+      }
     }
-    hp[0] = hp[0] + sa;
-    hp[1] = hp[1] + sb;
+    hp[0] = ha + sa;
+    hp[1] = hb + sb;
   }
 }
 
@@ -243,23 +291,24 @@ void launch_residual_norm(float* h, const float* part, int ks, int T, int D, con
   const size_t stride = size_t(T) * size_t(D);
   const uint16_t* w16 = static_cast<const uint16_t*>(w);
   if (out_mode == kNormNone && ks <= 0) return;
-  switch (out_mode) {
-    case kNormNone:
-      residual_norm_kernel<kNormNone><<<T, kNormThreads, 0, st>>>(h, part, ks, stride, D, w16, eps, x_out, inv_scale,
-                                                                   col, mx_scales, mx_ld);
-      break;
-    case kNormE4M3:
-      residual_norm_kernel<kNormE4M3><<<T, kNormThreads, 0, st>>>(h, part, ks, stride, D, w16, eps, x_out, inv_scale,
-                                                                   col, mx_scales, mx_ld);
-      break;
-    case kNormMX:
-      residual_norm_kernel<kNormMX><<<T, kNormThreads, 0, st>>>(h, part, ks, stride, D, w16, eps, x_out, inv_scale,
-                                                                 col, mx_scales, mx_ld);
-      break;
-    default:
-      residual_norm_kernel<kNormF16><<<T, kNormThreads, 0, st>>>(h, part, ks, stride, D, w16, eps, x_out, inv_scale,
-                                                                  col, mx_scales, mx_ld);
+  const int cpt = (D / 8 + kNormThreads - 1) / kNormThreads;   // 1 .. kNormMaxPerThread (D <= 8192)
+  auto go = [&](auto kern) {
+    kern<<<T, kNormThreads, 0, st>>>(h, part, ks, stride, D, w16, eps, x_out, inv_scale, col, mx_scales, mx_ld);
+  };
+#define HR_NORM_CPT(MODE)                                      \
+  switch (cpt) {                                               \
+    case 1: go(residual_norm_kernel<MODE, 1>); break;          \
+    case 2: go(residual_norm_kernel<MODE, 2>); break;          \
+    case 3: go(residual_norm_kernel<MODE, 3>); break;          \
+    default: go(residual_norm_kernel<MODE, 4>);                \
   }
+  switch (out_mode) {
+    case kNormNone: HR_NORM_CPT(kNormNone); break;
+    case kNormE4M3: HR_NORM_CPT(kNormE4M3); break;
+    case kNormMX: HR_NORM_CPT(kNormMX); break;
+    default: HR_NORM_CPT(kNormF16);
+  }
+#undef HR_NORM_CPT
 }
 
 // z = RMS(h[row]) * w (fp32); out rows s (hi) and n_rows + s (lo), bf16, stride D.
