@@ -976,7 +976,12 @@ static int tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const
   if constexpr (EPI == HR_EPI_SWIGLU) {
     if (M <= 64) return tiled_fill<EPI, FP8, 64, 128, 2, 2, 6, 128, false, PK>(x, w, M, N, Kb, e, st, go);
     if (M > 384) {
-      if constexpr (FP8) return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128, false, PK>(x, w, M, N, Kb, e, st, go);
+      if constexpr (FP8) {
+        // e4m3, 385-576 rows: 192 x 256 tiles with 64-byte slabs (228
+        // workgroups; the FP8 layer at 544 rows 174 -> 165 us)
+        if (M <= 576) return tiled_fill<EPI, FP8, 192, 256, 2, 4, 4, 64, false, PK>(x, w, M, N, Kb, e, st, go);
+        return tiled_fill<EPI, FP8, 128, 128, 4, 2, 4, 128, false, PK>(x, w, M, N, Kb, e, st, go);
+      }
       // packed weights, 385-576 rows: 192-row tiles, 3 x 76 = 228 workgroups
       // for the 4B gate/up instead of 152 (M = 512: 76.9 -> 67.4 us; with the
       // in-register conversion the 192-row tile only broke even)
@@ -995,6 +1000,9 @@ static int tiled(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, const
     return tiled_fill<EPI, FP8, 64, 64, 2, 2, 8, 128, false, PK>(x, w, M, N, Kb, e, st, go);
   } else {
     if constexpr (FP8) {
+      // e4m3 O and down at 385-576 rows: 128 x 128 tiles split 2 ways (the
+      // FP8 layer 165 -> 159 us against 64 x 64 unsplit)
+      if (M > 384 && M <= 576) return tiled_fill<EPI, FP8, 128, 128, 2, 4, 4, 128, false, PK>(x, w, M, N, Kb, e, st, go, 2);
       if (M > 128) return tiled_fill<EPI, FP8, 64, 64, 2, 2, 4, 128, false, PK>(x, w, M, N, Kb, e, st, go);
     }
     if (M > 1024) return tiled_fill<EPI, FP8, 128, 128, 2, 4, 4, 128, false, PK>(x, w, M, N, Kb, e, st, go);

@@ -182,7 +182,9 @@ def test_linear_down_shapes(H, M):
     _linear_case(H, M, 2560, 9728, H.HR_EPI_RESIDUAL, seed=M + 7)
 
 
-@pytest.mark.parametrize("M", [13, 200])
+# 13 rows: skinny; 200: tiled; 512: the 385-576-row e4m3 tiles (192 x 256
+# SwiGLU, 128 x 128 residual split 2)
+@pytest.mark.parametrize("M", [13, 200, 512])
 def test_linear_fp8(H, M):
     _linear_case(H, M, 512, 1024, H.HR_EPI_F32, fp8=True, seed=M)
     _linear_case(H, M, 256, 512, H.HR_EPI_RESIDUAL, fp8=True, seed=M)
