@@ -199,8 +199,11 @@ def test_linear_rejects_bad_shapes(H):
 
 
 # ----------------------------------------------------------------------------- A6 / A9 fused
+# D sets the chunks per thread (2560: 2, 256: 1, 6144: 3, 8192: 4); ks above 4
+# takes several batches of partial loads
 @pytest.mark.parametrize("T,D,ks,fmt", [(13, 2560, 5, "f16"), (512, 2560, 6, "f16"), (300, 256, 1, "e4m3"),
-                                        (7, 2560, 0, "f16"), (40, 2560, 3, "none")])
+                                        (7, 2560, 0, "f16"), (40, 2560, 3, "none"), (9, 8192, 6, "f16"),
+                                        (5, 6144, 3, "e4m3"), (3, 4096, 9, "none")])
 def test_residual_rmsnorm(H, T, D, ks, fmt):
     """h += p0 + ... + p_{ks-1} (split order), then RMS(h) * w in fp16 / e4m3
     (or nothing), against float64; run twice on the same inputs the bits must
