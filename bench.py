@@ -508,14 +508,16 @@ def cpu_baseline(m, P, host_layers, shared_host):
 
 def probe(H, m, layers, shared, dev_layers):
     """Launches for the counter runs (rocprofv3 --pmc): three P=512 stack
-    steps, the FP8 layer, the memory-bound kernels at sweep sizes and a
-    256 MiB device copy whose counter readings calibrate the byte counters."""
+    steps, three P=13 steps (the weight-streaming projections), the FP8
+    layer, the memory-bound kernels at sweep sizes and a 256 MiB device copy
+    whose counter readings calibrate the byte counters."""
     import torch
-    st = Stack(H, m, 512, dev_layers, layers, shared)
-    for _ in range(3):
-        st.step()
-    torch.cuda.synchronize()
-    del st
+    for P in (512, 13):
+        st = Stack(H, m, P, dev_layers, layers, shared)
+        for _ in range(3):
+            st.step()
+        torch.cuda.synchronize()
+        del st
     fp8_layer(H, m, dev_layers[0], reps=2)
     sweep = hbm_sweep(H, m, shared, reps=2)
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
