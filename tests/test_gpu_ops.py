@@ -400,6 +400,9 @@ def test_qknorm_rope_attention(H, model, lens, slots, causal, used, fp8):
     (4, 2, 64, [6, 70], [0, 10], True, None),
     (8, 8, 64, [33], [0], True, None),
     (32, 8, 128, [100], [0], False, [90]),
+    # causal rows of 4+ tiles on a short grid (the head split, two wave groups)
+    (32, 8, 128, [512], [0], True, None),
+    (32, 8, 128, [300, 129], [0, 50], True, None),
     # one row per sequence (decode steps: the decode kernel, one chunk per row)
     (32, 8, 128, [1, 1, 1], [0, 700, 2000], True, None),
     (4, 2, 64, [1, 1], [5, 130], True, None),
