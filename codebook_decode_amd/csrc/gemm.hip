@@ -886,10 +886,13 @@ static void skinny(const uint8_t* x, const uint8_t* w, int M, int N, int Kb, con
   constexpr int NB1 = (EPI == HR_EPI_SWIGLU) ? 2 : CB1;
   if (mb == 1) {
     // all of a wave's steps in one batch when they fit (5 steps x NB = 1 block
-    // measured faster than 4 + 1; at NB = 2 the 5-step batch costs occupancy)
+    // measured faster than 4 + 1; at NB = 2 the 5-step batch costs occupancy,
+    // except for the fp32 epilogue, whose grid (the merged QKV rows: 192
+    // workgroups) has one workgroup per CU anyway: M = 13, 9.4 -> 8.9 us)
     if (spw <= 2) gemm_skinny_kernel<8, 1, EPI, FP8, 2, CB1, PK><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
     else if (spw == 3) gemm_skinny_kernel<8, 1, EPI, FP8, 3, CB1, PK><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
-    else if (spw == 5 && NB1 == 1) gemm_skinny_kernel<8, 1, EPI, FP8, 5, CB1, PK><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
+    else if (spw == 5 && (NB1 == 1 || EPI == HR_EPI_F32))
+      gemm_skinny_kernel<8, 1, EPI, FP8, 5, CB1, PK><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
     else gemm_skinny_kernel<8, 1, EPI, FP8, 4, CB1, PK><<<grid, 512, 0, st>>>(x, w, M, N, Kb, e);
   } else if (EPI == HR_EPI_SWIGLU) {
     if (mb == 2) gemm_skinny_kernel<4, 2, EPI, FP8, 4, 1, PK><<<grid, 256, 0, st>>>(x, w, M, N, Kb, e);

@@ -174,58 +174,51 @@ void launch_qknorm_rope_kv(const void* qkv, int T, int Hq, int Hkv, int d, float
 // softmax from LDS, which saves the round trip of q through memory and a
 // launch whose work is tiny at these sizes.  The rows get the same arithmetic
 // as in qknorm_rope_kv_kernel (pairs_sumsq, rope_pairs, rope_angle), so the
-// cache receives the same bits.  8 waves; wave w takes queries w, w + 8, ...
-// (NQ of them, the last ones clamped and discarded, so that no loop branches).
-// Scores: lane j takes key j; the k rows sit in LDS padded by 16 bytes (one
-// 16-byte read per lane and d step, no bank conflict), q rows are broadcast
-// reads.  Softmax in fp32 (base 2, the scale folded into one multiply) with the
-// exact row max; the max and the sum are DPP reductions within rows of 16
-// lanes and a fixed-order combination of the 4 rows.  P V: lane l owns output
-// dims 2l and 2l + 1 and takes each probability from lane j by readlane.  The
-// output is o / l rounded once (fp16, or e4m3 of o / l times out_inv).  q is
-// held in fp16 and k, v in bf16, the values the separate kernels store.
+// cache receives the same bits.  8 waves share the row work (a wave takes
+// rows of one kind); then one wave computes the head's attention as one block
+// of 32 queries x 32 keys with v_mfma_f32_32x32x16_f16, in the form of
+// attention_kernel: S^T = K Q^T (the
+// lane's accumulator column is query l % 32, its 16 rows keys
+// 8(r/4) + 4(l/32) + r%4), the softmax per lane plus one exchange with lane
+// l ^ 32, then O^T = V^T P^T with the lane's own probabilities as the B
+// operand.  LDS holds q in fp16 (as the separate q/k-norm kernel stores it),
+// k and v as their bf16 cache values widened exactly to fp16, v transposed
+// (its columns past the prompt zero, so masked keys add 0 x 0).  Rows past the
+// prompt read its last row (finite; their scores are masked or their outputs
+// not stored).  Softmax in fp32, base 2 with the scale folded into one FMA,
+// probabilities rounded to fp16 for the MFMA; the output is o / l rounded once
+// (fp16, or e4m3 of o / l times out_inv).
 // Causal: keys j <= i; otherwise keys j < used_keys[s].
-template <int CTRL>
-__device__ __forceinline__ float dpp_row(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float lane_f(float v, int j) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
-}
-// max / sum over the wave: within each row of 16 lanes (quad swaps, then the
-// half-row and row mirrors: every source lane exists), then over the 4 rows
-__device__ __forceinline__ float wave_max_dpp(float v) {
-  v = fmaxf(v, dpp_row<0xb1>(v));
-  v = fmaxf(v, dpp_row<0x4e>(v));
-  v = fmaxf(v, dpp_row<0x141>(v));
-  v = fmaxf(v, dpp_row<0x140>(v));
-  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
-}
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  v = v + dpp_row<0xb1>(v);
-  v = v + dpp_row<0x4e>(v);
-  v = v + dpp_row<0x141>(v);
-  v = v + dpp_row<0x140>(v);
-  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
-}
-
 constexpr int kSmallWaves = 8;
 
-template <int D, int NQ>
+__device__ __forceinline__ floatx16 mfma32x16_f16(u32x4 a, u32x4 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                0, 0);
+}
+
+template <int D>
 __global__ __launch_bounds__(64 * kSmallWaves) void rope_attn_small_kernel(
     const float* __restrict__ qkv, int Hq, int Hkv, const RopeFreq freq, float eps,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ cache_slot, const int32_t* __restrict__ used_keys,
     int causal, const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw, uint16_t* __restrict__ kc,
     uint16_t* __restrict__ vc, int capacity, float scale_log2, void* __restrict__ out, int out_fp8,
     float out_inv) {
+  static_assert(kSmallRows == 32, "one 32 x 32 block of queries and keys");
   constexpr int NT = 64 * kSmallWaves;
-  constexpr int HALF = D / 2, L = D / 16, PER = NT / L;     // lanes per head row, rows per round
-  constexpr int NR = (3 * kSmallRows + PER - 1) / PER;      // rounds of rows (all loads in flight)
-  constexpr int KLD = D + 8;                                 // padded k row (elements)
+  constexpr int HALF = D / 2, L = D / 16, RPW = kWave / L;  // lanes per head row, rows per wave
+  // rounds of head rows (all loads in flight): a wave takes RPW rows of one
+  // kind (q, k or v), ceil(len / RPW) waves per kind, so no wave branches on
+  // the kind and the three kinds run side by side
+  constexpr int NR = (3 * ((kSmallRows + RPW - 1) / RPW) + kSmallWaves - 1) / kSmallWaves;
+  constexpr int LD = D + 8;                                  // padded q / k row (elements)
+  // key stride of v^T: 17 words, odd, so the 32 rows of a fragment read and
+  // the rows 8c + 2e that a v row's 8 lanes scatter to fall in distinct banks
+  constexpr int VLD = kSmallRows + 2;
+  constexpr int NKS = D / 16, NDB = D / 32;
   __shared__ float s_cos[kSmallRows][HALF], s_sin[kSmallRows][HALF];
-  __shared__ __attribute__((aligned(16))) uint16_t s_q[kSmallRows][D];
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[kSmallRows][KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[kSmallRows][D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[kSmallRows][LD];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[kSmallRows][LD];
+  __shared__ __attribute__((aligned(16))) uint16_t s_vt[D][VLD];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hq = blockIdx.x, s = blockIdx.y;
@@ -237,14 +230,16 @@ __global__ __launch_bounds__(64 * kSmallWaves) void rope_attn_small_kernel(
   const long long crow0 = (long long)cache_slot[s] * capacity;
   const int n_rows = Hq + 2 * Hkv;
   const int c = tid % L;
+  const int kw_waves = (len + RPW - 1) / RPW;                // waves per kind
 
-  // rows rr < 3 len: q of token rr, then k of token rr - len, then v
+  // round k of wave w is slot w' = 8 k + w: kind w' / kw_waves (0 q, 1 k, 2 v),
+  // row RPW (w' % kw_waves) + lane / L of that kind
   F8 lo[NR], hi[NR];
 #pragma unroll
   for (int k = 0; k < NR; ++k) {
-    const int rr = tid / L + k * PER;
-    if (rr < 3 * len) {
-      const int kind = rr / len, i = rr - kind * len;
+    const int slot = k * kSmallWaves + wave, kind = slot / kw_waves;
+    const int i = (slot % kw_waves) * RPW + lane / L;
+    if (kind < 3 && i < len) {
       const int head = kind == 0 ? hq : (kind == 1 ? Hq + g : Hq + Hkv + g);
       const float* src = qkv + (size_t(t0 + i) * n_rows + head) * D;
       lo[k] = load_f8(src + 8 * c);
@@ -262,34 +257,46 @@ __global__ __launch_bounds__(64 * kSmallWaves) void rope_attn_small_kernel(
     const int i = a / HALF, m = a % HALF;
     rope_angle(i, freq.inv[m], s_cos[i][m], s_sin[i][m]);
   }
+  // v^T zeroed (the columns past the prompt stay zero: their probabilities are 0)
+  for (int a = tid; a < D * (kSmallRows / 2); a += NT)
+    reinterpret_cast<uint32_t*>(&s_vt[0][0])[(a / (kSmallRows / 2)) * (VLD / 2) + a % (kSmallRows / 2)] = 0u;
   __syncthreads();
 
 #pragma unroll
   for (int k = 0; k < NR; ++k) {
-    const int rr = tid / L + k * PER;
+    const int slot = k * kSmallWaves + wave, kind = slot / kw_waves;
+    const int i = (slot % kw_waves) * RPW + lane / L;
     const float ss = group_sum(pairs_sumsq(lo[k], hi[k]), L);   // every lane of the wave takes part
-    if (rr >= 3 * len) continue;
-    const int kind = rr / len, i = rr - kind * len;
+    if (kind >= 3 || i >= len) continue;
     const bool kv_row = write_kv && (causal || i < n_keys);
     if (kind < 2) {
       const float inv = 1.0f / __builtin_sqrtf(ss / float(D) + eps);
       F8 r0, r1;
       rope_pairs(lo[k], hi[k], kind == 0 ? wq0 : wk0, kind == 0 ? wq1 : wk1, inv, &s_cos[i][8 * c],
                  &s_sin[i][8 * c], r0, r1);
-      const u32x4 o0 = kind == 0 ? pack8_f16(r0) : pack8_bf16(r0);
-      const u32x4 o1 = kind == 0 ? pack8_f16(r1) : pack8_bf16(r1);
-      uint16_t* row = kind == 0 ? &s_q[i][0] : &s_k[i][0];
-      *reinterpret_cast<u32x4*>(row + 8 * c) = o0;
-      *reinterpret_cast<u32x4*>(row + HALF + 8 * c) = o1;
-      if (kind == 1 && kv_row) {
-        uint16_t* dst = kc + (size_t(crow0 + i) * Hkv + g) * D;
-        *reinterpret_cast<u32x4*>(dst + 8 * c) = o0;
-        *reinterpret_cast<u32x4*>(dst + HALF + 8 * c) = o1;
+      if (kind == 0) {
+        *reinterpret_cast<u32x4*>(&s_q[i][8 * c]) = pack8_f16(r0);
+        *reinterpret_cast<u32x4*>(&s_q[i][HALF + 8 * c]) = pack8_f16(r1);
+      } else {
+        const u32x4 o0 = pack8_bf16(r0), o1 = pack8_bf16(r1);
+        *reinterpret_cast<u32x4*>(&s_k[i][8 * c]) = bf8_to_f16x8(o0);
+        *reinterpret_cast<u32x4*>(&s_k[i][HALF + 8 * c]) = bf8_to_f16x8(o1);
+        if (kv_row) {
+          uint16_t* dst = kc + (size_t(crow0 + i) * Hkv + g) * D;
+          *reinterpret_cast<u32x4*>(dst + 8 * c) = o0;
+          *reinterpret_cast<u32x4*>(dst + HALF + 8 * c) = o1;
+        }
       }
     } else {
       const u32x4 v0 = pack8_bf16(lo[k]), v1 = pack8_bf16(hi[k]);
-      *reinterpret_cast<u32x4*>(&s_v[i][8 * c]) = v0;
-      *reinterpret_cast<u32x4*>(&s_v[i][HALF + 8 * c]) = v1;
+      const u32x4 h0 = bf8_to_f16x8(v0), h1 = bf8_to_f16x8(v1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s_vt[8 * c + 2 * e][i] = uint16_t(h0[e]);
+        s_vt[8 * c + 2 * e + 1][i] = uint16_t(h0[e] >> 16);
+        s_vt[HALF + 8 * c + 2 * e][i] = uint16_t(h1[e]);
+        s_vt[HALF + 8 * c + 2 * e + 1][i] = uint16_t(h1[e] >> 16);
+      }
       if (kv_row) {
         uint16_t* dst = vc + (size_t(crow0 + i) * Hkv + g) * D;
         *reinterpret_cast<u32x4*>(dst + 8 * c) = v0;
@@ -298,78 +305,82 @@ __global__ __launch_bounds__(64 * kSmallWaves) void rope_attn_small_kernel(
     }
   }
   __syncthreads();
-  if (wave >= len) return;                                   // no query for this wave (no barrier follows)
+  if (wave != 0) return;                                     // one wave per head (no barrier follows)
 
-  // scores of queries i = wave + 8 qi (clamped to the last row) against key j = lane
-  int qrow[NQ];
+  const int half = lane >> 5, r32 = lane & 31;
+  const int qrow = min(r32, len - 1), krow = qrow;           // rows past the prompt: its last row
+  floatx16 sc;
 #pragma unroll
-  for (int qi = 0; qi < NQ; ++qi) qrow[qi] = min(wave + kSmallWaves * qi, len - 1);
-  const int krow = lane < n_keys ? lane : n_keys - 1;
-  float acc[NQ];
+  for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
-  for (int qi = 0; qi < NQ; ++qi) acc[qi] = 0.f;
-#pragma unroll 4
-  for (int d8 = 0; d8 < D / 8; ++d8) {
-    const u32x4 kv = *reinterpret_cast<const u32x4*>(&s_k[krow][8 * d8]);
-    u32x4 qv[NQ];
+  for (int ks = 0; ks < NKS; ++ks) {
+    const u32x4 kf = *reinterpret_cast<const u32x4*>(&s_k[krow][16 * ks + 8 * half]);
+    const u32x4 qf = *reinterpret_cast<const u32x4*>(&s_q[qrow][16 * ks + 8 * half]);
+    sc = mfma32x16_f16(kf, qf, sc);
+  }
+  // lane: query j = r32; element r: key 8(r/4) + 4 half + r%4
+  const int j_max = causal ? r32 : n_keys - 1;
+  float mt = -INFINITY;
 #pragma unroll
-    for (int qi = 0; qi < NQ; ++qi) qv[qi] = *reinterpret_cast<const u32x4*>(&s_q[qrow[qi]][8 * d8]);
+  for (int r = 0; r < 16; ++r) {
+    const int key = 8 * (r >> 2) + 4 * half + (r & 3);
+    if (key > j_max) sc[r] = -INFINITY;
+    mt = fmaxf(mt, sc[r]);
+  }
+  mt = fmaxf(mt, __shfl_xor(mt, 32, kWave)) * scale_log2;   // scale > 0: the max commutes
+  float l_part = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float kf = bf_at(kv, e);
+  for (int r = 0; r < 16; ++r) {
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], scale_log2, -mt));   // masked: 0
+    sc[r] = p;
+    l_part += p;
+  }
+  const float l = l_part + __shfl_xor(l_part, 32, kWave);
+  floatx16 o[NDB];
 #pragma unroll
-      for (int qi = 0; qi < NQ; ++qi) acc[qi] += h_at(qv[qi], e) * kf;
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  // the k slots of lane half h are keys {4h..4h+3, 8+4h..8+4h+3} of a 16-key
+  // step for both operands: the lane's own probabilities r = 8kk..8kk+7
+  const int n_kk = len > 16 ? 2 : 1;                         // keys 16..31 all masked otherwise
+  for (int kk = 0; kk < n_kk; ++kk) {
+    u32x4 pb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pb[e] = pack_f16x2(sc[8 * kk + 2 * e], sc[8 * kk + 2 * e + 1]);
+    const int kb = 16 * kk + 4 * half;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const uint32_t* vrow = reinterpret_cast<const uint32_t*>(&s_vt[32 * db + r32][0]) + kb / 2;   // 4-byte aligned
+      o[db] = mfma32x16_f16(u32x4{vrow[0], vrow[1], vrow[4], vrow[5]}, pb, o[db]);
     }
   }
-  float p[NQ], inv_l[NQ];
+  if (r32 >= len) return;
+  const float inv_l = 1.0f / l;                              // key 0 is always visible: l >= 1
+  const size_t orow = (size_t(t0 + r32) * Hq + hq) * D;
 #pragma unroll
-  for (int qi = 0; qi < NQ; ++qi) {
-    const int i = wave + kSmallWaves * qi;
-    const bool ok = causal ? lane <= i : lane < n_keys;      // lane 0 always: the max is finite
-    const float x = ok ? acc[qi] * scale_log2 : -INFINITY;
-    const float mx = wave_max_dpp(x);
-    p[qi] = ok ? exp2f(x - mx) : 0.f;
-    inv_l[qi] = 1.0f / wave_sum_dpp(p[qi]);
-  }
-
-  // o = P V: lane l owns dims 2l, 2l + 1
-  const int dl = lane < HALF ? lane : HALF - 1;
-  float o0[NQ], o1[NQ];
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-  for (int qi = 0; qi < NQ; ++qi) o0[qi] = o1[qi] = 0.f;
-  const int j_end = causal ? min(len, wave + kSmallWaves * (NQ - 1) + 1) : n_keys;
-#pragma unroll 4
-  for (int j = 0; j < j_end; ++j) {
-    const uint32_t vv = *reinterpret_cast<const uint32_t*>(&s_v[j][2 * dl]);
-    const float v0 = bf_lo(vv), v1 = bf_hi(vv);
-#pragma unroll
-    for (int qi = 0; qi < NQ; ++qi) {
-      const float pj = lane_f(p[qi], j);
-      o0[qi] += pj * v0;
-      o1[qi] += pj * v1;
-    }
-  }
-  if (lane < HALF) {
-#pragma unroll
-    for (int qi = 0; qi < NQ; ++qi) {
-      const int i = wave + kSmallWaves * qi;
-      if (i < len) {
-        const float y0 = o0[qi] * inv_l[qi], y1 = o1[qi] * inv_l[qi];
-        const size_t orow = (size_t(t0 + i) * Hq + hq) * D + 2 * lane;
-        if (out_fp8)
-          *reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(out) + orow) =
-              uint16_t(f2e4m3(y0 * out_inv) | (f2e4m3(y1 * out_inv) << 8));
-        else
-          *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + orow) = pack_f16x2(y0, y1);
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = 32 * db + 8 * rg + 4 * half;
+      const float y0 = o[db][4 * rg] * inv_l, y1 = o[db][4 * rg + 1] * inv_l;
+      const float y2 = o[db][4 * rg + 2] * inv_l, y3 = o[db][4 * rg + 3] * inv_l;
+      if (out_fp8) {
+        *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(out) + orow + d0) =
+            f2e4m3(y0 * out_inv) | (f2e4m3(y1 * out_inv) << 8) | (f2e4m3(y2 * out_inv) << 16) |
+            (f2e4m3(y3 * out_inv) << 24);
+      } else {
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow + d0) =
+            u32x2{pack_f16x2(y0, y1), pack_f16x2(y2, y3)};
       }
     }
-  }
 }
 
 void launch_rope_attn_small(const void* qkv, int n_seq, int max_len, int Hq, int Hkv, int d, float theta, float eps,
                             const int32_t* cu, const int32_t* cache_slot, const int32_t* used_keys, bool causal,
                             const void* qw, const void* kw, void* kc, void* vc, int capacity, void* out, bool fp8,
                             float out_inv, hipStream_t st) {
+  (void)max_len;
   const RopeFreq freq = rope_freq(d, theta);
   const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf(float(d));
   const dim3 grid(Hq, n_seq);
@@ -379,17 +390,8 @@ void launch_rope_attn_small(const void* qkv, int n_seq, int max_len, int Hq, int
         static_cast<const uint16_t*>(qw), static_cast<const uint16_t*>(kw), static_cast<uint16_t*>(kc),
         static_cast<uint16_t*>(vc), capacity, scale_log2, out, fp8 ? 1 : 0, out_inv);
   };
-  // queries per wave: the longest sequence's rows over the 8 waves
-  const int nq = (max_len + kSmallWaves - 1) / kSmallWaves;
-  if (d == 128) {
-    if (nq <= 1) go(rope_attn_small_kernel<128, 1>);
-    else if (nq == 2) go(rope_attn_small_kernel<128, 2>);
-    else go(rope_attn_small_kernel<128, 4>);
-  } else {
-    if (nq <= 1) go(rope_attn_small_kernel<64, 1>);
-    else if (nq == 2) go(rope_attn_small_kernel<64, 2>);
-    else go(rope_attn_small_kernel<64, 4>);
-  }
+  if (d == 128) go(rope_attn_small_kernel<128>);
+  else go(rope_attn_small_kernel<64>);
 }
 
 }  // namespace hr
