@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
 // MXFP4 of x * col (OCP MX blocks of 32, the 4 threads of a block adjacent
 // lanes), or nothing (the last layer's residual).  ks = 0: the plain RMSNorm
 // of h.  One row per workgroup, 8 values per thread, 128-bit accesses.
-template <int OUT, int CPT>
+template <int OUT, int CPT, int KB>
 __global__ __launch_bounds__(kNormThreads) void residual_norm_kernel(
     float* __restrict__ h, const float* __restrict__ part, int ks, size_t part_stride, int D,
     const uint16_t* __restrict__ w, float eps, void* __restrict__ x_out, float inv_scale,
@@ -141,7 +141,6 @@ __global__ __launch_bounds__(kNormThreads) void residual_norm_kernel(
   // h and every partial of the thread's chunks are requested before any sum
   // (KB partials per batch): the loads overlap instead of one memory round
   // trip per partial and chunk.  The sums keep the split order, h + (p0 + p1 + ...).
-  constexpr int KB = 4;
   floatx4 ha[CPT], hb[CPT], sa[CPT], sb[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
@@ -152,7 +151,9 @@ __global__ __launch_bounds__(kNormThreads) void residual_norm_kernel(
       hb[c] = hp[1];
     }
   }
-  for (int kz0 = 0; kz0 < ks; kz0 += KB) {
+  // KB = 6 is launched for ks <= 6 only: a single batch
+  const int kz_end = KB == 6 ? min(ks, 1) : ks;
+  for (int kz0 = 0; kz0 < kz_end; kz0 += KB) {
     floatx4 qa[KB][CPT], qb[KB][CPT];
 #pragma unroll
     for (int u = 0; u < KB; ++u)
@@ -295,12 +296,16 @@ void launch_residual_norm(float* h, const float* part, int ks, int T, int D, con
   auto go = [&](auto kern) {
     kern<<<T, kNormThreads, 0, st>>>(h, part, ks, stride, D, w16, eps, x_out, inv_scale, col, mx_scales, mx_ld);
   };
-#define HR_NORM_CPT(MODE)                                      \
-  switch (cpt) {                                               \
-    case 1: go(residual_norm_kernel<MODE, 1>); break;          \
-    case 2: go(residual_norm_kernel<MODE, 2>); break;          \
-    case 3: go(residual_norm_kernel<MODE, 3>); break;          \
-    default: go(residual_norm_kernel<MODE, 4>);                \
+  // partials per load batch: 4, or 6 for the five splits of the small-batch
+  // residual projections at 2 chunks per thread (hidden sizes 2049-4096: one
+  // round trip instead of two; the larger batch costs registers, so only there)
+  const bool kb6 = cpt == 2 && ks > 4 && ks <= 6;
+#define HR_NORM_CPT(MODE)                                                                   \
+  switch (cpt) {                                                                            \
+    case 1: go(residual_norm_kernel<MODE, 1, 4>); break;                                    \
+    case 2: kb6 ? go(residual_norm_kernel<MODE, 2, 6>) : go(residual_norm_kernel<MODE, 2, 4>); break; \
+    case 3: go(residual_norm_kernel<MODE, 3, 4>); break;                                    \
+    default: go(residual_norm_kernel<MODE, 4, 4>);                                          \
   }
   switch (out_mode) {
     case kNormNone: HR_NORM_CPT(kNormNone); break;
