@@ -167,6 +167,8 @@ struct Ws {
   float *part_o, *part_ml;   // key-chunk partials of the split attention (null: no split)
   uint8_t *mx_s1, *mx_s2;    // MXFP4 block scales: O / gate-up input, down input (ld mx_ld)
   int mx_ld;                 // rows of the scale layouts: T rounded up to the 256-row tile
+  uint8_t *k16, *v16;        // fp16 copies of the batch's K and V rows [Tp][Hkv][d] (null: none)
+  int Tp;                    // their rows: T rounded up to 32
 };
 
 // Batches of up to kAttnSplitT rows may split long attention rows into key
@@ -240,6 +242,14 @@ size_t ws_layout(const hr_dims* d, int32_t T, Ws* w, uint8_t* base) {
     const size_t rows = part_rows(t);
     tmp.part_o = reinterpret_cast<float*>(take(rows * A * 4));
     tmp.part_ml = reinterpret_cast<float*>(take(rows * d->n_q_heads * 8));
+  }
+  tmp.k16 = tmp.v16 = nullptr;
+  tmp.Tp = 0;
+  if (hr::qkv_rope_fits(T, d->head_dim)) {
+    tmp.Tp = (T + 31) / 32 * 32;
+    const size_t bytes = size_t(tmp.Tp) * d->n_kv_heads * d->head_dim * 2;
+    tmp.k16 = take(bytes);
+    tmp.v16 = take(bytes);
   }
   if (w) *w = tmp;
   return off;
@@ -362,6 +372,16 @@ bool qkv_rope_fused(const hr_dims* d, const hr_batch* b) {
   return hr::qkv_rope_fits(b->total_tokens, d->head_dim);
 }
 
+// Attention from the fp16 K / V copies that the fused QKV + step A3 launch
+// writes (hr::launch_attention_f16): every sequence starts at position 0 (its
+// keys are its own rows) and at a row that is a multiple of 8.
+bool attn_f16(const hr_batch* b, const Ws& w, bool fused_qkv) {
+  if (!fused_qkv || !w.k16) return false;
+  for (int s = 0; s < b->n_seq; ++s)
+    if (b->h_start_pos[s] != 0 || b->h_cu_seqlens[s] % 8 != 0) return false;
+  return true;
+}
+
 // Input norm of a layer in its format: fp16 for the bf16 and MXFP4 bands
 // (their QKV GEMM takes fp16 activations), e4m3 with the layer's QKV scale.
 void in_norm_mode(const hr_layer* L, int* mode, float* inv) {
@@ -388,9 +408,16 @@ hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_layer* next, c
     hr::launch_residual_norm(h, nullptr, 0, T, D, L->in_norm_w, eps, mode, w.x, inv, nullptr, nullptr, 0, st);
   }
   const bool fused_qkv = qkv_rope_fused(d, b);
+  const bool f16_attn = attn_f16(b, w, fused_qkv);
   if (fused_qkv) {
-    const hr::QkvRope qr{w.q, kv->k, kv->v, b->cu_seqlens, b->start_pos, b->cache_slot, b->used_keys, b->n_seq,
-                         d->causal, kv->capacity, Hq, Hkv, dh, L->q_norm_w, L->k_norm_w, eps, w.rope};
+    hr::QkvRope qr{w.q, kv->k, kv->v, b->cu_seqlens, b->start_pos, b->cache_slot, b->used_keys, b->n_seq,
+                   d->causal, kv->capacity, Hq, Hkv, dh, L->q_norm_w, L->k_norm_w, eps, w.rope,
+                   nullptr, nullptr, 0};
+    if (f16_attn) {
+      qr.k16 = w.k16;
+      qr.v16 = w.v16;
+      qr.Tp = w.Tp;
+    }
     hr::launch_qkv_rope(w.x, L->w_qkv, L->ws_qkv, L->as_qkv, fp8, pk, T, D, qr, st);
   } else {
     hr::launch_linear(w.x, L->w_qkv, L->ws_qkv, L->as_qkv, fp8, pk, T, NQKV, D, HR_EPI_F32, w.qkv, 0.f, nullptr,
@@ -409,9 +436,13 @@ hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_layer* next, c
       hr::launch_qknorm_rope_kv(w.qkv, T, Hq, Hkv, dh, d->rope_theta, eps, b->cu_seqlens, b->start_pos,
                                 b->cache_slot, b->used_keys, b->n_seq, d->causal != 0, L->q_norm_w, L->k_norm_w,
                                 w.q, kv->k, kv->v, kv->capacity, st);
-    hr::launch_attention(w.q, kv->k, kv->v, b->cu_seqlens, b->start_pos, b->cache_slot, b->used_keys, b->n_seq,
-                         b->max_seqlen, Hq, Hkv, dh, kv->capacity, d->causal != 0, w.attn, fp8,
-                         fp8 ? 1.0f / L->as_o : 1.f, st, &split);
+    if (f16_attn)
+      hr::launch_attention_f16(w.q, w.k16, w.v16, w.Tp, b->cu_seqlens, b->used_keys, b->n_seq, b->max_seqlen, Hq,
+                               Hkv, dh, d->causal != 0, w.attn, fp8, fp8 ? 1.0f / L->as_o : 1.f, st);
+    else
+      hr::launch_attention(w.q, kv->k, kv->v, b->cu_seqlens, b->start_pos, b->cache_slot, b->used_keys, b->n_seq,
+                           b->max_seqlen, Hq, Hkv, dh, kv->capacity, d->causal != 0, w.attn, fp8,
+                           fp8 ? 1.0f / L->as_o : 1.f, st, &split);
   }
   // after the down projection: the residual completed, fused with the next
   // layer's input norm (or alone after the last layer)
@@ -1002,6 +1033,35 @@ hr_status hr_attention(const hr_dims* dims, const hr_batch* batch, const void* q
                        kv->capacity, dims->causal != 0, out, out_type == HR_FP8_E4M3,
                        out_type == HR_FP8_E4M3 ? 1.0f / out_scale : 1.f, stream, &plan);
   return check_launch("attention");
+}
+
+hr_status hr_attention_f16(const hr_dims* dims, const hr_batch* batch, const void* q, const void* k16,
+                           const void* v16, int32_t Tp, void* out, hr_wtype out_type, float out_scale,
+                           hipStream_t stream) {
+  HR_TRY(check_dims(dims));
+  hr_kv unbounded{nullptr, nullptr, INT32_MAX, INT32_MAX};   // no cache: slots and capacity unchecked
+  HR_TRY(check_batch(dims, batch, &unbounded));
+  HR_TRY(need(q, "q"));
+  HR_TRY(need(k16, "k16"));
+  HR_TRY(need(v16, "v16"));
+  HR_TRY(need(out, "out"));
+  if (out_type != HR_F16 && out_type != HR_FP8_E4M3) return fail(HR_EINVAL, "out_type: HR_F16 or HR_FP8_E4M3");
+  if (out_type == HR_FP8_E4M3 && !(out_scale > 0.f)) return fail(HR_EINVAL, "out_scale must be > 0");
+  const int T = batch->total_tokens;
+  if (Tp % 32 != 0 || Tp < (T + 31) / 32 * 32)
+    return fail(HR_EINVAL, "Tp = %d: a multiple of 32 of at least %d", Tp, (T + 31) / 32 * 32);
+  for (int s = 0; s < batch->n_seq; ++s) {
+    if (batch->h_start_pos[s] != 0)
+      return fail(HR_EUNSUPPORTED, "start_pos[%d] = %d: every sequence must start at position 0", s,
+                  batch->h_start_pos[s]);
+    if (batch->h_cu_seqlens[s] % 8 != 0)
+      return fail(HR_EUNSUPPORTED, "cu_seqlens[%d] = %d is not a multiple of 8", s, batch->h_cu_seqlens[s]);
+  }
+  if (T == 0) return HR_OK;
+  hr::launch_attention_f16(q, k16, v16, Tp, batch->cu_seqlens, batch->used_keys, batch->n_seq, batch->max_seqlen,
+                           dims->n_q_heads, dims->n_kv_heads, dims->head_dim, dims->causal != 0, out,
+                           out_type == HR_FP8_E4M3, out_type == HR_FP8_E4M3 ? 1.0f / out_scale : 1.f, stream);
+  return check_launch("attention_f16");
 }
 
 hr_status hr_qknorm_rope_attention(const hr_dims* dims, const hr_batch* batch, const void* qkv,

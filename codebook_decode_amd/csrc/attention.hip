@@ -38,6 +38,13 @@ __device__ __forceinline__ floatx16 mfma32_f16(u32x4 a, u32x4 b, floatx16 c) {
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// wait until at most N of this thread's vector-memory loads are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm_f16() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // Key chunks of a query block with n_tiles 64-key tiles: at least chunk_tiles
 // tiles per chunk, and no more chunks than n_slots (longer rows take longer
 // chunks).  chunk_tiles == 0: one chunk.
@@ -418,6 +425,284 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(
   }
 }
 
+// ============================================================ attention over fp16 copies
+// A batch whose keys are all its own rows (every sequence from position 0)
+// and whose QKV launch also wrote fp16 copies of its K and V rows
+// ([Tp][Hkv][d]): the tiles need no conversion, so they go HBM -> LDS by
+// global_load_lds (no register round trip) and every wave can stage its own.
+// That lets the work be balanced: a workgroup takes one query head and the
+// query blocks p and nb-1-p of a sequence (32 rows each; causal: the longest
+// and shortest rows together), and its 4 waves split the two blocks' 32-key
+// tiles, each wave a contiguous run of one block's tiles (waves in proportion
+// to the blocks' tiles, at least one each).  Per tile and wave, as in
+// attention_kernel: S^T = K Q^T with v_mfma_f32_32x32x16_f16 (lane: query
+// l % 32, keys 8(r/4) + 4(l/32) + r%4), the online softmax in base 2
+// (reference max moved only when exceeded by more than 8), O^T += V^T P^T with
+// the lane's own fp16 probabilities as the B operand; the V^T fragment (4
+// consecutive keys of one d per read) comes from the row-major V tile through
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane i = 4e + q supplies the
+// address of 4 elements of row e, and lane 4q + c receives element c of rows
+// 0..3 -- so lane i points at key K0 + i/4, dims 4(i%4)..+3 of its 16-dim
+// group.  Each wave double-buffers its tiles in its own LDS (2 x 2 x 8 KB at
+// d 128), the copies swizzled on the global side so the fragment reads hit
+// distinct banks (k rows of 16 chunks: chunk c of row r at c ^ (r % 16), of 8:
+// c ^ ((r / 2) % 8); v rows: c ^ 4 (r % 4), of 8 chunks c ^ 4 ((r / 2) % 2)).
+// At the end the waves of a block merge their (max, sum, output) through LDS
+// in wave order.  Rows past the copies' last row read that row (finite; their
+// scores are masked).
+constexpr int kF16Waves = 4;
+constexpr int kF16KT = 32;                   // keys per tile
+
+template <int DH>
+constexpr size_t attention_f16_lds() { return size_t(kF16Waves) * 2 * 2 * kF16KT * DH * 2; }
+
+// max of a lane's value and lane l ^ 32's (v_permlane32_swap: one VALU, no LDS)
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+}
+
+template <int DH>
+__global__ __launch_bounds__(64 * kF16Waves) void attention_f16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k16, const uint16_t* __restrict__ v16, int Tp,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ used_keys, int Hq, int Hkv, int causal,
+    float scale_log2, void* __restrict__ out, int out_fp8, float out_inv) {
+  constexpr int KT = kF16KT;
+  constexpr int NKS = DH / 16, NDB = DH / 32;
+  constexpr int KCH = DH / 8;                // 16-byte chunks of a k row
+  constexpr int TB = KT * DH * 2;            // bytes of a k tile (and of a v^T tile)
+  constexpr int NCP = TB / 1024;             // 1-KB wave copies per tile
+  constexpr int STAGE = 2 * TB;
+  static_assert(TB % 1024 == 0, "whole wave copies");
+  extern __shared__ __attribute__((aligned(16))) uint8_t f16_smem[];
+
+  const int s = blockIdx.z, hh = blockIdx.y, p = blockIdx.x;
+  const int g = hh / (Hq / Hkv);
+  const int tok0 = cu[s], len = cu[s + 1] - tok0;
+  const int nb = (len + 31) / 32;
+  const int b_long = nb - 1 - p;
+  if (p > b_long) return;                    // whole workgroup, before any barrier
+  const bool single = p == b_long;
+  const int used = causal ? 0 : used_keys[s];
+  const int nk_l = causal ? min(32 * b_long + 31, len - 1) + 1 : used;
+  const int nk_s = single ? 0 : (causal ? 32 * p + 32 : used);
+  const int t_l = (nk_l + KT - 1) / KT, t_s = (nk_s + KT - 1) / KT;
+  int w_l = kF16Waves;
+  if (!single) w_l = max(1, min(kF16Waves - 1, (kF16Waves * t_l + (t_l + t_s) / 2) / (t_l + t_s)));
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  const bool on_long = wave < w_l;
+  const int blk = on_long ? b_long : p;
+  const int nw = on_long ? w_l : kF16Waves - w_l;
+  const int wj = on_long ? wave : wave - w_l;          // the wave's place among its block's
+  const int n_tiles = on_long ? t_l : t_s;
+  const int n_keys = on_long ? nk_l : nk_s;
+  const int ct = (n_tiles + nw - 1) / nw;
+  const int kt0 = min(n_tiles, wj * ct), kt1 = min(n_tiles, kt0 + ct);
+
+  const int half = lane >> 5, r32 = lane & 31;
+  const int i0 = 32 * blk;
+  const int iq = i0 + r32;                   // this lane's query (sequence-relative)
+  const bool qok = iq < len;
+  u32x4 qf[NKS];
+  {
+    const uint16_t* qrow = q + (size_t(tok0 + (qok ? iq : 0)) * Hq + hh) * DH;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qrow + ks * 16 + half * 8);
+  }
+
+  uint8_t* wl = f16_smem + size_t(wave) * 2 * STAGE;
+  const uint8_t* kb = reinterpret_cast<const uint8_t*>(k16) + (size_t(tok0) * Hkv + g) * DH * 2;
+  const size_t krow = size_t(Hkv) * DH * 2;                      // bytes from one key row to the next
+  const uint8_t* vb = reinterpret_cast<const uint8_t*>(v16) + (size_t(tok0) * Hkv + g) * DH * 2;
+  const int key_last = Tp - tok0 - 1;                          // last row of the copies (relative)
+  // chunk swizzles of a k row and of a v row (see above)
+  auto kswz_of = [](int r) { return KCH == 16 ? (r & 15) : ((r >> 1) & 7); };
+  auto vswz_of = [](int r) { return KCH == 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
+  // a thread's copy i of a tile is its copy i of tile 0 moved by a uniform
+  // step (KT rows of k, KT columns of v^T): a uniform base plus one byte
+  // offset per copy, no per-tile address arithmetic
+  uint32_t koff[NCP], voff[NCP];
+#pragma unroll
+  for (int i = 0; i < NCP; ++i) {
+    const int sl = 64 * i + lane, r = sl / KCH;
+    koff[i] = uint32_t(r) * uint32_t(krow) + uint32_t((sl % KCH) ^ kswz_of(r)) * 16;
+    voff[i] = uint32_t(r) * uint32_t(krow) + uint32_t((sl % KCH) ^ vswz_of(r)) * 16;
+  }
+  auto fetch = [&](int kt, int stg) {
+    uint8_t* dk = wl + stg * STAGE;
+    uint8_t* dv = dk + TB;
+    if (kt * KT + KT - 1 <= key_last) {      // uniform: the whole tile inside the copies
+      const uint8_t* kt_base = kb + size_t(kt) * KT * krow;
+      const uint8_t* vt_base = vb + size_t(kt) * KT * krow;
+#pragma unroll
+      for (int i = 0; i < NCP; ++i) lds_dma16(kt_base + koff[i], dk + i * 1024);
+#pragma unroll
+      for (int i = 0; i < NCP; ++i) lds_dma16(vt_base + voff[i], dv + i * 1024);
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < NCP; ++i) {
+      const int sl = 64 * i + lane, r = sl / KCH;
+      const size_t row = size_t(min(kt * KT + r, key_last)) * krow;
+      lds_dma16(kb + row + ((sl % KCH) ^ kswz_of(r)) * 16, dk + i * 1024);
+      lds_dma16(vb + row + ((sl % KCH) ^ vswz_of(r)) * 16, dv + i * 1024);
+    }
+  };
+
+  floatx16 o[NDB];
+#pragma unroll
+  for (int j = 0; j < NDB; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[j][r] = 0.f;
+  float m_run = -__builtin_inff();
+  float l_part = 0.f;
+  const int kswz = kswz_of(r32);
+  // the lane's transposed-read address in a v tile, relative to key 16 kk +
+  // 8 x and dim block db: row 4 (lane / 32) + (lane % 16) / 4, dims
+  // 16 ((lane / 16) % 2) + 4 (lane % 4) .. + 3 (a half chunk)
+  const int tr_row = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  if (kt0 < kt1) fetch(kt0, 0);
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int stg = (kt - kt0) & 1;
+    asm volatile("" ::: "memory");
+    if (kt + 1 < kt1) {
+      fetch(kt + 1, stg ^ 1);                // the other stage: read by the previous tile, done
+      wait_vm_f16<2 * NCP>();                // this tile's copies (and q) landed
+    } else {
+      wait_vm_f16<0>();
+    }
+    asm volatile("" ::: "memory");
+    const uint8_t* sk = wl + stg * STAGE;
+    const uint8_t* sv = sk + TB;
+    const int k0 = kt * KT;
+    // every fragment of the tile requested at once: the k reads ahead of the
+    // score MFMAs, the v^T reads behind the softmax
+    u32x4 kf[NKS];
+    u32x2 vf[2][NDB][2];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      kf[ks] = *reinterpret_cast<const u32x4*>(sk + (r32 * KCH + ((2 * ks + half) ^ kswz)) * 16);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int r = 16 * kk + 8 * x + tr_row, vs = vswz_of(r);   // r % 4 = tr_row % 4: vs per lane
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int dd = 32 * db + tr_dim;
+          const uint8_t* a = sv + r * (DH * 2) + (((dd >> 3) ^ vs) << 4) + (dd & 7) * 2;
+          vf[kk][db][x] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)(a)));
+        }
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    floatx16 sc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) sc = mfma32_f16(kf[ks], qf[ks], sc);
+    const bool need_mask = causal ? (k0 + KT - 1 > i0) : (k0 + KT > n_keys);
+    if (need_mask) {
+      const int j_max = causal ? iq : n_keys - 1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (j > j_max) sc[r] = -__builtin_inff();
+      }
+    }
+    float mt = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[r]);
+    mt = max_xor32(mt) * scale_log2;         // scale > 0: max commutes
+    const bool grow = mt > m_run + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;   // 0 from -inf
+      if (grow) m_run = mt;
+      l_part *= alpha;
+#pragma unroll
+      for (int j = 0; j < NDB; ++j) o[j] *= alpha;
+    }
+    const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], scale_log2, -m_use));
+      sc[r] = pr;
+      psum += pr;
+    }
+    l_part += psum;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 pb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pb[e] = pack_f16x2(sc[8 * kk + 2 * e], sc[8 * kk + 2 * e + 1]);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        o[db] = mfma32_f16(u32x4{vf[kk][db][0][0], vf[kk][db][0][1], vf[kk][db][1][0], vf[kk][db][1][1]}, pb, o[db]);
+    }
+  }
+
+  // merge the block's waves (fixed order) through the now idle LDS
+  constexpr int kVals = 2 + 16 * NDB;
+  static_assert(size_t(kF16Waves) * 64 * kVals * 4 <= attention_f16_lds<DH>(), "merge buffer");
+  float* xch = reinterpret_cast<float*>(f16_smem);
+  wait_vm_f16<0>();
+  __syncthreads();                           // every wave is done with its tiles
+  {
+    float* my = xch + (size_t(wave) * 64 + lane) * kVals;
+    my[0] = m_run;
+    my[1] = l_part;
+#pragma unroll
+    for (int j = 0; j < NDB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) my[2 + 16 * j + r] = o[j][r];
+  }
+  __syncthreads();
+  if (wj != 0) return;
+  for (int w2 = 1; w2 < nw; ++w2) {
+    const float* ot = xch + (size_t(wave + w2) * 64 + lane) * kVals;
+    const float m2 = ot[0];
+    const float mm = fmaxf(m_run, m2);
+    const float a1 = (m_run == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
+    const float a2 = (m2 == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(m2 - mm);
+    l_part = l_part * a1 + ot[1] * a2;
+#pragma unroll
+    for (int j = 0; j < NDB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[j][r] = o[j][r] * a1 + ot[2 + 16 * j + r] * a2;
+    m_run = mm;
+  }
+  const float l = l_part + __shfl_xor(l_part, 32, kWave);
+  if (!qok) return;
+  const float inv_l = l > 0.f ? 1.0f / l : 0.f;
+  const size_t orow = (size_t(tok0 + iq) * Hq + hh) * DH;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = db * 32 + 8 * rg + 4 * half;
+      const float y0 = o[db][4 * rg] * inv_l, y1 = o[db][4 * rg + 1] * inv_l;
+      const float y2 = o[db][4 * rg + 2] * inv_l, y3 = o[db][4 * rg + 3] * inv_l;
+      if (out_fp8) {
+        const uint32_t w = f2e4m3(y0 * out_inv) | (f2e4m3(y1 * out_inv) << 8) |
+                           (f2e4m3(y2 * out_inv) << 16) | (f2e4m3(y3 * out_inv) << 24);
+        *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(out) + orow + d0) = w;
+      } else {
+        const u32x2 w = {pack_f16x2(y0, y1), pack_f16x2(y2, y3)};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow + d0) = w;
+      }
+    }
+}
+
 // ============================================================ decode attention
 // One query row per sequence (a decode step).  Workgroup = (key chunk, kv
 // head, sequence), 4 waves.  The chunk's keys are dealt KPW to a wave
@@ -699,6 +984,36 @@ static void launch_attn_t(const void* q, const void* kc, const void* vc, const i
 }
 
 int attention_qpw(int Hq, int Hkv) { return 32 * (4 / (Hq / Hkv)); }
+
+template <int DH>
+static void attention_f16_go(const dim3& grid, const void* q, const void* k16, const void* v16, int Tp,
+                             const int32_t* cu, const int32_t* used, int Hq, int Hkv, bool causal, float scale_log2,
+                             void* out, bool fp8, float out_inv, hipStream_t st) {
+  constexpr size_t kLds = attention_f16_lds<DH>();
+  auto kern = attention_f16_kernel<DH>;
+  if (kLds > 65536) {
+    // above the 64 KB default dynamic-LDS limit: raised once (a thread-safe
+    // static); a refusal surfaces as the launch's error
+    static const hipError_t raised = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(kLds));
+    (void)raised;
+  }
+  kern<<<grid, 64 * kF16Waves, kLds, st>>>(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k16),
+                                           static_cast<const uint16_t*>(v16), Tp, cu, used, Hq, Hkv, causal ? 1 : 0,
+                                           scale_log2, out, fp8 ? 1 : 0, out_inv);
+}
+
+void launch_attention_f16(const void* q, const void* k16, const void* v16, int Tp, const int32_t* cu,
+                          const int32_t* used, int n_seq, int max_len, int Hq, int Hkv, int d, bool causal,
+                          void* out, bool fp8, float out_inv, hipStream_t st) {
+  const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf(float(d));
+  const int nb = (max_len + 31) / 32;
+  const dim3 grid((nb + 1) / 2, Hq, n_seq);
+  if (d == 128)
+    attention_f16_go<128>(grid, q, k16, v16, Tp, cu, used, Hq, Hkv, causal, scale_log2, out, fp8, out_inv, st);
+  else
+    attention_f16_go<64>(grid, q, k16, v16, Tp, cu, used, Hq, Hkv, causal, scale_log2, out, fp8, out_inv, st);
+}
 
 void launch_decode_rope_attention(const void* qkv, const void* qw, const void* kw, float theta, float eps,
                                   void* kc, void* vc, const int32_t* cu, const int32_t* sp, const int32_t* slot,

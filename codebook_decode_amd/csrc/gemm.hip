@@ -717,19 +717,55 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(
       const long long crow = (long long)q.cache_slot[sq] * q.capacity + q.start_pos[sq] + ti;
       if (hidx < q.Hq + q.Hkv) {
         const bool is_q = hidx < q.Hq;
-        if (!is_q && !wkv) continue;
+        if (!is_q && !wkv && !q.k16) continue;
         const float inv = 1.0f / __builtin_sqrtf(ss / float(d) + q.eps);
         const float* cs = q.rope + size_t(t) * d + 8 * c;
         F8 o0, o1;
         rope_pairs(lo, up, is_q ? wq0 : wk0, is_q ? wq1 : wk1, inv, cs, cs + half, o0, o1);
-        uint16_t* dst = is_q ? static_cast<uint16_t*>(q.q_out) + (size_t(t) * q.Hq + hidx) * d
-                             : static_cast<uint16_t*>(q.kc) + (size_t(crow) * q.Hkv + (hidx - q.Hq)) * d;
-        *reinterpret_cast<u32x4*>(dst + 8 * c) = is_q ? pack8_f16(o0) : pack8_bf16(o0);
-        *reinterpret_cast<u32x4*>(dst + half + 8 * c) = is_q ? pack8_f16(o1) : pack8_bf16(o1);
-      } else if (wkv) {
-        uint16_t* dst = static_cast<uint16_t*>(q.vc) + (size_t(crow) * q.Hkv + (hidx - q.Hq - q.Hkv)) * d;
-        *reinterpret_cast<u32x4*>(dst + 8 * c) = pack8_bf16(lo);
-        *reinterpret_cast<u32x4*>(dst + half + 8 * c) = pack8_bf16(up);
+        if (is_q) {
+          uint16_t* dst = static_cast<uint16_t*>(q.q_out) + (size_t(t) * q.Hq + hidx) * d;
+          *reinterpret_cast<u32x4*>(dst + 8 * c) = pack8_f16(o0);
+          *reinterpret_cast<u32x4*>(dst + half + 8 * c) = pack8_f16(o1);
+        } else {
+          const u32x4 b0 = pack8_bf16(o0), b1 = pack8_bf16(o1);
+          if (wkv) {
+            uint16_t* dst = static_cast<uint16_t*>(q.kc) + (size_t(crow) * q.Hkv + (hidx - q.Hq)) * d;
+            *reinterpret_cast<u32x4*>(dst + 8 * c) = b0;
+            *reinterpret_cast<u32x4*>(dst + half + 8 * c) = b1;
+          }
+          if (q.k16) {   // the fp16 copy: the cache's bf16 values widened (exact)
+            uint16_t* dst = static_cast<uint16_t*>(q.k16) + (size_t(t) * q.Hkv + (hidx - q.Hq)) * d;
+            *reinterpret_cast<u32x4*>(dst + 8 * c) = bf8_to_f16x8(b0);
+            *reinterpret_cast<u32x4*>(dst + half + 8 * c) = bf8_to_f16x8(b1);
+          }
+        }
+      } else {
+        const u32x4 b0 = pack8_bf16(lo), b1 = pack8_bf16(up);
+        if (wkv) {
+          uint16_t* dst = static_cast<uint16_t*>(q.vc) + (size_t(crow) * q.Hkv + (hidx - q.Hq - q.Hkv)) * d;
+          *reinterpret_cast<u32x4*>(dst + 8 * c) = b0;
+          *reinterpret_cast<u32x4*>(dst + half + 8 * c) = b1;
+        }
+        if (q.k16) {   // the fp16 copy: the cache's bf16 values widened (exact)
+          uint16_t* dst = static_cast<uint16_t*>(q.v16) + (size_t(t) * q.Hkv + (hidx - q.Hq - q.Hkv)) * d;
+          *reinterpret_cast<u32x4*>(dst + 8 * c) = bf8_to_f16x8(b0);
+          *reinterpret_cast<u32x4*>(dst + half + 8 * c) = bf8_to_f16x8(b1);
+        }
+      }
+    }
+    if (q.k16) {
+      // rows T..Tp-1 of the fp16 copies: zero
+      for (int hi = 0; hi < heads; ++hi) {
+        const int hidx = (n0 + hi * d) / d;
+        if (hidx < q.Hq) continue;
+        const bool is_v = hidx >= q.Hq + q.Hkv;
+        uint16_t* cp = static_cast<uint16_t*>(is_v ? q.v16 : q.k16);
+        const int g = hidx - q.Hq - (is_v ? q.Hkv : 0);
+        for (int it = tid; it < BM * (d / 8); it += C::kThreads) {
+          const int t = m0 + it / (d / 8), c8 = it % (d / 8);
+          if (t < M || t >= q.Tp) continue;
+          *reinterpret_cast<u32x4*>(cp + (size_t(t) * q.Hkv + g) * d + 8 * c8) = u32x4{0u, 0u, 0u, 0u};
+        }
       }
     }
     return;

@@ -83,6 +83,13 @@ void launch_attention(const void* q, const void* kc, const void* vc, const int32
                       int max_len, int Hq, int Hkv, int d, int cap, bool causal, void* out, bool fp8,
                       float out_inv, hipStream_t st, const AttnSplit* split = nullptr);
 
+// Attention of a batch whose keys are all its own rows (every sequence starts
+// at position 0) from the fp16 copies the QKV + step A3 launch wrote (QkvRope
+// k16 / v16, Tp rows): grid (query-block pairs, Hq, n_seq), d 64 or 128.
+void launch_attention_f16(const void* q, const void* k16, const void* v16, int Tp, const int32_t* cu,
+                          const int32_t* used, int n_seq, int max_len, int Hq, int Hkv, int d, bool causal,
+                          void* out, bool fp8, float out_inv, hipStream_t st);
+
 // Decode steps (one row per sequence, causal): step A3 (q/k norm, RoPE, the new
 // row's K/V write) inside the decode attention launch; qkv = the merged QKV rows.
 void launch_decode_rope_attention(const void* qkv, const void* qw, const void* kw, float theta, float eps,
@@ -117,6 +124,12 @@ struct QkvRope {
   const void* kw;
   float eps;
   const float* rope;   // [T][d]: cos of pairs m < d/2, then their sin
+  // optional fp16 copies of this batch's keys and values for attention_f16
+  // (null: none): k16 and v16 [Tp][Hkv][d], the cache's rows widened to fp16
+  // (exact); rows T..Tp-1 zero (Tp = T rounded up to 32)
+  void* k16;
+  void* v16;
+  int Tp;
 };
 bool qkv_rope_fits(int M, int d);
 bool launch_qkv_rope(const void* x, const void* w, const float* w_scale, float x_scale, bool fp8, bool packed,

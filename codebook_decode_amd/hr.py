@@ -111,6 +111,7 @@ def lib() -> ctypes.CDLL:
             "hr_residual_rmsnorm": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_f32, c_vp, c_i32, c_f32, c_vp]),
             "hr_qknorm_rope_kv": (c_i32, [P(HrDims), P(HrBatch), c_vp, c_vp, c_vp, c_vp, P(HrKv), c_vp]),
             "hr_attention": (c_i32, [P(HrDims), P(HrBatch), c_vp, P(HrKv), c_vp, c_i32, c_f32, c_vp]),
+            "hr_attention_f16": (c_i32, [P(HrDims), P(HrBatch), c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_f32, c_vp]),
             "hr_qknorm_rope_attention": (c_i32, [P(HrDims), P(HrBatch), c_vp, c_vp, c_vp, P(HrKv), c_vp, c_i32,
                                                  c_f32, c_vp]),
             "hr_attention_chunked_workspace_bytes": (c_sz, [P(HrDims), c_i32, c_i32]),
@@ -363,6 +364,12 @@ def hr_qknorm_rope_kv(dims, batch: Batch, qkv, q_norm_w, k_norm_w, q_out, kv: Hr
 def hr_attention(dims, batch: Batch, q, kv: HrKv, out, out_type=HR_F16, out_scale=1.0, stream=None) -> None:
     _check(lib().hr_attention(ctypes.byref(dims), ctypes.byref(batch.c), ptr(q), ctypes.byref(kv), ptr(out),
                               out_type, out_scale, stream if stream is not None else current_stream()))
+
+
+def hr_attention_f16(dims, batch: Batch, q, k16, v16, Tp, out, out_type=HR_F16, out_scale=1.0, stream=None) -> None:
+    _check(lib().hr_attention_f16(ctypes.byref(dims), ctypes.byref(batch.c), ptr(q), ptr(k16), ptr(v16), Tp,
+                                  ptr(out), out_type, out_scale,
+                                  stream if stream is not None else current_stream()))
 
 
 def hr_qknorm_rope_attention(dims, batch: Batch, qkv, q_norm_w, k_norm_w, kv: HrKv, out, out_type=HR_F16,

@@ -105,6 +105,24 @@ hr_status hr_qknorm_rope_attention(const hr_dims* dims, const hr_batch* batch, c
 hr_status hr_attention(const hr_dims* dims, const hr_batch* batch, const void* q, const hr_kv* kv,
                        void* out, hr_wtype out_type, float out_scale, hipStream_t stream);
 
+/* The attention of hr_attention (step A4) for a batch whose keys are all its
+ * own rows -- every sequence starts at position 0 (HR_EUNSUPPORTED otherwise)
+ * -- read from fp16 copies instead of the cache: k16 and v16 [Tp][Hkv][d],
+ * row t the key / value row of batch row t; rows past the batch's T rows
+ * finite (zero); Tp a multiple of 32, at least T rounded up to 32 (HR_EINVAL).
+ * Every sequence must start at a batch row that is a multiple of 8
+ * (HR_EUNSUPPORTED).  These are the copies the layer entries' fused QKV +
+ * step A3 launch writes for 385-1024 rows (the cache's bf16 values widened to
+ * fp16, exact), and the layer entries take this path by themselves there.  The
+ * tiles go HBM -> LDS without conversion; a workgroup takes one query head and
+ * the 32-row query blocks p and nb-1-p of a sequence, its 4 waves splitting
+ * their 32-key tiles, merged in a fixed order.  q, out and the tolerances as
+ * in hr_attention; all pointers device memory, 16-byte aligned (HR_EALIGN);
+ * nothing is allocated. */
+hr_status hr_attention_f16(const hr_dims* dims, const hr_batch* batch, const void* q, const void* k16,
+                           const void* v16, int32_t Tp, void* out, hr_wtype out_type, float out_scale,
+                           hipStream_t stream);
+
 /* The same attention with each query block's keys split into chunks that run
  * in separate workgroups (more parallel work for a few long rows), followed by
  * a merge: chunk c keeps its running max m_c (base 2), sum l_c and unnormalised

@@ -304,6 +304,30 @@ def test_attention_chunked_validation(ct, slots, ws, ws_bytes, status):
 
 
 @pytest.mark.parametrize("case,status", [
+    ("ok", H.HR_OK),                            # zero rows: validated, nothing launched
+    ("continuation", H.HR_EUNSUPPORTED),        # a sequence past position 0: keys in the cache
+    ("start_row", H.HR_EUNSUPPORTED),           # a sequence starting at batch row 13 (not a multiple of 8)
+    ("tp_small", H.HR_EINVAL),                  # Tp below T rounded up to 32
+    ("tp_ragged", H.HR_EINVAL),                 # Tp not a multiple of 32
+    ("misaligned", H.HR_EALIGN),
+    ("no_copy", H.HR_EINVAL),
+    ("fp8_scale", H.HR_EINVAL),
+])
+def test_attention_f16_validation(case, status):
+    lib = H.lib()
+    d = dims()
+    lens = [0] if case == "ok" else ([13, 5] if case == "start_row" else [16, 5])
+    b = batch(lens, starts=[0, 7] if case == "continuation" else None)
+    T = sum(lens)
+    Tp = {"tp_small": 0 if T <= 32 else 32, "tp_ragged": 48}.get(case, (T + 31) // 32 * 32 or 32)
+    k16 = None if case == "no_copy" else (FAKE + 8 if case == "misaligned" else FAKE)
+    out_type = H.HR_FP8_E4M3 if case == "fp8_scale" else H.HR_F16
+    scale = 0.0 if case == "fp8_scale" else 1.0
+    st = lib.hr_attention_f16(ctypes.byref(d), ctypes.byref(b.c), FAKE, k16, FAKE, Tp, FAKE, out_type, scale, None)
+    assert st == status, (st, H.hr_last_error())
+
+
+@pytest.mark.parametrize("case,status", [
     ("continuation", H.HR_EUNSUPPORTED),        # a sequence past position 0
     ("long", H.HR_EUNSUPPORTED),                # 33 rows
     ("out_type", H.HR_EINVAL),

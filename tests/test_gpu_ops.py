@@ -436,7 +436,28 @@ def test_attention_chunked(H, Hq, Hkv, d, lens, starts, causal, used, ct, slots,
     _attention_case(H, Hq, Hkv, d, lens, starts, causal, used, chunked=(ct, slots), fp8=fp8)
 
 
-def _attention_case(H, Hq, Hkv, d, lens, starts, causal, used, chunked=None, fp8=False):
+# attention from fp16 copies of the keys and values (the layer's path for
+# 385-1024 rows from position 0): the copies built here from the same bf16
+# rows (widened exactly), every sequence at a batch row that is a multiple of
+# 8.  Cases: the P = 512 prompt (8 pairs of query blocks); four sequences with
+# odd and even block counts; a ragged last block with an e4m3 output and a
+# larger row count of the copies; head dim 64 with 2 query heads per kv head;
+# long rows with one query head per kv head; non-causal over the used keys
+# (the FP8 prompt shape, and one used key).
+@pytest.mark.parametrize("Hq,Hkv,d,lens,causal,used,fp8,tp_extra", [
+    (32, 8, 128, [512], True, None, False, 0),
+    (32, 8, 128, [296, 128, 40, 8], True, None, False, 0),
+    (32, 8, 128, [100], True, None, True, 64),
+    (4, 2, 64, [72, 33], True, None, False, 0),
+    (8, 8, 64, [1000], True, None, False, 0),
+    (32, 8, 128, [544], False, [512], False, 0),
+    (32, 8, 128, [96, 64], False, [90, 1], False, 0),
+])
+def test_attention_f16(H, Hq, Hkv, d, lens, causal, used, fp8, tp_extra):
+    _attention_case(H, Hq, Hkv, d, lens, [0] * len(lens), causal, used, fp8=fp8, f16_tp_extra=tp_extra)
+
+
+def _attention_case(H, Hq, Hkv, d, lens, starts, causal, used, chunked=None, fp8=False, f16_tp_extra=None):
     import torch
     from gpu_util import dev_bf16, dev_f16, f64_of, log, seeded_f16
     log(f"attention Hq={Hq} Hkv={Hkv} d={d} lens={lens} causal={causal} chunked={chunked} fp8={fp8}")
@@ -461,6 +482,17 @@ def _attention_case(H, Hq, Hkv, d, lens, starts, causal, used, chunked=None, fp8
         nb = H.hr_attention_chunked_workspace_bytes(dims, T, slots)
         ws = torch.full((nb // 4,), float("nan"), dtype=torch.float32, device="cuda")
         H.hr_attention_chunked(dims, b, dev_f16(q), kvd, out, ct, slots, ws, otype, out_scale)
+    elif f16_tp_extra is not None:
+        # batch row t of sequence s is its key row t - cu[s]: cache row s cap + t - cu[s]
+        Tp = (T + 31) // 32 * 32 + f16_tp_extra
+        k16 = np.zeros((Tp, Hkv, d), np.float16)
+        v16 = np.zeros((Tp, Hkv, d), np.float16)
+        cu0 = np.concatenate([[0], np.cumsum(lens)])
+        for s_ in range(n):
+            rows = slice(s_ * cap, s_ * cap + lens[s_])
+            k16[cu0[s_]:cu0[s_ + 1]] = nx.bf16_to_f64(kc[rows]).astype(np.float16)
+            v16[cu0[s_]:cu0[s_ + 1]] = nx.bf16_to_f64(vc[rows]).astype(np.float16)
+        H.hr_attention_f16(dims, b, dev_f16(q), dev_f16(k16), dev_f16(v16), Tp, out, otype, out_scale)
     else:
         H.hr_attention(dims, b, dev_f16(q), kvd, out, otype, out_scale)
     torch.cuda.synchronize()
