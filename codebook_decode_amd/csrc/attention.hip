@@ -45,6 +45,15 @@ __device__ __forceinline__ void wait_vm_f16() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// workgroup barrier without waiting for this thread's memory operations (the
+// copies it publishes were waited for); the empty asm keeps LDS accesses on
+// their side of it
+__device__ __forceinline__ void lds_barrier_f16() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Key chunks of a query block with n_tiles 64-key tiles: at least chunk_tiles
 // tiles per chunk, and no more chunks than n_slots (longer rows take longer
 // chunks).  chunk_tiles == 0: one chunk.
@@ -429,32 +438,37 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(
 // A batch whose keys are all its own rows (every sequence from position 0)
 // and whose QKV launch also wrote fp16 copies of its K and V rows
 // ([Tp][Hkv][d]): the tiles need no conversion, so they go HBM -> LDS by
-// global_load_lds (no register round trip) and every wave can stage its own.
-// That lets the work be balanced: a workgroup takes one query head and the
-// query blocks p and nb-1-p of a sequence (32 rows each; causal: the longest
-// and shortest rows together), and its 4 waves split the two blocks' 32-key
-// tiles, each wave a contiguous run of one block's tiles (waves in proportion
-// to the blocks' tiles, at least one each).  Per tile and wave, as in
-// attention_kernel: S^T = K Q^T with v_mfma_f32_32x32x16_f16 (lane: query
-// l % 32, keys 8(r/4) + 4(l/32) + r%4), the online softmax in base 2
-// (reference max moved only when exceeded by more than 8), O^T += V^T P^T with
-// the lane's own fp16 probabilities as the B operand; the V^T fragment (4
-// consecutive keys of one d per read) comes from the row-major V tile through
-// ds_read_b64_tr_b16: in each group of 16 lanes, lane i = 4e + q supplies the
-// address of 4 elements of row e, and lane 4q + c receives element c of rows
-// 0..3 -- so lane i points at key K0 + i/4, dims 4(i%4)..+3 of its 16-dim
-// group.  Each wave double-buffers its tiles in its own LDS (2 x 2 x 8 KB at
-// d 128), the copies swizzled on the global side so the fragment reads hit
-// distinct banks (k rows of 16 chunks: chunk c of row r at c ^ (r % 16), of 8:
-// c ^ ((r / 2) % 8); v rows: c ^ 4 (r % 4), of 8 chunks c ^ 4 ((r / 2) % 2)).
-// At the end the waves of a block merge their (max, sum, output) through LDS
-// in wave order.  Rows past the copies' last row read that row (finite; their
-// scores are masked).
-constexpr int kF16Waves = 4;
+// global_load_lds (no register round trip, no VALU).  A workgroup takes one
+// query head and the query blocks p and nb-1-p of a sequence (32 rows each;
+// causal: the longest and the shortest rows together, so every workgroup of a
+// prompt has the same number of tiles), as 8 waves: 4 tile streams, stream j
+// taking the 32-key tiles j, j+4, j+8, ... of the longer block, each stream
+// with a wave for each block (the shorter block's wave computes the tiles its
+// rows reach; both copy: the longer block's wave the k half, the other the v
+// half).  One barrier per step of 4 tiles; each stream double-buffers its
+// tiles (2 x 2 x 8 KB at d 128).  Workgroup ids are dealt with the kv head
+// varying fastest, so all workgroups of one kv head share an XCD's L2.  Per
+// tile and wave, as in attention_kernel: S^T = K Q^T with
+// v_mfma_f32_32x32x16_f16 (lane: query l % 32, keys 8(r/4) + 4(l/32) + r%4),
+// the online softmax in base 2 (reference max moved only when exceeded by
+// more than 8), O^T += V^T P^T with the lane's own fp16 probabilities as the B
+// operand; the V^T fragment (4 consecutive keys of one d per read) comes from
+// the row-major V tile through ds_read_b64_tr_b16: in each group of 16 lanes,
+// lane i = 4e + q supplies the address of 4 elements of row e, and lane
+// 4q + c receives element c of rows 0..3 -- so lane i points at key K0 + i/4,
+// dims 4(i%4)..+3 of its 16-dim group.  The copies are swizzled on the global
+// side so the fragment reads hit distinct banks (k rows of 16 chunks: chunk c
+// of row r at c ^ (r % 16), of 8: c ^ ((r / 2) % 8); v rows: c ^ 4 (r % 4),
+// of 8 chunks c ^ 4 ((r / 2) % 2)).  At the end the 4 streams of a block merge
+// their (max, sum, output) through LDS in stream order, and the normalised
+// rows are staged in LDS so they leave as whole 16-byte row chunks.  Rows
+// past the copies' last row read that row (finite; their scores are masked).
+constexpr int kF16Streams = 4;               // tile streams of a workgroup
+constexpr int kF16Waves = 2 * kF16Streams;   // a long-block and a short-block wave per stream
 constexpr int kF16KT = 32;                   // keys per tile
 
 template <int DH>
-constexpr size_t attention_f16_lds() { return size_t(kF16Waves) * 2 * 2 * kF16KT * DH * 2; }
+constexpr size_t attention_f16_lds() { return size_t(kF16Streams) * 2 * 2 * kF16KT * DH * 2; }
 
 // max of a lane's value and lane l ^ 32's (v_permlane32_swap: one VALU, no LDS)
 __device__ __forceinline__ float max_xor32(float x) {
@@ -475,15 +489,21 @@ __global__ __launch_bounds__(64 * kF16Waves) void attention_f16_kernel(
     float scale_log2, void* __restrict__ out, int out_fp8, float out_inv) {
   constexpr int KT = kF16KT;
   constexpr int NKS = DH / 16, NDB = DH / 32;
-  constexpr int KCH = DH / 8;                // 16-byte chunks of a k row
-  constexpr int TB = KT * DH * 2;            // bytes of a k tile (and of a v^T tile)
-  constexpr int NCP = TB / 1024;             // 1-KB wave copies per tile
+  constexpr int KCH = DH / 8;                // 16-byte chunks of a row
+  constexpr int TB = KT * DH * 2;            // bytes of a k tile (and of a v tile)
+  constexpr int NCP = TB / 1024;             // 1-KB wave copies per tile half
   constexpr int STAGE = 2 * TB;
   static_assert(TB % 1024 == 0, "whole wave copies");
   extern __shared__ __attribute__((aligned(16))) uint8_t f16_smem[];
 
-  const int s = blockIdx.z, hh = blockIdx.y, p = blockIdx.x;
-  const int g = hh / (Hq / Hkv);
+  // workgroup id -> (query-block pair, head) with the kv head varying
+  // fastest: consecutive ids go to the 8 XCDs in turn, so every workgroup of
+  // one kv head runs on one XCD and its K / V tiles are shared in that L2
+  const int G = Hq / Hkv;
+  const int wid = int(blockIdx.x) + int(gridDim.x) * int(blockIdx.y);
+  const int g = wid % Hkv, rest = wid / Hkv;
+  const int hh = g * G + rest % G, p = rest / G;
+  const int s = blockIdx.z;
   const int tok0 = cu[s], len = cu[s + 1] - tok0;
   const int nb = (len + 31) / 32;
   const int b_long = nb - 1 - p;
@@ -493,66 +513,53 @@ __global__ __launch_bounds__(64 * kF16Waves) void attention_f16_kernel(
   const int nk_l = causal ? min(32 * b_long + 31, len - 1) + 1 : used;
   const int nk_s = single ? 0 : (causal ? 32 * p + 32 : used);
   const int t_l = (nk_l + KT - 1) / KT, t_s = (nk_s + KT - 1) / KT;
-  int w_l = kF16Waves;
-  if (!single) w_l = max(1, min(kF16Waves - 1, (kF16Waves * t_l + (t_l + t_s) / 2) / (t_l + t_s)));
+  const int n_steps = (t_l + kF16Streams - 1) / kF16Streams;   // t_l >= t_s
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
-  const bool on_long = wave < w_l;
-  const int blk = on_long ? b_long : p;
-  const int nw = on_long ? w_l : kF16Waves - w_l;
-  const int wj = on_long ? wave : wave - w_l;          // the wave's place among its block's
-  const int n_tiles = on_long ? t_l : t_s;
-  const int n_keys = on_long ? nk_l : nk_s;
-  const int ct = (n_tiles + nw - 1) / nw;
-  const int kt0 = min(n_tiles, wj * ct), kt1 = min(n_tiles, kt0 + ct);
+  const int js = wave % kF16Streams;         // stream: tiles js, js + 4, js + 8, ...
+  const bool is_short = wave >= kF16Streams;
+  const int blk = is_short ? p : b_long;
+  const int n_my = is_short ? t_s : t_l;     // tiles of this wave's block
+  const int n_keys = is_short ? nk_s : nk_l;
 
   const int half = lane >> 5, r32 = lane & 31;
   const int i0 = 32 * blk;
   const int iq = i0 + r32;                   // this lane's query (sequence-relative)
-  const bool qok = iq < len;
   u32x4 qf[NKS];
   {
-    const uint16_t* qrow = q + (size_t(tok0 + (qok ? iq : 0)) * Hq + hh) * DH;
+    const uint16_t* qrow = q + (size_t(tok0 + (iq < len ? iq : 0)) * Hq + hh) * DH;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qrow + ks * 16 + half * 8);
   }
 
-  uint8_t* wl = f16_smem + size_t(wave) * 2 * STAGE;
-  const uint8_t* kb = reinterpret_cast<const uint8_t*>(k16) + (size_t(tok0) * Hkv + g) * DH * 2;
-  const size_t krow = size_t(Hkv) * DH * 2;                      // bytes from one key row to the next
-  const uint8_t* vb = reinterpret_cast<const uint8_t*>(v16) + (size_t(tok0) * Hkv + g) * DH * 2;
+  // the stream's tiles: the long-block wave copies the k half, the short-block
+  // wave the v half (a thread's copy i of a tile is its copy i of tile 0 moved
+  // by a uniform step of KT rows: a uniform base plus one byte offset)
+  uint8_t* sl_base = f16_smem + size_t(js) * 2 * STAGE;
+  const size_t krow = size_t(Hkv) * DH * 2;                    // bytes from one key row to the next
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(is_short ? v16 : k16) + (size_t(tok0) * Hkv + g) * DH * 2;
   const int key_last = Tp - tok0 - 1;                          // last row of the copies (relative)
-  // chunk swizzles of a k row and of a v row (see above)
   auto kswz_of = [](int r) { return KCH == 16 ? (r & 15) : ((r >> 1) & 7); };
   auto vswz_of = [](int r) { return KCH == 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
-  // a thread's copy i of a tile is its copy i of tile 0 moved by a uniform
-  // step (KT rows of k, KT columns of v^T): a uniform base plus one byte
-  // offset per copy, no per-tile address arithmetic
-  uint32_t koff[NCP], voff[NCP];
+  uint32_t off[NCP];
 #pragma unroll
   for (int i = 0; i < NCP; ++i) {
     const int sl = 64 * i + lane, r = sl / KCH;
-    koff[i] = uint32_t(r) * uint32_t(krow) + uint32_t((sl % KCH) ^ kswz_of(r)) * 16;
-    voff[i] = uint32_t(r) * uint32_t(krow) + uint32_t((sl % KCH) ^ vswz_of(r)) * 16;
+    off[i] = uint32_t(r) * uint32_t(krow) + uint32_t((sl % KCH) ^ (is_short ? vswz_of(r) : kswz_of(r))) * 16;
   }
-  auto fetch = [&](int kt, int stg) {
-    uint8_t* dk = wl + stg * STAGE;
-    uint8_t* dv = dk + TB;
-    if (kt * KT + KT - 1 <= key_last) {      // uniform: the whole tile inside the copies
-      const uint8_t* kt_base = kb + size_t(kt) * KT * krow;
-      const uint8_t* vt_base = vb + size_t(kt) * KT * krow;
+  auto fetch = [&](int t, int stg) {
+    uint8_t* dst = sl_base + stg * STAGE + (is_short ? TB : 0);
+    if (t * KT + KT - 1 <= key_last) {       // uniform: the whole tile inside the copies
+      const uint8_t* base = src + size_t(t) * KT * krow;
 #pragma unroll
-      for (int i = 0; i < NCP; ++i) lds_dma16(kt_base + koff[i], dk + i * 1024);
-#pragma unroll
-      for (int i = 0; i < NCP; ++i) lds_dma16(vt_base + voff[i], dv + i * 1024);
+      for (int i = 0; i < NCP; ++i) lds_dma16(base + off[i], dst + i * 1024);
       return;
     }
 #pragma unroll
     for (int i = 0; i < NCP; ++i) {
       const int sl = 64 * i + lane, r = sl / KCH;
-      const size_t row = size_t(min(kt * KT + r, key_last)) * krow;
-      lds_dma16(kb + row + ((sl % KCH) ^ kswz_of(r)) * 16, dk + i * 1024);
-      lds_dma16(vb + row + ((sl % KCH) ^ vswz_of(r)) * 16, dv + i * 1024);
+      lds_dma16(src + size_t(min(t * KT + r, key_last)) * krow + ((sl % KCH) ^ (is_short ? vswz_of(r) : kswz_of(r))) * 16,
+                dst + i * 1024);
     }
   };
 
@@ -570,32 +577,34 @@ __global__ __launch_bounds__(64 * kF16Waves) void attention_f16_kernel(
   const int tr_row = 4 * (lane >> 5) + ((lane & 15) >> 2);
   const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  if (kt0 < kt1) fetch(kt0, 0);
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int stg = (kt - kt0) & 1;
-    asm volatile("" ::: "memory");
-    if (kt + 1 < kt1) {
-      fetch(kt + 1, stg ^ 1);                // the other stage: read by the previous tile, done
-      wait_vm_f16<2 * NCP>();                // this tile's copies (and q) landed
-    } else {
-      wait_vm_f16<0>();
-    }
-    asm volatile("" ::: "memory");
-    const uint8_t* sk = wl + stg * STAGE;
+  if (js < t_l) fetch(js, 0);
+  for (int k = 0; k < n_steps; ++k) {
+    wait_vm_f16<0>();                        // this wave's half of step k (and q) landed
+    lds_barrier_f16();                       // both halves landed; step k-1's stage is free
+    const int t = k * kF16Streams + js;
+    if (t + kF16Streams < t_l) fetch(t + kF16Streams, (k + 1) & 1);
+    if (t >= n_my) continue;
+    const uint8_t* sk = sl_base + (k & 1) * STAGE;
     const uint8_t* sv = sk + TB;
-    const int k0 = kt * KT;
-    // every fragment of the tile requested at once: the k reads ahead of the
-    // score MFMAs, the v^T reads behind the softmax
+    const int k0 = t * KT;
+    // the k fragments ahead of the score MFMAs, then the v fragments, whose
+    // reads overlap the softmax (registers: the v reads reuse the k ones)
     u32x4 kf[NKS];
-    u32x2 vf[2][NDB][2];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
       kf[ks] = *reinterpret_cast<const u32x4*>(sk + (r32 * KCH + ((2 * ks + half) ^ kswz)) * 16);
+    __builtin_amdgcn_sched_barrier(0);
+    floatx16 sc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) sc = mfma32_f16(kf[ks], qf[ks], sc);
+    u32x2 vf[2][NDB][2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
-        const int r = 16 * kk + 8 * x + tr_row, vs = vswz_of(r);   // r % 4 = tr_row % 4: vs per lane
+        const int r = 16 * kk + 8 * x + tr_row, vs = vswz_of(r);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const int dd = 32 * db + tr_dim;
@@ -605,11 +614,6 @@ __global__ __launch_bounds__(64 * kF16Waves) void attention_f16_kernel(
         }
       }
     __builtin_amdgcn_sched_barrier(0);
-    floatx16 sc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) sc = mfma32_f16(kf[ks], qf[ks], sc);
     const bool need_mask = causal ? (k0 + KT - 1 > i0) : (k0 + KT > n_keys);
     if (need_mask) {
       const int j_max = causal ? iq : n_keys - 1;
@@ -651,40 +655,49 @@ __global__ __launch_bounds__(64 * kF16Waves) void attention_f16_kernel(
     }
   }
 
-  // merge the block's waves (fixed order) through the now idle LDS
+  // merge each block's streams (fixed order) through the now idle LDS: the
+  // stream-0 wave of a block keeps its state, the other three post theirs
+  // (value-major, so a wave's 64 lanes write 256 contiguous bytes)
   constexpr int kVals = 2 + 16 * NDB;
-  static_assert(size_t(kF16Waves) * 64 * kVals * 4 <= attention_f16_lds<DH>(), "merge buffer");
+  constexpr size_t kMerge = size_t(2 * (kF16Streams - 1)) * kVals * 64 * 4;
+  constexpr int SROW = DH * 2 + 16;          // a staged output row (bytes; 16 apart in banks)
+  static_assert(kMerge + 2 * 32 * SROW <= attention_f16_lds<DH>(), "merge and staging buffers");
   float* xch = reinterpret_cast<float*>(f16_smem);
-  wait_vm_f16<0>();
   __syncthreads();                           // every wave is done with its tiles
-  {
-    float* my = xch + (size_t(wave) * 64 + lane) * kVals;
+  const int slot0 = (is_short ? 1 : 0) * (kF16Streams - 1);
+  if (js > 0) {
+    float* my = xch + size_t(slot0 + js - 1) * kVals * 64 + lane;
     my[0] = m_run;
-    my[1] = l_part;
+    my[64] = l_part;
 #pragma unroll
     for (int j = 0; j < NDB; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) my[2 + 16 * j + r] = o[j][r];
+      for (int r = 0; r < 16; ++r) my[(2 + 16 * j + r) * 64] = o[j][r];
   }
   __syncthreads();
-  if (wj != 0) return;
-  for (int w2 = 1; w2 < nw; ++w2) {
-    const float* ot = xch + (size_t(wave + w2) * 64 + lane) * kVals;
+  if (js > 0 || (is_short && single)) return;
+#pragma unroll 1
+  for (int w2 = 1; w2 < kF16Streams; ++w2) {
+    const float* ot = xch + size_t(slot0 + w2 - 1) * kVals * 64 + lane;
     const float m2 = ot[0];
     const float mm = fmaxf(m_run, m2);
     const float a1 = (m_run == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
     const float a2 = (m2 == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(m2 - mm);
-    l_part = l_part * a1 + ot[1] * a2;
+    l_part = l_part * a1 + ot[64] * a2;
 #pragma unroll
-    for (int j = 0; j < NDB; ++j)
+    for (int j = 0; j < NDB; ++j) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[j][r] = o[j][r] * a1 + ot[2 + 16 * j + r] * a2;
+      for (int r = 0; r < 16; ++r) o[j][r] = o[j][r] * a1 + ot[(2 + 16 * j + r) * 64] * a2;
+      __builtin_amdgcn_sched_barrier(0);     // 16 values in flight at a time (registers)
+    }
     m_run = mm;
   }
   const float l = l_part + __shfl_xor(l_part, 32, kWave);
-  if (!qok) return;
   const float inv_l = l > 0.f ? 1.0f / l : 0.f;
-  const size_t orow = (size_t(tok0 + iq) * Hq + hh) * DH;
+  // the block's normalised rows go to LDS (this wave's own staging area) and
+  // leave as whole 16-byte chunks of a row: a lane's accumulators hold 4
+  // dims of one query, so direct stores would write 8 bytes per row and lane
+  uint8_t* stg = f16_smem + kMerge + (is_short ? 32 * SROW : 0);
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -692,15 +705,23 @@ __global__ __launch_bounds__(64 * kF16Waves) void attention_f16_kernel(
       const int d0 = db * 32 + 8 * rg + 4 * half;
       const float y0 = o[db][4 * rg] * inv_l, y1 = o[db][4 * rg + 1] * inv_l;
       const float y2 = o[db][4 * rg + 2] * inv_l, y3 = o[db][4 * rg + 3] * inv_l;
-      if (out_fp8) {
-        const uint32_t w = f2e4m3(y0 * out_inv) | (f2e4m3(y1 * out_inv) << 8) |
-                           (f2e4m3(y2 * out_inv) << 16) | (f2e4m3(y3 * out_inv) << 24);
-        *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(out) + orow + d0) = w;
-      } else {
-        const u32x2 w = {pack_f16x2(y0, y1), pack_f16x2(y2, y3)};
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow + d0) = w;
-      }
+      if (out_fp8)
+        *reinterpret_cast<uint32_t*>(stg + r32 * SROW + d0) =
+            f2e4m3(y0 * out_inv) | (f2e4m3(y1 * out_inv) << 8) | (f2e4m3(y2 * out_inv) << 16) |
+            (f2e4m3(y3 * out_inv) << 24);
+      else
+        *reinterpret_cast<u32x2*>(stg + r32 * SROW + 2 * d0) = u32x2{pack_f16x2(y0, y1), pack_f16x2(y2, y3)};
     }
+  const int eb = out_fp8 ? 1 : 2;            // output bytes per element
+  const int cpr = DH * eb / 16;              // 16-byte chunks per row
+  const int rpi = kWave / cpr;               // rows per store instruction
+  for (int r0 = 0; r0 < 32; r0 += rpi) {
+    const int r = r0 + lane / cpr, c = lane % cpr;
+    if (i0 + r < len) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * SROW + c * 16);
+      *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(out) + (size_t(tok0 + i0 + r) * Hq + hh) * DH * eb + c * 16) = v;
+    }
+  }
 }
 
 // ============================================================ decode attention

@@ -115,8 +115,9 @@ hr_status hr_attention(const hr_dims* dims, const hr_batch* batch, const void* q
  * step A3 launch writes for 385-1024 rows (the cache's bf16 values widened to
  * fp16, exact), and the layer entries take this path by themselves there.  The
  * tiles go HBM -> LDS without conversion; a workgroup takes one query head and
- * the 32-row query blocks p and nb-1-p of a sequence, its 4 waves splitting
- * their 32-key tiles, merged in a fixed order.  q, out and the tolerances as
+ * the 32-row query blocks p and nb-1-p of a sequence, 4 streams of 32-key
+ * tiles each feeding a wave of both blocks, the streams' partial softmaxes
+ * merged in a fixed order.  q, out and the tolerances as
  * in hr_attention; all pointers device memory, 16-byte aligned (HR_EALIGN);
  * nothing is allocated. */
 hr_status hr_attention_f16(const hr_dims* dims, const hr_batch* batch, const void* q, const void* k16,
