@@ -373,10 +373,15 @@ bool qkv_rope_fused(const hr_dims* d, const hr_batch* b) {
 }
 
 // Attention from the fp16 K / V copies that the fused QKV + step A3 launch
-// writes (hr::launch_attention_f16): every sequence starts at position 0 (its
-// keys are its own rows) and at a row that is a multiple of 8.
-bool attn_f16(const hr_batch* b, const Ws& w, bool fused_qkv) {
-  if (!fused_qkv || !w.k16) return false;
+// writes (hr::launch_attention_f16): causal batches whose sequences all start
+// at position 0 (their keys are their own rows) and at a row that is a
+// multiple of 8.  Measured against the cache kernel (µs, 32 / 8 heads x 128):
+// causal 400 rows 11.6 / 14.5, 512: 13.3 / 16.8, 2 x 256: 10.9 / 11.6, 640:
+// 23.6 / 25.4, 1024: 29.2 / 31.4; non-causal 544 rows over 512 used keys
+// 24.3 / 23.5 (no causal imbalance for the block pairs to even out), so
+// non-causal batches keep the cache kernel and skip the copies.
+bool attn_f16(const hr_dims* d, const hr_batch* b, const Ws& w, bool fused_qkv) {
+  if (!fused_qkv || !w.k16 || !d->causal) return false;
   for (int s = 0; s < b->n_seq; ++s)
     if (b->h_start_pos[s] != 0 || b->h_cu_seqlens[s] % 8 != 0) return false;
   return true;
@@ -408,7 +413,7 @@ hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_layer* next, c
     hr::launch_residual_norm(h, nullptr, 0, T, D, L->in_norm_w, eps, mode, w.x, inv, nullptr, nullptr, 0, st);
   }
   const bool fused_qkv = qkv_rope_fused(d, b);
-  const bool f16_attn = attn_f16(b, w, fused_qkv);
+  const bool f16_attn = attn_f16(d, b, w, fused_qkv);
   if (fused_qkv) {
     hr::QkvRope qr{w.q, kv->k, kv->v, b->cu_seqlens, b->start_pos, b->cache_slot, b->used_keys, b->n_seq,
                    d->causal, kv->capacity, Hq, Hkv, dh, L->q_norm_w, L->k_norm_w, eps, w.rope,

@@ -112,8 +112,9 @@ hr_status hr_attention(const hr_dims* dims, const hr_batch* batch, const void* q
  * finite (zero); Tp a multiple of 32, at least T rounded up to 32 (HR_EINVAL).
  * Every sequence must start at a batch row that is a multiple of 8
  * (HR_EUNSUPPORTED).  These are the copies the layer entries' fused QKV +
- * step A3 launch writes for 385-1024 rows (the cache's bf16 values widened to
- * fp16, exact), and the layer entries take this path by themselves there.  The
+ * step A3 launch writes for causal batches of 385-1024 rows (the cache's bf16
+ * values widened to fp16, exact), and the layer entries take this path by
+ * themselves there.  The
  * tiles go HBM -> LDS without conversion; a workgroup takes one query head and
  * the 32-row query blocks p and nb-1-p of a sequence, 4 streams of 32-key
  * tiles each feeding a wave of both blocks, the streams' partial softmaxes

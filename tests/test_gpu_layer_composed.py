@@ -96,9 +96,9 @@ def test_layer_matches_composed_steps(H, layers, T):
         H.hr_prefill_layer(dims, layer, b, hf, H.make_kv(kf, vf, cap, 1), ws)
         composed_layer(H, m, dims, b, dls[0], hc, H.make_kv(kc, vc, cap, 1), T, fused_short=1 < T <= 32)
         torch.cuda.synchronize()
-        # from 385 to 1024 rows the layer's attention reads the fp16 copies its
-        # fused QKV launch writes (hr_attention_f16's kernel): the same values in
-        # another summation order, so the hidden meets the bar instead of the bits
+        # from 385 to 1024 causal rows the layer's attention reads the fp16 copies
+        # its fused QKV launch writes (hr_attention_f16's kernel): the same values
+        # in another summation order, so the hidden meets the bar instead of the bits
         close("hidden", hf.cpu().numpy(), hc.cpu().numpy(), exact=not 384 < T <= 1024)
         close("K cache", kf[:T].float().cpu().numpy(), kc[:T].float().cpu().numpy())
         close("V cache", vf[:T].float().cpu().numpy(), vc[:T].float().cpu().numpy())
