@@ -100,6 +100,12 @@ CASES = [
     ("layer_d2560_p512", synth.QWEN3_4B, [512], [0], [0], 512),
     # above 1024 rows: the large-M tiles (varlen batches)
     ("layer_d2560_varlen_t1100", synth.QWEN3_4B, [600, 500], [0, 0], [0, 1], 600),
+    # 385-1024 causal rows from position 0: the attention over the fp16 K/V
+    # copies of the fused QKV launch, three sequences at batch rows 0, 296, 464
+    # (multiples of 8); then a batch starting a sequence at row 300, which
+    # keeps the cache kernel
+    ("layer_d2560_varlen_t600_f16", synth.QWEN3_4B, [296, 168, 136], [0, 0, 0], [2, 0, 1], 304),
+    ("layer_d2560_varlen_t429", synth.QWEN3_4B, [300, 129], [0, 0], [1, 0], 304),
 ]
 
 
