@@ -28,12 +28,11 @@ constexpr int kRopeTok = 4;     // tokens per workgroup
 constexpr int kRopeRows = 3;    // head-row rounds with loads in flight per thread
 
 __global__ __launch_bounds__(256) void qknorm_rope_kv_kernel(
-    const float* __restrict__ qkv, int T, int tpb, int Hq, int Hkv, int d, const RopeFreq freq, float eps,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ start_pos,
-    const int32_t* __restrict__ cache_slot, const int32_t* __restrict__ used_keys, int n_seq,
-    int causal, const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
-    uint16_t* __restrict__ q_out, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
-    int capacity) {
+    const float* __restrict__ qkv, const int32_t* __restrict__ cu, const int32_t* __restrict__ start_pos,
+    const int32_t* __restrict__ cache_slot, const int32_t* __restrict__ used_keys, int T, int tpb, int Hq, int Hkv,
+    int d, int n_seq, int causal, float eps, const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
+    uint16_t* __restrict__ q_out, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int capacity,
+    const RopeFreq freq) {   // the 512-byte table last: the pointers above fit the preloaded argument words
   __shared__ float s_cos[kRopeTok][64], s_sin[kRopeTok][64];
   __shared__ long long s_crow[kRopeTok];     // cache row (slot * capacity + position)
   __shared__ int s_wkv[kRopeTok];
@@ -160,10 +159,9 @@ void launch_qknorm_rope_kv(const void* qkv, int T, int Hq, int Hkv, int d, float
   const int blocks = (T + tpb - 1) / tpb;
   const RopeFreq freq = rope_freq(d, theta);
   qknorm_rope_kv_kernel<<<blocks, 256, 0, st>>>(
-      static_cast<const float*>(qkv), T, tpb, Hq, Hkv, d, freq, eps, cu, start_pos, cache_slot,
-      used_keys, n_seq, causal ? 1 : 0, static_cast<const uint16_t*>(qw),
-      static_cast<const uint16_t*>(kw), static_cast<uint16_t*>(q_out), static_cast<uint16_t*>(kc),
-      static_cast<uint16_t*>(vc), capacity);
+      static_cast<const float*>(qkv), cu, start_pos, cache_slot, used_keys, T, tpb, Hq, Hkv, d, n_seq,
+      causal ? 1 : 0, eps, static_cast<const uint16_t*>(qw), static_cast<const uint16_t*>(kw),
+      static_cast<uint16_t*>(q_out), static_cast<uint16_t*>(kc), static_cast<uint16_t*>(vc), capacity, freq);
 }
 
 // ======================================================= short prompts: steps A3 + A4
@@ -198,11 +196,11 @@ __device__ __forceinline__ floatx16 mfma32x16_f16(u32x4 a, u32x4 b, floatx16 c) 
 
 template <int D>
 __global__ __launch_bounds__(64 * kSmallWaves) void rope_attn_small_kernel(
-    const float* __restrict__ qkv, int Hq, int Hkv, const RopeFreq freq, float eps,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ cache_slot, const int32_t* __restrict__ used_keys,
-    int causal, const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw, uint16_t* __restrict__ kc,
-    uint16_t* __restrict__ vc, int capacity, float scale_log2, void* __restrict__ out, int out_fp8,
-    float out_inv) {
+    const float* __restrict__ qkv, const int32_t* __restrict__ cu, const int32_t* __restrict__ cache_slot,
+    const int32_t* __restrict__ used_keys, int Hq, int Hkv, int causal, float eps, const uint16_t* __restrict__ qw,
+    const uint16_t* __restrict__ kw, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int capacity,
+    float scale_log2, void* __restrict__ out, int out_fp8, float out_inv,
+    const RopeFreq freq) {   // the 512-byte table last: the pointers above fit the preloaded argument words
   static_assert(kSmallRows == 32, "one 32 x 32 block of queries and keys");
   constexpr int NT = 64 * kSmallWaves;
   constexpr int HALF = D / 2, L = D / 16, RPW = kWave / L;  // lanes per head row, rows per wave
@@ -386,9 +384,9 @@ void launch_rope_attn_small(const void* qkv, int n_seq, int max_len, int Hq, int
   const dim3 grid(Hq, n_seq);
   auto go = [&](auto kern) {
     kern<<<grid, 64 * kSmallWaves, 0, st>>>(
-        static_cast<const float*>(qkv), Hq, Hkv, freq, eps, cu, cache_slot, used_keys, causal ? 1 : 0,
+        static_cast<const float*>(qkv), cu, cache_slot, used_keys, Hq, Hkv, causal ? 1 : 0, eps,
         static_cast<const uint16_t*>(qw), static_cast<const uint16_t*>(kw), static_cast<uint16_t*>(kc),
-        static_cast<uint16_t*>(vc), capacity, scale_log2, out, fp8 ? 1 : 0, out_inv);
+        static_cast<uint16_t*>(vc), capacity, scale_log2, out, fp8 ? 1 : 0, out_inv, freq);
   };
   if (d == 128) go(rope_attn_small_kernel<128>);
   else go(rope_attn_small_kernel<64>);
