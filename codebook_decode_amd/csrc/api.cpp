@@ -387,6 +387,14 @@ bool attn_f16(const hr_dims* d, const hr_batch* b, const Ws& w, bool fused_qkv) 
   return true;
 }
 
+// The batch's RoPE angle table (workspace, built once per call) is read by
+// the fused QKV epilogue and by the short-prompt RoPE + attention launch
+// (whose workgroups otherwise compute their rows' angles in every layer).
+bool rope_table_used(const hr_dims* d, const hr_batch* b) {
+  if (one_row_batch(b) && d->causal) return false;   // decode steps: the decode launch
+  return qkv_rope_fused(d, b) || small_prompt(b) >= 0;
+}
+
 // Input norm of a layer in its format: fp16 for the bf16 and MXFP4 bands
 // (their QKV GEMM takes fp16 activations), e4m3 with the layer's QKV scale.
 void in_norm_mode(const hr_layer* L, int* mode, float* inv) {
@@ -435,7 +443,7 @@ hr_status run_layer(const hr_dims* d, const hr_layer* L, const hr_layer* next, c
   } else if (const int small = small_prompt(b); small >= 0) {
     hr::launch_rope_attn_small(w.qkv, b->n_seq, small, Hq, Hkv, dh, d->rope_theta, eps, b->cu_seqlens,
                                b->cache_slot, b->used_keys, d->causal != 0, L->q_norm_w, L->k_norm_w, kv->k, kv->v,
-                               kv->capacity, w.attn, fp8, fp8 ? 1.0f / L->as_o : 1.f, st);
+                               kv->capacity, w.attn, fp8, fp8 ? 1.0f / L->as_o : 1.f, st, w.rope);
   } else {
     if (!fused_qkv)
       hr::launch_qknorm_rope_kv(w.qkv, T, Hq, Hkv, dh, d->rope_theta, eps, b->cu_seqlens, b->start_pos,
@@ -522,7 +530,7 @@ hr_status hr_prefill_layer(const hr_dims* dims, const hr_layer* layer, const hr_
   if (ws_bytes < need_ws) return fail(HR_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need_ws);
   Ws w;
   ws_layout(dims, batch->total_tokens, &w, static_cast<uint8_t*>(ws));
-  if (qkv_rope_fused(dims, batch))
+  if (rope_table_used(dims, batch))
     hr::launch_rope_table(batch->cu_seqlens, batch->start_pos, batch->n_seq, batch->total_tokens, dims->head_dim,
                           dims->rope_theta, w.rope, stream);
   return run_layer(dims, layer, nullptr, batch, h, kv, w, false, stream);
@@ -576,7 +584,7 @@ hr_status enqueue_stack(const hr_dims* dims, const hr_layer* layers, const hr_ba
   const bool fp8 = L0.wtype == HR_FP8_E4M3;
   hr::launch_embed_rmsnorm(ids, embed, x_embeds, T, D, L0.in_norm_w, dims->rms_eps, h_out, w.x, fp8,
                            fp8 ? 1.0f / L0.as_qkv : 1.f, stream);
-  if (qkv_rope_fused(dims, batch))   // the angles are the same for every layer
+  if (rope_table_used(dims, batch))   // the angles are the same for every layer
     hr::launch_rope_table(batch->cu_seqlens, batch->start_pos, batch->n_seq, T, dims->head_dim, dims->rope_theta,
                           w.rope, stream);
   // every layer's input norm after the first is fused into the previous

@@ -59,10 +59,12 @@ void launch_qknorm_rope_kv(const void* qkv, int T, int Hq, int Hkv, int d, float
 // Short prompts from position 0 (every sequence at most kSmallRows rows):
 // q/k norm + RoPE + KV write and the attention in one launch, grid (Hq, n_seq)
 constexpr int kSmallRows = 32;
+// tab: the batch's RoPE angle table (launch_rope_table), or null: the
+// workgroups compute the angles of their rows themselves (the same bits)
 void launch_rope_attn_small(const void* qkv, int n_seq, int max_len, int Hq, int Hkv, int d, float theta, float eps,
                             const int32_t* cu, const int32_t* cache_slot, const int32_t* used_keys, bool causal,
                             const void* qw, const void* kw, void* kc, void* vc, int capacity, void* out, bool fp8,
-                            float out_inv, hipStream_t st);
+                            float out_inv, hipStream_t st, const float* tab = nullptr);
 
 // Key-chunk split of the attention (more workgroups for long rows): query
 // blocks with more than chunk_tiles 64-key tiles write fp32 partials per chunk

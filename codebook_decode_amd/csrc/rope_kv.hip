@@ -199,7 +199,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void rope_attn_small_kernel(
     const float* __restrict__ qkv, const int32_t* __restrict__ cu, const int32_t* __restrict__ cache_slot,
     const int32_t* __restrict__ used_keys, int Hq, int Hkv, int causal, float eps, const uint16_t* __restrict__ qw,
     const uint16_t* __restrict__ kw, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int capacity,
-    float scale_log2, void* __restrict__ out, int out_fp8, float out_inv,
+    float scale_log2, void* __restrict__ out, int out_fp8, float out_inv, const float* __restrict__ tab,
     const RopeFreq freq) {   // the 512-byte table last: the pointers above fit the preloaded argument words
   static_assert(kSmallRows == 32, "one 32 x 32 block of queries and keys");
   constexpr int NT = 64 * kSmallWaves;
@@ -251,9 +251,11 @@ __global__ __launch_bounds__(64 * kSmallWaves) void rope_attn_small_kernel(
   const u32x4 wq1 = *reinterpret_cast<const u32x4*>(qw + HALF + 8 * c);
   const u32x4 wk0 = *reinterpret_cast<const u32x4*>(kw + 8 * c);
   const u32x4 wk1 = *reinterpret_cast<const u32x4*>(kw + HALF + 8 * c);
-  for (int a = tid; a < len * HALF; a += NT) {
-    const int i = a / HALF, m = a % HALF;
-    rope_angle(i, freq.inv[m], s_cos[i][m], s_sin[i][m]);
+  if (!tab) {                                                 // else the batch's table (rope_table_kernel)
+    for (int a = tid; a < len * HALF; a += NT) {
+      const int i = a / HALF, m = a % HALF;
+      rope_angle(i, freq.inv[m], s_cos[i][m], s_sin[i][m]);
+    }
   }
   // v^T zeroed (the columns past the prompt stay zero: their probabilities are 0)
   for (int a = tid; a < D * (kSmallRows / 2); a += NT)
@@ -270,8 +272,9 @@ __global__ __launch_bounds__(64 * kSmallWaves) void rope_attn_small_kernel(
     if (kind < 2) {
       const float inv = 1.0f / __builtin_sqrtf(ss / float(D) + eps);
       F8 r0, r1;
-      rope_pairs(lo[k], hi[k], kind == 0 ? wq0 : wk0, kind == 0 ? wq1 : wk1, inv, &s_cos[i][8 * c],
-                 &s_sin[i][8 * c], r0, r1);
+      const float* cs = tab ? tab + size_t(t0 + i) * D + 8 * c : &s_cos[i][8 * c];
+      const float* sn = tab ? cs + HALF : &s_sin[i][8 * c];
+      rope_pairs(lo[k], hi[k], kind == 0 ? wq0 : wk0, kind == 0 ? wq1 : wk1, inv, cs, sn, r0, r1);
       if (kind == 0) {
         *reinterpret_cast<u32x4*>(&s_q[i][8 * c]) = pack8_f16(r0);
         *reinterpret_cast<u32x4*>(&s_q[i][HALF + 8 * c]) = pack8_f16(r1);
@@ -377,7 +380,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void rope_attn_small_kernel(
 void launch_rope_attn_small(const void* qkv, int n_seq, int max_len, int Hq, int Hkv, int d, float theta, float eps,
                             const int32_t* cu, const int32_t* cache_slot, const int32_t* used_keys, bool causal,
                             const void* qw, const void* kw, void* kc, void* vc, int capacity, void* out, bool fp8,
-                            float out_inv, hipStream_t st) {
+                            float out_inv, hipStream_t st, const float* tab) {
   (void)max_len;
   const RopeFreq freq = rope_freq(d, theta);
   const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf(float(d));
@@ -386,7 +389,7 @@ void launch_rope_attn_small(const void* qkv, int n_seq, int max_len, int Hq, int
     kern<<<grid, 64 * kSmallWaves, 0, st>>>(
         static_cast<const float*>(qkv), cu, cache_slot, used_keys, Hq, Hkv, causal ? 1 : 0, eps,
         static_cast<const uint16_t*>(qw), static_cast<const uint16_t*>(kw), static_cast<uint16_t*>(kc),
-        static_cast<uint16_t*>(vc), capacity, scale_log2, out, fp8 ? 1 : 0, out_inv, freq);
+        static_cast<uint16_t*>(vc), capacity, scale_log2, out, fp8 ? 1 : 0, out_inv, tab, freq);
   };
   if (d == 128) go(rope_attn_small_kernel<128>);
   else go(rope_attn_small_kernel<64>);
